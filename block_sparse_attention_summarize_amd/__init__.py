@@ -1,0 +1,254 @@
+"""Block-sparse attention with summary-based block routing on MI355X (gfx950).
+
+Thin ctypes binding of ``libbsa.so`` (C ABI in ``include/bsa.h``).  PyTorch is
+used only for device memory and streams: every step runs in the library's HIP
+kernels.  Importing this package fails loudly if the library has not been
+built (``python -m block_sparse_attention_summarize_amd.build``).
+
+Stages (names as in the C ABI):
+  summarize        keys -> per-block summaries (mean pool, or learned query)
+  route_topk       top-k block selection with forced blocks
+  route_entmax     alpha-entmax block support (histogram-started bisection)
+  attend_prefill   causal attention over the selected blocks' tokens
+  attend_decode    single-token decode over the selected blocks (split-KV)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libbsa.so not found at {LIB_PATH}; build it with "
+        "`python -m block_sparse_attention_summarize_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+F32, BF16 = 0, 1
+PREFILL, DECODE = 0, 1
+FORCE_DIAG, FORCE_FIRST, FORCE_TAIL = 1, 2, 4
+OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE = range(5)
+STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
+          -4: "BSA_ERR_WORKSPACE"}
+
+EXPORTS = ("bsa_summarize", "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill",
+           "bsa_attend_decode", "bsa_workspace_size", "bsa_last_error", "bsa_version")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+_P = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+_SP = ctypes.POINTER(Shape)
+lib.bsa_summarize.argtypes = [_SP, _P, _P, _P, _P]
+lib.bsa_route_topk.argtypes = [_SP, _P, _P, _P, _i32, _u32, _f32, _P, _P, _P, _P, _sz, _P]
+lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, _u32, _f32, _P,
+                                 _P, _P, _P, _P, _sz, _P]
+lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
+lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
+for _f in (lib.bsa_summarize, lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill,
+           lib.bsa_attend_decode):
+    _f.restype = ctypes.c_int
+lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
+lib.bsa_workspace_size.restype = _sz
+lib.bsa_last_error.restype = ctypes.c_char_p
+lib.bsa_version.restype = ctypes.c_char_p
+
+
+class BsaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def version() -> str:
+    return lib.bsa_version().decode()
+
+
+def _check(rc):
+    if rc != 0:
+        raise BsaError(rc, lib.bsa_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _strides(t):
+    if t is None:
+        return (0, 0, 0)
+    if t.stride(3) != 1:
+        raise ValueError("head_dim must be contiguous")
+    return tuple(int(s) for s in t.stride()[:3])
+
+
+def make_shape(*, batch, hq, hkv, d, B, dtype, mode, q_len, kv_len, q=None, k=None, v=None,
+               o=None) -> Shape:
+    s = Shape()
+    s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.block = batch, hq, hkv, d, B
+    s.dtype, s.mode, s.reserved = dtype, mode, 0
+    s.q_len, s.kv_len = q_len, kv_len
+    s.q_stride[:] = _strides(q)
+    s.k_stride[:] = _strides(k)
+    s.v_stride[:] = _strides(v)
+    s.o_stride[:] = _strides(o)
+    return s
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def workspace_size(op: int, shape: Shape, k_or_cap: int) -> int:
+    return int(lib.bsa_workspace_size(op, ctypes.byref(shape), k_or_cap))
+
+
+def _workspace(op, shape, k, device, ws=None):
+    n = workspace_size(op, shape, k)
+    if ws is not None and ws.numel() * ws.element_size() >= n:
+        return ws, n
+    return (torch.empty(max(n, 1), dtype=torch.uint8, device=device), n)
+
+
+def summarize(K: torch.Tensor, B: int, qbar: torch.Tensor | None = None,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """K [b, Hkv, L, d] -> fp32 summaries [b, Hkv, ceil(L/B), d]."""
+    b, hkv, L, d = K.shape
+    nblk = (L + B - 1) // B
+    S = out if out is not None else torch.empty((b, hkv, nblk, d), dtype=torch.float32,
+                                                device=K.device)
+    shape = make_shape(batch=b, hq=hkv, hkv=hkv, d=d, B=B, dtype=_dtype_code(K), mode=PREFILL,
+                       q_len=L, kv_len=L, k=K)
+    if qbar is not None:
+        qbar = qbar.contiguous().to(torch.float32)
+    _check(lib.bsa_summarize(ctypes.byref(shape), _ptr(K), _ptr(qbar), _ptr(S), _stream(K)))
+    return S
+
+
+def _route_shape(Q, S, B, decode, kv_len):
+    b, hq, n, d = Q.shape
+    hkv, nblk = S.shape[1], S.shape[2]
+    if decode:
+        kv_len = kv_len if kv_len is not None else nblk * B
+        return make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q), mode=DECODE,
+                          q_len=1, kv_len=kv_len, q=Q)
+    return make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q), mode=PREFILL,
+                      q_len=n, kv_len=n, q=Q)
+
+
+def route_topk(Q, S, B, k_total, force=0, decode=False, kv_len=None, kv_lens=None,
+               score_scale=0.0, want_scores=False, ws=None, out=None):
+    """Top-k routing.  Returns (idx, cnt) or (idx, cnt, scores)."""
+    shape = _route_shape(Q, S, B, decode, kv_len)
+    b, hkv, nblk = shape.batch, shape.n_kv_heads, S.shape[2]
+    nrow = 1 if decode else (shape.q_len + B - 1) // B
+    dev = Q.device
+    if out is not None:
+        idx, cnt = out
+    else:
+        idx = torch.empty((b, hkv, nrow, k_total), dtype=torch.int32, device=dev)
+        cnt = torch.empty((b, hkv, nrow), dtype=torch.int32, device=dev)
+    scores = torch.empty((b, hkv, nrow, nblk), dtype=torch.float32, device=dev) if want_scores else None
+    wsb, n = _workspace(OP_ROUTE_TOPK, shape, k_total, dev, ws)
+    _check(lib.bsa_route_topk(ctypes.byref(shape), _ptr(Q), _ptr(S), _ptr(kv_lens), k_total, force,
+                              score_scale, _ptr(idx), _ptr(cnt), _ptr(scores), _ptr(wsb), n,
+                              _stream(Q)))
+    return (idx, cnt, scores) if want_scores else (idx, cnt)
+
+
+def route_entmax(Q, S, B, alpha, gamma, cap, force=FORCE_DIAG, n_bins=16, max_iter=8,
+                 decode=False, kv_len=None, kv_lens=None, score_scale=0.0, want_probs=False,
+                 want_tau=False, ws=None):
+    """alpha-entmax routing.  Returns (idx, cnt, probs or None, tau or None)."""
+    shape = _route_shape(Q, S, B, decode, kv_len)
+    b, hq, hkv, nblk = shape.batch, shape.n_q_heads, shape.n_kv_heads, S.shape[2]
+    nrow = 1 if decode else (shape.q_len + B - 1) // B
+    dev = Q.device
+    width = cap + bin(force & 7).count("1")
+    idx = torch.empty((b, hkv, nrow, width), dtype=torch.int32, device=dev)
+    cnt = torch.empty((b, hkv, nrow), dtype=torch.int32, device=dev)
+    probs = torch.empty((b, hq, nrow, nblk), dtype=torch.float32, device=dev) if want_probs else None
+    tau = torch.empty((b, hq, nrow), dtype=torch.float32, device=dev) if want_tau else None
+    wsb, n = _workspace(OP_ROUTE_ENTMAX, shape, cap, dev, ws)
+    _check(lib.bsa_route_entmax(ctypes.byref(shape), _ptr(Q), _ptr(S), _ptr(kv_lens), alpha, gamma,
+                                n_bins, max_iter, cap, force, score_scale, _ptr(idx), _ptr(cnt),
+                                _ptr(probs), _ptr(tau), _ptr(wsb), n, _stream(Q)))
+    return idx, cnt, probs, tau
+
+
+def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None):
+    """Causal attention over the selected blocks.  Q [b, Hq, N, d], K/V [b, Hkv, N, d]."""
+    b, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    odt = out_dtype or Q.dtype
+    O = out if out is not None else torch.empty((b, hq, n, d), dtype=odt, device=Q.device)
+    shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q), mode=PREFILL,
+                       q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=O)
+    _check(lib.bsa_attend_prefill(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx),
+                                  _ptr(cnt), idx.shape[-1], sm_scale, _ptr(O), _dtype_code(O), None,
+                                  0, _stream(Q)))
+    return O
+
+
+def attend_decode(q, K, V, B, idx, cnt, kv_lens=None, sm_scale=0.0, out_dtype=None, ws=None,
+                  out=None):
+    """One query token per sequence.  q [b, Hq, 1, d], K/V caches [b, Hkv, L, d]."""
+    b, hq, _, d = q.shape
+    hkv, L = K.shape[1], K.shape[2]
+    odt = out_dtype or q.dtype
+    O = out if out is not None else torch.empty((b, hq, 1, d), dtype=odt, device=q.device)
+    shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(q), mode=DECODE,
+                       q_len=1, kv_len=L, q=q, k=K, v=V, o=O)
+    k_max = idx.shape[-1]
+    wsb, n = _workspace(OP_ATTEND_DECODE, shape, k_max, q.device, ws)
+    _check(lib.bsa_attend_decode(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(kv_lens),
+                                 _ptr(idx), _ptr(cnt), k_max, sm_scale, _ptr(O), _dtype_code(O),
+                                 _ptr(wsb), n, _stream(q)))
+    return O
+
+
+def prefill_topk(Q, K, V, B, k_total, force=0, S=None, out_dtype=None):
+    """Stage 0 + top-k routing + fine attention for causal prefill."""
+    S = summarize(K, B) if S is None else S
+    idx, cnt = route_topk(Q, S, B, k_total, force)
+    return attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype), idx, cnt
+
+
+def prefill_entmax(Q, K, V, B, alpha, gamma, cap, force=FORCE_DIAG, max_iter=8, S=None,
+                   out_dtype=None):
+    """Stage 0 + alpha-entmax routing + fine attention for causal prefill."""
+    S = summarize(K, B) if S is None else S
+    idx, cnt, _, _ = route_entmax(Q, S, B, alpha, gamma, cap, force, max_iter=max_iter)
+    return attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype), idx, cnt
+
+
+def decode_topk(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, out_dtype=None):
+    """Top-k routing over cached summaries + decode attention."""
+    idx, cnt = route_topk(q, S, B, k_total, force, decode=True, kv_len=K.shape[2], kv_lens=kv_lens)
+    return attend_decode(q, K, V, B, idx, cnt, kv_lens=kv_lens, out_dtype=out_dtype), idx, cnt

@@ -1,0 +1,412 @@
+// Host side of the C ABI in include/bsa.h: argument validation (before
+// anything is enqueued), workspace carving and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bsa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return BSA_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BSA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t nblk_of(const bsa_shape* s) { return (s->kv_len + s->block - 1) / s->block; }
+int64_t nrow_of(const bsa_shape* s) {
+  return s->mode == BSA_PREFILL ? (s->q_len + s->block - 1) / s->block : 1;
+}
+int popcount3(uint32_t f) { return (f & 1u) + ((f >> 1) & 1u) + ((f >> 2) & 1u); }
+int elem_bytes(int32_t dt) { return dt == BSA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point.
+int check_shape(const bsa_shape* s) {
+  if (!s) return fail(BSA_ERR_INVALID, "shape is NULL");
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(BSA_ERR_INVALID, "batch, n_q_heads and n_kv_heads must be >= 1");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(BSA_ERR_INVALID, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->mode != BSA_PREFILL && s->mode != BSA_DECODE)
+    return fail(BSA_ERR_INVALID, "mode must be BSA_PREFILL or BSA_DECODE");
+  if (s->reserved != 0) return fail(BSA_ERR_INVALID, "reserved field must be 0");
+  if (s->kv_len < 1) return fail(BSA_ERR_INVALID, "kv_len must be >= 1");
+  if (s->mode == BSA_PREFILL && s->q_len != s->kv_len)
+    return fail(BSA_ERR_INVALID, "prefill needs q_len == kv_len (got %lld, %lld)",
+                (long long)s->q_len, (long long)s->kv_len);
+  if (s->mode == BSA_DECODE && s->q_len != 1)
+    return fail(BSA_ERR_INVALID, "decode needs q_len == 1 (got %lld)", (long long)s->q_len);
+  if (s->dtype != BSA_F32 && s->dtype != BSA_BF16)
+    return fail(BSA_ERR_UNSUPPORTED, "dtype %d is not supported (BSA_F32, BSA_BF16)", s->dtype);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "head_dim %d is not supported (64, 128)", s->head_dim);
+  if (s->block != 64 && s->block != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "block %d is not supported (64, 128)", s->block);
+  const int64_t nblk = nblk_of(s);
+  const int64_t nrow = nrow_of(s);
+  // grids are 1-D with one workgroup per (batch, head, block) at most
+  const int64_t worst = static_cast<int64_t>(s->batch) * s->n_q_heads * nblk * 2;
+  if (worst >= (int64_t(1) << 31) || nblk * nrow >= (int64_t(1) << 40))
+    return fail(BSA_ERR_UNSUPPORTED, "problem too large for one launch");
+  return BSA_OK;
+}
+
+int check_strides(const char* name, const int64_t st[3], int32_t dtype) {
+  const int64_t q = dtype == BSA_BF16 ? 8 : 4;
+  for (int k = 0; k < 3; ++k) {
+    if (st[k] < 0) return fail(BSA_ERR_INVALID, "%s stride %d is negative", name, k);
+    if (st[k] % q != 0)
+      return fail(BSA_ERR_UNSUPPORTED, "%s stride %d (%lld) must be a multiple of %lld elements",
+                  name, k, (long long)st[k], (long long)q);
+  }
+  return BSA_OK;
+}
+
+int check_ptr(const char* name, const void* p) {
+  if (!p) return fail(BSA_ERR_INVALID, "%s is NULL", name);
+  if (!aligned16(p)) return fail(BSA_ERR_UNSUPPORTED, "%s must be 16-byte aligned", name);
+  return BSA_OK;
+}
+
+bsa::Strides3 st3(const int64_t s[3]) { return bsa::Strides3{s[0], s[1], s[2]}; }
+
+bsa::RowRule rule_of(const bsa_shape* s, int entmax, uint32_t force, const int32_t* kv_lens) {
+  bsa::RowRule r;
+  r.mode = s->mode;
+  r.entmax = entmax;
+  r.force = force;
+  r.B = s->block;
+  r.kv_len = s->kv_len;
+  r.kv_lens = s->mode == BSA_DECODE ? kv_lens : nullptr;
+  return r;
+}
+
+int check_force(const bsa_shape* s, uint32_t force) {
+  if (force & ~7u) return fail(BSA_ERR_INVALID, "unknown force flags 0x%x", force);
+  if (s->mode == BSA_PREFILL && (force & BSA_FORCE_TAIL))
+    return fail(BSA_ERR_INVALID, "BSA_FORCE_TAIL is only meaningful in decode");
+  return BSA_OK;
+}
+
+// Decode split: enough workgroups to fill the chip, LDS for the slice's scores.
+void decode_split(const bsa_shape* s, int32_t k_max, int* bps, int* splits) {
+  const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  int64_t b = (static_cast<int64_t>(k_max) * rows + 2047) / 2048;
+  if (b < 1) b = 1;
+  const int64_t cap = 8192 / (static_cast<int64_t>(G) * s->block);
+  if (b > cap) b = cap < 1 ? 1 : cap;
+  if (b > k_max) b = k_max;
+  *bps = static_cast<int>(b);
+  *splits = static_cast<int>((k_max + b - 1) / b);
+}
+
+size_t ws_route_topk(const bsa_shape* s) {
+  const size_t rows = static_cast<size_t>(s->batch) * s->n_kv_heads * nrow_of(s);
+  return align_up(rows * s->head_dim * 4) + align_up(rows * nblk_of(s) * 4);
+}
+size_t ws_route_entmax(const bsa_shape* s) {
+  const size_t hrows = static_cast<size_t>(s->batch) * s->n_q_heads * nrow_of(s);
+  return align_up(hrows * s->head_dim * 4) + align_up(hrows * nblk_of(s) * 4);
+}
+size_t ws_attend_decode(const bsa_shape* s, int32_t k_max) {
+  int bps, splits;
+  decode_split(s, k_max, &bps, &splits);
+  return align_up(static_cast<size_t>(s->batch) * s->n_q_heads * splits * (s->head_dim + 2) * 4);
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need)
+    return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
+  if (need > 0 && !ws) return fail(BSA_ERR_INVALID, "ws is NULL");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return fail(BSA_ERR_UNSUPPORTED, "ws must be %zu-byte aligned", kAlign);
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_last_error(void) { return g_err.c_str(); }
+
+const char* bsa_version(void) { return "libbsa 0.1 (gfx950)"; }
+
+size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
+  if (check_shape(s) != BSA_OK) return 0;
+  switch (op) {
+    case BSA_OP_ROUTE_TOPK:
+      return ws_route_topk(s);
+    case BSA_OP_ROUTE_ENTMAX:
+      return ws_route_entmax(s);
+    case BSA_OP_ATTEND_DECODE:
+      return k_or_cap >= 1 ? ws_attend_decode(s, k_or_cap) : 0;
+    default:
+      return 0;
+  }
+}
+
+int bsa_summarize(const bsa_shape* s, const void* K, const float* qbar, float* S, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if ((rc = check_ptr("K", K)) != BSA_OK) return rc;
+  if ((rc = check_ptr("S", S)) != BSA_OK) return rc;
+  if (qbar && !aligned16(qbar)) return fail(BSA_ERR_UNSUPPORTED, "qbar must be 16-byte aligned");
+  if ((rc = check_strides("K", s->k_stride, s->dtype)) != BSA_OK) return rc;
+  bsa::SummarizeArgs a;
+  a.K = K;
+  a.ks = st3(s->k_stride);
+  a.qbar = qbar;
+  a.S = S;
+  a.batch = s->batch;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.B = s->block;
+  a.nblk = static_cast<int>(nblk_of(s));
+  a.kv_len = s->kv_len;
+  a.bf16 = s->dtype == BSA_BF16;
+  return device_status(bsa::launch_summarize(a, static_cast<hipStream_t>(stream)), "summarize");
+}
+
+int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int32_t* kv_lens,
+                   int32_t k_total, uint32_t force, float score_scale, int32_t* idx, int32_t* cnt,
+                   float* scores_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if ((rc = check_force(s, force)) != BSA_OK) return rc;
+  if (k_total < 1 || k_total < popcount3(force))
+    return fail(BSA_ERR_INVALID, "k_total (%d) must be >= 1 and >= the number of forced blocks",
+                k_total);
+  if (!std::isfinite(score_scale)) return fail(BSA_ERR_INVALID, "score_scale must be finite");
+  if ((rc = check_ptr("Q", Q)) != BSA_OK) return rc;
+  if ((rc = check_ptr("S", S)) != BSA_OK) return rc;
+  if (!idx || !cnt) return fail(BSA_ERR_INVALID, "idx and cnt must not be NULL");
+  if (scores_out && !aligned16(scores_out))
+    return fail(BSA_ERR_UNSUPPORTED, "scores_out must be 16-byte aligned");
+  if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
+  if ((rc = check_ws(ws, ws_bytes, ws_route_topk(s))) != BSA_OK) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int nrow = static_cast<int>(nrow_of(s));
+  const int nblk = static_cast<int>(nblk_of(s));
+  const size_t rows = static_cast<size_t>(s->batch) * s->n_kv_heads * nrow;
+  float* qhat = static_cast<float*>(ws);
+  float* scores = scores_out ? scores_out
+                             : reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                        align_up(rows * s->head_dim * 4));
+  bsa::QPoolArgs qp;
+  qp.Q = Q;
+  qp.qs = st3(s->q_stride);
+  qp.qhat = qhat;
+  qp.batch = s->batch;
+  qp.hq = s->n_q_heads;
+  qp.hkv = s->n_kv_heads;
+  qp.d = s->head_dim;
+  qp.B = s->block;
+  qp.nrow = nrow;
+  qp.q_len = s->q_len;
+  qp.bf16 = s->dtype == BSA_BF16;
+  qp.group_sum = true;
+  hipError_t e = bsa::launch_qpool(qp, st);
+  if (e != hipSuccess) return device_status(e, "route_topk/qpool");
+  bsa::ScoreArgs sa;
+  sa.qhat = qhat;
+  sa.S = S;
+  sa.scores = scores;
+  sa.batch = s->batch;
+  sa.hkv = s->n_kv_heads;
+  sa.nrow = nrow;
+  sa.nblk = nblk;
+  sa.d = s->head_dim;
+  sa.scale = score_scale != 0.f ? score_scale : 1.f / std::sqrt(static_cast<float>(s->head_dim));
+  sa.rule = rule_of(s, 0, force, kv_lens);
+  e = bsa::launch_scores(sa, st);
+  if (e != hipSuccess) return device_status(e, "route_topk/scores");
+  bsa::SelectArgs se;
+  se.scores = scores;
+  se.idx = idx;
+  se.cnt = cnt;
+  se.batch = s->batch;
+  se.hkv = s->n_kv_heads;
+  se.nrow = nrow;
+  se.nblk = nblk;
+  se.k_total = k_total;
+  se.rule = sa.rule;
+  return device_status(bsa::launch_select_topk(se, st), "route_topk/select");
+}
+
+int bsa_route_entmax(const bsa_shape* s, const void* Q, const float* S, const int32_t* kv_lens,
+                     float alpha, float gamma, int32_t n_bins, int32_t max_iter, int32_t cap,
+                     uint32_t force, float score_scale, int32_t* idx, int32_t* cnt,
+                     float* probs_out, float* tau_out, void* ws, size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if ((rc = check_force(s, force)) != BSA_OK) return rc;
+  if (!(alpha > 1.f) || !std::isfinite(alpha)) return fail(BSA_ERR_INVALID, "alpha must be > 1");
+  if (!std::isfinite(gamma)) return fail(BSA_ERR_INVALID, "gamma must be finite");
+  if (n_bins != 16) return fail(BSA_ERR_INVALID, "n_bins must be 16 (got %d)", n_bins);
+  if (max_iter < 0 || max_iter > 32)
+    return fail(BSA_ERR_INVALID, "max_iter must be in [0, 32] (got %d)", max_iter);
+  if (cap < 1) return fail(BSA_ERR_INVALID, "cap must be >= 1 (got %d)", cap);
+  if (!std::isfinite(score_scale)) return fail(BSA_ERR_INVALID, "score_scale must be finite");
+  if ((rc = check_ptr("Q", Q)) != BSA_OK) return rc;
+  if ((rc = check_ptr("S", S)) != BSA_OK) return rc;
+  if (!idx || !cnt) return fail(BSA_ERR_INVALID, "idx and cnt must not be NULL");
+  if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
+  if ((rc = check_ws(ws, ws_bytes, ws_route_entmax(s))) != BSA_OK) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const int nrow = static_cast<int>(nrow_of(s));
+  const int nblk = static_cast<int>(nblk_of(s));
+  const size_t hrows = static_cast<size_t>(s->batch) * s->n_q_heads * nrow;
+  float* qhat = static_cast<float*>(ws);
+  float* xbuf = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(hrows * s->head_dim * 4));
+  bsa::QPoolArgs qp;
+  qp.Q = Q;
+  qp.qs = st3(s->q_stride);
+  qp.qhat = qhat;
+  qp.batch = s->batch;
+  qp.hq = s->n_q_heads;
+  qp.hkv = s->n_kv_heads;
+  qp.d = s->head_dim;
+  qp.B = s->block;
+  qp.nrow = nrow;
+  qp.q_len = s->q_len;
+  qp.bf16 = s->dtype == BSA_BF16;
+  qp.group_sum = false;
+  hipError_t e = bsa::launch_qpool(qp, st);
+  if (e != hipSuccess) return device_status(e, "route_entmax/qpool");
+  const float scale =
+      score_scale != 0.f ? score_scale : 1.f / std::sqrt(static_cast<float>(s->head_dim));
+  bsa::EntmaxArgs ea;
+  ea.qhat = qhat;
+  ea.S = S;
+  ea.idx = idx;
+  ea.cnt = cnt;
+  ea.probs = probs_out;
+  ea.tau = tau_out;
+  ea.xbuf = xbuf;
+  ea.batch = s->batch;
+  ea.hq = s->n_q_heads;
+  ea.hkv = s->n_kv_heads;
+  ea.nrow = nrow;
+  ea.nblk = nblk;
+  ea.d = s->head_dim;
+  ea.width = cap + popcount3(force);
+  ea.cap = cap;
+  ea.max_iter = max_iter;
+  ea.alpha = alpha;
+  ea.xscale = (alpha - 1.f) * gamma * scale;
+  ea.rule = rule_of(s, 1, force, kv_lens);
+  return device_status(bsa::launch_route_entmax(ea, st), "route_entmax");
+}
+
+static int attend_common(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                         const int32_t* idx, const int32_t* cnt, int32_t k_max, float sm_scale,
+                         void* O, int32_t o_dtype, bsa::AttendArgs& a) {
+  int rc;
+  if ((rc = check_ptr("Q", Q)) != BSA_OK) return rc;
+  if ((rc = check_ptr("K", K)) != BSA_OK) return rc;
+  if ((rc = check_ptr("V", V)) != BSA_OK) return rc;
+  if ((rc = check_ptr("O", O)) != BSA_OK) return rc;
+  if (!idx || !cnt) return fail(BSA_ERR_INVALID, "idx and cnt must not be NULL");
+  if (k_max < 1) return fail(BSA_ERR_INVALID, "k_max must be >= 1");
+  if (!std::isfinite(sm_scale)) return fail(BSA_ERR_INVALID, "sm_scale must be finite");
+  if (o_dtype != s->dtype && o_dtype != BSA_F32)
+    return fail(BSA_ERR_UNSUPPORTED, "o_dtype must be the input dtype or BSA_F32");
+  if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
+  if ((rc = check_strides("K", s->k_stride, s->dtype)) != BSA_OK) return rc;
+  if ((rc = check_strides("V", s->v_stride, s->dtype)) != BSA_OK) return rc;
+  if ((rc = check_strides("O", s->o_stride, o_dtype)) != BSA_OK) return rc;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.qs = st3(s->q_stride);
+  a.ks = st3(s->k_stride);
+  a.vs = st3(s->v_stride);
+  a.os = st3(s->o_stride);
+  a.idx = idx;
+  a.cnt = cnt;
+  a.kv_lens = nullptr;
+  a.ws = nullptr;
+  a.batch = s->batch;
+  a.hq = s->n_q_heads;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.B = s->block;
+  a.k_max = k_max;
+  a.nrow = static_cast<int>(nrow_of(s));
+  a.nblk = static_cast<int>(nblk_of(s));
+  a.splits = 1;
+  a.blocks_per_split = k_max;
+  a.q_len = s->q_len;
+  a.kv_len = s->kv_len;
+  a.sm_scale = sm_scale != 0.f ? sm_scale : 1.f / std::sqrt(static_cast<float>(s->head_dim));
+  a.bf16 = s->dtype == BSA_BF16;
+  a.out_f32 = o_dtype == BSA_F32;
+  return BSA_OK;
+}
+
+int bsa_attend_prefill(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                       const int32_t* idx, const int32_t* cnt, int32_t k_max, float sm_scale,
+                       void* O, int32_t o_dtype, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if (s->mode != BSA_PREFILL) return fail(BSA_ERR_INVALID, "bsa_attend_prefill needs BSA_PREFILL");
+  bsa::AttendArgs a;
+  if ((rc = attend_common(s, Q, K, V, idx, cnt, k_max, sm_scale, O, o_dtype, a)) != BSA_OK)
+    return rc;
+  return device_status(bsa::launch_attend_prefill(a, static_cast<hipStream_t>(stream)),
+                       "attend_prefill");
+}
+
+int bsa_attend_decode(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                      const int32_t* kv_lens, const int32_t* idx, const int32_t* cnt,
+                      int32_t k_max, float sm_scale, void* O, int32_t o_dtype, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if (s->mode != BSA_DECODE) return fail(BSA_ERR_INVALID, "bsa_attend_decode needs BSA_DECODE");
+  if (s->n_q_heads / s->n_kv_heads > 8)
+    return fail(BSA_ERR_UNSUPPORTED, "decode supports at most 8 query heads per KV head");
+  bsa::AttendArgs a;
+  if ((rc = attend_common(s, Q, K, V, idx, cnt, k_max, sm_scale, O, o_dtype, a)) != BSA_OK)
+    return rc;
+  if ((rc = check_ws(ws, ws_bytes, ws_attend_decode(s, k_max))) != BSA_OK) return rc;
+  decode_split(s, k_max, &a.blocks_per_split, &a.splits);
+  a.kv_lens = kv_lens;
+  a.ws = static_cast<float*>(ws);
+  return device_status(bsa::launch_attend_decode(a, static_cast<hipStream_t>(stream)),
+                       "attend_decode");
+}
+
+}  // extern "C"

@@ -1,0 +1,656 @@
+// Stage 2: exact softmax attention restricted to the tokens of the selected
+// blocks ("DashAttention", Declaração do Problema: fine-grained softmax over
+// the selected tokens; Estágio 2 with the routing bias switched off).
+//
+//   attend_prefill_bf16   gathered-KV causal prefill on bf16 MFMA.
+//                         A workgroup (4 wavefronts) owns one (batch, KV head,
+//                         query block) and up to 4 "units" of 64 queries x one
+//                         query head of the GQA group, so every K/V tile it
+//                         stages in LDS serves the whole group.  S^T = K Q^T
+//                         and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16
+//                         with fp32 accumulation; the online softmax is fp32.
+//   attend_prefill_f32    fp32 inputs: one query per lane, VALU dot products
+//                         (fp32 matrix rate is not the bound at these sizes).
+//   attend_decode         split-KV: each workgroup streams a slice of the
+//                         selected blocks of one (batch, KV head) from HBM and
+//                         writes a partial (max, sum, o) per query head.
+//   decode_combine        merges the slices.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bsa {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Position of key r (0..63) of a tile inside a transposed V row.  The S^T
+// accumulator of 16x16 tile kt leaves lane l holding keys 16kt + 4(l/16) + j
+// (j = 0..3); the PV step consumes 32 keys per MFMA with lane l supplying
+// 8 of them, so keys {32kk + 4G + j} and {32kk + 16 + 4G + j} (G = l/16) are
+// stored next to each other and one 16-byte LDS read fetches them.
+__device__ __forceinline__ int vt_pos(int r) {
+  const int kk = r >> 5, q = r & 31;
+  const int hi = q >> 4, rr = q & 15;
+  return 32 * kk + 8 * (rr >> 2) + 4 * hi + (rr & 3);
+}
+
+// Walk of the selected blocks as 64-key tiles: tile index T covers block
+// idx[T / nsub] (nsub = B/64 tiles per block) at offset (T % nsub) * 64.
+struct TileWalk {
+  const int32_t* list;
+  int n;       // number of list entries to use
+  int nsub;
+  int B;
+  int nblk;
+  int64_t kv_len;
+  int64_t qmax;  // last query position of the workgroup
+
+  // key0 of tile T, or -1 when the tile is invalid or entirely in the future.
+  __device__ __forceinline__ int64_t key0(int T) const {
+    const int j = list[T / nsub];
+    if (j < 0 || j >= nblk) return -1;
+    const int64_t k0 = static_cast<int64_t>(j) * B + (T % nsub) * 64;
+    if (k0 > qmax || k0 >= kv_len) return -1;
+    return k0;
+  }
+  __device__ __forceinline__ int next(int T) const {
+    for (++T; T < n * nsub; ++T)
+      if (key0(T) >= 0) return T;
+    return -1;
+  }
+};
+
+template <int D>
+struct PrefillLds {
+  static constexpr int KST = D + 8;   // K tile row stride (bf16 elements)
+  static constexpr int VST = 64 + 8;  // transposed V row stride
+  uint16_t k[2][64 * KST];
+  uint16_t v[2][D * VST];
+};
+
+// Map workgroup id -> (pair = b*hkv + g, query block i, sub-unit).  Heavy
+// query blocks (larger i select more blocks) go first, and when the
+// (batch, KV head) pairs divide evenly over the 8 XCDs (workgroups are
+// dispatched round-robin over them) every workgroup of a pair lands on the
+// same XCD, so the pair's K/V stays in one L2.
+__device__ __forceinline__ void map_wg(int id, int npair, int nrow, int wpb, int& pair, int& i,
+                                       int& sub) {
+  const int total = npair * nrow * wpb;
+  if (npair % 8 == 0 && total % 8 == 0) {
+    const int x = id % 8, s = id / 8;
+    const int per = (npair / 8) * wpb;
+    const int ir = s / per, rest = s % per;
+    pair = x + 8 * (rest / wpb);
+    sub = rest % wpb;
+    i = nrow - 1 - ir;
+    return;
+  }
+  if (8 % npair == 0 && nrow % (8 / npair) == 0) {
+    const int xpp = 8 / npair;
+    const int x = id % 8, s = id / 8;
+    pair = x % npair;
+    const int r = x / npair;
+    const int ir = (s / wpb) * xpp + r;
+    sub = s % wpb;
+    i = nrow - 1 - ir;
+    return;
+  }
+  const int ir = id / (npair * wpb);
+  const int rest = id % (npair * wpb);
+  pair = rest / wpb;
+  sub = rest % wpb;
+  i = nrow - 1 - ir;
+}
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int wpb) {
+  constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
+  constexpr int DT = D / 16;   // 16-row d tiles of O^T
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  constexpr int KITEMS = 64 * CPR / 256;  // K tile chunks per thread
+  constexpr int VITEMS = 32 * CPR / 256;  // V tile key-pair chunks per thread
+  __shared__ PrefillLds<D> lds;
+  using L = PrefillLds<D>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int G = a.hq / a.hkv;
+  const int nsub = a.B / 64;
+  const int units = G * nsub;
+  int pair, i, sub;
+  map_wg(blockIdx.x, a.batch * a.hkv, a.nrow, wpb, pair, i, sub);
+  const int b = pair / a.hkv, g = pair % a.hkv;
+
+  // this wave's unit: one query head and 64 queries of the block
+  const int u = sub * 4 + w;
+  const bool active = u < units;
+  const int hh = active ? u % G : 0;
+  const int qs = active ? u / G : 0;
+  const int h = g * G + hh;
+  const int64_t qpos0 = static_cast<int64_t>(i) * a.B + qs * 64;
+  // last query position of the workgroup (over its active units)
+  int qs_max = 0;
+  for (int uu = sub * 4; uu < sub * 4 + 4 && uu < units; ++uu) qs_max = max(qs_max, uu / G);
+  int64_t qmax = static_cast<int64_t>(i) * a.B + qs_max * 64 + 63;
+  if (qmax > a.q_len - 1) qmax = a.q_len - 1;
+
+  const int64_t rowid = static_cast<int64_t>(pair) * a.nrow + i;
+  int n = a.cnt[rowid];
+  n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
+  TileWalk walk{a.idx + rowid * a.k_max, n, nsub, a.B, a.nblk, a.kv_len, qmax};
+
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h;
+
+  // Q fragments (B operand of S^T = K Q^T): lane l holds query 16qt + l%16,
+  // d = 32ks + 8(l/16) .. +7.
+  uint4 qf[4][KS];
+  {
+    const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h;
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      const int64_t t = qpos0 + qt * 16 + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (active && t < a.q_len)
+          qf[qt][ks] = *reinterpret_cast<const uint4*>(Qg + t * a.qs.t + ks * 32 + (lane >> 4) * 8);
+        else
+          qf[qt][ks] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  f32x4 o[DT][4];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4], l[4];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    m[qt] = -INFINITY;
+    l[qt] = 0.f;
+  }
+  const float sc = a.sm_scale * kLog2e;
+
+  uint4 kreg[KITEMS];
+  uint4 vreg[VITEMS][2];
+  auto load_tile = [&](int64_t k0) {
+#pragma unroll
+    for (int it = 0; it < KITEMS; ++it) {
+      const int flat = tid + 256 * it;
+      const int r = flat / CPR, c = flat % CPR;
+      const int64_t t = k0 + r;
+      kreg[it] = t < a.kv_len ? *reinterpret_cast<const uint4*>(Kg + t * a.ks.t + c * 8)
+                              : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < VITEMS; ++it) {
+      const int flat = tid + 256 * it;
+      const int kp = flat % 32, c = flat / 32;
+      const int64_t t = k0 + 2 * kp;
+      vreg[it][0] = t < a.kv_len ? *reinterpret_cast<const uint4*>(Vg + t * a.vs.t + c * 8)
+                                 : make_uint4(0, 0, 0, 0);
+      vreg[it][1] = t + 1 < a.kv_len
+                        ? *reinterpret_cast<const uint4*>(Vg + (t + 1) * a.vs.t + c * 8)
+                        : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < KITEMS; ++it) {
+      const int flat = tid + 256 * it;
+      const int r = flat / CPR, c = flat % CPR;
+      *reinterpret_cast<uint4*>(&lds.k[buf][r * L::KST + c * 8]) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VITEMS; ++it) {
+      const int flat = tid + 256 * it;
+      const int kp = flat % 32, c = flat / 32;
+      const int pos = vt_pos(2 * kp);
+      const uint32_t a0[4] = {vreg[it][0].x, vreg[it][0].y, vreg[it][0].z, vreg[it][0].w};
+      const uint32_t a1[4] = {vreg[it][1].x, vreg[it][1].y, vreg[it][1].z, vreg[it][1].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // d = 8c + 2e (low halves) and 8c + 2e + 1 (high halves)
+        const uint32_t lo = (a0[e] & 0xffffu) | (a1[e] << 16);
+        const uint32_t hi = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&lds.v[buf][(c * 8 + 2 * e) * L::VST + pos]) = lo;
+        *reinterpret_cast<uint32_t*>(&lds.v[buf][(c * 8 + 2 * e + 1) * L::VST + pos]) = hi;
+      }
+    }
+  };
+
+  int T = walk.next(-1);
+  int buf = 0;
+  if (T >= 0) {
+    load_tile(walk.key0(T));
+    store_tile(0);
+  }
+  __syncthreads();
+  while (T >= 0) {
+    const int64_t k0 = walk.key0(T);
+    const int Tn = walk.next(T);
+    if (Tn >= 0) load_tile(walk.key0(Tn));
+
+    if (active) {
+      // S^T tile: keys 16kt + 4(l/16) + j, query column 16qt + l%16
+      f32x4 s[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const uint4 kf = *reinterpret_cast<const uint4*>(
+              &lds.k[buf][(kt * 16 + (lane & 15)) * L::KST + ks * 32 + (lane >> 4) * 8]);
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
+        }
+      }
+      const bool need_mask = (k0 + 63 > qpos0) || (k0 + 64 > a.kv_len);
+      uint4 pf[4][2];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const int64_t q = qpos0 + qt * 16 + (lane & 15);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v = s[kt][qt][j] * sc;
+            if (need_mask) {
+              const int64_t key = k0 + kt * 16 + (lane >> 4) * 4 + j;
+              if (key > q || key >= a.kv_len) v = -INFINITY;
+            }
+            s[kt][qt][j] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m[qt], mx);
+        const float base = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = exp2f(m[qt] - base);
+        m[qt] = mnew;
+        float rs = 0.f;
+        float p[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            p[kt][j] = exp2f(s[kt][qt][j] - base);
+            rs += p[kt][j];
+          }
+        l[qt] = l[qt] * alpha + rs;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= alpha;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          pf[qt][kk].x = pack_bf16x2(p[2 * kk][0], p[2 * kk][1]);
+          pf[qt][kk].y = pack_bf16x2(p[2 * kk][2], p[2 * kk][3]);
+          pf[qt][kk].z = pack_bf16x2(p[2 * kk + 1][0], p[2 * kk + 1][1]);
+          pf[qt][kk].w = pack_bf16x2(p[2 * kk + 1][2], p[2 * kk + 1][3]);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint4 vf = *reinterpret_cast<const uint4*>(
+              &lds.v[buf][(dt * 16 + (lane & 15)) * L::VST + kk * 32 + (lane >> 4) * 8]);
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) o[dt][qt] = mfma16(vf, pf[qt][kk], o[dt][qt]);
+        }
+      }
+    }
+    if (Tn >= 0) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    T = Tn;
+  }
+
+  if (!active) return;
+  uint8_t* Ob = static_cast<uint8_t*>(a.O);
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    float lt = l[qt];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int64_t t = qpos0 + qt * 16 + (lane & 15);
+    if (t >= a.q_len) continue;
+    const int64_t off = b * a.os.b + h * a.os.h + t * a.os.t;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d0 = dt * 16 + (lane >> 4) * 4;
+      const f32x4 v = o[dt][qt] * inv;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(Ob) + off + d0) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Ob) + off + d0) = pk;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 prefill: one query per lane, 32-key tiles in LDS read by broadcast.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
+  constexpr int KT = 32;
+  __shared__ float ks[KT][D];
+  __shared__ float vs[KT][D];
+  const int lane = threadIdx.x;
+  const int nsub = a.B / 64;
+  // grid: (b, h, i, qs)
+  int id = blockIdx.x;
+  const int qs = id % nsub;
+  id /= nsub;
+  const int i = id % a.nrow;
+  id /= a.nrow;
+  const int h = id % a.hq;
+  const int b = id / a.hq;
+  const int G = a.hq / a.hkv;
+  const int g = h / G;
+  const int64_t qpos0 = static_cast<int64_t>(i) * a.B + qs * 64;
+  const int64_t t = qpos0 + lane;
+  int64_t qmax = qpos0 + 63;
+  if (qmax > a.q_len - 1) qmax = a.q_len - 1;
+  const float* Qg = static_cast<const float*>(a.Q) + b * a.qs.b + h * a.qs.h;
+  const float* Kg = static_cast<const float*>(a.K) + b * a.ks.b + g * a.ks.h;
+  const float* Vg = static_cast<const float*>(a.V) + b * a.vs.b + g * a.vs.h;
+  const float sc = a.sm_scale * kLog2e;
+  float q[D], o[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    q[c] = t < a.q_len ? Qg[t * a.qs.t + c] * sc : 0.f;
+    o[c] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int64_t rowid = (static_cast<int64_t>(b) * a.hkv + g) * a.nrow + i;
+  int n = a.cnt[rowid];
+  n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
+  const int32_t* list = a.idx + rowid * a.k_max;
+  for (int s = 0; s < n; ++s) {
+    const int j = list[s];
+    if (j < 0 || j >= a.nblk) continue;
+    for (int64_t k0 = static_cast<int64_t>(j) * a.B; k0 < static_cast<int64_t>(j + 1) * a.B;
+         k0 += KT) {
+      if (k0 > qmax || k0 >= a.kv_len) break;
+      __syncthreads();
+      for (int e = lane; e < KT * D; e += 64) {
+        const int r = e / D, c = e % D;
+        const int64_t tt = k0 + r;
+        ks[r][c] = tt < a.kv_len ? Kg[tt * a.ks.t + c] : 0.f;
+        vs[r][c] = tt < a.kv_len ? Vg[tt * a.vs.t + c] : 0.f;
+      }
+      __syncthreads();
+      float sv[KT];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < KT; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc = fmaf(q[c], ks[r][c], acc);
+        const int64_t key = k0 + r;
+        sv[r] = (key > t || key >= a.kv_len) ? -INFINITY : acc;
+        mx = fmaxf(mx, sv[r]);
+      }
+      const float mnew = fmaxf(m, mx);
+      const float base = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(m - base);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int c = 0; c < D; ++c) o[c] *= alpha;
+#pragma unroll
+      for (int r = 0; r < KT; ++r) {
+        const float p = exp2f(sv[r] - base);
+        l += p;
+#pragma unroll
+        for (int c = 0; c < D; ++c) o[c] = fmaf(p, vs[r][c], o[c]);
+      }
+    }
+  }
+  if (t >= a.q_len) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float* Og = static_cast<float*>(a.O) + b * a.os.b + h * a.os.h + t * a.os.t;
+#pragma unroll
+  for (int c = 0; c < D; ++c) Og[c] = o[c] * inv;
+}
+
+// ---------------------------------------------------------------------------
+// Decode: split-KV over the selected blocks.
+// ---------------------------------------------------------------------------
+constexpr int kMaxGroup = 8;
+
+template <typename T, int D, int GM>
+__global__ __launch_bounds__(256) void attend_decode_split(AttendArgs a) {
+  constexpr int LPK = D / 8;          // lanes per key row
+  constexpr int KPS = 256 / LPK;      // keys per workgroup step
+  constexpr int PART = D + 2;         // floats per partial state
+  const int G = a.hq / a.hkv;
+  __shared__ float qsh[GM][D];
+  __shared__ float red[4][GM][D];
+  extern __shared__ float sc[];  // [GM][maxkeys]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int split = blockIdx.x % a.splits;
+  const int pair = blockIdx.x / a.splits;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  int64_t L = a.kv_lens ? static_cast<int64_t>(a.kv_lens[b]) : a.kv_len;
+  L = L < 1 ? 1 : (L > a.kv_len ? a.kv_len : L);
+  int n = a.cnt[pair];
+  n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
+  const int32_t* list = a.idx + static_cast<int64_t>(pair) * a.k_max;
+  const int s0 = split * a.blocks_per_split;
+  int s1 = s0 + a.blocks_per_split;
+  s1 = s1 > n ? n : s1;
+  const int nkeys = s1 > s0 ? (s1 - s0) * a.B : 0;
+  const int maxkeys = a.blocks_per_split * a.B;
+  const float scl = a.sm_scale * kLog2e;
+  for (int e = tid; e < G * D; e += 256) {
+    const int hh = e / D, c = e % D;
+    const T* qp = static_cast<const T*>(a.Q) + b * a.qs.b + (g * G + hh) * a.qs.h;
+    float v;
+    if constexpr (sizeof(T) == 2)
+      v = bf16_to_f32(qp[c]);
+    else
+      v = qp[c];
+    qsh[hh][c] = v * scl;
+  }
+  __syncthreads();
+  const T* Kg = static_cast<const T*>(a.K) + b * a.ks.b + g * a.ks.h;
+  const T* Vg = static_cast<const T*>(a.V) + b * a.vs.b + g * a.vs.h;
+  const int c = tid % LPK;
+  // phase 1: scores of every key of the slice, per query head
+  for (int k = tid / LPK; k < nkeys; k += KPS) {
+    const int j = list[s0 + k / a.B];
+    const int64_t tt = static_cast<int64_t>(j) * a.B + k % a.B;
+    const bool valid = j >= 0 && j < a.nblk && tt < L;
+    float kv[8];
+    if (valid)
+      load8_f32<T>(Kg + tt * a.ks.t + c * 8, kv);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kv[e] = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+      if (hh >= G) break;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf(kv[e], qsh[hh][c * 8 + e], s);
+      s = group_sum<LPK>(s);
+      if (c == 0) sc[hh * maxkeys + k] = valid ? s : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // phase 2: per head max and exp (wave w handles heads w, w+4, ...)
+  __shared__ float mh[GM], lh[GM];
+  for (int hh = w; hh < G; hh += 4) {
+    float mx = -INFINITY;
+    for (int k = lane; k < nkeys; k += 64) mx = fmaxf(mx, sc[hh * maxkeys + k]);
+    mx = wave_max(mx);
+    const float base = mx == -INFINITY ? 0.f : mx;
+    float sum = 0.f;
+    for (int k = lane; k < nkeys; k += 64) {
+      const float p = exp2f(sc[hh * maxkeys + k] - base);
+      sc[hh * maxkeys + k] = p;
+      sum += p;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) {
+      mh[hh] = mx;
+      lh[hh] = sum;
+    }
+  }
+  __syncthreads();
+  // phase 3: o_h = sum_k p_hk v_k
+  float acc[GM][8];
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
+  for (int k = tid / LPK; k < nkeys; k += KPS) {
+    const int j = list[s0 + k / a.B];
+    const int64_t tt = static_cast<int64_t>(j) * a.B + k % a.B;
+    const bool valid = j >= 0 && j < a.nblk && tt < L;
+    if (!valid) continue;
+    float vv[8];
+    load8_f32<T>(Vg + tt * a.vs.t + c * 8, vv);
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+      if (hh >= G) break;
+      const float p = sc[hh * maxkeys + k];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
+    }
+  }
+  // reduce over the lanes sharing a d-chunk, then over the waves
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[hh][e];
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      acc[hh][e] = v;
+    }
+  if (lane < LPK) {
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[w][hh][c * 8 + e] = acc[hh][e];
+  }
+  __syncthreads();
+  float* part = a.ws + (static_cast<int64_t>(pair) * a.splits + split) * G * PART;
+  for (int e = tid; e < G * D; e += 256) {
+    const int hh = e / D, cc = e % D;
+    part[hh * PART + 2 + cc] = red[0][hh][cc] + red[1][hh][cc] + red[2][hh][cc] + red[3][hh][cc];
+  }
+  if (tid < G) {
+    part[tid * PART + 0] = mh[tid];
+    part[tid * PART + 1] = lh[tid];
+  }
+}
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(D) void decode_combine(AttendArgs a) {
+  constexpr int PART = D + 2;
+  const int G = a.hq / a.hkv;
+  const int bh = blockIdx.x;  // (b, h)
+  const int b = bh / a.hq, h = bh % a.hq;
+  const int g = h / G, hh = h % G;
+  const int pair = b * a.hkv + g;
+  const float* part = a.ws + static_cast<int64_t>(pair) * a.splits * G * PART;
+  float M = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, part[(s * G + hh) * PART]);
+  const float base = M == -INFINITY ? 0.f : M;
+  float lsum = 0.f, o = 0.f;
+  const int c = threadIdx.x;
+  for (int s = 0; s < a.splits; ++s) {
+    const float* p = part + (s * G + hh) * PART;
+    const float f = exp2f(p[0] - base);
+    lsum += f * p[1];
+    o += f * p[2 + c];
+  }
+  const float v = lsum > 0.f ? o / lsum : 0.f;
+  const int64_t off = b * a.os.b + h * a.os.h;
+  if constexpr (OUT_F32)
+    static_cast<float*>(a.O)[off + c] = v;
+  else
+    static_cast<uint16_t*>(a.O)[off + c] = f32_to_bf16(v);
+}
+
+template <int D>
+hipError_t prefill_bf16_dispatch(const AttendArgs& a, hipStream_t stream) {
+  const int G = a.hq / a.hkv;
+  const int units = G * (a.B / 64);
+  const int wpb = (units + 3) / 4;
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow * wpb;
+  if (a.out_f32)
+    hipLaunchKernelGGL((attend_prefill_bf16<D, true>), dim3(grid), dim3(256), 0, stream, a, wpb);
+  else
+    hipLaunchKernelGGL((attend_prefill_bf16<D, false>), dim3(grid), dim3(256), 0, stream, a, wpb);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t decode_dispatch(const AttendArgs& a, hipStream_t stream) {
+  const int G = a.hq / a.hkv;
+  const size_t dyn = sizeof(float) * static_cast<size_t>(G) * a.blocks_per_split * a.B;
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.splits;
+  if (G <= 1)
+    hipLaunchKernelGGL((attend_decode_split<T, D, 1>), dim3(grid), dim3(256), dyn, stream, a);
+  else if (G <= 2)
+    hipLaunchKernelGGL((attend_decode_split<T, D, 2>), dim3(grid), dim3(256), dyn, stream, a);
+  else if (G <= 4)
+    hipLaunchKernelGGL((attend_decode_split<T, D, 4>), dim3(grid), dim3(256), dyn, stream, a);
+  else
+    hipLaunchKernelGGL((attend_decode_split<T, D, 8>), dim3(grid), dim3(256), dyn, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned cgrid = static_cast<unsigned>(a.batch) * a.hq;
+  if (a.out_f32)
+    hipLaunchKernelGGL((decode_combine<D, true>), dim3(cgrid), dim3(D), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_combine<D, false>), dim3(cgrid), dim3(D), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.d == 64 ? prefill_bf16_dispatch<64>(a, stream) : prefill_bf16_dispatch<128>(a, stream);
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hq * a.nrow * (a.B / 64);
+  if (a.d == 64)
+    hipLaunchKernelGGL(attend_prefill_f32<64>, dim3(grid), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attend_prefill_f32<128>, dim3(grid), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_decode(const AttendArgs& a, hipStream_t stream) {
+  if (a.bf16) return a.d == 64 ? decode_dispatch<uint16_t, 64>(a, stream) : decode_dispatch<uint16_t, 128>(a, stream);
+  return a.d == 64 ? decode_dispatch<float, 64>(a, stream) : decode_dispatch<float, 128>(a, stream);
+}
+
+}  // namespace bsa

@@ -1,0 +1,102 @@
+// Launch interface between the host layer (api.cpp) and the gfx950 kernels.
+// Every launcher enqueues on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// Strides are in elements; the head_dim stride is 1.
+struct Strides3 {
+  int64_t b, h, t;
+};
+
+struct SummarizeArgs {
+  const void* K;
+  Strides3 ks;
+  const float* qbar;  // nullptr -> mean
+  float* S;           // [batch, hkv, nblk, d]
+  int batch, hkv, d, B, nblk;
+  int64_t kv_len;
+  bool bf16;
+};
+hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
+
+// Routing query of every row.  Prefill: mean over the query block, decode:
+// the query itself.  group_sum: add the heads of each KV group (top-k) and
+// write [batch, hkv, nrow, d]; otherwise [batch, hq, nrow, d].
+struct QPoolArgs {
+  const void* Q;
+  Strides3 qs;
+  float* qhat;
+  int batch, hq, hkv, d, B, nrow;
+  int64_t q_len;
+  bool bf16, group_sum;
+};
+hipError_t launch_qpool(const QPoolArgs& a, hipStream_t stream);
+
+// Candidate range and forced blocks of a routing row are derived on the
+// device from (mode, row, kv_lens) exactly as documented in bsa.h.
+struct RowRule {
+  int mode;       // 0 prefill, 1 decode
+  int entmax;     // 1: prefill candidates exclude the diagonal
+  uint32_t force;
+  int B;
+  int64_t kv_len;
+  const int32_t* kv_lens;  // decode, may be null
+};
+
+// scores[row, j] = scale * qhat[row] . S[b, g, j] for candidate j, -inf else.
+struct ScoreArgs {
+  const float* qhat;  // [batch, hkv, nrow, d]
+  const float* S;     // [batch, hkv, nblk, d]
+  float* scores;      // [batch, hkv, nrow, nblk]
+  int batch, hkv, nrow, nblk, d;
+  float scale;
+  RowRule rule;
+};
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream);
+
+struct SelectArgs {
+  const float* scores;  // [rows, nblk]
+  int32_t* idx;         // [rows, k_total]
+  int32_t* cnt;         // [rows]
+  int batch, hkv, nrow, nblk, k_total;
+  RowRule rule;
+};
+hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream);
+
+struct EntmaxArgs {
+  const float* qhat;  // [batch, hq, nrow, d]
+  const float* S;     // [batch, hkv, nblk, d]
+  int32_t* idx;       // [batch, hkv, nrow, width]
+  int32_t* cnt;
+  float* probs;       // optional [batch, hq, nrow, nblk]
+  float* tau;         // optional [batch, hq, nrow]
+  float* xbuf;        // workspace [batch, hkv, nrow, G, nblk]
+  int batch, hq, hkv, nrow, nblk, d, width, cap, max_iter;
+  float alpha, xscale;  // x = xscale * qhat . s, xscale = (alpha-1)*gamma*score_scale
+  RowRule rule;
+};
+hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream);
+
+struct AttendArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  Strides3 qs, ks, vs, os;
+  const int32_t* idx;  // [batch, hkv, nrow, k_max]
+  const int32_t* cnt;
+  const int32_t* kv_lens;  // decode
+  float* ws;               // decode partial states
+  int batch, hq, hkv, d, B, k_max, nrow, nblk, splits, blocks_per_split;
+  int64_t q_len, kv_len;
+  float sm_scale;
+  bool bf16, out_f32;
+};
+hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_attend_decode(const AttendArgs& a, hipStream_t stream);
+
+}  // namespace bsa

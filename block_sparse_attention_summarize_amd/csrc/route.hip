@@ -1,0 +1,523 @@
+// Stage 1: block routing.
+//
+//   scores_kernel   coarse scores of every candidate block against the row's
+//                   routing query ("DashAttention", Declaração do Problema:
+//                   coarse attention scores between queries and block
+//                   summaries).  fp32 throughout: selections must agree with
+//                   an fp64 reference whenever the k-th/(k+1)-th gap exceeds
+//                   1e-4, so no reduced-precision matrix cores here.
+//   select_kernel   top-k with forced blocks and the lower-index tie rule
+//                   ("Gist Sparse Attention", section 2 item 3).  Exact radix
+//                   select on order-preserving uint32 keys (4 passes of 8
+//                   bits over an LDS histogram), then an ordered ballot scan
+//                   that resolves ties toward lower block ids and writes the
+//                   ascending list.
+//   entmax_kernel   alpha-entmax support per query head ("DashAttention",
+//                   Estágio 1) with the threshold bracketed by a 16-bin LDS
+//                   histogram and refined by bisection ("AdaSplash-2", 2.A),
+//                   GQA-averaged probabilities, cap by the same radix select.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bsa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kChunk = 128;  // candidate blocks scored per workgroup
+
+struct RowInfo {
+  int cand_end;  // candidates are [0, cand_end)
+  int own;       // the row's own block (diagonal / tail)
+  int forced[2];
+  int nforced;
+  int span;  // every block id that can appear in the selection is < span
+};
+
+// Candidate range and forced blocks of one routing row, as documented in bsa.h.
+__device__ inline RowInfo row_info(const RowRule& r, int b, int row) {
+  RowInfo ri;
+  if (r.mode == 0) {
+    ri.own = row;
+    ri.cand_end = r.entmax ? row : row + 1;
+  } else {
+    int64_t L = r.kv_lens ? static_cast<int64_t>(r.kv_lens[b]) : r.kv_len;
+    L = L < 1 ? 1 : (L > r.kv_len ? r.kv_len : L);
+    ri.own = static_cast<int>((L - 1) / r.B);
+    ri.cand_end = ri.own;
+  }
+  ri.nforced = 0;
+  if (r.force & 2u) ri.forced[ri.nforced++] = 0;
+  const bool own_forced = (r.force & 1u) || (r.mode == 1 && (r.force & 4u));
+  if (own_forced && !(ri.nforced == 1 && ri.forced[0] == ri.own)) ri.forced[ri.nforced++] = ri.own;
+  ri.span = ri.own + 1 > ri.cand_end ? ri.own + 1 : ri.cand_end;
+  return ri;
+}
+
+__device__ inline bool is_forced(const RowInfo& ri, int j) {
+  return (ri.nforced > 0 && ri.forced[0] == j) || (ri.nforced > 1 && ri.forced[1] == j);
+}
+
+// ---------------------------------------------------------------------------
+// Coarse scores.  d/4 lanes share one summary row (a float4 each); the dot is
+// finished with a butterfly over those lanes.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
+  constexpr int LPR = D / 4;           // lanes per summary row
+  constexpr int RPW = kWave / LPR;     // rows per wave step
+  const int nchunk = (a.nblk + kChunk - 1) / kChunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int rowid = blockIdx.x / nchunk;  // (b, g, row)
+  const int row = rowid % a.nrow;
+  const int bg = rowid / a.nrow;
+  const int b = bg / a.hkv;
+  const RowInfo ri = row_info(a.rule, b, row);
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int c = lane % LPR;
+  const float4 q = reinterpret_cast<const float4*>(a.qhat + static_cast<int64_t>(rowid) * D)[c];
+  const float* Sg = a.S + static_cast<int64_t>(bg) * a.nblk * D;
+  float* out = a.scores + static_cast<int64_t>(rowid) * a.nblk;
+  const int j0 = chunk * kChunk;
+  for (int jj = w * RPW + lane / LPR; jj < kChunk; jj += kWaves * RPW) {
+    const int j = j0 + jj;
+    if (j >= a.nblk) break;
+    float s = -INFINITY;
+    if (j < ri.cand_end) {
+      const float4 v = reinterpret_cast<const float4*>(Sg + static_cast<int64_t>(j) * D)[c];
+      float p = q.x * v.x;
+      p = fmaf(q.y, v.y, p);
+      p = fmaf(q.z, v.z, p);
+      p = fmaf(q.w, v.w, p);
+      p = group_sum<LPR>(p);
+      s = p * a.scale;
+    }
+    if (c == 0) out[j] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup-wide helpers (256 threads).
+// ---------------------------------------------------------------------------
+
+// Exclusive prefix count of `flag` over the workgroup in thread order.
+__device__ inline int block_scan(int flag, int* wave_tot, int& total) {
+  const uint64_t m = __ballot(flag);
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  if (lane == 0) wave_tot[w] = __popcll(m);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const int v = wave_tot[k];
+    off += k < w ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return off + lanes_below(m);
+}
+
+// Radix select: the key T of the m-th largest eligible element (1 <= m <=
+// #eligible) and how many elements equal to T belong to the top m.
+// `get(e, key)` returns whether element e is eligible and its key.
+template <typename Get>
+__device__ inline void radix_select(int n, int m, Get get, int* hist, int* bcast, uint32_t& T,
+                                    int& need) {
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = m;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int k = threadIdx.x; k < 256; k += kThreads) hist[k] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += kThreads) {
+      uint32_t key;
+      if (get(e, key) && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      // lane l owns bins 4l..4l+3; suffix sums from the top bin down
+      const int l = threadIdx.x;
+      const int h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
+      const int own = h0 + h1 + h2 + h3;
+      int incl = own;  // sum over lanes >= l
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_down(incl, o, kWave);
+        incl += (l + o < kWave) ? v : 0;
+      }
+      const int above = incl - own;  // elements in bins above this lane's bins
+      if (above < remaining && incl >= remaining) {
+        int cum = above, bin = 4 * l + 3;
+        const int hv[4] = {h0, h1, h2, h3};
+        for (int k = 3; k >= 0; --k) {
+          if (cum + hv[k] >= remaining) {
+            bin = 4 * l + k;
+            break;
+          }
+          cum += hv[k];
+        }
+        bcast[0] = bin;
+        bcast[1] = remaining - cum;
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = static_cast<uint32_t>(bcast[0]);
+    remaining = bcast[1];
+    prefix |= bin << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  T = prefix;
+  need = remaining;
+}
+
+// Writes the ascending selection (forced blocks + the routed top m of the
+// eligible elements, ties to lower ids) to idx[0:width], pads with -1 and
+// returns the count.  Elements range over [0, span).
+template <typename Get>
+__device__ inline int select_and_write(const RowInfo& ri, int span, int m, int n_elig, Get get,
+                                       int32_t* idx, int width, int* hist, int* bcast,
+                                       int* wave_tot) {
+  uint32_t T = 0;
+  int need = 0;
+  const bool all = m >= n_elig;
+  if (!all && m > 0) radix_select(span, m, get, hist, bcast, T, need);
+  int carry_eq = 0, carry_sel = 0;
+  for (int base = 0; base < span; base += kThreads) {
+    const int e = base + static_cast<int>(threadIdx.x);
+    uint32_t key = 0;
+    const bool elig = e < span && get(e, key);
+    const bool eq = elig && !all && m > 0 && key == T;
+    int tot_eq;
+    const int r_eq = block_scan(eq ? 1 : 0, wave_tot, tot_eq) + carry_eq;
+    bool sel;
+    if (e >= span)
+      sel = false;
+    else if (is_forced(ri, e))
+      sel = true;
+    else if (!elig || m == 0)
+      sel = false;
+    else if (all)
+      sel = true;
+    else
+      sel = key > T || (eq && r_eq < need);
+    int tot_sel;
+    const int pos = block_scan(sel ? 1 : 0, wave_tot, tot_sel) + carry_sel;
+    if (sel && pos < width) idx[pos] = e;
+    carry_eq += tot_eq;
+    carry_sel += tot_sel;
+  }
+  for (int p = carry_sel + static_cast<int>(threadIdx.x); p < width; p += kThreads) idx[p] = -1;
+  return carry_sel < width ? carry_sel : width;
+}
+
+// ---------------------------------------------------------------------------
+// Top-k select, one workgroup per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
+  __shared__ int hist[256];
+  __shared__ int bcast[2];
+  __shared__ int wave_tot[kWaves];
+  const int rowid = blockIdx.x;
+  const int row = rowid % a.nrow;
+  const int b = rowid / (a.nrow * a.hkv);
+  const RowInfo ri = row_info(a.rule, b, row);
+  const float* sc = a.scores + static_cast<int64_t>(rowid) * a.nblk;
+  const int n_elig = ri.cand_end - [&] {
+    int k = 0;
+    for (int f = 0; f < ri.nforced; ++f) k += ri.forced[f] < ri.cand_end ? 1 : 0;
+    return k;
+  }();
+  int m = a.k_total - ri.nforced;
+  m = m < 0 ? 0 : m;
+  auto get = [&](int e, uint32_t& key) -> bool {
+    if (e >= ri.cand_end || is_forced(ri, e)) return false;
+    key = float_key(sc[e]);
+    return true;
+  };
+  const int c = select_and_write(ri, ri.span, m, n_elig, get, a.idx + static_cast<int64_t>(rowid) * a.k_total,
+                                 a.k_total, hist, bcast, wave_tot);
+  if (threadIdx.x == 0) a.cnt[rowid] = c;
+}
+
+// ---------------------------------------------------------------------------
+// alpha-entmax routing, one workgroup per (b, g, row); wave w handles the
+// query heads w, w+4, ... of the group.  The logits of each head live in the
+// workspace row xbuf[head][0:nblk] (L1/L2 resident across the passes).
+// ---------------------------------------------------------------------------
+
+// [x - t]_+^(1/(alpha-1))
+__device__ __forceinline__ float emass(float x, float t, float alpha) {
+  const float d = x - t;
+  if (!(d > 0.f)) return 0.f;
+  if (alpha == 1.5f) return d * d;
+  if (alpha == 2.f) return d;
+  return powf(d, 1.f / (alpha - 1.f));
+}
+
+// Root of sum_k c_k [e_k - tau]_+^(1/(alpha-1)) = 1 for 16 values e_k sorted
+// descending with counts c_k: sort-based closed forms for alpha in {1.5, 2},
+// 64 bisection steps on [e_0 - 1, e_0] otherwise.
+__device__ inline float solve_bins(const float* e, const int* c, float alpha) {
+  if (alpha == 2.f || alpha == 1.5f) {
+    float n = 0.f, s1 = 0.f, s2 = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      if (c[r] == 0) continue;
+      const float cr = static_cast<float>(c[r]);
+      n += cr;
+      s1 += cr * e[r];
+      s2 += cr * e[r] * e[r];
+      float tau;
+      if (alpha == 2.f) {
+        tau = (s1 - 1.f) / n;
+      } else {
+        const float M = s1 / n;
+        float Q = 0.f;  // squared deviations, recomputed for accuracy
+        for (int k = 0; k <= r; ++k) {
+          const float dv = e[k] - M;
+          Q += static_cast<float>(c[k]) * dv * dv;
+        }
+        if (Q > 1.f) continue;
+        tau = M - sqrtf((1.f - Q) / n);
+      }
+      int nx = r + 1;
+      while (nx < 16 && c[nx] == 0) ++nx;
+      if (tau < e[r] && (nx >= 16 || tau >= e[nx])) return tau;
+    }
+  }
+  float lo = e[0] - 1.f, hi = e[0];
+  for (int it = 0; it < 64; ++it) {
+    const float mid = 0.5f * (lo + hi);
+    float f = 0.f;
+    for (int r = 0; r < 16; ++r) f += static_cast<float>(c[r]) * emass(e[r], mid, alpha);
+    if (f >= 1.f)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5f * (lo + hi);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
+  constexpr int LPR = D / 4;
+  constexpr int RPW = kWave / LPR;
+  __shared__ int hist[256];
+  __shared__ int bcast[2];
+  __shared__ int wave_tot[kWaves];
+  __shared__ int bins[kWaves][16];
+  const int G = a.hq / a.hkv;
+  const int rowid = blockIdx.x;  // (b, g, row)
+  const int row = rowid % a.nrow;
+  const int bg = rowid / a.nrow;
+  const int g = bg % a.hkv;
+  const int b = bg / a.hkv;
+  const RowInfo ri = row_info(a.rule, b, row);
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int n = ri.cand_end;  // candidate range; forced ids inside are excluded
+  float* xrow = a.xbuf + static_cast<int64_t>(rowid) * G * a.nblk;
+  const float* Sg = a.S + static_cast<int64_t>(bg) * a.nblk * D;
+  const float alpha = a.alpha;
+
+  for (int hh = w; hh < G; hh += kWaves) {
+    const int h = g * G + hh;
+    const int64_t hrow = (static_cast<int64_t>(b) * a.hq + h) * a.nrow + row;
+    float* x = xrow + static_cast<int64_t>(hh) * a.nblk;
+    // logits
+    const int c = lane % LPR;
+    const float4 q = reinterpret_cast<const float4*>(a.qhat + hrow * D)[c];
+    for (int j = lane / LPR; j < n; j += RPW) {
+      const float4 v = reinterpret_cast<const float4*>(Sg + static_cast<int64_t>(j) * D)[c];
+      float p = q.x * v.x;
+      p = fmaf(q.y, v.y, p);
+      p = fmaf(q.z, v.z, p);
+      p = fmaf(q.w, v.w, p);
+      p = group_sum<LPR>(p);
+      if (c == 0) x[j] = is_forced(ri, j) ? -INFINITY : p * a.xscale;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    // number of eligible candidates and the maximum
+    float xmax = -INFINITY;
+    int ne = 0;
+    for (int j = lane; j < n; j += kWave) {
+      const float v = x[j];
+      if (v != -INFINITY) {
+        xmax = fmaxf(xmax, v);
+        ++ne;
+      }
+    }
+    xmax = wave_max(xmax);
+    ne = wave_sum_i(ne);
+    float tau = __builtin_nanf("");
+    if (ne > 0) {
+      // 16-bin histogram of u = xmax - x on [0, 1)
+      if (lane < 16) bins[w][lane] = 0;
+      __builtin_amdgcn_wave_barrier();
+      for (int j = lane; j < n; j += kWave) {
+        const float v = x[j];
+        if (v == -INFINITY) continue;
+        const float u = xmax - v;
+        if (u < 1.f) {
+          int bin = static_cast<int>(floorf(u * 16.f));
+          bin = bin > 15 ? 15 : bin;
+          atomicAdd(&bins[w][bin], 1);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      int cnts[16];
+      float edge[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) cnts[k] = bins[w][k];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) edge[k] = xmax - static_cast<float>(k + 1) * 0.0625f;
+      const float tau_lo = solve_bins(edge, cnts, alpha);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) edge[k] = xmax - static_cast<float>(k) * 0.0625f;
+      const float tau_hi = solve_bins(edge, cnts, alpha);
+      float lo = fmaxf(tau_lo, xmax - 1.f);
+      float hi = fminf(tau_hi, xmax - powf(static_cast<float>(ne), 1.f - alpha));
+      bool resolved = false;
+      for (int it = 0;; ++it) {
+        int inside = 0;
+        for (int j = lane; j < n; j += kWave) {
+          const float v = x[j];
+          inside |= (v > lo && v <= hi) ? 1 : 0;
+        }
+        if (__ballot(inside) == 0) {
+          resolved = true;
+          break;
+        }
+        if (it >= a.max_iter) break;
+        const float mid = 0.5f * (lo + hi);
+        float f = 0.f;
+        for (int j = lane; j < n; j += kWave) f += emass(x[j], mid, alpha);
+        f = wave_sum(f);
+        if (f >= 1.f)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      tau = lo;
+      if (resolved) {
+        // exact threshold of the support {x > lo}
+        float s1 = 0.f;
+        int ns = 0;
+        for (int j = lane; j < n; j += kWave) {
+          const float v = x[j];
+          if (v > lo) {
+            s1 += v;
+            ++ns;
+          }
+        }
+        s1 = wave_sum(s1);
+        ns = wave_sum_i(ns);
+        const float nsf = static_cast<float>(ns);
+        if (alpha == 2.f) {
+          tau = (s1 - 1.f) / nsf;
+        } else if (alpha == 1.5f) {
+          const float M = s1 / nsf;
+          float Q = 0.f;
+          for (int j = lane; j < n; j += kWave) {
+            const float v = x[j];
+            if (v > lo) Q += (v - M) * (v - M);
+          }
+          Q = wave_sum(Q);
+          tau = M - sqrtf(fmaxf((1.f - Q) / nsf, 0.f));
+        } else {
+          float l2 = lo, h2 = lo + 1.f;  // the root is below max x <= lo + 1
+          for (int it = 0; it < 64; ++it) {
+            const float mid = 0.5f * (l2 + h2);
+            float f = 0.f;
+            for (int j = lane; j < n; j += kWave) {
+              const float v = x[j];
+              if (v > lo) f += emass(v, mid, alpha);
+            }
+            f = wave_sum(f);
+            if (f >= 1.f)
+              l2 = mid;
+            else
+              h2 = mid;
+          }
+          tau = 0.5f * (l2 + h2);
+        }
+      }
+      // probabilities, renormalised; stored over the logits
+      float z = 0.f;
+      for (int j = lane; j < n; j += kWave) z += emass(x[j], tau, alpha);
+      z = wave_sum(z);
+      const float iz = 1.f / z;
+      for (int j = lane; j < n; j += kWave) x[j] = emass(x[j], tau, alpha) * iz;
+    } else {
+      for (int j = lane; j < n; j += kWave) x[j] = 0.f;
+    }
+    if (a.tau && lane == 0) a.tau[hrow] = tau;
+    if (a.probs) {
+      float* pr = a.probs + hrow * a.nblk;
+      for (int j = lane; j < a.nblk; j += kWave) pr[j] = j < n ? x[j] : 0.f;
+    }
+  }
+  __syncthreads();
+  // GQA: mean probability over the group's heads; keep the positive ones,
+  // capped by the radix select.
+  const float invG = 1.f / static_cast<float>(G);
+  auto wbar = [&](int e) {
+    float s = 0.f;
+    for (int hh = 0; hh < G; ++hh) s += xrow[static_cast<int64_t>(hh) * a.nblk + e];
+    return s * invG;
+  };
+  int npos = 0;
+  for (int e = threadIdx.x; e < n; e += kThreads) npos += (!is_forced(ri, e) && wbar(e) > 0.f) ? 1 : 0;
+  npos = wave_sum_i(npos);
+  if (lane == 0) wave_tot[w] = npos;
+  __syncthreads();
+  int n_elig = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) n_elig += wave_tot[k];
+  __syncthreads();
+  auto get = [&](int e, uint32_t& key) -> bool {
+    if (e >= n || is_forced(ri, e)) return false;
+    const float v = wbar(e);
+    if (!(v > 0.f)) return false;
+    key = float_key(v);
+    return true;
+  };
+  const int c = select_and_write(ri, ri.span, a.cap, n_elig, get,
+                                 a.idx + static_cast<int64_t>(rowid) * a.width, a.width, hist,
+                                 bcast, wave_tot);
+  if (threadIdx.x == 0) a.cnt[rowid] = c;
+}
+
+}  // namespace
+
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
+  const int nchunk = (a.nblk + kChunk - 1) / kChunk;
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow * nchunk;
+  if (a.d == 64)
+    hipLaunchKernelGGL(scores_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(scores_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow;
+  hipLaunchKernelGGL(select_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream) {
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow;
+  if (a.d == 64)
+    hipLaunchKernelGGL(entmax_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(entmax_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,212 @@
+/*
+ * bsa.h -- C ABI of libbsa: block-sparse attention with summary-based block
+ * routing for AMD Instinct MI355X (gfx950).
+ *
+ * The method (three stages, each one call here):
+ *   Stage 0  bsa_summarize      keys of every block of B tokens are pooled into
+ *                               one summary vector ("DashAttention" page,
+ *                               section "Estágio 0: Resumo de Blocos Locais").
+ *   Stage 1  bsa_route_topk     every query block (prefill) or query token
+ *            bsa_route_entmax   (decode) scores the summaries and selects a set
+ *                               of blocks: top-k ("DashAttention", Declaração do
+ *                               Problema; "Gist Sparse Attention", section 2,
+ *                               item 3) or the support of alpha-entmax
+ *                               ("DashAttention", Estágio 1, equation
+ *                               w = alpha-entmax(gamma z)), whose threshold is
+ *                               found by bisection started from a 16-bin
+ *                               histogram ("AdaSplash-2", section 2.A).
+ *   Stage 2  bsa_attend_prefill exact softmax attention over the tokens of the
+ *            bsa_attend_decode  selected blocks only, causal prefill or one
+ *                               query token per sequence ("DashAttention",
+ *                               Contribuições item 4: prefill and incremental
+ *                               decode).
+ *
+ * Conventions shared by every call
+ *   - Tensors are device pointers owned by the caller.  The library never
+ *     allocates device memory; scratch space is the caller's `ws` buffer of at
+ *     least bsa_workspace_size(...) bytes (NULL allowed when that size is 0).
+ *   - Q, K, V, O are [batch, heads, tokens, head_dim] with head_dim contiguous
+ *     and explicit element strides for (batch, head, token).  Base pointers
+ *     must be 16-byte aligned and strides multiples of 8 elements (bf16) or 4
+ *     elements (fp32).
+ *   - Summaries S are fp32 [batch, n_kv_heads, n_blk, head_dim] contiguous,
+ *     n_blk = ceil(kv_len / block).
+ *   - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   - Selections are int32 [batch, n_kv_heads, n_rows, width], ascending block
+ *     ids padded with -1, plus a count [batch, n_kv_heads, n_rows].  n_rows is
+ *     ceil(q_len / block) in prefill and 1 in decode.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns BSA_OK or a negative bsa_status.  Arguments are
+ *     validated on the host before anything is enqueued: on an error nothing
+ *     runs and bsa_last_error() (thread-local) describes it.  A failed kernel
+ *     launch returns BSA_ERR_DEVICE.
+ *   - Device-side integer inputs (kv_lens, idx, cnt) are trusted for values
+ *     but never dereferenced out of bounds: lengths are clamped to
+ *     [1, kv_len], counts to [0, width], and block ids outside the valid range
+ *     are skipped.
+ *   - The library holds no state; calls on different streams may overlap as
+ *     long as their output buffers and workspaces do not.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype;
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID = -1,     /* malformed arguments */
+  BSA_ERR_UNSUPPORTED = -2, /* well-formed but outside the supported set */
+  BSA_ERR_DEVICE = -3,      /* a HIP launch failed */
+  BSA_ERR_WORKSPACE = -4    /* ws_bytes smaller than bsa_workspace_size() */
+} bsa_status;
+
+typedef enum { BSA_PREFILL = 0, BSA_DECODE = 1 } bsa_mode;
+
+/* Forced blocks: always in the selection, never counted as routed. */
+enum {
+  BSA_FORCE_DIAG = 1u,  /* prefill: the query block's own (diagonal) block;
+                           decode: the block holding the query (= TAIL) */
+  BSA_FORCE_FIRST = 2u, /* block 0 */
+  BSA_FORCE_TAIL = 4u   /* decode only: the last, possibly partial, block */
+};
+
+typedef enum {
+  BSA_OP_SUMMARIZE = 0,
+  BSA_OP_ROUTE_TOPK = 1,
+  BSA_OP_ROUTE_ENTMAX = 2,
+  BSA_OP_ATTEND_PREFILL = 3,
+  BSA_OP_ATTEND_DECODE = 4
+} bsa_op;
+
+/* Problem description, read only during the call. */
+typedef struct bsa_shape {
+  int32_t batch;      /* >= 1 */
+  int32_t n_q_heads;  /* Hq >= 1 */
+  int32_t n_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;   /* d: 64 or 128 */
+  int32_t block;      /* B: 64 or 128 */
+  int32_t dtype;      /* bsa_dtype of Q, K and V */
+  int32_t mode;       /* bsa_mode */
+  int32_t reserved;   /* must be 0 */
+  int64_t q_len;      /* prefill: N (== kv_len); decode: 1 */
+  int64_t kv_len;     /* prefill: N; decode: capacity of the K/V cache */
+  int64_t q_stride[3]; /* element strides of Q for (batch, head, token) */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} bsa_shape;
+
+/*
+ * Stage 0 -- block summaries ("DashAttention", Estágio 0).
+ *   K     [batch, Hkv, kv_len, d] in shape->dtype.
+ *   qbar  NULL: the zero-initialised learned query, i.e. the uniform mean of
+ *         the block's keys.  Otherwise fp32 [Hkv, d]: summary = sum_t w_t k_t
+ *         with w = softmax over the block of qbar . k_t / sqrt(d).
+ *   S     out, fp32 [batch, Hkv, n_blk, d].  A trailing partial block averages
+ *         the tokens present.  In decode only complete blocks are ever read by
+ *         the router, so S can be computed once and kept (a summary is fixed
+ *         once its block is complete).
+ * Errors: BSA_ERR_INVALID (null K or S, bad shape), BSA_ERR_UNSUPPORTED.
+ */
+int bsa_summarize(const bsa_shape *shape, const void *K, const float *qbar, float *S,
+                  void *stream);
+
+/*
+ * Stage 1, top-k ("DashAttention", Declaração do Problema; "Gist Sparse
+ * Attention", section 2, item 3).
+ *   Routing query of a row: prefill -- the mean of the query block's queries,
+ *   per head; decode -- the query itself.  The score of block j for KV head g
+ *   is score_scale * sum over the group's query heads of qhat_h . S_j
+ *   (score_scale 0 means 1/sqrt(d)).
+ *   Candidates: prefill row i -- blocks j <= i (causal); decode -- complete
+ *   blocks j < floor((L-1)/B), L = kv_lens[b] (NULL: every L = kv_len).
+ *   Forced blocks (force_flags, BSA_FORCE_*) are always selected; the other
+ *   k_total - #forced are the best candidates by (score desc, block asc).
+ *   idx   out int32 [batch, Hkv, n_rows, k_total] ascending, -1 padded.
+ *   cnt   out int32 [batch, Hkv, n_rows].
+ *   scores_out  NULL, or fp32 [batch, Hkv, n_rows, n_blk]: candidate scores,
+ *         -inf for non-candidates.
+ * Errors: BSA_ERR_INVALID (k_total < #forced or < 1, TAIL in prefill, null
+ * pointers, bad shape), BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
+ */
+int bsa_route_topk(const bsa_shape *shape, const void *Q, const float *S,
+                   const int32_t *kv_lens, int32_t k_total, uint32_t force_flags,
+                   float score_scale, int32_t *idx, int32_t *cnt, float *scores_out, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/*
+ * Stage 1, alpha-entmax ("DashAttention", Estágio 1; threshold per
+ * "AdaSplash-2", sections 1 and 2.A).  Per query head and row:
+ *   x_j = (alpha-1) * gamma * score_scale * qhat_h . S_j over the candidates
+ *   (prefill row i: j < i; decode: complete blocks before the tail; forced
+ *   blocks excluded), tau from a 16-bin histogram of x_max - x on [0, 1)
+ *   bracketing the root, then at most max_iter bisection steps, stopping once
+ *   no x lies inside the bracket; the exact tau of the resolved support is
+ *   used, else the bracket's lower end.  p_j = [x_j - tau]_+^(1/(alpha-1)),
+ *   renormalised.  The heads of a KV group average p; the blocks with a
+ *   positive average are kept, cut to the `cap` largest (ties: lower block)
+ *   when more; forced blocks are added.
+ *   idx   out int32 [batch, Hkv, n_rows, cap + #forced], cnt as above.
+ *   probs_out NULL or fp32 [batch, Hq, n_rows, n_blk] (0 outside candidates).
+ *   tau_out   NULL or fp32 [batch, Hq, n_rows] (NaN for rows without
+ *             candidates).
+ * Errors: BSA_ERR_INVALID (alpha <= 1, n_bins != 16, max_iter outside
+ * [0, 32], cap < 1, TAIL in prefill), BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
+ */
+int bsa_route_entmax(const bsa_shape *shape, const void *Q, const float *S,
+                     const int32_t *kv_lens, float alpha, float gamma, int32_t n_bins,
+                     int32_t max_iter, int32_t cap, uint32_t force_flags, float score_scale,
+                     int32_t *idx, int32_t *cnt, float *probs_out, float *tau_out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/*
+ * Stage 2, causal prefill ("DashAttention", Estágio 2 without routing bias).
+ * For query t of head h: softmax over the tokens t' <= t of the blocks in
+ * idx[b, g(h), t / B, 0:cnt] of (q_t . k_t') * sm_scale (0 means 1/sqrt(d)),
+ * times V.  An empty token set gives 0.
+ *   O     out [batch, Hq, q_len, d] with o_stride, dtype o_dtype: shape->dtype
+ *         or BSA_F32 (full-precision output for bf16 inputs).
+ *   k_max width of idx.
+ * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED.
+ */
+int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, const void *V,
+                       const int32_t *idx, const int32_t *cnt, int32_t k_max, float sm_scale,
+                       void *O, int32_t o_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Stage 2, decode: one query token per sequence at position L-1
+ * (L = kv_lens[b], NULL: kv_len), attending to the tokens t' < L of the blocks
+ * in idx[b, g(h), 0, 0:cnt].  The selected blocks are streamed in slices by
+ * several workgroups that write partial softmax states to `ws`, merged by a
+ * second kernel.
+ *   Q [batch, Hq, 1, d]; K, V [batch, Hkv, kv_len, d]; O [batch, Hq, 1, d].
+ * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
+ */
+int bsa_attend_decode(const bsa_shape *shape, const void *Q, const void *K, const void *V,
+                      const int32_t *kv_lens, const int32_t *idx, const int32_t *cnt,
+                      int32_t k_max, float sm_scale, void *O, int32_t o_dtype, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* Scratch bytes needed by `op` for this shape; k_or_cap is k_total (top-k),
+ * cap (entmax) or k_max (attend).  Returns 0 when none is needed or the
+ * arguments are invalid. */
+size_t bsa_workspace_size(int32_t op, const bsa_shape *shape, int32_t k_or_cap);
+
+/* Thread-local description of the last error ("" if none). */
+const char *bsa_last_error(void);
+
+/* Library version string. */
+const char *bsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

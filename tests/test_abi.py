@@ -1,0 +1,150 @@
+"""The C-ABI library loads, exports every entry point declared in
+include/bsa.h, and rejects malformed arguments on the host before any HIP
+call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+bsa = pytest.importorskip("block_sparse_attention_summarize_amd")
+lib = bsa.lib
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    return sorted(set(re.findall(r"\b(bsa_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(bsa.EXPORTS) == set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version():
+    assert "gfx950" in bsa.version()
+
+
+def shape(**kw):
+    base = dict(batch=1, hq=4, hkv=2, d=128, B=64, dtype=bsa.BF16, mode=bsa.PREFILL, q_len=256,
+                kv_len=256)
+    base.update(kw)
+    s = bsa.make_shape(**base)
+    st = (base["hq"] * base["kv_len"] * base["d"], base["kv_len"] * base["d"], base["d"])
+    for f in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        getattr(s, f)[:] = st
+    return s
+
+
+def err():
+    return lib.bsa_last_error().decode()
+
+
+def topk(s, k=4, force=0, ws_bytes=None, Q=FAKE, S=FAKE, idx=FAKE, cnt=FAKE, scale=0.0):
+    n = lib.bsa_workspace_size(bsa.OP_ROUTE_TOPK, ctypes.byref(s), k) if ws_bytes is None else ws_bytes
+    return lib.bsa_route_topk(ctypes.byref(s), Q, S, None, k, force, scale, idx, cnt, None,
+                              ctypes.c_void_p(0x200000), n, None)
+
+
+def entmax(s, alpha=1.5, n_bins=16, max_iter=8, cap=64, force=1):
+    n = lib.bsa_workspace_size(bsa.OP_ROUTE_ENTMAX, ctypes.byref(s), cap)
+    return lib.bsa_route_entmax(ctypes.byref(s), FAKE, FAKE, None, alpha, 1.0, n_bins, max_iter,
+                                cap, force, 0.0, FAKE, FAKE, None, None,
+                                ctypes.c_void_p(0x200000), n, None)
+
+
+def prefill(s, k_max=4, o_dtype=None, Q=FAKE, O=FAKE):
+    return lib.bsa_attend_prefill(ctypes.byref(s), Q, FAKE, FAKE, FAKE, FAKE, k_max, 0.0, O,
+                                  s.dtype if o_dtype is None else o_dtype, None, 0, None)
+
+
+def test_shape_validation():
+    assert lib.bsa_summarize(None, FAKE, None, FAKE, None) == -1
+    assert "NULL" in err()
+    assert topk(shape(hq=3, hkv=2)) == -1 and "multiple" in err()
+    assert topk(shape(batch=0)) == -1
+    assert topk(shape(d=96)) == -2 and "head_dim" in err()
+    assert topk(shape(B=32)) == -2 and "block" in err()
+    assert topk(shape(dtype=7)) == -2
+    assert topk(shape(mode=3)) == -1
+    assert topk(shape(q_len=128)) == -1 and "q_len == kv_len" in err()
+    assert topk(shape(mode=bsa.DECODE, q_len=2)) == -1 and "q_len == 1" in err()
+    s = shape()
+    s.reserved = 1
+    assert topk(s) == -1
+    s = shape()
+    s.q_stride[2] = 100  # not a multiple of 8 bf16 elements
+    assert topk(s) == -2 and "stride" in err()
+    s = shape()
+    s.q_stride[0] = -8
+    assert topk(s) == -1
+
+
+def test_pointer_validation():
+    assert topk(shape(), Q=None) == -1 and "Q is NULL" in err()
+    assert topk(shape(), Q=ctypes.c_void_p(0x100002)) == -2 and "aligned" in err()
+    assert topk(shape(), idx=None) == -1
+    assert prefill(shape(), O=None) == -1
+
+
+def test_route_topk_validation():
+    assert topk(shape(), k=0) == -1
+    assert topk(shape(), k=1, force=bsa.FORCE_DIAG | bsa.FORCE_FIRST) == -1 and "forced" in err()
+    assert topk(shape(), force=bsa.FORCE_TAIL) == -1 and "decode" in err()
+    assert topk(shape(), force=8) == -1
+    assert topk(shape(), scale=float("nan")) == -1
+    assert topk(shape(), ws_bytes=16) == -4 and "workspace" in err()
+
+
+def test_route_entmax_validation():
+    assert entmax(shape(), alpha=1.0) == -1 and "alpha" in err()
+    assert entmax(shape(), alpha=0.5) == -1
+    assert entmax(shape(), n_bins=8) == -1 and "n_bins" in err()
+    assert entmax(shape(), max_iter=-1) == -1
+    assert entmax(shape(), max_iter=33) == -1
+    assert entmax(shape(), cap=0) == -1
+
+
+def test_attend_validation():
+    assert prefill(shape(), k_max=0) == -1
+    assert prefill(shape(), o_dtype=5) == -2
+    assert prefill(shape(mode=bsa.DECODE, q_len=1)) == -1 and "PREFILL" in err()
+    s = shape(mode=bsa.DECODE, q_len=1, hq=32, hkv=2)
+    assert lib.bsa_attend_decode(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 0.0, FAKE,
+                                 bsa.BF16, FAKE, 1 << 20, None) == -2 and "8 query heads" in err()
+    s = shape(mode=bsa.DECODE, q_len=1)
+    assert lib.bsa_attend_decode(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 0.0, FAKE,
+                                 bsa.BF16, FAKE, 0, None) == -4
+
+
+def test_workspace_sizes():
+    s = shape(batch=2, hq=8, hkv=2, d=128, B=64, q_len=1000, kv_len=1000)
+    nrow = nblk = 16
+    rows = 2 * 2 * nrow
+    al = lambda x: (x + 255) // 256 * 256
+    assert lib.bsa_workspace_size(bsa.OP_ROUTE_TOPK, ctypes.byref(s), 4) == al(rows * 128 * 4) + al(rows * nblk * 4)
+    hrows = 2 * 8 * nrow
+    assert lib.bsa_workspace_size(bsa.OP_ROUTE_ENTMAX, ctypes.byref(s), 8) == al(hrows * 128 * 4) + al(hrows * nblk * 4)
+    assert lib.bsa_workspace_size(bsa.OP_ATTEND_PREFILL, ctypes.byref(s), 4) == 0
+    assert lib.bsa_workspace_size(bsa.OP_SUMMARIZE, ctypes.byref(s), 4) == 0
+    assert lib.bsa_workspace_size(bsa.OP_ROUTE_TOPK, None, 4) == 0
+    d = shape(batch=16, hq=32, hkv=8, mode=bsa.DECODE, q_len=1, kv_len=131072)
+    wsd = lib.bsa_workspace_size(bsa.OP_ATTEND_DECODE, ctypes.byref(d), 33)
+    # 128 (batch, KV head) rows, 33 blocks in slices of 3 -> 11 slices
+    assert wsd == al(16 * 32 * 11 * (128 + 2) * 4)
+
+
+def test_error_string_is_thread_local_and_cleared():
+    import threading
+    assert topk(shape(), k=0) == -1
+    msgs = []
+    t = threading.Thread(target=lambda: msgs.append(err()))
+    t.start()
+    t.join()
+    assert msgs == [""]
+    assert err() != ""
