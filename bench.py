@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of block-sparse attention with summary-based block routing on one
+MI355X.
+
+A step is one pass of the whole hot path over one batch of seeded synthetic
+input already resident in HBM: key summaries (Stage 0), top-k routing
+(Stage 1) and fine attention over the selected blocks (Stage 2).  The headline
+workload is causal bf16 GQA prefill, batch 1, 32 query / 8 KV heads,
+N = 32768, d = 128, B = 64, top-16 blocks per 64-query block.
+
+Printed: one JSON line.  `value` is prefill TFLOP/s counted on the selected
+blocks only (4 d flops per causal query-key pair actually attended) over the
+whole step.  `roofline` covers the dominant kernel (the MFMA attention) timed
+with HIP events on its stream inside the timed region; `cpu_baseline` is the
+fp64 oracle timed on this host on a bounded sample.  `extra.decode` reports
+the single-token decode workload (batch 16, 32/8 heads, L = 131072, top-32 +
+tail) as KV GB/s with the 256 MB last-level cache flushed between steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HEADLINE = "bf16_gqa_prefill_n32k"
+DECODE = "bf16_decode_l128k"
+COUNTERS = os.path.join(HERE, "profiles", "attend_prefill_bf16_gqa_n32k_counters.txt")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--no-decode", action="store_true", help="skip the decode extra")
+    p.add_argument("--cpu-sample-blocks", type=int, default=12)
+    return p.parse_args()
+
+
+def prefill_pairs(w, idx, cnt):
+    """Causal query-key pairs attended per the runtime selection, all heads."""
+    G = w.hq // w.hkv
+    nb = w.nblk
+    ntok = np.minimum(w.B, w.n - np.arange(nb) * w.B).astype(np.int64)
+    total = 0
+    for b in range(idx.shape[0]):
+        for g in range(idx.shape[1]):
+            for i in range(idx.shape[2]):
+                sel = idx[b, g, i, :cnt[b, g, i]]
+                sel = sel[(sel >= 0) & (sel <= i)]
+                below = sel[sel < i]
+                total += int(ntok[i] * ntok[below].sum())
+                if (sel == i).any():
+                    total += int(ntok[i] * (ntok[i] + 1) // 2)
+    return total * G
+
+
+def source_digest(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_src):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    fields = {}
+    for line in open(COUNTERS):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != source_digest(kernel_src):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, idx_h, cnt_h, total_flops, nsample):
+    """The fp64 oracle on this host: routing of every row, attention on a
+    seeded sample of query blocks, extrapolated by attended pairs."""
+    import oracle
+    t0 = time.perf_counter()
+    S = oracle.summarize(x["k"], w.B)
+    qh = oracle.qpool(x["q"], w.B)
+    oracle.route_topk(qh, S, w.B, w.k_total, w.force)
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(12345)
+    blocks = np.sort(rng.choice(w.nblk, size=min(nsample, w.nblk), replace=False))
+    req = np.array([[0, h, t] for i in blocks for h in range(w.hq)
+                    for t in range(i * w.B, min((i + 1) * w.B, w.n))], np.int64)
+    t0 = time.perf_counter()
+    _, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, idx_h, cnt_h, req=req)
+    t_att = time.perf_counter() - t0
+    total_pairs = total_flops / (4 * w.d)
+    t_total = t_route + t_att * total_pairs / max(int(pairs.sum()), 1)
+    return {"value": total_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"routing of all {w.batch * w.hkv * w.nblk} rows ({t_route:.1f} s) + attention "
+                      f"of {len(blocks)} seeded query blocks x {w.hq} heads ({t_att:.1f} s, "
+                      f"{int(pairs.sum())} pairs), extrapolated by pair count to the full step",
+            "seconds_per_step_extrapolated": t_total}
+
+
+def run_decode(bsa, torch, synth, parity, steps, warmup):
+    w = synth.WORKLOADS[DECODE]
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)  # cached summaries, computed once
+    lens = torch.tensor(w.lens(), dtype=torch.int32, device="cuda")
+    idx = torch.empty((w.batch, w.hkv, 1, w.k_total), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((w.batch, w.hkv, 1), dtype=torch.int32, device="cuda")
+    O = torch.empty_like(x["Q"])
+    shape_r = bsa._route_shape(x["Q"], S, w.B, True, w.n)
+    ws_r = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_TOPK, shape_r, w.k_total), dtype=torch.uint8,
+                       device="cuda")
+    shape_a = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B, dtype=bsa.BF16,
+                             mode=bsa.DECODE, q_len=1, kv_len=w.n, q=x["Q"], k=x["K"], v=x["V"])
+    ws_a = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_DECODE, shape_a, w.k_total),
+                       dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+
+    def step():
+        bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, decode=True, kv_len=w.n, kv_lens=lens,
+                       ws=ws_r, out=(idx, cnt))
+        bsa.attend_decode(x["Q"], x["K"], x["V"], w.B, idx, cnt, kv_lens=lens, ws=ws_a, out=O)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    times, t_route = [], []
+    for _ in range(max(steps, 5)):
+        flush.fill_(1.0)  # evict the last-level cache (untimed)
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, decode=True, kv_len=w.n, kv_lens=lens,
+                       ws=ws_r, out=(idx, cnt))
+        e1.record()
+        bsa.attend_decode(x["Q"], x["K"], x["V"], w.B, idx, cnt, kv_lens=lens, ws=ws_a, out=O)
+        e2.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e2) * 1e-3)
+        t_route.append(e0.elapsed_time(e1) * 1e-3)
+    c = cnt.cpu().numpy()
+    kv_bytes = int(c.sum()) * w.B * w.d * 2 * 2  # selected K and V blocks (all full here)
+    sum_bytes = w.batch * w.hkv * (w.nblk - 1) * w.d * 4  # fp32 summaries of the candidates
+    qo_bytes = 2 * w.batch * w.hq * w.d * 2
+    total = kv_bytes + sum_bytes + qo_bytes
+    t = float(np.median(times))
+    return {"workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "kv_len": w.n,
+            "head_dim": w.d, "block": w.B, "top_k": w.k_total - 1, "forced": "tail",
+            "us_per_step_median": t * 1e6, "us_per_step_min": float(np.min(times)) * 1e6,
+            "us_route_median": float(np.median(t_route)) * 1e6,
+            "bytes_per_step": total, "kv_bytes": kv_bytes, "summary_bytes": sum_bytes,
+            "GB_per_s": total / t / 1e9, "KV_GB_per_s": kv_bytes / t / 1e9,
+            "frac_hbm_peak": total / t / 1e9 / PEAK_HBM_GBS,
+            "cache_flush": "512 MiB write before every timed step"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the hot path runs on a single MI355X with no collectives)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_attention_summarize_amd as bsa
+    import synth
+    from tests import parity
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    w = synth.WORKLOADS[a.workload]
+    assert w.mode == "prefill" and w.router == "topk" and w.dtype == "bf16"
+    x = parity.make(w)
+    Q, K, V = x["Q"], x["K"], x["V"]
+    nrow = w.nblk
+    S = torch.empty((w.batch, w.hkv, w.nblk, w.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.batch, w.hkv, nrow, w.k_total), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((w.batch, w.hkv, nrow), dtype=torch.int32, device="cuda")
+    O = torch.empty_like(Q)
+    shape_r = bsa._route_shape(Q, S, w.B, False, None)
+    ws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_TOPK, shape_r, w.k_total), dtype=torch.uint8,
+                     device="cuda")
+    ev = []
+
+    def step(record=False):
+        bsa.summarize(K, w.B, out=S)
+        bsa.route_topk(Q, S, w.B, w.k_total, w.force, ws=ws, out=(idx, cnt))
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O)
+            e1.record()
+            ev.append((e0, e1))
+        else:
+            bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    flops = 4.0 * w.d * prefill_pairs(w, idx_h, cnt_h)
+    ms = elapsed / a.steps * 1e3
+    value = flops * a.steps / elapsed / 1e12
+    att_s = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+    achieved = flops / att_s / 1e12
+    kernel_src = os.path.join(HERE, "block_sparse_attention_summarize_amd", "csrc", "attend.hip")
+    out = {
+        "metric": "block-sparse attn prefill TFLOP/s (% MFMA peak); decode KV GB/s (% HBM)",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) with planted blocks)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "seq_len": w.n, "head_dim": w.d, "block": w.B, "top_k": w.k_total,
+                   "flops_per_step": flops, "sparsity_vs_causal":
+                       1.0 - flops / (4.0 * w.d * w.hq * w.n * (w.n + 1) / 2)},
+        "frac_mfma_peak_step": value / PEAK_BF16_TFLOPS,
+        "roofline": {"kernel": "attend_prefill_bf16", "bound": "mfma", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": read_traffic(kernel_src), "avg_launch_ms": att_s * 1e3},
+    }
+    if not a.no_decode:
+        out["extra"] = {"decode": run_decode(bsa, torch, synth, parity, a.steps, a.warmup)}
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, x, idx_h, cnt_h, flops, a.cpu_sample_blocks)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

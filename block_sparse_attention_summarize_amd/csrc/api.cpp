@@ -344,6 +344,16 @@ static int attend_common(const bsa_shape* s, const void* Q, const void* K, const
   if ((rc = check_strides("K", s->k_stride, s->dtype)) != BSA_OK) return rc;
   if ((rc = check_strides("V", s->v_stride, s->dtype)) != BSA_OK) return rc;
   if ((rc = check_strides("O", s->o_stride, o_dtype)) != BSA_OK) return rc;
+  // rows of one head are addressed with 32-bit offsets and must not overlap
+  const int64_t esz = elem_bytes(s->dtype);
+  const struct { const char* n; const int64_t* st; int64_t len; } heads[3] = {
+      {"Q", s->q_stride, s->q_len}, {"K", s->k_stride, s->kv_len}, {"V", s->v_stride, s->kv_len}};
+  for (const auto& hd : heads) {
+    if (hd.st[2] < s->head_dim)
+      return fail(BSA_ERR_INVALID, "%s token stride must be >= head_dim", hd.n);
+    if ((hd.len + 128) * hd.st[2] * esz >= (int64_t(1) << 31))
+      return fail(BSA_ERR_UNSUPPORTED, "%s: one head spans more than 2 GiB", hd.n);
+  }
   a.Q = Q;
   a.K = K;
   a.V = V;

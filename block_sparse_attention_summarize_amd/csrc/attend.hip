@@ -73,8 +73,8 @@ template <int D>
 struct PrefillLds {
   static constexpr int KST = D + 8;   // K tile row stride (bf16 elements)
   static constexpr int VST = 64 + 8;  // transposed V row stride
-  uint16_t k[2][64 * KST];
-  uint16_t v[2][D * VST];
+  alignas(16) uint16_t k[2][64 * KST];
+  alignas(16) uint16_t v[2][D * VST];
 };
 
 // Map workgroup id -> (pair = b*hkv + g, query block i, sub-unit).  Heavy
@@ -111,13 +111,37 @@ __device__ __forceinline__ void map_wg(int id, int npair, int nrow, int wpb, int
   i = nrow - 1 - ir;
 }
 
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int wpb) {
-  constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
-  constexpr int DT = D / 16;   // 16-row d tiles of O^T
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int KITEMS = 64 * CPR / 256;  // K tile chunks per thread
-  constexpr int VITEMS = 32 * CPR / 256;  // V tile key-pair chunks per thread
+// Raw buffer resource over [base, base + bytes): loads past the end return 0,
+// which zero-fills the ragged tail without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
+// Byte extent of one head's rows [0, len) with token stride st (elements).
+__device__ __forceinline__ uint32_t head_bytes(int64_t len, int64_t st, int d, int esz) {
+  return static_cast<uint32_t>(((len - 1) * st + d) * esz);
+}
+
+constexpr float kRescale = 8.f;  // lazy rescale threshold, log2 units
+
+// QT query tiles of 16 per wavefront, NW wavefronts per workgroup.  A "unit"
+// is one query head x 16*QT queries of the query block; the workgroup's
+// wavefronts take NW consecutive units of the same (batch, KV head, block),
+// so they share every K/V tile staged in LDS.
+template <int D, int QT, int NW, bool OUT_F32>
+__global__ __launch_bounds__(NW * 64, 1) void attend_prefill_bf16(AttendArgs a, int wpb) {
+  constexpr int NT = NW * 64;
+  constexpr int QPW = 16 * QT;  // queries per wave
+  constexpr int KS = D / 32;    // k-steps of S^T = K Q^T
+  constexpr int DT = D / 16;    // 16-row d tiles of O^T
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  constexpr int KTOT = 64 * CPR, VTOT = 32 * CPR;  // 16-byte K chunks, V key-pair chunks
+  constexpr int KITEMS = (KTOT + NT - 1) / NT;     // per thread
+  constexpr int VITEMS = (VTOT + NT - 1) / NT;
   __shared__ PrefillLds<D> lds;
   using L = PrefillLds<D>;
 
@@ -126,22 +150,21 @@ __global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int 
   const int w = tid >> 6;
   const int G = a.hq / a.hkv;
   const int nsub = a.B / 64;
-  const int units = G * nsub;
+  const int qsub = a.B / QPW;  // query sub-blocks per block
+  const int units = G * qsub;
   int pair, i, sub;
   map_wg(blockIdx.x, a.batch * a.hkv, a.nrow, wpb, pair, i, sub);
   const int b = pair / a.hkv, g = pair % a.hkv;
 
-  // this wave's unit: one query head and 64 queries of the block
-  const int u = sub * 4 + w;
+  const int u = sub * NW + w;
   const bool active = u < units;
   const int hh = active ? u % G : 0;
   const int qs = active ? u / G : 0;
   const int h = g * G + hh;
-  const int64_t qpos0 = static_cast<int64_t>(i) * a.B + qs * 64;
-  // last query position of the workgroup (over its active units)
+  const int qpos0 = i * a.B + qs * QPW;
   int qs_max = 0;
-  for (int uu = sub * 4; uu < sub * 4 + 4 && uu < units; ++uu) qs_max = max(qs_max, uu / G);
-  int64_t qmax = static_cast<int64_t>(i) * a.B + qs_max * 64 + 63;
+  for (int uu = sub * NW; uu < sub * NW + NW && uu < units; ++uu) qs_max = max(qs_max, uu / G);
+  int64_t qmax = static_cast<int64_t>(i) * a.B + qs_max * QPW + QPW - 1;
   if (qmax > a.q_len - 1) qmax = a.q_len - 1;
 
   const int64_t rowid = static_cast<int64_t>(pair) * a.nrow + i;
@@ -149,73 +172,72 @@ __global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int 
   n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
   TileWalk walk{a.idx + rowid * a.k_max, n, nsub, a.B, a.nblk, a.kv_len, qmax};
 
-  const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h;
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h;
+  const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
+                            head_bytes(a.kv_len, a.ks.t, D, 2));
+  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
+                            head_bytes(a.kv_len, a.vs.t, D, 2));
+  const uint32_t kst = static_cast<uint32_t>(a.ks.t * 2), vst = static_cast<uint32_t>(a.vs.t * 2);
 
   // Q fragments (B operand of S^T = K Q^T): lane l holds query 16qt + l%16,
-  // d = 32ks + 8(l/16) .. +7.
-  uint4 qf[4][KS];
+  // d = 32ks + 8(l/16) .. +7.  Rows past q_len read as zero.
+  uint4 qf[QT][KS];
   {
-    const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h;
+    const auto rq = make_rsrc(static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h,
+                              active ? head_bytes(a.q_len, a.qs.t, D, 2) : 0u);
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      const int64_t t = qpos0 + qt * 16 + (lane & 15);
+    for (int qt = 0; qt < QT; ++qt) {
+      const uint32_t t = static_cast<uint32_t>(qpos0 + qt * 16 + (lane & 15));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (active && t < a.q_len)
-          qf[qt][ks] = *reinterpret_cast<const uint4*>(Qg + t * a.qs.t + ks * 32 + (lane >> 4) * 8);
-        else
-          qf[qt][ks] = make_uint4(0, 0, 0, 0);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        qf[qt][ks] = buf_load16(rq, t * static_cast<uint32_t>(a.qs.t * 2) + (ks * 32 + (lane >> 4) * 8) * 2);
     }
   }
 
-  f32x4 o[DT][4];
+  f32x4 o[DT][QT];
+  f32x4 lsum[QT];
+  float m[QT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4], l[4];
-#pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
+    lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m[qt] = -INFINITY;
-    l[qt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sc = a.sm_scale * kLog2e;
+  const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
 
   uint4 kreg[KITEMS];
   uint4 vreg[VITEMS][2];
-  auto load_tile = [&](int64_t k0) {
+  auto load_tile = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < KITEMS; ++it) {
-      const int flat = tid + 256 * it;
+      const int flat = tid + NT * it;
       const int r = flat / CPR, c = flat % CPR;
-      const int64_t t = k0 + r;
-      kreg[it] = t < a.kv_len ? *reinterpret_cast<const uint4*>(Kg + t * a.ks.t + c * 8)
-                              : make_uint4(0, 0, 0, 0);
+      if (KTOT % NT == 0 || flat < KTOT)
+        kreg[it] = buf_load16(rk, static_cast<uint32_t>(k0 + r) * kst + c * 16);
     }
 #pragma unroll
     for (int it = 0; it < VITEMS; ++it) {
-      const int flat = tid + 256 * it;
+      const int flat = tid + NT * it;
+      if (VTOT % NT != 0 && flat >= VTOT) continue;
       const int kp = flat % 32, c = flat / 32;
-      const int64_t t = k0 + 2 * kp;
-      vreg[it][0] = t < a.kv_len ? *reinterpret_cast<const uint4*>(Vg + t * a.vs.t + c * 8)
-                                 : make_uint4(0, 0, 0, 0);
-      vreg[it][1] = t + 1 < a.kv_len
-                        ? *reinterpret_cast<const uint4*>(Vg + (t + 1) * a.vs.t + c * 8)
-                        : make_uint4(0, 0, 0, 0);
+      const uint32_t t = static_cast<uint32_t>(k0 + 2 * kp);
+      vreg[it][0] = buf_load16(rv, t * vst + c * 16);
+      vreg[it][1] = buf_load16(rv, (t + 1) * vst + c * 16);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < KITEMS; ++it) {
-      const int flat = tid + 256 * it;
+      const int flat = tid + NT * it;
       const int r = flat / CPR, c = flat % CPR;
-      *reinterpret_cast<uint4*>(&lds.k[buf][r * L::KST + c * 8]) = kreg[it];
+      if (KTOT % NT == 0 || flat < KTOT)
+        *reinterpret_cast<uint4*>(&lds.k[buf][r * L::KST + c * 8]) = kreg[it];
     }
 #pragma unroll
     for (int it = 0; it < VITEMS; ++it) {
-      const int flat = tid + 256 * it;
+      const int flat = tid + NT * it;
+      if (VTOT % NT != 0 && flat >= VTOT) continue;
       const int kp = flat % 32, c = flat / 32;
       const int pos = vt_pos(2 * kp);
       const uint32_t a0[4] = {vreg[it][0].x, vreg[it][0].y, vreg[it][0].z, vreg[it][0].w};
@@ -223,8 +245,8 @@ __global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // d = 8c + 2e (low halves) and 8c + 2e + 1 (high halves)
-        const uint32_t lo = (a0[e] & 0xffffu) | (a1[e] << 16);
-        const uint32_t hi = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+        const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
         *reinterpret_cast<uint32_t*>(&lds.v[buf][(c * 8 + 2 * e) * L::VST + pos]) = lo;
         *reinterpret_cast<uint32_t*>(&lds.v[buf][(c * 8 + 2 * e + 1) * L::VST + pos]) = hi;
       }
@@ -234,22 +256,22 @@ __global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int 
   int T = walk.next(-1);
   int buf = 0;
   if (T >= 0) {
-    load_tile(walk.key0(T));
+    load_tile(static_cast<int>(walk.key0(T)));
     store_tile(0);
   }
   __syncthreads();
   while (T >= 0) {
-    const int64_t k0 = walk.key0(T);
+    const int k0 = static_cast<int>(walk.key0(T));
     const int Tn = walk.next(T);
-    if (Tn >= 0) load_tile(walk.key0(Tn));
+    if (Tn >= 0) load_tile(static_cast<int>(walk.key0(Tn)));
 
     if (active) {
-      // S^T tile: keys 16kt + 4(l/16) + j, query column 16qt + l%16
-      f32x4 s[4][4];
+      // S^T tiles: lane l holds keys 16kt + 4(l/16) + j of query column 16qt + l%16
+      f32x4 s[4][QT];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qt = 0; qt < QT; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -257,45 +279,55 @@ __global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int 
           const uint4 kf = *reinterpret_cast<const uint4*>(
               &lds.k[buf][(kt * 16 + (lane & 15)) * L::KST + ks * 32 + (lane >> 4) * 8]);
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
+          for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
         }
       }
-      const bool need_mask = (k0 + 63 > qpos0) || (k0 + 64 > a.kv_len);
-      uint4 pf[4][2];
+      // causal mask, only on tiles that reach past the wave's first query
+      if (k0 + 63 > qpos0) {
+        const int rel0 = k0 - qpos0 + (lane >> 4) * 4 - (lane & 15);
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        const int64_t q = qpos0 + qt * 16 + (lane & 15);
-        float mx = -INFINITY;
+        for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float v = s[kt][qt][j] * sc;
-            if (need_mask) {
-              const int64_t key = k0 + kt * 16 + (lane >> 4) * 4 + j;
-              if (key > q || key >= a.kv_len) v = -INFINITY;
-            }
-            s[kt][qt][j] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mnew = fmaxf(m[qt], mx);
-        const float base = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(m[qt] - base);
-        m[qt] = mnew;
-        float rs = 0.f;
+            for (int j = 0; j < 4; ++j)
+              if (rel0 + kt * 16 + j - qt * 16 > 0) s[kt][qt][j] = -INFINITY;
+      }
+      // running max per query; rescale the accumulators only when it grows by
+      // more than 2^kRescale (p stays <= 2^kRescale, exact after normalising)
+      float mx[QT];
+      bool grow = false;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float v = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
+#pragma unroll
+        for (int kt = 1; kt < 4; ++kt)
+          v = fmaxf(v, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
+        v = fmaxf(v, __shfl_xor(v, 16, 64));
+        v = fmaxf(v, __shfl_xor(v, 32, 64));
+        mx[qt] = v * sc;
+        grow |= mx[qt] > m[qt] + kRescale;
+      }
+      if (__ballot(grow) != 0) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float mn = fmaxf(m[qt], mx[qt]);
+          const float f = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qt] - mn);
+          m[qt] = mn;
+          lsum[qt] *= f;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= f;
+        }
+      }
+      uint4 pf[QT][2];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float nb = m[qt] == -INFINITY ? 0.f : -m[qt];
         float p[4][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            p[kt][j] = exp2f(s[kt][qt][j] - base);
-            rs += p[kt][j];
-          }
-        l[qt] = l[qt] * alpha + rs;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= alpha;
+          for (int j = 0; j < 4; ++j) p[kt][j] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], sc, nb));
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           pf[qt][kk].x = pack_bf16x2(p[2 * kk][0], p[2 * kk][1]);
@@ -307,11 +339,13 @@ __global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int 
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
+        for (int qt = 0; qt < QT; ++qt) lsum[qt] = mfma16(ones, pf[qt][kk], lsum[qt]);
+#pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const uint4 vf = *reinterpret_cast<const uint4*>(
               &lds.v[buf][(dt * 16 + (lane & 15)) * L::VST + kk * 32 + (lane >> 4) * 8]);
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt) o[dt][qt] = mfma16(vf, pf[qt][kk], o[dt][qt]);
+          for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf, pf[qt][kk], o[dt][qt]);
         }
       }
     }
@@ -324,10 +358,9 @@ __global__ __launch_bounds__(256, 1) void attend_prefill_bf16(AttendArgs a, int 
   if (!active) return;
   uint8_t* Ob = static_cast<uint8_t*>(a.O);
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    float lt = l[qt];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+  for (int qt = 0; qt < QT; ++qt) {
+    // every row of the ones-product holds the column sum of the bf16 weights
+    const float lt = lsum[qt][0];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int64_t t = qpos0 + qt * 16 + (lane & 15);
     if (t >= a.q_len) continue;
@@ -600,17 +633,24 @@ __global__ __launch_bounds__(D) void decode_combine(AttendArgs a) {
     static_cast<uint16_t*>(a.O)[off + c] = f32_to_bf16(v);
 }
 
-template <int D>
-hipError_t prefill_bf16_dispatch(const AttendArgs& a, hipStream_t stream) {
+template <int D, int QT, int NW>
+hipError_t prefill_bf16_launch(const AttendArgs& a, hipStream_t stream) {
   const int G = a.hq / a.hkv;
-  const int units = G * (a.B / 64);
-  const int wpb = (units + 3) / 4;
+  const int units = G * (a.B / (16 * QT));
+  const int wpb = (units + NW - 1) / NW;
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow * wpb;
   if (a.out_f32)
-    hipLaunchKernelGGL((attend_prefill_bf16<D, true>), dim3(grid), dim3(256), 0, stream, a, wpb);
+    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, true>), dim3(grid), dim3(NW * 64), 0, stream,
+                       a, wpb);
   else
-    hipLaunchKernelGGL((attend_prefill_bf16<D, false>), dim3(grid), dim3(256), 0, stream, a, wpb);
+    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, false>), dim3(grid), dim3(NW * 64), 0, stream,
+                       a, wpb);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t prefill_bf16_dispatch(const AttendArgs& a, hipStream_t stream) {
+  return prefill_bf16_launch<D, 2, 8>(a, stream);
 }
 
 template <typename T, int D>
