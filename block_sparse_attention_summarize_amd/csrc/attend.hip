@@ -127,6 +127,7 @@ __device__ __forceinline__ uint32_t head_bytes(int64_t len, int64_t st, int d, i
 }
 
 constexpr float kRescale = 8.f;  // lazy rescale threshold, log2 units
+constexpr int kMaxTiles = 1024;  // tile-list chunk staged in LDS
 
 // QT query tiles of 16 per wavefront, NW wavefronts per workgroup.  A "unit"
 // is one query head x 16*QT queries of the query block; the workgroup's
@@ -143,6 +144,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attend_prefill_bf16(AttendArgs a, 
   constexpr int KITEMS = (KTOT + NT - 1) / NT;     // per thread
   constexpr int VITEMS = (VTOT + NT - 1) / NT;
   __shared__ PrefillLds<D> lds;
+  __shared__ int lds_tiles[kMaxTiles];
+  __shared__ int lds_ntiles;
   using L = PrefillLds<D>;
 
   const int tid = threadIdx.x;
@@ -253,106 +256,127 @@ __global__ __launch_bounds__(NW * 64, 1) void attend_prefill_bf16(AttendArgs a, 
     }
   };
 
-  int T = walk.next(-1);
-  int buf = 0;
-  if (T >= 0) {
-    load_tile(static_cast<int>(walk.key0(T)));
-    store_tile(0);
-  }
-  __syncthreads();
-  while (T >= 0) {
-    const int k0 = static_cast<int>(walk.key0(T));
-    const int Tn = walk.next(T);
-    if (Tn >= 0) load_tile(static_cast<int>(walk.key0(Tn)));
+  // The workgroup's tiles (valid, not entirely in its future) are compacted
+  // into LDS by wave 0, kMaxTiles raw entries at a time, so the main loop
+  // reads its next key offset from LDS instead of a dependent global load.
+  const int nraw = n * nsub;
+  for (int base = 0; base < nraw; base += kMaxTiles) {
+    if (w == 0) {
+      int c = 0;
+      for (int r = 0; r < kMaxTiles && base + r < nraw; r += 64) {
+        const int T = base + r + lane;
+        const int64_t k0 = T < nraw ? walk.key0(T) : -1;
+        const uint64_t mk = __ballot(k0 >= 0);
+        if (k0 >= 0) lds_tiles[c + lanes_below(mk)] = static_cast<int>(k0);
+        c += __popcll(mk);
+      }
+      if (lane == 0) lds_ntiles = c;
+    }
+    __syncthreads();
+    const int ntiles = lds_ntiles;
+    int buf = 0;
+    if (ntiles > 0) {
+      load_tile(lds_tiles[0]);
+      store_tile(0);
+    }
+    // Drain every outstanding vector load (the Q fragments) here, so that the
+    // loop's only pending loads are the next tile's prefetch and the MFMAs on
+    // the current tile never wait for it.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int k0 = lds_tiles[t];
+      const bool more = t + 1 < ntiles;
+      if (more) load_tile(lds_tiles[t + 1]);
 
-    if (active) {
-      // S^T tiles: lane l holds keys 16kt + 4(l/16) + j of query column 16qt + l%16
-      f32x4 s[4][QT];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const uint4 kf = *reinterpret_cast<const uint4*>(
-              &lds.k[buf][(kt * 16 + (lane & 15)) * L::KST + ks * 32 + (lane >> 4) * 8]);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
-        }
-      }
-      // causal mask, only on tiles that reach past the wave's first query
-      if (k0 + 63 > qpos0) {
-        const int rel0 = k0 - qpos0 + (lane >> 4) * 4 - (lane & 15);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (rel0 + kt * 16 + j - qt * 16 > 0) s[kt][qt][j] = -INFINITY;
-      }
-      // running max per query; rescale the accumulators only when it grows by
-      // more than 2^kRescale (p stays <= 2^kRescale, exact after normalising)
-      float mx[QT];
-      bool grow = false;
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        float v = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
-#pragma unroll
-        for (int kt = 1; kt < 4; ++kt)
-          v = fmaxf(v, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
-        v = fmaxf(v, __shfl_xor(v, 16, 64));
-        v = fmaxf(v, __shfl_xor(v, 32, 64));
-        mx[qt] = v * sc;
-        grow |= mx[qt] > m[qt] + kRescale;
-      }
-      if (__ballot(grow) != 0) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const float mn = fmaxf(m[qt], mx[qt]);
-          const float f = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qt] - mn);
-          m[qt] = mn;
-          lsum[qt] *= f;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= f;
-        }
-      }
-      uint4 pf[QT][2];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const float nb = m[qt] == -INFINITY ? 0.f : -m[qt];
-        float p[4][4];
+      if (active) {
+        // S^T tiles: lane l holds keys 16kt + 4(l/16) + j of query column 16qt + l%16
+        f32x4 s[4][QT];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[kt][j] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], sc, nb));
+          for (int qt = 0; qt < QT; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            const uint4 kf = *reinterpret_cast<const uint4*>(
+                &lds.k[buf][(kt * 16 + (lane & 15)) * L::KST + ks * 32 + (lane >> 4) * 8]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
+          }
+        }
+        // causal mask, only on tiles that reach past the wave's first query
+        if (k0 + 63 > qpos0) {
+          const int rel0 = k0 - qpos0 + (lane >> 4) * 4 - (lane & 15);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (rel0 + kt * 16 + j - qt * 16 > 0) s[kt][qt][j] = -INFINITY;
+        }
+        // running max per query; rescale the accumulators only when it grows by
+        // more than 2^kRescale (p stays <= 2^kRescale, exact after normalising)
+        float mx[QT];
+        bool grow = false;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          float v = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
+#pragma unroll
+          for (int kt = 1; kt < 4; ++kt)
+            v = fmaxf(v, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
+          v = fmaxf(v, __shfl_xor(v, 16, 64));
+          v = fmaxf(v, __shfl_xor(v, 32, 64));
+          mx[qt] = v * sc;
+          grow |= mx[qt] > m[qt] + kRescale;
+        }
+        if (__ballot(grow) != 0) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            const float mn = fmaxf(m[qt], mx[qt]);
+            const float f = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qt] - mn);
+            m[qt] = mn;
+            lsum[qt] *= f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= f;
+          }
+        }
+        uint4 pf[QT][2];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float nb = m[qt] == -INFINITY ? 0.f : -m[qt];
+          float p[4][4];
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[kt][j] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], sc, nb));
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            pf[qt][kk].x = pack_bf16x2(p[2 * kk][0], p[2 * kk][1]);
+            pf[qt][kk].y = pack_bf16x2(p[2 * kk][2], p[2 * kk][3]);
+            pf[qt][kk].z = pack_bf16x2(p[2 * kk + 1][0], p[2 * kk + 1][1]);
+            pf[qt][kk].w = pack_bf16x2(p[2 * kk + 1][2], p[2 * kk + 1][3]);
+          }
+        }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          pf[qt][kk].x = pack_bf16x2(p[2 * kk][0], p[2 * kk][1]);
-          pf[qt][kk].y = pack_bf16x2(p[2 * kk][2], p[2 * kk][3]);
-          pf[qt][kk].z = pack_bf16x2(p[2 * kk + 1][0], p[2 * kk + 1][1]);
-          pf[qt][kk].w = pack_bf16x2(p[2 * kk + 1][2], p[2 * kk + 1][3]);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) lsum[qt] = mfma16(ones, pf[qt][kk], lsum[qt]);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint4 vf = *reinterpret_cast<const uint4*>(
+                &lds.v[buf][(dt * 16 + (lane & 15)) * L::VST + kk * 32 + (lane >> 4) * 8]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf, pf[qt][kk], o[dt][qt]);
+          }
         }
       }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) lsum[qt] = mfma16(ones, pf[qt][kk], lsum[qt]);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint4 vf = *reinterpret_cast<const uint4*>(
-              &lds.v[buf][(dt * 16 + (lane & 15)) * L::VST + kk * 32 + (lane >> 4) * 8]);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf, pf[qt][kk], o[dt][qt]);
-        }
-      }
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
-    if (Tn >= 0) store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    T = Tn;
   }
 
   if (!active) return;
