@@ -44,7 +44,21 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-decode", action="store_true", help="skip the decode extra")
     p.add_argument("--cpu-sample-blocks", type=int, default=12)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (counter calibration)")
     return p.parse_args()
+
+
+def copy_calibration(mib, reps=3):
+    """A plain device-to-device copy of known size: the reference reading for
+    the FETCH_SIZE / WRITE_SIZE counters (each launch reads and writes MIB MiB)."""
+    import torch
+    x = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": mib * 1024 * 1024, "launches": reps}))
 
 
 def prefill_pairs(w, idx, cnt):
@@ -120,36 +134,25 @@ def run_decode(bsa, torch, synth, parity, steps, warmup):
     idx = torch.empty((w.batch, w.hkv, 1, w.k_total), dtype=torch.int32, device="cuda")
     cnt = torch.empty((w.batch, w.hkv, 1), dtype=torch.int32, device="cuda")
     O = torch.empty_like(x["Q"])
-    shape_r = bsa._route_shape(x["Q"], S, w.B, True, w.n)
-    ws_r = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_TOPK, shape_r, w.k_total), dtype=torch.uint8,
-                       device="cuda")
-    shape_a = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B, dtype=bsa.BF16,
-                             mode=bsa.DECODE, q_len=1, kv_len=w.n, q=x["Q"], k=x["K"], v=x["V"])
-    ws_a = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_DECODE, shape_a, w.k_total),
-                       dtype=torch.uint8, device="cuda")
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
 
     def step():
-        bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, decode=True, kv_len=w.n, kv_lens=lens,
-                       ws=ws_r, out=(idx, cnt))
-        bsa.attend_decode(x["Q"], x["K"], x["V"], w.B, idx, cnt, kv_lens=lens, ws=ws_a, out=O)
+        # routing over the cached summaries + attention, one launch
+        bsa.decode_step(x["Q"], x["K"], x["V"], S, w.B, w.k_total, w.force, kv_lens=lens, out=O,
+                        sel=(idx, cnt))
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    times, t_route = [], []
+    times = []
     for _ in range(max(steps, 5)):
-        flush.fill_(1.0)  # evict the last-level cache (untimed)
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        flush.sum()  # evict the last-level cache by reading 512 MiB (untimed, no dirty lines)
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
         e0.record()
-        bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, decode=True, kv_len=w.n, kv_lens=lens,
-                       ws=ws_r, out=(idx, cnt))
+        step()
         e1.record()
-        bsa.attend_decode(x["Q"], x["K"], x["V"], w.B, idx, cnt, kv_lens=lens, ws=ws_a, out=O)
-        e2.record()
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e2) * 1e-3)
-        t_route.append(e0.elapsed_time(e1) * 1e-3)
+        times.append(e0.elapsed_time(e1) * 1e-3)
     c = cnt.cpu().numpy()
     kv_bytes = int(c.sum()) * w.B * w.d * 2 * 2  # selected K and V blocks (all full here)
     sum_bytes = w.batch * w.hkv * (w.nblk - 1) * w.d * 4  # fp32 summaries of the candidates
@@ -159,15 +162,17 @@ def run_decode(bsa, torch, synth, parity, steps, warmup):
     return {"workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "kv_len": w.n,
             "head_dim": w.d, "block": w.B, "top_k": w.k_total - 1, "forced": "tail",
             "us_per_step_median": t * 1e6, "us_per_step_min": float(np.min(times)) * 1e6,
-            "us_route_median": float(np.median(t_route)) * 1e6,
             "bytes_per_step": total, "kv_bytes": kv_bytes, "summary_bytes": sum_bytes,
             "GB_per_s": total / t / 1e9, "KV_GB_per_s": kv_bytes / t / 1e9,
             "frac_hbm_peak": total / t / 1e9 / PEAK_HBM_GBS,
-            "cache_flush": "512 MiB write before every timed step"}
+            "cache_flush": "512 MiB read before every timed step"}
 
 
 def main():
     a = parse()
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the hot path runs on a single MI355X with no collectives)", file=sys.stderr)

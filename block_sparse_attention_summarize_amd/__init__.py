@@ -38,7 +38,8 @@ STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BS
           -4: "BSA_ERR_WORKSPACE"}
 
 EXPORTS = ("bsa_summarize", "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill",
-           "bsa_attend_decode", "bsa_workspace_size", "bsa_last_error", "bsa_version")
+           "bsa_attend_decode", "bsa_decode_topk", "bsa_workspace_size", "bsa_last_error",
+           "bsa_version")
 
 
 class Shape(ctypes.Structure):
@@ -64,8 +65,10 @@ lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, 
                                  _P, _P, _P, _P, _sz, _P]
 lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
+lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
+                                _P]
 for _f in (lib.bsa_summarize, lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill,
-           lib.bsa_attend_decode):
+           lib.bsa_attend_decode, lib.bsa_decode_topk):
     _f.restype = ctypes.c_int
 lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
 lib.bsa_workspace_size.restype = _sz
@@ -216,8 +219,7 @@ def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None)
     return O
 
 
-def attend_decode(q, K, V, B, idx, cnt, kv_lens=None, sm_scale=0.0, out_dtype=None, ws=None,
-                  out=None):
+def attend_decode(q, K, V, B, idx, cnt, kv_lens=None, sm_scale=0.0, out_dtype=None, out=None):
     """One query token per sequence.  q [b, Hq, 1, d], K/V caches [b, Hkv, L, d]."""
     b, hq, _, d = q.shape
     hkv, L = K.shape[1], K.shape[2]
@@ -225,12 +227,33 @@ def attend_decode(q, K, V, B, idx, cnt, kv_lens=None, sm_scale=0.0, out_dtype=No
     O = out if out is not None else torch.empty((b, hq, 1, d), dtype=odt, device=q.device)
     shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(q), mode=DECODE,
                        q_len=1, kv_len=L, q=q, k=K, v=V, o=O)
-    k_max = idx.shape[-1]
-    wsb, n = _workspace(OP_ATTEND_DECODE, shape, k_max, q.device, ws)
     _check(lib.bsa_attend_decode(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(kv_lens),
-                                 _ptr(idx), _ptr(cnt), k_max, sm_scale, _ptr(O), _dtype_code(O),
-                                 _ptr(wsb), n, _stream(q)))
+                                 _ptr(idx), _ptr(cnt), idx.shape[-1], sm_scale, _ptr(O),
+                                 _dtype_code(O), None, 0, _stream(q)))
     return O
+
+
+def decode_step(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, score_scale=0.0,
+                sm_scale=0.0, out_dtype=None, out=None, want_selection=True, sel=None):
+    """Top-k routing over cached summaries and decode attention in one launch.
+    Returns (O, idx, cnt) (idx, cnt are None when want_selection is False)."""
+    b, hq, _, d = q.shape
+    hkv, L = K.shape[1], K.shape[2]
+    odt = out_dtype or q.dtype
+    O = out if out is not None else torch.empty((b, hq, 1, d), dtype=odt, device=q.device)
+    if sel is not None:
+        idx, cnt = sel
+    elif want_selection:
+        idx = torch.empty((b, hkv, 1, k_total), dtype=torch.int32, device=q.device)
+        cnt = torch.empty((b, hkv, 1), dtype=torch.int32, device=q.device)
+    else:
+        idx = cnt = None
+    shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(q), mode=DECODE,
+                       q_len=1, kv_len=L, q=q, k=K, v=V, o=O)
+    _check(lib.bsa_decode_topk(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(S),
+                               _ptr(kv_lens), k_total, force, score_scale, sm_scale, _ptr(idx),
+                               _ptr(cnt), _ptr(O), _dtype_code(O), _stream(q)))
+    return O, idx, cnt
 
 
 def prefill_topk(Q, K, V, B, k_total, force=0, S=None, out_dtype=None):
@@ -249,6 +272,6 @@ def prefill_entmax(Q, K, V, B, alpha, gamma, cap, force=FORCE_DIAG, max_iter=8, 
 
 
 def decode_topk(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, out_dtype=None):
-    """Top-k routing over cached summaries + decode attention."""
+    """Top-k routing over cached summaries + decode attention (two calls)."""
     idx, cnt = route_topk(q, S, B, k_total, force, decode=True, kv_len=K.shape[2], kv_lens=kv_lens)
     return attend_decode(q, K, V, B, idx, cnt, kv_lens=kv_lens, out_dtype=out_dtype), idx, cnt

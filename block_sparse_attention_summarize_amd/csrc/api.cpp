@@ -115,19 +115,29 @@ int check_force(const bsa_shape* s, uint32_t force) {
   return BSA_OK;
 }
 
-// Decode split: enough workgroups to fill the chip, LDS for the slice's scores.
-void decode_split(const bsa_shape* s, int32_t k_max, int* bps, int* splits) {
-  const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads;
+// Workgroups per decode row: the GQA group is split over hsplit workgroups
+// (at most 8 query heads each) until the grid covers the 256 CUs.
+int decode_hsplit(const bsa_shape* s) {
   const int G = s->n_q_heads / s->n_kv_heads;
-  int64_t b = (static_cast<int64_t>(k_max) * rows + 2047) / 2048;
-  if (b < 1) b = 1;
-  const int64_t cap = 8192 / (static_cast<int64_t>(G) * s->block);
-  if (b > cap) b = cap < 1 ? 1 : cap;
-  if (b > k_max) b = k_max;
-  *bps = static_cast<int>(b);
-  *splits = static_cast<int>((k_max + b - 1) / b);
+  const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads;
+  int h = 1;
+  while (G / h > 8 || (G % (2 * h) == 0 && rows * h < 256)) h *= 2;
+  return G % h == 0 ? h : -1;
+}
+int gs_template(int gs) { return gs <= 1 ? 1 : gs <= 2 ? 2 : gs <= 4 ? 4 : 8; }
+
+// LDS floats of the fused decode kernel; -1 when the row does not fit.
+int decode_lds(const bsa_shape* s, int hsplit, int32_t width) {
+  const int gs = gs_template((s->n_q_heads / s->n_kv_heads) / hsplit);
+  const int64_t nblk = nblk_of(s);
+  const int64_t f = bsa::decode_lds_floats(static_cast<int>(nblk), s->head_dim, gs);
+  if (nblk > (int64_t(1) << 24) || (f + width) * 4 > 96 * 1024) return -1;
+  return static_cast<int>(f);
 }
 
+// Decode routing normally runs the fused kernel with no scratch; the
+// size returned also covers the three-kernel path used when scores_out is
+// requested.
 size_t ws_route_topk(const bsa_shape* s) {
   const size_t rows = static_cast<size_t>(s->batch) * s->n_kv_heads * nrow_of(s);
   return align_up(rows * s->head_dim * 4) + align_up(rows * nblk_of(s) * 4);
@@ -136,12 +146,6 @@ size_t ws_route_entmax(const bsa_shape* s) {
   const size_t hrows = static_cast<size_t>(s->batch) * s->n_q_heads * nrow_of(s);
   return align_up(hrows * s->head_dim * 4) + align_up(hrows * nblk_of(s) * 4);
 }
-size_t ws_attend_decode(const bsa_shape* s, int32_t k_max) {
-  int bps, splits;
-  decode_split(s, k_max, &bps, &splits);
-  return align_up(static_cast<size_t>(s->batch) * s->n_q_heads * splits * (s->head_dim + 2) * 4);
-}
-
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (ws_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
@@ -149,6 +153,72 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need > 0 && !ws) return fail(BSA_ERR_INVALID, "ws is NULL");
   if (need > 0 && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
     return fail(BSA_ERR_UNSUPPORTED, "ws must be %zu-byte aligned", kAlign);
+  return BSA_OK;
+}
+
+// Fills the fused decode kernel's arguments shared by the three decode calls.
+int decode_args(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                       const float* S, const int32_t* kv_lens, int32_t* idx, int32_t* cnt,
+                       int32_t width, uint32_t force, float score_scale, float sm_scale, void* O,
+                       int32_t o_dtype, int route, int attend, bsa::DecodeArgs& a) {
+  int rc;
+  if (s->mode != BSA_DECODE) return fail(BSA_ERR_INVALID, "decode calls need BSA_DECODE");
+  if ((rc = check_ptr("Q", Q)) != BSA_OK) return rc;
+  if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
+  if (!std::isfinite(score_scale) || !std::isfinite(sm_scale))
+    return fail(BSA_ERR_INVALID, "scales must be finite");
+  if (route && (rc = check_ptr("S", S)) != BSA_OK) return rc;
+  if (attend) {
+    if ((rc = check_ptr("K", K)) != BSA_OK) return rc;
+    if ((rc = check_ptr("V", V)) != BSA_OK) return rc;
+    if ((rc = check_ptr("O", O)) != BSA_OK) return rc;
+    if (o_dtype != s->dtype && o_dtype != BSA_F32)
+      return fail(BSA_ERR_UNSUPPORTED, "o_dtype must be the input dtype or BSA_F32");
+    if ((rc = check_strides("K", s->k_stride, s->dtype)) != BSA_OK) return rc;
+    if ((rc = check_strides("V", s->v_stride, s->dtype)) != BSA_OK) return rc;
+    if ((rc = check_strides("O", s->o_stride, o_dtype)) != BSA_OK) return rc;
+    if (s->k_stride[2] < s->head_dim || s->v_stride[2] < s->head_dim)
+      return fail(BSA_ERR_INVALID, "K/V token stride must be >= head_dim");
+    // one head's rows are addressed with 32-bit byte offsets
+    const int64_t esz = elem_bytes(s->dtype);
+    if ((s->kv_len + 256) * s->k_stride[2] * esz >= (int64_t(1) << 31) ||
+        (s->kv_len + 256) * s->v_stride[2] * esz >= (int64_t(1) << 31))
+      return fail(BSA_ERR_UNSUPPORTED, "K/V: one head spans more than 2 GiB");
+  }
+  const int hsplit = attend ? decode_hsplit(s) : 1;
+  if (hsplit < 1)
+    return fail(BSA_ERR_UNSUPPORTED, "decode needs n_q_heads/n_kv_heads to split into <= 8 heads");
+  const int lds = decode_lds(s, hsplit, width);
+  if (lds < 0) return fail(BSA_ERR_UNSUPPORTED, "decode row too long for one workgroup's LDS");
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.qs = st3(s->q_stride);
+  a.ks = st3(s->k_stride);
+  a.vs = st3(s->v_stride);
+  a.os = st3(s->o_stride);
+  a.S = S;
+  a.kv_lens = kv_lens;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.batch = s->batch;
+  a.hq = s->n_q_heads;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.B = s->block;
+  a.nblk = static_cast<int>(nblk_of(s));
+  a.k_total = width;
+  a.hsplit = hsplit;
+  a.route = route;
+  a.attend = attend;
+  a.lds_floats = lds;
+  a.kv_len = s->kv_len;
+  a.force = force;
+  a.score_scale = score_scale != 0.f ? score_scale : 1.f / std::sqrt(static_cast<float>(s->head_dim));
+  a.sm_scale = sm_scale != 0.f ? sm_scale : 1.f / std::sqrt(static_cast<float>(s->head_dim));
+  a.bf16 = s->dtype == BSA_BF16;
+  a.out_f32 = o_dtype == BSA_F32;
   return BSA_OK;
 }
 
@@ -167,8 +237,6 @@ size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
       return ws_route_topk(s);
     case BSA_OP_ROUTE_ENTMAX:
       return ws_route_entmax(s);
-    case BSA_OP_ATTEND_DECODE:
-      return k_or_cap >= 1 ? ws_attend_decode(s, k_or_cap) : 0;
     default:
       return 0;
   }
@@ -212,11 +280,19 @@ int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int3
   if (scores_out && !aligned16(scores_out))
     return fail(BSA_ERR_UNSUPPORTED, "scores_out must be 16-byte aligned");
   if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
-  if ((rc = check_ws(ws, ws_bytes, ws_route_topk(s))) != BSA_OK) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s->mode == BSA_DECODE && scores_out == nullptr) {
+    // one fused routing kernel per decode step (scores never leave LDS)
+    bsa::DecodeArgs da;
+    if ((rc = decode_args(s, Q, nullptr, nullptr, S, kv_lens, idx, cnt, k_total, force,
+                          score_scale, 0.f, nullptr, s->dtype, 1, 0, da)) != BSA_OK)
+      return rc;
+    return device_status(bsa::launch_decode_fused(da, st), "route_topk/decode");
+  }
   const int nrow = static_cast<int>(nrow_of(s));
   const int nblk = static_cast<int>(nblk_of(s));
   const size_t rows = static_cast<size_t>(s->batch) * s->n_kv_heads * nrow;
+  if ((rc = check_ws(ws, ws_bytes, ws_route_topk(s))) != BSA_OK) return rc;
   float* qhat = static_cast<float*>(ws);
   float* scores = scores_out ? scores_out
                              : reinterpret_cast<float*>(static_cast<char*>(ws) +
@@ -364,8 +440,6 @@ static int attend_common(const bsa_shape* s, const void* Q, const void* K, const
   a.os = st3(s->o_stride);
   a.idx = idx;
   a.cnt = cnt;
-  a.kv_lens = nullptr;
-  a.ws = nullptr;
   a.batch = s->batch;
   a.hq = s->n_q_heads;
   a.hkv = s->n_kv_heads;
@@ -374,8 +448,6 @@ static int attend_common(const bsa_shape* s, const void* Q, const void* K, const
   a.k_max = k_max;
   a.nrow = static_cast<int>(nrow_of(s));
   a.nblk = static_cast<int>(nblk_of(s));
-  a.splits = 1;
-  a.blocks_per_split = k_max;
   a.q_len = s->q_len;
   a.kv_len = s->kv_len;
   a.sm_scale = sm_scale != 0.f ? sm_scale : 1.f / std::sqrt(static_cast<float>(s->head_dim));
@@ -403,20 +475,40 @@ int bsa_attend_decode(const bsa_shape* s, const void* Q, const void* K, const vo
                       const int32_t* kv_lens, const int32_t* idx, const int32_t* cnt,
                       int32_t k_max, float sm_scale, void* O, int32_t o_dtype, void* ws,
                       size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
   if (s->mode != BSA_DECODE) return fail(BSA_ERR_INVALID, "bsa_attend_decode needs BSA_DECODE");
-  if (s->n_q_heads / s->n_kv_heads > 8)
-    return fail(BSA_ERR_UNSUPPORTED, "decode supports at most 8 query heads per KV head");
-  bsa::AttendArgs a;
-  if ((rc = attend_common(s, Q, K, V, idx, cnt, k_max, sm_scale, O, o_dtype, a)) != BSA_OK)
+  if (!idx || !cnt) return fail(BSA_ERR_INVALID, "idx and cnt must not be NULL");
+  if (k_max < 1) return fail(BSA_ERR_INVALID, "k_max must be >= 1");
+  bsa::DecodeArgs a;
+  if ((rc = decode_args(s, Q, K, V, nullptr, kv_lens, const_cast<int32_t*>(idx),
+                        const_cast<int32_t*>(cnt), k_max, 0u, 0.f, sm_scale, O, o_dtype, 0, 1,
+                        a)) != BSA_OK)
     return rc;
-  if ((rc = check_ws(ws, ws_bytes, ws_attend_decode(s, k_max))) != BSA_OK) return rc;
-  decode_split(s, k_max, &a.blocks_per_split, &a.splits);
-  a.kv_lens = kv_lens;
-  a.ws = static_cast<float*>(ws);
-  return device_status(bsa::launch_attend_decode(a, static_cast<hipStream_t>(stream)),
+  return device_status(bsa::launch_decode_fused(a, static_cast<hipStream_t>(stream)),
                        "attend_decode");
+}
+
+int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                    const float* S, const int32_t* kv_lens, int32_t k_total, uint32_t force,
+                    float score_scale, float sm_scale, int32_t* idx, int32_t* cnt, void* O,
+                    int32_t o_dtype, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if ((rc = check_force(s, force)) != BSA_OK) return rc;
+  if (k_total < 1 || k_total < popcount3(force))
+    return fail(BSA_ERR_INVALID, "k_total (%d) must be >= 1 and >= the number of forced blocks",
+                k_total);
+  if ((idx == nullptr) != (cnt == nullptr))
+    return fail(BSA_ERR_INVALID, "idx and cnt must both be given or both be NULL");
+  bsa::DecodeArgs a;
+  if ((rc = decode_args(s, Q, K, V, S, kv_lens, idx, cnt, k_total, force, score_scale, sm_scale,
+                        O, o_dtype, 1, 1, a)) != BSA_OK)
+    return rc;
+  return device_status(bsa::launch_decode_fused(a, static_cast<hipStream_t>(stream)),
+                       "decode_topk");
 }
 
 }  // extern "C"

@@ -11,10 +11,7 @@
 //                         with fp32 accumulation; the online softmax is fp32.
 //   attend_prefill_f32    fp32 inputs: one query per lane, VALU dot products
 //                         (fp32 matrix rate is not the bound at these sizes).
-//   attend_decode         split-KV: each workgroup streams a slice of the
-//                         selected blocks of one (batch, KV head) from HBM and
-//                         writes a partial (max, sum, o) per query head.
-//   decode_combine        merges the slices.
+// Single-token decode lives in decode.hip.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -111,22 +108,15 @@ __device__ __forceinline__ void map_wg(int id, int npair, int nrow, int wpb, int
   i = nrow - 1 - ir;
 }
 
-// Raw buffer resource over [base, base + bytes): loads past the end return 0,
-// which zero-fills the ragged tail without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                           static_cast<int>(bytes), 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
-}
-
-// Byte extent of one head's rows [0, len) with token stride st (elements).
-__device__ __forceinline__ uint32_t head_bytes(int64_t len, int64_t st, int d, int esz) {
-  return static_cast<uint32_t>(((len - 1) * st + d) * esz);
-}
-
 constexpr float kRescale = 8.f;  // lazy rescale threshold, log2 units
+
+// Max over the four lanes l, l^16, l^32, l^48 (VALU lane swaps, no LDS).
+__device__ __forceinline__ float xmax16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 constexpr int kMaxTiles = 1024;  // tile-list chunk staged in LDS
 
 // QT query tiles of 16 per wavefront, NW wavefronts per workgroup.  A "unit"
@@ -134,7 +124,7 @@ constexpr int kMaxTiles = 1024;  // tile-list chunk staged in LDS
 // wavefronts take NW consecutive units of the same (batch, KV head, block),
 // so they share every K/V tile staged in LDS.
 template <int D, int QT, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64, 1) void attend_prefill_bf16(AttendArgs a, int wpb) {
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArgs a, int wpb) {
   constexpr int NT = NW * 64;
   constexpr int QPW = 16 * QT;  // queries per wave
   constexpr int KS = D / 32;    // k-steps of S^T = K Q^T
@@ -317,18 +307,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attend_prefill_bf16(AttendArgs a, 
               for (int j = 0; j < 4; ++j)
                 if (rel0 + kt * 16 + j - qt * 16 > 0) s[kt][qt][j] = -INFINITY;
         }
-        // running max per query; rescale the accumulators only when it grows by
-        // more than 2^kRescale (p stays <= 2^kRescale, exact after normalising)
+        // running max per query; the accumulators are rescaled only when it
+        // grows by more than 2^kRescale (p stays <= 2^kRescale, exact after
+        // normalising)
         float mx[QT];
         bool grow = false;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          float v = fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3]));
+          float v = -INFINITY;
 #pragma unroll
-          for (int kt = 1; kt < 4; ++kt)
+          for (int kt = 0; kt < 4; ++kt)
             v = fmaxf(v, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
-          v = fmaxf(v, __shfl_xor(v, 16, 64));
-          v = fmaxf(v, __shfl_xor(v, 32, 64));
+          v = xmax16(v);
           mx[qt] = v * sc;
           grow |= mx[qt] > m[qt] + kRescale;
         }
@@ -493,170 +483,6 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
   for (int c = 0; c < D; ++c) Og[c] = o[c] * inv;
 }
 
-// ---------------------------------------------------------------------------
-// Decode: split-KV over the selected blocks.
-// ---------------------------------------------------------------------------
-constexpr int kMaxGroup = 8;
-
-template <typename T, int D, int GM>
-__global__ __launch_bounds__(256) void attend_decode_split(AttendArgs a) {
-  constexpr int LPK = D / 8;          // lanes per key row
-  constexpr int KPS = 256 / LPK;      // keys per workgroup step
-  constexpr int PART = D + 2;         // floats per partial state
-  const int G = a.hq / a.hkv;
-  __shared__ float qsh[GM][D];
-  __shared__ float red[4][GM][D];
-  extern __shared__ float sc[];  // [GM][maxkeys]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int split = blockIdx.x % a.splits;
-  const int pair = blockIdx.x / a.splits;
-  const int b = pair / a.hkv, g = pair % a.hkv;
-  int64_t L = a.kv_lens ? static_cast<int64_t>(a.kv_lens[b]) : a.kv_len;
-  L = L < 1 ? 1 : (L > a.kv_len ? a.kv_len : L);
-  int n = a.cnt[pair];
-  n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
-  const int32_t* list = a.idx + static_cast<int64_t>(pair) * a.k_max;
-  const int s0 = split * a.blocks_per_split;
-  int s1 = s0 + a.blocks_per_split;
-  s1 = s1 > n ? n : s1;
-  const int nkeys = s1 > s0 ? (s1 - s0) * a.B : 0;
-  const int maxkeys = a.blocks_per_split * a.B;
-  const float scl = a.sm_scale * kLog2e;
-  for (int e = tid; e < G * D; e += 256) {
-    const int hh = e / D, c = e % D;
-    const T* qp = static_cast<const T*>(a.Q) + b * a.qs.b + (g * G + hh) * a.qs.h;
-    float v;
-    if constexpr (sizeof(T) == 2)
-      v = bf16_to_f32(qp[c]);
-    else
-      v = qp[c];
-    qsh[hh][c] = v * scl;
-  }
-  __syncthreads();
-  const T* Kg = static_cast<const T*>(a.K) + b * a.ks.b + g * a.ks.h;
-  const T* Vg = static_cast<const T*>(a.V) + b * a.vs.b + g * a.vs.h;
-  const int c = tid % LPK;
-  // phase 1: scores of every key of the slice, per query head
-  for (int k = tid / LPK; k < nkeys; k += KPS) {
-    const int j = list[s0 + k / a.B];
-    const int64_t tt = static_cast<int64_t>(j) * a.B + k % a.B;
-    const bool valid = j >= 0 && j < a.nblk && tt < L;
-    float kv[8];
-    if (valid)
-      load8_f32<T>(Kg + tt * a.ks.t + c * 8, kv);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kv[e] = 0.f;
-#pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-      if (hh >= G) break;
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf(kv[e], qsh[hh][c * 8 + e], s);
-      s = group_sum<LPK>(s);
-      if (c == 0) sc[hh * maxkeys + k] = valid ? s : -INFINITY;
-    }
-  }
-  __syncthreads();
-  // phase 2: per head max and exp (wave w handles heads w, w+4, ...)
-  __shared__ float mh[GM], lh[GM];
-  for (int hh = w; hh < G; hh += 4) {
-    float mx = -INFINITY;
-    for (int k = lane; k < nkeys; k += 64) mx = fmaxf(mx, sc[hh * maxkeys + k]);
-    mx = wave_max(mx);
-    const float base = mx == -INFINITY ? 0.f : mx;
-    float sum = 0.f;
-    for (int k = lane; k < nkeys; k += 64) {
-      const float p = exp2f(sc[hh * maxkeys + k] - base);
-      sc[hh * maxkeys + k] = p;
-      sum += p;
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      mh[hh] = mx;
-      lh[hh] = sum;
-    }
-  }
-  __syncthreads();
-  // phase 3: o_h = sum_k p_hk v_k
-  float acc[GM][8];
-#pragma unroll
-  for (int hh = 0; hh < GM; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-  for (int k = tid / LPK; k < nkeys; k += KPS) {
-    const int j = list[s0 + k / a.B];
-    const int64_t tt = static_cast<int64_t>(j) * a.B + k % a.B;
-    const bool valid = j >= 0 && j < a.nblk && tt < L;
-    if (!valid) continue;
-    float vv[8];
-    load8_f32<T>(Vg + tt * a.vs.t + c * 8, vv);
-#pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-      if (hh >= G) break;
-      const float p = sc[hh * maxkeys + k];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
-    }
-  }
-  // reduce over the lanes sharing a d-chunk, then over the waves
-#pragma unroll
-  for (int hh = 0; hh < GM; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[hh][e];
-#pragma unroll
-      for (int o = LPK; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      acc[hh][e] = v;
-    }
-  if (lane < LPK) {
-#pragma unroll
-    for (int hh = 0; hh < GM; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[w][hh][c * 8 + e] = acc[hh][e];
-  }
-  __syncthreads();
-  float* part = a.ws + (static_cast<int64_t>(pair) * a.splits + split) * G * PART;
-  for (int e = tid; e < G * D; e += 256) {
-    const int hh = e / D, cc = e % D;
-    part[hh * PART + 2 + cc] = red[0][hh][cc] + red[1][hh][cc] + red[2][hh][cc] + red[3][hh][cc];
-  }
-  if (tid < G) {
-    part[tid * PART + 0] = mh[tid];
-    part[tid * PART + 1] = lh[tid];
-  }
-}
-
-template <int D, bool OUT_F32>
-__global__ __launch_bounds__(D) void decode_combine(AttendArgs a) {
-  constexpr int PART = D + 2;
-  const int G = a.hq / a.hkv;
-  const int bh = blockIdx.x;  // (b, h)
-  const int b = bh / a.hq, h = bh % a.hq;
-  const int g = h / G, hh = h % G;
-  const int pair = b * a.hkv + g;
-  const float* part = a.ws + static_cast<int64_t>(pair) * a.splits * G * PART;
-  float M = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, part[(s * G + hh) * PART]);
-  const float base = M == -INFINITY ? 0.f : M;
-  float lsum = 0.f, o = 0.f;
-  const int c = threadIdx.x;
-  for (int s = 0; s < a.splits; ++s) {
-    const float* p = part + (s * G + hh) * PART;
-    const float f = exp2f(p[0] - base);
-    lsum += f * p[1];
-    o += f * p[2 + c];
-  }
-  const float v = lsum > 0.f ? o / lsum : 0.f;
-  const int64_t off = b * a.os.b + h * a.os.h;
-  if constexpr (OUT_F32)
-    static_cast<float*>(a.O)[off + c] = v;
-  else
-    static_cast<uint16_t*>(a.O)[off + c] = f32_to_bf16(v);
-}
-
 template <int D, int QT, int NW>
 hipError_t prefill_bf16_launch(const AttendArgs& a, hipStream_t stream) {
   const int G = a.hq / a.hkv;
@@ -674,30 +500,7 @@ hipError_t prefill_bf16_launch(const AttendArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t prefill_bf16_dispatch(const AttendArgs& a, hipStream_t stream) {
-  return prefill_bf16_launch<D, 2, 8>(a, stream);
-}
-
-template <typename T, int D>
-hipError_t decode_dispatch(const AttendArgs& a, hipStream_t stream) {
-  const int G = a.hq / a.hkv;
-  const size_t dyn = sizeof(float) * static_cast<size_t>(G) * a.blocks_per_split * a.B;
-  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.splits;
-  if (G <= 1)
-    hipLaunchKernelGGL((attend_decode_split<T, D, 1>), dim3(grid), dim3(256), dyn, stream, a);
-  else if (G <= 2)
-    hipLaunchKernelGGL((attend_decode_split<T, D, 2>), dim3(grid), dim3(256), dyn, stream, a);
-  else if (G <= 4)
-    hipLaunchKernelGGL((attend_decode_split<T, D, 4>), dim3(grid), dim3(256), dyn, stream, a);
-  else
-    hipLaunchKernelGGL((attend_decode_split<T, D, 8>), dim3(grid), dim3(256), dyn, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const unsigned cgrid = static_cast<unsigned>(a.batch) * a.hq;
-  if (a.out_f32)
-    hipLaunchKernelGGL((decode_combine<D, true>), dim3(cgrid), dim3(D), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_combine<D, false>), dim3(cgrid), dim3(D), 0, stream, a);
-  return hipGetLastError();
+  return prefill_bf16_launch<D, 2, 4>(a, stream);
 }
 
 }  // namespace
@@ -710,11 +513,6 @@ hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream) {
   else
     hipLaunchKernelGGL(attend_prefill_f32<128>, dim3(grid), dim3(64), 0, stream, a);
   return hipGetLastError();
-}
-
-hipError_t launch_attend_decode(const AttendArgs& a, hipStream_t stream) {
-  if (a.bf16) return a.d == 64 ? decode_dispatch<uint16_t, 64>(a, stream) : decode_dispatch<uint16_t, 128>(a, stream);
-  return a.d == 64 ? decode_dispatch<float, 64>(a, stream) : decode_dispatch<float, 128>(a, stream);
 }
 
 }  // namespace bsa

@@ -57,6 +57,40 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
+
+// Sums over W consecutive lanes (W in 8, 16, 32, 64) with DPP moves inside
+// 16-lane rows and gfx950 lane swaps across rows: VALU only, no LDS crossbar.
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swap16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <int W>
+__device__ __forceinline__ float lane_sum(float v) {
+  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "lane_sum width");
+  v += dppf<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dppf<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dppf<0x141>(v);  // row_half_mirror: the other quad of the 8-lane half
+  if constexpr (W >= 16) v += dppf<0x140>(v);  // row_mirror: the other half of the row
+  if constexpr (W >= 32) v = swap16_sum(v);
+  if constexpr (W >= 64) v = swap32_sum(v);
+  return v;
+}
 __device__ __forceinline__ float wave_max(float v) { return group_max<kWave>(v); }
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
@@ -72,6 +106,37 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros, so ragged tails need no branches (and no serialising waits).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+// Byte extent of one head's rows [0, len) with token stride st (elements).
+__device__ __forceinline__ uint32_t head_bytes(int64_t len, int64_t st, int d, int esz) {
+  return len < 1 ? 0u : static_cast<uint32_t>(((len - 1) * st + d) * esz);
+}
+// 8 consecutive elements at byte offset `off` as fp32 (bf16 or fp32 storage).
+template <typename T>
+__device__ __forceinline__ void buf_load8_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint4 u = buf_load16(r, off);
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+    v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+    v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+  } else {
+    const uint4 a = buf_load16(r, off), b = buf_load16(r, off + 16);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+}
 
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {

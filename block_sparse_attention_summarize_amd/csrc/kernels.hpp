@@ -89,14 +89,33 @@ struct AttendArgs {
   Strides3 qs, ks, vs, os;
   const int32_t* idx;  // [batch, hkv, nrow, k_max]
   const int32_t* cnt;
-  const int32_t* kv_lens;  // decode
-  float* ws;               // decode partial states
-  int batch, hq, hkv, d, B, k_max, nrow, nblk, splits, blocks_per_split;
+  int batch, hq, hkv, d, B, k_max, nrow, nblk;
   int64_t q_len, kv_len;
   float sm_scale;
   bool bf16, out_f32;
 };
 hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream);
-hipError_t launch_attend_decode(const AttendArgs& a, hipStream_t stream);
+
+// Single-token decode: routing (route = 1) and/or attention (attend = 1) for
+// every (batch, KV head) row, hsplit workgroups per row splitting the query
+// heads.  Without routing, the selection is read from idx/cnt.
+struct DecodeArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  Strides3 qs, ks, vs, os;
+  const float* S;          // [batch, hkv, nblk, d] summaries
+  const int32_t* kv_lens;  // may be null
+  int32_t* idx;            // [batch, hkv, 1, k_total]: out when routing, else in
+  int32_t* cnt;
+  int batch, hq, hkv, d, B, nblk, k_total, hsplit, route, attend, lds_floats;
+  int64_t kv_len;
+  uint32_t force;
+  float score_scale, sm_scale;
+  bool bf16, out_f32;
+};
+int decode_lds_floats(int nblk, int d, int gs_max);
+hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace bsa

@@ -18,6 +18,7 @@
 //                   GQA-averaged probabilities, cap by the same radix select.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace bsa {
 
@@ -26,38 +27,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 128;  // candidate blocks scored per workgroup
-
-struct RowInfo {
-  int cand_end;  // candidates are [0, cand_end)
-  int own;       // the row's own block (diagonal / tail)
-  int forced[2];
-  int nforced;
-  int span;  // every block id that can appear in the selection is < span
-};
-
-// Candidate range and forced blocks of one routing row, as documented in bsa.h.
-__device__ inline RowInfo row_info(const RowRule& r, int b, int row) {
-  RowInfo ri;
-  if (r.mode == 0) {
-    ri.own = row;
-    ri.cand_end = r.entmax ? row : row + 1;
-  } else {
-    int64_t L = r.kv_lens ? static_cast<int64_t>(r.kv_lens[b]) : r.kv_len;
-    L = L < 1 ? 1 : (L > r.kv_len ? r.kv_len : L);
-    ri.own = static_cast<int>((L - 1) / r.B);
-    ri.cand_end = ri.own;
-  }
-  ri.nforced = 0;
-  if (r.force & 2u) ri.forced[ri.nforced++] = 0;
-  const bool own_forced = (r.force & 1u) || (r.mode == 1 && (r.force & 4u));
-  if (own_forced && !(ri.nforced == 1 && ri.forced[0] == ri.own)) ri.forced[ri.nforced++] = ri.own;
-  ri.span = ri.own + 1 > ri.cand_end ? ri.own + 1 : ri.cand_end;
-  return ri;
-}
-
-__device__ inline bool is_forced(const RowInfo& ri, int j) {
-  return (ri.nforced > 0 && ri.forced[0] == j) || (ri.nforced > 1 && ri.forced[1] == j);
-}
 
 // ---------------------------------------------------------------------------
 // Coarse scores.  d/4 lanes share one summary row (a float4 each); the dot is
@@ -99,123 +68,6 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup-wide helpers (256 threads).
-// ---------------------------------------------------------------------------
-
-// Exclusive prefix count of `flag` over the workgroup in thread order.
-__device__ inline int block_scan(int flag, int* wave_tot, int& total) {
-  const uint64_t m = __ballot(flag);
-  const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
-  if (lane == 0) wave_tot[w] = __popcll(m);
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) {
-    const int v = wave_tot[k];
-    off += k < w ? v : 0;
-    tot += v;
-  }
-  __syncthreads();
-  total = tot;
-  return off + lanes_below(m);
-}
-
-// Radix select: the key T of the m-th largest eligible element (1 <= m <=
-// #eligible) and how many elements equal to T belong to the top m.
-// `get(e, key)` returns whether element e is eligible and its key.
-template <typename Get>
-__device__ inline void radix_select(int n, int m, Get get, int* hist, int* bcast, uint32_t& T,
-                                    int& need) {
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = m;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int k = threadIdx.x; k < 256; k += kThreads) hist[k] = 0;
-    __syncthreads();
-    for (int e = threadIdx.x; e < n; e += kThreads) {
-      uint32_t key;
-      if (get(e, key) && (key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-      // lane l owns bins 4l..4l+3; suffix sums from the top bin down
-      const int l = threadIdx.x;
-      const int h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
-      const int own = h0 + h1 + h2 + h3;
-      int incl = own;  // sum over lanes >= l
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int v = __shfl_down(incl, o, kWave);
-        incl += (l + o < kWave) ? v : 0;
-      }
-      const int above = incl - own;  // elements in bins above this lane's bins
-      if (above < remaining && incl >= remaining) {
-        int cum = above, bin = 4 * l + 3;
-        const int hv[4] = {h0, h1, h2, h3};
-        for (int k = 3; k >= 0; --k) {
-          if (cum + hv[k] >= remaining) {
-            bin = 4 * l + k;
-            break;
-          }
-          cum += hv[k];
-        }
-        bcast[0] = bin;
-        bcast[1] = remaining - cum;
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = static_cast<uint32_t>(bcast[0]);
-    remaining = bcast[1];
-    prefix |= bin << shift;
-    pmask |= 255u << shift;
-    __syncthreads();
-  }
-  T = prefix;
-  need = remaining;
-}
-
-// Writes the ascending selection (forced blocks + the routed top m of the
-// eligible elements, ties to lower ids) to idx[0:width], pads with -1 and
-// returns the count.  Elements range over [0, span).
-template <typename Get>
-__device__ inline int select_and_write(const RowInfo& ri, int span, int m, int n_elig, Get get,
-                                       int32_t* idx, int width, int* hist, int* bcast,
-                                       int* wave_tot) {
-  uint32_t T = 0;
-  int need = 0;
-  const bool all = m >= n_elig;
-  if (!all && m > 0) radix_select(span, m, get, hist, bcast, T, need);
-  int carry_eq = 0, carry_sel = 0;
-  for (int base = 0; base < span; base += kThreads) {
-    const int e = base + static_cast<int>(threadIdx.x);
-    uint32_t key = 0;
-    const bool elig = e < span && get(e, key);
-    const bool eq = elig && !all && m > 0 && key == T;
-    int tot_eq;
-    const int r_eq = block_scan(eq ? 1 : 0, wave_tot, tot_eq) + carry_eq;
-    bool sel;
-    if (e >= span)
-      sel = false;
-    else if (is_forced(ri, e))
-      sel = true;
-    else if (!elig || m == 0)
-      sel = false;
-    else if (all)
-      sel = true;
-    else
-      sel = key > T || (eq && r_eq < need);
-    int tot_sel;
-    const int pos = block_scan(sel ? 1 : 0, wave_tot, tot_sel) + carry_sel;
-    if (sel && pos < width) idx[pos] = e;
-    carry_eq += tot_eq;
-    carry_sel += tot_sel;
-  }
-  for (int p = carry_sel + static_cast<int>(threadIdx.x); p < width; p += kThreads) idx[p] = -1;
-  return carry_sel < width ? carry_sel : width;
-}
-
-// ---------------------------------------------------------------------------
 // Top-k select, one workgroup per row.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
@@ -239,8 +91,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
     key = float_key(sc[e]);
     return true;
   };
-  const int c = select_and_write(ri, ri.span, m, n_elig, get, a.idx + static_cast<int64_t>(rowid) * a.k_total,
-                                 a.k_total, hist, bcast, wave_tot);
+  int32_t* idx = a.idx + static_cast<int64_t>(rowid) * a.k_total;
+  const int c = select_and_write<kThreads>(
+      ri, ri.span, m, n_elig, get, [&](int p, int e) { idx[p] = e; }, a.k_total, hist, bcast,
+      wave_tot);
   if (threadIdx.x == 0) a.cnt[rowid] = c;
 }
 
@@ -487,9 +341,10 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
     key = float_key(v);
     return true;
   };
-  const int c = select_and_write(ri, ri.span, a.cap, n_elig, get,
-                                 a.idx + static_cast<int64_t>(rowid) * a.width, a.width, hist,
-                                 bcast, wave_tot);
+  int32_t* idx = a.idx + static_cast<int64_t>(rowid) * a.width;
+  const int c = select_and_write<kThreads>(
+      ri, ri.span, a.cap, n_elig, get, [&](int p, int e) { idx[p] = e; }, a.width, hist, bcast,
+      wave_tot);
   if (threadIdx.x == 0) a.cnt[rowid] = c;
 }
 

@@ -20,6 +20,8 @@
  *                               query token per sequence ("DashAttention",
  *                               Contribuições item 4: prefill and incremental
  *                               decode).
+ *   Decode   bsa_decode_topk    Stage 1 (top-k) and Stage 2 for one decode
+ *                               step in a single launch.
  *
  * Conventions shared by every call
  *   - Tensors are device pointers owned by the caller.  The library never
@@ -183,16 +185,30 @@ int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, con
 /*
  * Stage 2, decode: one query token per sequence at position L-1
  * (L = kv_lens[b], NULL: kv_len), attending to the tokens t' < L of the blocks
- * in idx[b, g(h), 0, 0:cnt].  The selected blocks are streamed in slices by
- * several workgroups that write partial softmax states to `ws`, merged by a
- * second kernel.
+ * in idx[b, g(h), 0, 0:cnt].  One launch: each (batch, KV head) row is
+ * handled by one or more workgroups (the GQA group split across them) that
+ * stream the selected blocks and merge their partial softmax states on chip.
  *   Q [batch, Hq, 1, d]; K, V [batch, Hkv, kv_len, d]; O [batch, Hq, 1, d].
- * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
+ *   ws is unused (may be NULL).
+ * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED (more than 8 query heads per
+ * workgroup after splitting, or a row whose scores do not fit in LDS).
  */
 int bsa_attend_decode(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                       const int32_t *kv_lens, const int32_t *idx, const int32_t *cnt,
                       int32_t k_max, float sm_scale, void *O, int32_t o_dtype, void *ws,
                       size_t ws_bytes, void *stream);
+
+/*
+ * Decode step in one launch: top-k routing over the cached summaries S
+ * (exactly as bsa_route_topk in decode mode) followed by bsa_attend_decode on
+ * that selection, without the selection leaving the chip.
+ *   idx, cnt  NULL, or outputs as in bsa_route_topk (both or neither).
+ * Errors: as bsa_route_topk and bsa_attend_decode.
+ */
+int bsa_decode_topk(const bsa_shape *shape, const void *Q, const void *K, const void *V,
+                    const float *S, const int32_t *kv_lens, int32_t k_total,
+                    uint32_t force_flags, float score_scale, float sm_scale, int32_t *idx,
+                    int32_t *cnt, void *O, int32_t o_dtype, void *stream);
 
 /* Scratch bytes needed by `op` for this shape; k_or_cap is k_total (top-k),
  * cap (entmax) or k_max (attend).  Returns 0 when none is needed or the

@@ -114,12 +114,19 @@ def test_attend_validation():
     assert prefill(shape(), k_max=0) == -1
     assert prefill(shape(), o_dtype=5) == -2
     assert prefill(shape(mode=bsa.DECODE, q_len=1)) == -1 and "PREFILL" in err()
-    s = shape(mode=bsa.DECODE, q_len=1, hq=32, hkv=2)
+    s = shape(mode=bsa.DECODE, q_len=1, hq=9, hkv=1)  # 9 heads per KV head: no even split
     assert lib.bsa_attend_decode(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 0.0, FAKE,
-                                 bsa.BF16, FAKE, 1 << 20, None) == -2 and "8 query heads" in err()
+                                 bsa.BF16, None, 0, None) == -2 and "8 heads" in err()
+    s = shape(mode=bsa.DECODE, q_len=1, kv_len=64 * 40000)  # scores of a row exceed the LDS
+    assert lib.bsa_attend_decode(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 0.0, FAKE,
+                                 bsa.BF16, None, 0, None) == -2 and "LDS" in err()
     s = shape(mode=bsa.DECODE, q_len=1)
-    assert lib.bsa_attend_decode(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 0.0, FAKE,
-                                 bsa.BF16, FAKE, 0, None) == -4
+    assert lib.bsa_attend_decode(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, FAKE, 4, 0.0, FAKE,
+                                 bsa.BF16, None, 0, None) == -1
+    assert lib.bsa_decode_topk(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, 4, bsa.FORCE_TAIL,
+                               0.0, 0.0, FAKE, None, FAKE, bsa.BF16, None) == -1 and "both" in err()
+    assert lib.bsa_decode_topk(ctypes.byref(shape()), FAKE, FAKE, FAKE, FAKE, None, 4, 0,
+                               0.0, 0.0, None, None, FAKE, bsa.BF16, None) == -1 and "DECODE" in err()
 
 
 def test_workspace_sizes():
@@ -134,9 +141,8 @@ def test_workspace_sizes():
     assert lib.bsa_workspace_size(bsa.OP_SUMMARIZE, ctypes.byref(s), 4) == 0
     assert lib.bsa_workspace_size(bsa.OP_ROUTE_TOPK, None, 4) == 0
     d = shape(batch=16, hq=32, hkv=8, mode=bsa.DECODE, q_len=1, kv_len=131072)
-    wsd = lib.bsa_workspace_size(bsa.OP_ATTEND_DECODE, ctypes.byref(d), 33)
-    # 128 (batch, KV head) rows, 33 blocks in slices of 3 -> 11 slices
-    assert wsd == al(16 * 32 * 11 * (128 + 2) * 4)
+    # decode attention runs in one launch without scratch
+    assert lib.bsa_workspace_size(bsa.OP_ATTEND_DECODE, ctypes.byref(d), 33) == 0
 
 
 def test_error_string_is_thread_local_and_cleared():

@@ -251,3 +251,36 @@ def test_determinism_and_strides():
     Vt = x["V"].transpose(1, 2).contiguous().transpose(1, 2)
     O3, i3, c3 = bsa.prefill_topk(Qt, Kt, Vt, w.B, w.k_total)
     assert torch.equal(i1, i3) and torch.equal(O1, O3)
+
+
+@pytest.mark.parametrize("name", list(DECODE))
+def test_route_topk_decode_fused_kernel(name):
+    """Decode routing without scores_out runs the single fused routing kernel."""
+    w = DECODE[name]
+    print(f"[route_topk fused decode] {name}", flush=True)
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    idx, cnt = bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, decode=True, kv_len=w.n,
+                              kv_lens=_kv_lens_dev(w))
+    parity.check_topk_rows(w, _cpu(idx), _cpu(cnt), _route_ref(w, x))
+
+
+@pytest.mark.parametrize("name", list(DECODE))
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_decode_step_single_launch(name, out_f32):
+    w = DECODE[name]
+    print(f"[decode_step] {name} out_f32={out_f32}", flush=True)
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    O, idx, cnt = bsa.decode_step(x["Q"], x["K"], x["V"], S, w.B, w.k_total, w.force,
+                                  kv_lens=_kv_lens_dev(w),
+                                  out_dtype=torch.float32 if out_f32 else None)
+    parity.check_topk_rows(w, _cpu(idx), _cpu(cnt), _route_ref(w, x))
+    ref, _ = oracle.attend(x["q"], x["k"], x["v"], w.B, _cpu(idx), _cpu(cnt),
+                           mode=oracle.MODE_DECODE, kv_lens=w.lens())
+    parity.check_attention(w, _cpu(O).reshape(ref.shape), ref, out_f32 or w.dtype == "f32")
+    # without selection outputs the result is identical
+    O2, _, _ = bsa.decode_step(x["Q"], x["K"], x["V"], S, w.B, w.k_total, w.force,
+                               kv_lens=_kv_lens_dev(w), want_selection=False,
+                               out_dtype=torch.float32 if out_f32 else None)
+    assert torch.equal(O, O2)
