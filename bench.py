@@ -27,6 +27,8 @@ import time
 
 import numpy as np
 
+import synth
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
@@ -59,6 +61,20 @@ def copy_calibration(mib, reps=3):
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": mib * 1024 * 1024, "launches": reps}))
+
+
+def device_inputs(w, torch):
+    """Seeded q, k, v of workload w: exact fp32 host copies and device tensors."""
+    out = {}
+    for name in ("q", "k", "v"):
+        stored, exact = synth.gen_stored(w, name)
+        if w.dtype == "bf16":
+            dev = torch.from_numpy(stored.view(np.int16)).to("cuda").view(torch.bfloat16)
+        else:
+            dev = torch.from_numpy(stored).to("cuda")
+        out[name] = exact
+        out[name.upper()] = dev
+    return out
 
 
 def prefill_pairs(w, idx, cnt):
@@ -126,20 +142,21 @@ def cpu_baseline(w, x, idx_h, cnt_h, total_flops, nsample):
             "seconds_per_step_extrapolated": t_total}
 
 
-def run_decode(bsa, torch, synth, parity, steps, warmup):
+def run_decode(bsa, torch, steps, warmup):
     w = synth.WORKLOADS[DECODE]
-    x = parity.make(w)
+    x = device_inputs(w, torch)
     S = bsa.summarize(x["K"], w.B)  # cached summaries, computed once
     lens = torch.tensor(w.lens(), dtype=torch.int32, device="cuda")
     idx = torch.empty((w.batch, w.hkv, 1, w.k_total), dtype=torch.int32, device="cuda")
     cnt = torch.empty((w.batch, w.hkv, 1), dtype=torch.int32, device="cuda")
     O = torch.empty_like(x["Q"])
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    ws = bsa.decode_workspace(x["Q"], x["K"], w.B, w.k_total)
 
     def step():
-        # routing over the cached summaries + attention, one launch
+        # routing over the cached summaries + attention
         bsa.decode_step(x["Q"], x["K"], x["V"], S, w.B, w.k_total, w.force, kv_lens=lens, out=O,
-                        sel=(idx, cnt))
+                        sel=(idx, cnt), ws=ws)
 
     for _ in range(warmup):
         step()
@@ -179,15 +196,12 @@ def main():
         sys.exit(2)
     import torch
     import block_sparse_attention_summarize_amd as bsa
-    import synth
-    from tests import parity
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     w = synth.WORKLOADS[a.workload]
     assert w.mode == "prefill" and w.router == "topk" and w.dtype == "bf16"
-    x = parity.make(w)
+    x = device_inputs(w, torch)
     Q, K, V = x["Q"], x["K"], x["V"]
     nrow = w.nblk
     S = torch.empty((w.batch, w.hkv, w.nblk, w.d), dtype=torch.float32, device="cuda")
@@ -242,7 +256,7 @@ def main():
                      "traffic": read_traffic(kernel_src), "avg_launch_ms": att_s * 1e3},
     }
     if not a.no_decode:
-        out["extra"] = {"decode": run_decode(bsa, torch, synth, parity, a.steps, a.warmup)}
+        out["extra"] = {"decode": run_decode(bsa, torch, a.steps, a.warmup)}
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, idx_h, cnt_h, flops, a.cpu_sample_blocks)
     print(json.dumps(out), flush=True)

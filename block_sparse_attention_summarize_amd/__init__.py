@@ -33,7 +33,8 @@ lib = ctypes.CDLL(LIB_PATH)
 F32, BF16 = 0, 1
 PREFILL, DECODE = 0, 1
 FORCE_DIAG, FORCE_FIRST, FORCE_TAIL = 1, 2, 4
-OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE = range(5)
+OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE, \
+    OP_DECODE_TOPK = range(6)
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
@@ -66,7 +67,7 @@ lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, 
 lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
 lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
-                                _P]
+                                _P, _sz, _P]
 for _f in (lib.bsa_summarize, lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill,
            lib.bsa_attend_decode, lib.bsa_decode_topk):
     _f.restype = ctypes.c_int
@@ -166,8 +167,9 @@ def _route_shape(Q, S, B, decode, kv_len):
 
 
 def route_topk(Q, S, B, k_total, force=0, decode=False, kv_len=None, kv_lens=None,
-               score_scale=0.0, want_scores=False, ws=None, out=None):
-    """Top-k routing.  Returns (idx, cnt) or (idx, cnt, scores)."""
+               score_scale=0.0, want_scores=False, ws=None, out=None, partitioned=True):
+    """Top-k routing.  Returns (idx, cnt) or (idx, cnt, scores).  In decode,
+    partitioned=False passes no workspace (one workgroup per row routes)."""
     shape = _route_shape(Q, S, B, decode, kv_len)
     b, hkv, nblk = shape.batch, shape.n_kv_heads, S.shape[2]
     nrow = 1 if decode else (shape.q_len + B - 1) // B
@@ -178,7 +180,10 @@ def route_topk(Q, S, B, k_total, force=0, decode=False, kv_len=None, kv_lens=Non
         idx = torch.empty((b, hkv, nrow, k_total), dtype=torch.int32, device=dev)
         cnt = torch.empty((b, hkv, nrow), dtype=torch.int32, device=dev)
     scores = torch.empty((b, hkv, nrow, nblk), dtype=torch.float32, device=dev) if want_scores else None
-    wsb, n = _workspace(OP_ROUTE_TOPK, shape, k_total, dev, ws)
+    if decode and not partitioned and not want_scores:
+        wsb, n = None, 0
+    else:
+        wsb, n = _workspace(OP_ROUTE_TOPK, shape, k_total, dev, ws)
     _check(lib.bsa_route_topk(ctypes.byref(shape), _ptr(Q), _ptr(S), _ptr(kv_lens), k_total, force,
                               score_scale, _ptr(idx), _ptr(cnt), _ptr(scores), _ptr(wsb), n,
                               _stream(Q)))
@@ -234,7 +239,7 @@ def attend_decode(q, K, V, B, idx, cnt, kv_lens=None, sm_scale=0.0, out_dtype=No
 
 
 def decode_step(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, score_scale=0.0,
-                sm_scale=0.0, out_dtype=None, out=None, want_selection=True, sel=None):
+                sm_scale=0.0, out_dtype=None, out=None, want_selection=True, sel=None, ws=None):
     """Top-k routing over cached summaries and decode attention in one launch.
     Returns (O, idx, cnt) (idx, cnt are None when want_selection is False)."""
     b, hq, _, d = q.shape
@@ -250,10 +255,20 @@ def decode_step(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, score_sc
         idx = cnt = None
     shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(q), mode=DECODE,
                        q_len=1, kv_len=L, q=q, k=K, v=V, o=O)
+    wsb, n = _workspace(OP_DECODE_TOPK, shape, k_total, q.device, ws)
     _check(lib.bsa_decode_topk(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(S),
                                _ptr(kv_lens), k_total, force, score_scale, sm_scale, _ptr(idx),
-                               _ptr(cnt), _ptr(O), _dtype_code(O), _stream(q)))
+                               _ptr(cnt), _ptr(O), _dtype_code(O), _ptr(wsb), n, _stream(q)))
     return O, idx, cnt
+
+
+def decode_workspace(q, K, B, k_total):
+    """A workspace for decode_step on these shapes (reusable across steps)."""
+    b, hq, _, d = q.shape
+    shape = make_shape(batch=b, hq=hq, hkv=K.shape[1], d=d, B=B, dtype=_dtype_code(q),
+                       mode=DECODE, q_len=1, kv_len=K.shape[2], q=q, k=K, v=K, o=q)
+    return torch.empty(max(workspace_size(OP_DECODE_TOPK, shape, k_total), 1), dtype=torch.uint8,
+                       device=q.device)
 
 
 def prefill_topk(Q, K, V, B, k_total, force=0, S=None, out_dtype=None):

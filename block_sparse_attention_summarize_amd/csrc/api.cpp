@@ -2,6 +2,7 @@
 // anything is enqueued), workspace carving and kernel dispatch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -126,6 +127,42 @@ int decode_hsplit(const bsa_shape* s) {
 }
 int gs_template(int gs) { return gs <= 1 ? 1 : gs <= 2 ? 2 : gs <= 4 ? 4 : 8; }
 
+// Partitioned decode: `parts` workgroups per row over disjoint data, so that
+// the grid covers the 256 CUs; used when the GQA group has at most 8 heads and
+// fewer than 256 blocks are routed.
+int decode_parts(const bsa_shape* s, int32_t k_total, uint32_t force) {
+  const int G = s->n_q_heads / s->n_kv_heads;
+  const int64_t rows = static_cast<int64_t>(s->batch) * s->n_kv_heads;
+  const int m = k_total - popcount3(force);
+  if (G > 8 || m >= 256) return 0;
+  // Splitting pays only when one workgroup per row would leave most CUs
+  // idle: at 128 rows (2 parts) the single fused launch is faster (72 us
+  // against 83 us for 16 x 8 rows of 128k tokens), since a part's share is
+  // too small to keep enough loads in flight.
+  int parts = static_cast<int>((256 + rows - 1) / rows);
+  if (parts < 3) return 0;
+  parts = parts > 8 ? 8 : parts;
+  const int64_t per = (nblk_of(s) + parts - 1) / parts;
+  const int64_t cap = ((per + 255) / 256) * k_total;
+  if (per * 4 + cap * 16 > 96 * 1024) return 0;
+  const int64_t tot = static_cast<int64_t>(parts) * k_total;
+  const int64_t cap2 = ((tot + 255) / 256) * k_total;
+  if (k_total * 4 + cap2 * 16 + k_total * 8 + 8 * 8 * (s->head_dim + 2) * 4 > 96 * 1024) return 0;
+  return parts;
+}
+struct DecodeWs {
+  size_t cand, part, total;
+};
+DecodeWs decode_ws(const bsa_shape* s, int parts, int32_t k_total, bool attend) {
+  const size_t rows = static_cast<size_t>(s->batch) * s->n_kv_heads;
+  const size_t G = s->n_q_heads / s->n_kv_heads;
+  DecodeWs w;
+  w.cand = align_up(rows * parts * k_total * 4);
+  w.part = attend ? align_up(rows * parts * G * (s->head_dim + 2) * 4) : 0;
+  w.total = parts > 0 ? 2 * w.cand + w.part : 0;
+  return w;
+}
+
 // LDS floats of the fused decode kernel; -1 when the row does not fit.
 int decode_lds(const bsa_shape* s, int hsplit, int32_t width) {
   const int gs = gs_template((s->n_q_heads / s->n_kv_heads) / hsplit);
@@ -138,7 +175,11 @@ int decode_lds(const bsa_shape* s, int hsplit, int32_t width) {
 // Decode routing normally runs the fused kernel with no scratch; the
 // size returned also covers the three-kernel path used when scores_out is
 // requested.
-size_t ws_route_topk(const bsa_shape* s) {
+size_t ws_route_topk(const bsa_shape* s, int32_t k_total = 0, uint32_t force = 0) {
+  if (s->mode == BSA_DECODE && k_total > 0) {
+    const int parts = decode_parts(s, k_total, force);
+    if (parts > 0) return decode_ws(s, parts, k_total, false).total;
+  }
   const size_t rows = static_cast<size_t>(s->batch) * s->n_kv_heads * nrow_of(s);
   return align_up(rows * s->head_dim * 4) + align_up(rows * nblk_of(s) * 4);
 }
@@ -234,7 +275,14 @@ size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
   if (check_shape(s) != BSA_OK) return 0;
   switch (op) {
     case BSA_OP_ROUTE_TOPK:
-      return ws_route_topk(s);
+      // decode: the size also admits the partitioned path for any force flags
+      return s->mode == BSA_DECODE ? std::max(ws_route_topk(s), ws_route_topk(s, k_or_cap, 7u))
+                                   : ws_route_topk(s);
+    case BSA_OP_DECODE_TOPK: {
+      if (s->mode != BSA_DECODE || k_or_cap < 1) return 0;
+      const int parts = decode_parts(s, k_or_cap, 7u);
+      return parts > 0 ? decode_ws(s, parts, k_or_cap, true).total : 0;
+    }
     case BSA_OP_ROUTE_ENTMAX:
       return ws_route_entmax(s);
     default:
@@ -282,11 +330,24 @@ int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int3
   if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (s->mode == BSA_DECODE && scores_out == nullptr) {
-    // one fused routing kernel per decode step (scores never leave LDS)
     bsa::DecodeArgs da;
     if ((rc = decode_args(s, Q, nullptr, nullptr, S, kv_lens, idx, cnt, k_total, force,
                           score_scale, 0.f, nullptr, s->dtype, 1, 0, da)) != BSA_OK)
       return rc;
+    const int parts = decode_parts(s, k_total, force);
+    const DecodeWs dw = decode_ws(s, parts, k_total, false);
+    if (parts > 0 && ws != nullptr && ws_bytes >= dw.total &&
+        (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0) {
+      // partitioned routing: every CU streams a distinct slice of the summaries
+      char* base = static_cast<char*>(ws);
+      da.parts = parts;
+      da.mpad = k_total;
+      da.cand_key = reinterpret_cast<uint32_t*>(base);
+      da.cand_id = reinterpret_cast<int32_t*>(base + dw.cand);
+      da.part = nullptr;
+      return device_status(bsa::launch_decode_parts(da, st), "route_topk/decode");
+    }
+    // one workgroup per row, scores never leave LDS
     return device_status(bsa::launch_decode_fused(da, st), "route_topk/decode");
   }
   const int nrow = static_cast<int>(nrow_of(s));
@@ -494,7 +555,7 @@ int bsa_attend_decode(const bsa_shape* s, const void* Q, const void* K, const vo
 int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void* V,
                     const float* S, const int32_t* kv_lens, int32_t k_total, uint32_t force,
                     float score_scale, float sm_scale, int32_t* idx, int32_t* cnt, void* O,
-                    int32_t o_dtype, void* stream) {
+                    int32_t o_dtype, void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
   if ((rc = check_force(s, force)) != BSA_OK) return rc;
@@ -507,8 +568,19 @@ int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void
   if ((rc = decode_args(s, Q, K, V, S, kv_lens, idx, cnt, k_total, force, score_scale, sm_scale,
                         O, o_dtype, 1, 1, a)) != BSA_OK)
     return rc;
-  return device_status(bsa::launch_decode_fused(a, static_cast<hipStream_t>(stream)),
-                       "decode_topk");
+  const int parts = decode_parts(s, k_total, force);
+  const DecodeWs dw = decode_ws(s, parts, k_total, true);
+  if ((rc = check_ws(ws, ws_bytes, dw.total)) != BSA_OK) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (parts == 0)
+    return device_status(bsa::launch_decode_fused(a, st), "decode_topk");
+  char* base = static_cast<char*>(ws);
+  a.parts = parts;
+  a.mpad = k_total;
+  a.cand_key = reinterpret_cast<uint32_t*>(base);
+  a.cand_id = reinterpret_cast<int32_t*>(base + dw.cand);
+  a.part = reinterpret_cast<float*>(base + 2 * dw.cand);
+  return device_status(bsa::launch_decode_parts(a, st), "decode_topk");
 }
 
 }  // extern "C"

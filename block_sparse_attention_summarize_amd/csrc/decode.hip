@@ -8,7 +8,7 @@
 // query's own block are streamed from HBM with several 16-byte loads in
 // flight per lane, scored in fp32, and the top-k (forced blocks added, ties
 // to the lower block id) is selected by the exact radix select in LDS.
-// Phase A: the selected blocks are streamed in 32-key chunks, each wavefront
+// Phase A: the selected blocks are streamed in chunks of keys, each wavefront
 // keeping an online softmax per query head; the wavefronts' partial states
 // are merged in LDS.  Decode is bound by HBM transfers (summaries + the
 // selected K/V), so everything stays on the VALU.
@@ -41,7 +41,11 @@ template <typename T, int D, int GS>
 __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   constexpr int LPK = D / 8;       // lanes per key row (8 elements each)
   constexpr int KPI = kWave / LPK;  // keys per wave load instruction
-  constexpr int KPC = 32 / KPI;     // load instructions per 32-key chunk
+  // keys per chunk: two chunks of K and V are in registers at once, so the
+  // chunk shrinks as the head slice (accumulators) or the element size grows
+  constexpr int CK = sizeof(T) == 2 ? (GS <= 2 ? 32 : 16) : (GS <= 1 ? 16 : 8);
+  constexpr int KPC = CK / KPI;     // load instructions per chunk
+  static_assert(KPC >= 1, "chunk shorter than one load instruction");
   constexpr int LPR = D / 4;       // lanes per fp32 summary row
   constexpr int RPW = kWave / LPR;  // summary rows per wave load instruction
   extern __shared__ float dyn[];    // [nblk] scores, then the merge buffer
@@ -95,14 +99,19 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
     const float4 q4 = reinterpret_cast<const float4*>(qh)[c4];
     const auto rs = make_rsrc(a.S + static_cast<int64_t>(row) * a.nblk * D,
                               static_cast<uint32_t>(n) * D * 4);  // candidates only
-    constexpr int STEP = kNW * RPW;  // rows per workgroup load round
-    for (int base = 0; base < n; base += STEP * kUnroll) {
-      uint4 v[kUnroll];
+    constexpr int STEP = kNW * RPW;        // rows per workgroup load instruction
+    constexpr int ROUND = STEP * kUnroll;  // rows per load round
+    // two register buffers: the next round's loads are in flight while the
+    // current one is reduced (rows past n read as zero, nothing is written)
+    uint4 va[kUnroll], vb[kUnroll];
+    auto issue = [&](int base, uint4 (&v)[kUnroll]) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const uint32_t j = static_cast<uint32_t>(base + u * STEP + w * RPW + lane / LPR);
-        v[u] = buf_load16(rs, j * (D * 4) + c4 * 16);  // rows >= n read as zero
+        v[u] = buf_load16(rs, j * (D * 4) + c4 * 16);
       }
+    };
+    auto reduce = [&](int base, const uint4 (&v)[kUnroll]) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int j = base + u * STEP + w * RPW + lane / LPR;
@@ -113,10 +122,17 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
         p = lane_sum<LPR>(p);
         if (c4 == 0 && j < n) dyn[j] = p * a.score_scale;
       }
+    };
+    if (n > 0) issue(0, va);
+    for (int base = 0; base < n; base += 2 * ROUND) {
+      issue(base + ROUND, vb);
+      reduce(base, va);
+      if (base + ROUND >= n) break;
+      issue(base + 2 * ROUND, va);
+      reduce(base + ROUND, vb);
     }
     __syncthreads();
-    int n_elig = n;
-    for (int f = 0; f < ri.nforced; ++f) n_elig -= ri.forced[f] < n ? 1 : 0;
+    const int n_elig = n - ri.nforced_below(n);
     int m = a.k_total - ri.nforced;
     m = m < 0 ? 0 : m;
     auto get = [&](int e, uint32_t& key) -> bool {
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   }
   __syncthreads();
   const int nsel = sel_n;
-  const int cpb = a.B / 32;  // 32-key chunks per block
+  const int cpb = a.B / CK;  // chunks per block
   const int nchunk = nsel * cpb;
   // K/V rows at or past L read as zero through the buffer resources
   const auto rk = make_rsrc(static_cast<const T*>(a.K) + b * a.ks.b + g * a.ks.h,
@@ -179,23 +195,47 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
   }
-  for (int ch = w; ch < nchunk; ch += kNW) {
+  constexpr int RPL = sizeof(T) == 2 ? 1 : 2;  // 16-byte loads per 8 elements
+  // Chunk ch covers keys [t0, t0 + CK) of selected block sel[ch / cpb];
+  // invalid chunks load from an out-of-range offset (zeros) and are masked.
+  auto chunk_t0 = [&](int ch) -> int {
+    if (ch >= nchunk) return -1;
     const int j = sel[ch / cpb];
-    if (j < 0 || j >= a.nblk) continue;
-    const int t0 = j * a.B + (ch % cpb) * 32;
-    float kv[KPC][8], vv[KPC][8];
+    return (j >= 0 && j < a.nblk) ? j * a.B + (ch % cpb) * CK : -1;
+  };
+  auto issue = [&](int ch, uint4 (&kb)[KPC][RPL], uint4 (&vb)[KPC][RPL]) {
+    const int t0 = chunk_t0(ch);
+#pragma unroll
+    for (int it = 0; it < KPC; ++it) {
+      const uint32_t t = static_cast<uint32_t>(t0 + it * KPI + kg);
+      const uint32_t ko = t0 < 0 ? 0xFFFFFF00u : t * kst + c8 * 8 * sizeof(T);
+      const uint32_t vo = t0 < 0 ? 0xFFFFFF00u : t * vst + c8 * 8 * sizeof(T);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        kb[it][r] = buf_load16(rk, ko + 16 * r);
+        vb[it][r] = buf_load16(rv, vo + 16 * r);
+      }
+    }
+  };
+  auto unpack = [&](const uint4 (&u)[RPL], float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+      x[0] = bf16_lo(u[0].x); x[1] = bf16_hi(u[0].x);
+      x[2] = bf16_lo(u[0].y); x[3] = bf16_hi(u[0].y);
+      x[4] = bf16_lo(u[0].z); x[5] = bf16_hi(u[0].z);
+      x[6] = bf16_lo(u[0].w); x[7] = bf16_hi(u[0].w);
+    } else {
+      x[0] = __uint_as_float(u[0].x); x[1] = __uint_as_float(u[0].y);
+      x[2] = __uint_as_float(u[0].z); x[3] = __uint_as_float(u[0].w);
+      x[4] = __uint_as_float(u[RPL - 1].x); x[5] = __uint_as_float(u[RPL - 1].y);
+      x[6] = __uint_as_float(u[RPL - 1].z); x[7] = __uint_as_float(u[RPL - 1].w);
+    }
+  };
+  auto compute = [&](int ch, const uint4 (&kb)[KPC][RPL], const uint4 (&vb)[KPC][RPL]) {
+    const int t0 = chunk_t0(ch);
+    if (t0 < 0) return;
     bool ok[KPC];
 #pragma unroll
-    for (int it = 0; it < KPC; ++it) {
-      const int t = t0 + it * KPI + kg;
-      ok[it] = t < L;
-      buf_load8_f32<T>(rk, static_cast<uint32_t>(t) * kst + c8 * 8 * sizeof(T), kv[it]);
-    }
-#pragma unroll
-    for (int it = 0; it < KPC; ++it) {
-      const int t = t0 + it * KPI + kg;
-      buf_load8_f32<T>(rv, static_cast<uint32_t>(t) * vst + c8 * 8 * sizeof(T), vv[it]);
-    }
+    for (int it = 0; it < KPC; ++it) ok[it] = t0 + it * KPI + kg < L;
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
       if (hh >= gs) break;
@@ -203,9 +243,11 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int it = 0; it < KPC; ++it) {
+        float kv[8];
+        unpack(kb[it], kv);
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(kv[it][e], qa[hh][c8 * 8 + e], acc);
+        for (int e = 0; e < 8; ++e) acc = fmaf(kv[e], qa[hh][c8 * 8 + e], acc);
         acc = lane_sum<LPK>(acc);
         s[it] = ok[it] ? acc : -INFINITY;
         mx = fmaxf(mx, s[it]);
@@ -222,11 +264,24 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
 #pragma unroll
       for (int it = 0; it < KPC; ++it) {
         const float p = __builtin_amdgcn_exp2f(s[it] - base);
+        float vv[8];
+        unpack(vb[it], vv);
         ls += p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(p, vv[it][e], o[hh][e]);
+        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(p, vv[e], o[hh][e]);
       }
       l[hh] = l[hh] * f + ls;
+    }
+  };
+  {
+    uint4 ka[KPC][RPL], va2[KPC][RPL], kb2[KPC][RPL], vb2[KPC][RPL];
+    if (w < nchunk) issue(w, ka, va2);
+    for (int ch = w; ch < nchunk; ch += 2 * kNW) {
+      issue(ch + kNW, kb2, vb2);
+      compute(ch, ka, va2);
+      if (ch + kNW >= nchunk) break;
+      issue(ch + 2 * kNW, ka, va2);
+      compute(ch + kNW, kb2, vb2);
     }
   }
   // reduce over the key groups of the wave (lanes sharing c8), then merge the
@@ -307,6 +362,529 @@ int decode_lds_floats(int nblk, int d, int gs_max) {
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream) {
   if (a.bf16) return a.d == 64 ? launch_t<uint16_t, 64>(a, stream) : launch_t<uint16_t, 128>(a, stream);
   return a.d == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
+}
+
+}  // namespace bsa
+
+// ===========================================================================
+// Partitioned decode step: every (batch, KV head) row is served by `parts`
+// workgroups that stream disjoint data, so all CUs pull distinct bytes.
+//   decode_route_part   partition p scores the candidate blocks
+//                       [p*per, (p+1)*per) and keeps its exact local top-m
+//                       (a block in the global top-m is in its partition's
+//                       top-m under the same tie rule).
+//   decode_attend_part  merges the parts' candidates into the row's top-m,
+//                       adds the forced blocks, attends a contiguous share of
+//                       the selected blocks for every query head and writes
+//                       its partial softmax state.
+//   decode_combine      merges the parts' partial states of a row into O.
+// ===========================================================================
+namespace bsa {
+namespace {
+
+constexpr int kSel = 256;  // elements per wave-level selection slice (4 per lane)
+
+__device__ __forceinline__ void part_map(int id, int rows, int parts, int& row, int& p) {
+  if (rows % 8 == 0) {  // the parts of a row on one XCD (shared L2)
+    const int x = id % 8, s = id / 8;
+    p = s % parts;
+    row = (s / parts) * 8 + x;
+  } else {
+    row = id / parts;
+    p = id % parts;
+  }
+}
+
+// Reduces `len` (key, id) candidates held in LDS in id order (src) to their
+// top-m, also in id order, by rounds of per-wave slice selections; returns
+// the final count.  The result is left in `out` (mpad entries, -1 padded).
+// Requires m < kSel.  `load(i, key, id, valid)` reads element i of the first
+// round's source.
+template <int NT, typename Load>
+__device__ int tournament(int len, int m, Load load, uint32_t* bufk0, int32_t* bufi0,
+                          uint32_t* bufk1, int32_t* bufi1, uint32_t* outk, int32_t* outi,
+                          int mpad) {
+  constexpr int NW = NT / kWave;
+  __shared__ int final_count;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  uint32_t* srck = nullptr;
+  int32_t* srci = nullptr;
+  uint32_t* dk = bufk0;
+  int32_t* di = bufi0;
+  bool first = true;
+  for (;;) {
+    const int nslice = (len + kSel - 1) / kSel;
+    const bool last = nslice <= 1;
+    for (int sl = w; sl < (nslice > 0 ? nslice : 1); sl += NW) {
+      uint32_t key[4];
+      int32_t id[4];
+      bool valid[4], sel[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = sl * kSel + e * kWave + lane;
+        if (first) {
+          load(i, key[e], id[e], valid[e]);
+          valid[e] = valid[e] && i < len;
+        } else {
+          valid[e] = i < len && srci[i] >= 0;
+          key[e] = valid[e] ? srck[i] : 0u;
+          id[e] = valid[e] ? srci[i] : -1;
+        }
+      }
+      wave_topm<4>(key, valid, m, sel);
+      uint32_t* ok = last ? outk : dk + sl * m;
+      int32_t* oi = last ? outi : di + sl * m;
+      const int width = last ? mpad : m;
+      int base = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t mk = __ballot(sel[e]);
+        if (sel[e]) {
+          const int pos = base + lanes_below(mk);
+          ok[pos] = key[e];
+          oi[pos] = id[e];
+        }
+        base += __popcll(mk);
+      }
+      for (int q = base + lane; q < width; q += kWave) oi[q] = -1;
+      if (last && lane == 0) final_count = base;
+    }
+    __syncthreads();
+    if (last) break;
+    len = nslice * m;
+    srck = dk;
+    srci = di;
+    dk = (dk == bufk0) ? bufk1 : bufk0;
+    di = (di == bufi0) ? bufi1 : bufi0;
+    first = false;
+  }
+  return final_count;
+}
+
+template <int D>
+__global__ __launch_bounds__(kNT) void decode_route_part(DecodeArgs a) {
+  constexpr int LPR = D / 4;
+  constexpr int RPW = kWave / LPR;
+  extern __shared__ float dyn[];  // [per] scores, then 2 x 2 x tournament buffers
+  __shared__ float qh[D];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rows = a.batch * a.hkv;
+  int row, p;
+  part_map(blockIdx.x, rows, a.parts, row, p);
+  const int b = row / a.hkv, g = row % a.hkv;
+  const int G = a.hq / a.hkv;
+  RowRule rule;
+  rule.mode = 1;
+  rule.entmax = 0;
+  rule.force = a.force;
+  rule.B = a.B;
+  rule.kv_len = a.kv_len;
+  rule.kv_lens = a.kv_lens;
+  const RowInfo ri = row_info(rule, b, 0);
+  const int n = ri.cand_end;
+  const int per = (n + a.parts - 1) / a.parts;
+  const int lo = p * per < n ? p * per : n;
+  const int hi = lo + per < n ? lo + per : n;
+  const int len = hi - lo;
+  int m = a.k_total - ri.nforced;
+  m = m < 0 ? 0 : m;
+  if (a.bf16) {
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.Q) + b * a.qs.b;
+    for (int c = tid; c < D; c += kNT) {
+      float s = 0.f;
+      for (int hh = 0; hh < G; ++hh) s += bf16_to_f32(Qb[(g * G + hh) * a.qs.h + c]);
+      qh[c] = s;
+    }
+  } else {
+    const float* Qb = static_cast<const float*>(a.Q) + b * a.qs.b;
+    for (int c = tid; c < D; c += kNT) {
+      float s = 0.f;
+      for (int hh = 0; hh < G; ++hh) s += Qb[(g * G + hh) * a.qs.h + c];
+      qh[c] = s;
+    }
+  }
+  __syncthreads();
+  const int c4 = lane % LPR;
+  const float4 q4 = reinterpret_cast<const float4*>(qh)[c4];
+  const auto rs = make_rsrc(a.S + (static_cast<int64_t>(row) * a.nblk + lo) * D,
+                            static_cast<uint32_t>(len) * D * 4);
+  constexpr int STEP = kNW * RPW;
+  constexpr int ROUND = STEP * kUnroll;
+  uint4 va[kUnroll], vb[kUnroll];
+  auto issue = [&](int base, uint4 (&v)[kUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t j = static_cast<uint32_t>(base + u * STEP + w * RPW + lane / LPR);
+      v[u] = buf_load16(rs, j * (D * 4) + c4 * 16);
+    }
+  };
+  auto reduce = [&](int base, const uint4 (&v)[kUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = base + u * STEP + w * RPW + lane / LPR;
+      float s = q4.x * __uint_as_float(v[u].x);
+      s = fmaf(q4.y, __uint_as_float(v[u].y), s);
+      s = fmaf(q4.z, __uint_as_float(v[u].z), s);
+      s = fmaf(q4.w, __uint_as_float(v[u].w), s);
+      s = lane_sum<LPR>(s);
+      if (c4 == 0 && j < len) dyn[j] = s * a.score_scale;
+    }
+  };
+  if (len > 0) issue(0, va);
+  for (int base = 0; base < len; base += 2 * ROUND) {
+    issue(base + ROUND, vb);
+    reduce(base, va);
+    if (base + ROUND >= len) break;
+    issue(base + 2 * ROUND, va);
+    reduce(base + ROUND, vb);
+  }
+  __syncthreads();
+  // local top-m of the partition, kept in block-id order
+  const int cap = ((len + kSel - 1) / kSel) * m;
+  uint32_t* bk0 = reinterpret_cast<uint32_t*>(dyn + a.lds_floats);
+  int32_t* bi0 = reinterpret_cast<int32_t*>(bk0 + cap);
+  uint32_t* bk1 = reinterpret_cast<uint32_t*>(bi0 + cap);
+  int32_t* bi1 = reinterpret_cast<int32_t*>(bk1 + cap);
+  const int64_t off = (static_cast<int64_t>(row) * a.parts + p) * a.mpad;
+  tournament<kNT>(
+      len, m,
+      [&](int i, uint32_t& key, int32_t& id, bool& valid) {
+        const int j = lo + i;
+        valid = i < len && !is_forced(ri, j);
+        key = valid ? float_key(dyn[i]) : 0u;
+        id = j;
+      },
+      bk0, bi0, bk1, bi1, a.cand_key + off, a.cand_id + off, a.mpad);
+}
+
+template <typename T, int D, int GS>
+__global__ __launch_bounds__(kNT) void decode_attend_part(DecodeArgs a) {
+  constexpr int LPK = D / 8;
+  constexpr int KPI = kWave / LPK;
+  constexpr int CK = sizeof(T) == 2 ? (GS <= 2 ? 32 : 16) : (GS <= 1 ? 16 : 8);
+  constexpr int KPC = CK / KPI;
+  constexpr int RPL = sizeof(T) == 2 ? 1 : 2;
+  constexpr int PART = D + 2;
+  extern __shared__ float dyn[];
+  __shared__ float qa[GS][D];
+  __shared__ int sel_n;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rows = a.batch * a.hkv;
+  int row, p;
+  part_map(blockIdx.x, rows, a.attend ? a.parts : 1, row, p);
+  const int b = row / a.hkv, g = row % a.hkv;
+  const int G = a.hq / a.hkv;
+  RowRule rule;
+  rule.mode = 1;
+  rule.entmax = 0;
+  rule.force = a.force;
+  rule.B = a.B;
+  rule.kv_len = a.kv_len;
+  rule.kv_lens = a.kv_lens;
+  const RowInfo ri = row_info(rule, b, 0);
+  int64_t L = a.kv_lens ? static_cast<int64_t>(a.kv_lens[b]) : a.kv_len;
+  L = L < 1 ? 1 : (L > a.kv_len ? a.kv_len : L);
+  int m = a.k_total - ri.nforced;
+  m = m < 0 ? 0 : m;
+  // ---- merge the parts' candidates (already in block-id order) ----
+  const int total = a.parts * a.mpad;
+  int* sel = reinterpret_cast<int*>(dyn);  // [k_total]
+  uint32_t* bk0 = reinterpret_cast<uint32_t*>(sel + a.k_total);
+  const int cap = ((total + kSel - 1) / kSel) * (m > 0 ? m : 1);
+  int32_t* bi0 = reinterpret_cast<int32_t*>(bk0 + cap);
+  uint32_t* bk1 = reinterpret_cast<uint32_t*>(bi0 + cap);
+  int32_t* bi1 = reinterpret_cast<int32_t*>(bk1 + cap);
+  uint32_t* fk = reinterpret_cast<uint32_t*>(bi1 + cap);
+  int32_t* fi = reinterpret_cast<int32_t*>(fk + a.mpad);
+  const uint32_t* ck = a.cand_key + static_cast<int64_t>(row) * total;
+  const int32_t* ci = a.cand_id + static_cast<int64_t>(row) * total;
+  const int nr = tournament<kNT>(
+      total, m,
+      [&](int i, uint32_t& key, int32_t& id, bool& valid) {
+        id = i < total ? ci[i] : -1;
+        valid = id >= 0;
+        key = valid ? ck[i] : 0u;
+      },
+      bk0, bi0, bk1, bi1, fk, fi, a.mpad);
+  if (tid == 0) {
+    // ascending: block 0 when forced first, the routed ids (all between),
+    // then the row's own block when forced (f0 <= f1 and both bracket the
+    // candidates, which lie strictly between them)
+    int c = 0;
+    const bool lead = ri.f0 == 0 && (a.force & 2u);
+    if (lead) sel[c++] = 0;
+    for (int q = 0; q < nr; ++q) sel[c++] = fi[q];
+    if (!lead && ri.f0 >= 0) sel[c++] = ri.f0;
+    if (ri.f1 >= 0) sel[c++] = ri.f1;
+    sel_n = c;
+  }
+  __syncthreads();
+  const int nsel = sel_n;
+  if (a.idx != nullptr && p == 0) {
+    int32_t* gidx = a.idx + static_cast<int64_t>(row) * a.k_total;
+    for (int q = tid; q < a.k_total; q += kNT) gidx[q] = q < nsel ? sel[q] : -1;
+    if (tid == 0) a.cnt[row] = nsel;
+  }
+  if (!a.attend) return;
+
+  // ---- attention over this part's share of the selected blocks ----
+  const float scl = a.sm_scale * kLog2e;
+  for (int e = tid; e < G * D; e += kNT) {
+    const int hh = e / D, c = e % D;
+    const T* qp = static_cast<const T*>(a.Q) + b * a.qs.b + (g * G + hh) * a.qs.h;
+    float v;
+    if constexpr (sizeof(T) == 2)
+      v = bf16_to_f32(qp[c]);
+    else
+      v = qp[c];
+    qa[hh][c] = v * scl;
+  }
+  __syncthreads();
+  const int s0 = (nsel * p) / a.parts, s1 = (nsel * (p + 1)) / a.parts;
+  const int cpb = a.B / CK;
+  const int nchunk = (s1 - s0) * cpb;
+  const auto rk = make_rsrc(static_cast<const T*>(a.K) + b * a.ks.b + g * a.ks.h,
+                            head_bytes(L, a.ks.t, D, sizeof(T)));
+  const auto rv = make_rsrc(static_cast<const T*>(a.V) + b * a.vs.b + g * a.vs.h,
+                            head_bytes(L, a.vs.t, D, sizeof(T)));
+  const uint32_t kst = static_cast<uint32_t>(a.ks.t * sizeof(T));
+  const uint32_t vst = static_cast<uint32_t>(a.vs.t * sizeof(T));
+  const int c8 = lane % LPK, kg = lane / LPK;
+  float mm[GS], l[GS], o[GS][8];
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh) {
+    mm[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+  }
+  auto chunk_t0 = [&](int ch) -> int {
+    if (ch >= nchunk) return -1;
+    const int j = sel[s0 + ch / cpb];
+    return (j >= 0 && j < a.nblk) ? j * a.B + (ch % cpb) * CK : -1;
+  };
+  auto issue = [&](int ch, uint4 (&kb)[KPC][RPL], uint4 (&vb)[KPC][RPL]) {
+    const int t0 = chunk_t0(ch);
+#pragma unroll
+    for (int it = 0; it < KPC; ++it) {
+      const uint32_t t = static_cast<uint32_t>(t0 + it * KPI + kg);
+      const uint32_t ko = t0 < 0 ? 0xFFFFFF00u : t * kst + c8 * 8 * sizeof(T);
+      const uint32_t vo = t0 < 0 ? 0xFFFFFF00u : t * vst + c8 * 8 * sizeof(T);
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        kb[it][r] = buf_load16(rk, ko + 16 * r);
+        vb[it][r] = buf_load16(rv, vo + 16 * r);
+      }
+    }
+  };
+  auto unpack = [&](const uint4 (&u)[RPL], float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+      x[0] = bf16_lo(u[0].x); x[1] = bf16_hi(u[0].x);
+      x[2] = bf16_lo(u[0].y); x[3] = bf16_hi(u[0].y);
+      x[4] = bf16_lo(u[0].z); x[5] = bf16_hi(u[0].z);
+      x[6] = bf16_lo(u[0].w); x[7] = bf16_hi(u[0].w);
+    } else {
+      x[0] = __uint_as_float(u[0].x); x[1] = __uint_as_float(u[0].y);
+      x[2] = __uint_as_float(u[0].z); x[3] = __uint_as_float(u[0].w);
+      x[4] = __uint_as_float(u[RPL - 1].x); x[5] = __uint_as_float(u[RPL - 1].y);
+      x[6] = __uint_as_float(u[RPL - 1].z); x[7] = __uint_as_float(u[RPL - 1].w);
+    }
+  };
+  auto compute = [&](int ch, const uint4 (&kb)[KPC][RPL], const uint4 (&vb)[KPC][RPL]) {
+    const int t0 = chunk_t0(ch);
+    if (t0 < 0) return;
+    bool ok[KPC];
+#pragma unroll
+    for (int it = 0; it < KPC; ++it) ok[it] = t0 + it * KPI + kg < L;
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+      if (hh >= G) break;
+      float s[KPC];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int it = 0; it < KPC; ++it) {
+        float kv[8];
+        unpack(kb[it], kv);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(kv[e], qa[hh][c8 * 8 + e], acc);
+        acc = lane_sum<LPK>(acc);
+        s[it] = ok[it] ? acc : -INFINITY;
+        mx = fmaxf(mx, s[it]);
+      }
+      if constexpr (LPK == 8) mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
+      mx = swap32_max(swap16_max(mx));
+      const float mn = fmaxf(mm[hh], mx);
+      const float base = mn == -INFINITY ? 0.f : mn;
+      const float f = __builtin_amdgcn_exp2f(mm[hh] - base);
+      mm[hh] = mn;
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] *= f;
+#pragma unroll
+      for (int it = 0; it < KPC; ++it) {
+        const float pw = __builtin_amdgcn_exp2f(s[it] - base);
+        float vv[8];
+        unpack(vb[it], vv);
+        ls += pw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pw, vv[e], o[hh][e]);
+      }
+      l[hh] = l[hh] * f + ls;
+    }
+  };
+  {
+    uint4 ka[KPC][RPL], va2[KPC][RPL], kb2[KPC][RPL], vb2[KPC][RPL];
+    if (w < nchunk) issue(w, ka, va2);
+    for (int ch = w; ch < nchunk; ch += 2 * kNW) {
+      issue(ch + kNW, kb2, vb2);
+      compute(ch, ka, va2);
+      if (ch + kNW >= nchunk) break;
+      issue(ch + 2 * kNW, ka, va2);
+      compute(ch + kNW, kb2, vb2);
+    }
+  }
+  // merge the waves in LDS (reusing the candidate area), then publish the
+  // workgroup's partial state
+  float* merge = reinterpret_cast<float*>(fi + a.mpad);
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh) {
+    if (hh >= G) break;
+    float lt = l[hh];
+    if constexpr (LPK == 8) lt += __shfl_xor(lt, 8, kWave);
+    lt = swap32_sum(swap16_sum(lt));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = o[hh][e];
+      if constexpr (LPK == 8) v += __shfl_xor(v, 8, kWave);
+      v = swap32_sum(swap16_sum(v));
+      if (kg == 0) merge[(w * GS + hh) * PART + 2 + c8 * 8 + e] = v;
+    }
+    if (lane == 0) {
+      merge[(w * GS + hh) * PART + 0] = mm[hh];
+      merge[(w * GS + hh) * PART + 1] = lt;
+    }
+  }
+  __syncthreads();
+  float* mypart = a.part + (static_cast<int64_t>(row) * a.parts + p) * G * PART;
+  for (int e = tid; e < G * PART; e += kNT) {
+    const int hh = e / PART, c = e % PART;
+    float M = -INFINITY;
+    for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, merge[(ww * GS + hh) * PART]);
+    float v;
+    if (c == 0) {
+      v = M;
+    } else {
+      const float base = M == -INFINITY ? 0.f : M;
+      v = 0.f;
+      for (int ww = 0; ww < kNW; ++ww) {
+        const float* pp = merge + (ww * GS + hh) * PART;
+        v += __builtin_amdgcn_exp2f(pp[0] - base) * pp[c];
+      }
+    }
+    mypart[e] = v;
+  }
+}
+
+// Merges the parts' partial softmax states of a row and writes O.  A kernel
+// of its own: the stream order publishes the partial states across XCDs
+// (the L2s of different XCDs are not coherent, and an agent-scope fence per
+// workgroup would write back and invalidate a whole L2 each time).
+__global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
+  constexpr int PART_PAD = 2;
+  const int row = blockIdx.x;
+  const int b = row / a.hkv, g = row % a.hkv;
+  const int G = a.hq / a.hkv;
+  const int part_w = a.d + PART_PAD;
+  const float* rp = a.part + static_cast<int64_t>(row) * a.parts * G * part_w;
+  for (int e = threadIdx.x; e < G * a.d; e += blockDim.x) {
+    const int hh = e / a.d, c = e % a.d;
+    float M = -INFINITY;
+    for (int q = 0; q < a.parts; ++q) M = fmaxf(M, rp[(q * G + hh) * part_w]);
+    const float base = M == -INFINITY ? 0.f : M;
+    float ls = 0.f, acc = 0.f;
+    for (int q = 0; q < a.parts; ++q) {
+      const float* pp = rp + (q * G + hh) * part_w;
+      const float f = __builtin_amdgcn_exp2f(pp[0] - base);
+      ls += f * pp[1];
+      acc += f * pp[2 + c];
+    }
+    const float v = ls > 0.f ? acc / ls : 0.f;
+    const int64_t off = b * a.os.b + (g * G + hh) * a.os.h + c;
+    if (a.out_f32)
+      static_cast<float*>(a.O)[off] = v;
+    else
+      static_cast<uint16_t*>(a.O)[off] = f32_to_bf16(v);
+  }
+}
+
+template <typename T, int D, int GS>
+hipError_t launch_attend_part(const DecodeArgs& a, size_t dyn, hipStream_t stream) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attend_part<T, D, GS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * (a.attend ? a.parts : 1);
+  hipLaunchKernelGGL((decode_attend_part<T, D, GS>), dim3(grid), dim3(kNT), dyn, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.attend) return e;
+  hipLaunchKernelGGL(decode_combine, dim3(a.batch * a.hkv), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_attend_part_t(const DecodeArgs& a, size_t dyn, hipStream_t stream) {
+  const int G = a.hq / a.hkv;
+  if (G <= 1) return launch_attend_part<T, D, 1>(a, dyn, stream);
+  if (G <= 2) return launch_attend_part<T, D, 2>(a, dyn, stream);
+  if (G <= 4) return launch_attend_part<T, D, 4>(a, dyn, stream);
+  return launch_attend_part<T, D, 8>(a, dyn, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_parts(const DecodeArgs& a, hipStream_t stream) {
+  const int rows = a.batch * a.hkv;
+  int m = a.k_total;  // upper bound of the routed count
+  // routing kernel LDS: partition scores + two tournament ping-pong buffers
+  const int per = (a.nblk + a.parts - 1) / a.parts;
+  const int cap1 = ((per + kSel - 1) / kSel) * m;
+  const size_t dyn1 = static_cast<size_t>(per) * 4 + static_cast<size_t>(cap1) * 16;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_route_part<64>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024)) != hipSuccess)
+      return e;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_route_part<128>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024)) != hipSuccess)
+      return e;
+    attr = true;
+  }
+  DecodeArgs r = a;
+  r.lds_floats = per;
+  const unsigned grid1 = static_cast<unsigned>(rows) * a.parts;
+  if (a.d == 64)
+    hipLaunchKernelGGL(decode_route_part<64>, dim3(grid1), dim3(kNT), dyn1, stream, r);
+  else
+    hipLaunchKernelGGL(decode_route_part<128>, dim3(grid1), dim3(kNT), dyn1, stream, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int G = a.hq / a.hkv;
+  const int gs = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  const int total = a.parts * a.mpad;
+  const int cap2 = ((total + kSel - 1) / kSel) * (m > 0 ? m : 1);
+  size_t dyn2 = static_cast<size_t>(a.k_total) * 4 + static_cast<size_t>(cap2) * 16 +
+                static_cast<size_t>(a.mpad) * 8;
+  dyn2 += static_cast<size_t>(kNW) * gs * (a.d + 2) * 4;
+  if (a.bf16)
+    return a.d == 64 ? launch_attend_part_t<uint16_t, 64>(a, dyn2, stream)
+                     : launch_attend_part_t<uint16_t, 128>(a, dyn2, stream);
+  return a.d == 64 ? launch_attend_part_t<float, 64>(a, dyn2, stream)
+                   : launch_attend_part_t<float, 128>(a, dyn2, stream);
 }
 
 }  // namespace bsa

@@ -114,8 +114,16 @@ struct DecodeArgs {
   uint32_t force;
   float score_scale, sm_scale;
   bool bf16, out_f32;
+  // partitioned decode (parts workgroups per row over disjoint data)
+  int parts, mpad;       // candidates kept per partition (>= routed count)
+  uint32_t* cand_key;    // [rows, parts, mpad] order-preserving score keys
+  int32_t* cand_id;      // [rows, parts, mpad] block ids, -1 = none
+  float* part;           // [rows, parts, G, d + 2] partial softmax states
 };
 int decode_lds_floats(int nblk, int d, int gs_max);
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream);
+// Partitioned decode step: routing kernel then attention kernel.  With
+// attend = 0 the second kernel only merges the candidates into idx/cnt.
+hipError_t launch_decode_parts(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace bsa

@@ -79,11 +79,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   const int b = rowid / (a.nrow * a.hkv);
   const RowInfo ri = row_info(a.rule, b, row);
   const float* sc = a.scores + static_cast<int64_t>(rowid) * a.nblk;
-  const int n_elig = ri.cand_end - [&] {
-    int k = 0;
-    for (int f = 0; f < ri.nforced; ++f) k += ri.forced[f] < ri.cand_end ? 1 : 0;
-    return k;
-  }();
+  const int n_elig = ri.cand_end - ri.nforced_below(ri.cand_end);
   int m = a.k_total - ri.nforced;
   m = m < 0 ? 0 : m;
   auto get = [&](int e, uint32_t& key) -> bool {

@@ -10,9 +10,10 @@ namespace bsa {
 struct RowInfo {
   int cand_end;  // candidates are [0, cand_end)
   int own;       // the row's own block (diagonal / tail)
-  int forced[2];
+  int f0, f1;    // forced blocks, -1 when absent (scalars: no private array)
   int nforced;
-  int span;  // every block id that can appear in the selection is < span
+  int span;      // every block id that can appear in the selection is < span
+  __device__ int nforced_below(int n) const { return (f0 >= 0 && f0 < n) + (f1 >= 0 && f1 < n); }
 };
 
 // Candidate range and forced blocks of one routing row, as documented in bsa.h.
@@ -27,17 +28,16 @@ __device__ inline RowInfo row_info(const RowRule& r, int b, int row) {
     ri.own = static_cast<int>((L - 1) / r.B);
     ri.cand_end = ri.own;
   }
-  ri.nforced = 0;
-  if (r.force & 2u) ri.forced[ri.nforced++] = 0;
+  const bool first = (r.force & 2u) != 0;
   const bool own_forced = (r.force & 1u) || (r.mode == 1 && (r.force & 4u));
-  if (own_forced && !(ri.nforced == 1 && ri.forced[0] == ri.own)) ri.forced[ri.nforced++] = ri.own;
+  ri.f0 = first ? 0 : (own_forced ? ri.own : -1);
+  ri.f1 = (first && own_forced && ri.own != 0) ? ri.own : -1;
+  ri.nforced = (ri.f0 >= 0) + (ri.f1 >= 0);
   ri.span = ri.own + 1 > ri.cand_end ? ri.own + 1 : ri.cand_end;
   return ri;
 }
 
-__device__ inline bool is_forced(const RowInfo& ri, int j) {
-  return (ri.nforced > 0 && ri.forced[0] == j) || (ri.nforced > 1 && ri.forced[1] == j);
-}
+__device__ inline bool is_forced(const RowInfo& ri, int j) { return j == ri.f0 || j == ri.f1; }
 
 // ---------------------------------------------------------------------------
 // Workgroup-wide helpers for NT threads.
@@ -155,6 +155,56 @@ __device__ inline int select_and_write(const RowInfo& ri, int span, int m, int n
   }
   for (int p = carry_sel + static_cast<int>(threadIdx.x); p < width; p += NT) out(p, -1);
   return carry_sel < width ? carry_sel : width;
+}
+
+}  // namespace bsa
+
+namespace bsa {
+
+// Exact top-m of up to 64*E elements held by one wavefront: element e of lane
+// l is element number e*64 + l, and that number must follow the block-id order
+// (lower number = lower id), so ties resolve toward the lower id.  Finds the
+// m-th largest key with an MSB-first bitwise search (ballot counts, no LDS,
+// no barriers), then takes every larger key and the first `need` equal keys.
+// sel[e] is set for the selected elements; returns how many were selected.
+template <int E>
+__device__ inline int wave_topm(const uint32_t (&key)[E], const bool (&valid)[E], int m,
+                                bool (&sel)[E]) {
+  int nvalid = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) nvalid += __popcll(__ballot(valid[e]));
+  if (m >= nvalid) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) sel[e] = valid[e];
+    return nvalid;
+  }
+  if (m <= 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) sel[e] = false;
+    return 0;
+  }
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) c += __popcll(__ballot(valid[e] && key[e] >= cand));
+    if (c >= m) T = cand;
+  }
+  int greater = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) greater += __popcll(__ballot(valid[e] && key[e] > T));
+  const int need = m - greater;
+  int before = 0;  // tied elements with a lower element number
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool tie = valid[e] && key[e] == T;
+    const uint64_t mk = __ballot(tie);
+    const int rank = before + lanes_below(mk);
+    sel[e] = valid[e] && (key[e] > T || (tie && rank < need));
+    before += __popcll(mk);
+  }
+  return m;
 }
 
 }  // namespace bsa

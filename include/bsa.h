@@ -84,7 +84,8 @@ typedef enum {
   BSA_OP_ROUTE_TOPK = 1,
   BSA_OP_ROUTE_ENTMAX = 2,
   BSA_OP_ATTEND_PREFILL = 3,
-  BSA_OP_ATTEND_DECODE = 4
+  BSA_OP_ATTEND_DECODE = 4,
+  BSA_OP_DECODE_TOPK = 5
 } bsa_op;
 
 /* Problem description, read only during the call. */
@@ -135,6 +136,9 @@ int bsa_summarize(const bsa_shape *shape, const void *K, const float *qbar, floa
  *   cnt   out int32 [batch, Hkv, n_rows].
  *   scores_out  NULL, or fp32 [batch, Hkv, n_rows, n_blk]: candidate scores,
  *         -inf for non-candidates.
+ *   ws    prefill: bsa_workspace_size(BSA_OP_ROUTE_TOPK, ...) bytes.  Decode:
+ *         with that much ws the summaries are scored by several workgroups
+ *         per row (partitioned); with ws NULL one workgroup per row routes.
  * Errors: BSA_ERR_INVALID (k_total < #forced or < 1, TAIL in prefill, null
  * pointers, bad shape), BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
  */
@@ -199,16 +203,27 @@ int bsa_attend_decode(const bsa_shape *shape, const void *Q, const void *K, cons
                       size_t ws_bytes, void *stream);
 
 /*
- * Decode step in one launch: top-k routing over the cached summaries S
- * (exactly as bsa_route_topk in decode mode) followed by bsa_attend_decode on
- * that selection, without the selection leaving the chip.
+ * Decode step: top-k routing over the cached summaries S (exactly as
+ * bsa_route_topk in decode mode) followed by attention on that selection
+ * (as bsa_attend_decode), without the selection round-tripping through the
+ * caller.  When the GQA group has at most 8 query heads and fewer than 256
+ * blocks are routed, every (batch, KV head) row is served by several
+ * workgroups over disjoint data: a routing kernel keeps each summary slice's
+ * exact local top-k in ws, and an attention kernel merges them, attends its
+ * share of the selected blocks into a partial softmax state in ws, and a
+ * combine kernel merges a row's partial states into O.  Otherwise one
+ * workgroup per row does everything in one launch and ws is unused.
  *   idx, cnt  NULL, or outputs as in bsa_route_topk (both or neither).
+ *   ws        bsa_workspace_size(BSA_OP_DECODE_TOPK, shape, k_total) bytes,
+ *             256-byte aligned; its contents need no initialisation and are
+ *             scratch afterwards.  Calls sharing one ws must not overlap.
  * Errors: as bsa_route_topk and bsa_attend_decode.
  */
 int bsa_decode_topk(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                     const float *S, const int32_t *kv_lens, int32_t k_total,
                     uint32_t force_flags, float score_scale, float sm_scale, int32_t *idx,
-                    int32_t *cnt, void *O, int32_t o_dtype, void *stream);
+                    int32_t *cnt, void *O, int32_t o_dtype, void *ws, size_t ws_bytes,
+                    void *stream);
 
 /* Scratch bytes needed by `op` for this shape; k_or_cap is k_total (top-k),
  * cap (entmax) or k_max (attend).  Returns 0 when none is needed or the

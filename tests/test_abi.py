@@ -124,9 +124,14 @@ def test_attend_validation():
     assert lib.bsa_attend_decode(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, FAKE, 4, 0.0, FAKE,
                                  bsa.BF16, None, 0, None) == -1
     assert lib.bsa_decode_topk(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, 4, bsa.FORCE_TAIL,
-                               0.0, 0.0, FAKE, None, FAKE, bsa.BF16, None) == -1 and "both" in err()
+                               0.0, 0.0, FAKE, None, FAKE, bsa.BF16, FAKE, 1 << 20,
+                               None) == -1 and "both" in err()
     assert lib.bsa_decode_topk(ctypes.byref(shape()), FAKE, FAKE, FAKE, FAKE, None, 4, 0,
-                               0.0, 0.0, None, None, FAKE, bsa.BF16, None) == -1 and "DECODE" in err()
+                               0.0, 0.0, None, None, FAKE, bsa.BF16, FAKE, 1 << 20,
+                               None) == -1 and "DECODE" in err()
+    assert lib.bsa_decode_topk(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, 4, bsa.FORCE_TAIL,
+                               0.0, 0.0, None, None, FAKE, bsa.BF16, FAKE, 16,
+                               None) == -4 and "workspace" in err()
 
 
 def test_workspace_sizes():
@@ -143,6 +148,14 @@ def test_workspace_sizes():
     d = shape(batch=16, hq=32, hkv=8, mode=bsa.DECODE, q_len=1, kv_len=131072)
     # decode attention runs in one launch without scratch
     assert lib.bsa_workspace_size(bsa.OP_ATTEND_DECODE, ctypes.byref(d), 33) == 0
+    # 128 rows: one fused launch, no scratch
+    assert lib.bsa_workspace_size(bsa.OP_DECODE_TOPK, ctypes.byref(d), 33) == 0
+    # 4 x 8 rows: 8 workgroups per row; candidates (keys + ids) and partial
+    # states for 4 heads
+    d = shape(batch=4, hq=32, hkv=8, mode=bsa.DECODE, q_len=1, kv_len=131072)
+    rows, parts, G = 4 * 8, 8, 4
+    want = 2 * al(rows * parts * 33 * 4) + al(rows * parts * G * 130 * 4)
+    assert lib.bsa_workspace_size(bsa.OP_DECODE_TOPK, ctypes.byref(d), 33) == want
 
 
 def test_error_string_is_thread_local_and_cleared():

@@ -253,22 +253,34 @@ def test_determinism_and_strides():
     assert torch.equal(i1, i3) and torch.equal(O1, O3)
 
 
-@pytest.mark.parametrize("name", list(DECODE))
-def test_route_topk_decode_fused_kernel(name):
-    """Decode routing without scores_out runs the single fused routing kernel."""
-    w = DECODE[name]
-    print(f"[route_topk fused decode] {name}", flush=True)
+DECODE_WIDE = {
+    # 16 query heads per KV head: the single-kernel decode path (heads split)
+    "decode_g16": W["bf16_decode_l128k"].scaled(batch=2, hq=16, hkv=1, n=64 * 33 + 5, k_total=7,
+                                                kv_lens=(64 * 33 + 5, 999)),
+    # more routed blocks than the partitioned path keeps
+    "decode_k300": W["bf16_decode_l128k"].scaled(batch=1, hq=4, hkv=1, n=64 * 400, k_total=301,
+                                                 kv_lens=(64 * 400,)),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE) + list(DECODE_WIDE))
+@pytest.mark.parametrize("partitioned", [True, False])
+def test_route_topk_decode_kernels(name, partitioned):
+    """Decode routing without scores_out: partitioned kernels (with workspace)
+    or the single-workgroup-per-row kernel (without)."""
+    w = {**DECODE, **DECODE_WIDE}[name]
+    print(f"[route_topk decode] {name} partitioned={partitioned}", flush=True)
     x = parity.make(w)
     S = bsa.summarize(x["K"], w.B)
     idx, cnt = bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, decode=True, kv_len=w.n,
-                              kv_lens=_kv_lens_dev(w))
+                              kv_lens=_kv_lens_dev(w), partitioned=partitioned)
     parity.check_topk_rows(w, _cpu(idx), _cpu(cnt), _route_ref(w, x))
 
 
-@pytest.mark.parametrize("name", list(DECODE))
+@pytest.mark.parametrize("name", list(DECODE) + list(DECODE_WIDE))
 @pytest.mark.parametrize("out_f32", [False, True])
-def test_decode_step_single_launch(name, out_f32):
-    w = DECODE[name]
+def test_decode_step(name, out_f32):
+    w = {**DECODE, **DECODE_WIDE}[name]
     print(f"[decode_step] {name} out_f32={out_f32}", flush=True)
     x = parity.make(w)
     S = bsa.summarize(x["K"], w.B)
@@ -279,8 +291,10 @@ def test_decode_step_single_launch(name, out_f32):
     ref, _ = oracle.attend(x["q"], x["k"], x["v"], w.B, _cpu(idx), _cpu(cnt),
                            mode=oracle.MODE_DECODE, kv_lens=w.lens())
     parity.check_attention(w, _cpu(O).reshape(ref.shape), ref, out_f32 or w.dtype == "f32")
-    # without selection outputs the result is identical
-    O2, _, _ = bsa.decode_step(x["Q"], x["K"], x["V"], S, w.B, w.k_total, w.force,
-                               kv_lens=_kv_lens_dev(w), want_selection=False,
-                               out_dtype=torch.float32 if out_f32 else None)
-    assert torch.equal(O, O2)
+    # without selection outputs, and on a reused (dirty) workspace, the result is identical
+    ws = torch.full((1 << 22,), 255, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        O2, _, _ = bsa.decode_step(x["Q"], x["K"], x["V"], S, w.B, w.k_total, w.force,
+                                   kv_lens=_kv_lens_dev(w), want_selection=False, ws=ws,
+                                   out_dtype=torch.float32 if out_f32 else None)
+        assert torch.equal(O, O2)
