@@ -1,11 +1,15 @@
 // Stage 1: block routing.
 //
-//   scores_kernel   coarse scores of every candidate block against the row's
-//                   routing query ("DashAttention", Declaração do Problema:
+//   scores_tiled    coarse scores of every candidate block against the row's
+//   scores_kernel   routing query ("DashAttention", Declaração do Problema:
 //                   coarse attention scores between queries and block
 //                   summaries).  fp32 throughout: selections must agree with
 //                   an fp64 reference whenever the k-th/(k+1)-th gap exceeds
-//                   1e-4, so no reduced-precision matrix cores here.
+//                   1e-4, so no reduced-precision matrix cores here.  Prefill
+//                   rows of one KV head share its summaries, so the scores are
+//                   a small GEMM tiled 64 x 64 through LDS (scores_tiled);
+//                   decode rows each have their own summaries and are a GEMV
+//                   streamed from memory (scores_kernel).
 //   select_kernel   top-k with forced blocks and the lower-index tie rule
 //                   ("Gist Sparse Attention", section 2 item 3).  Exact radix
 //                   select on order-preserving uint32 keys (4 passes of 8
@@ -29,8 +33,9 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 128;  // candidate blocks scored per workgroup
 
 // ---------------------------------------------------------------------------
-// Coarse scores.  d/4 lanes share one summary row (a float4 each); the dot is
-// finished with a butterfly over those lanes.
+// Decode scores (one row per (b, g), its own summaries).  d/4 lanes share one
+// summary row (a float4 each); the dot is finished with a butterfly over those
+// lanes.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
@@ -64,6 +69,91 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
       s = p * a.scale;
     }
     if (c == 0) out[j] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill scores: one workgroup per 64 rows x 64 blocks tile of one (b, g).
+// The q-hat and summary tiles are staged in LDS (rows padded by 4 floats);
+// thread (tr, tj) accumulates rows tr + 16m and blocks tj + 16n, m, n < 4.
+// Tiles right of every row's candidates only write -inf (the candidate end
+// grows with the row in prefill).
+// ---------------------------------------------------------------------------
+constexpr int kTile = 64;
+constexpr int kPad = 4;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
+  __shared__ float qs[kTile][D + kPad];
+  __shared__ float ss[kTile][D + kPad];
+  const int nrt = (a.nrow + kTile - 1) / kTile;
+  const int njt = (a.nblk + kTile - 1) / kTile;
+  int id = blockIdx.x;
+  const int jt = id % njt;
+  id /= njt;
+  const int rt = id % nrt;
+  const int bg = id / nrt;
+  const int b = bg / a.hkv;
+  const int r0 = rt * kTile, j0 = jt * kTile;
+  const int rn = a.nrow - r0 < kTile ? a.nrow - r0 : kTile;
+  const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  float* out = a.scores + (static_cast<int64_t>(bg) * a.nrow + r0) * a.nblk + j0;
+  if (j0 >= r0 + rn - (a.rule.entmax ? 1 : 0)) {  // right of the last row's candidates
+    for (int e = tid; e < kTile * kTile; e += kThreads) {
+      const int r = e / kTile, j = e % kTile;
+      if (r < rn && j < jn) out[static_cast<int64_t>(r) * a.nblk + j] = -INFINITY;
+    }
+    return;
+  }
+  constexpr int V4 = D / 4;
+  const float* qg = a.qhat + (static_cast<int64_t>(bg) * a.nrow + r0) * D;
+  const float* sg = a.S + (static_cast<int64_t>(bg) * a.nblk + j0) * D;
+  // rows past the ends read as zeros (buffer loads outside the extent)
+  const auto rq = make_rsrc(qg, static_cast<uint32_t>(rn) * D * 4);
+  const auto rs = make_rsrc(sg, static_cast<uint32_t>(jn) * D * 4);
+  for (int e = tid; e < kTile * V4; e += kThreads) {
+    const int r = e / V4, c = e % V4;
+    *reinterpret_cast<uint4*>(&qs[r][c * 4]) = buf_load16(rq, static_cast<uint32_t>(e) * 16);
+    *reinterpret_cast<uint4*>(&ss[r][c * 4]) = buf_load16(rs, static_cast<uint32_t>(e) * 16);
+  }
+  __syncthreads();
+  const int tr = w * 4 + lane / 16, tj = lane % 16;
+  float acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = 0.f;
+#pragma unroll 2
+  for (int k = 0; k < D; k += 4) {
+    float4 qv[4], sv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) qv[m] = *reinterpret_cast<const float4*>(&qs[tr + 16 * m][k]);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) sv[n] = *reinterpret_cast<const float4*>(&ss[tj + 16 * n][k]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        float t = acc[m][n];
+        t = fmaf(qv[m].x, sv[n].x, t);
+        t = fmaf(qv[m].y, sv[n].y, t);
+        t = fmaf(qv[m].z, sv[n].z, t);
+        t = fmaf(qv[m].w, sv[n].w, t);
+        acc[m][n] = t;
+      }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int r = tr + 16 * m;
+    // prefill: the candidates of row r0 + r are [0, r0 + r) or [0, r0 + r + 1)
+    const int cend = r0 + r + (a.rule.entmax ? 0 : 1) - j0;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int j = tj + 16 * n;
+      if (r < rn && j < jn)
+        out[static_cast<int64_t>(r) * a.nblk + j] = j < cend ? acc[m][n] * a.scale : -INFINITY;
+    }
   }
 }
 
@@ -347,6 +437,16 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
 }  // namespace
 
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
+  if (a.rule.mode == 0) {
+    const unsigned tiles = static_cast<unsigned>((a.nrow + kTile - 1) / kTile) *
+                           static_cast<unsigned>((a.nblk + kTile - 1) / kTile);
+    const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * tiles;
+    if (a.d == 64)
+      hipLaunchKernelGGL(scores_tiled<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(scores_tiled<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   const int nchunk = (a.nblk + kChunk - 1) / kChunk;
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow * nchunk;
   if (a.d == 64)
