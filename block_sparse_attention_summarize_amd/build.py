@@ -18,6 +18,10 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "pool.hip", "route.hip", "attend.hip", "decode.hip"]
+# The attention kernels mask with -inf and never produce NaN on finite
+# inputs; without NaNs to honour, fmaxf lowers to bare v_max/v_max3 instead
+# of first quieting every MFMA result (one extra VALU op per input).
+EXTRA_FLAGS = {"attend.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
 
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
@@ -29,7 +33,7 @@ COMMON_FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -117,6 +117,9 @@ __device__ __forceinline__ float xmax16(float v) {
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
+}
 constexpr int kMaxTiles = 1024;  // tile-list chunk staged in LDS
 
 // QT query tiles of 16 per wavefront, NW wavefronts per workgroup.  A "unit"
@@ -314,10 +317,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
         bool grow = false;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          float v = -INFINITY;
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-            v = fmaxf(v, fmaxf(fmaxf(s[kt][qt][0], s[kt][qt][1]), fmaxf(s[kt][qt][2], s[kt][qt][3])));
+          // 16 values in 8 three-input maxes
+          const float t0 = max3f(s[0][qt][0], s[0][qt][1], s[0][qt][2]);
+          const float t1 = max3f(s[0][qt][3], s[1][qt][0], s[1][qt][1]);
+          const float t2 = max3f(s[1][qt][2], s[1][qt][3], s[2][qt][0]);
+          const float t3 = max3f(s[2][qt][1], s[2][qt][2], s[2][qt][3]);
+          const float t4 = max3f(s[3][qt][0], s[3][qt][1], s[3][qt][2]);
+          const float t5 = max3f(t0, t1, t2);
+          const float t6 = max3f(t3, t4, s[3][qt][3]);
+          float v = fmaxf(t5, t6);
           v = xmax16(v);
           mx[qt] = v * sc;
           grow |= mx[qt] > m[qt] + kRescale;
