@@ -4,11 +4,13 @@
 //
 //   attend_prefill_bf16   gathered-KV causal prefill on bf16 MFMA.
 //                         A workgroup (4 wavefronts) owns one (batch, KV head,
-//                         query block) and up to 4 "units" of 64 queries x one
+//                         query block) and up to 4 "units" of 32 queries x one
 //                         query head of the GQA group, so every K/V tile it
-//                         stages in LDS serves the whole group.  S^T = K Q^T
+//                         stages in LDS serves several heads.  S^T = K Q^T
 //                         and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16
 //                         with fp32 accumulation; the online softmax is fp32.
+//                         V stays row-major in LDS and its transposed MFMA
+//                         operand comes from ds_read_b64_tr_b16.
 //   attend_prefill_f32    fp32 inputs: one query per lane, VALU dot products
 //                         (fp32 matrix rate is not the bound at these sizes).
 // Single-token decode lives in decode.hip.
@@ -21,23 +23,13 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Position of key r (0..63) of a tile inside a transposed V row.  The S^T
-// accumulator of 16x16 tile kt leaves lane l holding keys 16kt + 4(l/16) + j
-// (j = 0..3); the PV step consumes 32 keys per MFMA with lane l supplying
-// 8 of them, so keys {32kk + 4G + j} and {32kk + 16 + 4G + j} (G = l/16) are
-// stored next to each other and one 16-byte LDS read fetches them.
-__device__ __forceinline__ int vt_pos(int r) {
-  const int kk = r >> 5, q = r & 31;
-  const int hi = q >> 4, rr = q & 15;
-  return 32 * kk + 8 * (rr >> 2) + 4 * hi + (rr & 3);
 }
 
 // Walk of the selected blocks as 64-key tiles: tile index T covers block
@@ -66,12 +58,13 @@ struct TileWalk {
   }
 };
 
+// Double-buffered K and V tiles, both row-major (64 keys x D), rows padded
+// by 8 bf16 so that the fragment reads of 16 rows spread over the banks.
 template <int D>
 struct PrefillLds {
-  static constexpr int KST = D + 8;   // K tile row stride (bf16 elements)
-  static constexpr int VST = 64 + 8;  // transposed V row stride
+  static constexpr int KST = D + 8;  // row stride (bf16 elements)
   alignas(16) uint16_t k[2][64 * KST];
-  alignas(16) uint16_t v[2][D * VST];
+  alignas(16) uint16_t v[2][64 * KST];
 };
 
 // Map workgroup id -> (pair = b*hkv + g, query block i, sub-unit).  Heavy
@@ -133,9 +126,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   constexpr int KS = D / 32;    // k-steps of S^T = K Q^T
   constexpr int DT = D / 16;    // 16-row d tiles of O^T
   constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int KTOT = 64 * CPR, VTOT = 32 * CPR;  // 16-byte K chunks, V key-pair chunks
-  constexpr int KITEMS = (KTOT + NT - 1) / NT;     // per thread
-  constexpr int VITEMS = (VTOT + NT - 1) / NT;
+  constexpr int KTOT = 64 * CPR;                // 16-byte chunks per K (or V) tile
+  constexpr int KITEMS = (KTOT + NT - 1) / NT;  // per thread
   __shared__ PrefillLds<D> lds;
   __shared__ int lds_tiles[kMaxTiles];
   __shared__ int lds_ntiles;
@@ -203,7 +195,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
 
   uint4 kreg[KITEMS];
-  uint4 vreg[VITEMS][2];
+  uint4 vreg[KITEMS];
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < KITEMS; ++it) {
@@ -213,13 +205,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
         kreg[it] = buf_load16(rk, static_cast<uint32_t>(k0 + r) * kst + c * 16);
     }
 #pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
+    for (int it = 0; it < KITEMS; ++it) {
       const int flat = tid + NT * it;
-      if (VTOT % NT != 0 && flat >= VTOT) continue;
-      const int kp = flat % 32, c = flat / 32;
-      const uint32_t t = static_cast<uint32_t>(k0 + 2 * kp);
-      vreg[it][0] = buf_load16(rv, t * vst + c * 16);
-      vreg[it][1] = buf_load16(rv, (t + 1) * vst + c * 16);
+      const int r = flat / CPR, c = flat % CPR;
+      if (KTOT % NT == 0 || flat < KTOT)
+        vreg[it] = buf_load16(rv, static_cast<uint32_t>(k0 + r) * vst + c * 16);
     }
   };
   auto store_tile = [&](int buf) {
@@ -231,21 +221,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
         *reinterpret_cast<uint4*>(&lds.k[buf][r * L::KST + c * 8]) = kreg[it];
     }
 #pragma unroll
-    for (int it = 0; it < VITEMS; ++it) {
+    for (int it = 0; it < KITEMS; ++it) {
       const int flat = tid + NT * it;
-      if (VTOT % NT != 0 && flat >= VTOT) continue;
-      const int kp = flat % 32, c = flat / 32;
-      const int pos = vt_pos(2 * kp);
-      const uint32_t a0[4] = {vreg[it][0].x, vreg[it][0].y, vreg[it][0].z, vreg[it][0].w};
-      const uint32_t a1[4] = {vreg[it][1].x, vreg[it][1].y, vreg[it][1].z, vreg[it][1].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // d = 8c + 2e (low halves) and 8c + 2e + 1 (high halves)
-        const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-        *reinterpret_cast<uint32_t*>(&lds.v[buf][(c * 8 + 2 * e) * L::VST + pos]) = lo;
-        *reinterpret_cast<uint32_t*>(&lds.v[buf][(c * 8 + 2 * e + 1) * L::VST + pos]) = hi;
-      }
+      const int r = flat / CPR, c = flat % CPR;
+      if (KTOT % NT == 0 || flat < KTOT)
+        *reinterpret_cast<uint4*>(&lds.v[buf][r * L::KST + c * 8]) = vreg[it];
     }
   };
 
@@ -364,8 +344,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
           for (int qt = 0; qt < QT; ++qt) lsum[qt] = mfma16(ones, pf[qt][kk], lsum[qt]);
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const uint4 vf = *reinterpret_cast<const uint4*>(
-                &lds.v[buf][(dt * 16 + (lane & 15)) * L::VST + kk * 32 + (lane >> 4) * 8]);
+            // V^T fragment by two transposing reads of the row-major V tile:
+            // keys 32kk + 4G + e and 32kk + 16 + 4G + e (G = lane/16) for
+            // column 16dt + lane%16, the key order of the P fragment
+            const int s16 = lane & 15;
+            const uint16_t* vp = &lds.v[buf][(kk * 32 + (lane >> 4) * 4 + (s16 >> 2)) * L::KST +
+                                             dt * 16 + 4 * (s16 & 3)];
+            typedef __attribute__((address_space(3))) v4i16 lds_v4;
+            const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp));
+            const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 16 * L::KST));
+            const uint2 u0 = __builtin_bit_cast(uint2, r0), u1 = __builtin_bit_cast(uint2, r1);
+            const uint4 vf = make_uint4(u0.x, u0.y, u1.x, u1.y);
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf, pf[qt][kk], o[dt][qt]);
           }
