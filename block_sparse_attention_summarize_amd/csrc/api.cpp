@@ -379,6 +379,8 @@ int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int3
   sa.scores = scores;
   sa.batch = s->batch;
   sa.hkv = s->n_kv_heads;
+  sa.qheads = s->n_kv_heads;  // q-hat summed over each group
+  sa.group = 1;
   sa.nrow = nrow;
   sa.nblk = nblk;
   sa.d = s->head_dim;
@@ -441,9 +443,24 @@ int bsa_route_entmax(const bsa_shape* s, const void* Q, const float* S, const in
   if (e != hipSuccess) return device_status(e, "route_entmax/qpool");
   const float scale =
       score_scale != 0.f ? score_scale : 1.f / std::sqrt(static_cast<float>(s->head_dim));
+  // logits x = (alpha - 1) gamma score_scale q-hat . s of every query head,
+  // -inf outside the candidates
+  bsa::ScoreArgs sa;
+  sa.qhat = qhat;
+  sa.S = S;
+  sa.scores = xbuf;
+  sa.batch = s->batch;
+  sa.hkv = s->n_kv_heads;
+  sa.qheads = s->n_q_heads;
+  sa.group = s->n_q_heads / s->n_kv_heads;
+  sa.nrow = nrow;
+  sa.nblk = nblk;
+  sa.d = s->head_dim;
+  sa.scale = (alpha - 1.f) * gamma * scale;
+  sa.rule = rule_of(s, 1, force, kv_lens);
+  e = bsa::launch_scores(sa, st);
+  if (e != hipSuccess) return device_status(e, "route_entmax/scores");
   bsa::EntmaxArgs ea;
-  ea.qhat = qhat;
-  ea.S = S;
   ea.idx = idx;
   ea.cnt = cnt;
   ea.probs = probs_out;
@@ -454,12 +471,10 @@ int bsa_route_entmax(const bsa_shape* s, const void* Q, const float* S, const in
   ea.hkv = s->n_kv_heads;
   ea.nrow = nrow;
   ea.nblk = nblk;
-  ea.d = s->head_dim;
   ea.width = cap + popcount3(force);
   ea.cap = cap;
   ea.max_iter = max_iter;
   ea.alpha = alpha;
-  ea.xscale = (alpha - 1.f) * gamma * scale;
   ea.rule = rule_of(s, 1, force, kv_lens);
   return device_status(bsa::launch_route_entmax(ea, st), "route_entmax");
 }

@@ -48,11 +48,14 @@ struct RowRule {
 };
 
 // scores[row, j] = scale * qhat[row] . S[b, g, j] for candidate j, -inf else.
+// qhat holds `qheads` heads per batch (the KV heads for top-k, whose q-hat is
+// already summed over the group, or the query heads for entmax); head h reads
+// the summaries of KV head h / group.
 struct ScoreArgs {
-  const float* qhat;  // [batch, hkv, nrow, d]
+  const float* qhat;  // [batch, qheads, nrow, d]
   const float* S;     // [batch, hkv, nblk, d]
-  float* scores;      // [batch, hkv, nrow, nblk]
-  int batch, hkv, nrow, nblk, d;
+  float* scores;      // [batch, qheads, nrow, nblk]
+  int batch, hkv, qheads, group, nrow, nblk, d;
   float scale;
   RowRule rule;
 };
@@ -68,15 +71,14 @@ struct SelectArgs {
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream);
 
 struct EntmaxArgs {
-  const float* qhat;  // [batch, hq, nrow, d]
-  const float* S;     // [batch, hkv, nblk, d]
   int32_t* idx;       // [batch, hkv, nrow, width]
   int32_t* cnt;
   float* probs;       // optional [batch, hq, nrow, nblk]
   float* tau;         // optional [batch, hq, nrow]
-  float* xbuf;        // workspace [batch, hkv, nrow, G, nblk]
-  int batch, hq, hkv, nrow, nblk, d, width, cap, max_iter;
-  float alpha, xscale;  // x = xscale * qhat . s, xscale = (alpha-1)*gamma*score_scale
+  float* xbuf;        // logits from the scores kernel [batch, hq, nrow, nblk]; overwritten
+                      // with the probabilities
+  int batch, hq, hkv, nrow, nblk, width, cap, max_iter;
+  float alpha;
   RowRule rule;
 };
 hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream);

@@ -17,8 +17,9 @@
 //                   that resolves ties toward lower block ids and writes the
 //                   ascending list.
 //   entmax_kernel   alpha-entmax support per query head ("DashAttention",
-//                   Estágio 1) with the threshold bracketed by a 16-bin LDS
-//                   histogram and refined by bisection ("AdaSplash-2", 2.A),
+//                   Estágio 1) over logits produced by the scores kernels,
+//                   with the threshold bracketed by a 16-bin LDS histogram
+//                   and refined by bisection ("AdaSplash-2", 2.A),
 //                   GQA-averaged probabilities, cap by the same radix select.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -43,10 +44,11 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
   constexpr int RPW = kWave / LPR;     // rows per wave step
   const int nchunk = (a.nblk + kChunk - 1) / kChunk;
   const int chunk = blockIdx.x % nchunk;
-  const int rowid = blockIdx.x / nchunk;  // (b, g, row)
+  const int rowid = blockIdx.x / nchunk;  // (b, q-hat head, row)
   const int row = rowid % a.nrow;
-  const int bg = rowid / a.nrow;
-  const int b = bg / a.hkv;
+  const int bh = rowid / a.nrow;
+  const int b = bh / a.qheads;
+  const int bg = b * a.hkv + (bh % a.qheads) / a.group;
   const RowInfo ri = row_info(a.rule, b, row);
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
@@ -92,13 +94,14 @@ __global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
   const int jt = id % njt;
   id /= njt;
   const int rt = id % nrt;
-  const int bg = id / nrt;
-  const int b = bg / a.hkv;
+  const int bh = id / nrt;  // (b, q-hat head)
+  const int b = bh / a.qheads;
+  const int sg_row = b * a.hkv + (bh % a.qheads) / a.group;
   const int r0 = rt * kTile, j0 = jt * kTile;
   const int rn = a.nrow - r0 < kTile ? a.nrow - r0 : kTile;
   const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float* out = a.scores + (static_cast<int64_t>(bg) * a.nrow + r0) * a.nblk + j0;
+  float* out = a.scores + (static_cast<int64_t>(bh) * a.nrow + r0) * a.nblk + j0;
   if (j0 >= r0 + rn - (a.rule.entmax ? 1 : 0)) {  // right of the last row's candidates
     for (int e = tid; e < kTile * kTile; e += kThreads) {
       const int r = e / kTile, j = e % kTile;
@@ -107,8 +110,8 @@ __global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
     return;
   }
   constexpr int V4 = D / 4;
-  const float* qg = a.qhat + (static_cast<int64_t>(bg) * a.nrow + r0) * D;
-  const float* sg = a.S + (static_cast<int64_t>(bg) * a.nblk + j0) * D;
+  const float* qg = a.qhat + (static_cast<int64_t>(bh) * a.nrow + r0) * D;
+  const float* sg = a.S + (static_cast<int64_t>(sg_row) * a.nblk + j0) * D;
   // rows past the ends read as zeros (buffer loads outside the extent)
   const auto rq = make_rsrc(qg, static_cast<uint32_t>(rn) * D * 4);
   const auto rs = make_rsrc(sg, static_cast<uint32_t>(jn) * D * 4);
@@ -242,10 +245,7 @@ __device__ inline float solve_bins(const float* e, const int* c, float alpha) {
   return 0.5f * (lo + hi);
 }
 
-template <int D>
 __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
-  constexpr int LPR = D / 4;
-  constexpr int RPW = kWave / LPR;
   __shared__ int hist[256];
   __shared__ int bcast[2];
   __shared__ int wave_tot[kWaves];
@@ -260,25 +260,20 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int n = ri.cand_end;  // candidate range; forced ids inside are excluded
-  float* xrow = a.xbuf + static_cast<int64_t>(rowid) * G * a.nblk;
-  const float* Sg = a.S + static_cast<int64_t>(bg) * a.nblk * D;
+  // logits of head g*G + hh of this row, from the scores kernel
+  auto xrow_of = [&](int hh) {
+    return a.xbuf + ((static_cast<int64_t>(b) * a.hq + g * G + hh) * a.nrow + row) * a.nblk;
+  };
   const float alpha = a.alpha;
 
   for (int hh = w; hh < G; hh += kWaves) {
     const int h = g * G + hh;
     const int64_t hrow = (static_cast<int64_t>(b) * a.hq + h) * a.nrow + row;
-    float* x = xrow + static_cast<int64_t>(hh) * a.nblk;
-    // logits
-    const int c = lane % LPR;
-    const float4 q = reinterpret_cast<const float4*>(a.qhat + hrow * D)[c];
-    for (int j = lane / LPR; j < n; j += RPW) {
-      const float4 v = reinterpret_cast<const float4*>(Sg + static_cast<int64_t>(j) * D)[c];
-      float p = q.x * v.x;
-      p = fmaf(q.y, v.y, p);
-      p = fmaf(q.z, v.z, p);
-      p = fmaf(q.w, v.w, p);
-      p = group_sum<LPR>(p);
-      if (c == 0) x[j] = is_forced(ri, j) ? -INFINITY : p * a.xscale;
+    float* x = xrow_of(hh);
+    // forced blocks inside the candidate range take no part in the entmax
+    if (lane == 0) {
+      if (ri.f0 >= 0 && ri.f0 < n) x[ri.f0] = -INFINITY;
+      if (ri.f1 >= 0 && ri.f1 < n) x[ri.f1] = -INFINITY;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -406,9 +401,11 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
   // GQA: mean probability over the group's heads; keep the positive ones,
   // capped by the radix select.
   const float invG = 1.f / static_cast<float>(G);
+  const int64_t hstride = static_cast<int64_t>(a.nrow) * a.nblk;  // between heads
+  const float* xrow = xrow_of(0);
   auto wbar = [&](int e) {
     float s = 0.f;
-    for (int hh = 0; hh < G; ++hh) s += xrow[static_cast<int64_t>(hh) * a.nblk + e];
+    for (int hh = 0; hh < G; ++hh) s += xrow[static_cast<int64_t>(hh) * hstride + e];
     return s * invG;
   };
   int npos = 0;
@@ -440,7 +437,7 @@ hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
   if (a.rule.mode == 0) {
     const unsigned tiles = static_cast<unsigned>((a.nrow + kTile - 1) / kTile) *
                            static_cast<unsigned>((a.nblk + kTile - 1) / kTile);
-    const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * tiles;
+    const unsigned grid = static_cast<unsigned>(a.batch) * a.qheads * tiles;
     if (a.d == 64)
       hipLaunchKernelGGL(scores_tiled<64>, dim3(grid), dim3(kThreads), 0, stream, a);
     else
@@ -448,7 +445,7 @@ hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int nchunk = (a.nblk + kChunk - 1) / kChunk;
-  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow * nchunk;
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.qheads * a.nrow * nchunk;
   if (a.d == 64)
     hipLaunchKernelGGL(scores_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
@@ -464,10 +461,7 @@ hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
 
 hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow;
-  if (a.d == 64)
-    hipLaunchKernelGGL(entmax_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(entmax_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(entmax_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
