@@ -96,6 +96,11 @@ __device__ __forceinline__ float lane_sum(float v) {
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) { return group_max<kWave>(v); }
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

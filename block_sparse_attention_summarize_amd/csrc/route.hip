@@ -202,50 +202,70 @@ __device__ __forceinline__ float emass(float x, float t, float alpha) {
   return powf(d, 1.f / (alpha - 1.f));
 }
 
-// Root of sum_k c_k [e_k - tau]_+^(1/(alpha-1)) = 1 for 16 values e_k sorted
-// descending with counts c_k: sort-based closed forms for alpha in {1.5, 2},
-// 64 bisection steps on [e_0 - 1, e_0] otherwise.
-__device__ inline float solve_bins(const float* e, const int* c, float alpha) {
-  if (alpha == 2.f || alpha == 1.5f) {
-    float n = 0.f, s1 = 0.f, s2 = 0.f;
+// [x - t]_+^(1/(alpha-1)) in fp64 (the bracket and bisection state)
+__device__ __forceinline__ double emass_d(double x, double t, double alpha) {
+  const double d = x - t;
+  if (!(d > 0.0)) return 0.0;
+  if (alpha == 1.5) return d * d;
+  if (alpha == 2.0) return d;
+  return pow(d, 1.0 / (alpha - 1.0));
+}
+
+// Root of sum_k c_k [e_k - tau]_+^(1/(alpha-1)) = 1 for the 16 bin values
+// e_k = xm - (k + off) / 16 (descending) with counts c_k (in LDS): sort-based
+// closed forms for alpha in {1.5, 2}, 64 bisection steps on [e_0 - 1, e_0]
+// otherwise.  fp64: the closed forms cancel (1 - Q) when few bins are in the
+// support.
+struct BinVals {
+  double xm;
+  int off;
+  __device__ double operator[](int k) const { return xm - static_cast<double>(k + off) * 0.0625; }
+};
+__device__ inline double solve_bins(const BinVals& e, const int* c, double alpha) {
+  if (alpha == 2.0 || alpha == 1.5) {
+    double n = 0.0, s1 = 0.0;
     for (int r = 0; r < 16; ++r) {
       if (c[r] == 0) continue;
-      const float cr = static_cast<float>(c[r]);
+      const double cr = static_cast<double>(c[r]);
       n += cr;
       s1 += cr * e[r];
-      s2 += cr * e[r] * e[r];
-      float tau;
-      if (alpha == 2.f) {
-        tau = (s1 - 1.f) / n;
+      double tau;
+      if (alpha == 2.0) {
+        tau = (s1 - 1.0) / n;
       } else {
-        const float M = s1 / n;
-        float Q = 0.f;  // squared deviations, recomputed for accuracy
+        const double M = s1 / n;
+        double Q = 0.0;  // squared deviations, recomputed for accuracy
         for (int k = 0; k <= r; ++k) {
-          const float dv = e[k] - M;
-          Q += static_cast<float>(c[k]) * dv * dv;
+          const double dv = e[k] - M;
+          Q += static_cast<double>(c[k]) * dv * dv;
         }
-        if (Q > 1.f) continue;
-        tau = M - sqrtf((1.f - Q) / n);
+        if (Q > 1.0) continue;
+        tau = M - sqrt((1.0 - Q) / n);
       }
       int nx = r + 1;
       while (nx < 16 && c[nx] == 0) ++nx;
       if (tau < e[r] && (nx >= 16 || tau >= e[nx])) return tau;
     }
   }
-  float lo = e[0] - 1.f, hi = e[0];
+  double lo = e[0] - 1.0, hi = e[0];
   for (int it = 0; it < 64; ++it) {
-    const float mid = 0.5f * (lo + hi);
-    float f = 0.f;
-    for (int r = 0; r < 16; ++r) f += static_cast<float>(c[r]) * emass(e[r], mid, alpha);
-    if (f >= 1.f)
+    const double mid = 0.5 * (lo + hi);
+    double f = 0.0;
+    for (int r = 0; r < 16; ++r) f += static_cast<double>(c[r]) * emass_d(e[r], mid, alpha);
+    if (f >= 1.0)
       lo = mid;
     else
       hi = mid;
   }
-  return 0.5f * (lo + hi);
+  return 0.5 * (lo + hi);
 }
 
+// IN_LDS: the group's logit rows are copied once into LDS (G * nblk floats of
+// dynamic LDS) and every pass runs there; otherwise the passes read the
+// workspace rows in place.
+template <bool IN_LDS>
 __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
+  extern __shared__ float xsh[];
   __shared__ int hist[256];
   __shared__ int bcast[2];
   __shared__ int wave_tot[kWaves];
@@ -261,17 +281,28 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
   const int w = threadIdx.x / kWave;
   const int n = ri.cand_end;  // candidate range; forced ids inside are excluded
   // logits of head g*G + hh of this row, from the scores kernel
-  auto xrow_of = [&](int hh) {
+  auto grow_of = [&](int hh) {
     return a.xbuf + ((static_cast<int64_t>(b) * a.hq + g * G + hh) * a.nrow + row) * a.nblk;
   };
+  auto xrow_of = [&](int hh) {
+    return IN_LDS ? xsh + static_cast<int64_t>(hh) * a.nblk : grow_of(hh);
+  };
   const float alpha = a.alpha;
+  if constexpr (IN_LDS) {
+    for (int hh = 0; hh < G; ++hh) {
+      const float* src = grow_of(hh);
+      for (int j = threadIdx.x; j < n; j += kThreads)
+        xsh[hh * a.nblk + j] = is_forced(ri, j) ? -INFINITY : src[j];
+    }
+    __syncthreads();
+  }
 
   for (int hh = w; hh < G; hh += kWaves) {
     const int h = g * G + hh;
     const int64_t hrow = (static_cast<int64_t>(b) * a.hq + h) * a.nrow + row;
     float* x = xrow_of(hh);
     // forced blocks inside the candidate range take no part in the entmax
-    if (lane == 0) {
+    if (!IN_LDS && lane == 0) {
       if (ri.f0 >= 0 && ri.f0 < n) x[ri.f0] = -INFINITY;
       if (ri.f1 >= 0 && ri.f1 < n) x[ri.f1] = -INFINITY;
     }
@@ -305,23 +336,18 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
         }
       }
       __builtin_amdgcn_wave_barrier();
-      int cnts[16];
-      float edge[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) cnts[k] = bins[w][k];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) edge[k] = xmax - static_cast<float>(k + 1) * 0.0625f;
-      const float tau_lo = solve_bins(edge, cnts, alpha);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) edge[k] = xmax - static_cast<float>(k) * 0.0625f;
-      const float tau_hi = solve_bins(edge, cnts, alpha);
-      float lo = fmaxf(tau_lo, xmax - 1.f);
-      float hi = fminf(tau_hi, xmax - powf(static_cast<float>(ne), 1.f - alpha));
+      const double ad = alpha, xm = xmax;
+      // lower bin edges bound tau from below, upper edges from above
+      const double tau_lo = solve_bins(BinVals{xm, 1}, bins[w], ad);
+      const double tau_hi = solve_bins(BinVals{xm, 0}, bins[w], ad);
+      // bracket and bisection in fp64, like the threshold they converge to
+      double lo = fmax(tau_lo, xm - 1.0);
+      double hi = fmin(tau_hi, xm - pow(static_cast<double>(ne), 1.0 - ad));
       bool resolved = false;
       for (int it = 0;; ++it) {
         int inside = 0;
         for (int j = lane; j < n; j += kWave) {
-          const float v = x[j];
+          const double v = x[j];
           inside |= (v > lo && v <= hi) ? 1 : 0;
         }
         if (__ballot(inside) == 0) {
@@ -329,19 +355,21 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
           break;
         }
         if (it >= a.max_iter) break;
-        const float mid = 0.5f * (lo + hi);
-        float f = 0.f;
-        for (int j = lane; j < n; j += kWave) f += emass(x[j], mid, alpha);
-        f = wave_sum(f);
-        if (f >= 1.f)
+        const double mid = 0.5 * (lo + hi);
+        double f = 0.0;
+        for (int j = lane; j < n; j += kWave) f += emass_d(x[j], mid, ad);
+        f = wave_sum_d(f);
+        if (f >= 1.0)
           lo = mid;
         else
           hi = mid;
       }
-      tau = lo;
+      tau = static_cast<float>(lo);
       if (resolved) {
-        // exact threshold of the support {x > lo}
-        float s1 = 0.f;
+        // exact threshold of the support {x > lo}.  The closed forms are
+        // evaluated in fp64: for alpha = 1.5, 1 - Q cancels when the support
+        // is small, and fp32 would lose digits that tau itself does not lose.
+        double s1 = 0.0;
         int ns = 0;
         for (int j = lane; j < n; j += kWave) {
           const float v = x[j];
@@ -350,36 +378,36 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
             ++ns;
           }
         }
-        s1 = wave_sum(s1);
+        s1 = wave_sum_d(s1);
         ns = wave_sum_i(ns);
-        const float nsf = static_cast<float>(ns);
+        const double nsd = static_cast<double>(ns);
         if (alpha == 2.f) {
-          tau = (s1 - 1.f) / nsf;
+          tau = static_cast<float>((s1 - 1.0) / nsd);
         } else if (alpha == 1.5f) {
-          const float M = s1 / nsf;
-          float Q = 0.f;
+          const double M = s1 / nsd;
+          double Q = 0.0;
           for (int j = lane; j < n; j += kWave) {
-            const float v = x[j];
+            const double v = x[j];
             if (v > lo) Q += (v - M) * (v - M);
           }
-          Q = wave_sum(Q);
-          tau = M - sqrtf(fmaxf((1.f - Q) / nsf, 0.f));
+          Q = wave_sum_d(Q);
+          tau = static_cast<float>(M - sqrt(fmax((1.0 - Q) / nsd, 0.0)));
         } else {
-          float l2 = lo, h2 = lo + 1.f;  // the root is below max x <= lo + 1
+          double l2 = lo, h2 = lo + 1.0;  // the root is below max x <= lo + 1
           for (int it = 0; it < 64; ++it) {
-            const float mid = 0.5f * (l2 + h2);
-            float f = 0.f;
+            const double mid = 0.5 * (l2 + h2);
+            double f = 0.0;
             for (int j = lane; j < n; j += kWave) {
-              const float v = x[j];
-              if (v > lo) f += emass(v, mid, alpha);
+              const double v = x[j];
+              if (v > lo) f += emass_d(v, mid, ad);
             }
-            f = wave_sum(f);
-            if (f >= 1.f)
+            f = wave_sum_d(f);
+            if (f >= 1.0)
               l2 = mid;
             else
               h2 = mid;
           }
-          tau = 0.5f * (l2 + h2);
+          tau = static_cast<float>(0.5 * (l2 + h2));
         }
       }
       // probabilities, renormalised; stored over the logits
@@ -401,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
   // GQA: mean probability over the group's heads; keep the positive ones,
   // capped by the radix select.
   const float invG = 1.f / static_cast<float>(G);
-  const int64_t hstride = static_cast<int64_t>(a.nrow) * a.nblk;  // between heads
+  const int64_t hstride = IN_LDS ? a.nblk : static_cast<int64_t>(a.nrow) * a.nblk;  // between heads
   const float* xrow = xrow_of(0);
   auto wbar = [&](int e) {
     float s = 0.f;
@@ -461,7 +489,11 @@ hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
 
 hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow;
-  hipLaunchKernelGGL(entmax_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  const size_t dyn = static_cast<size_t>(a.hq / a.hkv) * a.nblk * sizeof(float);
+  if (dyn <= 64 * 1024)
+    hipLaunchKernelGGL(entmax_kernel<true>, dim3(grid), dim3(kThreads), dyn, stream, a);
+  else
+    hipLaunchKernelGGL(entmax_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

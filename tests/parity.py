@@ -64,6 +64,17 @@ def forced_set(w, b, row, kv_lens=None):
     return F
 
 
+def entmax_clear(w, ref):
+    """Head-rows whose entmax threshold is decided robustly: every logit is
+    more than GAP from tau, and the bisection resolved the support before its
+    last allowed step.  A support resolved only at the last step can flip to
+    unresolved (tau = the bracket's lower end) under a 1e-7 change of the
+    logits, e.g. their fp32 rounding, so its tau is compared for validity
+    only."""
+    early = (ref["resolved"] != 0) & (ref["iters"] < w.max_iter)
+    return (ref["margin"] > GAP) & (early | (w.max_iter == 0))
+
+
 def check_topk_rows(w, gidx, gcnt, ref, report=None):
     """Selections: exact where the gap rule applies, valid elsewhere."""
     idx, cnt, scores, gap = ref["idx"], ref["cnt"], ref["scores"], ref["gap"]
