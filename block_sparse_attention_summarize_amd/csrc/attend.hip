@@ -44,8 +44,9 @@ struct TileWalk {
   int64_t qmax;  // last query position of the workgroup
 
   // key0 of tile T, or -1 when the tile is invalid or entirely in the future.
-  __device__ __forceinline__ int64_t key0(int T) const {
-    const int j = list[T / nsub];
+  __device__ __forceinline__ int64_t key0(int T) const { return key0_of(list[T / nsub], T); }
+  // the same with the list entry j = list[T / nsub] already read
+  __device__ __forceinline__ int64_t key0_of(int j, int T) const {
     if (j < 0 || j >= nblk) return -1;
     const int64_t k0 = static_cast<int64_t>(j) * B + (T % nsub) * 64;
     if (k0 > qmax || k0 >= kv_len) return -1;
@@ -159,6 +160,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   int n = a.cnt[rowid];
   n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
   TileWalk walk{a.idx + rowid * a.k_max, n, nsub, a.B, a.nblk, a.kv_len, qmax};
+  // the first 64 list entries are read before the count arrives, so the two
+  // loads overlap instead of following each other
+  int jpre = -1;
+  if (w == 0 && lane < a.k_max * nsub) jpre = walk.list[lane / nsub];
 
   const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
                             head_bytes(a.kv_len, a.ks.t, D, 2));
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
       int c = 0;
       for (int r = 0; r < kMaxTiles && base + r < nraw; r += 64) {
         const int T = base + r + lane;
-        const int64_t k0 = T < nraw ? walk.key0(T) : -1;
+        const int64_t k0 = T >= nraw ? -1 : (T < 64 ? walk.key0_of(jpre, T) : walk.key0(T));
         const uint64_t mk = __ballot(k0 >= 0);
         if (k0 >= 0) lds_tiles[c + lanes_below(mk)] = static_cast<int>(k0);
         c += __popcll(mk);
