@@ -168,7 +168,8 @@ int decode_lds(const bsa_shape* s, int hsplit, int32_t width) {
   const int gs = gs_template((s->n_q_heads / s->n_kv_heads) / hsplit);
   const int64_t nblk = nblk_of(s);
   const int64_t f = bsa::decode_lds_floats(static_cast<int>(nblk), s->head_dim, gs);
-  if (nblk > (int64_t(1) << 24) || (f + width) * 4 > 96 * 1024) return -1;
+  if (nblk > (int64_t(1) << 24)) return -1;
+  if ((f + bsa::decode_sel_ints(static_cast<int>(nblk), width)) * 4 > 96 * 1024) return -1;
   return static_cast<int>(f);
 }
 

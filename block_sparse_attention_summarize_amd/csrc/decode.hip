@@ -70,18 +70,25 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   int64_t L = a.kv_lens ? static_cast<int64_t>(a.kv_lens[b]) : a.kv_len;
   L = L < 1 ? 1 : (L > a.kv_len ? a.kv_len : L);
   const T* Qb = static_cast<const T*>(a.Q) + b * a.qs.b;
+  const float scl = a.sm_scale * kLog2e;
+  auto qval = [&](int h, int c) {
+    const T* qp = Qb + h * a.qs.h;
+    if constexpr (sizeof(T) == 2)
+      return bf16_to_f32(qp[c]);
+    else
+      return static_cast<float>(qp[c]);
+  };
+  // the attention's query heads (scaled for exp2) and the routing query (the
+  // group's sum) are read together, before the summaries stream
+  for (int e = tid; e < gs * D; e += kNT) {
+    const int hh = e / D, c = e % D;
+    qa[hh][c] = qval(h0 + hh, c) * scl;
+  }
 
   if (a.route) {
-    // routing query: sum of the group's query heads
     for (int c = tid; c < D; c += kNT) {
       float s = 0.f;
-      for (int hh = 0; hh < G; ++hh) {
-        const T* qp = Qb + (g * G + hh) * a.qs.h;
-        if constexpr (sizeof(T) == 2)
-          s += bf16_to_f32(qp[c]);
-        else
-          s += qp[c];
-      }
+      for (int hh = 0; hh < G; ++hh) s += qval(g * G + hh, c);
       qh[c] = s;
     }
     __syncthreads();
@@ -142,18 +149,55 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
     };
     int32_t* gidx = a.idx ? a.idx + static_cast<int64_t>(row) * a.k_total : nullptr;
     const bool write = gidx != nullptr && hs == 0;
-    const int c = select_and_write<kNT>(
-        ri, ri.span, m, n_elig, get,
-        [&](int p, int e) {
-          sel[p] = e;
-          if (write) gidx[p] = e;
-        },
-        a.k_total, hist, bcast, wave_tot);
-    if (tid == 0) {
-      sel_n = c;
-      if (write && a.cnt) a.cnt[row] = c;
+    if (m < kSel) {
+      // per-wave exact top-m of 256-candidate slices, then of the survivors
+      // (ballot bit-splitting, two barriers per round); forced blocks added
+      // around the routed ids, which lie strictly between them
+      const int cap = ((n + kSel - 1) / kSel) * (m > 0 ? m : 1);
+      uint32_t* bk0 = reinterpret_cast<uint32_t*>(sel + a.k_total);
+      int32_t* bi0 = reinterpret_cast<int32_t*>(bk0 + cap);
+      uint32_t* bk1 = reinterpret_cast<uint32_t*>(bi0 + cap);
+      int32_t* bi1 = reinterpret_cast<int32_t*>(bk1 + cap);
+      uint32_t* fk = reinterpret_cast<uint32_t*>(bi1 + cap);
+      int32_t* fi = reinterpret_cast<int32_t*>(fk + a.k_total);
+      const int nr = m == 0 ? 0
+                            : tournament<kNT>(
+                                  n, m,
+                                  [&](int i, uint32_t& key, int32_t& id, bool& valid) {
+                                    valid = i < n && !is_forced(ri, i);
+                                    key = valid ? float_key(dyn[i]) : 0u;
+                                    id = i;
+                                  },
+                                  bk0, bi0, bk1, bi1, fk, fi, a.k_total);
+      const int lead = (ri.f0 == 0 && (a.force & 2u)) ? 1 : 0;
+      for (int q = tid; q < nr; q += kNT) sel[lead + q] = fi[q];
+      if (tid == 0) {
+        int c = lead + nr;
+        if (lead) sel[0] = 0;
+        if (!lead && ri.f0 >= 0) sel[c++] = ri.f0;
+        if (ri.f1 >= 0) sel[c++] = ri.f1;
+        sel_n = c;
+      }
+      __syncthreads();
+      if (write) {
+        const int c = sel_n;
+        for (int p = tid; p < a.k_total; p += kNT) gidx[p] = p < c ? sel[p] : -1;
+        if (tid == 0 && a.cnt) a.cnt[row] = c;
+      }
+    } else {
+      const int c = select_and_write<kNT>(
+          ri, ri.span, m, n_elig, get,
+          [&](int p, int e) {
+            sel[p] = e;
+            if (write) gidx[p] = e;
+          },
+          a.k_total, hist, bcast, wave_tot);
+      if (tid == 0) {
+        sel_n = c;
+        if (write && a.cnt) a.cnt[row] = c;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   } else {
     int c = a.cnt[row];
     c = c < 0 ? 0 : (c > a.k_total ? a.k_total : c);
@@ -164,18 +208,6 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   if (!a.attend) return;
 
   // ---- attention over the selected blocks for heads h0 .. h0+gs-1 ----
-  const float scl = a.sm_scale * kLog2e;
-  for (int e = tid; e < gs * D; e += kNT) {
-    const int hh = e / D, c = e % D;
-    const T* qp = Qb + (h0 + hh) * a.qs.h;
-    float v;
-    if constexpr (sizeof(T) == 2)
-      v = bf16_to_f32(qp[c]);
-    else
-      v = qp[c];
-    qa[hh][c] = v * scl;
-  }
-  __syncthreads();
   const int nsel = sel_n;
   const int cpb = a.B / CK;  // chunks per block
   const int nchunk = nsel * cpb;
@@ -330,7 +362,7 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
 
 template <typename T, int D, int GS>
 hipError_t launch_gs(const DecodeArgs& a, hipStream_t stream) {
-  const size_t dyn = static_cast<size_t>(a.lds_floats) * 4 + static_cast<size_t>(a.k_total) * 4;
+  const size_t dyn = (static_cast<size_t>(a.lds_floats) + decode_sel_ints(a.nblk, a.k_total)) * 4;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused<T, D, GS>),
@@ -359,6 +391,13 @@ int decode_lds_floats(int nblk, int d, int gs_max) {
   return nblk > merge ? nblk : merge;
 }
 
+int decode_sel_ints(int nblk, int k_total) {
+  // the selection, then (top-m below kSel) four tournament buffers and its
+  // output keys and ids
+  const long cap = ((static_cast<long>(nblk) + kSel - 1) / kSel) * (k_total > 0 ? k_total : 1);
+  return static_cast<int>(k_total + (k_total < kSel ? 4 * cap + 2 * k_total : 0));
+}
+
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream) {
   if (a.bf16) return a.d == 64 ? launch_t<uint16_t, 64>(a, stream) : launch_t<uint16_t, 128>(a, stream);
   return a.d == 64 ? launch_t<float, 64>(a, stream) : launch_t<float, 128>(a, stream);
@@ -382,8 +421,6 @@ hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream) {
 namespace bsa {
 namespace {
 
-constexpr int kSel = 256;  // elements per wave-level selection slice (4 per lane)
-
 __device__ __forceinline__ void part_map(int id, int rows, int parts, int& row, int& p) {
   if (rows % 8 == 0) {  // the parts of a row on one XCD (shared L2)
     const int x = id % 8, s = id / 8;
@@ -395,71 +432,6 @@ __device__ __forceinline__ void part_map(int id, int rows, int parts, int& row, 
   }
 }
 
-// Reduces `len` (key, id) candidates held in LDS in id order (src) to their
-// top-m, also in id order, by rounds of per-wave slice selections; returns
-// the final count.  The result is left in `out` (mpad entries, -1 padded).
-// Requires m < kSel.  `load(i, key, id, valid)` reads element i of the first
-// round's source.
-template <int NT, typename Load>
-__device__ int tournament(int len, int m, Load load, uint32_t* bufk0, int32_t* bufi0,
-                          uint32_t* bufk1, int32_t* bufi1, uint32_t* outk, int32_t* outi,
-                          int mpad) {
-  constexpr int NW = NT / kWave;
-  __shared__ int final_count;
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-  uint32_t* srck = nullptr;
-  int32_t* srci = nullptr;
-  uint32_t* dk = bufk0;
-  int32_t* di = bufi0;
-  bool first = true;
-  for (;;) {
-    const int nslice = (len + kSel - 1) / kSel;
-    const bool last = nslice <= 1;
-    for (int sl = w; sl < (nslice > 0 ? nslice : 1); sl += NW) {
-      uint32_t key[4];
-      int32_t id[4];
-      bool valid[4], sel[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = sl * kSel + e * kWave + lane;
-        if (first) {
-          load(i, key[e], id[e], valid[e]);
-          valid[e] = valid[e] && i < len;
-        } else {
-          valid[e] = i < len && srci[i] >= 0;
-          key[e] = valid[e] ? srck[i] : 0u;
-          id[e] = valid[e] ? srci[i] : -1;
-        }
-      }
-      wave_topm<4>(key, valid, m, sel);
-      uint32_t* ok = last ? outk : dk + sl * m;
-      int32_t* oi = last ? outi : di + sl * m;
-      const int width = last ? mpad : m;
-      int base = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint64_t mk = __ballot(sel[e]);
-        if (sel[e]) {
-          const int pos = base + lanes_below(mk);
-          ok[pos] = key[e];
-          oi[pos] = id[e];
-        }
-        base += __popcll(mk);
-      }
-      for (int q = base + lane; q < width; q += kWave) oi[q] = -1;
-      if (last && lane == 0) final_count = base;
-    }
-    __syncthreads();
-    if (last) break;
-    len = nslice * m;
-    srck = dk;
-    srci = di;
-    dk = (dk == bufk0) ? bufk1 : bufk0;
-    di = (di == bufi0) ? bufi1 : bufi0;
-    first = false;
-  }
-  return final_count;
-}
 
 template <int D>
 __global__ __launch_bounds__(kNT) void decode_route_part(DecodeArgs a) {

@@ -123,6 +123,7 @@ struct DecodeArgs {
   float* part;           // [rows, parts, G, d + 2] partial softmax states
 };
 int decode_lds_floats(int nblk, int d, int gs_max);
+int decode_sel_ints(int nblk, int k_total);  // LDS ints after the floats
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream);
 // Partitioned decode step: routing kernel then attention kernel.  With
 // attend = 0 the second kernel only merges the candidates into idx/cnt.

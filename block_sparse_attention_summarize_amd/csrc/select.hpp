@@ -207,4 +207,73 @@ __device__ inline int wave_topm(const uint32_t (&key)[E], const bool (&valid)[E]
   return m;
 }
 
+
+constexpr int kSel = 256;  // elements per wave-level selection slice (4 per lane)
+
+// Reduces `len` (key, id) candidates held in LDS in id order (src) to their
+// top-m, also in id order, by rounds of per-wave slice selections; returns
+// the final count.  The result is left in `out` (mpad entries, -1 padded).
+// Requires m < kSel.  `load(i, key, id, valid)` reads element i of the first
+// round's source.
+template <int NT, typename Load>
+__device__ int tournament(int len, int m, Load load, uint32_t* bufk0, int32_t* bufi0,
+                          uint32_t* bufk1, int32_t* bufi1, uint32_t* outk, int32_t* outi,
+                          int mpad) {
+  constexpr int NW = NT / kWave;
+  __shared__ int final_count;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  uint32_t* srck = nullptr;
+  int32_t* srci = nullptr;
+  uint32_t* dk = bufk0;
+  int32_t* di = bufi0;
+  bool first = true;
+  for (;;) {
+    const int nslice = (len + kSel - 1) / kSel;
+    const bool last = nslice <= 1;
+    for (int sl = w; sl < (nslice > 0 ? nslice : 1); sl += NW) {
+      uint32_t key[4];
+      int32_t id[4];
+      bool valid[4], sel[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = sl * kSel + e * kWave + lane;
+        if (first) {
+          load(i, key[e], id[e], valid[e]);
+          valid[e] = valid[e] && i < len;
+        } else {
+          valid[e] = i < len && srci[i] >= 0;
+          key[e] = valid[e] ? srck[i] : 0u;
+          id[e] = valid[e] ? srci[i] : -1;
+        }
+      }
+      wave_topm<4>(key, valid, m, sel);
+      uint32_t* ok = last ? outk : dk + sl * m;
+      int32_t* oi = last ? outi : di + sl * m;
+      const int width = last ? mpad : m;
+      int base = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t mk = __ballot(sel[e]);
+        if (sel[e]) {
+          const int pos = base + lanes_below(mk);
+          ok[pos] = key[e];
+          oi[pos] = id[e];
+        }
+        base += __popcll(mk);
+      }
+      for (int q = base + lane; q < width; q += kWave) oi[q] = -1;
+      if (last && lane == 0) final_count = base;
+    }
+    __syncthreads();
+    if (last) break;
+    len = nslice * m;
+    srck = dk;
+    srci = di;
+    dk = (dk == bufk0) ? bufk1 : bufk0;
+    di = (di == bufi0) ? bufi1 : bufi0;
+    first = false;
+  }
+  return final_count;
+}
+
 }  // namespace bsa
