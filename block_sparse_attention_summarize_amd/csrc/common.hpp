@@ -60,7 +60,6 @@ __device__ __forceinline__ float group_max(float v) {
   for (int o = width / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) { return group_sum<kWave>(v); }
 
 // Sums over W consecutive lanes (W in 8, 16, 32, 64) with DPP moves inside
 // 16-lane rows and gfx950 lane swaps across rows: VALU only, no LDS crossbar.
@@ -95,15 +94,53 @@ __device__ __forceinline__ float lane_sum(float v) {
   if constexpr (W >= 64) v = swap32_sum(v);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) { return group_max<kWave>(v); }
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// Whole-wave reductions with the same DPP / lane-swap sequence (every lane
+// ends with the result).  32-bit values move as they are; a double moves as
+// its two halves through the same permutation.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_u(uint32_t v, Op op) {
+  v = op(v, dppu<0xB1>(v));
+  v = op(v, dppu<0x4E>(v));
+  v = op(v, dppu<0x141>(v));
+  v = op(v, dppu<0x140>(v));
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r[0], r[1]);
+}
+__device__ __forceinline__ float wave_sum(float v) { return lane_sum<kWave>(v); }
+__device__ __forceinline__ float wave_max(float v) {
+  return __uint_as_float(wave_reduce_u(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+  }));
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
+  return static_cast<int>(wave_reduce_u(static_cast<uint32_t>(v), [](uint32_t x, uint32_t y) { return x + y; }));
+}
+template <int CTRL>
+__device__ __forceinline__ double dppd(double v) {
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  return __builtin_bit_cast(double, make_uint2(dppu<CTRL>(u.x), dppu<CTRL>(u.y)));
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += dppd<0xB1>(v);
+  v += dppd<0x4E>(v);
+  v += dppd<0x141>(v);
+  v += dppd<0x140>(v);
 #pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  for (int k = 0; k < 2; ++k) {
+    const uint2 u = __builtin_bit_cast(uint2, v);
+    const auto lo = k == 0 ? __builtin_amdgcn_permlane16_swap(u.x, u.x, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u.x, u.x, false, false);
+    const auto hi = k == 0 ? __builtin_amdgcn_permlane16_swap(u.y, u.y, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u.y, u.y, false, false);
+    v = __builtin_bit_cast(double, make_uint2(lo[0], hi[0])) +
+        __builtin_bit_cast(double, make_uint2(lo[1], hi[1]));
+  }
   return v;
 }
 

@@ -79,6 +79,7 @@ struct EntmaxArgs {
                       // with the probabilities
   int batch, hq, hkv, nrow, nblk, width, cap, max_iter;
   float alpha;
+  int tourn;  // set by the launcher: cap below the tournament slice and its buffers fit
   RowRule rule;
 };
 hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream);

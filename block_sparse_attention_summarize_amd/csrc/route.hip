@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
   }
   __syncthreads();
   // GQA: mean probability over the group's heads; keep the positive ones,
-  // capped by the radix select.
+  // capped (per-wave tournament below kSel, radix select otherwise).
   const float invG = 1.f / static_cast<float>(G);
   const int64_t hstride = IN_LDS ? a.nblk : static_cast<int64_t>(a.nrow) * a.nblk;  // between heads
   const float* xrow = xrow_of(0);
@@ -436,6 +436,44 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
     for (int hh = 0; hh < G; ++hh) s += xrow[static_cast<int64_t>(hh) * hstride + e];
     return s * invG;
   };
+  int32_t* idx = a.idx + static_cast<int64_t>(rowid) * a.width;
+  if (a.tourn) {
+    // buffers after the logit rows (if those are in LDS)
+    const int capb = ((n + kSel - 1) / kSel) * a.cap;
+    uint32_t* bk0 = reinterpret_cast<uint32_t*>(xsh + (IN_LDS ? G * a.nblk : 0));
+    int32_t* bi0 = reinterpret_cast<int32_t*>(bk0 + capb);
+    uint32_t* bk1 = reinterpret_cast<uint32_t*>(bi0 + capb);
+    int32_t* bi1 = reinterpret_cast<int32_t*>(bk1 + capb);
+    uint32_t* fk = reinterpret_cast<uint32_t*>(bi1 + capb);
+    int32_t* fi = reinterpret_cast<int32_t*>(fk + a.cap);
+    const int nr = tournament<kThreads>(
+        n, a.cap,
+        [&](int i, uint32_t& key, int32_t& id, bool& valid) {
+          float v = 0.f;
+          valid = false;
+          if (i < n && !is_forced(ri, i)) {
+            v = wbar(i);
+            valid = v > 0.f;
+          }
+          key = valid ? float_key(v) : 0u;
+          id = i;
+        },
+        bk0, bi0, bk1, bi1, fk, fi, a.cap);
+    // ascending: block 0 when forced first, the routed ids (strictly between
+    // the forced ones), then the row's own block when forced
+    const int lead = (ri.f0 == 0 && (a.rule.force & 2u)) ? 1 : 0;
+    const int tail0 = (!lead && ri.f0 >= 0) ? ri.f0 : -1;
+    const int total = lead + nr + (tail0 >= 0) + (ri.f1 >= 0);
+    for (int p = threadIdx.x; p < a.width; p += kThreads) {
+      int v = -1;
+      if (p < lead) v = 0;
+      else if (p < lead + nr) v = fi[p - lead];
+      else if (p < total) v = (p == lead + nr && tail0 >= 0) ? tail0 : ri.f1;
+      idx[p] = v;
+    }
+    if (threadIdx.x == 0) a.cnt[rowid] = total;
+    return;
+  }
   int npos = 0;
   for (int e = threadIdx.x; e < n; e += kThreads) npos += (!is_forced(ri, e) && wbar(e) > 0.f) ? 1 : 0;
   npos = wave_sum_i(npos);
@@ -452,7 +490,6 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
     key = float_key(v);
     return true;
   };
-  int32_t* idx = a.idx + static_cast<int64_t>(rowid) * a.width;
   const int c = select_and_write<kThreads>(
       ri, ri.span, a.cap, n_elig, get, [&](int p, int e) { idx[p] = e; }, a.width, hist, bcast,
       wave_tot);
@@ -489,11 +526,16 @@ hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
 
 hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow;
-  const size_t dyn = static_cast<size_t>(a.hq / a.hkv) * a.nblk * sizeof(float);
-  if (dyn <= 64 * 1024)
-    hipLaunchKernelGGL(entmax_kernel<true>, dim3(grid), dim3(kThreads), dyn, stream, a);
+  const size_t rows = static_cast<size_t>(a.hq / a.hkv) * a.nblk * sizeof(float);
+  const size_t capb = ((static_cast<size_t>(a.nblk) + kSel - 1) / kSel) * a.cap;
+  const size_t tb = (4 * capb + 2 * static_cast<size_t>(a.cap)) * 4;
+  EntmaxArgs b = a;
+  b.tourn = a.cap < kSel && tb <= 48 * 1024;
+  const size_t extra = b.tourn ? tb : 0;
+  if (rows + extra <= 64 * 1024)
+    hipLaunchKernelGGL(entmax_kernel<true>, dim3(grid), dim3(kThreads), rows + extra, stream, b);
   else
-    hipLaunchKernelGGL(entmax_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(entmax_kernel<false>, dim3(grid), dim3(kThreads), extra, stream, b);
   return hipGetLastError();
 }
 
