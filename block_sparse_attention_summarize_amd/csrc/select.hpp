@@ -167,15 +167,22 @@ namespace bsa {
 // m-th largest key with an MSB-first bitwise search (ballot counts, no LDS,
 // no barriers), then takes every larger key and the first `need` equal keys.
 // sel[e] is set for the selected elements; returns how many were selected.
+// Invalid elements take key 0, below every valid key (the order-preserving
+// key of a float is 0 only for a NaN with the sign bit set, which is treated
+// as invalid), so the search compares keys alone.
 template <int E>
 __device__ inline int wave_topm(const uint32_t (&key)[E], const bool (&valid)[E], int m,
                                 bool (&sel)[E]) {
+  uint32_t k[E];
   int nvalid = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) nvalid += __popcll(__ballot(valid[e]));
+  for (int e = 0; e < E; ++e) {
+    k[e] = valid[e] ? key[e] : 0u;
+    nvalid += __popcll(__ballot(k[e] != 0u));
+  }
   if (m >= nvalid) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) sel[e] = valid[e];
+    for (int e = 0; e < E; ++e) sel[e] = k[e] != 0u;
     return nvalid;
   }
   if (m <= 0) {
@@ -183,25 +190,27 @@ __device__ inline int wave_topm(const uint32_t (&key)[E], const bool (&valid)[E]
     for (int e = 0; e < E; ++e) sel[e] = false;
     return 0;
   }
+  // T ends as the m-th largest key: the largest value with >= m keys >= T
   uint32_t T = 0;
+#pragma unroll
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int c = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) c += __popcll(__ballot(valid[e] && key[e] >= cand));
-    if (c >= m) T = cand;
+    for (int e = 0; e < E; ++e) c += __popcll(__ballot(k[e] >= cand));
+    T = c >= m ? cand : T;
   }
   int greater = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) greater += __popcll(__ballot(valid[e] && key[e] > T));
+  for (int e = 0; e < E; ++e) greater += __popcll(__ballot(k[e] > T));
   const int need = m - greater;
   int before = 0;  // tied elements with a lower element number
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const bool tie = valid[e] && key[e] == T;
+    const bool tie = k[e] == T;
     const uint64_t mk = __ballot(tie);
     const int rank = before + lanes_below(mk);
-    sel[e] = valid[e] && (key[e] > T || (tie && rank < need));
+    sel[e] = k[e] > T || (tie && rank < need);
     before += __popcll(mk);
   }
   return m;
