@@ -38,7 +38,7 @@ OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECOD
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
-EXPORTS = ("bsa_summarize", "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill",
+EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill",
            "bsa_attend_decode", "bsa_decode_topk", "bsa_workspace_size", "bsa_last_error",
            "bsa_version")
 
@@ -61,6 +61,7 @@ _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 _SP = ctypes.POINTER(Shape)
 lib.bsa_summarize.argtypes = [_SP, _P, _P, _P, _P]
+lib.bsa_summarize_blocks.argtypes = [_SP, _P, _P, _P, _P, _P]
 lib.bsa_route_topk.argtypes = [_SP, _P, _P, _P, _i32, _u32, _f32, _P, _P, _P, _P, _sz, _P]
 lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, _u32, _f32, _P,
                                  _P, _P, _P, _P, _sz, _P]
@@ -164,6 +165,20 @@ def _route_shape(Q, S, B, decode, kv_len):
                           q_len=1, kv_len=kv_len, q=Q)
     return make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q), mode=PREFILL,
                       q_len=n, kv_len=n, q=Q)
+
+
+def summarize_blocks(K: torch.Tensor, B: int, blk: torch.Tensor, S: torch.Tensor,
+                     qbar: torch.Tensor | None = None) -> torch.Tensor:
+    """Recompute S[b, :, blk[b], :] of a cache K [b, Hkv, L, d] (blk int32 [b]
+    on the device; out-of-range entries skip their sequence).  Returns S."""
+    b, hkv, L, d = K.shape
+    shape = make_shape(batch=b, hq=hkv, hkv=hkv, d=d, B=B, dtype=_dtype_code(K), mode=PREFILL,
+                       q_len=L, kv_len=L, k=K)
+    if qbar is not None:
+        qbar = qbar.contiguous().to(torch.float32)
+    _check(lib.bsa_summarize_blocks(ctypes.byref(shape), _ptr(K), _ptr(qbar), _ptr(blk), _ptr(S),
+                                    _stream(K)))
+    return S
 
 
 def route_topk(Q, S, B, k_total, force=0, decode=False, kv_len=None, kv_lens=None,

@@ -303,6 +303,7 @@ int bsa_summarize(const bsa_shape* s, const void* K, const float* qbar, float* S
   a.ks = st3(s->k_stride);
   a.qbar = qbar;
   a.S = S;
+  a.blk = nullptr;
   a.batch = s->batch;
   a.hkv = s->n_kv_heads;
   a.d = s->head_dim;
@@ -311,6 +312,32 @@ int bsa_summarize(const bsa_shape* s, const void* K, const float* qbar, float* S
   a.kv_len = s->kv_len;
   a.bf16 = s->dtype == BSA_BF16;
   return device_status(bsa::launch_summarize(a, static_cast<hipStream_t>(stream)), "summarize");
+}
+
+int bsa_summarize_blocks(const bsa_shape* s, const void* K, const float* qbar, const int32_t* blk,
+                         float* S, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if ((rc = check_ptr("K", K)) != BSA_OK) return rc;
+  if ((rc = check_ptr("S", S)) != BSA_OK) return rc;
+  if (!blk) return fail(BSA_ERR_INVALID, "blk must not be NULL");
+  if (qbar && !aligned16(qbar)) return fail(BSA_ERR_UNSUPPORTED, "qbar must be 16-byte aligned");
+  if ((rc = check_strides("K", s->k_stride, s->dtype)) != BSA_OK) return rc;
+  bsa::SummarizeArgs a;
+  a.K = K;
+  a.ks = st3(s->k_stride);
+  a.qbar = qbar;
+  a.S = S;
+  a.blk = blk;
+  a.batch = s->batch;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.B = s->block;
+  a.nblk = static_cast<int>(nblk_of(s));
+  a.kv_len = s->kv_len;
+  a.bf16 = s->dtype == BSA_BF16;
+  return device_status(bsa::launch_summarize(a, static_cast<hipStream_t>(stream)),
+                       "summarize_blocks");
 }
 
 int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int32_t* kv_lens,

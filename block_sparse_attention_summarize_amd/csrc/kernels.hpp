@@ -17,6 +17,7 @@ struct SummarizeArgs {
   Strides3 ks;
   const float* qbar;  // nullptr -> mean
   float* S;           // [batch, hkv, nblk, d]
+  const int32_t* blk;  // nullptr: every block; else [batch] the one block per sequence, -1 none
   int batch, hkv, d, B, nblk;
   int64_t kv_len;
   bool bf16;

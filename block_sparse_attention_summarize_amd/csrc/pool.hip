@@ -24,10 +24,13 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(SummarizeArgs a) {
   __shared__ float wts[128];
 
   const int tid = threadIdx.x;
-  const int j = blockIdx.x % a.nblk;
-  const int bg = blockIdx.x / a.nblk;
+  // all blocks: one workgroup per (b, g, block); one block per sequence:
+  // one workgroup per (b, g) for the block blk[b] (none when out of range)
+  const int bg = a.blk ? static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x) / a.nblk;
   const int g = bg % a.hkv;
   const int b = bg / a.hkv;
+  const int j = a.blk ? a.blk[b] : static_cast<int>(blockIdx.x) % a.nblk;
+  if (j < 0 || j >= a.nblk) return;
   const int64_t t0 = static_cast<int64_t>(j) * a.B;
   const int64_t rem = a.kv_len - t0;
   const int cnt = static_cast<int>(rem < a.B ? rem : a.B);
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void qpool_kernel(QPoolArgs a) {
 
 template <typename T, int D>
 hipError_t summarize_dispatch(const SummarizeArgs& a, hipStream_t stream) {
-  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nblk;
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * (a.blk ? 1 : a.nblk);
   if (a.qbar)
     hipLaunchKernelGGL((summarize_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, stream, a);
   else

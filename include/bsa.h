@@ -5,7 +5,9 @@
  * The method (three stages, each one call here):
  *   Stage 0  bsa_summarize      keys of every block of B tokens are pooled into
  *                               one summary vector ("DashAttention" page,
- *                               section "Estágio 0: Resumo de Blocos Locais").
+ *                               section "Estágio 0: Resumo de Blocos Locais");
+ *            bsa_summarize_blocks  one block per sequence, for a growing
+ *                               decode cache.
  *   Stage 1  bsa_route_topk     every query block (prefill) or query token
  *            bsa_route_entmax   (decode) scores the summaries and selects a set
  *                               of blocks: top-k ("DashAttention", Declaração do
@@ -120,6 +122,23 @@ typedef struct bsa_shape {
  */
 int bsa_summarize(const bsa_shape *shape, const void *K, const float *qbar, float *S,
                   void *stream);
+
+/*
+ * Stage 0 for a growing decode cache ("DashAttention", Estágio 0: a block's
+ * summary is computed once, when the block is complete, and then reused).
+ * Recomputes one block summary per sequence instead of the whole cache: for
+ * sequence b, S[b, :, blk[b], :] from the keys of block blk[b] (a block
+ * reaching past kv_len averages the tokens present, as in bsa_summarize).
+ *   blk   int32 [batch] on the device: the block index of each sequence, or
+ *         any value outside [0, n_blk) for none.  After appending a token at
+ *         position L_b - 1, the block that just completed is L_b / B - 1 when
+ *         L_b % B == 0.
+ *   K, qbar, S as bsa_summarize (S holds the earlier summaries; only the
+ *         named blocks are written).
+ * Errors: BSA_ERR_INVALID (null K, S or blk, bad shape), BSA_ERR_UNSUPPORTED.
+ */
+int bsa_summarize_blocks(const bsa_shape *shape, const void *K, const float *qbar,
+                         const int32_t *blk, float *S, void *stream);
 
 /*
  * Stage 1, top-k ("DashAttention", Declaração do Problema; "Gist Sparse

@@ -66,6 +66,8 @@ def prefill(s, k_max=4, o_dtype=None, Q=FAKE, O=FAKE):
 def test_shape_validation():
     assert lib.bsa_summarize(None, FAKE, None, FAKE, None) == -1
     assert "NULL" in err()
+    assert lib.bsa_summarize_blocks(ctypes.byref(shape()), FAKE, None, None, FAKE, None) == -1
+    assert "blk" in err()
     assert topk(shape(hq=3, hkv=2)) == -1 and "multiple" in err()
     assert topk(shape(batch=0)) == -1
     assert topk(shape(d=96)) == -2 and "head_dim" in err()

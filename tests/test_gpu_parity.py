@@ -80,6 +80,34 @@ def test_summarize(name):
     np.testing.assert_allclose(_cpu(S2), ref2, rtol=0, atol=2e-5)
 
 
+def test_summarize_blocks_incremental():
+    """Per-sequence block update of a decode cache: each named block equals the
+    full summary bit for bit (same kernel arithmetic) and the oracle; entries
+    outside [0, n_blk) leave their sequence untouched."""
+    w = DECODE["decode"]  # lengths 2560, 1537, 64, 1
+    x = parity.make(w)
+    full = bsa.summarize(x["K"], w.B)
+    qbar = torch.from_numpy(np.random.default_rng(6).standard_normal((w.hkv, w.d)).astype(np.float32)).cuda()
+    full_q = bsa.summarize(x["K"], w.B, qbar=qbar)
+    # the block each token append just completed (L % B == 0), and arbitrary ones
+    for blk_list in ([int(L) // w.B - 1 if L % w.B == 0 else -1 for L in w.lens()], [39, 5, 0, 40]):
+        blk = torch.tensor(blk_list, dtype=torch.int32, device="cuda")
+        for ref_full, q in ((full, None), (full_q, qbar)):
+            S = ref_full.clone()
+            for b, j in enumerate(blk_list):
+                if 0 <= j < w.nblk:
+                    S[b, :, j, :] = float("nan")
+            before = S.clone()
+            bsa.summarize_blocks(x["K"], w.B, blk, S, qbar=q)
+            torch.cuda.synchronize()
+            assert torch.equal(S, ref_full), blk_list
+            for b, j in enumerate(blk_list):
+                if not (0 <= j < w.nblk):
+                    assert torch.equal(S[b].isnan(), before[b].isnan())
+    ref = oracle.summarize(x["k"], w.B)
+    np.testing.assert_allclose(_cpu(full), ref, rtol=0, atol=2e-6)
+
+
 def _route_ref(w, x):
     S = oracle.summarize(x["k"], w.B)
     if w.mode == "decode":
