@@ -59,13 +59,16 @@ struct TileWalk {
   }
 };
 
-// Double-buffered K and V tiles, both row-major (64 keys x D), rows padded
-// by 8 bf16 so that the fragment reads of 16 rows spread over the banks.
+// Double-buffered K and V tiles, both row-major (64 keys x D).  Row padding
+// spreads each read instruction over all 64 banks: K fragments read 16 B from
+// 16 rows (a 16-B pad staggers rows by 4 banks); the transposing V reads take
+// 32 B from each of 8 rows per half-wave (a 32-B pad staggers rows by 8).
 template <int D>
 struct PrefillLds {
-  static constexpr int KST = D + 8;  // row stride (bf16 elements)
+  static constexpr int KST = D + 8;   // K row stride (bf16 elements)
+  static constexpr int VST = D + 16;  // V row stride
   alignas(16) uint16_t k[2][64 * KST];
-  alignas(16) uint16_t v[2][64 * KST];
+  alignas(16) uint16_t v[2][64 * VST];
 };
 
 // Map workgroup id -> (pair = b*hkv + g, query block i, sub-unit).  Heavy
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
       const int flat = tid + NT * it;
       const int r = flat / CPR, c = flat % CPR;
       if (KTOT % NT == 0 || flat < KTOT)
-        *reinterpret_cast<uint4*>(&lds.v[buf][r * L::KST + c * 8]) = vreg[it];
+        *reinterpret_cast<uint4*>(&lds.v[buf][r * L::VST + c * 8]) = vreg[it];
     }
   };
 
@@ -353,11 +356,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
             // keys 32kk + 4G + e and 32kk + 16 + 4G + e (G = lane/16) for
             // column 16dt + lane%16, the key order of the P fragment
             const int s16 = lane & 15;
-            const uint16_t* vp = &lds.v[buf][(kk * 32 + (lane >> 4) * 4 + (s16 >> 2)) * L::KST +
+            const uint16_t* vp = &lds.v[buf][(kk * 32 + (lane >> 4) * 4 + (s16 >> 2)) * L::VST +
                                              dt * 16 + 4 * (s16 & 3)];
             typedef __attribute__((address_space(3))) v4i16 lds_v4;
             const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp));
-            const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 16 * L::KST));
+            const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 16 * L::VST));
             const uint2 u0 = __builtin_bit_cast(uint2, r0), u1 = __builtin_bit_cast(uint2, r1);
             const uint4 vf = make_uint4(u0.x, u0.y, u1.x, u1.y);
 #pragma unroll
