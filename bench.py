@@ -12,9 +12,12 @@ Printed: one JSON line.  `value` is prefill TFLOP/s counted on the selected
 blocks only (4 d flops per causal query-key pair actually attended) over the
 whole step.  `roofline` covers the dominant kernel (the MFMA attention) timed
 with HIP events on its stream inside the timed region; `cpu_baseline` is the
-fp64 oracle timed on this host on a bounded sample.  `extra.decode` reports
-the single-token decode workload (batch 16, 32/8 heads, L = 131072, top-32 +
-tail) as KV GB/s with the 256 MB last-level cache flushed between steps.
+fp64 oracle timed on this host on a bounded sample.  `extra` holds the other
+workloads of the method: `decode` (batch 16, 32/8 heads, L = 131072, top-32 +
+tail; GB/s with the 256 MB last-level cache flushed between steps),
+`entmax_prefill_n64k` (alpha = 1.5 entmax routing, N = 65536, cap 64) and
+`bf16_long_prefill_n256k` (16/2 heads, N = 262144, B = 128, top-32), each
+with its step time, per-stage times and attention TFLOP/s.
 """
 from __future__ import annotations
 
@@ -34,6 +37,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "bf16_gqa_prefill_n32k"
 DECODE = "bf16_decode_l128k"
+ENTMAX = "entmax_prefill_n64k"
+LONG = "bf16_long_prefill_n256k"
 COUNTERS = os.path.join(HERE, "profiles", "attend_prefill_bf16_gqa_n32k_counters.txt")
 
 
@@ -45,6 +50,8 @@ def parse():
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-decode", action="store_true", help="skip the decode extra")
+    p.add_argument("--no-entmax", action="store_true", help="skip the entmax prefill extra")
+    p.add_argument("--no-long", action="store_true", help="skip the N=262144 prefill extra")
     p.add_argument("--cpu-sample-blocks", type=int, default=12)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
@@ -142,6 +149,94 @@ def cpu_baseline(w, x, idx_h, cnt_h, total_flops, nsample):
             "seconds_per_step_extrapolated": t_total}
 
 
+def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
+    """One prefill step = summaries + routing (top-k or entmax) + fine attention.
+    Times `steps` steps back to back (host clock around the synchronised
+    region) and each stage with HIP events on the current stream."""
+    x = device_inputs(w, torch)
+    Q, K, V = x["Q"], x["K"], x["V"]
+    nrow = w.nblk
+    S = torch.empty((w.batch, w.hkv, w.nblk, w.d), dtype=torch.float32, device="cuda")
+    O = torch.empty_like(Q)
+    shape_r = bsa._route_shape(Q, S, w.B, False, None)
+    if w.router == "topk":
+        idx = torch.empty((w.batch, w.hkv, nrow, w.k_total), dtype=torch.int32, device="cuda")
+        cnt = torch.empty((w.batch, w.hkv, nrow), dtype=torch.int32, device="cuda")
+        ws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_TOPK, shape_r, w.k_total),
+                         dtype=torch.uint8, device="cuda")
+    else:
+        ws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_ENTMAX, shape_r, w.cap),
+                         dtype=torch.uint8, device="cuda")
+    sel = {}
+    ev = []
+
+    def route():
+        if w.router == "topk":
+            bsa.route_topk(Q, S, w.B, w.k_total, w.force, ws=ws, out=(idx, cnt))
+            sel["idx"], sel["cnt"] = idx, cnt
+        else:
+            sel["idx"], sel["cnt"], _, _ = bsa.route_entmax(
+                Q, S, w.B, w.alpha, w.gamma, w.cap, w.force, n_bins=w.n_bins,
+                max_iter=w.max_iter, ws=ws)
+
+    def step(record=False):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record()
+        bsa.summarize(K, w.B, out=S)
+        if record:
+            e[1].record()
+        route()
+        if record:
+            e[2].record()
+        bsa.attend_prefill(Q, K, V, w.B, sel["idx"], sel["cnt"], out=O)
+        if record:
+            e[3].record()
+            ev.append(e)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    idx_h, cnt_h = sel["idx"].cpu().numpy(), sel["cnt"].cpu().numpy()
+    flops = 4.0 * w.d * prefill_pairs(w, idx_h, cnt_h)
+    stage = lambda a_, b_: float(np.mean([e[a_].elapsed_time(e[b_]) for e in ev]))
+    res = {"workload": w.name, "flops": flops, "elapsed_s": elapsed,
+           "attend_s": stage(2, 3) * 1e-3,
+           "stages_ms": {"summarize": stage(0, 1), "route": stage(1, 2), "attend": stage(2, 3)},
+           "sparsity_vs_causal": 1.0 - flops / (4.0 * w.d * w.hq * w.n * (w.n + 1) / 2),
+           "idx_h": idx_h, "cnt_h": cnt_h, "steps": steps}
+    if keep_inputs:
+        res["x"] = x
+    else:
+        del x, Q, K, V, O, S, sel
+        torch.cuda.empty_cache()
+    return res
+
+
+def prefill_extra(r):
+    """JSON summary of a non-headline prefill workload."""
+    w = synth.WORKLOADS[r["workload"]]
+    ms = r["elapsed_s"] / r["steps"] * 1e3
+    att = r["flops"] / r["attend_s"] / 1e12
+    out = {"workload": w.name, "router": w.router, "batch": w.batch, "q_heads": w.hq,
+           "kv_heads": w.hkv, "seq_len": w.n, "head_dim": w.d, "block": w.B,
+           "ms_per_step": ms, "flops_per_step": r["flops"],
+           "TFLOP_per_s_step": r["flops"] / ms / 1e9,
+           "attend_TFLOP_per_s": att, "attend_frac_mfma_peak": att / PEAK_BF16_TFLOPS,
+           "stages_ms": r["stages_ms"], "sparsity_vs_causal": r["sparsity_vs_causal"],
+           "mean_selected_blocks": float(r["cnt_h"].mean())}
+    if w.router == "topk":
+        out["top_k"] = w.k_total
+    else:
+        out.update(alpha=w.alpha, gamma=w.gamma, cap=w.cap, max_iter=w.max_iter)
+    return out
+
+
 def run_decode(bsa, torch, steps, warmup):
     w = synth.WORKLOADS[DECODE]
     x = device_inputs(w, torch)
@@ -200,45 +295,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     w = synth.WORKLOADS[a.workload]
-    assert w.mode == "prefill" and w.router == "topk" and w.dtype == "bf16"
-    x = device_inputs(w, torch)
-    Q, K, V = x["Q"], x["K"], x["V"]
-    nrow = w.nblk
-    S = torch.empty((w.batch, w.hkv, w.nblk, w.d), dtype=torch.float32, device="cuda")
-    idx = torch.empty((w.batch, w.hkv, nrow, w.k_total), dtype=torch.int32, device="cuda")
-    cnt = torch.empty((w.batch, w.hkv, nrow), dtype=torch.int32, device="cuda")
-    O = torch.empty_like(Q)
-    shape_r = bsa._route_shape(Q, S, w.B, False, None)
-    ws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_TOPK, shape_r, w.k_total), dtype=torch.uint8,
-                     device="cuda")
-    ev = []
-
-    def step(record=False):
-        bsa.summarize(K, w.B, out=S)
-        bsa.route_topk(Q, S, w.B, w.k_total, w.force, ws=ws, out=(idx, cnt))
-        if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O)
-            e1.record()
-            ev.append((e0, e1))
-        else:
-            bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O)
-
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step(record=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
-    flops = 4.0 * w.d * prefill_pairs(w, idx_h, cnt_h)
+    assert w.mode == "prefill" and w.dtype == "bf16"
+    r = run_prefill(bsa, torch, w, a.steps, a.warmup)
+    flops, elapsed = r["flops"], r["elapsed_s"]
     ms = elapsed / a.steps * 1e3
     value = flops * a.steps / elapsed / 1e12
-    att_s = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e-3
+    att_s = r["attend_s"]
     achieved = flops / att_s / 1e12
     kernel_src = os.path.join(HERE, "block_sparse_attention_summarize_amd", "csrc", "attend.hip")
     out = {
@@ -248,17 +310,25 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) with planted blocks)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
                    "seq_len": w.n, "head_dim": w.d, "block": w.B, "top_k": w.k_total,
-                   "flops_per_step": flops, "sparsity_vs_causal":
-                       1.0 - flops / (4.0 * w.d * w.hq * w.n * (w.n + 1) / 2)},
+                   "flops_per_step": flops, "sparsity_vs_causal": r["sparsity_vs_causal"]},
         "frac_mfma_peak_step": value / PEAK_BF16_TFLOPS,
+        "stages_ms": r["stages_ms"],
         "roofline": {"kernel": "attend_prefill_bf16", "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": read_traffic(kernel_src), "avg_launch_ms": att_s * 1e3},
     }
+    extra = {}
     if not a.no_decode:
-        out["extra"] = {"decode": run_decode(bsa, torch, a.steps, a.warmup)}
+        extra["decode"] = run_decode(bsa, torch, a.steps, a.warmup)
+    for name, flag in ((ENTMAX, a.no_entmax), (LONG, a.no_long)):
+        if not flag:
+            extra[name] = prefill_extra(run_prefill(bsa, torch, synth.WORKLOADS[name], a.steps,
+                                                    a.warmup, keep_inputs=False))
+    if extra:
+        out["extra"] = extra
     if not a.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, x, idx_h, cnt_h, flops, a.cpu_sample_blocks)
+        out["cpu_baseline"] = cpu_baseline(w, r["x"], r["idx_h"], r["cnt_h"], flops,
+                                           a.cpu_sample_blocks)
     print(json.dumps(out), flush=True)
 
 
