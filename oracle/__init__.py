@@ -26,6 +26,7 @@ FORCE_FIRST = 2
 FORCE_TAIL = 4
 MODE_PREFILL = 0
 MODE_DECODE = 1
+MODE_TOKEN = 2  # causal prefill routed per query token
 
 
 def build(force: bool = True) -> str:
@@ -62,6 +63,7 @@ def _load():
                                          P, P, P, P, P, P, P, P]
         lib.orc_attend.argtypes = [P, P, P, I, I, I, I, I, I, I, ctypes.c_int, P, P, P, I, D,
                                    P, I, P, P]
+        lib.orc_token_union.argtypes = [P, P, I, I, I, I, I, P, P, P]
         lib.orc_version.restype = ctypes.c_char_p
         _lib = lib
     return _lib
@@ -191,6 +193,23 @@ def attend(Q, K, V, B, idx, cnt, req=None, mode=MODE_PREFILL, kv_lens=None, sm_s
                        _ptr(idx), _ptr(cnt), kmax, float(sm_scale), _ptr(req), req.shape[0],
                        _ptr(O), _ptr(pairs))
     return O, pairs
+
+
+def token_union(idx, cnt, nblk):
+    """Active blocks of every 64-query tile from per-token selections.
+    idx [nb, hkv, n, width], cnt [nb, hkv, n].  Returns (uidx, ucnt, ubits):
+    uidx [nb, hkv, ntile, nblk] ascending, -1 padded; ucnt [nb, hkv, ntile];
+    ubits [nb, hkv, ntile, nblk] uint64, bit r = token 64*tile + r selected it."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    cnt = np.ascontiguousarray(cnt, dtype=np.int32)
+    nb, hkv, n, width = idx.shape
+    ntile = (n + 63) // 64
+    uidx = np.empty((nb, hkv, ntile, nblk), np.int32)
+    ucnt = np.empty((nb, hkv, ntile), np.int32)
+    ubits = np.empty((nb, hkv, ntile, nblk), np.uint64)
+    _load().orc_token_union(_ptr(idx), _ptr(cnt), nb, hkv, n, width, nblk, _ptr(uidx),
+                            _ptr(ucnt), _ptr(ubits))
+    return uidx, ucnt, ubits
 
 
 def version() -> str:

@@ -43,6 +43,7 @@
 
 #define ORC_MODE_PREFILL 0
 #define ORC_MODE_DECODE 1
+#define ORC_MODE_TOKEN 2 /* causal prefill routed per query token */
 
 const char *orc_version(void) { return "bsa-oracle 1"; }
 
@@ -139,14 +140,17 @@ void orc_qpool(const float *Q, int64_t nb, int64_t nh, int64_t n, int64_t d, int
  *     tail = floor((L-1)/B) is incomplete and has no summary, so candidates are
  *     the complete blocks j < tail; TAIL (and DIAG, its synonym) forces the
  *     tail block, FIRST forces block 0.
+ *   token (row = query position t of a causal prefill, routed on its own as
+ *     "DashAttention", Estágio 1 routes each query): as prefill with the
+ *     query's own block t / B in place of the query block.
  * Forced blocks are removed from the candidate set by the callers.
  */
 static int64_t row_setup(int mode, int entmax, int64_t row, int64_t kv_len, int64_t B,
                          uint32_t force, int64_t *forced, int *nforced) {
   int64_t own, cand_end;
-  if (mode == ORC_MODE_PREFILL) {
-    own = row;
-    cand_end = entmax ? row : row + 1;
+  if (mode == ORC_MODE_PREFILL || mode == ORC_MODE_TOKEN) {
+    own = mode == ORC_MODE_TOKEN ? row / B : row;
+    cand_end = entmax ? own : own + 1;
   } else {
     own = (kv_len - 1) / B;
     cand_end = own;
@@ -561,6 +565,7 @@ void orc_route_entmax(const double *qhat, const double *S, int64_t nb, int64_t h
  *
  *   Q : [nb, hq, nq, d];  K, V : [nb, hkv, nk, d]  (fp32).
  *   prefill: nq == nk, query t sits at position t, its routing row is t / B.
+ *   token  : as prefill, but query t has a routing row of its own (row t).
  *   decode : nq == 1, query of batch b sits at position kv_lens[b]-1, row 0.
  *   idx/cnt: [nb, hkv, nrow, kmax] / [nb, hkv, nrow] from the router.
  *   req    : [nreq, 3] (b, h, t) query rows to compute (t ignored in decode).
@@ -576,7 +581,7 @@ void orc_attend(const float *Q, const float *K, const float *V, int64_t nb, int6
                 double sm_scale, const int64_t *req, int64_t nreq, double *O, int64_t *pairs) {
   (void)nb;
   int64_t G = hq / hkv;
-  int64_t nrow = (mode == ORC_MODE_PREFILL) ? (nq + B - 1) / B : 1;
+  int64_t nrow = (mode == ORC_MODE_PREFILL) ? (nq + B - 1) / B : (mode == ORC_MODE_TOKEN ? nq : 1);
   int64_t cap = kmax * B + 1;
   double *a = (double *)malloc(sizeof(double) * (size_t)cap);
   int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
@@ -584,9 +589,9 @@ void orc_attend(const float *Q, const float *K, const float *V, int64_t nb, int6
     int64_t b = req[rq * 3 + 0], h = req[rq * 3 + 1], t = req[rq * 3 + 2];
     int64_t g = h / G;
     int64_t pos, row, len;
-    if (mode == ORC_MODE_PREFILL) {
+    if (mode == ORC_MODE_PREFILL || mode == ORC_MODE_TOKEN) {
       pos = t;
-      row = t / B;
+      row = mode == ORC_MODE_TOKEN ? t : t / B;
       len = nk;
     } else {
       pos = kv_lens[b] - 1;
@@ -626,4 +631,56 @@ void orc_attend(const float *Q, const float *K, const float *V, int64_t nb, int6
   }
   free(a);
   free(tok);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Stage 2 with per-token selections: the tile's active blocks as a bit mask. */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Active-block mask of a query tile ("DashAttention", Estágio 2,
+ * Implementação: the attention kernel walks the active blocks given by a
+ * bit-packed mask).  Queries are grouped in tiles of 64 consecutive tokens;
+ * a block is active for a tile when at least one of its tokens selected it,
+ * and bit r of that block's word says whether token 64*tile + r did.
+ *
+ *   idx/cnt : [nb, hkv, n, width] / [nb, hkv, n] per-token selections
+ *             (entries outside [0, nblk) are ignored).
+ *   Outputs per (b, g, tile), ntile = ceil(n / 64):
+ *     uidx [.., nblk] active blocks in ascending order, -1 padded;
+ *     ucnt [..] their number;
+ *     ubits[.., nblk] the 64-bit token word of each listed block, 0 padded.
+ */
+void orc_token_union(const int32_t *idx, const int32_t *cnt, int64_t nb, int64_t hkv, int64_t n,
+                     int64_t width, int64_t nblk, int32_t *uidx, int32_t *ucnt, uint64_t *ubits) {
+  int64_t ntile = (n + 63) / 64;
+  uint64_t *word = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)(nblk > 0 ? nblk : 1));
+  for (int64_t b = 0; b < nb; ++b)
+    for (int64_t g = 0; g < hkv; ++g)
+      for (int64_t tile = 0; tile < ntile; ++tile) {
+        for (int64_t j = 0; j < nblk; ++j) word[j] = 0;
+        for (int64_t r = 0; r < 64 && tile * 64 + r < n; ++r) {
+          int64_t row = (b * hkv + g) * n + tile * 64 + r;
+          int64_t c = cnt[row];
+          if (c > width) c = width;
+          for (int64_t e = 0; e < c; ++e) {
+            int64_t j = idx[row * width + e];
+            if (j >= 0 && j < nblk) word[j] |= (uint64_t)1 << r;
+          }
+        }
+        int64_t out = ((b * hkv + g) * ntile + tile) * nblk;
+        int64_t u = 0;
+        for (int64_t j = 0; j < nblk; ++j)
+          if (word[j]) {
+            uidx[out + u] = (int32_t)j;
+            ubits[out + u] = word[j];
+            ++u;
+          }
+        ucnt[(b * hkv + g) * ntile + tile] = (int32_t)u;
+        for (int64_t v = u; v < nblk; ++v) {
+          uidx[out + v] = -1;
+          ubits[out + v] = 0;
+        }
+      }
+  free(word);
 }
