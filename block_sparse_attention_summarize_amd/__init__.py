@@ -11,6 +11,9 @@ Stages (names as in the C ABI):
   route_entmax     alpha-entmax block support (histogram-started bisection)
   attend_prefill   causal attention over the selected blocks' tokens
   attend_decode    single-token decode over the selected blocks (split-KV)
+  token_mask       per-token selections -> active-block masks of 64-query tiles
+Per-token routing (every query token routed on its own) is the `token=True`
+variant of route_topk / route_entmax / attend_prefill.
 """
 from __future__ import annotations
 
@@ -31,16 +34,16 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16 = 0, 1
-PREFILL, DECODE = 0, 1
+PREFILL, DECODE, TOKEN = 0, 1, 2
 FORCE_DIAG, FORCE_FIRST, FORCE_TAIL = 1, 2, 4
 OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE, \
     OP_DECODE_TOPK = range(6)
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
-EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill",
-           "bsa_attend_decode", "bsa_decode_topk", "bsa_workspace_size", "bsa_last_error",
-           "bsa_version")
+EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_route_topk", "bsa_route_entmax",
+           "bsa_attend_prefill", "bsa_token_mask", "bsa_attend_decode", "bsa_decode_topk",
+           "bsa_workspace_size", "bsa_last_error", "bsa_version")
 
 
 class Shape(ctypes.Structure):
@@ -66,11 +69,12 @@ lib.bsa_route_topk.argtypes = [_SP, _P, _P, _P, _i32, _u32, _f32, _P, _P, _P, _P
 lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, _u32, _f32, _P,
                                  _P, _P, _P, _P, _sz, _P]
 lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
+lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
 lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
                                 _P, _sz, _P]
-for _f in (lib.bsa_summarize, lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill,
-           lib.bsa_attend_decode, lib.bsa_decode_topk):
+for _f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_route_topk, lib.bsa_route_entmax,
+           lib.bsa_attend_prefill, lib.bsa_token_mask, lib.bsa_attend_decode, lib.bsa_decode_topk):
     _f.restype = ctypes.c_int
 lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
 lib.bsa_workspace_size.restype = _sz
@@ -156,15 +160,21 @@ def summarize(K: torch.Tensor, B: int, qbar: torch.Tensor | None = None,
     return S
 
 
-def _route_shape(Q, S, B, decode, kv_len):
+def _route_shape(Q, S, B, decode, kv_len, token=False):
     b, hq, n, d = Q.shape
     hkv, nblk = S.shape[1], S.shape[2]
     if decode:
         kv_len = kv_len if kv_len is not None else nblk * B
         return make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q), mode=DECODE,
                           q_len=1, kv_len=kv_len, q=Q)
-    return make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q), mode=PREFILL,
-                      q_len=n, kv_len=n, q=Q)
+    return make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q),
+                      mode=TOKEN if token else PREFILL, q_len=n, kv_len=n, q=Q)
+
+
+def _nrow(shape, B):
+    if shape.mode == DECODE:
+        return 1
+    return shape.q_len if shape.mode == TOKEN else (shape.q_len + B - 1) // B
 
 
 def summarize_blocks(K: torch.Tensor, B: int, blk: torch.Tensor, S: torch.Tensor,
@@ -182,12 +192,14 @@ def summarize_blocks(K: torch.Tensor, B: int, blk: torch.Tensor, S: torch.Tensor
 
 
 def route_topk(Q, S, B, k_total, force=0, decode=False, kv_len=None, kv_lens=None,
-               score_scale=0.0, want_scores=False, ws=None, out=None, partitioned=True):
+               score_scale=0.0, want_scores=False, ws=None, out=None, partitioned=True,
+               token=False):
     """Top-k routing.  Returns (idx, cnt) or (idx, cnt, scores).  In decode,
-    partitioned=False passes no workspace (one workgroup per row routes)."""
-    shape = _route_shape(Q, S, B, decode, kv_len)
+    partitioned=False passes no workspace (one workgroup per row routes).
+    token=True routes every query token (rows = tokens)."""
+    shape = _route_shape(Q, S, B, decode, kv_len, token)
     b, hkv, nblk = shape.batch, shape.n_kv_heads, S.shape[2]
-    nrow = 1 if decode else (shape.q_len + B - 1) // B
+    nrow = _nrow(shape, B)
     dev = Q.device
     if out is not None:
         idx, cnt = out
@@ -207,15 +219,19 @@ def route_topk(Q, S, B, k_total, force=0, decode=False, kv_len=None, kv_lens=Non
 
 def route_entmax(Q, S, B, alpha, gamma, cap, force=FORCE_DIAG, n_bins=16, max_iter=8,
                  decode=False, kv_len=None, kv_lens=None, score_scale=0.0, want_probs=False,
-                 want_tau=False, ws=None):
-    """alpha-entmax routing.  Returns (idx, cnt, probs or None, tau or None)."""
-    shape = _route_shape(Q, S, B, decode, kv_len)
+                 want_tau=False, ws=None, token=False, out=None):
+    """alpha-entmax routing.  Returns (idx, cnt, probs or None, tau or None).
+    token=True routes every query token (rows = tokens)."""
+    shape = _route_shape(Q, S, B, decode, kv_len, token)
     b, hq, hkv, nblk = shape.batch, shape.n_q_heads, shape.n_kv_heads, S.shape[2]
-    nrow = 1 if decode else (shape.q_len + B - 1) // B
+    nrow = _nrow(shape, B)
     dev = Q.device
     width = cap + bin(force & 7).count("1")
-    idx = torch.empty((b, hkv, nrow, width), dtype=torch.int32, device=dev)
-    cnt = torch.empty((b, hkv, nrow), dtype=torch.int32, device=dev)
+    if out is not None:
+        idx, cnt = out
+    else:
+        idx = torch.empty((b, hkv, nrow, width), dtype=torch.int32, device=dev)
+        cnt = torch.empty((b, hkv, nrow), dtype=torch.int32, device=dev)
     probs = torch.empty((b, hq, nrow, nblk), dtype=torch.float32, device=dev) if want_probs else None
     tau = torch.empty((b, hq, nrow), dtype=torch.float32, device=dev) if want_tau else None
     wsb, n = _workspace(OP_ROUTE_ENTMAX, shape, cap, dev, ws)
@@ -225,18 +241,45 @@ def route_entmax(Q, S, B, alpha, gamma, cap, force=FORCE_DIAG, n_bins=16, max_it
     return idx, cnt, probs, tau
 
 
-def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None):
-    """Causal attention over the selected blocks.  Q [b, Hq, N, d], K/V [b, Hkv, N, d]."""
+def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None, token=False,
+                   ws=None):
+    """Causal attention over the selected blocks.  Q [b, Hq, N, d], K/V [b, Hkv, N, d].
+    token=True: idx/cnt are per-token selections [b, Hkv, N, width]."""
     b, hq, n, d = Q.shape
     hkv = K.shape[1]
     odt = out_dtype or Q.dtype
     O = out if out is not None else torch.empty((b, hq, n, d), dtype=odt, device=Q.device)
-    shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q), mode=PREFILL,
-                       q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=O)
+    shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q),
+                       mode=TOKEN if token else PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K,
+                       v=V, o=O)
+    wsb, nws = _workspace(OP_ATTEND_PREFILL, shape, idx.shape[-1], Q.device, ws) if token \
+        else (None, 0)
     _check(lib.bsa_attend_prefill(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx),
-                                  _ptr(cnt), idx.shape[-1], sm_scale, _ptr(O), _dtype_code(O), None,
-                                  0, _stream(Q)))
+                                  _ptr(cnt), idx.shape[-1], sm_scale, _ptr(O), _dtype_code(O),
+                                  _ptr(wsb), nws, _stream(Q)))
     return O
+
+
+def token_mask(idx, cnt, B, kv_len=None, out=None):
+    """Per-token selections idx [b, Hkv, N, width] / cnt [b, Hkv, N] -> the
+    active blocks of every 64-query tile: (uidx [b, Hkv, T, nblk] int32,
+    ucnt [b, Hkv, T] int32, ubits [b, Hkv, T, nblk] int64 holding the 64-bit
+    token words), T = ceil(N / 64), nblk = ceil(kv_len / B)."""
+    b, hkv, n, width = idx.shape
+    kv_len = n if kv_len is None else kv_len
+    nblk = (kv_len + B - 1) // B
+    ntile = (n + 63) // 64
+    if out is not None:
+        uidx, ucnt, ubits = out
+    else:
+        uidx = torch.empty((b, hkv, ntile, nblk), dtype=torch.int32, device=idx.device)
+        ucnt = torch.empty((b, hkv, ntile), dtype=torch.int32, device=idx.device)
+        ubits = torch.empty((b, hkv, ntile, nblk), dtype=torch.int64, device=idx.device)
+    shape = make_shape(batch=b, hq=hkv, hkv=hkv, d=64, B=B, dtype=F32, mode=TOKEN, q_len=n,
+                       kv_len=kv_len)
+    _check(lib.bsa_token_mask(ctypes.byref(shape), _ptr(idx), _ptr(cnt), width, _ptr(uidx),
+                              _ptr(ucnt), _ptr(ubits), _stream(idx)))
+    return uidx, ucnt, ubits
 
 
 def attend_decode(q, K, V, B, idx, cnt, kv_lens=None, sm_scale=0.0, out_dtype=None, out=None):
@@ -299,6 +342,21 @@ def prefill_entmax(Q, K, V, B, alpha, gamma, cap, force=FORCE_DIAG, max_iter=8, 
     S = summarize(K, B) if S is None else S
     idx, cnt, _, _ = route_entmax(Q, S, B, alpha, gamma, cap, force, max_iter=max_iter)
     return attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype), idx, cnt
+
+
+def prefill_token_topk(Q, K, V, B, k_total, force=FORCE_DIAG, S=None, out_dtype=None):
+    """Stage 0 + per-token top-k routing + masked fine attention."""
+    S = summarize(K, B) if S is None else S
+    idx, cnt = route_topk(Q, S, B, k_total, force, token=True)
+    return attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype, token=True), idx, cnt
+
+
+def prefill_token_entmax(Q, K, V, B, alpha, gamma, cap, force=FORCE_DIAG, max_iter=8, S=None,
+                         out_dtype=None):
+    """Stage 0 + per-token alpha-entmax routing + masked fine attention."""
+    S = summarize(K, B) if S is None else S
+    idx, cnt, _, _ = route_entmax(Q, S, B, alpha, gamma, cap, force, max_iter=max_iter, token=True)
+    return attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype, token=True), idx, cnt
 
 
 def decode_topk(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, out_dtype=None):

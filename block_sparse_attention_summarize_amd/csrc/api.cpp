@@ -39,9 +39,14 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int64_t nblk_of(const bsa_shape* s) { return (s->kv_len + s->block - 1) / s->block; }
+// Routing rows: query blocks (prefill), query tokens (token), one (decode).
 int64_t nrow_of(const bsa_shape* s) {
+  if (s->mode == BSA_TOKEN) return s->q_len;
   return s->mode == BSA_PREFILL ? (s->q_len + s->block - 1) / s->block : 1;
 }
+// 64-query tiles of per-token attention.
+int64_t ntile_of(const bsa_shape* s) { return (s->q_len + 63) / 64; }
+constexpr int64_t kMaxTokenBlocks = 4096;  // one LDS word per block in the mask kernel (32 KiB)
 int popcount3(uint32_t f) { return (f & 1u) + ((f >> 1) & 1u) + ((f >> 2) & 1u); }
 int elem_bytes(int32_t dt) { return dt == BSA_BF16 ? 2 : 4; }
 
@@ -55,11 +60,11 @@ int check_shape(const bsa_shape* s) {
   if (s->n_q_heads % s->n_kv_heads != 0)
     return fail(BSA_ERR_INVALID, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
                 s->n_q_heads, s->n_kv_heads);
-  if (s->mode != BSA_PREFILL && s->mode != BSA_DECODE)
-    return fail(BSA_ERR_INVALID, "mode must be BSA_PREFILL or BSA_DECODE");
+  if (s->mode != BSA_PREFILL && s->mode != BSA_DECODE && s->mode != BSA_TOKEN)
+    return fail(BSA_ERR_INVALID, "mode must be BSA_PREFILL, BSA_DECODE or BSA_TOKEN");
   if (s->reserved != 0) return fail(BSA_ERR_INVALID, "reserved field must be 0");
   if (s->kv_len < 1) return fail(BSA_ERR_INVALID, "kv_len must be >= 1");
-  if (s->mode == BSA_PREFILL && s->q_len != s->kv_len)
+  if (s->mode != BSA_DECODE && s->q_len != s->kv_len)
     return fail(BSA_ERR_INVALID, "prefill needs q_len == kv_len (got %lld, %lld)",
                 (long long)s->q_len, (long long)s->kv_len);
   if (s->mode == BSA_DECODE && s->q_len != 1)
@@ -74,7 +79,9 @@ int check_shape(const bsa_shape* s) {
   const int64_t nrow = nrow_of(s);
   // grids are 1-D with one workgroup per (batch, head, block) at most
   const int64_t worst = static_cast<int64_t>(s->batch) * s->n_q_heads * nblk * 2;
-  if (worst >= (int64_t(1) << 31) || nblk * nrow >= (int64_t(1) << 40))
+  const int64_t rows = static_cast<int64_t>(s->batch) * s->n_q_heads * nrow;
+  if (worst >= (int64_t(1) << 31) || rows >= (int64_t(1) << 31) ||
+      nblk * nrow >= (int64_t(1) << 40))
     return fail(BSA_ERR_UNSUPPORTED, "problem too large for one launch");
   return BSA_OK;
 }
@@ -111,7 +118,7 @@ bsa::RowRule rule_of(const bsa_shape* s, int entmax, uint32_t force, const int32
 
 int check_force(const bsa_shape* s, uint32_t force) {
   if (force & ~7u) return fail(BSA_ERR_INVALID, "unknown force flags 0x%x", force);
-  if (s->mode == BSA_PREFILL && (force & BSA_FORCE_TAIL))
+  if (s->mode != BSA_DECODE && (force & BSA_FORCE_TAIL))
     return fail(BSA_ERR_INVALID, "BSA_FORCE_TAIL is only meaningful in decode");
   return BSA_OK;
 }
@@ -187,6 +194,19 @@ size_t ws_route_topk(const bsa_shape* s, int32_t k_total = 0, uint32_t force = 0
 size_t ws_route_entmax(const bsa_shape* s) {
   const size_t hrows = static_cast<size_t>(s->batch) * s->n_q_heads * nrow_of(s);
   return align_up(hrows * s->head_dim * 4) + align_up(hrows * nblk_of(s) * 4);
+}
+// Per-token attention: the tile masks (uidx, ubits, ucnt) live in ws.
+struct MaskWs {
+  size_t uidx, ubits, ucnt, total;
+};
+MaskWs mask_ws(const bsa_shape* s) {
+  const size_t rows = static_cast<size_t>(s->batch) * s->n_kv_heads * ntile_of(s);
+  MaskWs w;
+  w.uidx = align_up(rows * nblk_of(s) * 4);
+  w.ubits = align_up(rows * nblk_of(s) * 8);
+  w.ucnt = align_up(rows * 4);
+  w.total = w.uidx + w.ubits + w.ucnt;
+  return w;
 }
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (ws_bytes < need)
@@ -286,6 +306,8 @@ size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
     }
     case BSA_OP_ROUTE_ENTMAX:
       return ws_route_entmax(s);
+    case BSA_OP_ATTEND_PREFILL:
+      return s->mode == BSA_TOKEN ? mask_ws(s).total : 0;
     default:
       return 0;
   }
@@ -394,7 +416,7 @@ int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int3
   qp.hq = s->n_q_heads;
   qp.hkv = s->n_kv_heads;
   qp.d = s->head_dim;
-  qp.B = s->block;
+  qp.B = s->mode == BSA_TOKEN ? 1 : s->block;  // token rows: the query itself
   qp.nrow = nrow;
   qp.q_len = s->q_len;
   qp.bf16 = s->dtype == BSA_BF16;
@@ -462,7 +484,7 @@ int bsa_route_entmax(const bsa_shape* s, const void* Q, const float* S, const in
   qp.hq = s->n_q_heads;
   qp.hkv = s->n_kv_heads;
   qp.d = s->head_dim;
-  qp.B = s->block;
+  qp.B = s->mode == BSA_TOKEN ? 1 : s->block;
   qp.nrow = nrow;
   qp.q_len = s->q_len;
   qp.bf16 = s->dtype == BSA_BF16;
@@ -544,6 +566,7 @@ static int attend_common(const bsa_shape* s, const void* Q, const void* K, const
   a.os = st3(s->o_stride);
   a.idx = idx;
   a.cnt = cnt;
+  a.bits = nullptr;
   a.batch = s->batch;
   a.hq = s->n_q_heads;
   a.hkv = s->n_kv_heads;
@@ -560,19 +583,69 @@ static int attend_common(const bsa_shape* s, const void* Q, const void* K, const
   return BSA_OK;
 }
 
+static int token_mask_args(const bsa_shape* s, const int32_t* idx, const int32_t* cnt,
+                           int32_t width, int32_t* uidx, int32_t* ucnt, uint64_t* ubits,
+                           bsa::TokenMaskArgs& m) {
+  if (s->mode != BSA_TOKEN) return fail(BSA_ERR_INVALID, "per-token masks need BSA_TOKEN");
+  if (!idx || !cnt) return fail(BSA_ERR_INVALID, "idx and cnt must not be NULL");
+  if (!uidx || !ucnt || !ubits) return fail(BSA_ERR_INVALID, "uidx, ucnt and ubits must not be NULL");
+  if (width < 1) return fail(BSA_ERR_INVALID, "width must be >= 1");
+  if (nblk_of(s) > kMaxTokenBlocks)
+    return fail(BSA_ERR_UNSUPPORTED, "per-token masks support at most %lld blocks",
+                (long long)kMaxTokenBlocks);
+  m.idx = idx;
+  m.cnt = cnt;
+  m.uidx = uidx;
+  m.ucnt = ucnt;
+  m.ubits = ubits;
+  m.batch = s->batch;
+  m.hkv = s->n_kv_heads;
+  m.width = width;
+  m.nblk = static_cast<int>(nblk_of(s));
+  m.ntile = static_cast<int>(ntile_of(s));
+  m.q_len = s->q_len;
+  return BSA_OK;
+}
+
+int bsa_token_mask(const bsa_shape* s, const int32_t* idx, const int32_t* cnt, int32_t width,
+                   int32_t* uidx, int32_t* ucnt, uint64_t* ubits, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  bsa::TokenMaskArgs m;
+  if ((rc = token_mask_args(s, idx, cnt, width, uidx, ucnt, ubits, m)) != BSA_OK) return rc;
+  return device_status(bsa::launch_token_mask(m, static_cast<hipStream_t>(stream)), "token_mask");
+}
+
 int bsa_attend_prefill(const bsa_shape* s, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const int32_t* cnt, int32_t k_max, float sm_scale,
                        void* O, int32_t o_dtype, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
-  if (s->mode != BSA_PREFILL) return fail(BSA_ERR_INVALID, "bsa_attend_prefill needs BSA_PREFILL");
+  if (s->mode == BSA_DECODE)
+    return fail(BSA_ERR_INVALID, "bsa_attend_prefill needs BSA_PREFILL or BSA_TOKEN");
   bsa::AttendArgs a;
   if ((rc = attend_common(s, Q, K, V, idx, cnt, k_max, sm_scale, O, o_dtype, a)) != BSA_OK)
     return rc;
-  return device_status(bsa::launch_attend_prefill(a, static_cast<hipStream_t>(stream)),
-                       "attend_prefill");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s->mode == BSA_TOKEN) {
+    // per-token selections -> tile masks in ws -> masked tile attention
+    const MaskWs mw = mask_ws(s);
+    if ((rc = check_ws(ws, ws_bytes, mw.total)) != BSA_OK) return rc;
+    char* base = static_cast<char*>(ws);
+    bsa::TokenMaskArgs m;
+    if ((rc = token_mask_args(s, idx, cnt, k_max, reinterpret_cast<int32_t*>(base),
+                              reinterpret_cast<int32_t*>(base + mw.uidx + mw.ubits),
+                              reinterpret_cast<uint64_t*>(base + mw.uidx), m)) != BSA_OK)
+      return rc;
+    const hipError_t e = bsa::launch_token_mask(m, st);
+    if (e != hipSuccess) return device_status(e, "attend_prefill/token_mask");
+    a.idx = m.uidx;
+    a.cnt = m.ucnt;
+    a.bits = m.ubits;
+    a.k_max = m.nblk;
+    a.nrow = m.ntile;
+  }
+  return device_status(bsa::launch_attend_prefill(a, st), "attend_prefill");
 }
 
 int bsa_attend_decode(const bsa_shape* s, const void* Q, const void* K, const void* V,

@@ -13,6 +13,11 @@
 //                         operand comes from ds_read_b64_tr_b16.
 //   attend_prefill_f32    fp32 inputs: one query per lane, VALU dot products
 //                         (fp32 matrix rate is not the bound at these sizes).
+// With per-token selections (TOK) a row is a tile of 64 queries whose list
+// holds the blocks any of its tokens selected, each with a 64-bit word of the
+// tokens that did; a query's scores on a block its token did not select are
+// masked to -inf ("DashAttention", Estágio 2, Implementação: active blocks
+// from a bit-packed mask).
 // Single-token decode lives in decode.hip.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -118,12 +123,13 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_fmaxf(a, __builtin_fmaxf(b, c));
 }
 constexpr int kMaxTiles = 1024;  // tile-list chunk staged in LDS
+constexpr int kMaxTilesTok = 512;  // the same with a 64-bit token word per tile
 
 // QT query tiles of 16 per wavefront, NW wavefronts per workgroup.  A "unit"
 // is one query head x 16*QT queries of the query block; the workgroup's
 // wavefronts take NW consecutive units of the same (batch, KV head, block),
 // so they share every K/V tile staged in LDS.
-template <int D, int QT, int NW, bool OUT_F32>
+template <int D, int QT, int NW, bool OUT_F32, bool TOK>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArgs a, int wpb) {
   constexpr int NT = NW * 64;
   constexpr int QPW = 16 * QT;  // queries per wave
@@ -132,8 +138,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   constexpr int KTOT = 64 * CPR;                // 16-byte chunks per K (or V) tile
   constexpr int KITEMS = (KTOT + NT - 1) / NT;  // per thread
+  constexpr int MAXT = TOK ? kMaxTilesTok : kMaxTiles;
   __shared__ PrefillLds<D> lds;
-  __shared__ int lds_tiles[kMaxTiles];
+  __shared__ int lds_tiles[MAXT];
+  __shared__ uint64_t lds_tbits[TOK ? MAXT : 1];
   __shared__ int lds_ntiles;
   using L = PrefillLds<D>;
 
@@ -142,7 +150,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   const int w = tid >> 6;
   const int G = a.hq / a.hkv;
   const int nsub = a.B / 64;
-  const int qsub = a.B / QPW;  // query sub-blocks per block
+  const int qb = TOK ? 64 : a.B;  // queries per row
+  const int qsub = qb / QPW;      // query sub-blocks per row
   const int units = G * qsub;
   int pair, i, sub;
   map_wg(blockIdx.x, a.batch * a.hkv, a.nrow, wpb, pair, i, sub);
@@ -153,10 +162,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   const int hh = active ? u % G : 0;
   const int qs = active ? u / G : 0;
   const int h = g * G + hh;
-  const int qpos0 = i * a.B + qs * QPW;
+  const int qpos0 = i * qb + qs * QPW;
   int qs_max = 0;
   for (int uu = sub * NW; uu < sub * NW + NW && uu < units; ++uu) qs_max = max(qs_max, uu / G);
-  int64_t qmax = static_cast<int64_t>(i) * a.B + qs_max * QPW + QPW - 1;
+  int64_t qmax = static_cast<int64_t>(i) * qb + qs_max * QPW + QPW - 1;
   if (qmax > a.q_len - 1) qmax = a.q_len - 1;
 
   const int64_t rowid = static_cast<int64_t>(pair) * a.nrow + i;
@@ -241,14 +250,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   // into LDS by wave 0, kMaxTiles raw entries at a time, so the main loop
   // reads its next key offset from LDS instead of a dependent global load.
   const int nraw = n * nsub;
-  for (int base = 0; base < nraw; base += kMaxTiles) {
+  for (int base = 0; base < nraw; base += MAXT) {
     if (w == 0) {
       int c = 0;
-      for (int r = 0; r < kMaxTiles && base + r < nraw; r += 64) {
+      for (int r = 0; r < MAXT && base + r < nraw; r += 64) {
         const int T = base + r + lane;
         const int64_t k0 = T >= nraw ? -1 : (T < 64 ? walk.key0_of(jpre, T) : walk.key0(T));
         const uint64_t mk = __ballot(k0 >= 0);
-        if (k0 >= 0) lds_tiles[c + lanes_below(mk)] = static_cast<int>(k0);
+        if (k0 >= 0) {
+          lds_tiles[c + lanes_below(mk)] = static_cast<int>(k0);
+          if constexpr (TOK) lds_tbits[c + lanes_below(mk)] = a.bits[rowid * a.k_max + T / nsub];
+        }
         c += __popcll(mk);
       }
       if (lane == 0) lds_ntiles = c;
@@ -269,8 +281,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
       const int k0 = lds_tiles[t];
       const bool more = t + 1 < ntiles;
       if (more) load_tile(lds_tiles[t + 1]);
+      // TOK: bit 16qt + c says whether query qpos0 + 16qt + c selected the
+      // tile's block; a wave none of whose queries did skips the tile
+      uint64_t qbits = ~0ull;
+      if constexpr (TOK) qbits = lds_tbits[t] >> (qs * QPW);
 
-      if (active) {
+      if (active && (!TOK || (qbits & (QPW == 64 ? ~0ull : (1ull << QPW) - 1)) != 0)) {
         // S^T tiles: lane l holds keys 16kt + 4(l/16) + j of query column 16qt + l%16
         f32x4 s[4][QT];
 #pragma unroll
@@ -286,6 +302,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
           }
+        }
+        if constexpr (TOK) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt)
+            if (!((qbits >> (qt * 16 + (lane & 15))) & 1ull))
+#pragma unroll
+              for (int kt = 0; kt < 4; ++kt) s[kt][qt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         }
         // causal mask, only on tiles that reach past the wave's first query
         if (k0 + 63 > qpos0) {
@@ -410,7 +433,9 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
   __shared__ float ks[KT][D];
   __shared__ float vs[KT][D];
   const int lane = threadIdx.x;
-  const int nsub = a.B / 64;
+  const bool tok = a.bits != nullptr;  // rows are 64-query tiles
+  const int nsub = tok ? 1 : a.B / 64;
+  const int qb = tok ? 64 : a.B;
   // grid: (b, h, i, qs)
   int id = blockIdx.x;
   const int qs = id % nsub;
@@ -421,7 +446,7 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
   const int b = id / a.hq;
   const int G = a.hq / a.hkv;
   const int g = h / G;
-  const int64_t qpos0 = static_cast<int64_t>(i) * a.B + qs * 64;
+  const int64_t qpos0 = static_cast<int64_t>(i) * qb + qs * 64;
   const int64_t t = qpos0 + lane;
   int64_t qmax = qpos0 + 63;
   if (qmax > a.q_len - 1) qmax = a.q_len - 1;
@@ -443,6 +468,8 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
   for (int s = 0; s < n; ++s) {
     const int j = list[s];
     if (j < 0 || j >= a.nblk) continue;
+    // this lane's token selected block j (always, for block rows)
+    const bool on = !tok || ((a.bits[rowid * a.k_max + s] >> lane) & 1ull);
     for (int64_t k0 = static_cast<int64_t>(j) * a.B; k0 < static_cast<int64_t>(j + 1) * a.B;
          k0 += KT) {
       if (k0 > qmax || k0 >= a.kv_len) break;
@@ -462,7 +489,7 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
 #pragma unroll
         for (int c = 0; c < D; ++c) acc = fmaf(q[c], ks[r][c], acc);
         const int64_t key = k0 + r;
-        sv[r] = (key > t || key >= a.kv_len) ? -INFINITY : acc;
+        sv[r] = (key > t || key >= a.kv_len || !on) ? -INFINITY : acc;
         mx = fmaxf(mx, sv[r]);
       }
       const float mnew = fmaxf(m, mx);
@@ -488,31 +515,32 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
   for (int c = 0; c < D; ++c) Og[c] = o[c] * inv;
 }
 
-template <int D, int QT, int NW>
+template <int D, int QT, int NW, bool TOK>
 hipError_t prefill_bf16_launch(const AttendArgs& a, hipStream_t stream) {
   const int G = a.hq / a.hkv;
-  const int units = G * (a.B / (16 * QT));
+  const int units = G * ((TOK ? 64 : a.B) / (16 * QT));
   const int wpb = (units + NW - 1) / NW;
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow * wpb;
   if (a.out_f32)
-    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, true>), dim3(grid), dim3(NW * 64), 0, stream,
-                       a, wpb);
+    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, true, TOK>), dim3(grid), dim3(NW * 64), 0,
+                       stream, a, wpb);
   else
-    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, false>), dim3(grid), dim3(NW * 64), 0, stream,
-                       a, wpb);
+    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, false, TOK>), dim3(grid), dim3(NW * 64), 0,
+                       stream, a, wpb);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t prefill_bf16_dispatch(const AttendArgs& a, hipStream_t stream) {
-  return prefill_bf16_launch<D, 2, 4>(a, stream);
+  return a.bits ? prefill_bf16_launch<D, 2, 4, true>(a, stream)
+                : prefill_bf16_launch<D, 2, 4, false>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream) {
   if (a.bf16) return a.d == 64 ? prefill_bf16_dispatch<64>(a, stream) : prefill_bf16_dispatch<128>(a, stream);
-  const unsigned grid = static_cast<unsigned>(a.batch) * a.hq * a.nrow * (a.B / 64);
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hq * a.nrow * (a.bits ? 1 : a.B / 64);
   if (a.d == 64)
     hipLaunchKernelGGL(attend_prefill_f32<64>, dim3(grid), dim3(64), 0, stream, a);
   else

@@ -24,8 +24,8 @@ struct SummarizeArgs {
 };
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
 
-// Routing query of every row.  Prefill: mean over the query block, decode:
-// the query itself.  group_sum: add the heads of each KV group (top-k) and
+// Routing query of every row.  Prefill: mean over the query block, decode
+// and per-token routing (B = 1): the query itself.  group_sum: add the heads of each KV group (top-k) and
 // write [batch, hkv, nrow, d]; otherwise [batch, hq, nrow, d].
 struct QPoolArgs {
   const void* Q;
@@ -40,7 +40,7 @@ hipError_t launch_qpool(const QPoolArgs& a, hipStream_t stream);
 // Candidate range and forced blocks of a routing row are derived on the
 // device from (mode, row, kv_lens) exactly as documented in bsa.h.
 struct RowRule {
-  int mode;       // 0 prefill, 1 decode
+  int mode;       // 0 prefill (row = query block), 1 decode, 2 prefill routed per token
   int entmax;     // 1: prefill candidates exclude the diagonal
   uint32_t force;
   int B;
@@ -93,12 +93,30 @@ struct AttendArgs {
   Strides3 qs, ks, vs, os;
   const int32_t* idx;  // [batch, hkv, nrow, k_max]
   const int32_t* cnt;
+  // Per-token selections: nullptr for block rows (row i = queries [iB, iB+B)).
+  // Otherwise row i is the query tile [64i, 64i+64), idx/cnt its active
+  // blocks and bits[row, e] the tile's tokens that selected block idx[row, e].
+  const uint64_t* bits;
   int batch, hq, hkv, d, B, k_max, nrow, nblk;
   int64_t q_len, kv_len;
   float sm_scale;
   bool bf16, out_f32;
 };
 hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream);
+
+// Active blocks of every 64-query tile from per-token selections
+// idx/cnt [batch, hkv, q_len, width]: uidx/ucnt the ascending union over the
+// tile's tokens (-1 padded to nblk), ubits the tokens that selected each.
+struct TokenMaskArgs {
+  const int32_t* idx;
+  const int32_t* cnt;
+  int32_t* uidx;   // [batch, hkv, ntile, nblk]
+  int32_t* ucnt;   // [batch, hkv, ntile]
+  uint64_t* ubits; // [batch, hkv, ntile, nblk]
+  int batch, hkv, width, nblk, ntile;
+  int64_t q_len;
+};
+hipError_t launch_token_mask(const TokenMaskArgs& a, hipStream_t stream);
 
 // Single-token decode: routing (route = 1) and/or attention (attend = 1) for
 // every (batch, KV head) row, hsplit workgroups per row splitting the query

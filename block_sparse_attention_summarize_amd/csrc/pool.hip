@@ -128,6 +128,37 @@ __global__ __launch_bounds__(kThreads) void qpool_kernel(QPoolArgs a) {
   }
 }
 
+// Per-token routing query (rows of one token): q-hat[b, o, t] = sum over the
+// nh heads of group o of q[b, h, t], one thread per 8 elements of a row.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void qtok_kernel(QPoolArgs a, int64_t total) {
+  constexpr int CPR = D / 8;
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (e >= total) return;
+  const int nout = a.group_sum ? a.hkv : a.hq;
+  const int nh = a.group_sum ? a.hq / a.hkv : 1;
+  const int c = static_cast<int>(e % CPR);
+  const int64_t r = e / CPR;  // (b, o, t)
+  const int64_t t = r % a.q_len;
+  const int64_t bo = r / a.q_len;
+  const int o = static_cast<int>(bo % nout);
+  const int64_t b = bo / nout;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  for (int hh = 0; hh < nh; ++hh) {
+    float qv[8];
+    load8_f32<T>(static_cast<const T*>(a.Q) + b * a.qs.b + (o * nh + hh) * a.qs.h + t * a.qs.t +
+                     c * 8,
+                 qv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] += qv[k];
+  }
+  float4* out = reinterpret_cast<float4*>(a.qhat + r * D + c * 8);
+  out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
 template <typename T, int D>
 hipError_t summarize_dispatch(const SummarizeArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * (a.blk ? 1 : a.nblk);
@@ -141,6 +172,12 @@ hipError_t summarize_dispatch(const SummarizeArgs& a, hipStream_t stream) {
 template <typename T, int D>
 hipError_t qpool_dispatch(const QPoolArgs& a, hipStream_t stream) {
   const int nout = a.group_sum ? a.hkv : a.hq;
+  if (a.B == 1) {
+    const int64_t total = static_cast<int64_t>(a.batch) * nout * a.q_len * (D / 8);
+    const unsigned grid = static_cast<unsigned>((total + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL((qtok_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, a, total);
+    return hipGetLastError();
+  }
   const unsigned grid = static_cast<unsigned>(a.batch) * nout * a.nrow;
   hipLaunchKernelGGL((qpool_kernel<T, D>), dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();

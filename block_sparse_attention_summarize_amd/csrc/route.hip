@@ -102,7 +102,11 @@ __global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
   const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float* out = a.scores + (static_cast<int64_t>(bh) * a.nrow + r0) * a.nblk + j0;
-  if (j0 >= r0 + rn - (a.rule.entmax ? 1 : 0)) {  // right of the last row's candidates
+  // candidates of row r: blocks before own(r) (entmax) or up to it (top-k),
+  // own(r) = r for query-block rows and r / B for token rows
+  const int ce = a.rule.entmax ? 0 : 1;
+  const int tok_b = a.rule.mode == 2 ? a.rule.B : 1;
+  if (j0 >= (r0 + rn - 1) / tok_b + ce) {  // right of the last row's candidates
     for (int e = tid; e < kTile * kTile; e += kThreads) {
       const int r = e / kTile, j = e % kTile;
       if (r < rn && j < jn) out[static_cast<int64_t>(r) * a.nblk + j] = -INFINITY;
@@ -149,8 +153,7 @@ __global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int r = tr + 16 * m;
-    // prefill: the candidates of row r0 + r are [0, r0 + r) or [0, r0 + r + 1)
-    const int cend = r0 + r + (a.rule.entmax ? 0 : 1) - j0;
+    const int cend = (r0 + r) / tok_b + ce - j0;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int j = tj + 16 * n;
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
 }  // namespace
 
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
-  if (a.rule.mode == 0) {
+  if (a.rule.mode != 1) {
     const unsigned tiles = static_cast<unsigned>((a.nrow + kTile - 1) / kTile) *
                            static_cast<unsigned>((a.nblk + kTile - 1) / kTile);
     const unsigned grid = static_cast<unsigned>(a.batch) * a.qheads * tiles;

@@ -19,9 +19,9 @@ struct RowInfo {
 // Candidate range and forced blocks of one routing row, as documented in bsa.h.
 __device__ inline RowInfo row_info(const RowRule& r, int b, int row) {
   RowInfo ri;
-  if (r.mode == 0) {
-    ri.own = row;
-    ri.cand_end = r.entmax ? row : row + 1;
+  if (r.mode != 1) {  // prefill: row = query block; token: row = query token
+    ri.own = r.mode == 2 ? row / r.B : row;
+    ri.cand_end = r.entmax ? ri.own : ri.own + 1;
   } else {
     int64_t L = r.kv_lens ? static_cast<int64_t>(r.kv_lens[b]) : r.kv_len;
     L = L < 1 ? 1 : (L > r.kv_len ? r.kv_len : L);

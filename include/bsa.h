@@ -22,6 +22,8 @@
  *                               query token per sequence ("DashAttention",
  *                               Contribuições item 4: prefill and incremental
  *                               decode).
+ *            bsa_token_mask     per-token selections (BSA_TOKEN) as active-block
+ *                               masks of 64-query tiles.
  *   Decode   bsa_decode_topk    Stage 1 (top-k) and Stage 2 for one decode
  *                               step in a single launch.
  *
@@ -38,7 +40,7 @@
  *   - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
  *   - Selections are int32 [batch, n_kv_heads, n_rows, width], ascending block
  *     ids padded with -1, plus a count [batch, n_kv_heads, n_rows].  n_rows is
- *     ceil(q_len / block) in prefill and 1 in decode.
+ *     ceil(q_len / block) in prefill, q_len in token mode and 1 in decode.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns BSA_OK or a negative bsa_status.  Arguments are
  *     validated on the host before anything is enqueued: on an error nothing
@@ -71,11 +73,16 @@ typedef enum {
   BSA_ERR_WORKSPACE = -4    /* ws_bytes smaller than bsa_workspace_size() */
 } bsa_status;
 
-typedef enum { BSA_PREFILL = 0, BSA_DECODE = 1 } bsa_mode;
+/* BSA_TOKEN: causal prefill routed per query token ("DashAttention",
+ * Estágio 1 routes each query): the routing rows are the q_len query tokens,
+ * token t's own block is t / B, and attention runs over 64-query tiles with
+ * per-token masks (bsa_token_mask). */
+typedef enum { BSA_PREFILL = 0, BSA_DECODE = 1, BSA_TOKEN = 2 } bsa_mode;
 
 /* Forced blocks: always in the selection, never counted as routed. */
 enum {
   BSA_FORCE_DIAG = 1u,  /* prefill: the query block's own (diagonal) block;
+                           token: the block holding the token;
                            decode: the block holding the query (= TAIL) */
   BSA_FORCE_FIRST = 2u, /* block 0 */
   BSA_FORCE_TAIL = 4u   /* decode only: the last, possibly partial, block */
@@ -100,8 +107,8 @@ typedef struct bsa_shape {
   int32_t dtype;      /* bsa_dtype of Q, K and V */
   int32_t mode;       /* bsa_mode */
   int32_t reserved;   /* must be 0 */
-  int64_t q_len;      /* prefill: N (== kv_len); decode: 1 */
-  int64_t kv_len;     /* prefill: N; decode: capacity of the K/V cache */
+  int64_t q_len;      /* prefill, token: N (== kv_len); decode: 1 */
+  int64_t kv_len;     /* prefill, token: N; decode: capacity of the K/V cache */
   int64_t q_stride[3]; /* element strides of Q for (batch, head, token) */
   int64_t k_stride[3];
   int64_t v_stride[3];
@@ -144,11 +151,12 @@ int bsa_summarize_blocks(const bsa_shape *shape, const void *K, const float *qba
  * Stage 1, top-k ("DashAttention", Declaração do Problema; "Gist Sparse
  * Attention", section 2, item 3).
  *   Routing query of a row: prefill -- the mean of the query block's queries,
- *   per head; decode -- the query itself.  The score of block j for KV head g
+ *   per head; decode and token mode -- the query itself.  The score of block j for KV head g
  *   is score_scale * sum over the group's query heads of qhat_h . S_j
  *   (score_scale 0 means 1/sqrt(d)).
- *   Candidates: prefill row i -- blocks j <= i (causal); decode -- complete
- *   blocks j < floor((L-1)/B), L = kv_lens[b] (NULL: every L = kv_len).
+ *   Candidates: prefill row i -- blocks j <= i (causal); token row t -- blocks
+ *   j <= t / B; decode -- complete blocks j < floor((L-1)/B), L = kv_lens[b]
+ *   (NULL: every L = kv_len).
  *   Forced blocks (force_flags, BSA_FORCE_*) are always selected; the other
  *   k_total - #forced are the best candidates by (score desc, block asc).
  *   idx   out int32 [batch, Hkv, n_rows, k_total] ascending, -1 padded.
@@ -170,8 +178,8 @@ int bsa_route_topk(const bsa_shape *shape, const void *Q, const float *S,
  * Stage 1, alpha-entmax ("DashAttention", Estágio 1; threshold per
  * "AdaSplash-2", sections 1 and 2.A).  Per query head and row:
  *   x_j = (alpha-1) * gamma * score_scale * qhat_h . S_j over the candidates
- *   (prefill row i: j < i; decode: complete blocks before the tail; forced
- *   blocks excluded), tau from a 16-bin histogram of x_max - x on [0, 1)
+ *   (prefill row i: j < i; token row t: j < t / B; decode: complete blocks
+ *   before the tail; forced blocks excluded), tau from a 16-bin histogram of x_max - x on [0, 1)
  *   bracketing the root, then at most max_iter bisection steps, stopping once
  *   no x lies inside the bracket; the exact tau of the resolved support is
  *   used, else the bracket's lower end.  p_j = [x_j - tau]_+^(1/(alpha-1)),
@@ -199,11 +207,36 @@ int bsa_route_entmax(const bsa_shape *shape, const void *Q, const float *S,
  *   O     out [batch, Hq, q_len, d] with o_stride, dtype o_dtype: shape->dtype
  *         or BSA_F32 (full-precision output for bf16 inputs).
  *   k_max width of idx.
- * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED.
+ *   Token mode (shape->mode == BSA_TOKEN): idx/cnt are per-token selections
+ *   [batch, Hkv, q_len, k_max] and query t attends over idx[b, g(h), t, :cnt].
+ *   The call first builds the 64-query tile masks of bsa_token_mask in ws
+ *   (bsa_workspace_size(BSA_OP_ATTEND_PREFILL, ...) bytes, 256-byte aligned,
+ *   scratch afterwards), then attends tile by tile over the active blocks,
+ *   masking each query's scores on blocks its token did not select.  In
+ *   prefill mode ws is unused.
+ * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
  */
 int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                        const int32_t *idx, const int32_t *cnt, int32_t k_max, float sm_scale,
                        void *O, int32_t o_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Active-block masks of per-token selections ("DashAttention", Estágio 2,
+ * Implementação: the attention kernel iterates over the active blocks of a
+ * bit-packed mask).  Queries are grouped in tiles of 64 tokens,
+ * ntile = ceil(q_len / 64).  For each (b, g, tile):
+ *   uidx  out int32 [batch, Hkv, ntile, n_blk]: the blocks selected by at
+ *         least one of the tile's tokens, ascending, -1 padded;
+ *   ucnt  out int32 [batch, Hkv, ntile]: their number;
+ *   ubits out uint64 [batch, Hkv, ntile, n_blk]: for entry e, bit r is set
+ *         when token 64*tile + r has uidx[e] among idx[b, g, token, :cnt];
+ *         0 padded.
+ *   idx/cnt  per-token selections [batch, Hkv, q_len, width] (shape->mode
+ *         must be BSA_TOKEN); entries outside [0, n_blk) are ignored.
+ * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED (more than 4096 blocks).
+ */
+int bsa_token_mask(const bsa_shape *shape, const int32_t *idx, const int32_t *cnt, int32_t width,
+                   int32_t *uidx, int32_t *ucnt, uint64_t *ubits, void *stream);
 
 /*
  * Stage 2, decode: one query token per sequence at position L-1

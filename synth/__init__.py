@@ -8,12 +8,16 @@ method's arithmetic.  Recipe (stated once here, used everywhere):
   tensor stream s is drawn with ``numpy.random.default_rng(SeedSequence([seed,
   s, b, h, c])).standard_normal((rows, d), dtype=float32)``, so any slice can be
   regenerated without drawing the whole tensor; streams: q=0, k=1, v=2, u=3,
-  planted key blocks=4, planted query positions=5;
+  planted key blocks=4, planted query positions=5, query-tile components=6;
 * planting (the long-context retrieval structure): a unit vector
   u = g/|g|, g ~ N(0, I_d) (stream 3, fp64), a set of planted key blocks drawn
   without replacement (stream 4, identical for every KV head) whose keys get
   ``+ amp * u``, and round(frac * N) query positions (stream 5) whose queries get
   ``+ amp * u`` in every query head;
+* query locality (loc_amp > 0): every tile of 64 consecutive query tokens
+  shares a component c ~ N(0, I_d) per (batch, head, tile), drawn as stream 6
+  with one row per tile, and its queries get ``+ loc_amp * c`` (before the
+  planting), so nearby tokens route alike without routing identically;
 * bf16 tensors are the round-to-nearest-even bf16 of the fp32 values.
 """
 from __future__ import annotations
@@ -25,7 +29,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 CHUNK = 4096
-STREAM_Q, STREAM_K, STREAM_V, STREAM_U, STREAM_PK, STREAM_PQ = 0, 1, 2, 3, 4, 5
+STREAM_Q, STREAM_K, STREAM_V, STREAM_U, STREAM_PK, STREAM_PQ, STREAM_QL = 0, 1, 2, 3, 4, 5, 6
+QTILE = 64  # query tokens sharing one locality component
 
 FORCE_DIAG = 1
 FORCE_FIRST = 2
@@ -42,7 +47,7 @@ class Workload:
     n: int  # prefill: sequence length N; decode: cache length L
     d: int
     B: int
-    mode: str  # "prefill" or "decode"
+    mode: str  # "prefill", "token" (prefill routed per query token) or "decode"
     router: str  # "topk" or "entmax"
     k_total: int = 0
     force: int = 0
@@ -56,6 +61,7 @@ class Workload:
     planted_query_frac: float = 0.0
     amp: float = 3.0
     kv_lens: tuple = ()  # decode only; empty -> all equal to n
+    loc_amp: float = 0.0  # query-tile component amplitude
 
     @property
     def nblk(self) -> int:
@@ -63,7 +69,12 @@ class Workload:
 
     @property
     def q_len(self) -> int:
-        return self.n if self.mode == "prefill" else 1
+        return 1 if self.mode == "decode" else self.n
+
+    @property
+    def nrow(self) -> int:
+        """Routing rows: query blocks (prefill), tokens (token), 1 (decode)."""
+        return {"prefill": self.nblk, "token": self.n, "decode": 1}[self.mode]
 
     @property
     def idx_width(self) -> int:
@@ -190,7 +201,16 @@ def gen(w: Workload, name: str, heads=None, t0: int = 0, t1=None, batches=None):
             a, e = max(t0, j * w.B), min(t1, (j + 1) * w.B)
             if a < e:
                 out[:, :, a - t0:e - t0, :] += w.amp * u
-    if name == "q" and w.planted_query_frac > 0 and w.mode == "prefill":
+    if name == "q" and w.loc_amp > 0 and w.mode != "decode":
+        tiles = (rows + QTILE - 1) // QTILE
+        a, e = t0 // QTILE, (t1 - 1) // QTILE + 1
+        for bi, b in enumerate(batches):
+            for hi, h in enumerate(heads):
+                c = np.empty((e - a, w.d), np.float32)
+                _fill(w, STREAM_QL, nh, tiles, a, e, b, h, c)
+                tok = np.arange(t0, t1) // QTILE - a
+                out[bi, hi] += np.float32(w.loc_amp) * c[tok]
+    if name == "q" and w.planted_query_frac > 0 and w.mode != "decode":
         u = planted_vector(w).astype(np.float32)
         pos = planted_query_positions(w)
         pos = pos[(pos >= t0) & (pos < t1)]

@@ -45,18 +45,25 @@ def make(w: synth.Workload):
 
 
 def topk_mode(w):
-    return oracle.MODE_DECODE if w.mode == "decode" else oracle.MODE_PREFILL
+    return {"decode": oracle.MODE_DECODE, "token": oracle.MODE_TOKEN}.get(w.mode,
+                                                                          oracle.MODE_PREFILL)
+
+
+def own_block(w, row):
+    """The routing row's own block in prefill (the row) or token mode (row // B)."""
+    return row // w.B if w.mode == "token" else row
 
 
 def forced_set(w, b, row, kv_lens=None):
-    """Forced blocks of a routing row (prefill: DIAG -> row, FIRST -> 0;
-    decode: TAIL/DIAG -> the block of the query, FIRST -> 0)."""
+    """Forced blocks of a routing row (prefill: DIAG -> row, token: DIAG ->
+    row // B, FIRST -> 0; decode: TAIL/DIAG -> the block of the query,
+    FIRST -> 0)."""
     F = set()
     if w.force & synth.FORCE_FIRST:
         F.add(0)
-    if w.mode == "prefill":
+    if w.mode in ("prefill", "token"):
         if w.force & synth.FORCE_DIAG:
-            F.add(row)
+            F.add(own_block(w, row))
     else:
         L = int(w.lens()[b] if kv_lens is None else kv_lens[b])
         if w.force & (synth.FORCE_DIAG | synth.FORCE_TAIL):

@@ -169,3 +169,30 @@ def test_error_string_is_thread_local_and_cleared():
     t.join()
     assert msgs == [""]
     assert err() != ""
+
+
+def test_token_mode_validation_and_workspace():
+    al = lambda x: (x + 255) // 256 * 256
+    s = shape(batch=2, hq=8, hkv=2, d=128, B=64, mode=bsa.TOKEN, q_len=1000, kv_len=1000)
+    nblk, ntile = 16, 16
+    rows = 2 * 2 * 1000  # one routing row per token
+    assert lib.bsa_workspace_size(bsa.OP_ROUTE_TOPK, ctypes.byref(s), 4) == \
+        al(rows * 128 * 4) + al(rows * nblk * 4)
+    hrows = 2 * 8 * 1000
+    assert lib.bsa_workspace_size(bsa.OP_ROUTE_ENTMAX, ctypes.byref(s), 8) == \
+        al(hrows * 128 * 4) + al(hrows * nblk * 4)
+    trows = 2 * 2 * ntile  # 64-query tiles: active ids, token words, counts
+    need = al(trows * nblk * 4) + al(trows * nblk * 8) + al(trows * 4)
+    assert lib.bsa_workspace_size(bsa.OP_ATTEND_PREFILL, ctypes.byref(s), 4) == need
+    assert topk(s, force=bsa.FORCE_TAIL) == -1 and "decode" in err()
+    assert topk(shape(mode=bsa.TOKEN, q_len=128)) == -1 and "q_len == kv_len" in err()
+    # the tile masks need their workspace
+    assert lib.bsa_attend_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.0, FAKE,
+                                  bsa.BF16, ctypes.c_void_p(0x200000), need - 1, None) == -4
+    mask = lambda sh, idx=FAKE, width=4: lib.bsa_token_mask(ctypes.byref(sh), idx, FAKE, width,
+                                                             FAKE, FAKE, FAKE, None)
+    assert mask(shape()) == -1 and "BSA_TOKEN" in err()
+    assert mask(s, idx=None) == -1
+    assert mask(s, width=0) == -1
+    big = shape(hq=2, hkv=2, mode=bsa.TOKEN, q_len=64 * 4097, kv_len=64 * 4097)
+    assert mask(big) == -2 and "4096" in err()

@@ -1,0 +1,237 @@
+"""GPU parity of per-token routing ("DashAttention", Estágio 1 routes every
+query) and of the masked tile attention over per-token selections
+(Estágio 2, Implementação), against the fp64 oracle's token mode on seeded
+inputs small enough to check every row, spanning several tiles and a ragged
+tail.  Calls go through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+import block_sparse_attention_summarize_amd as bsa  # noqa: E402
+
+W = synth.WORKLOADS
+TOPK = {
+    "tok_bf16_gqa": W["bf16_gqa_prefill_n32k"].scaled(mode="token", hq=8, hkv=2, n=64 * 21 + 37,
+                                                      k_total=6, force=synth.FORCE_DIAG,
+                                                      planted_blocks=5, loc_amp=2.0),
+    "tok_f32_d64_first": W["fp32_prefill_n1k"].scaled(mode="token", n=64 * 9 + 17, hq=4, hkv=2,
+                                                      k_total=3,
+                                                      force=synth.FORCE_DIAG | synth.FORCE_FIRST),
+    "tok_f32_d128": W["fp32_prefill_n1k"].scaled(mode="token", d=128, n=64 * 6 + 5, hq=2, hkv=1,
+                                                 k_total=4, force=0, loc_amp=1.0),
+    # B = 128: two 64-key sub-tiles per block; no forced diagonal
+    "tok_b128_noforce": W["bf16_long_prefill_n256k"].scaled(mode="token", hq=4, hkv=1,
+                                                            n=128 * 9 + 50, k_total=4, force=0,
+                                                            planted_blocks=3, loc_amp=2.0),
+    "tok_d64_mha": W["bf16_gqa_prefill_n32k"].scaled(mode="token", d=64, hq=3, hkv=3,
+                                                     n=64 * 7 + 1, k_total=3,
+                                                     force=synth.FORCE_DIAG, planted_blocks=2),
+}
+ENTMAX = {
+    "tok_entmax_g4": W["entmax_prefill_n64k"].scaled(mode="token", hq=8, hkv=2, n=64 * 30 + 5,
+                                                     cap=16, gamma=4.0, planted_blocks=5,
+                                                     loc_amp=2.0),
+    "tok_entmax_g1_cap64": W["entmax_prefill_n64k"].scaled(mode="token", hq=4, hkv=1, n=64 * 25,
+                                                           cap=64, gamma=1.0, planted_blocks=4),
+    "tok_entmax_a2": W["entmax_prefill_n64k"].scaled(mode="token", hq=4, hkv=2, n=64 * 12 + 33,
+                                                     cap=6, gamma=16.0, alpha=2.0, loc_amp=1.0),
+}
+
+
+def _cpu(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(TOPK))
+def test_token_route_topk(name):
+    w = TOPK[name]
+    print(f"[token route_topk] {name}", flush=True)
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    idx, cnt, sc = bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, want_scores=True, token=True)
+    assert idx.shape == (w.batch, w.hkv, w.n, w.k_total)
+    ref = oracle.route_topk(x["q"].astype(np.float64), oracle.summarize(x["k"], w.B), w.B,
+                            w.k_total, w.force, mode=oracle.MODE_TOKEN)
+    gs = _cpu(sc)
+    fin = np.isfinite(ref["scores"])
+    assert np.array_equal(fin, np.isfinite(gs))
+    np.testing.assert_allclose(gs[fin], ref["scores"][fin], rtol=0, atol=1e-5)
+    rep = {}
+    parity.check_topk_rows(w, _cpu(idx), _cpu(cnt), ref, rep)
+    print(rep)
+
+
+@pytest.mark.parametrize("name", list(ENTMAX))
+def test_token_route_entmax(name):
+    w = ENTMAX[name]
+    print(f"[token route_entmax] {name}", flush=True)
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    idx, cnt, probs, tau = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
+                                            max_iter=w.max_iter, want_probs=True, want_tau=True,
+                                            token=True)
+    ref = oracle.route_entmax(x["q"].astype(np.float64), oracle.summarize(x["k"], w.B), w.B,
+                              w.alpha, w.gamma, w.cap, w.force, max_iter=w.max_iter,
+                              mode=oracle.MODE_TOKEN)
+    gp, gt = _cpu(probs), _cpu(tau)
+    rt = ref["tau"]
+    fin = np.isfinite(rt)
+    assert np.array_equal(fin, np.isfinite(gt))
+    clear = parity.entmax_clear(w, ref)
+    assert np.abs(gt[fin & clear] - rt[fin & clear]).max(initial=0) < 2e-5
+    assert np.abs(gp - ref["probs"])[clear].max(initial=0) < 2e-5
+    gi, gc = _cpu(idx), _cpu(cnt)
+    row_clear = (clear.reshape(w.batch, w.hkv, w.hq // w.hkv, -1).all(axis=2)
+                 & (ref["capgap"] > parity.GAP))
+    same = (gi == ref["idx"]).all(-1) & (gc == ref["cnt"])
+    assert same[row_clear].all(), f"{int((~same & row_clear).sum())} clear rows differ"
+    for r in zip(*np.nonzero(~same)):
+        sel = gi[r][:gc[r]]
+        own = r[2] // w.B
+        assert own in sel and np.all(np.diff(sel) > 0) and sel.max() <= own
+    print(f"rows {same.size}, clear {int(row_clear.sum())}, match {same.mean():.4f}, "
+          f"mean count {gc.mean():.1f}")
+
+
+def _random_token_selection(rng, w, width, p_invalid=0.0):
+    """Per-token selections with varied sets (not from a router): each token
+    picks a few causal blocks, sometimes none.  With p_invalid some listed ids
+    are replaced by ids outside [0, nblk), which the library skips.  Returns
+    (idx, cnt) with those ids and (idx, cnt) of the valid ids only, the form
+    the oracle takes."""
+    idx = np.full((w.batch, w.hkv, w.n, width), -1, np.int32)
+    cnt = np.zeros((w.batch, w.hkv, w.n), np.int32)
+    for b in range(w.batch):
+        for g in range(w.hkv):
+            for t in range(w.n):
+                own = t // w.B
+                c = int(rng.integers(0, min(width, own + 1) + 1))
+                sel = np.sort(rng.choice(own + 1, size=c, replace=False))
+                idx[b, g, t, :c] = sel
+                cnt[b, g, t] = c
+    clean_idx, clean_cnt = idx.copy(), cnt.copy()
+    if p_invalid > 0:
+        bad = rng.random(idx.shape) < p_invalid
+        idx[bad] = rng.choice([-7, w.nblk, w.nblk + 100], size=int(bad.sum()))
+        for r in zip(*np.nonzero(bad.any(-1))):
+            keep = [j for j in idx[r][:cnt[r]] if 0 <= j < w.nblk]
+            clean_idx[r] = -1
+            clean_idx[r][:len(keep)] = keep
+            clean_cnt[r] = len(keep)
+    return idx, cnt, clean_idx, clean_cnt
+
+
+@pytest.mark.parametrize("name", ["tok_bf16_gqa", "tok_b128_noforce"])
+def test_token_mask_matches_oracle(name):
+    w = TOPK[name]
+    print(f"[token_mask] {name}", flush=True)
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    idx, cnt = bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, token=True)
+    gi, gc = _cpu(idx), _cpu(cnt)
+    cases = [(gi, gc)]
+    rng = np.random.default_rng(w.seed + 77)
+    ri, rc, _, _ = _random_token_selection(rng, w, 5, p_invalid=0.05)
+    rc[0, 0, :3] = [-2, 9, 5]  # negative and over-width counts are clamped
+    cases.append((ri, rc))
+    for ci, cc in cases:
+        uidx, ucnt, ubits = bsa.token_mask(torch.from_numpy(ci).cuda(), torch.from_numpy(cc).cuda(),
+                                           w.B)
+        ru, rn, rb = oracle.token_union(ci, cc, w.nblk)
+        assert np.array_equal(_cpu(ucnt), rn)
+        assert np.array_equal(_cpu(uidx), ru)
+        assert np.array_equal(_cpu(ubits).view(np.uint64), rb)
+    print(f"tiles {rn.size}, mean active blocks {rn.mean():.1f}")
+
+
+@pytest.mark.parametrize("name", list(TOPK))
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_token_attend(name, out_f32):
+    w = TOPK[name]
+    print(f"[token attend] {name} out_f32={out_f32}", flush=True)
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    idx, cnt = bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, token=True)
+    O = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt,
+                           out_dtype=torch.float32 if out_f32 else None, token=True)
+    ref, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, _cpu(idx), _cpu(cnt),
+                               mode=oracle.MODE_TOKEN)
+    worst = parity.check_attention(w, _cpu(O).reshape(ref.shape), ref, out_f32 or w.dtype == "f32")
+    print(f"max abs err {worst:.3e}, pairs {int(pairs.sum())}")
+
+
+@pytest.mark.parametrize("name", ["tok_bf16_gqa", "tok_f32_d128", "tok_b128_noforce"])
+def test_token_attend_varied_and_empty_selections(name):
+    """Selections that differ token by token (including empty ones and
+    invalid ids): every query attends exactly over its own token set."""
+    w = TOPK[name]
+    print(f"[token attend varied] {name}", flush=True)
+    x = parity.make(w)
+    rng = np.random.default_rng(w.seed + 99)
+    ri, rc, ci, cc = _random_token_selection(rng, w, 4, p_invalid=0.03)
+    O = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, torch.from_numpy(ri).cuda(),
+                           torch.from_numpy(rc).cuda(), out_dtype=torch.float32, token=True)
+    ref, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, ci, cc, mode=oracle.MODE_TOKEN)
+    Oh = _cpu(O).reshape(ref.shape)
+    worst = parity.check_attention(w, Oh, ref, True)
+    assert np.all(Oh[pairs == 0] == 0)
+    print(f"max abs err {worst:.3e}, empty rows {int((pairs == 0).sum())}")
+
+
+@pytest.mark.parametrize("name", list(ENTMAX))
+def test_token_entmax_pipeline_attention(name):
+    w = ENTMAX[name]
+    print(f"[token entmax pipeline] {name}", flush=True)
+    x = parity.make(w)
+    O, idx, cnt = bsa.prefill_token_entmax(x["Q"], x["K"], x["V"], w.B, w.alpha, w.gamma, w.cap,
+                                           max_iter=w.max_iter)
+    ref, _ = oracle.attend(x["q"], x["k"], x["v"], w.B, _cpu(idx), _cpu(cnt),
+                           mode=oracle.MODE_TOKEN)
+    worst = parity.check_attention(w, _cpu(O).reshape(ref.shape), ref, False)
+    print(f"max abs err {worst:.3e}")
+
+
+def test_token_all_blocks_equals_dense_attention():
+    """k covering every causal block: per-token routing selects everything
+    and the masked attention is dense causal attention."""
+    w = TOPK["tok_bf16_gqa"]
+    x = parity.make(w)
+    O, idx, cnt = bsa.prefill_token_topk(x["Q"], x["K"], x["V"], w.B, w.nblk, force=0,
+                                         out_dtype=torch.float32)
+    t = np.arange(w.n)
+    assert np.array_equal(_cpu(cnt), np.broadcast_to(t // w.B + 1, cnt.shape))
+    G = w.hq // w.hkv
+    q = torch.from_numpy(x["q"]).double()
+    k = torch.from_numpy(np.repeat(x["k"], G, 1)).double()
+    v = torch.from_numpy(np.repeat(x["v"], G, 1)).double()
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True).numpy()
+    parity.check_attention(w, _cpu(O), ref, True)
+
+
+def test_token_mode_argument_errors():
+    w = TOPK["tok_bf16_gqa"]
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    idx, cnt = bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force, token=True)
+    with pytest.raises(bsa.BsaError, match="BSA_ERR_INVALID"):
+        bsa.route_topk(x["Q"], S, w.B, w.k_total, synth.FORCE_TAIL, token=True)
+    shape = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B, dtype=bsa.BF16,
+                           mode=bsa.TOKEN, q_len=w.n, kv_len=w.n, q=x["Q"], k=x["K"], v=x["V"],
+                           o=x["Q"])
+    need = bsa.workspace_size(bsa.OP_ATTEND_PREFILL, shape, w.k_total)
+    assert need > 0
+    O = torch.empty_like(x["Q"])
+    small = torch.empty(need // 2, dtype=torch.uint8, device="cuda")
+    import ctypes
+    rc = bsa.lib.bsa_attend_prefill(ctypes.byref(shape), bsa._ptr(x["Q"]), bsa._ptr(x["K"]),
+                                    bsa._ptr(x["V"]), bsa._ptr(idx), bsa._ptr(cnt), w.k_total,
+                                    0.0, bsa._ptr(O), bsa.BF16, bsa._ptr(small), need // 2, None)
+    assert rc == -4  # BSA_ERR_WORKSPACE, nothing enqueued
