@@ -15,9 +15,11 @@ with HIP events on its stream inside the timed region; `cpu_baseline` is the
 fp64 oracle timed on this host on a bounded sample.  `extra` holds the other
 workloads of the method: `decode` (batch 16, 32/8 heads, L = 131072, top-32 +
 tail; GB/s with the 256 MB last-level cache flushed between steps),
-`entmax_prefill_n64k` (alpha = 1.5 entmax routing, N = 65536, cap 64) and
-`bf16_long_prefill_n256k` (16/2 heads, N = 262144, B = 128, top-32), each
-with its step time, per-stage times and attention TFLOP/s.
+`entmax_prefill_n64k` (alpha = 1.5 entmax routing, N = 65536, cap 64),
+`bf16_long_prefill_n256k` (16/2 heads, N = 262144, B = 128, top-32) and
+`token_entmax_prefill_n32k` (every query token routed by alpha-entmax, cap
+32, attention over 64-query tile masks), each with its step time, per-stage
+times and attention TFLOP/s.
 """
 from __future__ import annotations
 
@@ -39,6 +41,7 @@ HEADLINE = "bf16_gqa_prefill_n32k"
 DECODE = "bf16_decode_l128k"
 ENTMAX = "entmax_prefill_n64k"
 LONG = "bf16_long_prefill_n256k"
+TOKEN = "token_entmax_prefill_n32k"
 COUNTERS = os.path.join(HERE, "profiles", "attend_prefill_bf16_gqa_n32k_counters.txt")
 
 
@@ -52,6 +55,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true", help="skip the decode extra")
     p.add_argument("--no-entmax", action="store_true", help="skip the entmax prefill extra")
     p.add_argument("--no-long", action="store_true", help="skip the N=262144 prefill extra")
+    p.add_argument("--no-token", action="store_true", help="skip the per-token routing extra")
     p.add_argument("--cpu-sample-blocks", type=int, default=12)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
@@ -100,6 +104,19 @@ def prefill_pairs(w, idx, cnt):
                 if (sel == i).any():
                     total += int(ntok[i] * (ntok[i] + 1) // 2)
     return total * G
+
+
+def token_pairs(w, idx, cnt):
+    """Causal query-key pairs attended with per-token selections, all heads:
+    a selected block before the token's own is B keys, its own block
+    t mod B + 1 keys."""
+    t = np.arange(w.n)
+    own = (t // w.B)[None, None, :, None]
+    listed = np.arange(idx.shape[-1])[None, None, None, :] < cnt[..., None]
+    below = listed & (idx >= 0) & (idx < own)
+    diag = listed & (idx == own)
+    pairs = int(below.sum()) * w.B + int((diag * ((t % w.B) + 1)[None, None, :, None]).sum())
+    return pairs * (w.hq // w.hkv)
 
 
 def source_digest(path):
@@ -155,29 +172,34 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
     region) and each stage with HIP events on the current stream."""
     x = device_inputs(w, torch)
     Q, K, V = x["Q"], x["K"], x["V"]
-    nrow = w.nblk
+    token = w.mode == "token"
+    nrow = w.nrow
     S = torch.empty((w.batch, w.hkv, w.nblk, w.d), dtype=torch.float32, device="cuda")
     O = torch.empty_like(Q)
-    shape_r = bsa._route_shape(Q, S, w.B, False, None)
+    shape_r = bsa._route_shape(Q, S, w.B, False, None, token)
+    idx = torch.empty((w.batch, w.hkv, nrow, w.idx_width), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((w.batch, w.hkv, nrow), dtype=torch.int32, device="cuda")
     if w.router == "topk":
-        idx = torch.empty((w.batch, w.hkv, nrow, w.k_total), dtype=torch.int32, device="cuda")
-        cnt = torch.empty((w.batch, w.hkv, nrow), dtype=torch.int32, device="cuda")
         ws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_TOPK, shape_r, w.k_total),
                          dtype=torch.uint8, device="cuda")
     else:
         ws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_ENTMAX, shape_r, w.cap),
                          dtype=torch.uint8, device="cuda")
-    sel = {}
+    aws = None
+    if token:  # the tile masks of the per-token attention
+        shape_a = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B,
+                                 dtype=bsa.BF16, mode=bsa.TOKEN, q_len=w.n, kv_len=w.n)
+        aws = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_PREFILL, shape_a, w.idx_width),
+                          dtype=torch.uint8, device="cuda")
+    sel = {"idx": idx, "cnt": cnt}
     ev = []
 
     def route():
         if w.router == "topk":
-            bsa.route_topk(Q, S, w.B, w.k_total, w.force, ws=ws, out=(idx, cnt))
-            sel["idx"], sel["cnt"] = idx, cnt
+            bsa.route_topk(Q, S, w.B, w.k_total, w.force, ws=ws, out=(idx, cnt), token=token)
         else:
-            sel["idx"], sel["cnt"], _, _ = bsa.route_entmax(
-                Q, S, w.B, w.alpha, w.gamma, w.cap, w.force, n_bins=w.n_bins,
-                max_iter=w.max_iter, ws=ws)
+            bsa.route_entmax(Q, S, w.B, w.alpha, w.gamma, w.cap, w.force, n_bins=w.n_bins,
+                             max_iter=w.max_iter, ws=ws, token=token, out=(idx, cnt))
 
     def step(record=False):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
@@ -189,7 +211,7 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
         route()
         if record:
             e[2].record()
-        bsa.attend_prefill(Q, K, V, w.B, sel["idx"], sel["cnt"], out=O)
+        bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O, token=token, ws=aws)
         if record:
             e[3].record()
             ev.append(e)
@@ -202,18 +224,34 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
         step(record=True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    idx_h, cnt_h = sel["idx"].cpu().numpy(), sel["cnt"].cpu().numpy()
-    flops = 4.0 * w.d * prefill_pairs(w, idx_h, cnt_h)
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    flops = 4.0 * w.d * (token_pairs(w, idx_h, cnt_h) if token else prefill_pairs(w, idx_h, cnt_h))
     stage = lambda a_, b_: float(np.mean([e[a_].elapsed_time(e[b_]) for e in ev]))
     res = {"workload": w.name, "flops": flops, "elapsed_s": elapsed,
            "attend_s": stage(2, 3) * 1e-3,
            "stages_ms": {"summarize": stage(0, 1), "route": stage(1, 2), "attend": stage(2, 3)},
            "sparsity_vs_causal": 1.0 - flops / (4.0 * w.d * w.hq * w.n * (w.n + 1) / 2),
            "idx_h": idx_h, "cnt_h": cnt_h, "steps": steps}
+    if token:
+        # the tile masks alone, and how much of the tiles' query x key area
+        # the tokens' own selections cover
+        uidx, ucnt, ubits = bsa.token_mask(idx, cnt, w.B)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            bsa.token_mask(idx, cnt, w.B, out=(uidx, ucnt, ubits))
+        e1.record()
+        torch.cuda.synchronize()
+        area = float(ucnt.double().sum().item()) * 64 * w.B * (w.hq // w.hkv)
+        res["token"] = {"mask_ms": e0.elapsed_time(e1) / 10,
+                        "mean_active_blocks_per_tile": float(ucnt.float().mean().item()),
+                        "selected_fraction_of_tile_area": flops / (4.0 * w.d) / area}
+        del uidx, ucnt, ubits
     if keep_inputs:
         res["x"] = x
     else:
-        del x, Q, K, V, O, S, sel
+        del x, Q, K, V, O, S, sel, idx, cnt, ws, aws
         torch.cuda.empty_cache()
     return res
 
@@ -234,6 +272,10 @@ def prefill_extra(r):
         out["top_k"] = w.k_total
     else:
         out.update(alpha=w.alpha, gamma=w.gamma, cap=w.cap, max_iter=w.max_iter)
+    if "token" in r:
+        out["routing"] = "per token"
+        out["query_locality_amp"] = w.loc_amp
+        out.update(r["token"])
     return out
 
 
@@ -320,7 +362,7 @@ def main():
     extra = {}
     if not a.no_decode:
         extra["decode"] = run_decode(bsa, torch, a.steps, a.warmup)
-    for name, flag in ((ENTMAX, a.no_entmax), (LONG, a.no_long)):
+    for name, flag in ((ENTMAX, a.no_entmax), (LONG, a.no_long), (TOKEN, a.no_token)):
         if not flag:
             extra[name] = prefill_extra(run_prefill(bsa, torch, synth.WORKLOADS[name], a.steps,
                                                     a.warmup, keep_inputs=False))

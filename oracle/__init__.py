@@ -60,9 +60,9 @@ def _load():
         lib.orc_entmax_row.restype = D
         lib.orc_route_entmax.argtypes = [P, P, I, I, I, I, I, I, I, ctypes.c_int, P, D, D,
                                          ctypes.c_int, ctypes.c_int, I, ctypes.c_uint32, D, I,
-                                         P, P, P, P, P, P, P, P]
+                                         P, P, P, P, P, P, P, P, P]
         lib.orc_attend.argtypes = [P, P, P, I, I, I, I, I, I, I, ctypes.c_int, P, P, P, I, D,
-                                   P, I, P, P]
+                                   P, I, P, P, P, D]
         lib.orc_token_union.argtypes = [P, P, I, I, I, I, I, P, P, P]
         lib.orc_version.restype = ctypes.c_char_p
         _lib = lib
@@ -142,7 +142,7 @@ def entmax_row(x, alpha, n_bins=16, max_iter=8):
 def route_entmax(qhat, S, B, alpha, gamma, cap, force=FORCE_DIAG, n_bins=16, max_iter=8,
                  mode=MODE_PREFILL, kv_lens=None, score_scale=None, idx_width=None):
     """Entmax routing.  Returns dict(idx, cnt, probs, tau, margin, capgap,
-    resolved, iters)."""
+    resolved, iters, wsel)."""
     qhat = _f64(qhat)
     S = _f64(S)
     nb, hq, nrow, d = qhat.shape
@@ -160,16 +160,21 @@ def route_entmax(qhat, S, B, alpha, gamma, cap, force=FORCE_DIAG, n_bins=16, max
     capgap = np.empty((nb, hkv, nrow), np.float64)
     resolved = np.empty((nb, hq, nrow), np.int32)
     iters = np.empty((nb, hq, nrow), np.int32)
+    wsel = np.empty((nb, hkv, nrow, idx_width), np.float64)
     _load().orc_route_entmax(_ptr(qhat), _ptr(S), nb, hq, hkv, nrow, nblk, d, B, mode, _ptr(kl),
                              float(alpha), float(gamma), n_bins, max_iter, cap, force,
                              float(score_scale), idx_width, _ptr(idx), _ptr(cnt), _ptr(probs),
-                             _ptr(tau), _ptr(margin), _ptr(capgap), _ptr(resolved), _ptr(iters))
+                             _ptr(tau), _ptr(margin), _ptr(capgap), _ptr(resolved), _ptr(iters),
+                             _ptr(wsel))
     return dict(idx=idx, cnt=cnt, probs=probs, tau=tau, margin=margin, capgap=capgap,
-                resolved=resolved, iters=iters)
+                resolved=resolved, iters=iters, wsel=wsel)
 
 
-def attend(Q, K, V, B, idx, cnt, req=None, mode=MODE_PREFILL, kv_lens=None, sm_scale=None):
-    """Fine attention over the selected blocks for the requested (b, h, t) rows.
+def attend(Q, K, V, B, idx, cnt, req=None, mode=MODE_PREFILL, kv_lens=None, sm_scale=None,
+           wsel=None, sigma=0.0):
+    """Fine attention over the selected blocks for the requested (b, h, t) rows;
+    with wsel (routing weights in the layout of idx) the prior-induced softmax
+    of strength sigma.
 
     Returns (O [nreq, d] fp64, pairs [nreq] int64).  req=None means every row."""
     Q = _f32(Q)
@@ -189,9 +194,12 @@ def attend(Q, K, V, B, idx, cnt, req=None, mode=MODE_PREFILL, kv_lens=None, sm_s
     kl = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int64)
     O = np.empty((req.shape[0], d), np.float64)
     pairs = np.empty(req.shape[0], np.int64)
+    if wsel is not None:
+        wsel = np.ascontiguousarray(wsel, dtype=np.float64)
+        assert wsel.shape == idx.shape
     _load().orc_attend(_ptr(Q), _ptr(K), _ptr(V), nb, hq, hkv, nq, nk, d, B, mode, _ptr(kl),
                        _ptr(idx), _ptr(cnt), kmax, float(sm_scale), _ptr(req), req.shape[0],
-                       _ptr(O), _ptr(pairs))
+                       _ptr(O), _ptr(pairs), _ptr(wsel), float(sigma))
     return O, pairs
 
 

@@ -472,13 +472,18 @@ double orc_entmax_row(const double *x, int64_t n, double alpha, int n_bins, int 
  *   capgap  [nb, hkv, nrow] (may be NULL): wbar_(cap) - wbar_(cap+1) among
  *           nonzero wbar, +inf when the cap does not bind.
  *   resolved/iters [nb, hq, nrow] (may be NULL).
+ *   wsel    [nb, hkv, nrow, idx_width] (may be NULL): the routing weight of
+ *           each listed block, wbar_j for a routed block and 1 for a forced
+ *           one (forced blocks have no routing score: "DashAttention",
+ *           Estágio 2, the diagonal keeps a branch of its own); 0 padded.
  */
 void orc_route_entmax(const double *qhat, const double *S, int64_t nb, int64_t hq, int64_t hkv,
                       int64_t nrow, int64_t nblk, int64_t d, int64_t B, int mode,
                       const int64_t *kv_lens, double alpha, double gamma, int n_bins, int max_iter,
                       int64_t cap, uint32_t force, double score_scale, int64_t idx_width,
                       int32_t *idx, int32_t *cnt, double *probs, double *tau_out, double *margin,
-                      double *capgap, int32_t *resolved_out, int32_t *iters_out) {
+                      double *capgap, int32_t *resolved_out, int32_t *iters_out,
+                      double *wsel) {
   int64_t G = hq / hkv;
   double *x = (double *)malloc(sizeof(double) * (size_t)(nblk + 1));
   double *p = (double *)malloc(sizeof(double) * (size_t)(nblk + 1));
@@ -545,6 +550,19 @@ void orc_route_entmax(const double *qhat, const double *S, int64_t nb, int64_t h
         cnt[rowid] = (int32_t)ns;
         for (int64_t a = 0; a < idx_width; ++a)
           idx[rowid * idx_width + a] = a < ns ? (int32_t)sel[a] : -1;
+        if (wsel)
+          for (int64_t a = 0; a < idx_width; ++a) {
+            double w = 0.0;
+            if (a < ns) {
+              if (is_forced(sel[a], forced, nforced)) {
+                w = 1.0;
+              } else {
+                for (int64_t k = 0; k < keep; ++k)
+                  if (kw[k].j == sel[a]) w = kw[k].key;
+              }
+            }
+            wsel[rowid * idx_width + a] = w;
+          }
       }
   free(x);
   free(p);
@@ -573,17 +591,27 @@ void orc_route_entmax(const double *qhat, const double *S, int64_t nb, int64_t h
  *   positions <= the query's position (causal) and < the sequence length.
  *   a_t' = q . k_t' * sm_scale; p = exp(a - max a) / sum; o = sum p v.
  *   An empty T gives o = 0.
+ *   wsel  : NULL, or the routing weight w of every listed block (layout of
+ *           idx).  Prior-induced softmax ("DashAttention", Estágio 2): the
+ *           softmax is taken against a reference g in place of the uniform
+ *           one, p maximising z.p - KL(p || g), i.e. p ~ g exp(z); g gives
+ *           every token of listed block j the weight w_j^sigma (sigma = 0:
+ *           uniform over T, sigma = 1: the routing weights), so the logits
+ *           gain sigma * ln w_j.  A listed block with w_j <= 0 has g = 0 and
+ *           is left out of T.
  *   O     : [nreq, d] fp64.   pairs : [nreq] (may be NULL) = |T|.
  */
 void orc_attend(const float *Q, const float *K, const float *V, int64_t nb, int64_t hq,
                 int64_t hkv, int64_t nq, int64_t nk, int64_t d, int64_t B, int mode,
                 const int64_t *kv_lens, const int32_t *idx, const int32_t *cnt, int64_t kmax,
-                double sm_scale, const int64_t *req, int64_t nreq, double *O, int64_t *pairs) {
+                double sm_scale, const int64_t *req, int64_t nreq, double *O, int64_t *pairs,
+                const double *wsel, double sigma) {
   (void)nb;
   int64_t G = hq / hkv;
   int64_t nrow = (mode == ORC_MODE_PREFILL) ? (nq + B - 1) / B : (mode == ORC_MODE_TOKEN ? nq : 1);
   int64_t cap = kmax * B + 1;
   double *a = (double *)malloc(sizeof(double) * (size_t)cap);
+  double *bias = (double *)malloc(sizeof(double) * (size_t)cap);
   int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
   for (int64_t rq = 0; rq < nreq; ++rq) {
     int64_t b = req[rq * 3 + 0], h = req[rq * 3 + 1], t = req[rq * 3 + 2];
@@ -606,7 +634,16 @@ void orc_attend(const float *Q, const float *K, const float *V, int64_t nb, int6
     int64_t nt = 0;
     for (int64_t s = 0; s < cnt[rowid]; ++s) {
       int64_t j = idx[rowid * kmax + s];
-      for (int64_t tp = j * B; tp < (j + 1) * B && tp < len && tp <= pos; ++tp) tok[nt++] = tp;
+      double bj = 0.0;
+      if (wsel) {
+        double w = wsel[rowid * kmax + s];
+        if (!(w > 0.0)) continue;
+        bj = sigma * log(w);
+      }
+      for (int64_t tp = j * B; tp < (j + 1) * B && tp < len && tp <= pos; ++tp) {
+        bias[nt] = bj;
+        tok[nt++] = tp;
+      }
     }
     double *o = O + rq * d;
     for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
@@ -616,7 +653,7 @@ void orc_attend(const float *Q, const float *K, const float *V, int64_t nb, int6
     for (int64_t u = 0; u < nt; ++u) {
       double acc = 0.0;
       for (int64_t c = 0; c < d; ++c) acc += (double)qv[c] * (double)kb[tok[u] * d + c];
-      a[u] = acc * sm_scale;
+      a[u] = acc * sm_scale + bias[u];
       if (a[u] > mx) mx = a[u];
     }
     double z = 0.0;
@@ -630,6 +667,7 @@ void orc_attend(const float *Q, const float *K, const float *V, int64_t nb, int6
     }
   }
   free(a);
+  free(bias);
   free(tok);
 }
 

@@ -93,7 +93,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of the method's hot path.
+# The workloads of the method's hot path.
 WORKLOADS = {
     "fp32_prefill_n1k": Workload(
         "fp32_prefill_n1k", "f32", 1, 2, 2, 1024, 64, 64, "prefill", "topk",
@@ -112,6 +112,12 @@ WORKLOADS = {
         "bf16_long_prefill_n256k", "bf16", 1, 16, 2, 262144, 128, 128, "prefill", "topk",
         k_total=32, force=FORCE_DIAG | FORCE_FIRST, seed=4, planted_blocks=64,
         planted_query_frac=0.01),
+    # every query token routed on its own (alpha-entmax per token), queries
+    # with 64-token locality; attention over the active blocks of 64-query tiles
+    "token_entmax_prefill_n32k": Workload(
+        "token_entmax_prefill_n32k", "bf16", 1, 32, 8, 32768, 128, 64, "token", "entmax",
+        alpha=1.5, gamma=4.0, cap=32, n_bins=16, max_iter=8, force=FORCE_DIAG, seed=5,
+        planted_blocks=32, planted_query_frac=0.01, loc_amp=4.0),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

@@ -1,8 +1,8 @@
-"""Parity at the full sizes of the five workloads, in the launch
+"""Parity at the full sizes of the benchmark's workloads, in the launch
 configuration the benchmark times.
 
 Routing is checked on every row (bit-exact where the gap rule applies, valid
-elsewhere).  Attention is checked in full where the oracle finishes in
+elsewhere; per-token routing on sampled tokens).  Attention is checked in full where the oracle finishes in
 seconds (fp32 prefill N=1024, decode) and otherwise on every query token of a
 few seeded query blocks for every head (the first, the last, and seeded
 picks), against the fp64 oracle attending over the GPU's own selection.
@@ -149,4 +149,68 @@ def test_full_decode_step():
     worst = parity.check_attention(w, _cpu(O).reshape(out.shape), out, False)
     print(f"attention: all {out.shape[0]} rows, max abs err {worst:.3e}", flush=True)
     del x, S, O, idx, cnt, ws, Sref
+    _free()
+
+
+def test_full_token_entmax_prefill():
+    """Per-token entmax routing at full size: sampled tokens' rows are checked
+    one by one (a token's row is the decode row of a cache of length t + 1),
+    the tile masks of every tile, and attention on every query of a few
+    sampled tiles for every head."""
+    w = W["token_entmax_prefill_n32k"]
+    print(f"[full token entmax prefill] {w}", flush=True)
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    idx, cnt, probs, tau = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
+                                            max_iter=w.max_iter, want_probs=True, want_tau=True,
+                                            token=True)
+    O = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt, token=True)
+    uidx, ucnt, ubits = bsa.token_mask(idx, cnt, w.B)
+    torch.cuda.synchronize()
+    gi, gc = _cpu(idx), _cpu(cnt)
+    Sref = oracle.summarize(x["k"], w.B)
+    assert np.abs(_cpu(S) - Sref).max() < 2e-6
+    rng = np.random.default_rng(w.seed + 200)
+    tiles = sorted({0, (w.n - 1) // 64} | set(rng.choice(w.n // 64, size=2, replace=False).tolist()))
+    toks = sorted(set(rng.choice(w.n, size=96, replace=False).tolist())
+                  | {t for tl in tiles for t in (tl * 64, tl * 64 + 63)} | {w.n - 1})
+    gp, gt = _cpu(probs), _cpu(tau)
+    checked = same_n = clear_n = 0
+    for t in toks:
+        one = oracle.route_entmax(x["q"][:, :, t:t + 1].astype(np.float64), Sref, w.B, w.alpha,
+                                  w.gamma, w.cap, w.force, max_iter=w.max_iter,
+                                  mode=oracle.MODE_DECODE, kv_lens=[t + 1])
+        clear = parity.entmax_clear(w, one)[:, :, 0]
+        fin = np.isfinite(one["tau"][:, :, 0])
+        assert np.array_equal(fin, np.isfinite(gt[:, :, t]))
+        m = fin & clear
+        assert np.abs(gt[:, :, t][m] - one["tau"][:, :, 0][m]).max(initial=0) < 2e-5
+        assert np.abs(gp[:, :, t] - one["probs"][:, :, 0])[clear].max(initial=0) < 2e-5
+        row_clear = clear.reshape(w.batch, w.hkv, -1).all(-1) & (one["capgap"][:, :, 0] > parity.GAP)
+        same = (gi[:, :, t] == one["idx"][:, :, 0]).all(-1) & (gc[:, :, t] == one["cnt"][:, :, 0])
+        assert same[row_clear].all(), f"token {t}: clear rows differ"
+        for g in np.nonzero(~same[0])[0]:
+            sel = gi[0, g, t, :gc[0, g, t]]
+            assert t // w.B in sel and np.all(np.diff(sel) > 0) and sel.max() <= t // w.B
+        checked += same.size
+        same_n += int(same.sum())
+        clear_n += int(row_clear.sum())
+    print(f"routing: {checked} sampled rows, clear {clear_n}, match {same_n / checked:.4f}, "
+          f"mean count {gc.mean():.1f}", flush=True)
+    # the tile masks of every tile, bit-exact against the oracle's union of
+    # the GPU's per-token selections
+    ru, rn, rb = oracle.token_union(gi, gc, w.nblk)
+    gu, gn, gb = _cpu(uidx), _cpu(ucnt), _cpu(ubits).view(np.uint64)
+    assert np.array_equal(gn, rn) and np.array_equal(gu, ru) and np.array_equal(gb, rb)
+    print(f"tile masks: {rn.size} tiles, mean active blocks {rn.mean():.1f}", flush=True)
+    del probs, tau, gp, gu, gb, ru, rb, uidx, ubits
+    req = np.array([[0, h, t] for tl in tiles for h in range(w.hq)
+                    for t in range(tl * 64, min(tl * 64 + 64, w.n))], np.int64)
+    ref, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, gi, gc, req=req,
+                               mode=oracle.MODE_TOKEN)
+    got = _cpu(O)[req[:, 0], req[:, 1], req[:, 2]]
+    worst = parity.check_attention(w, got, ref, False)
+    print(f"attention: tiles {tiles}, {len(req)} rows, {int(pairs.sum())} pairs, "
+          f"max abs err {worst:.3e}", flush=True)
+    del x, S, O, idx, cnt
     _free()

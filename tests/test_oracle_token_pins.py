@@ -184,3 +184,23 @@ def test_token_union_reconstructs_every_tokens_selection(n):
             got = {int(j) for j, w in zip(u, bits) if (int(w) >> r) & 1}
             want = set(idx[b, g, t, :cnt[b, g, t]].tolist()) if t < n else set()
             assert got == want, (b, g, t)
+
+
+@pytest.mark.parametrize("force", [oracle.FORCE_DIAG, oracle.FORCE_DIAG | oracle.FORCE_FIRST])
+def test_token_entmax_row_equals_decode_row_at_its_position(force):
+    """A token's entmax routing is the decode routing of a cache of length
+    t + 1 with that token as the query (same candidates, blocks before t / B;
+    same forced blocks), so single rows of a long sequence can be checked
+    one by one."""
+    rng = _rng(2600)
+    B, n, d, hq, hkv = 8, 70, 16, 4, 2
+    Q = rng.standard_normal((1, hq, n, d)).astype(np.float32)
+    K = rng.standard_normal((1, hkv, n, d)).astype(np.float32)
+    S = oracle.summarize(K, B)
+    tok = oracle.route_entmax(Q, S, B, 1.5, 4.0, cap=3, force=force, mode=oracle.MODE_TOKEN)
+    for t in [0, 7, 8, 33, 69]:
+        one = oracle.route_entmax(Q[:, :, t:t + 1], S, B, 1.5, 4.0, cap=3, force=force,
+                                  mode=oracle.MODE_DECODE, kv_lens=[t + 1])
+        np.testing.assert_array_equal(one["idx"][:, :, 0], tok["idx"][:, :, t])
+        np.testing.assert_array_equal(one["cnt"][:, :, 0], tok["cnt"][:, :, t])
+        np.testing.assert_array_equal(one["probs"][:, :, 0], tok["probs"][:, :, t])
