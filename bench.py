@@ -185,12 +185,15 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
     else:
         ws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_ENTMAX, shape_r, w.cap),
                          dtype=torch.uint8, device="cuda")
+    prior = w.router == "entmax" and w.sigma != 0.0
+    wsel = torch.empty(idx.shape, dtype=torch.float32, device="cuda") if prior else None
     aws = None
-    if token:  # the tile masks of the per-token attention
+    if token:  # the tile masks (and prior bias) of the per-token attention
         shape_a = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B,
                                  dtype=bsa.BF16, mode=bsa.TOKEN, q_len=w.n, kv_len=w.n)
-        aws = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_PREFILL, shape_a, w.idx_width),
-                          dtype=torch.uint8, device="cuda")
+        op = bsa.OP_ATTEND_PREFILL_PRIOR if prior else bsa.OP_ATTEND_PREFILL
+        aws = torch.empty(bsa.workspace_size(op, shape_a, w.idx_width), dtype=torch.uint8,
+                          device="cuda")
     sel = {"idx": idx, "cnt": cnt}
     ev = []
 
@@ -199,7 +202,7 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
             bsa.route_topk(Q, S, w.B, w.k_total, w.force, ws=ws, out=(idx, cnt), token=token)
         else:
             bsa.route_entmax(Q, S, w.B, w.alpha, w.gamma, w.cap, w.force, n_bins=w.n_bins,
-                             max_iter=w.max_iter, ws=ws, token=token, out=(idx, cnt))
+                             max_iter=w.max_iter, ws=ws, token=token, out=(idx, cnt), wsel=wsel)
 
     def step(record=False):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
@@ -211,7 +214,8 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
         route()
         if record:
             e[2].record()
-        bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O, token=token, ws=aws)
+        bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O, token=token, ws=aws, wsel=wsel,
+                           sigma=w.sigma)
         if record:
             e[3].record()
             ev.append(e)
@@ -251,7 +255,7 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
     if keep_inputs:
         res["x"] = x
     else:
-        del x, Q, K, V, O, S, sel, idx, cnt, ws, aws
+        del x, Q, K, V, O, S, sel, idx, cnt, ws, aws, wsel
         torch.cuda.empty_cache()
     return res
 
@@ -276,6 +280,8 @@ def prefill_extra(r):
         out["routing"] = "per token"
         out["query_locality_amp"] = w.loc_amp
         out.update(r["token"])
+    if w.router == "entmax":
+        out["prior_sigma"] = w.sigma
     return out
 
 

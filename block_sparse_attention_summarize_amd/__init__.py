@@ -37,7 +37,7 @@ F32, BF16 = 0, 1
 PREFILL, DECODE, TOKEN = 0, 1, 2
 FORCE_DIAG, FORCE_FIRST, FORCE_TAIL = 1, 2, 4
 OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE, \
-    OP_DECODE_TOPK = range(6)
+    OP_DECODE_TOPK, OP_ATTEND_PREFILL_PRIOR = range(7)
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
@@ -67,8 +67,9 @@ lib.bsa_summarize.argtypes = [_SP, _P, _P, _P, _P]
 lib.bsa_summarize_blocks.argtypes = [_SP, _P, _P, _P, _P, _P]
 lib.bsa_route_topk.argtypes = [_SP, _P, _P, _P, _i32, _u32, _f32, _P, _P, _P, _P, _sz, _P]
 lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, _u32, _f32, _P,
-                                 _P, _P, _P, _P, _sz, _P]
-lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
+                                 _P, _P, _P, _P, _P, _sz, _P]
+lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32, _P, _i32, _P, _sz,
+                                   _P]
 lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
 lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
@@ -219,9 +220,10 @@ def route_topk(Q, S, B, k_total, force=0, decode=False, kv_len=None, kv_lens=Non
 
 def route_entmax(Q, S, B, alpha, gamma, cap, force=FORCE_DIAG, n_bins=16, max_iter=8,
                  decode=False, kv_len=None, kv_lens=None, score_scale=0.0, want_probs=False,
-                 want_tau=False, ws=None, token=False, out=None):
+                 want_tau=False, ws=None, token=False, out=None, wsel=None):
     """alpha-entmax routing.  Returns (idx, cnt, probs or None, tau or None).
-    token=True routes every query token (rows = tokens)."""
+    token=True routes every query token (rows = tokens).  wsel: an fp32 tensor
+    shaped like idx to receive the routing weight of every listed block."""
     shape = _route_shape(Q, S, B, decode, kv_len, token)
     b, hq, hkv, nblk = shape.batch, shape.n_q_heads, shape.n_kv_heads, S.shape[2]
     nrow = _nrow(shape, B)
@@ -235,16 +237,19 @@ def route_entmax(Q, S, B, alpha, gamma, cap, force=FORCE_DIAG, n_bins=16, max_it
     probs = torch.empty((b, hq, nrow, nblk), dtype=torch.float32, device=dev) if want_probs else None
     tau = torch.empty((b, hq, nrow), dtype=torch.float32, device=dev) if want_tau else None
     wsb, n = _workspace(OP_ROUTE_ENTMAX, shape, cap, dev, ws)
+    if wsel is not None:
+        assert wsel.shape == idx.shape and wsel.dtype == torch.float32 and wsel.is_contiguous()
     _check(lib.bsa_route_entmax(ctypes.byref(shape), _ptr(Q), _ptr(S), _ptr(kv_lens), alpha, gamma,
                                 n_bins, max_iter, cap, force, score_scale, _ptr(idx), _ptr(cnt),
-                                _ptr(probs), _ptr(tau), _ptr(wsb), n, _stream(Q)))
+                                _ptr(probs), _ptr(tau), _ptr(wsel), _ptr(wsb), n, _stream(Q)))
     return idx, cnt, probs, tau
 
 
 def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None, token=False,
-                   ws=None):
+                   ws=None, wsel=None, sigma=0.0):
     """Causal attention over the selected blocks.  Q [b, Hq, N, d], K/V [b, Hkv, N, d].
-    token=True: idx/cnt are per-token selections [b, Hkv, N, width]."""
+    token=True: idx/cnt are per-token selections [b, Hkv, N, width].
+    wsel (routing weights shaped like idx) and sigma: prior-induced softmax."""
     b, hq, n, d = Q.shape
     hkv = K.shape[1]
     odt = out_dtype or Q.dtype
@@ -252,11 +257,13 @@ def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None,
     shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q),
                        mode=TOKEN if token else PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K,
                        v=V, o=O)
-    wsb, nws = _workspace(OP_ATTEND_PREFILL, shape, idx.shape[-1], Q.device, ws) if token \
-        else (None, 0)
+    op = OP_ATTEND_PREFILL if wsel is None else OP_ATTEND_PREFILL_PRIOR
+    wsb, nws = _workspace(op, shape, idx.shape[-1], Q.device, ws) if token else (None, 0)
+    if wsel is not None:
+        assert wsel.shape == idx.shape and wsel.dtype == torch.float32 and wsel.is_contiguous()
     _check(lib.bsa_attend_prefill(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx),
-                                  _ptr(cnt), idx.shape[-1], sm_scale, _ptr(O), _dtype_code(O),
-                                  _ptr(wsb), nws, _stream(Q)))
+                                  _ptr(cnt), idx.shape[-1], sm_scale, _ptr(wsel), sigma, _ptr(O),
+                                  _dtype_code(O), _ptr(wsb), nws, _stream(Q)))
     return O
 
 
@@ -336,12 +343,25 @@ def prefill_topk(Q, K, V, B, k_total, force=0, S=None, out_dtype=None):
     return attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype), idx, cnt
 
 
+def _wsel_like(Q, S, B, cap, force, token, sigma):
+    if sigma is None:
+        return None
+    b, hkv, nblk = Q.shape[0], S.shape[1], S.shape[2]
+    nrow = Q.shape[2] if token else (Q.shape[2] + B - 1) // B
+    width = cap + bin(force & 7).count("1")
+    return torch.empty((b, hkv, nrow, width), dtype=torch.float32, device=Q.device)
+
+
 def prefill_entmax(Q, K, V, B, alpha, gamma, cap, force=FORCE_DIAG, max_iter=8, S=None,
-                   out_dtype=None):
-    """Stage 0 + alpha-entmax routing + fine attention for causal prefill."""
+                   out_dtype=None, sigma=None):
+    """Stage 0 + alpha-entmax routing + fine attention for causal prefill;
+    sigma (not None): prior-induced softmax with the routing weights."""
     S = summarize(K, B) if S is None else S
-    idx, cnt, _, _ = route_entmax(Q, S, B, alpha, gamma, cap, force, max_iter=max_iter)
-    return attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype), idx, cnt
+    wsel = _wsel_like(Q, S, B, cap, force, False, sigma)
+    idx, cnt, _, _ = route_entmax(Q, S, B, alpha, gamma, cap, force, max_iter=max_iter, wsel=wsel)
+    O = attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype, wsel=wsel,
+                       sigma=sigma or 0.0)
+    return O, idx, cnt
 
 
 def prefill_token_topk(Q, K, V, B, k_total, force=FORCE_DIAG, S=None, out_dtype=None):
@@ -352,11 +372,16 @@ def prefill_token_topk(Q, K, V, B, k_total, force=FORCE_DIAG, S=None, out_dtype=
 
 
 def prefill_token_entmax(Q, K, V, B, alpha, gamma, cap, force=FORCE_DIAG, max_iter=8, S=None,
-                         out_dtype=None):
-    """Stage 0 + per-token alpha-entmax routing + masked fine attention."""
+                         out_dtype=None, sigma=None):
+    """Stage 0 + per-token alpha-entmax routing + masked fine attention;
+    sigma (not None): prior-induced softmax with the routing weights."""
     S = summarize(K, B) if S is None else S
-    idx, cnt, _, _ = route_entmax(Q, S, B, alpha, gamma, cap, force, max_iter=max_iter, token=True)
-    return attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype, token=True), idx, cnt
+    wsel = _wsel_like(Q, S, B, cap, force, True, sigma)
+    idx, cnt, _, _ = route_entmax(Q, S, B, alpha, gamma, cap, force, max_iter=max_iter, token=True,
+                                  wsel=wsel)
+    O = attend_prefill(Q, K, V, B, idx, cnt, out_dtype=out_dtype, token=True, wsel=wsel,
+                       sigma=sigma or 0.0)
+    return O, idx, cnt
 
 
 def decode_topk(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, out_dtype=None):

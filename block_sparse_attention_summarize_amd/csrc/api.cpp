@@ -195,17 +195,19 @@ size_t ws_route_entmax(const bsa_shape* s) {
   const size_t hrows = static_cast<size_t>(s->batch) * s->n_q_heads * nrow_of(s);
   return align_up(hrows * s->head_dim * 4) + align_up(hrows * nblk_of(s) * 4);
 }
-// Per-token attention: the tile masks (uidx, ubits, ucnt) live in ws.
+// Per-token attention: the tile masks (uidx, ubits, ucnt) and, with a prior,
+// the per-query bias of every listed block (ubias) live in ws.
 struct MaskWs {
-  size_t uidx, ubits, ucnt, total;
+  size_t uidx, ubits, ucnt, ubias, total;
 };
-MaskWs mask_ws(const bsa_shape* s) {
+MaskWs mask_ws(const bsa_shape* s, bool prior) {
   const size_t rows = static_cast<size_t>(s->batch) * s->n_kv_heads * ntile_of(s);
   MaskWs w;
   w.uidx = align_up(rows * nblk_of(s) * 4);
   w.ubits = align_up(rows * nblk_of(s) * 8);
   w.ucnt = align_up(rows * 4);
-  w.total = w.uidx + w.ubits + w.ucnt;
+  w.ubias = prior ? align_up(rows * nblk_of(s) * 64 * 4) : 0;
+  w.total = w.uidx + w.ubits + w.ucnt + w.ubias;
   return w;
 }
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -227,8 +229,8 @@ int decode_args(const bsa_shape* s, const void* Q, const void* K, const void* V,
   if (s->mode != BSA_DECODE) return fail(BSA_ERR_INVALID, "decode calls need BSA_DECODE");
   if ((rc = check_ptr("Q", Q)) != BSA_OK) return rc;
   if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
-  if (!std::isfinite(score_scale) || !std::isfinite(sm_scale))
-    return fail(BSA_ERR_INVALID, "scales must be finite");
+  if (!std::isfinite(score_scale) || !std::isfinite(sm_scale) || sm_scale < 0.f)
+    return fail(BSA_ERR_INVALID, "scales must be finite and sm_scale >= 0 (0: 1/sqrt(d))");
   if (route && (rc = check_ptr("S", S)) != BSA_OK) return rc;
   if (attend) {
     if ((rc = check_ptr("K", K)) != BSA_OK) return rc;
@@ -307,7 +309,9 @@ size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
     case BSA_OP_ROUTE_ENTMAX:
       return ws_route_entmax(s);
     case BSA_OP_ATTEND_PREFILL:
-      return s->mode == BSA_TOKEN ? mask_ws(s).total : 0;
+      return s->mode == BSA_TOKEN ? mask_ws(s, false).total : 0;
+    case BSA_OP_ATTEND_PREFILL_PRIOR:
+      return s->mode == BSA_TOKEN ? mask_ws(s, true).total : 0;
     default:
       return 0;
   }
@@ -454,7 +458,8 @@ int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int3
 int bsa_route_entmax(const bsa_shape* s, const void* Q, const float* S, const int32_t* kv_lens,
                      float alpha, float gamma, int32_t n_bins, int32_t max_iter, int32_t cap,
                      uint32_t force, float score_scale, int32_t* idx, int32_t* cnt,
-                     float* probs_out, float* tau_out, void* ws, size_t ws_bytes, void* stream) {
+                     float* probs_out, float* tau_out, float* wsel_out, void* ws, size_t ws_bytes,
+                     void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
   if ((rc = check_force(s, force)) != BSA_OK) return rc;
@@ -515,6 +520,7 @@ int bsa_route_entmax(const bsa_shape* s, const void* Q, const float* S, const in
   ea.cnt = cnt;
   ea.probs = probs_out;
   ea.tau = tau_out;
+  ea.wsel = wsel_out;
   ea.xbuf = xbuf;
   ea.batch = s->batch;
   ea.hq = s->n_q_heads;
@@ -539,7 +545,8 @@ static int attend_common(const bsa_shape* s, const void* Q, const void* K, const
   if ((rc = check_ptr("O", O)) != BSA_OK) return rc;
   if (!idx || !cnt) return fail(BSA_ERR_INVALID, "idx and cnt must not be NULL");
   if (k_max < 1) return fail(BSA_ERR_INVALID, "k_max must be >= 1");
-  if (!std::isfinite(sm_scale)) return fail(BSA_ERR_INVALID, "sm_scale must be finite");
+  if (!std::isfinite(sm_scale) || sm_scale < 0.f)
+    return fail(BSA_ERR_INVALID, "sm_scale must be finite and >= 0 (0: 1/sqrt(d))");
   if (o_dtype != s->dtype && o_dtype != BSA_F32)
     return fail(BSA_ERR_UNSUPPORTED, "o_dtype must be the input dtype or BSA_F32");
   if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
@@ -567,6 +574,9 @@ static int attend_common(const bsa_shape* s, const void* Q, const void* K, const
   a.idx = idx;
   a.cnt = cnt;
   a.bits = nullptr;
+  a.wsel = nullptr;
+  a.tbias = nullptr;
+  a.sigma = 0.f;
   a.batch = s->batch;
   a.hq = s->n_q_heads;
   a.hkv = s->n_kv_heads;
@@ -604,6 +614,9 @@ static int token_mask_args(const bsa_shape* s, const int32_t* idx, const int32_t
   m.nblk = static_cast<int>(nblk_of(s));
   m.ntile = static_cast<int>(ntile_of(s));
   m.q_len = s->q_len;
+  m.wsel = nullptr;
+  m.ubias = nullptr;
+  m.sigma = 0.f;
   return BSA_OK;
 }
 
@@ -618,18 +631,22 @@ int bsa_token_mask(const bsa_shape* s, const int32_t* idx, const int32_t* cnt, i
 
 int bsa_attend_prefill(const bsa_shape* s, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const int32_t* cnt, int32_t k_max, float sm_scale,
-                       void* O, int32_t o_dtype, void* ws, size_t ws_bytes, void* stream) {
+                       const float* wsel, float sigma, void* O, int32_t o_dtype, void* ws,
+                       size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
   if (s->mode == BSA_DECODE)
     return fail(BSA_ERR_INVALID, "bsa_attend_prefill needs BSA_PREFILL or BSA_TOKEN");
+  if (!std::isfinite(sigma)) return fail(BSA_ERR_INVALID, "sigma must be finite");
+  if (wsel && !aligned16(wsel)) return fail(BSA_ERR_UNSUPPORTED, "wsel must be 16-byte aligned");
   bsa::AttendArgs a;
   if ((rc = attend_common(s, Q, K, V, idx, cnt, k_max, sm_scale, O, o_dtype, a)) != BSA_OK)
     return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (s->mode == BSA_TOKEN) {
-    // per-token selections -> tile masks in ws -> masked tile attention
-    const MaskWs mw = mask_ws(s);
+    // per-token selections -> tile masks (and prior bias) in ws -> masked
+    // tile attention
+    const MaskWs mw = mask_ws(s, wsel != nullptr);
     if ((rc = check_ws(ws, ws_bytes, mw.total)) != BSA_OK) return rc;
     char* base = static_cast<char*>(ws);
     bsa::TokenMaskArgs m;
@@ -637,13 +654,22 @@ int bsa_attend_prefill(const bsa_shape* s, const void* Q, const void* K, const v
                               reinterpret_cast<int32_t*>(base + mw.uidx + mw.ubits),
                               reinterpret_cast<uint64_t*>(base + mw.uidx), m)) != BSA_OK)
       return rc;
+    if (wsel) {
+      m.wsel = wsel;
+      m.sigma = sigma;
+      m.ubias = reinterpret_cast<float*>(base + mw.uidx + mw.ubits + mw.ucnt);
+    }
     const hipError_t e = bsa::launch_token_mask(m, st);
     if (e != hipSuccess) return device_status(e, "attend_prefill/token_mask");
     a.idx = m.uidx;
     a.cnt = m.ucnt;
     a.bits = m.ubits;
+    a.tbias = m.ubias;
     a.k_max = m.nblk;
     a.nrow = m.ntile;
+  } else if (wsel) {
+    a.wsel = wsel;
+    a.sigma = sigma;
   }
   return device_status(bsa::launch_attend_prefill(a, st), "attend_prefill");
 }

@@ -18,6 +18,9 @@
 // tokens that did; a query's scores on a block its token did not select are
 // masked to -inf ("DashAttention", Estágio 2, Implementação: active blocks
 // from a bit-packed mask).
+// With a prior (BIAS) the scores of every key of a listed block gain the
+// routing bias sigma * ln w of that block (block rows) or of that block for
+// that query (token tiles), the prior-induced softmax of Estágio 2.
 // Single-token decode lives in decode.hip.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -129,7 +132,7 @@ constexpr int kMaxTilesTok = 512;  // the same with a 64-bit token word per tile
 // is one query head x 16*QT queries of the query block; the workgroup's
 // wavefronts take NW consecutive units of the same (batch, KV head, block),
 // so they share every K/V tile staged in LDS.
-template <int D, int QT, int NW, bool OUT_F32, bool TOK>
+template <int D, int QT, int NW, bool OUT_F32, bool TOK, bool BIAS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArgs a, int wpb) {
   constexpr int NT = NW * 64;
   constexpr int QPW = 16 * QT;  // queries per wave
@@ -142,6 +145,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   __shared__ PrefillLds<D> lds;
   __shared__ int lds_tiles[MAXT];
   __shared__ uint64_t lds_tbits[TOK ? MAXT : 1];
+  // BIAS: the tile's bias in score units (block rows) or its list entry (token tiles)
+  __shared__ float lds_tbias[BIAS && !TOK ? MAXT : 1];
+  __shared__ int lds_tent[BIAS && TOK ? MAXT : 1];
   __shared__ int lds_ntiles;
   using L = PrefillLds<D>;
 
@@ -209,7 +215,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
     for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float sc = a.sm_scale * kLog2e;
+  const float inv_sm = 1.f / a.sm_scale;
   const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+  // token tiles with a prior: this lane's query columns' bias for the current
+  // and the next tile (score units)
+  float bcur[QT], bnxt[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) bcur[qt] = bnxt[qt] = 0.f;
+  auto load_bias = [&](int tt, float (&dst)[QT]) {
+    const float* bp = a.tbias + (rowid * a.k_max + lds_tent[tt]) * 64 + qs * QPW + (lane & 15);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) dst[qt] = bp[qt * 16] * inv_sm;
+  };
 
   uint4 kreg[KITEMS];
   uint4 vreg[KITEMS];
@@ -255,11 +272,25 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
       int c = 0;
       for (int r = 0; r < MAXT && base + r < nraw; r += 64) {
         const int T = base + r + lane;
-        const int64_t k0 = T >= nraw ? -1 : (T < 64 ? walk.key0_of(jpre, T) : walk.key0(T));
+        int64_t k0 = T >= nraw ? -1 : (T < 64 ? walk.key0_of(jpre, T) : walk.key0(T));
+        float tb = 0.f;
+        if constexpr (BIAS && !TOK) {
+          // routing weight of the tile's block: w <= 0 drops it, else ln-bias
+          if (k0 >= 0) {
+            const float wv = a.wsel[rowid * a.k_max + T / nsub];
+            if (wv > 0.f)
+              tb = a.sigma * __logf(wv) * inv_sm;
+            else
+              k0 = -1;
+          }
+        }
         const uint64_t mk = __ballot(k0 >= 0);
         if (k0 >= 0) {
-          lds_tiles[c + lanes_below(mk)] = static_cast<int>(k0);
-          if constexpr (TOK) lds_tbits[c + lanes_below(mk)] = a.bits[rowid * a.k_max + T / nsub];
+          const int pos = c + lanes_below(mk);
+          lds_tiles[pos] = static_cast<int>(k0);
+          if constexpr (TOK) lds_tbits[pos] = a.bits[rowid * a.k_max + T / nsub];
+          if constexpr (BIAS && !TOK) lds_tbias[pos] = tb;
+          if constexpr (BIAS && TOK) lds_tent[pos] = T / nsub;
         }
         c += __popcll(mk);
       }
@@ -270,6 +301,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
     int buf = 0;
     if (ntiles > 0) {
       load_tile(lds_tiles[0]);
+      if constexpr (BIAS && TOK) load_bias(0, bcur);
       store_tile(0);
     }
     // Drain every outstanding vector load (the Q fragments) here, so that the
@@ -280,7 +312,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
     for (int t = 0; t < ntiles; ++t) {
       const int k0 = lds_tiles[t];
       const bool more = t + 1 < ntiles;
-      if (more) load_tile(lds_tiles[t + 1]);
+      if (more) {
+        load_tile(lds_tiles[t + 1]);
+        if constexpr (BIAS && TOK) load_bias(t + 1, bnxt);
+      }
+      // bias of the tile for each query column (score units)
+      float tb[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        if constexpr (BIAS && TOK)
+          tb[qt] = bcur[qt];
+        else if constexpr (BIAS)
+          tb[qt] = lds_tbias[t];
+        else
+          tb[qt] = 0.f;
+      }
       // TOK: bit 16qt + c says whether query qpos0 + 16qt + c selected the
       // tile's block; a wave none of whose queries did skips the tile
       uint64_t qbits = ~0ull;
@@ -338,7 +384,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
           const float t6 = max3f(t3, t4, s[3][qt][3]);
           float v = fmaxf(t5, t6);
           v = xmax16(v);
-          mx[qt] = v * sc;
+          mx[qt] = BIAS ? (v + tb[qt]) * sc : v * sc;
           grow |= mx[qt] > m[qt] + kRescale;
         }
         if (__ballot(grow) != 0) {
@@ -355,7 +401,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
         uint4 pf[QT][2];
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-          const float nb = m[qt] == -INFINITY ? 0.f : -m[qt];
+          float nb = m[qt] == -INFINITY ? 0.f : -m[qt];
+          if constexpr (BIAS) nb = fmaf(tb[qt], sc, nb);
           float p[4][4];
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
@@ -392,6 +439,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
         }
       }
       if (more) store_tile(buf ^ 1);
+      if constexpr (BIAS && TOK) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) bcur[qt] = bnxt[qt];
+      }
       __syncthreads();
       buf ^= 1;
     }
@@ -469,7 +520,17 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
     const int j = list[s];
     if (j < 0 || j >= a.nblk) continue;
     // this lane's token selected block j (always, for block rows)
-    const bool on = !tok || ((a.bits[rowid * a.k_max + s] >> lane) & 1ull);
+    bool on = !tok || ((a.bits[rowid * a.k_max + s] >> lane) & 1ull);
+    // prior: bias of the block for this query, log2 units (scores are too)
+    float bias2 = 0.f;
+    if (a.tbias) {
+      bias2 = a.tbias[(rowid * a.k_max + s) * 64 + lane] * kLog2e;
+    } else if (a.wsel) {
+      const float wv = a.wsel[rowid * a.k_max + s];
+      if (!(wv > 0.f)) continue;
+      bias2 = a.sigma * __log2f(wv);
+    }
+    on = on && bias2 != -INFINITY;
     for (int64_t k0 = static_cast<int64_t>(j) * a.B; k0 < static_cast<int64_t>(j + 1) * a.B;
          k0 += KT) {
       if (k0 > qmax || k0 >= a.kv_len) break;
@@ -489,7 +550,7 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
 #pragma unroll
         for (int c = 0; c < D; ++c) acc = fmaf(q[c], ks[r][c], acc);
         const int64_t key = k0 + r;
-        sv[r] = (key > t || key >= a.kv_len || !on) ? -INFINITY : acc;
+        sv[r] = (key > t || key >= a.kv_len || !on) ? -INFINITY : acc + bias2;
         mx = fmaxf(mx, sv[r]);
       }
       const float mnew = fmaxf(m, mx);
@@ -515,25 +576,28 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
   for (int c = 0; c < D; ++c) Og[c] = o[c] * inv;
 }
 
-template <int D, int QT, int NW, bool TOK>
+template <int D, int QT, int NW, bool TOK, bool BIAS>
 hipError_t prefill_bf16_launch(const AttendArgs& a, hipStream_t stream) {
   const int G = a.hq / a.hkv;
   const int units = G * ((TOK ? 64 : a.B) / (16 * QT));
   const int wpb = (units + NW - 1) / NW;
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow * wpb;
   if (a.out_f32)
-    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, true, TOK>), dim3(grid), dim3(NW * 64), 0,
-                       stream, a, wpb);
+    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, true, TOK, BIAS>), dim3(grid),
+                       dim3(NW * 64), 0, stream, a, wpb);
   else
-    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, false, TOK>), dim3(grid), dim3(NW * 64), 0,
-                       stream, a, wpb);
+    hipLaunchKernelGGL((attend_prefill_bf16<D, QT, NW, false, TOK, BIAS>), dim3(grid),
+                       dim3(NW * 64), 0, stream, a, wpb);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t prefill_bf16_dispatch(const AttendArgs& a, hipStream_t stream) {
-  return a.bits ? prefill_bf16_launch<D, 2, 4, true>(a, stream)
-                : prefill_bf16_launch<D, 2, 4, false>(a, stream);
+  if (a.bits)
+    return a.tbias ? prefill_bf16_launch<D, 2, 4, true, true>(a, stream)
+                   : prefill_bf16_launch<D, 2, 4, true, false>(a, stream);
+  return a.wsel ? prefill_bf16_launch<D, 2, 4, false, true>(a, stream)
+                : prefill_bf16_launch<D, 2, 4, false, false>(a, stream);
 }
 
 }  // namespace

@@ -76,6 +76,8 @@ struct EntmaxArgs {
   int32_t* cnt;
   float* probs;       // optional [batch, hq, nrow, nblk]
   float* tau;         // optional [batch, hq, nrow]
+  float* wsel;        // optional [batch, hkv, nrow, width]: group-mean p of each listed
+                      // block, 1 for forced blocks, 0 padded
   float* xbuf;        // logits from the scores kernel [batch, hq, nrow, nblk]; overwritten
                       // with the probabilities
   int batch, hq, hkv, nrow, nblk, width, cap, max_iter;
@@ -97,6 +99,14 @@ struct AttendArgs {
   // Otherwise row i is the query tile [64i, 64i+64), idx/cnt its active
   // blocks and bits[row, e] the tile's tokens that selected block idx[row, e].
   const uint64_t* bits;
+  // Prior-induced softmax (nullptr: plain softmax).  Block rows: wsel holds
+  // the routing weight w of every entry of idx (layout of idx); the scores of
+  // its keys gain sigma * ln w, and an entry with w <= 0 is skipped.  Token
+  // tiles: tbias [row, entry, 64 queries] holds that bias per query already
+  // (-inf where the query's token did not select the block).
+  const float* wsel;
+  const float* tbias;
+  float sigma;
   int batch, hq, hkv, d, B, k_max, nrow, nblk;
   int64_t q_len, kv_len;
   float sm_scale;
@@ -113,6 +123,11 @@ struct TokenMaskArgs {
   int32_t* uidx;   // [batch, hkv, ntile, nblk]
   int32_t* ucnt;   // [batch, hkv, ntile]
   uint64_t* ubits; // [batch, hkv, ntile, nblk]
+  // optional prior: per-token weights wsel [batch, hkv, q_len, width] ->
+  // ubias [batch, hkv, ntile, nblk, 64] = sigma * ln w (-inf: not selected)
+  const float* wsel;
+  float* ubias;
+  float sigma;
   int batch, hkv, width, nblk, ntile;
   int64_t q_len;
 };

@@ -6,7 +6,10 @@
 //
 // One workgroup per tile: the tile's selection rows are contiguous, so they
 // are read coalesced and OR-ed into one LDS word per block (ds_or_b64); a
-// workgroup scan then compacts the non-zero words in block order.
+// workgroup scan then compacts the non-zero words in block order.  With
+// routing weights, the tile's prior bias sigma * ln w of every (listed block,
+// query) is laid out next to it, -inf where the query did not select the
+// block (the prior-induced softmax of Estágio 2).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -18,7 +21,7 @@ namespace {
 constexpr int kMaskThreads = 256;
 
 __global__ __launch_bounds__(kMaskThreads) void token_mask_kernel(TokenMaskArgs a) {
-  extern __shared__ unsigned long long words[];  // [nblk]
+  extern __shared__ unsigned long long words[];  // [nblk], then the bias pass's int posmap[nblk]
   __shared__ int cnts[64];
   __shared__ int wave_tot[kMaskThreads / kWave];
   const int tid = threadIdx.x;
@@ -51,8 +54,28 @@ __global__ __launch_bounds__(kMaskThreads) void token_mask_kernel(TokenMaskArgs 
     if (wv != 0ull) {
       a.uidx[out + pos] = j;
       a.ubits[out + pos] = wv;
+      if (a.ubias) reinterpret_cast<int*>(words + a.nblk)[j] = pos;
     }
     base += tot;
+  }
+  if (a.ubias) {
+    // every (listed block, query) slot starts at -inf; the selecting tokens
+    // then write their own (a barrier orders the two stores to one slot)
+    float* ub = a.ubias + out * 64;
+    for (int e = tid; e < base * 64; e += kMaskThreads) ub[e] = -INFINITY;
+    __syncthreads();
+    const int* posmap = reinterpret_cast<const int*>(words + a.nblk);
+    const float* wsrc = a.wsel + (bg * a.q_len + t0) * a.width;
+    for (int e = tid; e < ntok * a.width; e += kMaskThreads) {
+      const int r = e / a.width;
+      if (e - r * a.width < cnts[r]) {
+        const int j = src[e];
+        if (j >= 0 && j < a.nblk) {
+          const float wv = wsrc[e];
+          ub[posmap[j] * 64 + r] = wv > 0.f ? a.sigma * __logf(wv) : -INFINITY;
+        }
+      }
+    }
   }
   for (int u = base + tid; u < a.nblk; u += kMaskThreads) {
     a.uidx[out + u] = -1;
@@ -65,7 +88,7 @@ __global__ __launch_bounds__(kMaskThreads) void token_mask_kernel(TokenMaskArgs 
 
 hipError_t launch_token_mask(const TokenMaskArgs& a, hipStream_t stream) {
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.ntile;
-  const size_t lds = static_cast<size_t>(a.nblk) * sizeof(unsigned long long);
+  const size_t lds = static_cast<size_t>(a.nblk) * (sizeof(unsigned long long) + (a.ubias ? 4 : 0));
   hipLaunchKernelGGL(token_mask_kernel, dim3(grid), dim3(kMaskThreads), lds, stream, a);
   return hipGetLastError();
 }

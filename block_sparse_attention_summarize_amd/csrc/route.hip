@@ -467,12 +467,22 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
     const int lead = (ri.f0 == 0 && (a.rule.force & 2u)) ? 1 : 0;
     const int tail0 = (!lead && ri.f0 >= 0) ? ri.f0 : -1;
     const int total = lead + nr + (tail0 >= 0) + (ri.f1 >= 0);
+    float* wsel = a.wsel ? a.wsel + static_cast<int64_t>(rowid) * a.width : nullptr;
     for (int p = threadIdx.x; p < a.width; p += kThreads) {
       int v = -1;
-      if (p < lead) v = 0;
-      else if (p < lead + nr) v = fi[p - lead];
-      else if (p < total) v = (p == lead + nr && tail0 >= 0) ? tail0 : ri.f1;
+      float wv = 0.f;
+      if (p < lead) {
+        v = 0;
+        wv = 1.f;
+      } else if (p < lead + nr) {
+        v = fi[p - lead];
+        wv = wsel ? wbar(v) : 0.f;
+      } else if (p < total) {
+        v = (p == lead + nr && tail0 >= 0) ? tail0 : ri.f1;
+        wv = 1.f;
+      }
       idx[p] = v;
+      if (wsel) wsel[p] = wv;
     }
     if (threadIdx.x == 0) a.cnt[rowid] = total;
     return;
@@ -493,9 +503,14 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
     key = float_key(v);
     return true;
   };
+  float* wsel = a.wsel ? a.wsel + static_cast<int64_t>(rowid) * a.width : nullptr;
   const int c = select_and_write<kThreads>(
-      ri, ri.span, a.cap, n_elig, get, [&](int p, int e) { idx[p] = e; }, a.width, hist, bcast,
-      wave_tot);
+      ri, ri.span, a.cap, n_elig, get,
+      [&](int p, int e) {
+        idx[p] = e;
+        if (wsel) wsel[p] = e < 0 ? 0.f : (is_forced(ri, e) ? 1.f : wbar(e));
+      },
+      a.width, hist, bcast, wave_tot);
   if (threadIdx.x == 0) a.cnt[rowid] = c;
 }
 

@@ -94,7 +94,8 @@ typedef enum {
   BSA_OP_ROUTE_ENTMAX = 2,
   BSA_OP_ATTEND_PREFILL = 3,
   BSA_OP_ATTEND_DECODE = 4,
-  BSA_OP_DECODE_TOPK = 5
+  BSA_OP_DECODE_TOPK = 5,
+  BSA_OP_ATTEND_PREFILL_PRIOR = 6 /* bsa_attend_prefill with wsel != NULL */
 } bsa_op;
 
 /* Problem description, read only during the call. */
@@ -190,14 +191,19 @@ int bsa_route_topk(const bsa_shape *shape, const void *Q, const float *S,
  *   probs_out NULL or fp32 [batch, Hq, n_rows, n_blk] (0 outside candidates).
  *   tau_out   NULL or fp32 [batch, Hq, n_rows] (NaN for rows without
  *             candidates).
+ *   wsel_out  NULL or fp32 [batch, Hkv, n_rows, cap + #forced], the layout of
+ *             idx: the routing weight w of each listed block -- the group's
+ *             mean probability for a routed block, 1 for a forced block (it
+ *             has no routing score), 0 in the padding.  Input of the
+ *             prior-induced softmax of bsa_attend_prefill.
  * Errors: BSA_ERR_INVALID (alpha <= 1, n_bins != 16, max_iter outside
  * [0, 32], cap < 1, TAIL in prefill), BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
  */
 int bsa_route_entmax(const bsa_shape *shape, const void *Q, const float *S,
                      const int32_t *kv_lens, float alpha, float gamma, int32_t n_bins,
                      int32_t max_iter, int32_t cap, uint32_t force_flags, float score_scale,
-                     int32_t *idx, int32_t *cnt, float *probs_out, float *tau_out, void *ws,
-                     size_t ws_bytes, void *stream);
+                     int32_t *idx, int32_t *cnt, float *probs_out, float *tau_out,
+                     float *wsel_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Stage 2, causal prefill ("DashAttention", Estágio 2 without routing bias).
@@ -207,18 +213,27 @@ int bsa_route_entmax(const bsa_shape *shape, const void *Q, const float *S,
  *   O     out [batch, Hq, q_len, d] with o_stride, dtype o_dtype: shape->dtype
  *         or BSA_F32 (full-precision output for bf16 inputs).
  *   k_max width of idx.
- *   Token mode (shape->mode == BSA_TOKEN): idx/cnt are per-token selections
+ *   sm_scale  >= 0; 0 means 1/sqrt(d).
+ *   wsel, sigma  prior-induced softmax ("DashAttention", Estágio 2): NULL for
+ *         the plain softmax, else fp32 routing weights in the layout of idx
+ *         (wsel_out of bsa_route_entmax).  The softmax is taken against the
+ *         reference g that gives each key of listed block j the weight
+ *         w_j^sigma, i.e. those keys' logits gain sigma * ln w_j; a listed
+ *         block with w_j <= 0 is dropped (g = 0).  sigma must be finite.
+ *   Token mode (shape->mode == BSA_TOKEN): idx/cnt (and wsel) are per-token
  *   [batch, Hkv, q_len, k_max] and query t attends over idx[b, g(h), t, :cnt].
  *   The call first builds the 64-query tile masks of bsa_token_mask in ws
- *   (bsa_workspace_size(BSA_OP_ATTEND_PREFILL, ...) bytes, 256-byte aligned,
- *   scratch afterwards), then attends tile by tile over the active blocks,
- *   masking each query's scores on blocks its token did not select.  In
- *   prefill mode ws is unused.
+ *   (bsa_workspace_size(BSA_OP_ATTEND_PREFILL, ...) bytes, or
+ *   BSA_OP_ATTEND_PREFILL_PRIOR with wsel, which adds each tile's per-query
+ *   bias; 256-byte aligned, scratch afterwards), then attends tile by tile
+ *   over the active blocks, masking each query's scores on blocks its token
+ *   did not select.  In prefill mode ws is unused.
  * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
  */
 int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                        const int32_t *idx, const int32_t *cnt, int32_t k_max, float sm_scale,
-                       void *O, int32_t o_dtype, void *ws, size_t ws_bytes, void *stream);
+                       const float *wsel, float sigma, void *O, int32_t o_dtype, void *ws,
+                       size_t ws_bytes, void *stream);
 
 /*
  * Active-block masks of per-token selections ("DashAttention", Estágio 2,

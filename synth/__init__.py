@@ -62,6 +62,7 @@ class Workload:
     amp: float = 3.0
     kv_lens: tuple = ()  # decode only; empty -> all equal to n
     loc_amp: float = 0.0  # query-tile component amplitude
+    sigma: float = 0.0  # prior strength of the fine softmax (entmax routing); 0: plain softmax
 
     @property
     def nblk(self) -> int:
@@ -113,11 +114,12 @@ WORKLOADS = {
         k_total=32, force=FORCE_DIAG | FORCE_FIRST, seed=4, planted_blocks=64,
         planted_query_frac=0.01),
     # every query token routed on its own (alpha-entmax per token), queries
-    # with 64-token locality; attention over the active blocks of 64-query tiles
+    # with 64-token locality; attention over the active blocks of 64-query
+    # tiles with the routing weights as the softmax prior (sigma = 1)
     "token_entmax_prefill_n32k": Workload(
         "token_entmax_prefill_n32k", "bf16", 1, 32, 8, 32768, 128, 64, "token", "entmax",
         alpha=1.5, gamma=4.0, cap=32, n_bins=16, max_iter=8, force=FORCE_DIAG, seed=5,
-        planted_blocks=32, planted_query_frac=0.01, loc_amp=4.0),
+        planted_blocks=32, planted_query_frac=0.01, loc_amp=4.0, sigma=1.0),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

@@ -54,13 +54,14 @@ def topk(s, k=4, force=0, ws_bytes=None, Q=FAKE, S=FAKE, idx=FAKE, cnt=FAKE, sca
 def entmax(s, alpha=1.5, n_bins=16, max_iter=8, cap=64, force=1):
     n = lib.bsa_workspace_size(bsa.OP_ROUTE_ENTMAX, ctypes.byref(s), cap)
     return lib.bsa_route_entmax(ctypes.byref(s), FAKE, FAKE, None, alpha, 1.0, n_bins, max_iter,
-                                cap, force, 0.0, FAKE, FAKE, None, None,
+                                cap, force, 0.0, FAKE, FAKE, None, None, None,
                                 ctypes.c_void_p(0x200000), n, None)
 
 
-def prefill(s, k_max=4, o_dtype=None, Q=FAKE, O=FAKE):
-    return lib.bsa_attend_prefill(ctypes.byref(s), Q, FAKE, FAKE, FAKE, FAKE, k_max, 0.0, O,
-                                  s.dtype if o_dtype is None else o_dtype, None, 0, None)
+def prefill(s, k_max=4, o_dtype=None, Q=FAKE, O=FAKE, sm_scale=0.0, wsel=None, sigma=0.0):
+    return lib.bsa_attend_prefill(ctypes.byref(s), Q, FAKE, FAKE, FAKE, FAKE, k_max, sm_scale,
+                                  wsel, sigma, O, s.dtype if o_dtype is None else o_dtype, None, 0,
+                                  None)
 
 
 def test_shape_validation():
@@ -115,6 +116,9 @@ def test_route_entmax_validation():
 def test_attend_validation():
     assert prefill(shape(), k_max=0) == -1
     assert prefill(shape(), o_dtype=5) == -2
+    assert prefill(shape(), sm_scale=-0.1) == -1 and "sm_scale" in err()
+    assert prefill(shape(), wsel=FAKE, sigma=float("inf")) == -1 and "sigma" in err()
+    assert prefill(shape(), wsel=ctypes.c_void_p(0x100004), sigma=1.0) == -2
     assert prefill(shape(mode=bsa.DECODE, q_len=1)) == -1 and "PREFILL" in err()
     s = shape(mode=bsa.DECODE, q_len=1, hq=9, hkv=1)  # 9 heads per KV head: no even split
     assert lib.bsa_attend_decode(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 0.0, FAKE,
@@ -187,8 +191,15 @@ def test_token_mode_validation_and_workspace():
     assert topk(s, force=bsa.FORCE_TAIL) == -1 and "decode" in err()
     assert topk(shape(mode=bsa.TOKEN, q_len=128)) == -1 and "q_len == kv_len" in err()
     # the tile masks need their workspace
+    assert lib.bsa_attend_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.0, None,
+                                  0.0, FAKE, bsa.BF16, ctypes.c_void_p(0x200000), need - 1,
+                                  None) == -4
+    # with routing weights the tiles' per-query bias is added
+    prior = lib.bsa_workspace_size(bsa.OP_ATTEND_PREFILL_PRIOR, ctypes.byref(s), 4)
+    assert prior == need + al(trows * nblk * 64 * 4)
     assert lib.bsa_attend_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.0, FAKE,
-                                  bsa.BF16, ctypes.c_void_p(0x200000), need - 1, None) == -4
+                                  1.0, FAKE, bsa.BF16, ctypes.c_void_p(0x200000), prior - 1,
+                                  None) == -4
     mask = lambda sh, idx=FAKE, width=4: lib.bsa_token_mask(ctypes.byref(sh), idx, FAKE, width,
                                                              FAKE, FAKE, FAKE, None)
     assert mask(shape()) == -1 and "BSA_TOKEN" in err()

@@ -161,13 +161,15 @@ def test_full_token_entmax_prefill():
     print(f"[full token entmax prefill] {w}", flush=True)
     x = parity.make(w)
     S = bsa.summarize(x["K"], w.B)
+    wsel = torch.empty((w.batch, w.hkv, w.n, w.idx_width), dtype=torch.float32, device="cuda")
     idx, cnt, probs, tau = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
                                             max_iter=w.max_iter, want_probs=True, want_tau=True,
-                                            token=True)
-    O = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt, token=True)
+                                            token=True, wsel=wsel)
+    O = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt, token=True, wsel=wsel,
+                           sigma=w.sigma)
     uidx, ucnt, ubits = bsa.token_mask(idx, cnt, w.B)
     torch.cuda.synchronize()
-    gi, gc = _cpu(idx), _cpu(cnt)
+    gi, gc, gw = _cpu(idx), _cpu(cnt), _cpu(wsel)
     Sref = oracle.summarize(x["k"], w.B)
     assert np.abs(_cpu(S) - Sref).max() < 2e-6
     rng = np.random.default_rng(w.seed + 200)
@@ -189,6 +191,7 @@ def test_full_token_entmax_prefill():
         row_clear = clear.reshape(w.batch, w.hkv, -1).all(-1) & (one["capgap"][:, :, 0] > parity.GAP)
         same = (gi[:, :, t] == one["idx"][:, :, 0]).all(-1) & (gc[:, :, t] == one["cnt"][:, :, 0])
         assert same[row_clear].all(), f"token {t}: clear rows differ"
+        assert np.abs(gw[:, :, t] - one["wsel"][:, :, 0])[row_clear].max(initial=0) < 2e-5
         for g in np.nonzero(~same[0])[0]:
             sel = gi[0, g, t, :gc[0, g, t]]
             assert t // w.B in sel and np.all(np.diff(sel) > 0) and sel.max() <= t // w.B
@@ -207,7 +210,7 @@ def test_full_token_entmax_prefill():
     req = np.array([[0, h, t] for tl in tiles for h in range(w.hq)
                     for t in range(tl * 64, min(tl * 64 + 64, w.n))], np.int64)
     ref, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, gi, gc, req=req,
-                               mode=oracle.MODE_TOKEN)
+                               mode=oracle.MODE_TOKEN, wsel=gw, sigma=w.sigma)
     got = _cpu(O)[req[:, 0], req[:, 1], req[:, 2]]
     worst = parity.check_attention(w, got, ref, False)
     print(f"attention: tiles {tiles}, {len(req)} rows, {int(pairs.sum())} pairs, "

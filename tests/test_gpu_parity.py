@@ -177,8 +177,10 @@ def test_route_entmax(name):
     print(f"[route_entmax] {name}", flush=True)
     x = parity.make(w)
     S = bsa.summarize(x["K"], w.B)
+    wsel = torch.empty((w.batch, w.hkv, w.nblk, w.idx_width), dtype=torch.float32, device="cuda")
     idx, cnt, probs, tau = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
-                                            max_iter=w.max_iter, want_probs=True, want_tau=True)
+                                            max_iter=w.max_iter, want_probs=True, want_tau=True,
+                                            wsel=wsel)
     ref = oracle.route_entmax(oracle.qpool(x["q"], w.B), oracle.summarize(x["k"], w.B), w.B,
                               w.alpha, w.gamma, w.cap, w.force, max_iter=w.max_iter)
     gp, gt = _cpu(probs), _cpu(tau)
@@ -193,12 +195,67 @@ def test_route_entmax(name):
     row_clear = clear.reshape(w.batch, w.hkv, w.hq // w.hkv, -1).all(axis=2) & (ref["capgap"] > parity.GAP)
     same = (gi == ref["idx"]).all(-1) & (gc == ref["cnt"])
     assert same[row_clear].all(), f"{int((~same & row_clear).sum())} clear rows differ"
+    # routing weights of the listed blocks (group-mean p, 1 when forced)
+    gw = _cpu(wsel)
+    assert np.abs(gw - ref["wsel"])[row_clear].max(initial=0) < 2e-5
     # every row: the diagonal is present, ids ascending and within the causal range
     for r in zip(*np.nonzero(~same)):
         sel = gi[r][:gc[r]]
         assert r[2] in sel and np.all(np.diff(sel) > 0) and sel.max() <= r[2]
     print(f"rows {same.size}, clear {int(row_clear.sum())}, match {same.mean():.4f}, "
           f"mean support {float((ref['probs'] > 0).sum(-1).mean()):.1f}")
+
+
+@pytest.mark.parametrize("sigma", [0.5, 1.0])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_prior_induced_attention(sigma, out_f32):
+    """Entmax routing weights as the prior of the fine softmax: the scores of
+    each listed block's keys gain sigma * ln w."""
+    w = ENTMAX["entmax_g8_cap8"]
+    print(f"[prior attention] sigma={sigma} out_f32={out_f32}", flush=True)
+    x = parity.make(w)
+    O, idx, cnt = bsa.prefill_entmax(x["Q"], x["K"], x["V"], w.B, w.alpha, w.gamma, w.cap,
+                                     out_dtype=torch.float32 if out_f32 else None, sigma=sigma)
+    # the same selection's weights, as the pipeline computed them
+    S = bsa.summarize(x["K"], w.B)
+    wsel = torch.empty(idx.shape, dtype=torch.float32, device="cuda")
+    bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force, wsel=wsel)
+    ref, _ = oracle.attend(x["q"], x["k"], x["v"], w.B, _cpu(idx), _cpu(cnt), wsel=_cpu(wsel),
+                           sigma=sigma)
+    plain, _ = oracle.attend(x["q"], x["k"], x["v"], w.B, _cpu(idx), _cpu(cnt))
+    worst = parity.check_attention(w, _cpu(O).reshape(ref.shape), ref, out_f32)
+    print(f"max abs err {worst:.3e}; the prior moves the output by {np.abs(ref - plain).max():.3e}")
+
+
+def test_prior_weights_zero_and_forced():
+    """Hand-set weights: zero drops a block, 1 leaves it unbiased."""
+    w = SMALL["bf16_gqa"]
+    x = parity.make(w)
+    S = bsa.summarize(x["K"], w.B)
+    idx, cnt = bsa.route_topk(x["Q"], S, w.B, w.k_total, w.force)
+    rng = np.random.default_rng(5)
+    wh = rng.uniform(0.01, 1.0, idx.shape).astype(np.float32)
+    wh[rng.random(idx.shape) < 0.2] = 0.0
+    wsel = torch.from_numpy(wh).cuda()
+    O = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt, out_dtype=torch.float32,
+                           wsel=wsel, sigma=0.8)
+    ref, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, _cpu(idx), _cpu(cnt), wsel=wh,
+                               sigma=0.8)
+    Oh = _cpu(O).reshape(ref.shape)
+    parity.check_attention(w, Oh, ref, True)
+    assert np.all(Oh[pairs == 0] == 0)
+    # fp32 inputs: the VALU kernel
+    wf = SMALL["fp32_d128_ragged"]
+    xf = parity.make(wf)
+    Sf = bsa.summarize(xf["K"], wf.B)
+    idx, cnt = bsa.route_topk(xf["Q"], Sf, wf.B, wf.k_total, wf.force)
+    wh = rng.uniform(0.01, 1.0, idx.shape).astype(np.float32)
+    wh[rng.random(idx.shape) < 0.2] = 0.0
+    O = bsa.attend_prefill(xf["Q"], xf["K"], xf["V"], wf.B, idx, cnt,
+                           wsel=torch.from_numpy(wh).cuda(), sigma=1.3)
+    ref, _ = oracle.attend(xf["q"], xf["k"], xf["v"], wf.B, _cpu(idx), _cpu(cnt), wsel=wh,
+                           sigma=1.3)
+    parity.check_attention(wf, _cpu(O).reshape(ref.shape), ref, True)
 
 
 def test_prefill_entmax_pipeline_attention():

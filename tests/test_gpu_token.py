@@ -75,9 +75,10 @@ def test_token_route_entmax(name):
     print(f"[token route_entmax] {name}", flush=True)
     x = parity.make(w)
     S = bsa.summarize(x["K"], w.B)
+    wsel = torch.empty((w.batch, w.hkv, w.n, w.idx_width), dtype=torch.float32, device="cuda")
     idx, cnt, probs, tau = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
                                             max_iter=w.max_iter, want_probs=True, want_tau=True,
-                                            token=True)
+                                            token=True, wsel=wsel)
     ref = oracle.route_entmax(x["q"].astype(np.float64), oracle.summarize(x["k"], w.B), w.B,
                               w.alpha, w.gamma, w.cap, w.force, max_iter=w.max_iter,
                               mode=oracle.MODE_TOKEN)
@@ -93,6 +94,7 @@ def test_token_route_entmax(name):
                  & (ref["capgap"] > parity.GAP))
     same = (gi == ref["idx"]).all(-1) & (gc == ref["cnt"])
     assert same[row_clear].all(), f"{int((~same & row_clear).sum())} clear rows differ"
+    assert np.abs(_cpu(wsel) - ref["wsel"])[row_clear].max(initial=0) < 2e-5
     for r in zip(*np.nonzero(~same)):
         sel = gi[r][:gc[r]]
         own = r[2] // w.B
@@ -199,6 +201,53 @@ def test_token_entmax_pipeline_attention(name):
     print(f"max abs err {worst:.3e}")
 
 
+@pytest.mark.parametrize("name", ["tok_entmax_g4", "tok_entmax_a2"])
+@pytest.mark.parametrize("sigma", [0.5, 1.0])
+def test_token_prior_induced_attention(name, sigma):
+    """Per-token entmax weights as each query's own prior: the tile kernel
+    adds sigma * ln w of the query's token for every listed block."""
+    w = ENTMAX[name]
+    print(f"[token prior attention] {name} sigma={sigma}", flush=True)
+    x = parity.make(w)
+    O, idx, cnt = bsa.prefill_token_entmax(x["Q"], x["K"], x["V"], w.B, w.alpha, w.gamma, w.cap,
+                                           max_iter=w.max_iter, out_dtype=torch.float32,
+                                           sigma=sigma)
+    S = bsa.summarize(x["K"], w.B)
+    wsel = torch.empty(idx.shape, dtype=torch.float32, device="cuda")
+    bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force, max_iter=w.max_iter,
+                     token=True, wsel=wsel)
+    ref, _ = oracle.attend(x["q"], x["k"], x["v"], w.B, _cpu(idx), _cpu(cnt),
+                           mode=oracle.MODE_TOKEN, wsel=_cpu(wsel), sigma=sigma)
+    worst = parity.check_attention(w, _cpu(O).reshape(ref.shape), ref, True)
+    print(f"max abs err {worst:.3e}")
+
+
+@pytest.mark.parametrize("name", ["tok_bf16_gqa", "tok_f32_d128", "tok_b128_noforce"])
+def test_token_prior_random_weights(name):
+    """Varied per-token selections and hand-set weights (some zero: the
+    block drops out for that token only)."""
+    w = TOPK[name]
+    x = parity.make(w)
+    rng = np.random.default_rng(w.seed + 123)
+    ri, rc, ci, cc = _random_token_selection(rng, w, 4, p_invalid=0.03)
+    wh = rng.uniform(0.01, 1.0, ri.shape).astype(np.float32)
+    wh[rng.random(ri.shape) < 0.15] = 0.0
+    # the oracle's copy keeps the weights of the valid ids, in their order
+    wc = np.zeros(ci.shape)
+    for r in zip(*np.nonzero(rc)):
+        keep = [wh[r][s] for s in range(rc[r]) if 0 <= ri[r][s] < w.nblk]
+        wc[r][:len(keep)] = keep
+    O = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, torch.from_numpy(ri).cuda(),
+                           torch.from_numpy(rc).cuda(), out_dtype=torch.float32, token=True,
+                           wsel=torch.from_numpy(wh).cuda(), sigma=0.7)
+    ref, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, ci, cc, mode=oracle.MODE_TOKEN,
+                               wsel=wc, sigma=0.7)
+    Oh = _cpu(O).reshape(ref.shape)
+    worst = parity.check_attention(w, Oh, ref, True)
+    assert np.all(Oh[pairs == 0] == 0)
+    print(f"max abs err {worst:.3e}, empty rows {int((pairs == 0).sum())}")
+
+
 def test_token_all_blocks_equals_dense_attention():
     """k covering every causal block: per-token routing selects everything
     and the masked attention is dense causal attention."""
@@ -233,5 +282,6 @@ def test_token_mode_argument_errors():
     import ctypes
     rc = bsa.lib.bsa_attend_prefill(ctypes.byref(shape), bsa._ptr(x["Q"]), bsa._ptr(x["K"]),
                                     bsa._ptr(x["V"]), bsa._ptr(idx), bsa._ptr(cnt), w.k_total,
-                                    0.0, bsa._ptr(O), bsa.BF16, bsa._ptr(small), need // 2, None)
+                                    0.0, None, 0.0, bsa._ptr(O), bsa.BF16, bsa._ptr(small),
+                                    need // 2, None)
     assert rc == -4  # BSA_ERR_WORKSPACE, nothing enqueued
