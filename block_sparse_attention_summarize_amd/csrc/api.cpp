@@ -440,7 +440,7 @@ int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int3
   sa.d = s->head_dim;
   sa.scale = score_scale != 0.f ? score_scale : 1.f / std::sqrt(static_cast<float>(s->head_dim));
   sa.rule = rule_of(s, 0, force, kv_lens);
-  e = bsa::launch_scores(sa, st);
+  e = bsa::launch_scores(sa, st, scores_out != nullptr);
   if (e != hipSuccess) return device_status(e, "route_topk/scores");
   bsa::SelectArgs se;
   se.scores = scores;
@@ -513,7 +513,7 @@ int bsa_route_entmax(const bsa_shape* s, const void* Q, const float* S, const in
   sa.d = s->head_dim;
   sa.scale = (alpha - 1.f) * gamma * scale;
   sa.rule = rule_of(s, 1, force, kv_lens);
-  e = bsa::launch_scores(sa, st);
+  e = bsa::launch_scores(sa, st, false);
   if (e != hipSuccess) return device_status(e, "route_entmax/scores");
   bsa::EntmaxArgs ea;
   ea.idx = idx;

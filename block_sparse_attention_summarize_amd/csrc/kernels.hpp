@@ -60,7 +60,9 @@ struct ScoreArgs {
   float scale;
   RowRule rule;
 };
-hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream);
+// fill: also write -inf over whole tiles beyond every row's candidates (a
+// caller-visible score matrix); otherwise only tiles holding candidates.
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream, bool fill);
 
 struct SelectArgs {
   const float* scores;  // [rows, nblk]

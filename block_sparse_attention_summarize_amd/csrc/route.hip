@@ -75,17 +75,24 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill scores: one workgroup per 64 rows x 64 blocks tile of one (b, g).
-// The q-hat and summary tiles are staged in LDS (rows padded by 4 floats);
-// thread (tr, tj) accumulates rows tr + 16m and blocks tj + 16n, m, n < 4.
-// Tiles right of every row's candidates only write -inf (the candidate end
-// grows with the row in prefill).
+// Prefill and per-token scores: one workgroup per 64 rows x 64 blocks tile of
+// one (b, q-hat head).  The q-hat and summary tiles are staged in LDS (rows
+// padded by 4 floats; reads outside the rows present return zeros), and the
+// tile runs on the fp32 matrix cores: wavefront w owns rows 16w..16w+15 as
+// four 16 x 16 accumulators (v_mfma_f32_16x16x4_f32).
+// Lane l reads 4 consecutive d of its row (A) and of its block (B) from LDS
+// and feeds them to four MFMAs, so each MFMA's k-slice is {c, c+4, c+8, c+12}
+// of a 16-wide d chunk: the dot products run over every d exactly once, in
+// fp32 products and fp32 accumulation as on the VALU.  Unless `fill`, tiles
+// right of every row's candidates (the candidate end grows with the row) are
+// not written at all (their readers only look at the candidates).
 // ---------------------------------------------------------------------------
 constexpr int kTile = 64;
 constexpr int kPad = 4;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
+__global__ __launch_bounds__(kThreads) void scores_mfma(ScoreArgs a, int fill) {
   __shared__ float qs[kTile][D + kPad];
   __shared__ float ss[kTile][D + kPad];
   const int nrt = (a.nrow + kTile - 1) / kTile;
@@ -102,11 +109,10 @@ __global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
   const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   float* out = a.scores + (static_cast<int64_t>(bh) * a.nrow + r0) * a.nblk + j0;
-  // candidates of row r: blocks before own(r) (entmax) or up to it (top-k),
-  // own(r) = r for query-block rows and r / B for token rows
   const int ce = a.rule.entmax ? 0 : 1;
   const int tok_b = a.rule.mode == 2 ? a.rule.B : 1;
   if (j0 >= (r0 + rn - 1) / tok_b + ce) {  // right of the last row's candidates
+    if (!fill) return;
     for (int e = tid; e < kTile * kTile; e += kThreads) {
       const int r = e / kTile, j = e % kTile;
       if (r < rn && j < jn) out[static_cast<int64_t>(r) * a.nblk + j] = -INFINITY;
@@ -116,7 +122,6 @@ __global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
   constexpr int V4 = D / 4;
   const float* qg = a.qhat + (static_cast<int64_t>(bh) * a.nrow + r0) * D;
   const float* sg = a.S + (static_cast<int64_t>(sg_row) * a.nblk + j0) * D;
-  // rows past the ends read as zeros (buffer loads outside the extent)
   const auto rq = make_rsrc(qg, static_cast<uint32_t>(rn) * D * 4);
   const auto rs = make_rsrc(sg, static_cast<uint32_t>(jn) * D * 4);
   for (int e = tid; e < kTile * V4; e += kThreads) {
@@ -125,40 +130,34 @@ __global__ __launch_bounds__(kThreads) void scores_tiled(ScoreArgs a) {
     *reinterpret_cast<uint4*>(&ss[r][c * 4]) = buf_load16(rs, static_cast<uint32_t>(e) * 16);
   }
   __syncthreads();
-  const int tr = w * 4 + lane / 16, tj = lane % 16;
-  float acc[4][4];
+  f32x4_t acc[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = 0.f;
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int lr = lane & 15, lk = (lane >> 4) * 4;
 #pragma unroll 2
-  for (int k = 0; k < D; k += 4) {
-    float4 qv[4], sv[4];
+  for (int kc = 0; kc < D; kc += 16) {
+    const float4 av = *reinterpret_cast<const float4*>(&qs[16 * w + lr][kc + lk]);
+    float4 bv[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) qv[m] = *reinterpret_cast<const float4*>(&qs[tr + 16 * m][k]);
+    for (int ct = 0; ct < 4; ++ct) bv[ct] = *reinterpret_cast<const float4*>(&ss[16 * ct + lr][kc + lk]);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) sv[n] = *reinterpret_cast<const float4*>(&ss[tj + 16 * n][k]);
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        float t = acc[m][n];
-        t = fmaf(qv[m].x, sv[n].x, t);
-        t = fmaf(qv[m].y, sv[n].y, t);
-        t = fmaf(qv[m].z, sv[n].z, t);
-        t = fmaf(qv[m].w, sv[n].w, t);
-        acc[m][n] = t;
-      }
+    for (int ct = 0; ct < 4; ++ct) {
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv[ct].x, acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv[ct].y, acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv[ct].z, acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv[ct].w, acc[ct], 0, 0, 0);
+    }
   }
+  // lane l holds rows 16w + 4(l/16) + i, block 16ct + l%16
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int r = tr + 16 * m;
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + (lane >> 4) * 4 + i;
     const int cend = (r0 + r) / tok_b + ce - j0;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int j = tj + 16 * n;
+    for (int ct = 0; ct < 4; ++ct) {
+      const int j = 16 * ct + lr;
       if (r < rn && j < jn)
-        out[static_cast<int64_t>(r) * a.nblk + j] = j < cend ? acc[m][n] * a.scale : -INFINITY;
+        out[static_cast<int64_t>(r) * a.nblk + j] = j < cend ? acc[ct][i] * a.scale : -INFINITY;
     }
   }
 }
@@ -514,17 +513,342 @@ __global__ __launch_bounds__(kThreads) void entmax_kernel(EntmaxArgs a) {
   if (threadIdx.x == 0) a.cnt[rowid] = c;
 }
 
+// ---------------------------------------------------------------------------
+// alpha-entmax routing of short rows (<= 64 E candidates), one wavefront per
+// (b, g, row) and four rows per workgroup with no barrier between them: the
+// many short rows of per-token routing.  The wave keeps a head's logits in
+// registers (element e of lane l is block e*64 + l), runs the same histogram
+// bracket, bisection and exact threshold as entmax_kernel head by head,
+// accumulates the group's probabilities and takes the capped support with a
+// register top-m.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  return __builtin_bit_cast(double, make_uint2(__builtin_amdgcn_readlane(u.x, l),
+                                               __builtin_amdgcn_readlane(u.y, l)));
+}
+
+// Sum over the 16 lanes of each row (DPP within the row), for a double.
+__device__ __forceinline__ double row16_sum_d(double v) {
+  v += dppd<0xB1>(v);
+  v += dppd<0x4E>(v);
+  v += dppd<0x141>(v);
+  v += dppd<0x140>(v);
+  return v;
+}
+// Inclusive prefix sum over the 16 lanes of each row (DPP row shifts; lanes
+// shifted in from outside the row read 0).
+__device__ __forceinline__ int row16_scan_i(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  return v;
+}
+
+// Both histogram bounds of tau (the roots of the binned equation with every
+// bin's mass at its lower and at its upper edge, as solve_bins), relative to
+// xm, in one pass: lanes 0-15 hold bin r = lane with value -(r+1)/16, lanes
+// 16-31 bin r = lane-16 with value -r/16, and lane r of each row tries the
+// closed form of the prefix of bins 0..r.  The counts and the first and
+// second moments of the bin offsets are integers, so the prefix moments and
+// the variance numerator are exact.  `cl` is the count of bin lane & 15 on
+// lanes < 32.  Other alpha, or no valid prefix: 64 bisection steps on
+// [e_0 - 1, e_0] per row.  Returns (lower bound, upper bound).
+__device__ inline double2 bin_bounds(int cl, double alpha) {
+  const int lane = lane_id();
+  const int r = lane & 15;
+  const int off = lane < 16 ? 1 : 0;
+  const bool act = lane < 32;
+  const int c = act ? cl : 0;
+  const int kk = r + off;  // bin value -kk/16
+  const uint64_t nz = __ballot(act && c > 0);
+  double tau = 0.0;
+  bool ok = false;
+  if (alpha == 2.0 || alpha == 1.5) {
+    const int n = row16_scan_i(c);
+    const int b1 = row16_scan_i(c * kk);
+    const int a2 = row16_scan_i(c * kk * kk);
+    const double nd = static_cast<double>(n);
+    const double s1 = -static_cast<double>(b1) * 0.0625;  // sum of c e
+    ok = act && c > 0;
+    if (alpha == 2.0) {
+      tau = (s1 - 1.0) / nd;
+    } else {
+      // sum c (e - M)^2 = (n a2 - b1^2) / (256 n), exact numerator
+      const int64_t num = static_cast<int64_t>(n) * a2 - static_cast<int64_t>(b1) * b1;
+      const double Q = static_cast<double>(num) / (256.0 * nd);
+      ok = ok && !(Q > 1.0);
+      tau = s1 / nd - sqrt(fmax((1.0 - Q) / nd, 0.0));
+    }
+    const uint64_t rowbits = (nz >> (lane & 48)) & 0xFFFFull;
+    const uint64_t above = rowbits >> (r + 1);
+    const int nx = above ? r + 1 + __builtin_ctzll(above) : 16;
+    ok = ok && tau < -static_cast<double>(kk) * 0.0625 &&
+         (nx >= 16 || tau >= -static_cast<double>(nx + off) * 0.0625);
+  }
+  const uint64_t vm = __ballot(ok);
+  const uint32_t mlo = static_cast<uint32_t>(vm & 0xFFFFull);
+  const uint32_t mhi = static_cast<uint32_t>((vm >> 16) & 0xFFFFull);
+  double2 out;
+  if (mlo && mhi) {
+    out.x = readlane_d(tau, __builtin_ctz(mlo));
+    out.y = readlane_d(tau, 16 + __builtin_ctz(mhi));
+    return out;
+  }
+  double lo = -static_cast<double>(off) * 0.0625 - 1.0, hi = -static_cast<double>(off) * 0.0625;
+  for (int it = 0; it < 64; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    double f = act ? static_cast<double>(c) * emass_d(-static_cast<double>(kk) * 0.0625, mid, alpha)
+                   : 0.0;
+    f = row16_sum_d(f);
+    if (f >= 1.0)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const double t = 0.5 * (lo + hi);
+  out.x = mlo ? readlane_d(tau, __builtin_ctz(mlo)) : readlane_d(t, 0);
+  out.y = mhi ? readlane_d(tau, 16 + __builtin_ctz(mhi)) : readlane_d(t, 16);
+  return out;
+}
+
+// Threshold of one head's logits held K per lane (-inf: not a candidate):
+// bisection on [lo, hi] in fp64 until no logit lies inside the bracket (at
+// most max_iter steps), then the exact threshold of the resolved support, or
+// the bracket's lower end when unresolved.
+template <int K>
+__device__ inline float entmax_tau(const float (&x)[K], double lo, double hi, float alpha,
+                                   int max_iter) {
+  const double ad = alpha;
+  bool resolved = false;
+  for (int it = 0;; ++it) {
+    bool inside = false;
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      const double v = x[e];
+      inside |= v > lo && v <= hi;
+    }
+    if (__ballot(inside) == 0) {
+      resolved = true;
+      break;
+    }
+    if (it >= max_iter) break;
+    const double mid = 0.5 * (lo + hi);
+    double f = 0.0;
+#pragma unroll
+    for (int e = 0; e < K; ++e) f += emass_d(x[e], mid, ad);
+    f = wave_sum_d(f);
+    if (f >= 1.0)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  if (!resolved) return static_cast<float>(lo);
+  double s1 = 0.0;
+  int ns = 0;
+#pragma unroll
+  for (int e = 0; e < K; ++e)
+    if (x[e] > lo) {
+      s1 += x[e];
+      ++ns;
+    }
+  s1 = wave_sum_d(s1);
+  ns = wave_sum_i(ns);
+  const double nsd = static_cast<double>(ns);
+  if (alpha == 2.f) return static_cast<float>((s1 - 1.0) / nsd);
+  if (alpha == 1.5f) {
+    const double M = s1 / nsd;
+    double Q = 0.0;
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      const double v = x[e];
+      if (v > lo) Q += (v - M) * (v - M);
+    }
+    Q = wave_sum_d(Q);
+    return static_cast<float>(M - sqrt(fmax((1.0 - Q) / nsd, 0.0)));
+  }
+  double l2 = lo, h2 = lo + 1.0;
+  for (int it = 0; it < 64; ++it) {
+    const double mid = 0.5 * (l2 + h2);
+    double f = 0.0;
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      const double v = x[e];
+      if (v > lo) f += emass_d(v, mid, ad);
+    }
+    f = wave_sum_d(f);
+    if (f >= 1.0)
+      l2 = mid;
+    else
+      h2 = mid;
+  }
+  return static_cast<float>(0.5 * (l2 + h2));
+}
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void entmax_rows_kernel(EntmaxArgs a) {
+  __shared__ int bins[kWaves][16];
+  __shared__ float live_x[kWaves][kWave];
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * kWaves + w;  // (b, g, row)
+  if (rowid >= static_cast<int64_t>(a.batch) * a.hkv * a.nrow) return;
+  const int G = a.hq / a.hkv;
+  const int row = static_cast<int>(rowid % a.nrow);
+  const int64_t bg = rowid / a.nrow;
+  const int g = static_cast<int>(bg % a.hkv);
+  const int b = static_cast<int>(bg / a.hkv);
+  const RowInfo ri = row_info(a.rule, b, row);
+  const int n = ri.cand_end;  // <= 64 E
+  const float alpha = a.alpha;
+  const double ad = alpha;
+  float wsum[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) wsum[e] = 0.f;
+  for (int hh = 0; hh < G; ++hh) {
+    const int64_t hrow = (static_cast<int64_t>(b) * a.hq + g * G + hh) * a.nrow + row;
+    const float* xr = a.xbuf + hrow * a.nblk;
+    float x[E];
+    float xmax = -INFINITY;
+    int ne = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = e * kWave + lane;
+      x[e] = (j < n && !is_forced(ri, j)) ? xr[j] : -INFINITY;
+      if (x[e] != -INFINITY) {
+        xmax = fmaxf(xmax, x[e]);
+        ++ne;
+      }
+    }
+    xmax = wave_max(xmax);
+    ne = wave_sum_i(ne);
+    float tau = __builtin_nanf("");
+    float iz = 0.f;  // 1 / sum of the unnormalised masses (0: no candidates)
+    if (ne > 0) {
+      // 16-bin histogram of u = xmax - x on [0, 1)
+      if (lane < 16) bins[w][lane] = 0;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float u = xmax - x[e];
+        if (x[e] != -INFINITY && u < 1.f) {
+          int bin = static_cast<int>(floorf(u * 16.f));
+          bin = bin > 15 ? 15 : bin;
+          atomicAdd(&bins[w][bin], 1);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int cl = lane < 32 ? bins[w][lane & 15] : 0;
+      const double xm = xmax;
+      const double2 tb = bin_bounds(cl, ad);
+      const double nterm = alpha == 1.5f ? 1.0 / sqrt(static_cast<double>(ne))
+                           : alpha == 2.f ? 1.0 / static_cast<double>(ne)
+                                          : pow(static_cast<double>(ne), 1.0 - ad);
+      const double lo = fmax(xm + tb.x, xm - 1.0);
+      const double hi = fmin(xm + tb.y, xm - nterm);
+      // logits at or below lo never carry mass for a threshold in the
+      // bracket: pack the others one per lane when they fit
+      int nlive = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) nlive += __popcll(__ballot(static_cast<double>(x[e]) > lo));
+      if (nlive <= kWave) {
+        int base = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool live = static_cast<double>(x[e]) > lo;
+          const uint64_t mk = __ballot(live);
+          if (live) live_x[w][base + lanes_below(mk)] = x[e];
+          base += __popcll(mk);
+        }
+        __builtin_amdgcn_wave_barrier();
+        const float xl[1] = {lane < nlive ? live_x[w][lane] : -INFINITY};
+        __builtin_amdgcn_wave_barrier();
+        tau = entmax_tau<1>(xl, lo, hi, alpha, a.max_iter);
+      } else {
+        tau = entmax_tau<E>(x, lo, hi, alpha, a.max_iter);
+      }
+      float z = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) z += emass(x[e], tau, alpha);
+      z = wave_sum(z);
+      iz = 1.f / z;
+#pragma unroll
+      for (int e = 0; e < E; ++e) wsum[e] += emass(x[e], tau, alpha) * iz;
+    }
+    if (a.tau && lane == 0) a.tau[hrow] = tau;
+    if (a.probs) {
+      float* pr = a.probs + hrow * a.nblk;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int j = e * kWave + lane;
+        if (j < a.nblk) pr[j] = (j < n && ne > 0) ? emass(x[e], tau, alpha) * iz : 0.f;
+      }
+      for (int j = E * kWave + lane; j < a.nblk; j += kWave) pr[j] = 0.f;
+    }
+  }
+  // GQA: mean probability over the group's heads; keep the positive ones,
+  // capped at the `cap` largest (lower block first on ties)
+  const float invG = 1.f / static_cast<float>(G);
+  float wb[E];
+  uint32_t key[E];
+  bool valid[E], sel[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * kWave + lane;
+    wb[e] = wsum[e] * invG;
+    valid[e] = j < n && !is_forced(ri, j) && wb[e] > 0.f;
+    key[e] = valid[e] ? float_key(wb[e]) : 0u;
+  }
+  const int nr = wave_topm<E>(key, valid, a.cap, sel);
+  // ascending: block 0 when forced first, the routed ids (strictly between
+  // the forced ones), then the row's own block when forced
+  int32_t* idx = a.idx + rowid * a.width;
+  float* wsel = a.wsel ? a.wsel + rowid * a.width : nullptr;
+  const int lead = (ri.f0 == 0 && (a.rule.force & 2u)) ? 1 : 0;
+  const int tail0 = (!lead && ri.f0 >= 0) ? ri.f0 : -1;
+  const int total = lead + nr + (tail0 >= 0) + (ri.f1 >= 0);
+  int base = lead;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint64_t mk = __ballot(sel[e]);
+    if (sel[e]) {
+      const int pos = base + lanes_below(mk);
+      idx[pos] = e * kWave + lane;
+      if (wsel) wsel[pos] = wb[e];
+    }
+    base += __popcll(mk);
+  }
+  for (int q = lane; q < a.width; q += kWave) {
+    if (q >= lead && q < lead + nr) continue;
+    int v = -1;
+    float wv = 0.f;
+    if (q < lead) {
+      v = 0;
+      wv = 1.f;
+    } else if (q < total) {
+      v = (q == lead + nr && tail0 >= 0) ? tail0 : ri.f1;
+      wv = 1.f;
+    }
+    idx[q] = v;
+    if (wsel) wsel[q] = wv;
+  }
+  if (lane == 0) a.cnt[rowid] = total;
+}
+
 }  // namespace
 
-hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream) {
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream, bool fill) {
   if (a.rule.mode != 1) {
     const unsigned tiles = static_cast<unsigned>((a.nrow + kTile - 1) / kTile) *
                            static_cast<unsigned>((a.nblk + kTile - 1) / kTile);
     const unsigned grid = static_cast<unsigned>(a.batch) * a.qheads * tiles;
+    const int f = fill ? 1 : 0;
     if (a.d == 64)
-      hipLaunchKernelGGL(scores_tiled<64>, dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(scores_mfma<64>, dim3(grid), dim3(kThreads), 0, stream, a, f);
     else
-      hipLaunchKernelGGL(scores_tiled<128>, dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL(scores_mfma<128>, dim3(grid), dim3(kThreads), 0, stream, a, f);
     return hipGetLastError();
   }
   const int nchunk = (a.nblk + kChunk - 1) / kChunk;
@@ -543,6 +867,16 @@ hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream) {
+  if (a.rule.mode == 2 && a.nblk <= 16 * kWave) {
+    // per-token rows: many short rows, one wavefront each
+    const int64_t rows = static_cast<int64_t>(a.batch) * a.hkv * a.nrow;
+    const unsigned grid = static_cast<unsigned>((rows + kWaves - 1) / kWaves);
+    if (a.nblk <= 8 * kWave)
+      hipLaunchKernelGGL(entmax_rows_kernel<8>, dim3(grid), dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(entmax_rows_kernel<16>, dim3(grid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow;
   const size_t rows = static_cast<size_t>(a.hq / a.hkv) * a.nblk * sizeof(float);
   const size_t capb = ((static_cast<size_t>(a.nblk) + kSel - 1) / kSel) * a.cap;

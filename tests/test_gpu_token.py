@@ -43,6 +43,14 @@ ENTMAX = {
                                                            cap=64, gamma=1.0, planted_blocks=4),
     "tok_entmax_a2": W["entmax_prefill_n64k"].scaled(mode="token", hq=4, hkv=2, n=64 * 12 + 33,
                                                      cap=6, gamma=16.0, alpha=2.0, loc_amp=1.0),
+    # alpha outside {1.5, 2}: the histogram bracket by bisection
+    "tok_entmax_a175": W["entmax_prefill_n64k"].scaled(mode="token", hq=4, hkv=2, n=64 * 20 + 7,
+                                                       cap=8, gamma=8.0, alpha=1.75,
+                                                       force=synth.FORCE_DIAG | synth.FORCE_FIRST),
+    # 601 blocks: 16 logits per lane
+    "tok_entmax_e16": W["entmax_prefill_n64k"].scaled(mode="token", hq=2, hkv=1, n=64 * 600 + 9,
+                                                      cap=16, gamma=4.0, loc_amp=2.0,
+                                                      planted_blocks=8),
 }
 
 
