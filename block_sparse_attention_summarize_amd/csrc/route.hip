@@ -687,8 +687,8 @@ __device__ inline float entmax_tau(const float (&x)[K], double lo, double hi, fl
   return static_cast<float>(0.5 * (l2 + h2));
 }
 
-template <int E>
-__global__ __launch_bounds__(kThreads) void entmax_rows_kernel(EntmaxArgs a) {
+template <int E, int MINW>
+__global__ __launch_bounds__(kThreads, MINW) void entmax_rows_kernel(EntmaxArgs a) {
   __shared__ int bins[kWaves][16];
   __shared__ float live_x[kWaves][kWave];
   const int lane = lane_id();
@@ -871,10 +871,11 @@ hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream) {
     // per-token rows: many short rows, one wavefront each
     const int64_t rows = static_cast<int64_t>(a.batch) * a.hkv * a.nrow;
     const unsigned grid = static_cast<unsigned>((rows + kWaves - 1) / kWaves);
+    // latency-bound: 8 logits per lane fit three wavefronts per SIMD
     if (a.nblk <= 8 * kWave)
-      hipLaunchKernelGGL(entmax_rows_kernel<8>, dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((entmax_rows_kernel<8, 3>), dim3(grid), dim3(kThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL(entmax_rows_kernel<16>, dim3(grid), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((entmax_rows_kernel<16, 1>), dim3(grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
   }
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow;
