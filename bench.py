@@ -14,7 +14,8 @@ whole step.  `roofline` covers the dominant kernel (the MFMA attention) timed
 with HIP events on its stream inside the timed region; `cpu_baseline` is the
 fp64 oracle timed on this host on a bounded sample.  `extra` holds the other
 workloads of the method: `decode` (batch 16, 32/8 heads, L = 131072, top-32 +
-tail; GB/s with the 256 MB last-level cache flushed between steps),
+tail; GB/s with the 256 MB last-level cache flushed between steps; `paged`:
+the same step over the cache stored as a shuffled pool of 64-token pages),
 `entmax_prefill_n64k` (alpha = 1.5 entmax routing, N = 65536, cap 64),
 `bf16_long_prefill_n256k` (16/2 heads, N = 262144, B = 128, top-32) and
 `token_entmax_prefill_n32k` (every query token routed by alpha-entmax, cap
@@ -285,7 +286,7 @@ def prefill_extra(r):
     return out
 
 
-def run_decode(bsa, torch, steps, warmup):
+def run_decode(bsa, torch, steps, warmup, with_paged=True):
     w = synth.WORKLOADS[DECODE]
     x = device_inputs(w, torch)
     S = bsa.summarize(x["K"], w.B)  # cached summaries, computed once
@@ -301,18 +302,44 @@ def run_decode(bsa, torch, steps, warmup):
         bsa.decode_step(x["Q"], x["K"], x["V"], S, w.B, w.k_total, w.force, kv_lens=lens, out=O,
                         sel=(idx, cnt), ws=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(max(steps, 5)):
-        flush.sum()  # evict the last-level cache by reading 512 MiB (untimed, no dirty lines)
-        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-        e0.record()
-        step()
-        e1.record()
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e-3)
+        ts = []
+        for _ in range(max(steps, 5)):
+            flush.sum()  # evict the last-level cache by reading 512 MiB (untimed, no dirty lines)
+            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return ts
+
+    times = timed(step)
+    O_ref = O.clone()
+    paged = None
+    if with_paged:
+        # the same cache as a shuffled pool of pages of B tokens behind page tables
+        nb = w.nblk
+        perm = torch.randperm(w.batch * nb, generator=torch.Generator().manual_seed(7))
+        pool_of = lambda T: T.reshape(w.batch, w.hkv, nb, w.B, w.d).permute(0, 2, 1, 3, 4) \
+            .reshape(w.batch * nb, w.hkv, w.B, w.d)[perm.to("cuda")].contiguous()
+        Kp, Vp = pool_of(x["K"]), pool_of(x["V"])
+        table = torch.empty(w.batch * nb, dtype=torch.int32)
+        table[perm] = torch.arange(w.batch * nb, dtype=torch.int32)
+        table = table.reshape(w.batch, nb).to("cuda")
+        del x["K"], x["V"]
+
+        def pstep():
+            bsa.decode_step_paged(x["Q"], Kp, Vp, table, S, w.B, w.k_total, w.force, kv_lens=lens,
+                                  kv_len=w.n, out=O, want_selection=False, ws=ws)
+
+        ptimes = timed(pstep)
+        paged = {"us_per_step_median": float(np.median(ptimes)) * 1e6,
+                 "same_output_as_contiguous": bool(torch.equal(O, O_ref)),
+                 "pages": int(w.batch * nb), "page_tokens": w.B}
     c = cnt.cpu().numpy()
     kv_bytes = int(c.sum()) * w.B * w.d * 2 * 2  # selected K and V blocks (all full here)
     sum_bytes = w.batch * w.hkv * (w.nblk - 1) * w.d * 4  # fp32 summaries of the candidates
@@ -325,7 +352,9 @@ def run_decode(bsa, torch, steps, warmup):
             "bytes_per_step": total, "kv_bytes": kv_bytes, "summary_bytes": sum_bytes,
             "GB_per_s": total / t / 1e9, "KV_GB_per_s": kv_bytes / t / 1e9,
             "frac_hbm_peak": total / t / 1e9 / PEAK_HBM_GBS,
-            "cache_flush": "512 MiB read before every timed step"}
+            "cache_flush": "512 MiB read before every timed step"} | (
+        {} if paged is None else {"paged": paged | {
+            "GB_per_s": total / (paged["us_per_step_median"] * 1e-6) / 1e9}})
 
 
 def main():

@@ -41,9 +41,10 @@ OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECOD
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
-EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_route_topk", "bsa_route_entmax",
-           "bsa_attend_prefill", "bsa_token_mask", "bsa_attend_decode", "bsa_decode_topk",
-           "bsa_workspace_size", "bsa_last_error", "bsa_version")
+EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_summarize_blocks_paged",
+           "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill", "bsa_token_mask",
+           "bsa_attend_decode", "bsa_decode_topk", "bsa_decode_topk_paged", "bsa_workspace_size",
+           "bsa_last_error", "bsa_version")
 
 
 class Shape(ctypes.Structure):
@@ -57,6 +58,12 @@ class Shape(ctypes.Structure):
     ]
 
 
+class Pages(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("k_page_stride", ctypes.c_int64),
+                ("v_page_stride", ctypes.c_int64)]
+
+
 _P = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _u32 = ctypes.c_uint32
@@ -65,6 +72,10 @@ _sz = ctypes.c_size_t
 _SP = ctypes.POINTER(Shape)
 lib.bsa_summarize.argtypes = [_SP, _P, _P, _P, _P]
 lib.bsa_summarize_blocks.argtypes = [_SP, _P, _P, _P, _P, _P]
+_PP = ctypes.POINTER(Pages)
+lib.bsa_summarize_blocks_paged.argtypes = [_SP, _PP, _P, _P, _P, _P, _P]
+lib.bsa_decode_topk_paged.argtypes = [_SP, _PP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P,
+                                      _P, _i32, _P, _sz, _P]
 lib.bsa_route_topk.argtypes = [_SP, _P, _P, _P, _i32, _u32, _f32, _P, _P, _P, _P, _sz, _P]
 lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, _u32, _f32, _P,
                                  _P, _P, _P, _P, _P, _sz, _P]
@@ -74,8 +85,9 @@ lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
 lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
                                 _P, _sz, _P]
-for _f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_route_topk, lib.bsa_route_entmax,
-           lib.bsa_attend_prefill, lib.bsa_token_mask, lib.bsa_attend_decode, lib.bsa_decode_topk):
+for _f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_summarize_blocks_paged,
+           lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill, lib.bsa_token_mask,
+           lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged):
     _f.restype = ctypes.c_int
 lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
 lib.bsa_workspace_size.restype = _sz
@@ -325,6 +337,69 @@ def decode_step(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, score_sc
                                _ptr(kv_lens), k_total, force, score_scale, sm_scale, _ptr(idx),
                                _ptr(cnt), _ptr(O), _dtype_code(O), _ptr(wsb), n, _stream(q)))
     return O, idx, cnt
+
+
+def make_pages(table, Kp, Vp):
+    """Page description of a pool Kp / Vp [num_pages, Hkv, B, d] addressed by
+    table int32 [batch, max_pages] (device)."""
+    pg = Pages()
+    pg.table = table.data_ptr()
+    pg.max_pages = int(table.shape[1])
+    pg.num_pages = int(min(Kp.shape[0], Vp.shape[0]))
+    pg.k_page_stride = int(Kp.stride(0))
+    pg.v_page_stride = int(Vp.stride(0))
+    return pg
+
+
+def _paged_shape(q, Kp, Vp, B, kv_len, O=None):
+    b, hq, _, d = q.shape
+    s = make_shape(batch=b, hq=hq, hkv=Kp.shape[1], d=d, B=B, dtype=_dtype_code(q), mode=DECODE,
+                   q_len=1, kv_len=kv_len, q=q, o=O)
+    s.k_stride[:] = (0, int(Kp.stride(1)), int(Kp.stride(2)))
+    s.v_stride[:] = (0, int(Vp.stride(1)), int(Vp.stride(2)))
+    return s
+
+
+def decode_step_paged(q, Kp, Vp, table, S, B, k_total, force=FORCE_TAIL, kv_lens=None,
+                      kv_len=None, score_scale=0.0, sm_scale=0.0, out_dtype=None, out=None,
+                      want_selection=True, ws=None):
+    """decode_step over a paged cache: Kp / Vp [num_pages, Hkv, B, d], logical
+    block j of sequence b in page table[b, j].  kv_len: the logical capacity
+    (default table.shape[1] * B).  Returns (O, idx, cnt)."""
+    b, hq, _, d = q.shape
+    hkv = Kp.shape[1]
+    kv_len = table.shape[1] * B if kv_len is None else kv_len
+    odt = out_dtype or q.dtype
+    O = out if out is not None else torch.empty((b, hq, 1, d), dtype=odt, device=q.device)
+    if want_selection:
+        idx = torch.empty((b, hkv, 1, k_total), dtype=torch.int32, device=q.device)
+        cnt = torch.empty((b, hkv, 1), dtype=torch.int32, device=q.device)
+    else:
+        idx = cnt = None
+    shape = _paged_shape(q, Kp, Vp, B, kv_len, O)
+    pg = make_pages(table, Kp, Vp)
+    wsb, n = _workspace(OP_DECODE_TOPK, shape, k_total, q.device, ws)
+    _check(lib.bsa_decode_topk_paged(ctypes.byref(shape), ctypes.byref(pg), _ptr(q), _ptr(Kp),
+                                     _ptr(Vp), _ptr(S), _ptr(kv_lens), k_total, force, score_scale,
+                                     sm_scale, _ptr(idx), _ptr(cnt), _ptr(O), _dtype_code(O),
+                                     _ptr(wsb), n, _stream(q)))
+    return O, idx, cnt
+
+
+def summarize_blocks_paged(Kp, table, B, blk, S, kv_len=None, qbar=None):
+    """summarize_blocks over a paged key pool Kp [num_pages, Hkv, B, d]."""
+    hkv, d = Kp.shape[1], Kp.shape[3]
+    b = table.shape[0]
+    kv_len = table.shape[1] * B if kv_len is None else kv_len
+    shape = make_shape(batch=b, hq=hkv, hkv=hkv, d=d, B=B, dtype=_dtype_code(Kp), mode=DECODE,
+                       q_len=1, kv_len=kv_len)
+    shape.k_stride[:] = (0, int(Kp.stride(1)), int(Kp.stride(2)))
+    pg = make_pages(table, Kp, Kp)
+    if qbar is not None:
+        qbar = qbar.contiguous().to(torch.float32)
+    _check(lib.bsa_summarize_blocks_paged(ctypes.byref(shape), ctypes.byref(pg), _ptr(Kp),
+                                          _ptr(qbar), _ptr(blk), _ptr(S), _stream(Kp)))
+    return S
 
 
 def decode_workspace(q, K, B, k_total):

@@ -221,11 +221,30 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 }
 
 // Fills the fused decode kernel's arguments shared by the three decode calls.
+// A paged K/V cache: the table, its row length and the page strides.
+int check_pages(const bsa_shape* s, const bsa_pages* pg) {
+  if (!pg) return fail(BSA_ERR_INVALID, "pages is NULL");
+  if (!pg->table) return fail(BSA_ERR_INVALID, "pages->table is NULL");
+  if (pg->num_pages < 1) return fail(BSA_ERR_INVALID, "pages->num_pages must be >= 1");
+  if (pg->max_pages < nblk_of(s))
+    return fail(BSA_ERR_INVALID, "pages->max_pages (%d) must cover the %lld blocks of kv_len",
+                pg->max_pages, (long long)nblk_of(s));
+  const int64_t q = s->dtype == BSA_BF16 ? 8 : 4;
+  if (pg->k_page_stride < 0 || pg->v_page_stride < 0)
+    return fail(BSA_ERR_INVALID, "page strides must be >= 0");
+  if (pg->k_page_stride % q != 0 || pg->v_page_stride % q != 0)
+    return fail(BSA_ERR_UNSUPPORTED, "page strides must be multiples of %lld elements",
+                (long long)q);
+  return BSA_OK;
+}
+
 int decode_args(const bsa_shape* s, const void* Q, const void* K, const void* V,
                        const float* S, const int32_t* kv_lens, int32_t* idx, int32_t* cnt,
                        int32_t width, uint32_t force, float score_scale, float sm_scale, void* O,
-                       int32_t o_dtype, int route, int attend, bsa::DecodeArgs& a) {
+                       int32_t o_dtype, int route, int attend, bsa::DecodeArgs& a,
+                       const bsa_pages* pg = nullptr) {
   int rc;
+  a = bsa::DecodeArgs{};
   if (s->mode != BSA_DECODE) return fail(BSA_ERR_INVALID, "decode calls need BSA_DECODE");
   if ((rc = check_ptr("Q", Q)) != BSA_OK) return rc;
   if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
@@ -243,11 +262,21 @@ int decode_args(const bsa_shape* s, const void* Q, const void* K, const void* V,
     if ((rc = check_strides("O", s->o_stride, o_dtype)) != BSA_OK) return rc;
     if (s->k_stride[2] < s->head_dim || s->v_stride[2] < s->head_dim)
       return fail(BSA_ERR_INVALID, "K/V token stride must be >= head_dim");
-    // one head's rows are addressed with 32-bit byte offsets
+    // one head's rows (of a sequence, or of a page) are addressed with
+    // 32-bit byte offsets
     const int64_t esz = elem_bytes(s->dtype);
-    if ((s->kv_len + 256) * s->k_stride[2] * esz >= (int64_t(1) << 31) ||
-        (s->kv_len + 256) * s->v_stride[2] * esz >= (int64_t(1) << 31))
+    const int64_t rows = pg ? s->block : s->kv_len;
+    if ((rows + 256) * s->k_stride[2] * esz >= (int64_t(1) << 31) ||
+        (rows + 256) * s->v_stride[2] * esz >= (int64_t(1) << 31))
       return fail(BSA_ERR_UNSUPPORTED, "K/V: one head spans more than 2 GiB");
+    if (pg) {
+      if ((rc = check_pages(s, pg)) != BSA_OK) return rc;
+      a.table = pg->table;
+      a.max_pages = pg->max_pages;
+      a.num_pages = pg->num_pages;
+      a.page_k = pg->k_page_stride;
+      a.page_v = pg->v_page_stride;
+    }
   }
   const int hsplit = attend ? decode_hsplit(s) : 1;
   if (hsplit < 1)
@@ -324,7 +353,7 @@ int bsa_summarize(const bsa_shape* s, const void* K, const float* qbar, float* S
   if ((rc = check_ptr("S", S)) != BSA_OK) return rc;
   if (qbar && !aligned16(qbar)) return fail(BSA_ERR_UNSUPPORTED, "qbar must be 16-byte aligned");
   if ((rc = check_strides("K", s->k_stride, s->dtype)) != BSA_OK) return rc;
-  bsa::SummarizeArgs a;
+  bsa::SummarizeArgs a{};
   a.K = K;
   a.ks = st3(s->k_stride);
   a.qbar = qbar;
@@ -349,7 +378,7 @@ int bsa_summarize_blocks(const bsa_shape* s, const void* K, const float* qbar, c
   if (!blk) return fail(BSA_ERR_INVALID, "blk must not be NULL");
   if (qbar && !aligned16(qbar)) return fail(BSA_ERR_UNSUPPORTED, "qbar must be 16-byte aligned");
   if ((rc = check_strides("K", s->k_stride, s->dtype)) != BSA_OK) return rc;
-  bsa::SummarizeArgs a;
+  bsa::SummarizeArgs a{};
   a.K = K;
   a.ks = st3(s->k_stride);
   a.qbar = qbar;
@@ -384,7 +413,7 @@ int bsa_route_topk(const bsa_shape* s, const void* Q, const float* S, const int3
   if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (s->mode == BSA_DECODE && scores_out == nullptr) {
-    bsa::DecodeArgs da;
+    bsa::DecodeArgs da{};
     if ((rc = decode_args(s, Q, nullptr, nullptr, S, kv_lens, idx, cnt, k_total, force,
                           score_scale, 0.f, nullptr, s->dtype, 1, 0, da)) != BSA_OK)
       return rc;
@@ -694,10 +723,11 @@ int bsa_attend_decode(const bsa_shape* s, const void* Q, const void* K, const vo
                        "attend_decode");
 }
 
-int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void* V,
-                    const float* S, const int32_t* kv_lens, int32_t k_total, uint32_t force,
-                    float score_scale, float sm_scale, int32_t* idx, int32_t* cnt, void* O,
-                    int32_t o_dtype, void* ws, size_t ws_bytes, void* stream) {
+static int decode_topk_impl(const bsa_shape* s, const bsa_pages* pg, const void* Q,
+                            const void* K, const void* V, const float* S,
+                            const int32_t* kv_lens, int32_t k_total, uint32_t force,
+                            float score_scale, float sm_scale, int32_t* idx, int32_t* cnt,
+                            void* O, int32_t o_dtype, void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
   if ((rc = check_force(s, force)) != BSA_OK) return rc;
@@ -708,7 +738,7 @@ int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void
     return fail(BSA_ERR_INVALID, "idx and cnt must both be given or both be NULL");
   bsa::DecodeArgs a;
   if ((rc = decode_args(s, Q, K, V, S, kv_lens, idx, cnt, k_total, force, score_scale, sm_scale,
-                        O, o_dtype, 1, 1, a)) != BSA_OK)
+                        O, o_dtype, 1, 1, a, pg)) != BSA_OK)
     return rc;
   const int parts = decode_parts(s, k_total, force);
   const DecodeWs dw = decode_ws(s, parts, k_total, true);
@@ -723,6 +753,55 @@ int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void
   a.cand_id = reinterpret_cast<int32_t*>(base + dw.cand);
   a.part = reinterpret_cast<float*>(base + 2 * dw.cand);
   return device_status(bsa::launch_decode_parts(a, st), "decode_topk");
+}
+
+int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                    const float* S, const int32_t* kv_lens, int32_t k_total, uint32_t force,
+                    float score_scale, float sm_scale, int32_t* idx, int32_t* cnt, void* O,
+                    int32_t o_dtype, void* ws, size_t ws_bytes, void* stream) {
+  return decode_topk_impl(s, nullptr, Q, K, V, S, kv_lens, k_total, force, score_scale, sm_scale,
+                          idx, cnt, O, o_dtype, ws, ws_bytes, stream);
+}
+
+int bsa_decode_topk_paged(const bsa_shape* s, const bsa_pages* pages, const void* Q,
+                          const void* K, const void* V, const float* S, const int32_t* kv_lens,
+                          int32_t k_total, uint32_t force, float score_scale, float sm_scale,
+                          int32_t* idx, int32_t* cnt, void* O, int32_t o_dtype, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!pages) return fail(BSA_ERR_INVALID, "pages is NULL");
+  return decode_topk_impl(s, pages, Q, K, V, S, kv_lens, k_total, force, score_scale, sm_scale,
+                          idx, cnt, O, o_dtype, ws, ws_bytes, stream);
+}
+
+int bsa_summarize_blocks_paged(const bsa_shape* s, const bsa_pages* pages, const void* K,
+                               const float* qbar, const int32_t* blk, float* S, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if ((rc = check_pages(s, pages)) != BSA_OK) return rc;
+  if ((rc = check_ptr("K", K)) != BSA_OK) return rc;
+  if ((rc = check_ptr("S", S)) != BSA_OK) return rc;
+  if (!blk) return fail(BSA_ERR_INVALID, "blk must not be NULL");
+  if (qbar && !aligned16(qbar)) return fail(BSA_ERR_UNSUPPORTED, "qbar must be 16-byte aligned");
+  if ((rc = check_strides("K", s->k_stride, s->dtype)) != BSA_OK) return rc;
+  bsa::SummarizeArgs a{};
+  a.K = K;
+  a.ks = st3(s->k_stride);
+  a.qbar = qbar;
+  a.S = S;
+  a.blk = blk;
+  a.table = pages->table;
+  a.max_pages = pages->max_pages;
+  a.num_pages = pages->num_pages;
+  a.page_k = pages->k_page_stride;
+  a.batch = s->batch;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.B = s->block;
+  a.nblk = static_cast<int>(nblk_of(s));
+  a.kv_len = s->kv_len;
+  a.bf16 = s->dtype == BSA_BF16;
+  return device_status(bsa::launch_summarize(a, static_cast<hipStream_t>(stream)),
+                       "summarize_blocks_paged");
 }
 
 }  // extern "C"

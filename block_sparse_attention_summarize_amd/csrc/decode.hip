@@ -12,6 +12,10 @@
 // keeping an online softmax per query head; the wavefronts' partial states
 // are merged in LDS.  Decode is bound by HBM transfers (summaries + the
 // selected K/V), so everything stays on the VALU.
+// PAGED: the K/V cache is a pool of pages of B tokens; the selection is
+// translated through the sequence's page table into LDS once, and each chunk
+// load builds its buffer resource over its page (rows past the sequence
+// length read as zero, as in the contiguous layout).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -37,7 +41,7 @@ __device__ __forceinline__ void xcd_row(int id, int rows, int hsplit, int& row, 
   }
 }
 
-template <typename T, int D, int GS>
+template <typename T, int D, int GS, bool PAGED>
 __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   constexpr int LPK = D / 8;       // lanes per key row (8 elements each)
   constexpr int KPI = kWave / LPK;  // keys per wave load instruction
@@ -211,6 +215,18 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   const int nsel = sel_n;
   const int cpb = a.B / CK;  // chunks per block
   const int nchunk = nsel * cpb;
+  // paged: the selected blocks' pages (the selection buffers past sel[k_total]
+  // are free once the selection is made)
+  int* pgs = sel + a.k_total;
+  if constexpr (PAGED) {
+    for (int q = tid; q < nsel; q += kNT) {
+      const int j = sel[q];
+      const int pg = (j >= 0 && j < a.nblk && j < a.max_pages)
+                         ? a.table[static_cast<int64_t>(b) * a.max_pages + j] : -1;
+      pgs[q] = pg >= 0 && pg < a.num_pages ? pg : -1;
+    }
+    __syncthreads();
+  }
   // K/V rows at or past L read as zero through the buffer resources
   const auto rk = make_rsrc(static_cast<const T*>(a.K) + b * a.ks.b + g * a.ks.h,
                             head_bytes(L, a.ks.t, D, sizeof(T)));
@@ -236,7 +252,22 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
     return (j >= 0 && j < a.nblk) ? j * a.B + (ch % cpb) * CK : -1;
   };
   auto issue = [&](int ch, uint4 (&kb)[KPC][RPL], uint4 (&vb)[KPC][RPL]) {
-    const int t0 = chunk_t0(ch);
+    int t0 = chunk_t0(ch);
+    auto rkc = rk, rvc = rv;
+    if constexpr (PAGED) {
+      // the chunk's page (wave-uniform): rows [0, L - jB) of it are valid
+      const int pg = t0 < 0 ? -1 : __builtin_amdgcn_readfirstlane(pgs[ch / cpb]);
+      const int j = t0 < 0 ? 0 : t0 / a.B;
+      const int64_t rows = pg < 0 ? 0 : (L - static_cast<int64_t>(j) * a.B < a.B
+                                             ? L - static_cast<int64_t>(j) * a.B : a.B);
+      const int64_t pgo = pg < 0 ? 0 : pg;
+      rkc = make_rsrc(static_cast<const T*>(a.K) + pgo * a.page_k + g * a.ks.h,
+                      head_bytes(rows, a.ks.t, D, sizeof(T)));
+      rvc = make_rsrc(static_cast<const T*>(a.V) + pgo * a.page_v + g * a.vs.h,
+                      head_bytes(rows, a.vs.t, D, sizeof(T)));
+      if (pg < 0) t0 = -1;
+      else t0 -= j * a.B;  // page-relative
+    }
 #pragma unroll
     for (int it = 0; it < KPC; ++it) {
       const uint32_t t = static_cast<uint32_t>(t0 + it * KPI + kg);
@@ -244,8 +275,8 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
       const uint32_t vo = t0 < 0 ? 0xFFFFFF00u : t * vst + c8 * 8 * sizeof(T);
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
-        kb[it][r] = buf_load16(rk, ko + 16 * r);
-        vb[it][r] = buf_load16(rv, vo + 16 * r);
+        kb[it][r] = buf_load16(rkc, ko + 16 * r);
+        vb[it][r] = buf_load16(rvc, vo + 16 * r);
       }
     }
   };
@@ -360,19 +391,23 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   }
 }
 
-template <typename T, int D, int GS>
-hipError_t launch_gs(const DecodeArgs& a, hipStream_t stream) {
+template <typename T, int D, int GS, bool PAGED>
+hipError_t launch_gs_p(const DecodeArgs& a, hipStream_t stream) {
   const size_t dyn = (static_cast<size_t>(a.lds_floats) + decode_sel_ints(a.nblk, a.k_total)) * 4;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused<T, D, GS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_fused<T, D, GS, PAGED>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.hsplit;
-  hipLaunchKernelGGL((decode_fused<T, D, GS>), dim3(grid), dim3(kNT), dyn, stream, a);
+  hipLaunchKernelGGL((decode_fused<T, D, GS, PAGED>), dim3(grid), dim3(kNT), dyn, stream, a);
   return hipGetLastError();
+}
+template <typename T, int D, int GS>
+hipError_t launch_gs(const DecodeArgs& a, hipStream_t stream) {
+  return a.table ? launch_gs_p<T, D, GS, true>(a, stream) : launch_gs_p<T, D, GS, false>(a, stream);
 }
 
 template <typename T, int D>
@@ -393,9 +428,11 @@ int decode_lds_floats(int nblk, int d, int gs_max) {
 
 int decode_sel_ints(int nblk, int k_total) {
   // the selection, then (top-m below kSel) four tournament buffers and its
-  // output keys and ids
+  // output keys and ids; a paged cache reuses them for the selection's pages
+  // (at least k_total ints)
   const long cap = ((static_cast<long>(nblk) + kSel - 1) / kSel) * (k_total > 0 ? k_total : 1);
-  return static_cast<int>(k_total + (k_total < kSel ? 4 * cap + 2 * k_total : 0));
+  const long tb = k_total < kSel ? 4 * cap + 2 * k_total : 0;
+  return static_cast<int>(k_total + (tb > k_total ? tb : k_total));
 }
 
 hipError_t launch_decode_fused(const DecodeArgs& a, hipStream_t stream) {
@@ -529,7 +566,7 @@ __global__ __launch_bounds__(kNT) void decode_route_part(DecodeArgs a) {
       bk0, bi0, bk1, bi1, a.cand_key + off, a.cand_id + off, a.mpad);
 }
 
-template <typename T, int D, int GS>
+template <typename T, int D, int GS, bool PAGED>
 __global__ __launch_bounds__(kNT) void decode_attend_part(DecodeArgs a) {
   constexpr int LPK = D / 8;
   constexpr int KPI = kWave / LPK;
@@ -615,6 +652,17 @@ __global__ __launch_bounds__(kNT) void decode_attend_part(DecodeArgs a) {
   const int s0 = (nsel * p) / a.parts, s1 = (nsel * (p + 1)) / a.parts;
   const int cpb = a.B / CK;
   const int nchunk = (s1 - s0) * cpb;
+  // paged: the selected blocks' pages, over the (finished) tournament buffers
+  int* pgs = reinterpret_cast<int*>(bk0);
+  if constexpr (PAGED) {
+    for (int q = tid; q < nsel; q += kNT) {
+      const int j = sel[q];
+      const int pg = (j >= 0 && j < a.nblk && j < a.max_pages)
+                         ? a.table[static_cast<int64_t>(b) * a.max_pages + j] : -1;
+      pgs[q] = pg >= 0 && pg < a.num_pages ? pg : -1;
+    }
+    __syncthreads();
+  }
   const auto rk = make_rsrc(static_cast<const T*>(a.K) + b * a.ks.b + g * a.ks.h,
                             head_bytes(L, a.ks.t, D, sizeof(T)));
   const auto rv = make_rsrc(static_cast<const T*>(a.V) + b * a.vs.b + g * a.vs.h,
@@ -636,7 +684,22 @@ __global__ __launch_bounds__(kNT) void decode_attend_part(DecodeArgs a) {
     return (j >= 0 && j < a.nblk) ? j * a.B + (ch % cpb) * CK : -1;
   };
   auto issue = [&](int ch, uint4 (&kb)[KPC][RPL], uint4 (&vb)[KPC][RPL]) {
-    const int t0 = chunk_t0(ch);
+    int t0 = chunk_t0(ch);
+    auto rkc = rk, rvc = rv;
+    if constexpr (PAGED) {
+      // the chunk's page (wave-uniform): rows [0, L - jB) of it are valid
+      const int pg = t0 < 0 ? -1 : __builtin_amdgcn_readfirstlane(pgs[s0 + ch / cpb]);
+      const int j = t0 < 0 ? 0 : t0 / a.B;
+      const int64_t rows = pg < 0 ? 0 : (L - static_cast<int64_t>(j) * a.B < a.B
+                                             ? L - static_cast<int64_t>(j) * a.B : a.B);
+      const int64_t pgo = pg < 0 ? 0 : pg;
+      rkc = make_rsrc(static_cast<const T*>(a.K) + pgo * a.page_k + g * a.ks.h,
+                      head_bytes(rows, a.ks.t, D, sizeof(T)));
+      rvc = make_rsrc(static_cast<const T*>(a.V) + pgo * a.page_v + g * a.vs.h,
+                      head_bytes(rows, a.vs.t, D, sizeof(T)));
+      if (pg < 0) t0 = -1;
+      else t0 -= j * a.B;  // page-relative
+    }
 #pragma unroll
     for (int it = 0; it < KPC; ++it) {
       const uint32_t t = static_cast<uint32_t>(t0 + it * KPI + kg);
@@ -644,8 +707,8 @@ __global__ __launch_bounds__(kNT) void decode_attend_part(DecodeArgs a) {
       const uint32_t vo = t0 < 0 ? 0xFFFFFF00u : t * vst + c8 * 8 * sizeof(T);
 #pragma unroll
       for (int r = 0; r < RPL; ++r) {
-        kb[it][r] = buf_load16(rk, ko + 16 * r);
-        vb[it][r] = buf_load16(rv, vo + 16 * r);
+        kb[it][r] = buf_load16(rkc, ko + 16 * r);
+        vb[it][r] = buf_load16(rvc, vo + 16 * r);
       }
     }
   };
@@ -790,18 +853,25 @@ __global__ __launch_bounds__(256) void decode_combine(DecodeArgs a) {
   }
 }
 
-template <typename T, int D, int GS>
-hipError_t launch_attend_part(const DecodeArgs& a, size_t dyn, hipStream_t stream) {
+template <typename T, int D, int GS, bool PAGED>
+hipError_t launch_attend_part_p(const DecodeArgs& a, size_t dyn, hipStream_t stream) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attend_part<T, D, GS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_attend_part<T, D, GS, PAGED>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * (a.attend ? a.parts : 1);
-  hipLaunchKernelGGL((decode_attend_part<T, D, GS>), dim3(grid), dim3(kNT), dyn, stream, a);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL((decode_attend_part<T, D, GS, PAGED>), dim3(grid), dim3(kNT), dyn, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int GS>
+hipError_t launch_attend_part(const DecodeArgs& a, size_t dyn, hipStream_t stream) {
+  hipError_t e = a.table ? launch_attend_part_p<T, D, GS, true>(a, dyn, stream)
+                         : launch_attend_part_p<T, D, GS, false>(a, dyn, stream);
   if (e != hipSuccess || !a.attend) return e;
   hipLaunchKernelGGL(decode_combine, dim3(a.batch * a.hkv), dim3(256), 0, stream, a);
   return hipGetLastError();

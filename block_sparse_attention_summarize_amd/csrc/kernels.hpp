@@ -18,6 +18,11 @@ struct SummarizeArgs {
   const float* qbar;  // nullptr -> mean
   float* S;           // [batch, hkv, nblk, d]
   const int32_t* blk;  // nullptr: every block; else [batch] the one block per sequence, -1 none
+  // paged K (nullptr: contiguous with ks): block j of sequence b is page
+  // table[b * max_pages + j], its element (g, t, c) at page * page_k + g * ks.h + t * ks.t + c
+  const int32_t* table;
+  int max_pages, num_pages;
+  int64_t page_k;
   int batch, hkv, d, B, nblk;
   int64_t kv_len;
   bool bf16;
@@ -153,6 +158,12 @@ struct DecodeArgs {
   uint32_t force;
   float score_scale, sm_scale;
   bool bf16, out_f32;
+  // paged K/V (nullptr: contiguous [batch, hkv, kv_len, d] with ks/vs):
+  // logical block j of sequence b is page table[b * max_pages + j], whose
+  // element (g, t, c) sits at page * page_k + g * ks.h + t * ks.t + c (V alike)
+  const int32_t* table;
+  int max_pages, num_pages;  // pages outside [0, num_pages) read as zero
+  int64_t page_k, page_v;
   // partitioned decode (parts workgroups per row over disjoint data)
   int parts, mpad;       // candidates kept per partition (>= routed count)
   uint32_t* cand_key;    // [rows, parts, mpad] order-preserving score keys

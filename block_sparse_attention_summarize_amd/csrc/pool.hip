@@ -35,6 +35,12 @@ __global__ __launch_bounds__(kThreads) void summarize_kernel(SummarizeArgs a) {
   const int64_t rem = a.kv_len - t0;
   const int cnt = static_cast<int>(rem < a.B ? rem : a.B);
   const T* base = static_cast<const T*>(a.K) + b * a.ks.b + g * a.ks.h + t0 * a.ks.t;
+  if (a.table) {  // paged cache: the block's page holds its B rows
+    if (j >= a.max_pages) return;
+    const int pg = a.table[static_cast<int64_t>(b) * a.max_pages + j];
+    if (pg < 0 || pg >= a.num_pages) return;
+    base = static_cast<const T*>(a.K) + static_cast<int64_t>(pg) * a.page_k + g * a.ks.h;
+  }
   const int c = tid % TPR;
   const int r0 = tid / TPR;
 

@@ -25,7 +25,9 @@
  *            bsa_token_mask     per-token selections (BSA_TOKEN) as active-block
  *                               masks of 64-query tiles.
  *   Decode   bsa_decode_topk    Stage 1 (top-k) and Stage 2 for one decode
- *                               step in a single launch.
+ *                               step in a single launch (bsa_decode_topk_paged,
+ *                               bsa_summarize_blocks_paged: the same over a
+ *                               paged K/V cache).
  *
  * Conventions shared by every call
  *   - Tensors are device pointers owned by the caller.  The library never
@@ -117,6 +119,24 @@ typedef struct bsa_shape {
 } bsa_shape;
 
 /*
+ * A paged K/V cache (decode): a pool of num_pages pages of `block` tokens
+ * each.  Logical block j of sequence b is page table[b * max_pages + j]
+ * (device int32, owned by the caller; an entry outside [0, num_pages) means
+ * no page: its rows read as zero).  Element (kv head g, token t of
+ * the block, c) of page p of K sits at p * k_page_stride + g * k_stride[1] +
+ * t * k_stride[2] + c (V alike with v_page_stride and v_stride); k_stride[0]
+ * and v_stride[0] are not used.  max_pages must be >= n_blk (ceil(kv_len /
+ * block)); page strides are multiples of 8 (bf16) or 4 (fp32) elements.
+ */
+typedef struct bsa_pages {
+  const int32_t *table;
+  int32_t max_pages; /* row length of table */
+  int32_t num_pages; /* pages in the pool, >= 1 */
+  int64_t k_page_stride;
+  int64_t v_page_stride;
+} bsa_pages;
+
+/*
  * Stage 0 -- block summaries ("DashAttention", Estágio 0).
  *   K     [batch, Hkv, kv_len, d] in shape->dtype.
  *   qbar  NULL: the zero-initialised learned query, i.e. the uniform mean of
@@ -147,6 +167,17 @@ int bsa_summarize(const bsa_shape *shape, const void *K, const float *qbar, floa
  */
 int bsa_summarize_blocks(const bsa_shape *shape, const void *K, const float *qbar,
                          const int32_t *blk, float *S, void *stream);
+
+/*
+ * bsa_summarize_blocks over a paged key cache (see bsa_pages): S[b, :, blk[b]]
+ * from the keys of the page holding block blk[b] of sequence b (a negative
+ * table entry skips the sequence).  The block is summarised over
+ * min(block, kv_len - blk[b] * block) rows, as in bsa_summarize_blocks.
+ * Errors: as bsa_summarize_blocks, plus BSA_ERR_INVALID for a NULL or short
+ * page table.
+ */
+int bsa_summarize_blocks_paged(const bsa_shape *shape, const bsa_pages *pages, const void *K,
+                               const float *qbar, const int32_t *blk, float *S, void *stream);
 
 /*
  * Stage 1, top-k ("DashAttention", Declaração do Problema; "Gist Sparse
@@ -291,6 +322,21 @@ int bsa_decode_topk(const bsa_shape *shape, const void *Q, const void *K, const 
                     uint32_t force_flags, float score_scale, float sm_scale, int32_t *idx,
                     int32_t *cnt, void *O, int32_t o_dtype, void *ws, size_t ws_bytes,
                     void *stream);
+
+/*
+ * bsa_decode_topk over a paged K/V cache ("Gist Sparse Attention", section
+ * 2: only the selected blocks are fetched, so a cache stored in pages is read
+ * page by page through the sequence's table).  Routing reads the logical
+ * summaries S exactly as bsa_decode_topk; the attention reads each selected
+ * block from its page, rows at or past L as zero.  Same workspace, outputs
+ * and errors as bsa_decode_topk, plus BSA_ERR_INVALID for a NULL or short
+ * page table.  Results equal bsa_decode_topk on the gathered cache.
+ */
+int bsa_decode_topk_paged(const bsa_shape *shape, const bsa_pages *pages, const void *Q,
+                          const void *K, const void *V, const float *S, const int32_t *kv_lens,
+                          int32_t k_total, uint32_t force_flags, float score_scale,
+                          float sm_scale, int32_t *idx, int32_t *cnt, void *O, int32_t o_dtype,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Scratch bytes needed by `op` for this shape; k_or_cap is k_total (top-k),
  * cap (entmax) or k_max (attend).  Returns 0 when none is needed or the

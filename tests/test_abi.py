@@ -207,3 +207,32 @@ def test_token_mode_validation_and_workspace():
     assert mask(s, width=0) == -1
     big = shape(hq=2, hkv=2, mode=bsa.TOKEN, q_len=64 * 4097, kv_len=64 * 4097)
     assert mask(big) == -2 and "4096" in err()
+
+
+def test_paged_validation():
+    s = shape(batch=2, hq=8, hkv=2, mode=bsa.DECODE, q_len=1, kv_len=64 * 10)
+    s.k_stride[:] = (0, 64 * 128, 128)
+    s.v_stride[:] = (0, 64 * 128, 128)
+    pg = bsa.Pages()
+    pg.table, pg.max_pages, pg.num_pages = 0x300000, 10, 40
+    pg.k_page_stride = pg.v_page_stride = 2 * 64 * 128
+
+    def step(p, ws=1 << 20):
+        return lib.bsa_decode_topk_paged(ctypes.byref(s), p, FAKE, FAKE, FAKE, FAKE, None, 4,
+                                         bsa.FORCE_TAIL, 0.0, 0.0, None, None, FAKE, bsa.BF16,
+                                         ctypes.c_void_p(0x200000), ws, None)
+    assert step(None) == -1 and "pages" in err()
+    pg.max_pages = 9
+    assert step(ctypes.byref(pg)) == -1 and "max_pages" in err()
+    pg.max_pages, pg.num_pages = 10, 0
+    assert step(ctypes.byref(pg)) == -1 and "num_pages" in err()
+    pg.num_pages, pg.k_page_stride = 40, 2 * 64 * 128 + 4
+    assert step(ctypes.byref(pg)) == -2 and "multiples" in err()
+    pg.k_page_stride = 2 * 64 * 128
+    tbl = pg.table
+    pg.table = None
+    assert lib.bsa_summarize_blocks_paged(ctypes.byref(s), ctypes.byref(pg), FAKE, None, FAKE,
+                                          FAKE, None) == -1 and "table" in err()
+    pg.table = tbl
+    assert lib.bsa_summarize_blocks_paged(ctypes.byref(s), ctypes.byref(pg), FAKE, None, None,
+                                          FAKE, None) == -1 and "blk" in err()
