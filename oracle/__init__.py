@@ -64,6 +64,7 @@ def _load():
         lib.orc_attend.argtypes = [P, P, P, I, I, I, I, I, I, I, ctypes.c_int, P, P, P, I, D,
                                    P, I, P, P, P, D]
         lib.orc_token_union.argtypes = [P, P, I, I, I, I, I, P, P, P]
+        lib.orc_entmax_attend.argtypes = [P, P, P, I, I, I, I, I, D, D, P, I, P, P, P]
         lib.orc_version.restype = ctypes.c_char_p
         _lib = lib
     return _lib
@@ -218,6 +219,30 @@ def token_union(idx, cnt, nblk):
     _load().orc_token_union(_ptr(idx), _ptr(cnt), nb, hkv, n, width, nblk, _ptr(uidx),
                             _ptr(ucnt), _ptr(ubits))
     return uidx, ucnt, ubits
+
+
+def entmax_attend(Q, K, V, alpha, req=None, sm_scale=None):
+    """Causal token-level alpha-entmax attention for the requested (b, h, t)
+    rows (all rows when req is None).  Returns (O [nreq, d] fp64,
+    tau [nreq], support [nreq])."""
+    Q = _f32(Q)
+    K = _f32(K)
+    V = _f32(V)
+    nb, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    if req is None:
+        bb, hh, tt = np.meshgrid(np.arange(nb), np.arange(hq), np.arange(n), indexing="ij")
+        req = np.stack([bb.ravel(), hh.ravel(), tt.ravel()], axis=1)
+    req = np.ascontiguousarray(req, dtype=np.int64)
+    O = np.empty((req.shape[0], d), np.float64)
+    tau = np.empty(req.shape[0], np.float64)
+    sup = np.empty(req.shape[0], np.int64)
+    _load().orc_entmax_attend(_ptr(Q), _ptr(K), _ptr(V), nb, hq, hkv, n, d, float(alpha),
+                              float(sm_scale), _ptr(req), req.shape[0], _ptr(O), _ptr(tau),
+                              _ptr(sup))
+    return O, tau, sup
 
 
 def version() -> str:

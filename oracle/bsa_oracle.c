@@ -722,3 +722,68 @@ void orc_token_union(const int32_t *idx, const int32_t *cnt, int64_t nb, int64_t
       }
   free(word);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Token-level alpha-entmax attention.                                        */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Causal alpha-entmax attention over tokens ("AdaSplash-2", sections 1 and 2:
+ * the attention distribution of query t is alpha-entmax of its scores, exact
+ * zeros outside a data-dependent support, with the normaliser tau found per
+ * query).  For each requested (b, h, t):
+ *   x_j = (alpha-1) * sm_scale * q_t . k_j  for keys j <= t (KV head h / G),
+ *   tau solves sum_j [x_j - tau]_+^(1/(alpha-1)) = 1, found on the sorted x by
+ *   the exact prefix closed forms (alpha 1.5, 2) or 64 bisection steps
+ *   (other alpha) of solve_sorted,
+ *   p_j = [x_j - tau]_+^(1/(alpha-1)) / (their sum), o = sum_j p_j v_j.
+ *   Q : [nb, hq, n, d]; K, V : [nb, hkv, n, d] (fp32).
+ *   O : [nreq, d] fp64;  tau_out, support : [nreq] (may be NULL).
+ */
+void orc_entmax_attend(const float *Q, const float *K, const float *V, int64_t nb, int64_t hq,
+                       int64_t hkv, int64_t n, int64_t d, double alpha, double sm_scale,
+                       const int64_t *req, int64_t nreq, double *O, double *tau_out,
+                       int64_t *support) {
+  (void)nb;
+  int64_t G = hq / hkv;
+  double ex = 1.0 / (alpha - 1.0);
+  double *x = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double *xs = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  int64_t *ones = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+  for (int64_t a = 0; a < n; ++a) ones[a] = 1;
+  for (int64_t rq = 0; rq < nreq; ++rq) {
+    int64_t b = req[rq * 3 + 0], h = req[rq * 3 + 1], t = req[rq * 3 + 2];
+    int64_t g = h / G;
+    const float *qv = Q + ((b * hq + h) * n + t) * d;
+    const float *kb = K + ((b * hkv + g) * n) * d;
+    const float *vb = V + ((b * hkv + g) * n) * d;
+    int64_t m = t + 1;
+    for (int64_t j = 0; j < m; ++j) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < d; ++c) acc += (double)qv[c] * (double)kb[j * d + c];
+      x[j] = (alpha - 1.0) * sm_scale * acc;
+      xs[j] = x[j];
+    }
+    qsort(xs, (size_t)m, sizeof(double), cmp_dbl_desc);
+    double tau = solve_sorted(xs, ones, m, alpha);
+    double z = 0.0;
+    int64_t ns = 0;
+    for (int64_t j = 0; j < m; ++j) {
+      x[j] = x[j] > tau ? pow(x[j] - tau, ex) : 0.0;
+      z += x[j];
+      ns += x[j] > 0.0;
+    }
+    double *o = O + rq * d;
+    for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+    for (int64_t j = 0; j < m; ++j) {
+      if (x[j] == 0.0) continue;
+      double w = x[j] / z;
+      for (int64_t c = 0; c < d; ++c) o[c] += w * (double)vb[j * d + c];
+    }
+    if (tau_out) tau_out[rq] = tau;
+    if (support) support[rq] = ns;
+  }
+  free(x);
+  free(xs);
+  free(ones);
+}
