@@ -20,7 +20,9 @@ the same step over the cache stored as a shuffled pool of 64-token pages),
 `bf16_long_prefill_n256k` (16/2 heads, N = 262144, B = 128, top-32) and
 `token_entmax_prefill_n32k` (every query token routed by alpha-entmax, cap
 32, attention over 64-query tile masks), each with its step time, per-stage
-times and attention TFLOP/s.
+times and attention TFLOP/s, and `entmax_attn_prefill_n16k` (token-level
+alpha-entmax attention, dense causal with zero key tiles skipped) timed
+beside the dense causal softmax of the same inputs (every block selected).
 """
 from __future__ import annotations
 
@@ -43,6 +45,7 @@ DECODE = "bf16_decode_l128k"
 ENTMAX = "entmax_prefill_n64k"
 LONG = "bf16_long_prefill_n256k"
 TOKEN = "token_entmax_prefill_n32k"
+ENTMAX_ATTN = "entmax_attn_prefill_n16k"
 COUNTERS = os.path.join(HERE, "profiles", "attend_prefill_bf16_gqa_n32k_counters.txt")
 
 
@@ -57,6 +60,8 @@ def parse():
     p.add_argument("--no-entmax", action="store_true", help="skip the entmax prefill extra")
     p.add_argument("--no-long", action="store_true", help="skip the N=262144 prefill extra")
     p.add_argument("--no-token", action="store_true", help="skip the per-token routing extra")
+    p.add_argument("--no-entmax-attn", action="store_true",
+                   help="skip the token-level entmax attention extra")
     p.add_argument("--cpu-sample-blocks", type=int, default=12)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
@@ -286,6 +291,48 @@ def prefill_extra(r):
     return out
 
 
+def run_entmax_attn(bsa, torch, steps, warmup, refine=2):
+    """Token-level alpha-entmax attention (one call per step) and, on the same
+    inputs, the dense causal softmax through the block-sparse kernel with
+    every block selected.  TFLOP/s are dense-causal equivalents (4 d flops
+    per causal pair), the unit in which both are compared."""
+    w = synth.WORKLOADS[ENTMAX_ATTN]
+    x = device_inputs(w, torch)
+    Q, K, V = x["Q"], x["K"], x["V"]
+    O = torch.empty_like(Q)
+    nb = w.nblk
+    idx = torch.arange(nb, dtype=torch.int32, device="cuda").repeat(w.batch * w.hkv * nb, 1) \
+        .reshape(w.batch, w.hkv, nb, nb)
+    cnt = (torch.arange(nb, dtype=torch.int32, device="cuda") + 1).repeat(w.batch * w.hkv, 1) \
+        .reshape(w.batch, w.hkv, nb)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    t_ent = timed(lambda: bsa.attend_entmax(Q, K, V, w.alpha, refine=refine, out=O))
+    t_soft = timed(lambda: bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O))
+    dense = 4.0 * w.d * w.hq * w.batch * w.n * (w.n + 1) / 2
+    _, tau = bsa.attend_entmax(Q, K, V, w.alpha, refine=refine, want_tau=True)
+    torch.cuda.synchronize()
+    del x, Q, K, V, O, idx, cnt, tau
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+            "seq_len": w.n, "head_dim": w.d, "alpha": w.alpha, "refine": refine,
+            "query_scale": w.q_scale, "ms_per_step": t_ent,
+            "dense_equiv_TFLOP_per_s": dense / t_ent / 1e9,
+            "dense_softmax_ms": t_soft, "dense_softmax_TFLOP_per_s": dense / t_soft / 1e9,
+            "speedup_vs_dense_softmax": t_soft / t_ent}
+
+
 def run_decode(bsa, torch, steps, warmup, with_paged=True):
     w = synth.WORKLOADS[DECODE]
     x = device_inputs(w, torch)
@@ -401,6 +448,8 @@ def main():
         if not flag:
             extra[name] = prefill_extra(run_prefill(bsa, torch, synth.WORKLOADS[name], a.steps,
                                                     a.warmup, keep_inputs=False))
+    if not a.no_entmax_attn:
+        extra[ENTMAX_ATTN] = run_entmax_attn(bsa, torch, a.steps, a.warmup)
     if extra:
         out["extra"] = extra
     if not a.no_cpu:

@@ -43,8 +43,8 @@ STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BS
 
 EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_summarize_blocks_paged",
            "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill", "bsa_token_mask",
-           "bsa_attend_decode", "bsa_decode_topk", "bsa_decode_topk_paged", "bsa_workspace_size",
-           "bsa_last_error", "bsa_version")
+           "bsa_attend_decode", "bsa_decode_topk", "bsa_decode_topk_paged", "bsa_attend_entmax",
+           "bsa_workspace_size", "bsa_last_error", "bsa_version")
 
 
 class Shape(ctypes.Structure):
@@ -82,12 +82,14 @@ lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, 
 lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32, _P, _i32, _P, _sz,
                                    _P]
 lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
+lib.bsa_attend_entmax.argtypes = [_SP, _P, _P, _P, _f32, _i32, _f32, _P, _i32, _P, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
 lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
                                 _P, _sz, _P]
 for _f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_summarize_blocks_paged,
            lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill, lib.bsa_token_mask,
-           lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged):
+           lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged,
+           lib.bsa_attend_entmax):
     _f.restype = ctypes.c_int
 lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
 lib.bsa_workspace_size.restype = _sz
@@ -277,6 +279,21 @@ def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None,
                                   _ptr(cnt), idx.shape[-1], sm_scale, _ptr(wsel), sigma, _ptr(O),
                                   _dtype_code(O), _ptr(wsb), nws, _stream(Q)))
     return O
+
+
+def attend_entmax(Q, K, V, alpha, refine=2, sm_scale=0.0, out_dtype=None, out=None,
+                  want_tau=False):
+    """Causal token-level alpha-entmax attention (bf16 Q [b, Hq, N, d],
+    K/V [b, Hkv, N, d]).  Returns O, or (O, tau) with want_tau."""
+    b, hq, n, d = Q.shape
+    odt = out_dtype or Q.dtype
+    O = out if out is not None else torch.empty((b, hq, n, d), dtype=odt, device=Q.device)
+    tau = torch.empty((b, hq, n), dtype=torch.float32, device=Q.device) if want_tau else None
+    shape = make_shape(batch=b, hq=hq, hkv=K.shape[1], d=d, B=64, dtype=_dtype_code(Q),
+                       mode=PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=O)
+    _check(lib.bsa_attend_entmax(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), alpha, refine,
+                                 sm_scale, _ptr(O), _dtype_code(O), _ptr(tau), _stream(Q)))
+    return (O, tau) if want_tau else O
 
 
 def token_mask(idx, cnt, B, kv_len=None, out=None):

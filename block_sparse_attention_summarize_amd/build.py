@@ -17,11 +17,13 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.cpp", "pool.hip", "route.hip", "attend.hip", "decode.hip", "mask.hip"]
+SOURCES = ["api.cpp", "pool.hip", "route.hip", "attend.hip", "decode.hip", "mask.hip",
+           "entmax_attn.hip"]
 # The attention kernels mask with -inf and never produce NaN on finite
 # inputs; without NaNs to honour, fmaxf lowers to bare v_max/v_max3 instead
 # of first quieting every MFMA result (one extra VALU op per input).
-EXTRA_FLAGS = {"attend.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"attend.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"],
+               "entmax_attn.hip": ["-fno-honor-nans"]}
 
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-x", "hip",

@@ -755,6 +755,51 @@ static int decode_topk_impl(const bsa_shape* s, const bsa_pages* pg, const void*
   return device_status(bsa::launch_decode_parts(a, st), "decode_topk");
 }
 
+int bsa_attend_entmax(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                      float alpha, int32_t refine, float sm_scale, void* O, int32_t o_dtype,
+                      float* tau_out, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if (s->mode != BSA_PREFILL) return fail(BSA_ERR_INVALID, "bsa_attend_entmax needs BSA_PREFILL");
+  if (s->dtype != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax takes bf16 inputs");
+  if (!(alpha > 1.f) || !std::isfinite(alpha)) return fail(BSA_ERR_INVALID, "alpha must be > 1");
+  if (alpha > 2.f)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax supports 1 < alpha <= 2 (got %g)",
+                static_cast<double>(alpha));
+  if (refine < 0 || refine > 8)
+    return fail(BSA_ERR_INVALID, "refine must be in [0, 8] (got %d)", refine);
+  if ((s->q_len + 63) / 64 > bsa::entmax_attend_max_tiles())
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax supports at most %d tokens",
+                64 * bsa::entmax_attend_max_tiles());
+  if (tau_out && !aligned16(tau_out)) return fail(BSA_ERR_UNSUPPORTED, "tau_out must be 16-byte aligned");
+  // the shared argument checks of the attention calls (a dummy selection)
+  bsa::AttendArgs t;
+  static const int32_t one = 0;
+  if ((rc = attend_common(s, Q, K, V, &one, &one, 1, sm_scale, O, o_dtype, t)) != BSA_OK)
+    return rc;
+  bsa::EntmaxAttnArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.qs = t.qs;
+  a.ks = t.ks;
+  a.vs = t.vs;
+  a.os = t.os;
+  a.tau = tau_out;
+  a.batch = s->batch;
+  a.hq = s->n_q_heads;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.refine = refine;
+  a.n = s->q_len;
+  a.sm_scale = t.sm_scale;
+  a.alpha = alpha;
+  a.out_f32 = o_dtype == BSA_F32;
+  return device_status(bsa::launch_entmax_attend(a, static_cast<hipStream_t>(stream)),
+                       "attend_entmax");
+}
+
 int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void* V,
                     const float* S, const int32_t* kv_lens, int32_t k_total, uint32_t force,
                     float score_scale, float sm_scale, int32_t* idx, int32_t* cnt, void* O,

@@ -140,6 +140,25 @@ struct TokenMaskArgs {
 };
 hipError_t launch_token_mask(const TokenMaskArgs& a, hipStream_t stream);
 
+// Token-level alpha-entmax attention, causal prefill (bf16 Q/K/V, q_len ==
+// kv_len == n): o_t = sum_{j<=t} p_tj v_j, p_t = alpha-entmax of
+// (alpha-1) sm_scale q_t . k_j; `refine` hybrid steps after the histogram
+// bracket.
+struct EntmaxAttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  Strides3 qs, ks, vs, os;
+  float* tau;  // optional [batch, hq, n]: the threshold used, in units of x
+  int batch, hq, hkv, d, refine;
+  int64_t n;
+  float sm_scale, alpha;
+  bool out_f32;
+};
+int entmax_attend_max_tiles();
+hipError_t launch_entmax_attend(const EntmaxAttnArgs& a, hipStream_t stream);
+
 // Single-token decode: routing (route = 1) and/or attention (attend = 1) for
 // every (batch, KV head) row, hsplit workgroups per row splitting the query
 // heads.  Without routing, the selection is read from idx/cnt.

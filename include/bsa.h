@@ -24,6 +24,9 @@
  *                               decode).
  *            bsa_token_mask     per-token selections (BSA_TOKEN) as active-block
  *                               masks of 64-query tiles.
+ *            bsa_attend_entmax  token-level alpha-entmax attention
+ *                               ("AdaSplash-2"), dense causal, zero tiles
+ *                               skipped.
  *   Decode   bsa_decode_topk    Stage 1 (top-k) and Stage 2 for one decode
  *                               step in a single launch (bsa_decode_topk_paged,
  *                               bsa_summarize_blocks_paged: the same over a
@@ -265,6 +268,29 @@ int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, con
                        const int32_t *idx, const int32_t *cnt, int32_t k_max, float sm_scale,
                        const float *wsel, float sigma, void *O, int32_t o_dtype, void *ws,
                        size_t ws_bytes, void *stream);
+
+/*
+ * Token-level alpha-entmax attention, causal prefill ("AdaSplash-2", sections
+ * 1 and 2): the weights of query t over its keys j <= t are
+ * p = alpha-entmax(z_t), x_j = (alpha-1) z_j = (alpha-1) sm_scale q_t . k_j,
+ * p_j = [x_j - tau_t]_+^(1/(alpha-1)) with sum_j p_j = 1 (exact zeros outside
+ * the support); o_t = sum_j p_j v_j, with the weights renormalised by their
+ * sum.  tau_t is bracketed by a 16-bin histogram of x_max - x on [0, 1)
+ * ("AdaSplash-2", 2.A), then refined by `refine` hybrid steps (Halley for
+ * alpha <= 1.5, Newton for 1.5 < alpha <= 2; bisection when a step leaves the
+ * bracket); key tiles of 64 with no x above the bracket's lower end are
+ * skipped in the later passes.  alpha > 2 (the pages' secant branch) is not
+ * supported.
+ *   Q, K, V bf16 [batch, H, N, d] (q_len == kv_len == N <= 131072);
+ *   O [batch, Hq, N, d] bf16 or fp32 (o_dtype); sm_scale 0 means 1/sqrt(d).
+ *   refine in [0, 8] (0: tau = the histogram lower bound).
+ *   tau_out NULL or fp32 [batch, Hq, N]: the threshold used, in units of x.
+ * Errors: BSA_ERR_INVALID (alpha <= 1, refine outside [0, 8], bad shape),
+ * BSA_ERR_UNSUPPORTED (alpha > 2, fp32 inputs, N > 131072, strides).
+ */
+int bsa_attend_entmax(const bsa_shape *shape, const void *Q, const void *K, const void *V,
+                      float alpha, int32_t refine, float sm_scale, void *O, int32_t o_dtype,
+                      float *tau_out, void *stream);
 
 /*
  * Active-block masks of per-token selections ("DashAttention", Estágio 2,

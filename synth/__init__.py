@@ -8,7 +8,8 @@ method's arithmetic.  Recipe (stated once here, used everywhere):
   tensor stream s is drawn with ``numpy.random.default_rng(SeedSequence([seed,
   s, b, h, c])).standard_normal((rows, d), dtype=float32)``, so any slice can be
   regenerated without drawing the whole tensor; streams: q=0, k=1, v=2, u=3,
-  planted key blocks=4, planted query positions=5, query-tile components=6;
+  planted key blocks=4, planted query positions=5, query-tile components=6,
+  key-tile components=7;
 * planting (the long-context retrieval structure): a unit vector
   u = g/|g|, g ~ N(0, I_d) (stream 3, fp64), a set of planted key blocks drawn
   without replacement (stream 4, identical for every KV head) whose keys get
@@ -18,6 +19,13 @@ method's arithmetic.  Recipe (stated once here, used everywhere):
   shares a component c ~ N(0, I_d) per (batch, head, tile), drawn as stream 6
   with one row per tile, and its queries get ``+ loc_amp * c`` (before the
   planting), so nearby tokens route alike without routing identically;
+* key locality (kloc_amp > 0): likewise every tile of 64 consecutive keys
+  shares a component (stream 7, per (batch, KV head, tile)) added as
+  kloc_amp * c; with query locality this gives scores a block structure (a
+  query tile favours a few key tiles), as attention over real text has;
+* query scale (q_scale != 1): queries are multiplied by q_scale after the
+  locality component and before the planting, which sharpens the score
+  distribution the way trained attention heads are sharper than random ones;
 * bf16 tensors are the round-to-nearest-even bf16 of the fp32 values.
 """
 from __future__ import annotations
@@ -29,7 +37,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 CHUNK = 4096
-STREAM_Q, STREAM_K, STREAM_V, STREAM_U, STREAM_PK, STREAM_PQ, STREAM_QL = 0, 1, 2, 3, 4, 5, 6
+STREAM_Q, STREAM_K, STREAM_V, STREAM_U, STREAM_PK, STREAM_PQ, STREAM_QL, STREAM_KL = \
+    0, 1, 2, 3, 4, 5, 6, 7
 QTILE = 64  # query tokens sharing one locality component
 
 FORCE_DIAG = 1
@@ -48,7 +57,7 @@ class Workload:
     d: int
     B: int
     mode: str  # "prefill", "token" (prefill routed per query token) or "decode"
-    router: str  # "topk" or "entmax"
+    router: str  # "topk", "entmax", or "entmax_attn" (token-level entmax attention, no routing)
     k_total: int = 0
     force: int = 0
     alpha: float = 1.5
@@ -63,6 +72,8 @@ class Workload:
     kv_lens: tuple = ()  # decode only; empty -> all equal to n
     loc_amp: float = 0.0  # query-tile component amplitude
     sigma: float = 0.0  # prior strength of the fine softmax (entmax routing); 0: plain softmax
+    q_scale: float = 1.0  # queries multiplied by this (score temperature), before planting
+    kloc_amp: float = 0.0  # key-tile component amplitude
 
     @property
     def nblk(self) -> int:
@@ -120,6 +131,13 @@ WORKLOADS = {
         "token_entmax_prefill_n32k", "bf16", 1, 32, 8, 32768, 128, 64, "token", "entmax",
         alpha=1.5, gamma=4.0, cap=32, n_bins=16, max_iter=8, force=FORCE_DIAG, seed=5,
         planted_blocks=32, planted_query_frac=0.01, loc_amp=4.0, sigma=1.0),
+    # token-level alpha-entmax attention (no block routing): dense causal with
+    # zero key tiles skipped; block-structured scores (query and key tiles
+    # with shared components), queries sharpened by 2
+    "entmax_attn_prefill_n16k": Workload(
+        "entmax_attn_prefill_n16k", "bf16", 1, 32, 8, 16384, 128, 64, "prefill", "entmax_attn",
+        alpha=1.5, seed=6, q_scale=2.0, loc_amp=2.0, kloc_amp=2.0, planted_blocks=32,
+        planted_query_frac=0.01),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -209,15 +227,18 @@ def gen(w: Workload, name: str, heads=None, t0: int = 0, t1=None, batches=None):
             a, e = max(t0, j * w.B), min(t1, (j + 1) * w.B)
             if a < e:
                 out[:, :, a - t0:e - t0, :] += w.amp * u
-    if name == "q" and w.loc_amp > 0 and w.mode != "decode":
+    amp, lstream = (w.loc_amp, STREAM_QL) if name == "q" else (w.kloc_amp, STREAM_KL)
+    if name in ("q", "k") and amp > 0 and w.mode != "decode":
         tiles = (rows + QTILE - 1) // QTILE
         a, e = t0 // QTILE, (t1 - 1) // QTILE + 1
         for bi, b in enumerate(batches):
             for hi, h in enumerate(heads):
                 c = np.empty((e - a, w.d), np.float32)
-                _fill(w, STREAM_QL, nh, tiles, a, e, b, h, c)
+                _fill(w, lstream, nh, tiles, a, e, b, h, c)
                 tok = np.arange(t0, t1) // QTILE - a
-                out[bi, hi] += np.float32(w.loc_amp) * c[tok]
+                out[bi, hi] += np.float32(amp) * c[tok]
+    if name == "q" and w.q_scale != 1.0:
+        out *= np.float32(w.q_scale)
     if name == "q" and w.planted_query_frac > 0 and w.mode != "decode":
         u = planted_vector(w).astype(np.float32)
         pos = planted_query_positions(w)

@@ -1,0 +1,85 @@
+"""GPU parity of token-level alpha-entmax attention ("AdaSplash-2") against
+the fp64 oracle on seeded inputs: every row of small shapes spanning several
+64-query tiles and a ragged tail, sampled rows at a longer length.  Calls go
+through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+import block_sparse_attention_summarize_amd as bsa  # noqa: E402
+
+BASE = synth.WORKLOADS["entmax_attn_prefill_n16k"]
+CASES = {
+    "a15_gqa": BASE.scaled(hq=8, hkv=2, n=64 * 5 + 17, planted_blocks=2),
+    "a15_dense_scores": BASE.scaled(hq=4, hkv=1, n=64 * 4 + 3, q_scale=1.0, planted_blocks=2),
+    "a2_sparsemax": BASE.scaled(hq=4, hkv=2, n=64 * 3 + 40, alpha=2.0, planted_blocks=2),
+    "a125": BASE.scaled(hq=4, hkv=4, n=64 * 3 + 1, alpha=1.25, q_scale=2.0, planted_blocks=1),
+    "a175_newton": BASE.scaled(hq=4, hkv=2, n=64 * 3 + 9, alpha=1.75, q_scale=3.0, planted_blocks=1),
+    "a15_d64": BASE.scaled(hq=6, hkv=3, d=64, n=64 * 6, planted_blocks=2),
+}
+
+
+def _cpu(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_entmax_attention_matches_oracle(name, out_f32):
+    w = CASES[name]
+    print(f"[entmax attention] {name} out_f32={out_f32}", flush=True)
+    x = parity.make(w)
+    O, tau = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=2,
+                               out_dtype=torch.float32 if out_f32 else None, want_tau=True)
+    ref, rtau, sup = oracle.entmax_attend(x["q"], x["k"], x["v"], w.alpha)
+    worst = parity.check_attention(w, _cpu(O).reshape(ref.shape), ref, out_f32)
+    terr = np.abs(_cpu(tau).ravel() - rtau)
+    # Halley / Newton from the histogram bracket: converged after two steps
+    assert terr.max() < 1e-3, terr.max()
+    print(f"max abs err {worst:.3e}, tau err max {terr.max():.2e} median {np.median(terr):.2e}, "
+          f"mean support {sup.mean():.1f} of {(w.n + 1) / 2:.0f} keys")
+
+
+def test_entmax_attention_zero_query_is_the_causal_mean():
+    w = CASES["a15_gqa"]
+    x = parity.make(w)
+    Q = torch.zeros_like(x["Q"])
+    O = bsa.attend_entmax(Q, x["K"], x["V"], 1.5, out_dtype=torch.float32)
+    G = w.hq // w.hkv
+    v = np.repeat(x["v"].astype(np.float64), G, axis=1)
+    ref = np.cumsum(v, axis=2) / np.arange(1, w.n + 1)[None, None, :, None]
+    np.testing.assert_allclose(_cpu(O), ref, rtol=0, atol=2e-3)
+
+
+def test_entmax_attention_long_sampled():
+    w = BASE.scaled(n=8192, hq=8, hkv=2)
+    x = parity.make(w)
+    O = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, out_dtype=torch.float32)
+    rng = np.random.default_rng(9)
+    rows = sorted({0, 63, 64, w.n - 1} | set(rng.choice(w.n, 60, replace=False).tolist()))
+    req = np.array([[0, h, t] for h in range(w.hq) for t in rows], np.int64)
+    ref, _, sup = oracle.entmax_attend(x["q"], x["k"], x["v"], w.alpha, req=req)
+    got = _cpu(O)[req[:, 0], req[:, 1], req[:, 2]]
+    worst = parity.check_attention(w, got, ref, True)
+    print(f"{len(req)} sampled rows, max abs err {worst:.3e}, mean support {sup.mean():.1f}")
+
+
+def test_entmax_attention_argument_errors():
+    w = CASES["a15_gqa"]
+    x = parity.make(w)
+    with pytest.raises(bsa.BsaError, match="alpha"):
+        bsa.attend_entmax(x["Q"], x["K"], x["V"], 1.0)
+    with pytest.raises(bsa.BsaError, match="alpha <= 2"):
+        bsa.attend_entmax(x["Q"], x["K"], x["V"], 3.0)
+    with pytest.raises(bsa.BsaError, match="refine"):
+        bsa.attend_entmax(x["Q"], x["K"], x["V"], 1.5, refine=9)
+    with pytest.raises(bsa.BsaError, match="bf16"):
+        bsa.attend_entmax(x["Q"].float(), x["K"].float(), x["V"].float(), 1.5)
