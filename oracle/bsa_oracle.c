@@ -787,3 +787,87 @@ void orc_entmax_attend(const float *Q, const float *K, const float *V, int64_t n
   free(xs);
   free(ones);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Backward of the fine attention over the selected blocks.                   */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Gradients of the causal block-sparse attention (Stage 2, prefill rows; the
+ * backward pass the pages single out as where training time goes: "SSA",
+ * introduction; "AdaSplash-2", section 4, skipping zero blocks) for a fixed
+ * selection.  For every query t of head h with attended token set T(t)
+ * (as orc_attend, prefill mode):
+ *   a_u = sm_scale q_t . k_u, p = softmax(a) over T(t), o_t = sum_u p_u v_u,
+ *   D_t = dO_t . o_t,  dp_u = dO_t . v_u,  ds_u = p_u (dp_u - D_t),
+ *   dQ_t += sm_scale sum_u ds_u k_u,
+ *   dK_u += sm_scale ds_u q_t,  dV_u += p_u dO_t   (KV head h / G: the
+ *   group's query heads add into the same dK, dV).
+ *   Q, dO : [nb, hq, n, d];  K, V : [nb, hkv, n, d] (fp32); idx/cnt per query
+ *   block.  dQ [nb, hq, n, d], dK, dV [nb, hkv, n, d]: fp64, overwritten.
+ */
+void orc_attend_backward(const float *Q, const float *K, const float *V, const float *dO,
+                         int64_t nb, int64_t hq, int64_t hkv, int64_t n, int64_t d, int64_t B,
+                         const int32_t *idx, const int32_t *cnt, int64_t kmax, double sm_scale,
+                         double *dQ, double *dK, double *dV) {
+  int64_t G = hq / hkv;
+  int64_t nrow = (n + B - 1) / B;
+  int64_t cap = kmax * B + 1;
+  double *p = (double *)malloc(sizeof(double) * (size_t)cap);
+  int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+  double *o = (double *)malloc(sizeof(double) * (size_t)d);
+  for (int64_t a = 0; a < nb * hq * n * d; ++a) dQ[a] = 0.0;
+  for (int64_t a = 0; a < nb * hkv * n * d; ++a) dK[a] = dV[a] = 0.0;
+  for (int64_t b = 0; b < nb; ++b)
+    for (int64_t h = 0; h < hq; ++h)
+      for (int64_t t = 0; t < n; ++t) {
+        int64_t g = h / G;
+        int64_t rowid = (b * hkv + g) * nrow + t / B;
+        const float *qv = Q + ((b * hq + h) * n + t) * d;
+        const float *gv = dO + ((b * hq + h) * n + t) * d;
+        const float *kb = K + ((b * hkv + g) * n) * d;
+        const float *vb = V + ((b * hkv + g) * n) * d;
+        double *dq = dQ + ((b * hq + h) * n + t) * d;
+        double *dkb = dK + ((b * hkv + g) * n) * d;
+        double *dvb = dV + ((b * hkv + g) * n) * d;
+        int64_t nt = 0;
+        for (int64_t s = 0; s < cnt[rowid]; ++s) {
+          int64_t j = idx[rowid * kmax + s];
+          for (int64_t u = j * B; u < (j + 1) * B && u < n && u <= t; ++u) tok[nt++] = u;
+        }
+        if (nt == 0) continue;
+        double mx = -INFINITY, z = 0.0;
+        for (int64_t a = 0; a < nt; ++a) {
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c) acc += (double)qv[c] * (double)kb[tok[a] * d + c];
+          p[a] = acc * sm_scale;
+          if (p[a] > mx) mx = p[a];
+        }
+        for (int64_t a = 0; a < nt; ++a) {
+          p[a] = exp(p[a] - mx);
+          z += p[a];
+        }
+        for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t a = 0; a < nt; ++a) {
+          p[a] /= z;
+          for (int64_t c = 0; c < d; ++c) o[c] += p[a] * (double)vb[tok[a] * d + c];
+        }
+        double D = 0.0;
+        for (int64_t c = 0; c < d; ++c) D += (double)gv[c] * o[c];
+        for (int64_t a = 0; a < nt; ++a) {
+          const float *kv = kb + tok[a] * d;
+          const float *vv = vb + tok[a] * d;
+          double dp = 0.0;
+          for (int64_t c = 0; c < d; ++c) dp += (double)gv[c] * (double)vv[c];
+          double ds = p[a] * (dp - D);
+          for (int64_t c = 0; c < d; ++c) {
+            dq[c] += sm_scale * ds * (double)kv[c];
+            dkb[tok[a] * d + c] += sm_scale * ds * (double)qv[c];
+            dvb[tok[a] * d + c] += p[a] * (double)gv[c];
+          }
+        }
+      }
+  free(p);
+  free(tok);
+  free(o);
+}
