@@ -22,7 +22,9 @@ the same step over the cache stored as a shuffled pool of 64-token pages),
 32, attention over 64-query tile masks), each with its step time, per-stage
 times and attention TFLOP/s, and `entmax_attn_prefill_n16k` (token-level
 alpha-entmax attention, dense causal with zero key tiles skipped) timed
-beside the dense causal softmax of the same inputs (every block selected).
+beside the dense causal softmax of the same inputs (every block selected),
+and `backward` (the gradients dQ, dK, dV of the headline attention for its
+selection, beside the forward that feeds them).
 """
 from __future__ import annotations
 
@@ -57,6 +59,7 @@ def parse():
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-decode", action="store_true", help="skip the decode extra")
+    p.add_argument("--no-backward", action="store_true", help="skip the backward extra")
     p.add_argument("--no-entmax", action="store_true", help="skip the entmax prefill extra")
     p.add_argument("--no-long", action="store_true", help="skip the N=262144 prefill extra")
     p.add_argument("--no-token", action="store_true", help="skip the per-token routing extra")
@@ -260,6 +263,7 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
         del uidx, ucnt, ubits
     if keep_inputs:
         res["x"] = x
+        res["sel"] = (idx, cnt)
     else:
         del x, Q, K, V, O, S, sel, idx, cnt, ws, aws, wsel
         torch.cuda.empty_cache()
@@ -404,6 +408,60 @@ def run_decode(bsa, torch, steps, warmup, with_paged=True):
             "GB_per_s": total / (paged["us_per_step_median"] * 1e-6) / 1e9}})
 
 
+def run_backward(bsa, torch, w, r, steps, warmup):
+    """Training pass of the fine attention on the headline inputs and
+    selection: the forward with its log-normaliser, then the gradients dQ, dK,
+    dV for a seeded upstream gradient (bf16, same shapes as the inputs).
+    TFLOP/s use the usual accounting of 2.5x the forward's flops for the
+    backward (five products of the pair's size against the forward's two,
+    10 d flops per attended pair); the kernels execute seven (dQ recomputes
+    the scores and dP instead of atomically accumulating)."""
+    x = r["x"]
+    Q, K, V = x["Q"], x["K"], x["V"]
+    idx, cnt = r["sel"]
+    do_st, _ = synth.gen_stored(w, "do")
+    dO = torch.from_numpy(do_st.view(np.int16)).to("cuda").view(torch.bfloat16)
+    del do_st
+    O = torch.empty_like(Q)
+    L = torch.empty((w.batch, w.hq, w.n), dtype=torch.float32, device="cuda")
+    shape = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B, dtype=bsa.BF16,
+                           mode=bsa.PREFILL, q_len=w.n, kv_len=w.n, q=Q, k=K, v=V, o=O)
+    ws = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_BACKWARD, shape, idx.shape[-1]),
+                     dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        O_, L_ = bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O, want_lse=True)
+        L.copy_(L_)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    t_plain = timed(lambda: bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O))
+    fwd()
+    t_bwd = timed(lambda: bsa.attend_backward(Q, K, V, O, dO, L, w.B, idx, cnt, ws=ws))
+    fwd_flops = r["flops"]
+    bwd_flops = 2.5 * fwd_flops
+    out = {"workload": w.name, "forward_ms": t_plain, "backward_ms": t_bwd,
+           "train_step_ms": t_plain + t_bwd,
+           "backward_TFLOP_per_s": bwd_flops / t_bwd / 1e9,
+           "backward_frac_mfma_peak": bwd_flops / t_bwd / 1e9 / PEAK_BF16_TFLOPS,
+           "backward_executed_TFLOP_per_s": 3.5 * fwd_flops / t_bwd / 1e9,
+           "workspace_MiB": ws.numel() / 2**20,
+           "accounting": "backward flops = 2.5 x forward (10 d per attended pair)"}
+    del dO, O, L, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     a = parse()
     if a.copy_calibration:
@@ -442,6 +500,8 @@ def main():
                      "traffic": read_traffic(kernel_src), "avg_launch_ms": att_s * 1e3},
     }
     extra = {}
+    if not a.no_backward:
+        extra["backward"] = run_backward(bsa, torch, w, r, a.steps, a.warmup)
     if not a.no_decode:
         extra["decode"] = run_decode(bsa, torch, a.steps, a.warmup)
     for name, flag in ((ENTMAX, a.no_entmax), (LONG, a.no_long), (TOKEN, a.no_token)):

@@ -37,14 +37,14 @@ F32, BF16 = 0, 1
 PREFILL, DECODE, TOKEN = 0, 1, 2
 FORCE_DIAG, FORCE_FIRST, FORCE_TAIL = 1, 2, 4
 OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE, \
-    OP_DECODE_TOPK, OP_ATTEND_PREFILL_PRIOR = range(7)
+    OP_DECODE_TOPK, OP_ATTEND_PREFILL_PRIOR, OP_ATTEND_BACKWARD = range(8)
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
 EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_summarize_blocks_paged",
            "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill", "bsa_token_mask",
            "bsa_attend_decode", "bsa_decode_topk", "bsa_decode_topk_paged", "bsa_attend_entmax",
-           "bsa_workspace_size", "bsa_last_error", "bsa_version")
+           "bsa_attend_backward", "bsa_workspace_size", "bsa_last_error", "bsa_version")
 
 
 class Shape(ctypes.Structure):
@@ -79,8 +79,10 @@ lib.bsa_decode_topk_paged.argtypes = [_SP, _PP, _P, _P, _P, _P, _P, _i32, _u32, 
 lib.bsa_route_topk.argtypes = [_SP, _P, _P, _P, _i32, _u32, _f32, _P, _P, _P, _P, _sz, _P]
 lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, _u32, _f32, _P,
                                  _P, _P, _P, _P, _P, _sz, _P]
-lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32, _P, _i32, _P, _sz,
-                                   _P]
+lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32, _P, _i32, _P, _P,
+                                   _sz, _P]
+lib.bsa_attend_backward.argtypes = [_SP, _P, _P, _P, _P, _i32, _P, _P, _P, _P, _i32, _f32, _P, _P,
+                                    _P, _i32, _P, _sz, _P]
 lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
 lib.bsa_attend_entmax.argtypes = [_SP, _P, _P, _P, _f32, _i32, _f32, _P, _i32, _P, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
@@ -89,7 +91,7 @@ lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32,
 for _f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_summarize_blocks_paged,
            lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill, lib.bsa_token_mask,
            lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged,
-           lib.bsa_attend_entmax):
+           lib.bsa_attend_entmax, lib.bsa_attend_backward):
     _f.restype = ctypes.c_int
 lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
 lib.bsa_workspace_size.restype = _sz
@@ -260,14 +262,16 @@ def route_entmax(Q, S, B, alpha, gamma, cap, force=FORCE_DIAG, n_bins=16, max_it
 
 
 def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None, token=False,
-                   ws=None, wsel=None, sigma=0.0):
+                   ws=None, wsel=None, sigma=0.0, want_lse=False):
     """Causal attention over the selected blocks.  Q [b, Hq, N, d], K/V [b, Hkv, N, d].
     token=True: idx/cnt are per-token selections [b, Hkv, N, width].
-    wsel (routing weights shaped like idx) and sigma: prior-induced softmax."""
+    wsel (routing weights shaped like idx) and sigma: prior-induced softmax.
+    want_lse: also return the log-normaliser [b, Hq, N] fp32 the backward needs."""
     b, hq, n, d = Q.shape
     hkv = K.shape[1]
     odt = out_dtype or Q.dtype
     O = out if out is not None else torch.empty((b, hq, n, d), dtype=odt, device=Q.device)
+    L = torch.empty((b, hq, n), dtype=torch.float32, device=Q.device) if want_lse else None
     shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(Q),
                        mode=TOKEN if token else PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K,
                        v=V, o=O)
@@ -277,8 +281,54 @@ def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None,
         assert wsel.shape == idx.shape and wsel.dtype == torch.float32 and wsel.is_contiguous()
     _check(lib.bsa_attend_prefill(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx),
                                   _ptr(cnt), idx.shape[-1], sm_scale, _ptr(wsel), sigma, _ptr(O),
-                                  _dtype_code(O), _ptr(wsb), nws, _stream(Q)))
-    return O
+                                  _dtype_code(O), _ptr(L), _ptr(wsb), nws, _stream(Q)))
+    return (O, L) if want_lse else O
+
+
+def attend_backward(Q, K, V, O, dO, lse, B, idx, cnt, sm_scale=0.0, grad_dtype=None, ws=None):
+    """Gradients (dQ, dK, dV) of attend_prefill's output (block rows, bf16)
+    for upstream gradient dO, given the forward's O and lse.  The gradients
+    take the strides of Q, K, V; dO is brought to O's strides and Q's dtype."""
+    b, hq, n, d = Q.shape
+    gdt = grad_dtype or Q.dtype
+    dQ = torch.empty_strided(Q.size(), Q.stride(), dtype=gdt, device=Q.device)
+    dK = torch.empty_strided(K.size(), K.stride(), dtype=gdt, device=K.device)
+    dV = torch.empty_strided(V.size(), V.stride(), dtype=gdt, device=V.device)
+    if dO.dtype != Q.dtype or dO.stride() != O.stride():
+        t = torch.empty_strided(O.size(), O.stride(), dtype=Q.dtype, device=O.device)
+        t.copy_(dO)
+        dO = t
+    shape = make_shape(batch=b, hq=hq, hkv=K.shape[1], d=d, B=B, dtype=_dtype_code(Q),
+                       mode=PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=O)
+    wsb, nws = _workspace(OP_ATTEND_BACKWARD, shape, idx.shape[-1], Q.device, ws)
+    _check(lib.bsa_attend_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                   _dtype_code(O), _ptr(dO), _ptr(lse), _ptr(idx), _ptr(cnt),
+                                   idx.shape[-1], sm_scale, _ptr(dQ), _ptr(dK), _ptr(dV),
+                                   _dtype_code(dQ), _ptr(wsb), nws, _stream(Q)))
+    return dQ, dK, dV
+
+
+class _SparseAttention(torch.autograd.Function):
+    """attend_prefill (block rows) with attend_backward as its gradient; the
+    selection is an input without gradient."""
+
+    @staticmethod
+    def forward(ctx, Q, K, V, B, idx, cnt, sm_scale):
+        O, L = attend_prefill(Q, K, V, B, idx, cnt, sm_scale, want_lse=True)
+        ctx.save_for_backward(Q, K, V, O, L, idx, cnt)
+        ctx.B, ctx.sm_scale = B, sm_scale
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, O, L, idx, cnt = ctx.saved_tensors
+        dQ, dK, dV = attend_backward(Q, K, V, O, dO, L, ctx.B, idx, cnt, ctx.sm_scale)
+        return dQ, dK, dV, None, None, None, None
+
+
+def sparse_attention(Q, K, V, B, idx, cnt, sm_scale=0.0):
+    """Differentiable causal block-sparse attention over a fixed selection."""
+    return _SparseAttention.apply(Q, K, V, B, idx, cnt, sm_scale)
 
 
 def attend_entmax(Q, K, V, alpha, refine=2, sm_scale=0.0, out_dtype=None, out=None,

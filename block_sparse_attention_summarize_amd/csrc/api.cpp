@@ -210,6 +210,35 @@ MaskWs mask_ws(const bsa_shape* s, bool prior) {
   w.total = w.uidx + w.ubits + w.ucnt + w.ubias;
   return w;
 }
+// Backward: Delta, the transposed selection, the work plan and the partial
+// sums of key blocks split over several work items.
+constexpr int kBwdChunk = 32;                  // query blocks per key-side work item
+constexpr int64_t kMaxBwdBlocks = 16384;       // one LDS word per key block when marking
+struct BwdWs {
+  size_t delta, bits, items, red, counters, part, total;
+  int64_t max_items, max_red, slots, nwords;
+};
+BwdWs bwd_ws(const bsa_shape* s, int32_t k_max) {
+  BwdWs w{};
+  const int64_t npair = static_cast<int64_t>(s->batch) * s->n_kv_heads;
+  const int64_t nrow = nrow_of(s), nblk = nblk_of(s);
+  const int64_t k = std::max<int64_t>(1, std::min<int64_t>(k_max, nblk));
+  // (row, block) pairs with block <= row: sum over rows of min(k, r + 1)
+  const int64_t per = nrow <= k ? nrow * (nrow + 1) / 2 : k * (k + 1) / 2 + (nrow - k) * k;
+  const int64_t E = npair * per;
+  w.nwords = (nrow + 31) / 32;
+  w.max_items = npair * nblk + (E + kBwdChunk - 1) / kBwdChunk;
+  w.max_red = std::min<int64_t>(npair * nblk, E / (kBwdChunk + 1) + 1);
+  w.slots = E / kBwdChunk + w.max_red + 1;
+  w.delta = align_up(static_cast<size_t>(s->batch) * s->n_q_heads * s->q_len * 4);
+  w.bits = align_up(static_cast<size_t>(npair * w.nwords * nblk) * 4);
+  w.items = align_up(static_cast<size_t>(w.max_items) * 16);
+  w.red = align_up(static_cast<size_t>(w.max_red) * 16);
+  w.counters = align_up(8);
+  w.part = align_up(static_cast<size_t>(w.slots) * 2 * s->block * s->head_dim * 4);
+  w.total = w.delta + w.bits + w.items + w.red + w.counters + w.part;
+  return w;
+}
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (ws_bytes < need)
     return fail(BSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
@@ -341,6 +370,8 @@ size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
       return s->mode == BSA_TOKEN ? mask_ws(s, false).total : 0;
     case BSA_OP_ATTEND_PREFILL_PRIOR:
       return s->mode == BSA_TOKEN ? mask_ws(s, true).total : 0;
+    case BSA_OP_ATTEND_BACKWARD:
+      return s->mode == BSA_PREFILL && k_or_cap >= 1 ? bwd_ws(s, k_or_cap).total : 0;
     default:
       return 0;
   }
@@ -606,6 +637,7 @@ static int attend_common(const bsa_shape* s, const void* Q, const void* K, const
   a.wsel = nullptr;
   a.tbias = nullptr;
   a.sigma = 0.f;
+  a.lse = nullptr;
   a.batch = s->batch;
   a.hq = s->n_q_heads;
   a.hkv = s->n_kv_heads;
@@ -660,17 +692,20 @@ int bsa_token_mask(const bsa_shape* s, const int32_t* idx, const int32_t* cnt, i
 
 int bsa_attend_prefill(const bsa_shape* s, const void* Q, const void* K, const void* V,
                        const int32_t* idx, const int32_t* cnt, int32_t k_max, float sm_scale,
-                       const float* wsel, float sigma, void* O, int32_t o_dtype, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       const float* wsel, float sigma, void* O, int32_t o_dtype, float* lse,
+                       void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
   if (s->mode == BSA_DECODE)
     return fail(BSA_ERR_INVALID, "bsa_attend_prefill needs BSA_PREFILL or BSA_TOKEN");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return fail(BSA_ERR_UNSUPPORTED, "lse must be 4-byte aligned");
   if (!std::isfinite(sigma)) return fail(BSA_ERR_INVALID, "sigma must be finite");
   if (wsel && !aligned16(wsel)) return fail(BSA_ERR_UNSUPPORTED, "wsel must be 16-byte aligned");
   bsa::AttendArgs a;
   if ((rc = attend_common(s, Q, K, V, idx, cnt, k_max, sm_scale, O, o_dtype, a)) != BSA_OK)
     return rc;
+  a.lse = lse;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (s->mode == BSA_TOKEN) {
     // per-token selections -> tile masks (and prior bias) in ws -> masked
@@ -753,6 +788,88 @@ static int decode_topk_impl(const bsa_shape* s, const bsa_pages* pg, const void*
   a.cand_id = reinterpret_cast<int32_t*>(base + dw.cand);
   a.part = reinterpret_cast<float*>(base + 2 * dw.cand);
   return device_status(bsa::launch_decode_parts(a, st), "decode_topk");
+}
+
+int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                        const void* O, int32_t o_dtype, const void* dO, const float* lse,
+                        const int32_t* idx, const int32_t* cnt, int32_t k_max, float sm_scale,
+                        void* dQ, void* dK, void* dV, int32_t g_dtype, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if (s->mode != BSA_PREFILL) return fail(BSA_ERR_INVALID, "bsa_attend_backward needs BSA_PREFILL");
+  if (s->dtype != BSA_BF16)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_backward supports bf16 inputs only");
+  bsa::AttendArgs f;
+  if ((rc = attend_common(s, Q, K, V, idx, cnt, k_max, sm_scale, const_cast<void*>(O), o_dtype,
+                          f)) != BSA_OK)
+    return rc;
+  if ((rc = check_ptr("dO", dO)) != BSA_OK) return rc;
+  if ((rc = check_ptr("dQ", dQ)) != BSA_OK) return rc;
+  if ((rc = check_ptr("dK", dK)) != BSA_OK) return rc;
+  if ((rc = check_ptr("dV", dV)) != BSA_OK) return rc;
+  if (!lse) return fail(BSA_ERR_INVALID, "lse is NULL");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return fail(BSA_ERR_UNSUPPORTED, "lse must be 4-byte aligned");
+  if (g_dtype != s->dtype && g_dtype != BSA_F32)
+    return fail(BSA_ERR_UNSUPPORTED, "g_dtype must be the input dtype or BSA_F32");
+  if ((rc = check_strides("dO", s->o_stride, s->dtype)) != BSA_OK) return rc;
+  if ((rc = check_strides("dQ/dK/dV", s->q_stride, g_dtype)) != BSA_OK) return rc;
+  const int64_t gsz = elem_bytes(g_dtype), osz = elem_bytes(o_dtype);
+  if (s->o_stride[2] < s->head_dim) return fail(BSA_ERR_INVALID, "O token stride must be >= head_dim");
+  if ((s->q_len + 128) * s->o_stride[2] * std::max(osz, gsz) >= (int64_t(1) << 31) ||
+      (s->q_len + 128) * std::max({s->q_stride[2], s->k_stride[2], s->v_stride[2]}) * gsz >=
+          (int64_t(1) << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "one head spans more than 2 GiB");
+  if (nblk_of(s) > kMaxBwdBlocks)
+    return fail(BSA_ERR_UNSUPPORTED, "the backward supports at most %lld blocks",
+                (long long)kMaxBwdBlocks);
+  const BwdWs bw = bwd_ws(s, k_max);
+  if (bw.max_items >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "problem too large");
+  if ((rc = check_ws(ws, ws_bytes, bw.total)) != BSA_OK) return rc;
+  char* base = static_cast<char*>(ws);
+  bsa::BwdArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.dO = dO;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.qs = f.qs;
+  a.ks = f.ks;
+  a.vs = f.vs;
+  a.os = f.os;
+  a.lse = lse;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.delta = reinterpret_cast<float*>(base);
+  a.bits = reinterpret_cast<uint32_t*>(base + bw.delta);
+  a.items = reinterpret_cast<int4*>(base + bw.delta + bw.bits);
+  a.red = reinterpret_cast<int4*>(base + bw.delta + bw.bits + bw.items);
+  a.counters = reinterpret_cast<int*>(base + bw.delta + bw.bits + bw.items + bw.red);
+  a.part = reinterpret_cast<float*>(base + bw.delta + bw.bits + bw.items + bw.red + bw.counters);
+  a.batch = s->batch;
+  a.hq = s->n_q_heads;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.B = s->block;
+  a.k_max = k_max;
+  a.nrow = f.nrow;
+  a.nblk = f.nblk;
+  a.nwords = static_cast<int>(bw.nwords);
+  a.chunk = kBwdChunk;
+  a.max_items = static_cast<int>(bw.max_items);
+  a.max_red = static_cast<int>(bw.max_red);
+  a.n = s->q_len;
+  a.sm_scale = f.sm_scale;
+  a.bf16 = true;
+  a.o_f32 = o_dtype == BSA_F32;
+  a.g_f32 = g_dtype == BSA_F32;
+  static_assert(kBwdChunk <= 64, "chunk rows are staged in a 64-entry LDS list");
+  return device_status(bsa::launch_attend_backward(a, static_cast<hipStream_t>(stream)),
+                       "attend_backward");
 }
 
 int bsa_attend_entmax(const bsa_shape* s, const void* Q, const void* K, const void* V,

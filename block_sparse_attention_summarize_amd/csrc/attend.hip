@@ -24,6 +24,7 @@
 // Single-token decode lives in decode.hip.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "walk.hpp"
 
 namespace bsa {
 
@@ -34,38 +35,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-
-// Walk of the selected blocks as 64-key tiles: tile index T covers block
-// idx[T / nsub] (nsub = B/64 tiles per block) at offset (T % nsub) * 64.
-struct TileWalk {
-  const int32_t* list;
-  int n;       // number of list entries to use
-  int nsub;
-  int B;
-  int nblk;
-  int64_t kv_len;
-  int64_t qmax;  // last query position of the workgroup
-
-  // key0 of tile T, or -1 when the tile is invalid or entirely in the future.
-  __device__ __forceinline__ int64_t key0(int T) const { return key0_of(list[T / nsub], T); }
-  // the same with the list entry j = list[T / nsub] already read
-  __device__ __forceinline__ int64_t key0_of(int j, int T) const {
-    if (j < 0 || j >= nblk) return -1;
-    const int64_t k0 = static_cast<int64_t>(j) * B + (T % nsub) * 64;
-    if (k0 > qmax || k0 >= kv_len) return -1;
-    return k0;
-  }
-  __device__ __forceinline__ int next(int T) const {
-    for (++T; T < n * nsub; ++T)
-      if (key0(T) >= 0) return T;
-    return -1;
-  }
-};
 
 // Double-buffered K and V tiles, both row-major (64 keys x D).  Row padding
 // spreads each read instruction over all 64 banks: K fragments read 16 B from
@@ -78,40 +53,6 @@ struct PrefillLds {
   alignas(16) uint16_t k[2][64 * KST];
   alignas(16) uint16_t v[2][64 * VST];
 };
-
-// Map workgroup id -> (pair = b*hkv + g, query block i, sub-unit).  Heavy
-// query blocks (larger i select more blocks) go first, and when the
-// (batch, KV head) pairs divide evenly over the 8 XCDs (workgroups are
-// dispatched round-robin over them) every workgroup of a pair lands on the
-// same XCD, so the pair's K/V stays in one L2.
-__device__ __forceinline__ void map_wg(int id, int npair, int nrow, int wpb, int& pair, int& i,
-                                       int& sub) {
-  const int total = npair * nrow * wpb;
-  if (npair % 8 == 0 && total % 8 == 0) {
-    const int x = id % 8, s = id / 8;
-    const int per = (npair / 8) * wpb;
-    const int ir = s / per, rest = s % per;
-    pair = x + 8 * (rest / wpb);
-    sub = rest % wpb;
-    i = nrow - 1 - ir;
-    return;
-  }
-  if (8 % npair == 0 && nrow % (8 / npair) == 0) {
-    const int xpp = 8 / npair;
-    const int x = id % 8, s = id / 8;
-    pair = x % npair;
-    const int r = x / npair;
-    const int ir = (s / wpb) * xpp + r;
-    sub = s % wpb;
-    i = nrow - 1 - ir;
-    return;
-  }
-  const int ir = id / (npair * wpb);
-  const int rest = id % (npair * wpb);
-  pair = rest / wpb;
-  sub = rest % wpb;
-  i = nrow - 1 - ir;
-}
 
 constexpr float kRescale = 8.f;  // lazy rescale threshold, log2 units
 
@@ -457,6 +398,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const int64_t t = qpos0 + qt * 16 + (lane & 15);
     if (t >= a.q_len) continue;
+    // the normaliser in natural-log units (m and the scores are log2 units)
+    if (a.lse && lane < 16)
+      a.lse[(static_cast<int64_t>(b) * a.hq + h) * a.q_len + t] =
+          lt > 0.f ? (m[qt] + __log2f(lt)) * kLn2 : -INFINITY;
     const int64_t off = b * a.os.b + h * a.os.h + t * a.os.t;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -570,6 +515,9 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
     }
   }
   if (t >= a.q_len) return;
+  if (a.lse)
+    a.lse[(static_cast<int64_t>(b) * a.hq + h) * a.q_len + t] =
+        l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   float* Og = static_cast<float*>(a.O) + b * a.os.b + h * a.os.h + t * a.os.t;
 #pragma unroll

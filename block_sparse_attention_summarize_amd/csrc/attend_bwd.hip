@@ -1,0 +1,739 @@
+// Backward of Stage 2: gradients of the causal block-sparse attention for a
+// fixed selection ("AdaSplash-2", section 4: the backward pass dominates
+// training time and only the nonzero blocks are visited; "DashAttention",
+// Contribuições item 1: training through the sparse attention).
+//
+// With P the softmax weights recomputed from the forward's log-normaliser,
+// Delta_t = dO_t . O_t and dS = P (dP - Delta), dP = dO V^T:
+//   dQ = sm_scale dS K,  dK = sm_scale dS^T Q,  dV = P^T dO.
+//
+//   bwd_mark      bit r of word (r/32, j) of a KV head says that query block r
+//                 selected key block j: the selection transposed, written
+//                 whole (no atomics on global memory, nothing to clear).
+//   bwd_plan      one workgroup: per key block the number of selecting rows,
+//                 split into chunks of `chunk` rows; a flat list of work items
+//                 (key block, chunk) ordered by (batch, KV head) then block,
+//                 and the list of blocks whose chunks must be summed.  The
+//                 items running at a time then belong to one or two KV heads,
+//                 whose query and upstream-gradient rows (read once per
+//                 selecting block) stay in the memory-side cache; within a
+//                 head the blocks near the start, selected most, go first.
+//   bwd_dq        query side, the forward's walk: one workgroup per (batch,
+//                 KV head, query block, unit group) over the row's selected
+//                 key tiles staged in LDS.  S^T = K Q^T and dP^T = V dO^T on
+//                 bf16 MFMA, dS^T in fp32, dQ^T += K^T dS^T.  Also writes
+//                 Delta for the key side.
+//   bwd_dkv       key side: one workgroup per work item; each wave keeps 16
+//                 keys' K and V fragments in registers and the rows' Q / dO
+//                 tiles of every query head of the group stream through LDS.
+//                 S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS.
+//   bwd_reduce    blocks split into several chunks: the chunks' fp32 partials
+//                 summed in chunk order (deterministic), then stored.
+// Every gradient element is written exactly once; keys no query attends get 0.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "walk.hpp"
+
+namespace bsa {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxTilesBwd = 1024;  // tile-list chunk staged in LDS (query side)
+
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// A 64-row tile of D bf16 columns in LDS, rows padded by 16 elements: both
+// the row fragments (16 rows x one 16-byte chunk per lane group) and the
+// transposing reads (8 rows x 32 bytes per half-wave) then run without bank
+// conflicts (measured with the LDS bank-conflict counter on gfx950; an XOR
+// swizzle of the chunks conflicts on the row fragments).
+template <int D>
+struct Swz {
+  static constexpr int ST = D + 16;  // row stride, elements
+  // element offset of 16-byte chunk c of row r
+  __device__ static __forceinline__ int at(int r, int c) { return r * ST + (c << 3); }
+};
+
+// Transposed MFMA operand from a row-major tile: lane l gets column
+// 16 dt + l%16 of rows 32 kk + 4 (l/16) + e and 32 kk + 16 + 4 (l/16) + e,
+// e < 4 (the key order of a packed probability fragment).
+template <int D>
+__device__ __forceinline__ uint4 tr_frag(const uint16_t* tile, int kk, int dt, int lane) {
+  const int s16 = lane & 15;
+  const int r = kk * 32 + (lane >> 4) * 4 + (s16 >> 2);
+  const uint16_t* p = tile + Swz<D>::at(r, 2 * dt + ((s16 & 3) >> 1)) + 4 * (s16 & 1);
+  const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p));
+  const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(p + 16 * Swz<D>::ST));
+  const uint2 u0 = __builtin_bit_cast(uint2, r0), u1 = __builtin_bit_cast(uint2, r1);
+  return make_uint4(u0.x, u0.y, u1.x, u1.y);
+}
+
+// Row fragment: lane l gets row 16 rt + l%16, columns 32 ks + 8 (l/16) .. +7.
+template <int D>
+__device__ __forceinline__ uint4 row_frag(const uint16_t* tile, int rt, int ks, int lane) {
+  return *reinterpret_cast<const uint4*>(tile + Swz<D>::at(rt * 16 + (lane & 15), ks * 4 + (lane >> 4)));
+}
+
+// Four fp32 weights per lane of two 16-row accumulator tiles -> one bf16
+// operand fragment over 32 rows (rows 32kk + 4G + e, 32kk + 16 + 4G + e).
+__device__ __forceinline__ uint4 pack_frag(const f32x4& a, const f32x4& b) {
+  return make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                    pack_bf16x2(b[2], b[3]));
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48.
+__device__ __forceinline__ float xsum16(float v) { return swap32_sum(swap16_sum(v)); }
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix of v over the workgroup and its total.
+template <int NT>
+__device__ __forceinline__ int block_scan_int(int v, int* wave_tot, int& total) {
+  constexpr int NW = NT / kWave;
+  const int incl = wave_incl_scan(v);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == kWave - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    const int t = wave_tot[k];
+    off += k < w ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return off + incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Transposed selection and work plan
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_mark(BwdArgs a) {
+  extern __shared__ uint32_t words[];  // [nblk]
+  const int tid = threadIdx.x;
+  const int wd = blockIdx.x % a.nwords;
+  const int64_t pair = blockIdx.x / a.nwords;
+  for (int j = tid; j < a.nblk; j += 256) words[j] = 0u;
+  __syncthreads();
+  const int r0 = wd * 32;
+  const int nr = a.nrow - r0 < 32 ? a.nrow - r0 : 32;
+  for (int e = tid; e < nr * a.k_max; e += 256) {
+    const int rr = e / a.k_max, s = e - rr * a.k_max;
+    const int64_t row = pair * a.nrow + r0 + rr;
+    const int c = a.cnt[row];
+    if (s < (c > a.k_max ? a.k_max : c)) {
+      const int j = a.idx[row * a.k_max + s];
+      // block j is attended by row r only when it starts at or before the
+      // row's last query: j <= r (query and key blocks are both B long)
+      if (j >= 0 && j < a.nblk && j <= r0 + rr) atomicOr(&words[j], 1u << rr);
+    }
+  }
+  __syncthreads();
+  uint32_t* out = a.bits + (pair * a.nwords + wd) * a.nblk;
+  for (int j = tid; j < a.nblk; j += 256) out[j] = words[j];
+}
+
+__global__ __launch_bounds__(kPlanThreads) void bwd_plan(BwdArgs a) {
+  __shared__ int wave_tot[kPlanThreads / kWave];
+  const int tid = threadIdx.x;
+  const int npair = a.batch * a.hkv;
+  const int64_t total = static_cast<int64_t>(npair) * a.nblk;
+  int ibase = 0, sbase = 0, rbase = 0;
+  for (int64_t x0 = 0; x0 < total; x0 += kPlanThreads) {
+    const int64_t x = x0 + tid;
+    int p = 0, j = 0, nch = 0;
+    if (x < total) {
+      p = static_cast<int>(x / a.nblk);
+      j = static_cast<int>(x % a.nblk);
+      const uint32_t* col = a.bits + static_cast<int64_t>(p) * a.nwords * a.nblk + j;
+      int c = 0;
+      for (int w = 0; w < a.nwords; ++w) c += __popc(col[static_cast<int64_t>(w) * a.nblk]);
+      nch = c == 0 ? 1 : (c + a.chunk - 1) / a.chunk;  // an empty block still writes zeros
+    }
+    const bool multi = nch > 1;
+    int ti, ts, tr;
+    const int io = block_scan_int<kPlanThreads>(nch, wave_tot, ti);
+    const int so = block_scan_int<kPlanThreads>(multi ? nch : 0, wave_tot, ts);
+    const int ro = block_scan_int<kPlanThreads>(multi ? 1 : 0, wave_tot, tr);
+    for (int c = 0; c < nch; ++c)
+      a.items[ibase + io + c] = make_int4(p, j, c, multi ? sbase + so + c : -1);
+    if (multi) a.red[rbase + ro] = make_int4(p, j, sbase + so, nch);
+    ibase += ti;
+    sbase += ts;
+    rbase += tr;
+  }
+  if (tid == 0) {
+    a.counters[0] = ibase;
+    a.counters[1] = rbase;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query side: dQ (and Delta)
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqLds {
+  alignas(16) uint16_t k[2][64 * Swz<D>::ST];
+  alignas(16) uint16_t v[2][64 * Swz<D>::ST];
+};
+
+// QT query tiles of 16 per wavefront, NW wavefronts; a unit is one query head
+// x 16 QT queries of the query block, as in the forward kernel.
+template <int D, int QT, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
+  constexpr int NT = NW * 64;
+  constexpr int QPW = 16 * QT;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int KTOT = 64 * CPR;
+  constexpr int KITEMS = (KTOT + NT - 1) / NT;
+  __shared__ DqLds<D> lds;
+  __shared__ int lds_tiles[kMaxTilesBwd];
+  __shared__ int lds_ntiles;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int G = a.hq / a.hkv;
+  const int nsub = a.B / 64;
+  const int qsub = a.B / QPW;
+  const int units = G * qsub;
+  int pair, i, sub;
+  map_wg(blockIdx.x, a.batch * a.hkv, a.nrow, wpb, pair, i, sub);
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int u = sub * NW + w;
+  const bool active = u < units;
+  const int hh = active ? u % G : 0;
+  const int qs = active ? u / G : 0;
+  const int h = g * G + hh;
+  const int qpos0 = i * a.B + qs * QPW;
+  int qs_max = 0;
+  for (int uu = sub * NW; uu < sub * NW + NW && uu < units; ++uu) qs_max = max(qs_max, uu / G);
+  int64_t qmax = static_cast<int64_t>(i) * a.B + qs_max * QPW + QPW - 1;
+  if (qmax > a.n - 1) qmax = a.n - 1;
+
+  const int64_t rowid = static_cast<int64_t>(pair) * a.nrow + i;
+  int n = a.cnt[rowid];
+  n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
+  TileWalk walk{a.idx + rowid * a.k_max, n, nsub, a.B, a.nblk, a.n, qmax};
+
+  const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
+                            head_bytes(a.n, a.ks.t, D, 2));
+  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
+                            head_bytes(a.n, a.vs.t, D, 2));
+  const uint32_t kst = static_cast<uint32_t>(a.ks.t * 2), vst = static_cast<uint32_t>(a.vs.t * 2);
+
+  // Q and dO fragments (B operands): lane l holds query 16qt + l%16,
+  // d = 32ks + 8(l/16) .. +7; rows past n read as zero.
+  uint4 qf[QT][KS], df[QT][KS];
+  float dl[QT], lse2[QT];
+  {
+    const uint32_t qbytes = active ? head_bytes(a.n, a.qs.t, D, 2) : 0u;
+    const uint32_t obytes = active ? head_bytes(a.n, a.os.t, D, a.o_f32 ? 4 : 2) : 0u;
+    const auto rq = make_rsrc(static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h, qbytes);
+    const auto rdo = make_rsrc(static_cast<const uint16_t*>(a.dO) + b * a.os.b + h * a.os.h,
+                               active ? head_bytes(a.n, a.os.t, D, 2) : 0u);
+    const int oes = a.o_f32 ? 4 : 2;
+    const auto ro = make_rsrc(static_cast<const uint8_t*>(a.O) + (b * a.os.b + h * a.os.h) * oes,
+                              obytes);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int64_t t = qpos0 + qt * 16 + (lane & 15);
+      const uint32_t tq = static_cast<uint32_t>(t);
+      float part = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c0 = ks * 32 + (lane >> 4) * 8;
+        qf[qt][ks] = buf_load16(rq, tq * static_cast<uint32_t>(a.qs.t * 2) + c0 * 2);
+        df[qt][ks] = buf_load16(rdo, tq * static_cast<uint32_t>(a.os.t * 2) + c0 * 2);
+        float ov[8];
+        if (a.o_f32)
+          buf_load8_f32<float>(ro, tq * static_cast<uint32_t>(a.os.t * 4) + c0 * 4, ov);
+        else
+          buf_load8_f32<uint16_t>(ro, tq * static_cast<uint32_t>(a.os.t * 2) + c0 * 2, ov);
+        const uint4 dv = df[qt][ks];
+        part = fmaf(bf16_lo(dv.x), ov[0], part);
+        part = fmaf(bf16_hi(dv.x), ov[1], part);
+        part = fmaf(bf16_lo(dv.y), ov[2], part);
+        part = fmaf(bf16_hi(dv.y), ov[3], part);
+        part = fmaf(bf16_lo(dv.z), ov[4], part);
+        part = fmaf(bf16_hi(dv.z), ov[5], part);
+        part = fmaf(bf16_lo(dv.w), ov[6], part);
+        part = fmaf(bf16_hi(dv.w), ov[7], part);
+      }
+      dl[qt] = xsum16(part);
+      const int64_t hrow = (static_cast<int64_t>(b) * a.hq + h) * a.n;
+      float L = t < a.n ? a.lse[hrow + t] : -INFINITY;
+      // a query without weights (no key, or past the end) gets P = 0
+      lse2[qt] = L > -INFINITY ? L * kLog2e : INFINITY;
+      if (active && lane < 16 && t < a.n) a.delta[hrow + t] = dl[qt];
+    }
+  }
+
+  f32x4 acc[DT][QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float sc = a.sm_scale * kLog2e;
+
+  uint4 kreg[KITEMS], vreg[KITEMS];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < KITEMS; ++it) {
+      const int flat = tid + NT * it;
+      const int r = flat / CPR, c = flat % CPR;
+      if (KTOT % NT == 0 || flat < KTOT) {
+        kreg[it] = buf_load16(rk, static_cast<uint32_t>(k0 + r) * kst + c * 16);
+        vreg[it] = buf_load16(rv, static_cast<uint32_t>(k0 + r) * vst + c * 16);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < KITEMS; ++it) {
+      const int flat = tid + NT * it;
+      const int r = flat / CPR, c = flat % CPR;
+      if (KTOT % NT == 0 || flat < KTOT) {
+        *reinterpret_cast<uint4*>(&lds.k[buf][Swz<D>::at(r, c)]) = kreg[it];
+        *reinterpret_cast<uint4*>(&lds.v[buf][Swz<D>::at(r, c)]) = vreg[it];
+      }
+    }
+  };
+
+  const int nraw = n * nsub;
+  for (int base = 0; base < nraw; base += kMaxTilesBwd) {
+    if (w == 0) {
+      int c = 0;
+      for (int r = 0; r < kMaxTilesBwd && base + r < nraw; r += 64) {
+        const int T = base + r + lane;
+        const int64_t k0 = T >= nraw ? -1 : walk.key0(T);
+        const uint64_t mk = __ballot(k0 >= 0);
+        if (k0 >= 0) lds_tiles[c + lanes_below(mk)] = static_cast<int>(k0);
+        c += __popcll(mk);
+      }
+      if (lane == 0) lds_ntiles = c;
+    }
+    __syncthreads();
+    const int ntiles = lds_ntiles;
+    int buf = 0;
+    if (ntiles > 0) {
+      load_tile(lds_tiles[0]);
+      store_tile(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int k0 = lds_tiles[t];
+      const bool more = t + 1 < ntiles;
+      if (more) load_tile(lds_tiles[t + 1]);
+      // a wave whose queries all precede the tile has nothing to add
+      if (active && k0 <= qpos0 + QPW - 1) {
+        const uint16_t* kt_ = lds.k[buf];
+        const uint16_t* vt_ = lds.v[buf];
+        // S^T and dP^T, one 16-key slice at a time (lane l holds keys
+        // 16kt + 4(l/16) + j of query column 16qt + l%16), turned into dS^T
+        // and packed two slices per bf16 operand
+        const bool diag = k0 + 63 > qpos0;
+        const int rel0 = k0 - qpos0 + (lane >> 4) * 4 - (lane & 15);
+        uint4 dsf[QT][2];
+        f32x4 dsp[QT];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          f32x4 s[QT], dp[QT];
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            s[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const uint4 kf = row_frag<D>(kt_, kt, ks, lane);
+            const uint4 vf = row_frag<D>(vt_, kt, ks, lane);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+              s[qt] = mfma16(kf, qf[qt][ks], s[qt]);
+              dp[qt] = mfma16(vf, df[qt][ks], dp[qt]);
+            }
+          }
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            f32x4 ds;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float p = __builtin_amdgcn_exp2f(fmaf(s[qt][j], sc, -lse2[qt]));
+              if (diag && rel0 + kt * 16 + j - qt * 16 > 0) p = 0.f;  // key after query
+              ds[j] = p * (dp[qt][j] - dl[qt]);
+            }
+            if (kt & 1)
+              dsf[qt][kt >> 1] = pack_frag(dsp[qt], ds);
+            else
+              dsp[qt] = ds;
+          }
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint4 kf = tr_frag<D>(kt_, kk, dt, lane);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) acc[dt][qt] = mfma16(kf, dsf[qt][kk], acc[dt][qt]);
+          }
+      }
+      if (more) store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int64_t t = qpos0 + qt * 16 + (lane & 15);
+    if (t >= a.n) continue;
+    const int64_t off = b * a.qs.b + h * a.qs.h + t * a.qs.t;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d0 = dt * 16 + (lane >> 4) * 4;
+      const f32x4 v = acc[dt][qt] * a.sm_scale;
+      if (a.g_f32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.dQ) + off + d0) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dQ) + off + d0) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Key side: dK, dV
+// ---------------------------------------------------------------------------
+template <int D>
+struct DkvLds {
+  alignas(16) uint16_t q[2][64 * Swz<D>::ST];
+  alignas(16) uint16_t o[2][64 * Swz<D>::ST];  // dO
+  alignas(16) float lse2[2][64];
+  alignas(16) float dl[2][64];
+};
+constexpr int kMaxChunk = 64;
+
+// NW = B / 16 wavefronts, wave w owning keys 16w .. 16w+15 of the block.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int QTOT = 64 * CPR;
+  constexpr int QITEMS = (QTOT + NT - 1) / NT;
+  constexpr int B = NW * 16;
+  __shared__ DkvLds<D> lds;
+  __shared__ int rows[kMaxChunk];
+  __shared__ int lds_nr;
+
+  if (static_cast<int>(blockIdx.x) >= a.counters[0]) return;
+  const int4 item = a.items[blockIdx.x];
+  const int pair = item.x, j = item.y, chunk = item.z, slot = item.w;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int G = a.hq / a.hkv;
+
+  // rows of this chunk: ranks [chunk * a.chunk, +a.chunk) among the set bits
+  // of block j's column, ascending
+  if (w == 0) {
+    const int lo = chunk * a.chunk, hi = lo + a.chunk;
+    const uint32_t* col = a.bits + static_cast<int64_t>(pair) * a.nwords * a.nblk + j;
+    int base = 0;
+    for (int w0 = 0; w0 < a.nwords && base < hi; w0 += 64) {
+      const int wi = w0 + lane;
+      uint32_t word = wi < a.nwords ? col[static_cast<int64_t>(wi) * a.nblk] : 0u;
+      const int pc = __popc(word);
+      const int incl = wave_incl_scan(pc);
+      int rank = base + incl - pc;
+      while (word != 0u && rank < hi) {
+        const int bit = __builtin_ctz(word);
+        word &= word - 1u;
+        if (rank >= lo) rows[rank - lo] = wi * 32 + bit;
+        ++rank;
+      }
+      base += __shfl(incl, 63, kWave);
+    }
+    if (lane == 0) lds_nr = base <= lo ? 0 : (base < hi ? base : hi) - lo;
+  }
+
+  // K and V fragments of this wave's keys (B operands of S = Q K^T and
+  // dP = dO V^T): lane l holds key 16w + l%16, d = 32ks + 8(l/16) .. +7
+  const int64_t key0 = static_cast<int64_t>(j) * B + w * 16;
+  uint4 kf[KS], vf[KS];
+  {
+    const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
+                              head_bytes(a.n, a.ks.t, D, 2));
+    const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
+                              head_bytes(a.n, a.vs.t, D, 2));
+    const uint32_t t = static_cast<uint32_t>(key0 + (lane & 15));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = ks * 32 + (lane >> 4) * 8;
+      kf[ks] = buf_load16(rk, t * static_cast<uint32_t>(a.ks.t * 2) + c0 * 2);
+      vf[ks] = buf_load16(rv, t * static_cast<uint32_t>(a.vs.t * 2) + c0 * 2);
+    }
+  }
+  f32x4 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  const int nr = lds_nr;
+  const int qtiles = B / 64;              // 64-query tiles per query block
+  const int nunits = nr * G * qtiles;     // (row, head, query tile), row-major
+  const float sc = a.sm_scale * kLog2e;
+
+  uint4 qreg[QITEMS], oreg[QITEMS];
+  float lreg = 0.f, dreg = 0.f;
+  // unit u -> query head and first query position
+  auto unit_of = [&](int uu, int& h, int64_t& t0) {
+    const int qq = uu % qtiles;
+    const int rest = uu / qtiles;
+    h = g * G + rest % G;
+    t0 = static_cast<int64_t>(rows[rest / G]) * B + qq * 64;
+  };
+  auto load_unit = [&](int uu) {
+    int h;
+    int64_t t0;
+    unit_of(uu, h, t0);
+    const auto rq = make_rsrc(static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h,
+                              head_bytes(a.n, a.qs.t, D, 2));
+    const auto rdo = make_rsrc(static_cast<const uint16_t*>(a.dO) + b * a.os.b + h * a.os.h,
+                               head_bytes(a.n, a.os.t, D, 2));
+#pragma unroll
+    for (int it = 0; it < QITEMS; ++it) {
+      const int flat = tid + NT * it;
+      const int r = flat / CPR, c = flat % CPR;
+      if (QTOT % NT == 0 || flat < QTOT) {
+        const uint32_t t = static_cast<uint32_t>(t0 + r);
+        qreg[it] = buf_load16(rq, t * static_cast<uint32_t>(a.qs.t * 2) + c * 16);
+        oreg[it] = buf_load16(rdo, t * static_cast<uint32_t>(a.os.t * 2) + c * 16);
+      }
+    }
+    if (tid < 64) {
+      const int64_t t = t0 + tid;
+      const int64_t hrow = (static_cast<int64_t>(b) * a.hq + h) * a.n;
+      const float L = t < a.n ? a.lse[hrow + t] : -INFINITY;
+      lreg = L > -INFINITY ? L * kLog2e : INFINITY;
+      dreg = t < a.n ? a.delta[hrow + t] : 0.f;
+    }
+  };
+  auto store_unit = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < QITEMS; ++it) {
+      const int flat = tid + NT * it;
+      const int r = flat / CPR, c = flat % CPR;
+      if (QTOT % NT == 0 || flat < QTOT) {
+        *reinterpret_cast<uint4*>(&lds.q[buf][Swz<D>::at(r, c)]) = qreg[it];
+        *reinterpret_cast<uint4*>(&lds.o[buf][Swz<D>::at(r, c)]) = oreg[it];
+      }
+    }
+    if (tid < 64) {
+      lds.lse2[buf][tid] = lreg;
+      lds.dl[buf][tid] = dreg;
+    }
+  };
+
+  int buf = 0;
+  if (nunits > 0) {
+    load_unit(0);
+    store_unit(0);
+  }
+  __syncthreads();
+  for (int uu = 0; uu < nunits; ++uu) {
+    const bool more = uu + 1 < nunits;
+    if (more) load_unit(uu + 1);
+    int h;
+    int64_t t0;
+    unit_of(uu, h, t0);
+    (void)h;
+    // nothing to add when every key of the wave follows every query of the tile
+    if (key0 <= t0 + 63) {
+      const uint16_t* qt_ = lds.q[buf];
+      const uint16_t* ot_ = lds.o[buf];
+      // S and dP tiles: lane l holds queries 16qt + 4(l/16) + e of key 16w + l%16
+      f32x4 s[4], dp[4];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        s[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          s[qt] = mfma16(row_frag<D>(qt_, qt, ks, lane), kf[ks], s[qt]);
+          dp[qt] = mfma16(row_frag<D>(ot_, qt, ks, lane), vf[ks], dp[qt]);
+        }
+      const bool diag = key0 + 15 > t0;
+      const int64_t rel0 = key0 + (lane & 15) - t0 - (lane >> 4) * 4;  // key - query at qt = e = 0
+      f32x4 p[4], ds[4];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const float4 L = *reinterpret_cast<const float4*>(&lds.lse2[buf][qt * 16 + (lane >> 4) * 4]);
+        const float4 Dl = *reinterpret_cast<const float4*>(&lds.dl[buf][qt * 16 + (lane >> 4) * 4]);
+        const float Lv[4] = {L.x, L.y, L.z, L.w};
+        const float Dv[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[qt][e], sc, -Lv[e]));
+          if (diag && rel0 - qt * 16 - e > 0) pv = 0.f;  // key after query
+          p[qt][e] = pv;
+          ds[qt][e] = pv * (dp[qt][e] - Dv[e]);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint4 pf = pack_frag(p[2 * kk], p[2 * kk + 1]);
+        const uint4 sf = pack_frag(ds[2 * kk], ds[2 * kk + 1]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = mfma16(tr_frag<D>(ot_, kk, dt, lane), pf, dv[dt]);
+          dk[dt] = mfma16(tr_frag<D>(qt_, kk, dt, lane), sf, dk[dt]);
+        }
+      }
+    }
+    if (more) store_unit(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // lane l holds dK^T / dV^T rows d = 16dt + 4(l/16) + e of key 16w + l%16
+  const int64_t key = key0 + (lane & 15);
+  if (slot >= 0) {
+    float* pk = a.part + static_cast<int64_t>(slot) * 2 * B * D + (w * 16 + (lane & 15)) * D;
+    float* pv = pk + B * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d0 = dt * 16 + (lane >> 4) * 4;
+      *reinterpret_cast<float4*>(pk + d0) = make_float4(dk[dt][0], dk[dt][1], dk[dt][2], dk[dt][3]);
+      *reinterpret_cast<float4*>(pv + d0) = make_float4(dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]);
+    }
+    return;
+  }
+  if (key >= a.n) return;
+  const int64_t ok = b * a.ks.b + g * a.ks.h + key * a.ks.t;
+  const int64_t ov = b * a.vs.b + g * a.vs.h + key * a.vs.t;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int d0 = dt * 16 + (lane >> 4) * 4;
+    const f32x4 k4 = dk[dt] * a.sm_scale;
+    const f32x4 v4 = dv[dt];
+    if (a.g_f32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.dK) + ok + d0) = make_float4(k4[0], k4[1], k4[2], k4[3]);
+      *reinterpret_cast<float4*>(static_cast<float*>(a.dV) + ov + d0) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+    } else {
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dK) + ok + d0) =
+          make_uint2(pack_bf16x2(k4[0], k4[1]), pack_bf16x2(k4[2], k4[3]));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dV) + ov + d0) =
+          make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+    }
+  }
+}
+
+// Sum of the chunk partials of a split block, in chunk order; kRedSlices
+// workgroups share each block.
+constexpr int kRedSlices = 16;
+__global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
+  const int item = blockIdx.x / kRedSlices, slice = blockIdx.x % kRedSlices;
+  if (item >= a.counters[1]) return;
+  const int4 r = a.red[item];
+  const int pair = r.x, j = r.y, s0 = r.z, ns = r.w;
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int64_t bd = static_cast<int64_t>(a.B) * a.d;
+  const int64_t per = 2 * bd / kRedSlices;  // a multiple of 4 (B * d >= 4096)
+  for (int64_t e = slice * per + threadIdx.x * 4; e < (slice + 1) * per; e += 256 * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < ns; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(a.part + (s0 + s) * 2 * bd + e);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const bool isv = e >= bd;
+    const int64_t rem = isv ? e - bd : e;
+    const int64_t key = static_cast<int64_t>(j) * a.B + rem / a.d;
+    const int c = static_cast<int>(rem % a.d);
+    if (key >= a.n) continue;
+    if (!isv) {
+      acc.x *= a.sm_scale;
+      acc.y *= a.sm_scale;
+      acc.z *= a.sm_scale;
+      acc.w *= a.sm_scale;
+    }
+    const int64_t off = isv ? b * a.vs.b + g * a.vs.h + key * a.vs.t + c
+                            : b * a.ks.b + g * a.ks.h + key * a.ks.t + c;
+    void* dst = isv ? a.dV : a.dK;
+    if (a.g_f32)
+      *reinterpret_cast<float4*>(static_cast<float*>(dst) + off) = acc;
+    else
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + off) =
+          make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+  }
+}
+
+template <int D>
+hipError_t bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  const int npair = a.batch * a.hkv;
+  constexpr int QT = 2, NW = 4;
+  const int G = a.hq / a.hkv;
+  const int units = G * (a.B / (16 * QT));
+  const int wpb = (units + NW - 1) / NW;
+  hipLaunchKernelGGL((bwd_dq<D, QT, NW>), dim3(static_cast<unsigned>(npair) * a.nrow * wpb),
+                     dim3(NW * 64), 0, stream, a, wpb);
+  if (a.B == 64)
+    hipLaunchKernelGGL((bwd_dkv<D, 4>), dim3(a.max_items), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_dkv<D, 8>), dim3(a.max_items), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int attend_bwd_max_chunk() { return kMaxChunk; }
+
+hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream) {
+  const unsigned npair = static_cast<unsigned>(a.batch) * a.hkv;
+  hipLaunchKernelGGL(bwd_mark, dim3(npair * a.nwords), dim3(256), a.nblk * sizeof(uint32_t), stream, a);
+  hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (!a.bf16) return hipErrorInvalidValue;  // fp32 path not built
+  e = a.d == 64 ? bwd_bf16<64>(a, stream) : bwd_bf16<128>(a, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_reduce, dim3(a.max_red * kRedSlices), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -114,12 +114,47 @@ struct AttendArgs {
   const float* wsel;
   const float* tbias;
   float sigma;
+  // optional [batch, hq, q_len]: ln of the softmax normaliser of every query,
+  // ln sum_u exp(sm_scale q.k_u + bias_u) over its attended keys (-inf: none)
+  float* lse;
   int batch, hq, hkv, d, B, k_max, nrow, nblk;
   int64_t q_len, kv_len;
   float sm_scale;
   bool bf16, out_f32;
 };
 hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream);
+
+// Gradients of the causal block-sparse prefill attention (block rows, bf16,
+// q_len == kv_len == n) for a fixed selection idx/cnt [batch, hkv, nrow, k_max].
+// dQ, dK, dV are written with the strides of Q, K, V (elements of the
+// gradient dtype); dO has the strides of O.
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  void* dQ;
+  void* dK;
+  void* dV;
+  Strides3 qs, ks, vs, os;
+  const float* lse;  // [batch, hq, n] from the forward
+  const int32_t* idx;
+  const int32_t* cnt;
+  // workspace
+  float* delta;      // [batch, hq, n]: dO . O
+  uint32_t* bits;    // [batch * hkv, nwords, nblk]: bit r % 32 of word r / 32 = row r selected block j
+  int4* items;       // [max_items] (pair, block, chunk, partial slot or -1)
+  int4* red;         // [max_red] (pair, block, first slot, chunks)
+  int* counters;     // [2]: items, red
+  float* part;       // [slots, 2, B, d]: dK then dV partials of split blocks
+  int batch, hq, hkv, d, B, k_max, nrow, nblk, nwords, chunk, max_items, max_red;
+  int64_t n;
+  float sm_scale;
+  bool bf16, o_f32, g_f32;
+};
+int attend_bwd_max_chunk();
+hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream);
 
 // Active blocks of every 64-query tile from per-token selections
 // idx/cnt [batch, hkv, q_len, width]: uidx/ucnt the ascending union over the

@@ -22,6 +22,8 @@
  *                               query token per sequence ("DashAttention",
  *                               Contribuições item 4: prefill and incremental
  *                               decode).
+ *            bsa_attend_backward  gradients of the prefill attention for a
+ *                               fixed selection, zero blocks skipped.
  *            bsa_token_mask     per-token selections (BSA_TOKEN) as active-block
  *                               masks of 64-query tiles.
  *            bsa_attend_entmax  token-level alpha-entmax attention
@@ -100,7 +102,8 @@ typedef enum {
   BSA_OP_ATTEND_PREFILL = 3,
   BSA_OP_ATTEND_DECODE = 4,
   BSA_OP_DECODE_TOPK = 5,
-  BSA_OP_ATTEND_PREFILL_PRIOR = 6 /* bsa_attend_prefill with wsel != NULL */
+  BSA_OP_ATTEND_PREFILL_PRIOR = 6, /* bsa_attend_prefill with wsel != NULL */
+  BSA_OP_ATTEND_BACKWARD = 7       /* bsa_attend_backward; k_or_cap = k_max */
 } bsa_op;
 
 /* Problem description, read only during the call. */
@@ -262,12 +265,53 @@ int bsa_route_entmax(const bsa_shape *shape, const void *Q, const float *S,
  *   bias; 256-byte aligned, scratch afterwards), then attends tile by tile
  *   over the active blocks, masking each query's scores on blocks its token
  *   did not select.  In prefill mode ws is unused.
+ *   lse   NULL, or out fp32 [batch, Hq, q_len] contiguous: for every query the
+ *         natural log of its softmax normaliser, ln sum exp(logit) over the
+ *         keys it attends (logits with the prior bias when wsel is given);
+ *         -inf for a query that attends nothing.  bsa_attend_backward reads it.
  * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
  */
 int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                        const int32_t *idx, const int32_t *cnt, int32_t k_max, float sm_scale,
-                       const float *wsel, float sigma, void *O, int32_t o_dtype, void *ws,
-                       size_t ws_bytes, void *stream);
+                       const float *wsel, float sigma, void *O, int32_t o_dtype, float *lse,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of Stage 2, causal prefill with block rows and no prior: the
+ * gradients of bsa_attend_prefill's output for a fixed selection (the
+ * selection itself gets none).  The pages single out the backward pass as
+ * where training time goes and skip its zero blocks ("AdaSplash-2", section
+ * 4); training the sparse attention end to end is "DashAttention",
+ * Contribuições item 1.  For query t of head h with weights P_tu over its
+ * attended keys u (recomputed from lse) and upstream gradient dO_t:
+ *   Delta_t = dO_t . O_t,  dS_tu = P_tu (dO_t . v_u - Delta_t),
+ *   dQ_t = sm_scale sum_u dS_tu k_u,
+ *   dK_u = sm_scale sum_t dS_tu q_t,  dV_u = sum_t P_tu dO_t,
+ * the key sums running over every query head of the KV group.  Only the
+ * (query block, selected block) pairs are visited: once from the query side
+ * for dQ, once from the key side for dK and dV (rows that selected a block
+ * are gathered from a transposed copy of the selection; blocks selected by
+ * many rows are split over several workgroups and their parts summed in a
+ * fixed order, so results are deterministic).
+ *   Q, K, V, idx, cnt, k_max, sm_scale  as given to bsa_attend_prefill
+ *         (bf16 only; the entries of a row must be distinct, as the routing
+ *         calls produce them).
+ *   O     the forward output, o_dtype (bf16 or BSA_F32), with o_stride.
+ *   dO    bf16 [batch, Hq, q_len, d] with o_stride.
+ *   lse   fp32 [batch, Hq, q_len] written by bsa_attend_prefill.
+ *   dQ, dK, dV  out, g_dtype (bf16 or BSA_F32), with the strides of Q, K, V;
+ *         every element is written (0 for keys no query attends).
+ *   ws    bsa_workspace_size(BSA_OP_ATTEND_BACKWARD, shape, k_max) bytes,
+ *         256-byte aligned; scratch afterwards.
+ * Errors: BSA_ERR_INVALID (mode other than BSA_PREFILL, null pointers),
+ * BSA_ERR_UNSUPPORTED (fp32 inputs, more than 16384 blocks, strides,
+ * alignment), BSA_ERR_WORKSPACE.
+ */
+int bsa_attend_backward(const bsa_shape *shape, const void *Q, const void *K, const void *V,
+                        const void *O, int32_t o_dtype, const void *dO, const float *lse,
+                        const int32_t *idx, const int32_t *cnt, int32_t k_max, float sm_scale,
+                        void *dQ, void *dK, void *dV, int32_t g_dtype, void *ws,
+                        size_t ws_bytes, void *stream);
 
 /*
  * Token-level alpha-entmax attention, causal prefill ("AdaSplash-2", sections

@@ -65,7 +65,7 @@ def _load():
                                    P, I, P, P, P, D]
         lib.orc_token_union.argtypes = [P, P, I, I, I, I, I, P, P, P]
         lib.orc_entmax_attend.argtypes = [P, P, P, I, I, I, I, I, D, D, P, I, P, P, P]
-        lib.orc_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, I, D, P, P, P]
+        lib.orc_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, I, D, P, P, P, P]
         lib.orc_version.restype = ctypes.c_char_p
         _lib = lib
     return _lib
@@ -246,9 +246,10 @@ def entmax_attend(Q, K, V, alpha, req=None, sm_scale=None):
     return O, tau, sup
 
 
-def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None):
+def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None, rowmask=None):
     """Gradients (dQ, dK, dV) in fp64 of the causal block-sparse attention
-    (prefill rows, selection idx/cnt per query block) for upstream dO."""
+    (prefill rows, selection idx/cnt per query block) for upstream dO.
+    rowmask [nb, hkv, nrow] (bool): only those query blocks contribute."""
     Q, K, V, dO = _f32(Q), _f32(K), _f32(V), _f32(dO)
     nb, hq, n, d = Q.shape
     hkv = K.shape[1]
@@ -259,9 +260,12 @@ def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None):
     dQ = np.empty(Q.shape, np.float64)
     dK = np.empty(K.shape, np.float64)
     dV = np.empty(V.shape, np.float64)
+    if rowmask is not None:
+        rowmask = np.ascontiguousarray(rowmask, dtype=np.uint8)
+        assert rowmask.shape == cnt.shape
     _load().orc_attend_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), nb, hq, hkv, n, d, B,
-                                _ptr(idx), _ptr(cnt), idx.shape[-1], float(sm_scale), _ptr(dQ),
-                                _ptr(dK), _ptr(dV))
+                                _ptr(idx), _ptr(cnt), idx.shape[-1], float(sm_scale),
+                                _ptr(rowmask), _ptr(dQ), _ptr(dK), _ptr(dV))
     return dQ, dK, dV
 
 

@@ -805,11 +805,15 @@ void orc_entmax_attend(const float *Q, const float *K, const float *V, int64_t n
  *   group's query heads add into the same dK, dV).
  *   Q, dO : [nb, hq, n, d];  K, V : [nb, hkv, n, d] (fp32); idx/cnt per query
  *   block.  dQ [nb, hq, n, d], dK, dV [nb, hkv, n, d]: fp64, overwritten.
+ *   rowmask: NULL, or [nb, hkv, nrow] bytes; then only the queries of the
+ *   query blocks whose byte is nonzero contribute (a sample: dQ of those
+ *   queries, and dK, dV of every key block all of whose selecting rows are
+ *   in it, are exact).
  */
 void orc_attend_backward(const float *Q, const float *K, const float *V, const float *dO,
                          int64_t nb, int64_t hq, int64_t hkv, int64_t n, int64_t d, int64_t B,
                          const int32_t *idx, const int32_t *cnt, int64_t kmax, double sm_scale,
-                         double *dQ, double *dK, double *dV) {
+                         const uint8_t *rowmask, double *dQ, double *dK, double *dV) {
   int64_t G = hq / hkv;
   int64_t nrow = (n + B - 1) / B;
   int64_t cap = kmax * B + 1;
@@ -823,6 +827,7 @@ void orc_attend_backward(const float *Q, const float *K, const float *V, const f
       for (int64_t t = 0; t < n; ++t) {
         int64_t g = h / G;
         int64_t rowid = (b * hkv + g) * nrow + t / B;
+        if (rowmask && !rowmask[rowid]) continue;
         const float *qv = Q + ((b * hq + h) * n + t) * d;
         const float *gv = dO + ((b * hq + h) * n + t) * d;
         const float *kb = K + ((b * hkv + g) * n) * d;

@@ -9,7 +9,8 @@ method's arithmetic.  Recipe (stated once here, used everywhere):
   s, b, h, c])).standard_normal((rows, d), dtype=float32)``, so any slice can be
   regenerated without drawing the whole tensor; streams: q=0, k=1, v=2, u=3,
   planted key blocks=4, planted query positions=5, query-tile components=6,
-  key-tile components=7;
+  key-tile components=7, upstream gradients dO of the attention output=8
+  (shaped like q, plain N(0, 1), nothing added);
 * planting (the long-context retrieval structure): a unit vector
   u = g/|g|, g ~ N(0, I_d) (stream 3, fp64), a set of planted key blocks drawn
   without replacement (stream 4, identical for every KV head) whose keys get
@@ -37,8 +38,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 CHUNK = 4096
-STREAM_Q, STREAM_K, STREAM_V, STREAM_U, STREAM_PK, STREAM_PQ, STREAM_QL, STREAM_KL = \
-    0, 1, 2, 3, 4, 5, 6, 7
+STREAM_Q, STREAM_K, STREAM_V, STREAM_U, STREAM_PK, STREAM_PQ, STREAM_QL, STREAM_KL, STREAM_DO = \
+    0, 1, 2, 3, 4, 5, 6, 7, 8
 QTILE = 64  # query tokens sharing one locality component
 
 FORCE_DIAG = 1
@@ -201,10 +202,13 @@ def _threads() -> int:
 
 
 def gen(w: Workload, name: str, heads=None, t0: int = 0, t1=None, batches=None):
-    """Draw tensor `name` in {"q","k","v"} as fp32 [len(batches), len(heads), t1-t0, d],
-    with planting applied.  Defaults: every batch, head and row."""
+    """Draw tensor `name` in {"q","k","v","do"} as fp32 [len(batches), len(heads), t1-t0, d],
+    with planting applied ("do": the upstream gradient of the output, shaped
+    like q).  Defaults: every batch, head and row."""
     if name == "q":
         nh, rows, stream = w.hq, w.q_len, STREAM_Q
+    elif name == "do":
+        nh, rows, stream = w.hq, w.q_len, STREAM_DO
     elif name in ("k", "v"):
         nh, rows, stream = w.hkv, w.n, STREAM_K if name == "k" else STREAM_V
     else:

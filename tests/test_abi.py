@@ -60,8 +60,8 @@ def entmax(s, alpha=1.5, n_bins=16, max_iter=8, cap=64, force=1):
 
 def prefill(s, k_max=4, o_dtype=None, Q=FAKE, O=FAKE, sm_scale=0.0, wsel=None, sigma=0.0):
     return lib.bsa_attend_prefill(ctypes.byref(s), Q, FAKE, FAKE, FAKE, FAKE, k_max, sm_scale,
-                                  wsel, sigma, O, s.dtype if o_dtype is None else o_dtype, None, 0,
-                                  None)
+                                  wsel, sigma, O, s.dtype if o_dtype is None else o_dtype, None,
+                                  None, 0, None)
 
 
 def test_shape_validation():
@@ -192,14 +192,14 @@ def test_token_mode_validation_and_workspace():
     assert topk(shape(mode=bsa.TOKEN, q_len=128)) == -1 and "q_len == kv_len" in err()
     # the tile masks need their workspace
     assert lib.bsa_attend_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.0, None,
-                                  0.0, FAKE, bsa.BF16, ctypes.c_void_p(0x200000), need - 1,
-                                  None) == -4
+                                  0.0, FAKE, bsa.BF16, None, ctypes.c_void_p(0x200000),
+                                  need - 1, None) == -4
     # with routing weights the tiles' per-query bias is added
     prior = lib.bsa_workspace_size(bsa.OP_ATTEND_PREFILL_PRIOR, ctypes.byref(s), 4)
     assert prior == need + al(trows * nblk * 64 * 4)
     assert lib.bsa_attend_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 4, 0.0, FAKE,
-                                  1.0, FAKE, bsa.BF16, ctypes.c_void_p(0x200000), prior - 1,
-                                  None) == -4
+                                  1.0, FAKE, bsa.BF16, None, ctypes.c_void_p(0x200000),
+                                  prior - 1, None) == -4
     mask = lambda sh, idx=FAKE, width=4: lib.bsa_token_mask(ctypes.byref(sh), idx, FAKE, width,
                                                              FAKE, FAKE, FAKE, None)
     assert mask(shape()) == -1 and "BSA_TOKEN" in err()
@@ -236,3 +236,40 @@ def test_paged_validation():
     pg.table = tbl
     assert lib.bsa_summarize_blocks_paged(ctypes.byref(s), ctypes.byref(pg), FAKE, None, None,
                                           FAKE, None) == -1 and "blk" in err()
+
+
+def backward(s, k_max=4, o_dtype=None, g_dtype=None, lse=FAKE, dO=FAKE, ws_bytes=None,
+             sm_scale=0.0):
+    n = (lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD, ctypes.byref(s), k_max)
+         if ws_bytes is None else ws_bytes)
+    return lib.bsa_attend_backward(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE,
+                                   s.dtype if o_dtype is None else o_dtype, dO, lse, FAKE, FAKE,
+                                   k_max, sm_scale, FAKE, FAKE, FAKE,
+                                   s.dtype if g_dtype is None else g_dtype,
+                                   ctypes.c_void_p(0x200000), n, None)
+
+
+def test_backward_validation_and_workspace():
+    s = shape(q_len=64 * 10 + 5, kv_len=64 * 10 + 5)  # 11 query and key blocks
+    need = lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD, ctypes.byref(s), 4)
+    al = lambda x: (x + 255) // 256 * 256
+    nrow = nblk = 11
+    per = 4 * 5 // 2 + (nrow - 4) * 4  # (row, block <= row) pairs of one KV head, k = 4
+    E = 2 * per
+    items = 2 * nblk + -(-E // 32)
+    red = min(2 * nblk, E // 33 + 1)
+    slots = E // 32 + red + 1
+    assert need == (al(4 * 645 * 4) + al(2 * 1 * nblk * 4) + al(items * 16) + al(red * 16) + al(8)
+                    + al(slots * 2 * 64 * 128 * 4))
+    assert backward(s, ws_bytes=need - 1) == -4
+    assert backward(shape(mode=bsa.TOKEN)) == -1 and "BSA_PREFILL" in err()
+    assert backward(shape(dtype=bsa.F32)) == -2 and "bf16" in err()
+    assert backward(s, lse=None) == -1 and "lse" in err()
+    assert backward(s, dO=None) == -1 and "dO" in err()
+    assert backward(s, g_dtype=7) == -2 and "g_dtype" in err()
+    assert backward(s, sm_scale=-1.0) == -1
+    assert backward(s, lse=ctypes.c_void_p(0x100002)) == -2 and "aligned" in err()
+    # more key blocks than the marking kernel holds in LDS
+    big = shape(q_len=64 * 16385, kv_len=64 * 16385, hq=2, hkv=1)
+    assert backward(big, ws_bytes=0) == -2 and "16384" in err()
+    assert lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD, ctypes.byref(shape(mode=bsa.TOKEN)), 4) == 0

@@ -290,6 +290,6 @@ def test_token_mode_argument_errors():
     import ctypes
     rc = bsa.lib.bsa_attend_prefill(ctypes.byref(shape), bsa._ptr(x["Q"]), bsa._ptr(x["K"]),
                                     bsa._ptr(x["V"]), bsa._ptr(idx), bsa._ptr(cnt), w.k_total,
-                                    0.0, None, 0.0, bsa._ptr(O), bsa.BF16, bsa._ptr(small),
-                                    need // 2, None)
+                                    0.0, None, 0.0, bsa._ptr(O), bsa.BF16, None,
+                                    bsa._ptr(small), need // 2, None)
     assert rc == -4  # BSA_ERR_WORKSPACE, nothing enqueued

@@ -132,3 +132,28 @@ def test_backward_of_zero_upstream_is_zero_and_rows_without_blocks_contribute_no
     r = oracle.attend_backward(Q, K, V, dO2, 8, idx, cnt2)
     np.testing.assert_array_equal(r[1], dK)
     np.testing.assert_array_equal(r[2], dV)
+
+
+def test_backward_row_sample_is_the_restriction_of_the_full_gradient():
+    """Gradients are sums over queries: the sample of a set of query blocks
+    plus the sample of the rest is the full gradient, a sampled query's dQ is
+    its full dQ, and a key block whose selecting rows are all sampled gets its
+    full dK, dV."""
+    Q, K, V, dO, idx, cnt = _case(5400, n=48, B=8)
+    full = oracle.attend_backward(Q, K, V, dO, 8, idx, cnt)
+    mask = np.zeros(cnt.shape, bool)
+    mask[0, 0, [1, 4]] = True
+    mask[0, 1, 5] = True
+    a = oracle.attend_backward(Q, K, V, dO, 8, idx, cnt, rowmask=mask)
+    b = oracle.attend_backward(Q, K, V, dO, 8, idx, cnt, rowmask=~mask)
+    for f, x, y in zip(full, a, b):
+        np.testing.assert_allclose(x + y, f, rtol=0, atol=1e-12)
+    G = Q.shape[1] // K.shape[1]
+    for g, r in ((0, 1), (0, 4), (1, 5)):
+        for h in range(g * G, (g + 1) * G):
+            np.testing.assert_array_equal(a[0][0, h, 8 * r:8 * r + 8], full[0][0, h, 8 * r:8 * r + 8])
+    # the last block of KV head 1 is selected only by its own row (5)
+    sel = [r for r in range(6) if 5 in idx[0, 1, r, :cnt[0, 1, r]]]
+    assert sel == [5]
+    np.testing.assert_allclose(a[1][0, 1, 40:48], full[1][0, 1, 40:48], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(a[2][0, 1, 40:48], full[2][0, 1, 40:48], rtol=0, atol=1e-13)
