@@ -65,7 +65,11 @@ def _load():
                                    P, I, P, P, P, D]
         lib.orc_token_union.argtypes = [P, P, I, I, I, I, I, P, P, P]
         lib.orc_entmax_attend.argtypes = [P, P, P, I, I, I, I, I, D, D, P, I, P, P, P]
-        lib.orc_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, I, D, P, P, P, P]
+        lib.orc_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, I, D, P, P, D, P,
+                                            P, P, P]
+        lib.orc_entmax_vjp.argtypes = [P, P, I, D, P]
+        lib.orc_route_entmax_backward.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, D, D, D,
+                                                  ctypes.c_uint32, P, P]
         lib.orc_version.restype = ctypes.c_char_p
         _lib = lib
     return _lib
@@ -246,10 +250,13 @@ def entmax_attend(Q, K, V, alpha, req=None, sm_scale=None):
     return O, tau, sup
 
 
-def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None, rowmask=None):
+def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None, rowmask=None, wsel=None,
+                    sigma=0.0):
     """Gradients (dQ, dK, dV) in fp64 of the causal block-sparse attention
     (prefill rows, selection idx/cnt per query block) for upstream dO.
-    rowmask [nb, hkv, nrow] (bool): only those query blocks contribute."""
+    rowmask [nb, hkv, nrow] (bool): only those query blocks contribute.
+    wsel, sigma: the prior-induced softmax; then (dQ, dK, dV, dwsel) with
+    dwsel = dL/dw in the layout of idx."""
     Q, K, V, dO = _f32(Q), _f32(K), _f32(V), _f32(dO)
     nb, hq, n, d = Q.shape
     hkv = K.shape[1]
@@ -263,10 +270,46 @@ def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None, rowmask=None):
     if rowmask is not None:
         rowmask = np.ascontiguousarray(rowmask, dtype=np.uint8)
         assert rowmask.shape == cnt.shape
+    dwsel = None
+    if wsel is not None:
+        wsel = np.ascontiguousarray(wsel, dtype=np.float64)
+        assert wsel.shape == idx.shape
+        dwsel = np.empty(idx.shape, np.float64)
     _load().orc_attend_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), nb, hq, hkv, n, d, B,
                                 _ptr(idx), _ptr(cnt), idx.shape[-1], float(sm_scale),
-                                _ptr(rowmask), _ptr(dQ), _ptr(dK), _ptr(dV))
-    return dQ, dK, dV
+                                _ptr(rowmask), _ptr(wsel), float(sigma), _ptr(dwsel), _ptr(dQ),
+                                _ptr(dK), _ptr(dV))
+    return (dQ, dK, dV) if wsel is None else (dQ, dK, dV, dwsel)
+
+
+def entmax_vjp(p, dp, alpha):
+    """dL/dz of alpha-entmax at probabilities p (logits z, x = (alpha-1) z)
+    for dL/dp = dp."""
+    p = _f64(p)
+    dp = _f64(dp)
+    dz = np.empty_like(p)
+    _load().orc_entmax_vjp(_ptr(p), _ptr(dp), p.size, float(alpha), _ptr(dz))
+    return dz
+
+
+def route_entmax_backward(qhat, S, probs, idx, cnt, dwsel, n, B, alpha, gamma,
+                          score_scale=None, force=FORCE_DIAG):
+    """Routing part of the gradient (prefill block rows): dL/dQ and dL/dK in
+    fp64 through qhat -> logits -> entmax -> group mean w, given dL/dw."""
+    qhat, S, probs, dwsel = _f64(qhat), _f64(S), _f64(probs), _f64(dwsel)
+    nb, hq, nrow, d = qhat.shape
+    hkv = S.shape[1]
+    if score_scale is None:
+        score_scale = 1.0 / np.sqrt(d)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    cnt = np.ascontiguousarray(cnt, dtype=np.int32)
+    dQ = np.empty((nb, hq, n, d), np.float64)
+    dK = np.empty((nb, hkv, n, d), np.float64)
+    _load().orc_route_entmax_backward(_ptr(qhat), _ptr(S), _ptr(probs), _ptr(idx), _ptr(cnt),
+                                      idx.shape[-1], _ptr(dwsel), nb, hq, hkv, n, d, B,
+                                      float(alpha), float(gamma), float(score_scale), force,
+                                      _ptr(dQ), _ptr(dK))
+    return dQ, dK
 
 
 def version() -> str:

@@ -809,19 +809,28 @@ void orc_entmax_attend(const float *Q, const float *K, const float *V, int64_t n
  *   query blocks whose byte is nonzero contribute (a sample: dQ of those
  *   queries, and dK, dV of every key block all of whose selecting rows are
  *   in it, are exact).
+ *   wsel, sigma: the prior-induced softmax of orc_attend (NULL: none); the
+ *   logit of a key of listed block j gains sigma ln w_j, entries with
+ *   w_j <= 0 are skipped.  dwsel (NULL, or [nb, hkv, nrow, kmax]) receives
+ *   dL/dw_j = sigma / w_j * sum of dS over the entry's (query, key) pairs of
+ *   every head of the group (0 for skipped entries).
  */
 void orc_attend_backward(const float *Q, const float *K, const float *V, const float *dO,
                          int64_t nb, int64_t hq, int64_t hkv, int64_t n, int64_t d, int64_t B,
                          const int32_t *idx, const int32_t *cnt, int64_t kmax, double sm_scale,
-                         const uint8_t *rowmask, double *dQ, double *dK, double *dV) {
+                         const uint8_t *rowmask, const double *wsel, double sigma, double *dwsel,
+                         double *dQ, double *dK, double *dV) {
   int64_t G = hq / hkv;
   int64_t nrow = (n + B - 1) / B;
   int64_t cap = kmax * B + 1;
   double *p = (double *)malloc(sizeof(double) * (size_t)cap);
   int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+  int64_t *ent = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
   double *o = (double *)malloc(sizeof(double) * (size_t)d);
   for (int64_t a = 0; a < nb * hq * n * d; ++a) dQ[a] = 0.0;
   for (int64_t a = 0; a < nb * hkv * n * d; ++a) dK[a] = dV[a] = 0.0;
+  if (dwsel)
+    for (int64_t a = 0; a < nb * hkv * nrow * kmax; ++a) dwsel[a] = 0.0;
   for (int64_t b = 0; b < nb; ++b)
     for (int64_t h = 0; h < hq; ++h)
       for (int64_t t = 0; t < n; ++t) {
@@ -838,7 +847,11 @@ void orc_attend_backward(const float *Q, const float *K, const float *V, const f
         int64_t nt = 0;
         for (int64_t s = 0; s < cnt[rowid]; ++s) {
           int64_t j = idx[rowid * kmax + s];
-          for (int64_t u = j * B; u < (j + 1) * B && u < n && u <= t; ++u) tok[nt++] = u;
+          if (wsel && !(wsel[rowid * kmax + s] > 0.0)) continue;
+          for (int64_t u = j * B; u < (j + 1) * B && u < n && u <= t; ++u) {
+            ent[nt] = s;
+            tok[nt++] = u;
+          }
         }
         if (nt == 0) continue;
         double mx = -INFINITY, z = 0.0;
@@ -846,6 +859,7 @@ void orc_attend_backward(const float *Q, const float *K, const float *V, const f
           double acc = 0.0;
           for (int64_t c = 0; c < d; ++c) acc += (double)qv[c] * (double)kb[tok[a] * d + c];
           p[a] = acc * sm_scale;
+          if (wsel) p[a] += sigma * log(wsel[rowid * kmax + ent[a]]);
           if (p[a] > mx) mx = p[a];
         }
         for (int64_t a = 0; a < nt; ++a) {
@@ -865,6 +879,7 @@ void orc_attend_backward(const float *Q, const float *K, const float *V, const f
           double dp = 0.0;
           for (int64_t c = 0; c < d; ++c) dp += (double)gv[c] * (double)vv[c];
           double ds = p[a] * (dp - D);
+          if (dwsel) dwsel[rowid * kmax + ent[a]] += ds;
           for (int64_t c = 0; c < d; ++c) {
             dq[c] += sm_scale * ds * (double)kv[c];
             dkb[tok[a] * d + c] += sm_scale * ds * (double)qv[c];
@@ -872,7 +887,127 @@ void orc_attend_backward(const float *Q, const float *K, const float *V, const f
           }
         }
       }
+  if (dwsel)
+    for (int64_t a = 0; a < nb * hkv * nrow * kmax; ++a)
+      dwsel[a] = (wsel && wsel[a] > 0.0) ? dwsel[a] * sigma / wsel[a] : 0.0;
   free(p);
   free(tok);
+  free(ent);
   free(o);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward of the entmax routing (the routing weights' gradient reaching the */
+/* routing query and the summaries).                                         */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Vector-Jacobian product of alpha-entmax written in its logits z
+ * (p_j = [(alpha-1) z_j - tau]_+^(1/(alpha-1)), sum p = 1): differentiating
+ * the constraint gives dp_j = g_j (dz_j - <g, dz> / sum g) with
+ * g_j = p_j^(2-alpha) on the support and 0 off it, so the gradient of a loss
+ * with dL/dp = dp is dz_j = g_j (dp_j - <g, dp> / sum g).  ("DashAttention",
+ * Estágio 1: entmax routing is differentiable, unlike top-k.)
+ */
+void orc_entmax_vjp(const double *p, const double *dp, int64_t n, double alpha, double *dz) {
+  double sg = 0.0, sgd = 0.0;
+  for (int64_t a = 0; a < n; ++a)
+    if (p[a] > 0.0) {
+      double g = pow(p[a], 2.0 - alpha);
+      sg += g;
+      sgd += g * dp[a];
+    }
+  for (int64_t a = 0; a < n; ++a)
+    dz[a] = (p[a] > 0.0 && sg > 0.0) ? pow(p[a], 2.0 - alpha) * (dp[a] - sgd / sg) : 0.0;
+}
+
+/*
+ * Gradient of the loss through the entmax routing of prefill block rows
+ * (orc_route_entmax, mode prefill) given dL/dw for the listed blocks
+ * (dwsel, layout of idx; from orc_attend_backward).  The listed routed
+ * (not forced) block j of row r has w_j = (1/G) sum_h p_hj, so head h's
+ * probabilities get dp_hj = dw_j / G (0 for blocks not listed, e.g. cut by
+ * the cap); entmax's VJP gives dz over the head's candidates; the logits
+ * z_hj = gamma * score_scale * qhat_h . S_j give
+ *   dqhat_h += gamma * score_scale * sum_j dz_hj S_j,
+ *   dS_j   += gamma * score_scale * sum_{h in group, r} dz_hj qhat_h,
+ * and the mean pools (qhat = mean of the row's queries, S = mean of the
+ * block's keys, q-bar = 0) spread them evenly: dQ_t = dqhat_row(t) / n_row,
+ * dK_u = dS_block(u) / n_block (n = the block's token count).
+ *   qhat [nb, hq, nrow, d], S [nb, hkv, nblk, d], probs [nb, hq, nrow, nblk]
+ *   (fp64, from orc_qpool / orc_summarize / orc_route_entmax);
+ *   dQ [nb, hq, n, d], dK [nb, hkv, n, d]: fp64, overwritten with the
+ *   routing part only.
+ */
+void orc_route_entmax_backward(const double *qhat, const double *S, const double *probs,
+                               const int32_t *idx, const int32_t *cnt, int64_t idx_width,
+                               const double *dwsel, int64_t nb, int64_t hq, int64_t hkv,
+                               int64_t n, int64_t d, int64_t B, double alpha, double gamma,
+                               double score_scale, uint32_t force, double *dQ, double *dK) {
+  int64_t G = hq / hkv;
+  int64_t nrow = (n + B - 1) / B, nblk = nrow;
+  double *dp = (double *)malloc(sizeof(double) * (size_t)nblk);
+  double *pc = (double *)malloc(sizeof(double) * (size_t)nblk);
+  double *dz = (double *)malloc(sizeof(double) * (size_t)nblk);
+  int64_t *cj = (int64_t *)malloc(sizeof(int64_t) * (size_t)nblk);
+  double *dqh = (double *)calloc((size_t)(nb * hq * nrow * d), sizeof(double));
+  double *dS = (double *)calloc((size_t)(nb * hkv * nblk * d), sizeof(double));
+  double f = gamma * score_scale;
+  for (int64_t b = 0; b < nb; ++b)
+    for (int64_t h = 0; h < hq; ++h)
+      for (int64_t r = 0; r < nrow; ++r) {
+        int64_t g = h / G;
+        int64_t forced[3];
+        int nforced = 0;
+        int64_t cend = row_setup(ORC_MODE_PREFILL, 1, r, 0, B, force, forced, &nforced);
+        int64_t rowid = (b * hkv + g) * nrow + r, hrow = (b * hq + h) * nrow + r;
+        for (int64_t j = 0; j < nblk; ++j) dp[j] = 0.0;
+        for (int64_t a = 0; a < cnt[rowid]; ++a) {
+          int64_t j = idx[rowid * idx_width + a];
+          if (j >= 0 && j < nblk && !is_forced(j, forced, nforced))
+            dp[j] += dwsel[rowid * idx_width + a] / (double)G;
+        }
+        /* the head's candidates, as routed */
+        int64_t nc = 0;
+        for (int64_t j = 0; j < cend; ++j)
+          if (!is_forced(j, forced, nforced)) cj[nc++] = j;
+        double *dpl = (double *)malloc(sizeof(double) * (size_t)(nc + 1));
+        for (int64_t a = 0; a < nc; ++a) {
+          pc[a] = probs[hrow * nblk + cj[a]];
+          dpl[a] = dp[cj[a]];
+        }
+        orc_entmax_vjp(pc, dpl, nc, alpha, dz);
+        free(dpl);
+        const double *qv = qhat + hrow * d;
+        double *dq = dqh + hrow * d;
+        for (int64_t a = 0; a < nc; ++a) {
+          if (dz[a] == 0.0) continue;
+          const double *sv = S + ((b * hkv + g) * nblk + cj[a]) * d;
+          double *ds = dS + ((b * hkv + g) * nblk + cj[a]) * d;
+          for (int64_t c = 0; c < d; ++c) {
+            dq[c] += f * dz[a] * sv[c];
+            ds[c] += f * dz[a] * qv[c];
+          }
+        }
+      }
+  for (int64_t b = 0; b < nb; ++b) {
+    for (int64_t h = 0; h < hq; ++h)
+      for (int64_t t = 0; t < n; ++t) {
+        int64_t r = t / B, nr = (r + 1) * B < n ? B : n - r * B;
+        for (int64_t c = 0; c < d; ++c)
+          dQ[((b * hq + h) * n + t) * d + c] = dqh[((b * hq + h) * nrow + r) * d + c] / (double)nr;
+      }
+    for (int64_t g = 0; g < hkv; ++g)
+      for (int64_t u = 0; u < n; ++u) {
+        int64_t j = u / B, nj = (j + 1) * B < n ? B : n - j * B;
+        for (int64_t c = 0; c < d; ++c)
+          dK[((b * hkv + g) * n + u) * d + c] = dS[((b * hkv + g) * nblk + j) * d + c] / (double)nj;
+      }
+  }
+  free(dp);
+  free(pc);
+  free(dz);
+  free(cj);
+  free(dqh);
+  free(dS);
 }
