@@ -37,14 +37,15 @@ F32, BF16 = 0, 1
 PREFILL, DECODE, TOKEN = 0, 1, 2
 FORCE_DIAG, FORCE_FIRST, FORCE_TAIL = 1, 2, 4
 OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE, \
-    OP_DECODE_TOPK, OP_ATTEND_PREFILL_PRIOR, OP_ATTEND_BACKWARD = range(8)
+    OP_DECODE_TOPK, OP_ATTEND_PREFILL_PRIOR, OP_ATTEND_BACKWARD, OP_ROUTE_ENTMAX_BACKWARD = range(9)
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
 EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_summarize_blocks_paged",
            "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill", "bsa_token_mask",
            "bsa_attend_decode", "bsa_decode_topk", "bsa_decode_topk_paged", "bsa_attend_entmax",
-           "bsa_attend_backward", "bsa_workspace_size", "bsa_last_error", "bsa_version")
+           "bsa_attend_backward", "bsa_route_entmax_backward", "bsa_workspace_size",
+           "bsa_last_error", "bsa_version")
 
 
 class Shape(ctypes.Structure):
@@ -81,8 +82,10 @@ lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, 
                                  _P, _P, _P, _P, _P, _sz, _P]
 lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32, _P, _i32, _P, _P,
                                    _sz, _P]
-lib.bsa_attend_backward.argtypes = [_SP, _P, _P, _P, _P, _i32, _P, _P, _P, _P, _i32, _f32, _P, _P,
-                                    _P, _i32, _P, _sz, _P]
+lib.bsa_attend_backward.argtypes = [_SP, _P, _P, _P, _P, _i32, _P, _P, _P, _P, _i32, _f32, _P, _f32,
+                                    _P, _P, _P, _P, _i32, _P, _sz, _P]
+lib.bsa_route_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _P, _f32, _f32, _f32, _P,
+                                          _P, _i32, _P, _sz, _P]
 lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
 lib.bsa_attend_entmax.argtypes = [_SP, _P, _P, _P, _f32, _i32, _f32, _P, _i32, _P, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
@@ -91,7 +94,7 @@ lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32,
 for _f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_summarize_blocks_paged,
            lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill, lib.bsa_token_mask,
            lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged,
-           lib.bsa_attend_entmax, lib.bsa_attend_backward):
+           lib.bsa_attend_entmax, lib.bsa_attend_backward, lib.bsa_route_entmax_backward):
     _f.restype = ctypes.c_int
 lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
 lib.bsa_workspace_size.restype = _sz
@@ -285,10 +288,12 @@ def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None,
     return (O, L) if want_lse else O
 
 
-def attend_backward(Q, K, V, O, dO, lse, B, idx, cnt, sm_scale=0.0, grad_dtype=None, ws=None):
+def attend_backward(Q, K, V, O, dO, lse, B, idx, cnt, sm_scale=0.0, grad_dtype=None, ws=None,
+                    wsel=None, sigma=0.0, want_dwsel=False):
     """Gradients (dQ, dK, dV) of attend_prefill's output (block rows, bf16)
     for upstream gradient dO, given the forward's O and lse.  The gradients
-    take the strides of Q, K, V; dO is brought to O's strides and Q's dtype."""
+    take the strides of Q, K, V; dO is brought to O's strides and Q's dtype.
+    wsel, sigma: the forward's prior; want_dwsel: also return dL/dw."""
     b, hq, n, d = Q.shape
     gdt = grad_dtype or Q.dtype
     dQ = torch.empty_strided(Q.size(), Q.stride(), dtype=gdt, device=Q.device)
@@ -301,11 +306,32 @@ def attend_backward(Q, K, V, O, dO, lse, B, idx, cnt, sm_scale=0.0, grad_dtype=N
     shape = make_shape(batch=b, hq=hq, hkv=K.shape[1], d=d, B=B, dtype=_dtype_code(Q),
                        mode=PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=O)
     wsb, nws = _workspace(OP_ATTEND_BACKWARD, shape, idx.shape[-1], Q.device, ws)
+    dw = torch.empty(idx.shape, dtype=torch.float32, device=Q.device) if want_dwsel else None
+    if wsel is not None:
+        assert wsel.shape == idx.shape and wsel.dtype == torch.float32 and wsel.is_contiguous()
     _check(lib.bsa_attend_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(O),
                                    _dtype_code(O), _ptr(dO), _ptr(lse), _ptr(idx), _ptr(cnt),
-                                   idx.shape[-1], sm_scale, _ptr(dQ), _ptr(dK), _ptr(dV),
-                                   _dtype_code(dQ), _ptr(wsb), nws, _stream(Q)))
-    return dQ, dK, dV
+                                   idx.shape[-1], sm_scale, _ptr(wsel), sigma, _ptr(dw), _ptr(dQ),
+                                   _ptr(dK), _ptr(dV), _dtype_code(dQ), _ptr(wsb), nws,
+                                   _stream(Q)))
+    return (dQ, dK, dV, dw) if want_dwsel else (dQ, dK, dV)
+
+
+def route_entmax_backward(Q, S, probs, idx, cnt, dwsel, B, alpha, gamma, dQ, dK,
+                          score_scale=0.0, ws=None):
+    """Adds the gradient through the entmax routing weights (prefill block
+    rows) to dQ and dK in place: dwsel from attend_backward, probs the
+    routing's probs_out, S the summaries it scored.  Returns (dQ, dK)."""
+    b, hq, n, d = Q.shape
+    assert dQ.stride() == Q.stride() and dQ.dtype == dK.dtype
+    shape = make_shape(batch=b, hq=hq, hkv=S.shape[1], d=d, B=B, dtype=_dtype_code(Q),
+                       mode=PREFILL, q_len=n, kv_len=n, q=Q, k=dK, v=dK, o=Q)
+    wsb, nws = _workspace(OP_ROUTE_ENTMAX_BACKWARD, shape, 0, Q.device, ws)
+    _check(lib.bsa_route_entmax_backward(ctypes.byref(shape), _ptr(Q), _ptr(S), _ptr(probs),
+                                         _ptr(idx), _ptr(cnt), idx.shape[-1], _ptr(dwsel), alpha,
+                                         gamma, score_scale, _ptr(dQ), _ptr(dK),
+                                         _dtype_code(dQ), _ptr(wsb), nws, _stream(Q)))
+    return dQ, dK
 
 
 class _SparseAttention(torch.autograd.Function):

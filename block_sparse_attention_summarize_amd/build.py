@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "pool.hip", "route.hip", "attend.hip", "decode.hip", "mask.hip",
-           "entmax_attn.hip", "attend_bwd.hip"]
+           "entmax_attn.hip", "attend_bwd.hip", "route_bwd.hip"]
 # The attention kernels mask with -inf and never produce NaN on finite
 # inputs; without NaNs to honour, fmaxf lowers to bare v_max/v_max3 instead
 # of first quieting every MFMA result (one extra VALU op per input).

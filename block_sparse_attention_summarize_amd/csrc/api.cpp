@@ -215,7 +215,7 @@ MaskWs mask_ws(const bsa_shape* s, bool prior) {
 constexpr int kBwdChunk = 32;                  // query blocks per key-side work item
 constexpr int64_t kMaxBwdBlocks = 16384;       // one LDS word per key block when marking
 struct BwdWs {
-  size_t delta, bits, items, red, counters, part, total;
+  size_t delta, bits, items, red, counters, part, dbpart, total;
   int64_t max_items, max_red, slots, nwords;
 };
 BwdWs bwd_ws(const bsa_shape* s, int32_t k_max) {
@@ -236,7 +236,23 @@ BwdWs bwd_ws(const bsa_shape* s, int32_t k_max) {
   w.red = align_up(static_cast<size_t>(w.max_red) * 16);
   w.counters = align_up(8);
   w.part = align_up(static_cast<size_t>(w.slots) * 2 * s->block * s->head_dim * 4);
-  w.total = w.delta + w.bits + w.items + w.red + w.counters + w.part;
+  // per-unit sums of dS for dL/dw (the prior's gradient)
+  w.dbpart = align_up(static_cast<size_t>(npair * nrow) *
+                      bsa::attend_bwd_units(s->n_q_heads / s->n_kv_heads, s->block) *
+                      std::max<int32_t>(k_max, 1) * 4);
+  w.total = w.delta + w.bits + w.items + w.red + w.counters + w.part + w.dbpart;
+  return w;
+}
+// Routing backward: the routing queries and dL/d(logit) of every head-row.
+struct RouteBwdWs {
+  size_t qhat, dz, total;
+};
+RouteBwdWs route_bwd_ws(const bsa_shape* s) {
+  const size_t rows = static_cast<size_t>(s->batch) * s->n_q_heads * nrow_of(s);
+  RouteBwdWs w{};
+  w.qhat = align_up(rows * s->head_dim * 4);
+  w.dz = align_up(rows * nblk_of(s) * 4);
+  w.total = w.qhat + w.dz;
   return w;
 }
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -372,6 +388,8 @@ size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
       return s->mode == BSA_TOKEN ? mask_ws(s, true).total : 0;
     case BSA_OP_ATTEND_BACKWARD:
       return s->mode == BSA_PREFILL && k_or_cap >= 1 ? bwd_ws(s, k_or_cap).total : 0;
+    case BSA_OP_ROUTE_ENTMAX_BACKWARD:
+      return s->mode == BSA_PREFILL ? route_bwd_ws(s).total : 0;
     default:
       return 0;
   }
@@ -793,8 +811,8 @@ static int decode_topk_impl(const bsa_shape* s, const bsa_pages* pg, const void*
 int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const void* V,
                         const void* O, int32_t o_dtype, const void* dO, const float* lse,
                         const int32_t* idx, const int32_t* cnt, int32_t k_max, float sm_scale,
-                        void* dQ, void* dK, void* dV, int32_t g_dtype, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        const float* wsel, float sigma, float* dwsel, void* dQ, void* dK,
+                        void* dV, int32_t g_dtype, void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
   if (s->mode != BSA_PREFILL) return fail(BSA_ERR_INVALID, "bsa_attend_backward needs BSA_PREFILL");
@@ -813,6 +831,14 @@ int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const 
     return fail(BSA_ERR_UNSUPPORTED, "lse must be 4-byte aligned");
   if (g_dtype != s->dtype && g_dtype != BSA_F32)
     return fail(BSA_ERR_UNSUPPORTED, "g_dtype must be the input dtype or BSA_F32");
+  if (!std::isfinite(sigma)) return fail(BSA_ERR_INVALID, "sigma must be finite");
+  if (dwsel && !wsel) return fail(BSA_ERR_INVALID, "dwsel needs wsel");
+  if ((wsel && (reinterpret_cast<uintptr_t>(wsel) & 3u) != 0) ||
+      (dwsel && (reinterpret_cast<uintptr_t>(dwsel) & 3u) != 0))
+    return fail(BSA_ERR_UNSUPPORTED, "wsel and dwsel must be 4-byte aligned");
+  if (dwsel && k_max > bsa::attend_bwd_max_prior_width())
+    return fail(BSA_ERR_UNSUPPORTED, "dwsel supports k_max <= %d",
+                bsa::attend_bwd_max_prior_width());
   if ((rc = check_strides("dO", s->o_stride, s->dtype)) != BSA_OK) return rc;
   if ((rc = check_strides("dQ/dK/dV", s->q_stride, g_dtype)) != BSA_OK) return rc;
   const int64_t gsz = elem_bytes(g_dtype), osz = elem_bytes(o_dtype);
@@ -850,6 +876,13 @@ int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const 
   a.red = reinterpret_cast<int4*>(base + bw.delta + bw.bits + bw.items);
   a.counters = reinterpret_cast<int*>(base + bw.delta + bw.bits + bw.items + bw.red);
   a.part = reinterpret_cast<float*>(base + bw.delta + bw.bits + bw.items + bw.red + bw.counters);
+  a.wsel = wsel;
+  a.sigma = wsel ? sigma : 0.f;
+  a.dwsel = dwsel;
+  a.dbpart = dwsel ? reinterpret_cast<float*>(base + bw.delta + bw.bits + bw.items + bw.red +
+                                              bw.counters + bw.part)
+                   : nullptr;
+  a.units = bsa::attend_bwd_units(s->n_q_heads / s->n_kv_heads, s->block);
   a.batch = s->batch;
   a.hq = s->n_q_heads;
   a.hkv = s->n_kv_heads;
@@ -870,6 +903,77 @@ int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const 
   static_assert(kBwdChunk <= 64, "chunk rows are staged in a 64-entry LDS list");
   return device_status(bsa::launch_attend_backward(a, static_cast<hipStream_t>(stream)),
                        "attend_backward");
+}
+
+int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
+                              const float* probs, const int32_t* idx, const int32_t* cnt,
+                              int32_t width, const float* dwsel, float alpha, float gamma,
+                              float score_scale, void* dQ, void* dK, int32_t g_dtype, void* ws,
+                              size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if (s->mode != BSA_PREFILL)
+    return fail(BSA_ERR_INVALID, "bsa_route_entmax_backward needs BSA_PREFILL");
+  if ((rc = check_ptr("Q", Q)) != BSA_OK) return rc;
+  if ((rc = check_ptr("S", S)) != BSA_OK) return rc;
+  if ((rc = check_ptr("probs", probs)) != BSA_OK) return rc;
+  if ((rc = check_ptr("dQ", dQ)) != BSA_OK) return rc;
+  if ((rc = check_ptr("dK", dK)) != BSA_OK) return rc;
+  if (!idx || !cnt || !dwsel) return fail(BSA_ERR_INVALID, "idx, cnt and dwsel must not be NULL");
+  if (width < 1) return fail(BSA_ERR_INVALID, "width must be >= 1");
+  if (!(alpha > 1.f) || !std::isfinite(alpha)) return fail(BSA_ERR_INVALID, "alpha must be > 1");
+  if (!std::isfinite(gamma) || !std::isfinite(score_scale) || score_scale < 0.f)
+    return fail(BSA_ERR_INVALID, "gamma must be finite and score_scale finite and >= 0");
+  if (g_dtype != s->dtype && g_dtype != BSA_F32)
+    return fail(BSA_ERR_UNSUPPORTED, "g_dtype must be the input dtype or BSA_F32");
+  if ((rc = check_strides("Q", s->q_stride, s->dtype)) != BSA_OK) return rc;
+  if ((rc = check_strides("dQ/dK", s->q_stride, g_dtype)) != BSA_OK) return rc;
+  if ((rc = check_strides("dK", s->k_stride, g_dtype)) != BSA_OK) return rc;
+  const RouteBwdWs w = route_bwd_ws(s);
+  if ((rc = check_ws(ws, ws_bytes, w.total)) != BSA_OK) return rc;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  bsa::QPoolArgs qa{};
+  qa.Q = Q;
+  qa.qs = st3(s->q_stride);
+  qa.qhat = reinterpret_cast<float*>(base);
+  qa.batch = s->batch;
+  qa.hq = s->n_q_heads;
+  qa.hkv = s->n_kv_heads;
+  qa.d = s->head_dim;
+  qa.B = s->block;
+  qa.nrow = static_cast<int>(nrow_of(s));
+  qa.q_len = s->q_len;
+  qa.bf16 = s->dtype == BSA_BF16;
+  qa.group_sum = false;
+  hipError_t e = bsa::launch_qpool(qa, st);
+  if (e != hipSuccess) return device_status(e, "route_entmax_backward/qpool");
+  bsa::RouteBwdArgs a{};
+  a.qhat = qa.qhat;
+  a.S = S;
+  a.probs = probs;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.dwsel = dwsel;
+  a.dz = reinterpret_cast<float*>(base + w.qhat);
+  a.dQ = dQ;
+  a.dK = dK;
+  a.qs = st3(s->q_stride);
+  a.ks = st3(s->k_stride);
+  a.batch = s->batch;
+  a.hq = s->n_q_heads;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.B = s->block;
+  a.nrow = qa.nrow;
+  a.nblk = static_cast<int>(nblk_of(s));
+  a.width = width;
+  a.n = s->q_len;
+  a.alpha = alpha;
+  a.fscale = gamma * (score_scale != 0.f ? score_scale
+                                          : 1.f / std::sqrt(static_cast<float>(s->head_dim)));
+  a.g_f32 = g_dtype == BSA_F32;
+  return device_status(bsa::launch_route_entmax_backward(a, st), "route_entmax_backward");
 }
 
 int bsa_attend_entmax(const bsa_shape* s, const void* Q, const void* K, const void* V,

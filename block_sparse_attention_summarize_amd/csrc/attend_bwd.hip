@@ -45,7 +45,8 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPlanThreads = 1024;
-constexpr int kMaxTilesBwd = 1024;  // tile-list chunk staged in LDS (query side)
+constexpr int kMaxTilesBwd = 256;  // tile-list chunk staged in LDS (query side)
+constexpr int kMaxPriorEntries = 80;  // list width with a prior (per-wave sums in LDS)
 
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(256) void bwd_mark(BwdArgs a) {
       const int j = a.idx[row * a.k_max + s];
       // block j is attended by row r only when it starts at or before the
       // row's last query: j <= r (query and key blocks are both B long)
-      if (j >= 0 && j < a.nblk && j <= r0 + rr) atomicOr(&words[j], 1u << rr);
+      const bool live = !a.wsel || a.wsel[row * a.k_max + s] > 0.f;  // the prior drops w <= 0
+      if (j >= 0 && j < a.nblk && j <= r0 + rr && live) atomicOr(&words[j], 1u << rr);
     }
   }
   __syncthreads();
@@ -209,6 +211,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   constexpr int KITEMS = (KTOT + NT - 1) / NT;
   __shared__ DqLds<D> lds;
   __shared__ int lds_tiles[kMaxTilesBwd];
+  __shared__ int lds_tent[kMaxTilesBwd];    // list entry of each tile
+  __shared__ float lds_tbias[kMaxTilesBwd];  // prior bias of its block, score units
+  __shared__ float lds_db[NW][kMaxPriorEntries];  // per wave: dL/d(bias) per list entry
   __shared__ int lds_ntiles;
 
   const int tid = threadIdx.x;
@@ -321,15 +326,31 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
     }
   };
 
+  if (a.dbpart)
+    for (int e = lane; e < a.k_max; e += 64) lds_db[w][e] = 0.f;
   const int nraw = n * nsub;
   for (int base = 0; base < nraw; base += kMaxTilesBwd) {
     if (w == 0) {
       int c = 0;
       for (int r = 0; r < kMaxTilesBwd && base + r < nraw; r += 64) {
         const int T = base + r + lane;
-        const int64_t k0 = T >= nraw ? -1 : walk.key0(T);
+        int64_t k0 = T >= nraw ? -1 : walk.key0(T);
+        float tb = 0.f;
+        if (a.wsel && k0 >= 0) {
+          // the prior: sigma ln w of the tile's block, dropped when w <= 0
+          const float wv = a.wsel[rowid * a.k_max + T / nsub];
+          if (wv > 0.f)
+            tb = a.sigma * __logf(wv) / a.sm_scale;
+          else
+            k0 = -1;
+        }
         const uint64_t mk = __ballot(k0 >= 0);
-        if (k0 >= 0) lds_tiles[c + lanes_below(mk)] = static_cast<int>(k0);
+        if (k0 >= 0) {
+          const int pos = c + lanes_below(mk);
+          lds_tiles[pos] = static_cast<int>(k0);
+          lds_tent[pos] = T / nsub;
+          lds_tbias[pos] = tb;
+        }
         c += __popcll(mk);
       }
       if (lane == 0) lds_ntiles = c;
@@ -350,6 +371,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
       if (active && k0 <= qpos0 + QPW - 1) {
         const uint16_t* kt_ = lds.k[buf];
         const uint16_t* vt_ = lds.v[buf];
+        // exponent offset per query column: the block's bias minus lse
+        float eoff[QT];
+        const float tbs = lds_tbias[t] * sc;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) eoff[qt] = tbs - lse2[qt];
+        float dbs = 0.f;  // this wave's sum of dS over the tile (prior gradient)
         // S^T and dP^T, one 16-key slice at a time (lane l holds keys
         // 16kt + 4(l/16) + j of query column 16qt + l%16), turned into dS^T
         // and packed two slices per bf16 operand
@@ -380,9 +407,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
             f32x4 ds;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              float p = __builtin_amdgcn_exp2f(fmaf(s[qt][j], sc, -lse2[qt]));
+              float p = __builtin_amdgcn_exp2f(fmaf(s[qt][j], sc, eoff[qt]));
               if (diag && rel0 + kt * 16 + j - qt * 16 > 0) p = 0.f;  // key after query
               ds[j] = p * (dp[qt][j] - dl[qt]);
+              dbs += ds[j];
             }
             if (kt & 1)
               dsf[qt][kt >> 1] = pack_frag(dsp[qt], ds);
@@ -399,6 +427,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) acc[dt][qt] = mfma16(kf, dsf[qt][kk], acc[dt][qt]);
           }
+        if (a.dbpart) {
+          // this unit's part of dL/d(bias) of the tile's list entry (a block
+          // of two tiles adds twice)
+          dbs = wave_sum(dbs);
+          if (lane == 0) lds_db[w][lds_tent[t]] += dbs;
+        }
       }
       if (more) store_tile(buf ^ 1);
       __syncthreads();
@@ -407,6 +441,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   }
 
   if (!active) return;
+  if (a.dbpart)
+    for (int e = lane; e < a.k_max; e += 64)
+      a.dbpart[(rowid * a.units + u) * a.k_max + e] = lds_db[w][e];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     const int64_t t = qpos0 + qt * 16 + (lane & 15);
@@ -450,6 +487,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   constexpr int B = NW * 16;
   __shared__ DkvLds<D> lds;
   __shared__ int rows[kMaxChunk];
+  __shared__ float rbias[kMaxChunk];  // prior bias of block j in each row, score units
   __shared__ int lds_nr;
 
   if (static_cast<int>(blockIdx.x) >= a.counters[0]) return;
@@ -509,6 +547,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   }
   __syncthreads();
   const int nr = lds_nr;
+  if (a.wsel) {
+    // the routing weight of block j in each row's list: 8 threads per row
+    // scan the entries (a row lists j once; rows only hold j when w > 0)
+    for (int i = tid / 8; i < nr; i += NT / 8) {
+      const int64_t row = static_cast<int64_t>(pair) * a.nrow + rows[i];
+      const int c = min(a.cnt[row], a.k_max);
+      for (int e = tid % 8; e < c; e += 8)
+        if (a.idx[row * a.k_max + e] == j)
+          rbias[i] = a.sigma * __logf(a.wsel[row * a.k_max + e]) / a.sm_scale;
+    }
+  }
+  __syncthreads();
   const int qtiles = B / 64;              // 64-query tiles per query block
   const int nunits = nr * G * qtiles;     // (row, head, query tile), row-major
   const float sc = a.sm_scale * kLog2e;
@@ -597,6 +647,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
         }
       const bool diag = key0 + 15 > t0;
       const int64_t rel0 = key0 + (lane & 15) - t0 - (lane >> 4) * 4;  // key - query at qt = e = 0
+      const float tbs = a.wsel ? rbias[uu / qtiles / G] * sc : 0.f;  // the row's prior bias
       f32x4 p[4], ds[4];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
@@ -606,7 +657,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
         const float Dv[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[qt][e], sc, -Lv[e]));
+          float pv = __builtin_amdgcn_exp2f(fmaf(s[qt][e], sc, tbs - Lv[e]));
           if (diag && rel0 - qt * 16 - e > 0) pv = 0.f;  // key after query
           p[qt][e] = pv;
           ds[qt][e] = pv * (dp[qt][e] - Dv[e]);
@@ -703,6 +754,18 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
   }
 }
 
+// dL/dw of every list entry: sigma / w times the units' sums of dS.
+__global__ __launch_bounds__(64) void bwd_dwsel(BwdArgs a) {
+  const int64_t rowid = blockIdx.x;
+  const int c = a.cnt[rowid];
+  for (int e = threadIdx.x; e < a.k_max; e += 64) {
+    float acc = 0.f;
+    for (int u = 0; u < a.units; ++u) acc += a.dbpart[(rowid * a.units + u) * a.k_max + e];
+    const float wv = a.wsel[rowid * a.k_max + e];
+    a.dwsel[rowid * a.k_max + e] = e < c && wv > 0.f ? a.sigma / wv * acc : 0.f;
+  }
+}
+
 template <int D>
 hipError_t bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   const int npair = a.batch * a.hkv;
@@ -721,7 +784,8 @@ hipError_t bwd_bf16(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int attend_bwd_max_chunk() { return kMaxChunk; }
+int attend_bwd_units(int group, int B) { return group * (B / 32); }
+int attend_bwd_max_prior_width() { return kMaxPriorEntries; }
 
 hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream) {
   const unsigned npair = static_cast<unsigned>(a.batch) * a.hkv;
@@ -733,6 +797,8 @@ hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream) {
   e = a.d == 64 ? bwd_bf16<64>(a, stream) : bwd_bf16<128>(a, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce, dim3(a.max_red * kRedSlices), dim3(256), 0, stream, a);
+  if (a.dwsel)
+    hipLaunchKernelGGL(bwd_dwsel, dim3(static_cast<unsigned>(npair) * a.nrow), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -141,6 +141,12 @@ struct BwdArgs {
   const float* lse;  // [batch, hq, n] from the forward
   const int32_t* idx;
   const int32_t* cnt;
+  // prior-induced softmax (nullptr: none): routing weights in the layout of
+  // idx; entries with w <= 0 are skipped, listed keys' logits gain sigma ln w
+  const float* wsel;
+  float sigma;
+  float* dwsel;      // optional out, layout of idx: dL/dw (needs wsel)
+  float* dbpart;     // workspace [batch * hkv * nrow, units, k_max]: per-unit sums of dS
   // workspace
   float* delta;      // [batch, hq, n]: dO . O
   uint32_t* bits;    // [batch * hkv, nwords, nblk]: bit r % 32 of word r / 32 = row r selected block j
@@ -149,12 +155,34 @@ struct BwdArgs {
   int* counters;     // [2]: items, red
   float* part;       // [slots, 2, B, d]: dK then dV partials of split blocks
   int batch, hq, hkv, d, B, k_max, nrow, nblk, nwords, chunk, max_items, max_red;
+  int units;         // query-side units per row (query heads of a group x query sub-tiles)
   int64_t n;
   float sm_scale;
   bool bf16, o_f32, g_f32;
 };
-int attend_bwd_max_chunk();
+int attend_bwd_units(int group, int B);  // units per row of the query side
+int attend_bwd_max_prior_width();        // k_max limit when dL/dw is requested
 hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream);
+
+// Routing part of the gradient of entmax-routed prefill (block rows): dL/dw
+// of the listed blocks -> dQ, dK (added to the caller's gradients).
+struct RouteBwdArgs {
+  const float* qhat;   // [batch, hq, nrow, d] routing queries (workspace)
+  const float* S;      // [batch, hkv, nblk, d] summaries
+  const float* probs;  // [batch, hq, nrow, nblk] the routing probabilities
+  const int32_t* idx;  // [batch, hkv, nrow, width]
+  const int32_t* cnt;
+  const float* dwsel;  // layout of idx
+  float* dz;           // [batch, hq, nrow, nblk] workspace: dL/d(q-hat . S)
+  void* dQ;
+  void* dK;
+  Strides3 qs, ks;     // of dQ, dK (elements of the gradient dtype)
+  int batch, hq, hkv, d, B, nrow, nblk, width;
+  int64_t n;
+  float alpha, fscale;  // fscale = gamma * score_scale
+  bool g_f32;
+};
+hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t stream);
 
 // Active blocks of every 64-query tile from per-token selections
 // idx/cnt [batch, hkv, q_len, width]: uidx/ucnt the ascending union over the

@@ -24,6 +24,8 @@
  *                               decode).
  *            bsa_attend_backward  gradients of the prefill attention for a
  *                               fixed selection, zero blocks skipped.
+ *            bsa_route_entmax_backward  the gradient through the entmax
+ *                               routing weights to the queries and keys.
  *            bsa_token_mask     per-token selections (BSA_TOKEN) as active-block
  *                               masks of 64-query tiles.
  *            bsa_attend_entmax  token-level alpha-entmax attention
@@ -103,7 +105,8 @@ typedef enum {
   BSA_OP_ATTEND_DECODE = 4,
   BSA_OP_DECODE_TOPK = 5,
   BSA_OP_ATTEND_PREFILL_PRIOR = 6, /* bsa_attend_prefill with wsel != NULL */
-  BSA_OP_ATTEND_BACKWARD = 7       /* bsa_attend_backward; k_or_cap = k_max */
+  BSA_OP_ATTEND_BACKWARD = 7,      /* bsa_attend_backward; k_or_cap = k_max */
+  BSA_OP_ROUTE_ENTMAX_BACKWARD = 8 /* bsa_route_entmax_backward */
 } bsa_op;
 
 /* Problem description, read only during the call. */
@@ -277,9 +280,9 @@ int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, con
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Backward of Stage 2, causal prefill with block rows and no prior: the
- * gradients of bsa_attend_prefill's output for a fixed selection (the
- * selection itself gets none).  The pages single out the backward pass as
+ * Backward of Stage 2, causal prefill with block rows: the gradients of
+ * bsa_attend_prefill's output for a fixed selection (the selection itself
+ * gets none; with a prior, the routing weights do).  The pages single out the backward pass as
  * where training time goes and skip its zero blocks ("AdaSplash-2", section
  * 4); training the sparse attention end to end is "DashAttention",
  * Contribuições item 1.  For query t of head h with weights P_tu over its
@@ -293,9 +296,14 @@ int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, con
  * are gathered from a transposed copy of the selection; blocks selected by
  * many rows are split over several workgroups and their parts summed in a
  * fixed order, so results are deterministic).
- *   Q, K, V, idx, cnt, k_max, sm_scale  as given to bsa_attend_prefill
- *         (bf16 only; the entries of a row must be distinct, as the routing
- *         calls produce them).
+ *   Q, K, V, idx, cnt, k_max, sm_scale, wsel, sigma  as given to
+ *         bsa_attend_prefill (bf16 only; the entries of a row must be
+ *         distinct, as the routing calls produce them; wsel NULL: no prior).
+ *   dwsel NULL, or out fp32 in the layout of idx (needs wsel, k_max <= 80):
+ *         dL/dw_j = sigma / w_j * sum of dS_tu over the entry's (query, key)
+ *         pairs of every query head of the group (the logits of block j
+ *         carry sigma ln w_j); 0 for entries beyond cnt or with w_j <= 0.
+ *         bsa_route_entmax_backward carries it to Q and K.
  *   O     the forward output, o_dtype (bf16 or BSA_F32), with o_stride.
  *   dO    bf16 [batch, Hq, q_len, d] with o_stride.
  *   lse   fp32 [batch, Hq, q_len] written by bsa_attend_prefill.
@@ -310,8 +318,40 @@ int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, con
 int bsa_attend_backward(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                         const void *O, int32_t o_dtype, const void *dO, const float *lse,
                         const int32_t *idx, const int32_t *cnt, int32_t k_max, float sm_scale,
-                        void *dQ, void *dK, void *dV, int32_t g_dtype, void *ws,
-                        size_t ws_bytes, void *stream);
+                        const float *wsel, float sigma, float *dwsel, void *dQ, void *dK,
+                        void *dV, int32_t g_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of Stage 1, alpha-entmax routing of prefill block rows: the part of
+ * the gradient that flows through the routing weights into the queries and
+ * the keys ("DashAttention", Estágio 1: entmax routing is differentiable, so
+ * gradients pass the routing decision back to the block summaries of
+ * Estágio 0).  With w_j = (1/G) sum_h p_hj the listed routed blocks' weights
+ * (forced blocks have none), dp_hj = dw_j / G; with g = p^(2-alpha) on the
+ * support, the logits z_hj = gamma * score_scale * qhat_h . S_j get
+ * dz_j = g_j (dp_j - <g, dp> / sum g); then
+ *   dqhat_h = gamma * score_scale * sum_j dz_hj S_j,
+ *   dS_j = gamma * score_scale * sum over the group's heads and rows of dz q-hat,
+ * and the mean pools give every query of row r dqhat / (tokens of the row)
+ * and every key of block j dS_j / (tokens of the block) (summaries with a
+ * zero learned query).  These are ADDED to dQ and dK (run after
+ * bsa_attend_backward wrote the attention part).
+ *   Q      the forward's queries (the routing queries are recomputed).
+ *   S      fp32 [batch, Hkv, n_blk, d]: the summaries the routing used.
+ *   probs  fp32 [batch, Hq, n_rows, n_blk]: probs_out of bsa_route_entmax.
+ *   idx, cnt, width  the selection of bsa_route_entmax.
+ *   dwsel  fp32, layout of idx: from bsa_attend_backward.
+ *   alpha, gamma, score_scale  as given to bsa_route_entmax (0: 1/sqrt(d)).
+ *   dQ, dK in/out, g_dtype (input dtype or BSA_F32), strides of Q and K.
+ *   ws     bsa_workspace_size(BSA_OP_ROUTE_ENTMAX_BACKWARD, shape, 0) bytes.
+ * Errors: BSA_ERR_INVALID (mode other than BSA_PREFILL, alpha <= 1, null
+ * pointers), BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
+ */
+int bsa_route_entmax_backward(const bsa_shape *shape, const void *Q, const float *S,
+                              const float *probs, const int32_t *idx, const int32_t *cnt,
+                              int32_t width, const float *dwsel, float alpha, float gamma,
+                              float score_scale, void *dQ, void *dK, int32_t g_dtype, void *ws,
+                              size_t ws_bytes, void *stream);
 
 /*
  * Token-level alpha-entmax attention, causal prefill ("AdaSplash-2", sections

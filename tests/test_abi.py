@@ -239,14 +239,23 @@ def test_paged_validation():
 
 
 def backward(s, k_max=4, o_dtype=None, g_dtype=None, lse=FAKE, dO=FAKE, ws_bytes=None,
-             sm_scale=0.0):
+             sm_scale=0.0, wsel=None, sigma=0.0, dwsel=None):
     n = (lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD, ctypes.byref(s), k_max)
          if ws_bytes is None else ws_bytes)
     return lib.bsa_attend_backward(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE,
                                    s.dtype if o_dtype is None else o_dtype, dO, lse, FAKE, FAKE,
-                                   k_max, sm_scale, FAKE, FAKE, FAKE,
+                                   k_max, sm_scale, wsel, sigma, dwsel, FAKE, FAKE, FAKE,
                                    s.dtype if g_dtype is None else g_dtype,
                                    ctypes.c_void_p(0x200000), n, None)
+
+
+def route_backward(s, width=6, alpha=1.5, ws_bytes=None, dwsel=FAKE, g_dtype=None):
+    n = (lib.bsa_workspace_size(bsa.OP_ROUTE_ENTMAX_BACKWARD, ctypes.byref(s), 0)
+         if ws_bytes is None else ws_bytes)
+    return lib.bsa_route_entmax_backward(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, width,
+                                         dwsel, alpha, 1.0, 0.0, FAKE, FAKE,
+                                         s.dtype if g_dtype is None else g_dtype,
+                                         ctypes.c_void_p(0x200000), n, None)
 
 
 def test_backward_validation_and_workspace():
@@ -259,8 +268,9 @@ def test_backward_validation_and_workspace():
     items = 2 * nblk + -(-E // 32)
     red = min(2 * nblk, E // 33 + 1)
     slots = E // 32 + red + 1
+    units = 2 * (64 // 32)  # query heads per KV head x 32-query sub-tiles of a block
     assert need == (al(4 * 645 * 4) + al(2 * 1 * nblk * 4) + al(items * 16) + al(red * 16) + al(8)
-                    + al(slots * 2 * 64 * 128 * 4))
+                    + al(slots * 2 * 64 * 128 * 4) + al(2 * nrow * units * 4 * 4))
     assert backward(s, ws_bytes=need - 1) == -4
     assert backward(shape(mode=bsa.TOKEN)) == -1 and "BSA_PREFILL" in err()
     assert backward(shape(dtype=bsa.F32)) == -2 and "bf16" in err()
@@ -273,3 +283,20 @@ def test_backward_validation_and_workspace():
     big = shape(q_len=64 * 16385, kv_len=64 * 16385, hq=2, hkv=1)
     assert backward(big, ws_bytes=0) == -2 and "16384" in err()
     assert lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD, ctypes.byref(shape(mode=bsa.TOKEN)), 4) == 0
+
+
+def test_backward_prior_and_routing_backward_validation():
+    s = shape()
+    assert backward(s, dwsel=FAKE) == -1 and "dwsel needs wsel" in err()
+    assert backward(s, wsel=FAKE, sigma=float("nan")) == -1 and "sigma" in err()
+    assert backward(s, k_max=81, wsel=FAKE, dwsel=FAKE) == -2 and "80" in err()
+    assert backward(s, wsel=ctypes.c_void_p(0x100002)) == -2 and "aligned" in err()
+    need = lib.bsa_workspace_size(bsa.OP_ROUTE_ENTMAX_BACKWARD, ctypes.byref(s), 0)
+    al = lambda x: (x + 255) // 256 * 256
+    assert need == al(1 * 4 * 4 * 128 * 4) + al(1 * 4 * 4 * 4 * 4)  # q-hat + dz: 4 rows x 4 blocks
+    assert route_backward(s, ws_bytes=need - 1) == -4
+    assert route_backward(shape(mode=bsa.TOKEN)) == -1 and "BSA_PREFILL" in err()
+    assert route_backward(s, alpha=1.0) == -1 and "alpha" in err()
+    assert route_backward(s, dwsel=None) == -1 and "dwsel" in err()
+    assert route_backward(s, width=0) == -1
+    assert route_backward(s, g_dtype=5) == -2

@@ -218,3 +218,65 @@ def test_backward_full_size_headline_sampled():
     sv = dV.double().sum(dim=2)
     ref_v = x["dO"].double().reshape(1, w.hkv, G, w.n, w.d).sum(dim=(2, 3))
     assert float((sv - ref_v).abs().max()) <= 1e-3 * float(ref_v.abs().max() + w.n)
+
+
+ENT = W["entmax_prefill_n64k"]
+PRIOR_CASES = {
+    # entmax routing with a prior: the gradient reaches the routing weights,
+    # then through the routing to Q and K
+    "ent_b64": ENT.scaled(hq=8, hkv=2, n=64 * 12 + 17, gamma=16.0, cap=6, sigma=1.0,
+                          planted_blocks=2),
+    "ent_b128_d64": ENT.scaled(hq=8, hkv=2, d=64, n=128 * 7 + 40, B=128, gamma=24.0, cap=64,
+                               sigma=0.7, planted_blocks=1),
+}
+
+
+@pytest.mark.parametrize("name", list(PRIOR_CASES))
+@pytest.mark.parametrize("g_f32", [True, False])
+def test_backward_through_prior_and_entmax_routing(name, g_f32):
+    """The DashAttention chain: summaries -> entmax routing -> prior-induced
+    attention; dL/dw of the listed blocks and the total dQ, dK, dV (attention
+    part + routing part) against the oracle's chain on the oracle's own
+    routing, which must select the same blocks."""
+    w = PRIOR_CASES[name]
+    print(f"[prior + routing backward] {name} g_f32={g_f32}", flush=True)
+    x = _inputs(w)
+    S = bsa.summarize(x["K"], w.B)
+    width = w.idx_width
+    wsel = torch.empty((1, w.hkv, w.nblk, width), dtype=torch.float32, device="cuda")
+    idx, cnt, probs, _ = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
+                                          max_iter=w.max_iter, want_probs=True, wsel=wsel)
+    O, L = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt, wsel=wsel, sigma=w.sigma,
+                              want_lse=True)
+    dQ, dK, dV, dw = bsa.attend_backward(x["Q"], x["K"], x["V"], O, x["dO"], L, w.B, idx, cnt,
+                                         grad_dtype=torch.float32 if g_f32 else None, wsel=wsel,
+                                         sigma=w.sigma, want_dwsel=True)
+    dQa, dKa = dQ.clone(), dK.clone()
+    bsa.route_entmax_backward(x["Q"], S, probs, idx, cnt, dw, w.B, w.alpha, w.gamma, dQ, dK)
+    torch.cuda.synchronize()
+
+    So = oracle.summarize(x["k"], w.B)
+    qh = oracle.qpool(x["q"], w.B)
+    r = oracle.route_entmax(qh, So, w.B, w.alpha, w.gamma, w.cap, w.force, max_iter=w.max_iter,
+                            idx_width=width)
+    assert np.array_equal(r["idx"], _cpu(idx)) and np.array_equal(r["cnt"], _cpu(cnt))
+    rq, rk, rv, rdw = oracle.attend_backward(x["q"], x["k"], x["v"], x["do"], w.B, r["idx"],
+                                             r["cnt"], wsel=r["wsel"], sigma=w.sigma)
+    gq, gk = oracle.route_entmax_backward(qh, So, r["probs"], r["idx"], r["cnt"], rdw, w.n, w.B,
+                                          w.alpha, w.gamma)
+    assert np.abs(gq).max() > 1e-2 * np.abs(rq).max()  # the routing part matters here
+    if not g_f32:  # bf16 gradients: the totals, with their own rounding
+        e = [_check(nm, g, ref, True) for nm, g, ref in
+             (("dQ", dQ, rq + gq), ("dK", dK, rk + gk), ("dV", dV, rv))]
+        print("max err / scale: dQ %.2e dK %.2e dV %.2e" % tuple(e))
+        return
+    e = [_check("dwsel", dw, rdw, False),
+         _check("dQ attention part", dQa, rq, False),
+         _check("dK attention part", dKa, rk, False),
+         _check("dQ routing part", dQ - dQa, gq, False),
+         _check("dK routing part", dK - dKa, gk, False),
+         _check("dQ", dQ, rq + gq, False),
+         _check("dK", dK, rk + gk, False),
+         _check("dV", dV, rv, False)]
+    print("max err / scale: dw %.2e dQa %.2e dKa %.2e dQr %.2e dKr %.2e dQ %.2e dK %.2e "
+          "dV %.2e" % tuple(e))
