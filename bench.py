@@ -23,8 +23,11 @@ the same step over the cache stored as a shuffled pool of 64-token pages),
 times and attention TFLOP/s, and `entmax_attn_prefill_n16k` (token-level
 alpha-entmax attention, dense causal with zero key tiles skipped) timed
 beside the dense causal softmax of the same inputs (every block selected),
-and `backward` (the gradients dQ, dK, dV of the headline attention for its
-selection, beside the forward that feeds them).
+`backward` (the gradients dQ, dK, dV of the headline attention for its
+selection, beside the forward that feeds them) and `train_entmax_prior` (a
+training pass of entmax routing with the prior-induced softmax, sigma = 1, on
+the N = 65536 entmax inputs: forward, then the attention gradients with
+dL/dw and the routing gradient into dQ and dK).
 """
 from __future__ import annotations
 
@@ -462,6 +465,78 @@ def run_backward(bsa, torch, w, r, steps, warmup):
     return out
 
 
+def run_train_entmax(bsa, torch, steps, warmup, sigma=1.0):
+    """One training pass of entmax-routed prefill with the prior (the
+    N = 65536 entmax workload with sigma = 1): forward = summaries, entmax
+    routing (probabilities and weights kept), biased attention with its
+    log-normaliser; backward = attention gradients with dL/dw, then the
+    routing gradient added to dQ and dK.  Timed as two event-bracketed
+    phases per step."""
+    w = synth.WORKLOADS[ENTMAX]
+    x = device_inputs(w, torch)
+    Q, K, V = x["Q"], x["K"], x["V"]
+    del x
+    do_st, _ = synth.gen_stored(w, "do")
+    dO = torch.from_numpy(do_st.view(np.int16)).to("cuda").view(torch.bfloat16)
+    del do_st
+    width = w.idx_width
+    S = torch.empty((w.batch, w.hkv, w.nblk, w.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.batch, w.hkv, w.nblk, width), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((w.batch, w.hkv, w.nblk), dtype=torch.int32, device="cuda")
+    wsel = torch.empty(idx.shape, dtype=torch.float32, device="cuda")
+    O = torch.empty_like(Q)
+    shape_r = bsa._route_shape(Q, S, w.B, False, None, False)
+    rws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_ENTMAX, shape_r, w.cap), dtype=torch.uint8,
+                      device="cuda")
+    shape = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B, dtype=bsa.BF16,
+                           mode=bsa.PREFILL, q_len=w.n, kv_len=w.n, q=Q, k=K, v=V, o=O)
+    bws = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_BACKWARD, shape, width), dtype=torch.uint8,
+                      device="cuda")
+    gws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_ENTMAX_BACKWARD, shape, 0),
+                      dtype=torch.uint8, device="cuda")
+    st = {}
+
+    def forward():
+        bsa.summarize(K, w.B, out=S)
+        _, _, st["probs"], _ = bsa.route_entmax(Q, S, w.B, w.alpha, w.gamma, w.cap, w.force,
+                                                n_bins=w.n_bins, max_iter=w.max_iter, ws=rws,
+                                                out=(idx, cnt), wsel=wsel, want_probs=True)
+        _, st["L"] = bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O, wsel=wsel, sigma=sigma,
+                                        want_lse=True)
+
+    def backward():
+        dQ, dK, dV, dw = bsa.attend_backward(Q, K, V, O, dO, st["L"], w.B, idx, cnt, ws=bws,
+                                             wsel=wsel, sigma=sigma, want_dwsel=True,
+                                             grad_dtype=torch.float32)
+        bsa.route_entmax_backward(Q, S, st["probs"], idx, cnt, dw, w.B, w.alpha, w.gamma, dQ, dK,
+                                  ws=gws)
+
+    for _ in range(warmup):
+        forward()
+        backward()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        forward()
+        e[1].record()
+        backward()
+        e[2].record()
+        ev.append(e)
+    torch.cuda.synchronize()
+    fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    flops = 4.0 * w.d * prefill_pairs(w, idx.cpu().numpy(), cnt.cpu().numpy())
+    del Q, K, V, dO, S, idx, cnt, wsel, O, rws, bws, gws, st
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "prior_sigma": sigma, "forward_ms": fwd, "backward_ms": bwd,
+            "train_step_ms": fwd + bwd, "attention_flops": flops,
+            "backward_attention_TFLOP_per_s": 2.5 * flops / bwd / 1e9,
+            "note": "backward = attention gradients with dL/dw + routing gradient into dQ, dK; "
+                    "fp32 gradients"}
+
+
 def main():
     a = parse()
     if a.copy_calibration:
@@ -502,6 +577,7 @@ def main():
     extra = {}
     if not a.no_backward:
         extra["backward"] = run_backward(bsa, torch, w, r, a.steps, a.warmup)
+        extra["train_entmax_prior"] = run_train_entmax(bsa, torch, a.steps, a.warmup)
     if not a.no_decode:
         extra["decode"] = run_decode(bsa, torch, a.steps, a.warmup)
     for name, flag in ((ENTMAX, a.no_entmax), (LONG, a.no_long), (TOKEN, a.no_token)):
