@@ -245,14 +245,16 @@ BwdWs bwd_ws(const bsa_shape* s, int32_t k_max) {
 }
 // Routing backward: the routing queries and dL/d(logit) of every head-row.
 struct RouteBwdWs {
-  size_t qhat, dz, total;
+  size_t qhat, dz, dqh, dsp, total;
 };
 RouteBwdWs route_bwd_ws(const bsa_shape* s) {
   const size_t rows = static_cast<size_t>(s->batch) * s->n_q_heads * nrow_of(s);
   RouteBwdWs w{};
   w.qhat = align_up(rows * s->head_dim * 4);
   w.dz = align_up(rows * nblk_of(s) * 4);
-  w.total = w.qhat + w.dz;
+  w.dqh = align_up(rows * s->head_dim * 4);
+  w.dsp = align_up(rows * s->head_dim * 4);  // n_blk == n_rows in prefill
+  w.total = w.qhat + w.dz + w.dqh + w.dsp;
   return w;
 }
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -956,6 +958,8 @@ int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
   a.cnt = cnt;
   a.dwsel = dwsel;
   a.dz = reinterpret_cast<float*>(base + w.qhat);
+  a.dqh = reinterpret_cast<float*>(base + w.qhat + w.dz);
+  a.dsp = reinterpret_cast<float*>(base + w.qhat + w.dz + w.dqh);
   a.dQ = dQ;
   a.dK = dK;
   a.qs = st3(s->q_stride);

@@ -174,6 +174,8 @@ struct RouteBwdArgs {
   const int32_t* cnt;
   const float* dwsel;  // layout of idx
   float* dz;           // [batch, hq, nrow, nblk] workspace: dL/d(q-hat . S)
+  float* dqh;          // [batch, hq, nrow, d] workspace: dL/d(q-hat)
+  float* dsp;          // [batch, hq, nblk, d] workspace: each head's part of dL/dS
   void* dQ;
   void* dK;
   Strides3 qs, ks;     // of dQ, dK (elements of the gradient dtype)

@@ -9,10 +9,12 @@
 //                    the group of p_j, so dp_j = dw_j / G; with g = p^(2-alpha)
 //                    on the support, dz_j = g_j (dp_j - <g, dp> / sum g),
 //                    scaled by gamma * score_scale (the logits' factor).
-//   route_bwd_q      dqhat = dz S (over the row's candidates), spread over the
-//                    row's queries: dQ_t += dqhat / (tokens in the row).
-//   route_bwd_k      dS_j = sum over the group's heads and rows of dz q-hat,
-//                    spread over the block's keys: dK_u += dS / (tokens).
+//   route_bwd_gemm   dqhat = dz S (over the row's candidates) and each head's
+//                    part of dS_j = sum over rows of dz q-hat: fp32 products
+//                    on MFMA tiles staged in LDS.
+//   route_bwd_spread the mean pools' adjoint: dQ_t += dqhat_row / (tokens in
+//                    the row), dK_u += (sum over the group's heads of the
+//                    parts) / (tokens in the block), four elements a thread.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,6 +23,7 @@ namespace bsa {
 namespace {
 
 constexpr int kVjpThreads = 256;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int NT>
 __device__ __forceinline__ float block_sum(float v, float* red) {
@@ -79,68 +82,131 @@ __global__ __launch_bounds__(kVjpThreads) void entmax_vjp_rows(RouteBwdArgs a) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void add_to(void* base, int64_t off, float v) {
-  if constexpr (sizeof(T) == 4) {
-    static_cast<float*>(base)[off] += v;
-  } else {
-    uint16_t* q = static_cast<uint16_t*>(base) + off;
-    *q = f32_to_bf16(bf16_to_f32(*q) + v);
-  }
-}
+// Batched fp32 product on MFMA tiles, C[64 x D] = A[64 x K] B[K x D] per
+// workgroup, with A read through element strides (so it may be a transposed
+// view of dz) and both tiles staged in LDS with K contiguous.
+//   KEY = false: rows r (query blocks) of head h, K = blocks j < r:
+//                A = dz[h][r][j], B = S[g][j][c] -> dqhat[h][r][c].
+//   KEY = true:  rows j (key blocks), one head h of the group, K = rows
+//                r > j: A = dz[h][r][j], B = qhat[h][r][c] -> that head's
+//                part of dS[g][j][c] (the parts are summed when spread).
+constexpr int kGT = 64;      // output rows per workgroup, K per chunk
+constexpr int kGPad = 4;     // LDS row padding (floats)
 
-// One workgroup (d threads) per (batch, query head, row).
-template <typename GT>
-__global__ __launch_bounds__(128) void route_bwd_q(RouteBwdArgs a) {
-  const int64_t hrow = blockIdx.x;
-  const int r = static_cast<int>(hrow % a.nrow);
-  const int64_t bh = hrow / a.nrow;
-  const int h = static_cast<int>(bh % a.hq);
-  const int64_t b = bh / a.hq;
-  const int g = h / (a.hq / a.hkv);
-  const int c = threadIdx.x;
-  const float* dz = a.dz + hrow * a.nblk;
-  const float* S = a.S + (b * a.hkv + g) * a.nblk * a.d;
-  float acc0 = 0.f, acc1 = 0.f;
-  // candidates are the blocks before the row's own
-  int j = 0;
-  for (; j + 1 < r; j += 2) {
-    acc0 = fmaf(dz[j], S[static_cast<int64_t>(j) * a.d + c], acc0);
-    acc1 = fmaf(dz[j + 1], S[static_cast<int64_t>(j + 1) * a.d + c], acc1);
-  }
-  if (j < r) acc0 = fmaf(dz[j], S[static_cast<int64_t>(j) * a.d + c], acc0);
-  const int64_t t0 = static_cast<int64_t>(r) * a.B;
-  const int nr = static_cast<int>(a.n - t0 < a.B ? a.n - t0 : a.B);
-  const float v = (acc0 + acc1) / static_cast<float>(nr);
-  const int64_t base = b * a.qs.b + h * a.qs.h;
-  for (int t = 0; t < nr; ++t) add_to<GT>(a.dQ, base + (t0 + t) * a.qs.t + c, v);
-}
-
-// One workgroup (d threads) per (batch, KV head, key block).
-template <typename GT>
-__global__ __launch_bounds__(128) void route_bwd_k(RouteBwdArgs a) {
-  const int j = static_cast<int>(blockIdx.x % a.nblk);
-  const int64_t bg = blockIdx.x / a.nblk;
-  const int g = static_cast<int>(bg % a.hkv);
-  const int64_t b = bg / a.hkv;
+template <int D, bool KEY>
+__global__ __launch_bounds__(256) void route_bwd_gemm(RouteBwdArgs a) {
+  constexpr int KS = kGT + kGPad;
+  __shared__ float As[kGT][KS];  // [m][k]
+  __shared__ float Bs[D][KS];    // [c][k]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.hq / a.hkv;
-  const int c = threadIdx.x;
-  float acc0 = 0.f, acc1 = 0.f;
-  for (int hh = 0; hh < G; ++hh) {
-    const int64_t hb = (b * a.hq + g * G + hh) * a.nrow;
-    // rows after j have block j among their candidates
-    int r = j + 1;
-    for (; r + 1 < a.nrow; r += 2) {
-      acc0 = fmaf(a.dz[(hb + r) * a.nblk + j], a.qhat[(hb + r) * a.d + c], acc0);
-      acc1 = fmaf(a.dz[(hb + r + 1) * a.nblk + j], a.qhat[(hb + r + 1) * a.d + c], acc1);
+  const int nmt = (a.nrow + kGT - 1) / kGT;  // nrow == nblk (prefill)
+  const int mt = blockIdx.x % nmt;
+  const int64_t bh = blockIdx.x / nmt;  // (b, h)
+  const int m0 = mt * kGT;
+  const int mrows = a.nrow - m0 < kGT ? a.nrow - m0 : kGT;
+  f32x4_t acc[D / 16];
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one K chunk of 64 staged and multiplied
+  auto chunk = [&](const float* abase, int64_t am, int64_t ak, int kn, const float* bbase) {
+    __syncthreads();
+    for (int e = tid; e < kGT * kGT; e += 256) {
+      // walk the contiguous dimension of A across neighbouring threads
+      const int m = ak == 1 ? e / kGT : e % kGT;
+      const int k = ak == 1 ? e % kGT : e / kGT;
+      As[m][k] = (m < mrows && k < kn) ? abase[m * am + k * ak] : 0.f;
     }
-    if (r < a.nrow) acc0 = fmaf(a.dz[(hb + r) * a.nblk + j], a.qhat[(hb + r) * a.d + c], acc0);
+    for (int e = tid; e < kGT * D; e += 256) {
+      const int k = e / D, c = e % D;
+      Bs[c][k] = k < kn ? bbase[static_cast<int64_t>(k) * D + c] : 0.f;
+    }
+    __syncthreads();
+    const int lr = lane & 15, lk = (lane >> 4) * 4;
+#pragma unroll 4
+    for (int kc = 0; kc < kGT; kc += 16) {
+      const float4 av = *reinterpret_cast<const float4*>(&As[16 * w + lr][kc + lk]);
+#pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct) {
+        const float4 bv = *reinterpret_cast<const float4*>(&Bs[16 * ct + lr][kc + lk]);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[ct], 0, 0, 0);
+      }
+    }
+  };
+
+  const int64_t b = bh / a.hq;
+  const int h = static_cast<int>(bh % a.hq), g = h / G;
+  const int64_t hrow = bh * a.nrow;
+  if constexpr (!KEY) {
+    const float* S = a.S + (b * a.hkv + g) * a.nblk * D;
+    // candidates of rows m0.. are the blocks before them
+    const int kend = m0 + mrows - 1;
+    for (int k0 = 0; k0 < kend; k0 += kGT)
+      chunk(a.dz + (hrow + m0) * a.nblk + k0, a.nblk, 1, kend - k0 < kGT ? kend - k0 : kGT,
+            S + static_cast<int64_t>(k0) * D);
+  } else {
+    // rows after block m0 hold it among their candidates
+    for (int r0 = m0 + 1; r0 < a.nrow; r0 += kGT)
+      chunk(a.dz + (hrow + r0) * a.nblk + m0, 1, a.nblk, a.nrow - r0 < kGT ? a.nrow - r0 : kGT,
+            a.qhat + (hrow + r0) * D);
   }
-  const int64_t u0 = static_cast<int64_t>(j) * a.B;
-  const int nj = static_cast<int>(a.n - u0 < a.B ? a.n - u0 : a.B);
-  const float v = (acc0 + acc1) / static_cast<float>(nj);
-  const int64_t base = b * a.ks.b + g * a.ks.h;
-  for (int u = 0; u < nj; ++u) add_to<GT>(a.dK, base + (u0 + u) * a.ks.t + c, v);
+  // lane l holds rows 16w + 4(l/16) + i, columns 16ct + l%16
+  float* out = (KEY ? a.dsp : a.dqh) + (hrow + m0) * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = 16 * w + (lane >> 4) * 4 + i;
+    if (m < mrows)
+#pragma unroll
+      for (int ct = 0; ct < D / 16; ++ct) out[m * D + 16 * ct + (lane & 15)] = acc[ct][i];
+  }
+}
+
+// The mean pools' adjoint, added to the gradient: every token of block r
+// gets src[r] / (tokens of the block), summed over `parts` consecutive heads
+// of src (the group's heads for dK, one head for dQ).  Four elements per
+// thread; blockIdx.y is the batch.
+template <typename GT>
+__global__ __launch_bounds__(256) void route_bwd_spread(const float* src, int parts, void* dst,
+                                                        Strides3 st, int heads, int nrow, int B,
+                                                        int64_t n, int d) {
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  const int64_t per_head = n * d;
+  if (e >= heads * per_head) return;
+  const int64_t b = blockIdx.y, hd = e / per_head;
+  const int64_t rem = e % per_head;
+  const int64_t t = rem / d;
+  const int c = static_cast<int>(rem % d);
+  const int r = static_cast<int>(t / B);
+  const int nt = static_cast<int>(n - static_cast<int64_t>(r) * B < B ? n - static_cast<int64_t>(r) * B : B);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = 0; p < parts; ++p) {
+    const float4 x = *reinterpret_cast<const float4*>(
+        src + (((b * heads + hd) * parts + p) * nrow + r) * d + c);
+    v.x += x.x;
+    v.y += x.y;
+    v.z += x.z;
+    v.w += x.w;
+  }
+  const float inv = 1.f / static_cast<float>(nt);
+  const int64_t off = b * st.b + hd * st.h + t * st.t + c;
+  if constexpr (sizeof(GT) == 4) {
+    float4* q = reinterpret_cast<float4*>(static_cast<float*>(dst) + off);
+    float4 o = *q;
+    o.x += v.x * inv;
+    o.y += v.y * inv;
+    o.z += v.z * inv;
+    o.w += v.w * inv;
+    *q = o;
+  } else {
+    uint2* q = reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + off);
+    const uint2 o = *q;
+    *q = make_uint2(pack_bf16x2(bf16_lo(o.x) + v.x * inv, bf16_hi(o.x) + v.y * inv),
+                    pack_bf16x2(bf16_lo(o.y) + v.z * inv, bf16_hi(o.y) + v.w * inv));
+  }
 }
 
 }  // namespace
@@ -148,13 +214,30 @@ __global__ __launch_bounds__(128) void route_bwd_k(RouteBwdArgs a) {
 hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t stream) {
   const unsigned rows = static_cast<unsigned>(a.batch) * a.hq * a.nrow;
   hipLaunchKernelGGL(entmax_vjp_rows, dim3(rows), dim3(kVjpThreads), 0, stream, a);
-  const unsigned kblocks = static_cast<unsigned>(a.batch) * a.hkv * a.nblk;
-  if (a.g_f32) {
-    hipLaunchKernelGGL(route_bwd_q<float>, dim3(rows), dim3(a.d), 0, stream, a);
-    hipLaunchKernelGGL(route_bwd_k<float>, dim3(kblocks), dim3(a.d), 0, stream, a);
+  const unsigned nmt = static_cast<unsigned>((a.nrow + kGT - 1) / kGT);
+  const dim3 gg(static_cast<unsigned>(a.batch) * a.hq * nmt);
+  if (a.d == 64) {
+    hipLaunchKernelGGL((route_bwd_gemm<64, false>), gg, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((route_bwd_gemm<64, true>), gg, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(route_bwd_q<uint16_t>, dim3(rows), dim3(a.d), 0, stream, a);
-    hipLaunchKernelGGL(route_bwd_k<uint16_t>, dim3(kblocks), dim3(a.d), 0, stream, a);
+    hipLaunchKernelGGL((route_bwd_gemm<128, false>), gg, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((route_bwd_gemm<128, true>), gg, dim3(256), 0, stream, a);
+  }
+  const int G = a.hq / a.hkv;
+  auto grid_of = [&](int heads) {
+    const int64_t elems = static_cast<int64_t>(heads) * a.n * a.d / 4;
+    return dim3(static_cast<unsigned>((elems + 255) / 256), static_cast<unsigned>(a.batch));
+  };
+  if (a.g_f32) {
+    hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1,
+                       a.dQ, a.qs, a.hq, a.nrow, a.B, a.n, a.d);
+    hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp, G,
+                       a.dK, a.ks, a.hkv, a.nrow, a.B, a.n, a.d);
+  } else {
+    hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1,
+                       a.dQ, a.qs, a.hq, a.nrow, a.B, a.n, a.d);
+    hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp, G,
+                       a.dK, a.ks, a.hkv, a.nrow, a.B, a.n, a.d);
   }
   return hipGetLastError();
 }

@@ -293,7 +293,8 @@ def test_backward_prior_and_routing_backward_validation():
     assert backward(s, wsel=ctypes.c_void_p(0x100002)) == -2 and "aligned" in err()
     need = lib.bsa_workspace_size(bsa.OP_ROUTE_ENTMAX_BACKWARD, ctypes.byref(s), 0)
     al = lambda x: (x + 255) // 256 * 256
-    assert need == al(1 * 4 * 4 * 128 * 4) + al(1 * 4 * 4 * 4 * 4)  # q-hat + dz: 4 rows x 4 blocks
+    # q-hat, dz (4 rows x 4 blocks), dL/dq-hat and the heads' parts of dL/dS
+    assert need == 3 * al(1 * 4 * 4 * 128 * 4) + al(1 * 4 * 4 * 4 * 4)
     assert route_backward(s, ws_bytes=need - 1) == -4
     assert route_backward(shape(mode=bsa.TOKEN)) == -1 and "BSA_PREFILL" in err()
     assert route_backward(s, alpha=1.0) == -1 and "alpha" in err()
