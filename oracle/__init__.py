@@ -68,6 +68,7 @@ def _load():
         lib.orc_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, I, D, P, P, D, P,
                                             P, P, P]
         lib.orc_entmax_vjp.argtypes = [P, P, I, D, P]
+        lib.orc_entmax_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, D, D, P, P, P]
         lib.orc_route_entmax_backward.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, D, D, D,
                                                   ctypes.c_uint32, P, P]
         lib.orc_version.restype = ctypes.c_char_p
@@ -280,6 +281,23 @@ def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None, rowmask=None, wsel=
                                 _ptr(rowmask), _ptr(wsel), float(sigma), _ptr(dwsel), _ptr(dQ),
                                 _ptr(dK), _ptr(dV))
     return (dQ, dK, dV) if wsel is None else (dQ, dK, dV, dwsel)
+
+
+def entmax_attend_backward(Q, K, V, dO, alpha, sm_scale=None):
+    """Gradients (dQ, dK, dV) in fp64 of the causal token-level alpha-entmax
+    attention for upstream dO."""
+    Q, K, V, dO = _f32(Q), _f32(K), _f32(V), _f32(dO)
+    nb, hq, n, d = Q.shape
+    hkv = K.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    dQ = np.empty(Q.shape, np.float64)
+    dK = np.empty(K.shape, np.float64)
+    dV = np.empty(V.shape, np.float64)
+    _load().orc_entmax_attend_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), nb, hq, hkv, n, d,
+                                       float(alpha), float(sm_scale), _ptr(dQ), _ptr(dK),
+                                       _ptr(dV))
+    return dQ, dK, dV
 
 
 def entmax_vjp(p, dp, alpha):

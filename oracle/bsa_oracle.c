@@ -1011,3 +1011,81 @@ void orc_route_entmax_backward(const double *qhat, const double *S, const double
   free(dqh);
   free(dS);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Backward of the token-level alpha-entmax attention.                        */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Gradients of orc_entmax_attend's output for upstream dO ("AdaSplash-2",
+ * sections 1 and 4: the entmax attention is trained, its backward skipping
+ * the zero blocks).  Per query t of head h: p over the keys j <= t as in the
+ * forward (exact tau), dp_j = dO_t . v_j, dz = the entmax VJP of dp
+ * (orc_entmax_vjp: g = p^(2-alpha) on the support), and with
+ * z_j = sm_scale q_t . k_j:
+ *   dQ_t = sm_scale sum_j dz_j k_j,  dK_j += sm_scale dz_j q_t,
+ *   dV_j += p_j dO_t   (keys summed over the group's heads).
+ *   Q, dO : [nb, hq, n, d];  K, V : [nb, hkv, n, d] (fp32);
+ *   dQ, dK, dV fp64, overwritten.
+ */
+void orc_entmax_attend_backward(const float *Q, const float *K, const float *V, const float *dO,
+                                int64_t nb, int64_t hq, int64_t hkv, int64_t n, int64_t d,
+                                double alpha, double sm_scale, double *dQ, double *dK,
+                                double *dV) {
+  int64_t G = hq / hkv;
+  double ex = 1.0 / (alpha - 1.0);
+  double *x = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double *xs = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double *dp = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  double *dz = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+  int64_t *ones = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+  for (int64_t a = 0; a < n; ++a) ones[a] = 1;
+  for (int64_t a = 0; a < nb * hq * n * d; ++a) dQ[a] = 0.0;
+  for (int64_t a = 0; a < nb * hkv * n * d; ++a) dK[a] = dV[a] = 0.0;
+  for (int64_t b = 0; b < nb; ++b)
+    for (int64_t h = 0; h < hq; ++h)
+      for (int64_t t = 0; t < n; ++t) {
+        int64_t g = h / G;
+        const float *qv = Q + ((b * hq + h) * n + t) * d;
+        const float *gv = dO + ((b * hq + h) * n + t) * d;
+        const float *kb = K + ((b * hkv + g) * n) * d;
+        const float *vb = V + ((b * hkv + g) * n) * d;
+        double *dq = dQ + ((b * hq + h) * n + t) * d;
+        double *dkb = dK + ((b * hkv + g) * n) * d;
+        double *dvb = dV + ((b * hkv + g) * n) * d;
+        int64_t m = t + 1;
+        for (int64_t j = 0; j < m; ++j) {
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c) acc += (double)qv[c] * (double)kb[j * d + c];
+          x[j] = (alpha - 1.0) * sm_scale * acc;
+          xs[j] = x[j];
+        }
+        qsort(xs, (size_t)m, sizeof(double), cmp_dbl_desc);
+        double tau = solve_sorted(xs, ones, m, alpha);
+        double z = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+          x[j] = x[j] > tau ? pow(x[j] - tau, ex) : 0.0;
+          z += x[j];
+        }
+        for (int64_t j = 0; j < m; ++j) {
+          x[j] /= z; /* p */
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c) acc += (double)gv[c] * (double)vb[j * d + c];
+          dp[j] = acc;
+        }
+        orc_entmax_vjp(x, dp, m, alpha, dz);
+        for (int64_t j = 0; j < m; ++j) {
+          if (x[j] == 0.0) continue;
+          for (int64_t c = 0; c < d; ++c) {
+            dq[c] += sm_scale * dz[j] * (double)kb[j * d + c];
+            dkb[j * d + c] += sm_scale * dz[j] * (double)qv[c];
+            dvb[j * d + c] += x[j] * (double)gv[c];
+          }
+        }
+      }
+  free(x);
+  free(xs);
+  free(dp);
+  free(dz);
+  free(ones);
+}

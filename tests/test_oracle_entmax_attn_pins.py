@@ -97,3 +97,51 @@ def test_entmax_attention_weights_are_a_sparse_distribution_and_causal():
     K2[:, :, 20:] = 100.0
     O2, _, _ = oracle.entmax_attend(Q, K2, V, 1.5)
     np.testing.assert_array_equal(O2.reshape(2, 30, 32)[:, :20], O[:, :20])
+
+
+# ---------------------------------------------------------------------------
+# Backward of the entmax attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.25])
+def test_entmax_attention_backward_matches_central_differences(alpha):
+    """dQ, dK, dV against central differences of the forward oracle's
+    loss sum(dO * O) (exact thresholds, so the map is smooth away from
+    support changes)."""
+    Q, K, V = _case(4400, n=19, d=8, hq=2, hkv=1, scale=2.0)
+    dO = _rng(4401).standard_normal(Q.shape).astype(np.float32)
+    dQ, dK, dV = oracle.entmax_attend_backward(Q, K, V, dO, alpha)
+
+    def loss(Qx, Kx, Vx):
+        O, _, _ = oracle.entmax_attend(Qx, Kx, Vx, alpha)
+        return float((O.reshape(dO.shape) * dO.astype(np.float64)).sum())
+
+    rng = _rng(4402)
+    h = np.float32(2.0 ** -12)
+    for which, g in (("Q", dQ), ("K", dK), ("V", dV)):
+        X = {"Q": Q, "K": K, "V": V}[which]
+        for _ in range(10):
+            pos = tuple(int(rng.integers(0, s)) for s in X.shape)
+            xp, xm = X.copy(), X.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            step = float(xp[pos]) - float(xm[pos])
+            args_p = {"Q": Q, "K": K, "V": V, which: xp}
+            args_m = {"Q": Q, "K": K, "V": V, which: xm}
+            fd = (loss(args_p["Q"], args_p["K"], args_p["V"]) -
+                  loss(args_m["Q"], args_m["K"], args_m["V"])) / step
+            np.testing.assert_allclose(g[pos], fd, rtol=2e-3, atol=2e-6)
+
+
+def test_entmax_attention_backward_invariants():
+    """Shifting every key leaves each query's entmax unchanged (its VJP sums
+    to zero), so the key gradients sum to zero; the weights sum to one, so
+    the value gradients sum to the upstream gradients; with alpha = 2 and a
+    query whose support is one key, that query's dQ is zero."""
+    Q, K, V = _case(4500, n=33, d=16, hq=4, hkv=2, scale=3.0)
+    dO = _rng(4501).standard_normal(Q.shape).astype(np.float32)
+    dQ, dK, dV = oracle.entmax_attend_backward(Q, K, V, dO, 1.5)
+    np.testing.assert_allclose(dK.sum(axis=2), 0.0, atol=1e-11)
+    want = dO.astype(np.float64).reshape(1, 2, 2, 33, 16).sum(axis=(2, 3))
+    np.testing.assert_allclose(dV.sum(axis=2), want, atol=1e-11)
+    np.testing.assert_array_equal(dQ[:, :, 0], 0.0)  # token 0 attends only itself
