@@ -37,14 +37,16 @@ F32, BF16 = 0, 1
 PREFILL, DECODE, TOKEN = 0, 1, 2
 FORCE_DIAG, FORCE_FIRST, FORCE_TAIL = 1, 2, 4
 OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE, \
-    OP_DECODE_TOPK, OP_ATTEND_PREFILL_PRIOR, OP_ATTEND_BACKWARD, OP_ROUTE_ENTMAX_BACKWARD = range(9)
+    OP_DECODE_TOPK, OP_ATTEND_PREFILL_PRIOR, OP_ATTEND_BACKWARD, OP_ROUTE_ENTMAX_BACKWARD, \
+    OP_ATTEND_ENTMAX_BACKWARD = range(10)
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
 EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_summarize_blocks_paged",
            "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill", "bsa_token_mask",
            "bsa_attend_decode", "bsa_decode_topk", "bsa_decode_topk_paged", "bsa_attend_entmax",
-           "bsa_attend_backward", "bsa_route_entmax_backward", "bsa_workspace_size",
+           "bsa_attend_backward", "bsa_route_entmax_backward", "bsa_attend_entmax_backward",
+           "bsa_workspace_size",
            "bsa_last_error", "bsa_version")
 
 
@@ -84,6 +86,8 @@ lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32
                                    _sz, _P]
 lib.bsa_attend_backward.argtypes = [_SP, _P, _P, _P, _P, _i32, _P, _P, _P, _P, _i32, _f32, _P, _f32,
                                     _P, _P, _P, _P, _i32, _P, _sz, _P]
+lib.bsa_attend_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, _P, _i32,
+                                           _P, _sz, _P]
 lib.bsa_route_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _P, _f32, _f32, _f32, _P,
                                           _P, _i32, _P, _sz, _P]
 lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
@@ -94,7 +98,8 @@ lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32,
 for _f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_summarize_blocks_paged,
            lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill, lib.bsa_token_mask,
            lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged,
-           lib.bsa_attend_entmax, lib.bsa_attend_backward, lib.bsa_route_entmax_backward):
+           lib.bsa_attend_entmax, lib.bsa_attend_backward, lib.bsa_route_entmax_backward,
+           lib.bsa_attend_entmax_backward):
     _f.restype = ctypes.c_int
 lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
 lib.bsa_workspace_size.restype = _sz
@@ -370,6 +375,26 @@ def attend_entmax(Q, K, V, alpha, refine=2, sm_scale=0.0, out_dtype=None, out=No
     _check(lib.bsa_attend_entmax(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), alpha, refine,
                                  sm_scale, _ptr(O), _dtype_code(O), _ptr(tau), _stream(Q)))
     return (O, tau) if want_tau else O
+
+
+def attend_entmax_backward(Q, K, V, dO, tau, alpha, sm_scale=0.0, grad_dtype=None, ws=None):
+    """Gradients (dQ, dK, dV) of attend_entmax's output for upstream dO, given
+    the forward's tau (want_tau=True).  Gradients take the strides of Q, K, V."""
+    b, hq, n, d = Q.shape
+    gdt = grad_dtype or Q.dtype
+    dQ = torch.empty_strided(Q.size(), Q.stride(), dtype=gdt, device=Q.device)
+    dK = torch.empty_strided(K.size(), K.stride(), dtype=gdt, device=K.device)
+    dV = torch.empty_strided(V.size(), V.stride(), dtype=gdt, device=V.device)
+    if dO.dtype != Q.dtype:
+        dO = dO.to(Q.dtype)
+    shape = make_shape(batch=b, hq=hq, hkv=K.shape[1], d=d, B=64, dtype=_dtype_code(Q),
+                       mode=PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=dO)
+    wsb, nws = _workspace(OP_ATTEND_ENTMAX_BACKWARD, shape, 0, Q.device, ws)
+    _check(lib.bsa_attend_entmax_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V),
+                                          _ptr(dO), _ptr(tau), alpha, sm_scale, _ptr(dQ),
+                                          _ptr(dK), _ptr(dV), _dtype_code(dQ), _ptr(wsb), nws,
+                                          _stream(Q)))
+    return dQ, dK, dV
 
 
 def token_mask(idx, cnt, B, kv_len=None, out=None):

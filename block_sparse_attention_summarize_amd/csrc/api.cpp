@@ -392,6 +392,11 @@ size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
       return s->mode == BSA_PREFILL && k_or_cap >= 1 ? bwd_ws(s, k_or_cap).total : 0;
     case BSA_OP_ROUTE_ENTMAX_BACKWARD:
       return s->mode == BSA_PREFILL ? route_bwd_ws(s).total : 0;
+    case BSA_OP_ATTEND_ENTMAX_BACKWARD:
+      // each query's <g, dP> / sum g and normaliser
+      return s->mode == BSA_PREFILL
+                 ? 2 * align_up(static_cast<size_t>(s->batch) * s->n_q_heads * s->q_len * 4)
+                 : 0;
     default:
       return 0;
   }
@@ -978,6 +983,70 @@ int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
                                           : 1.f / std::sqrt(static_cast<float>(s->head_dim)));
   a.g_f32 = g_dtype == BSA_F32;
   return device_status(bsa::launch_route_entmax_backward(a, st), "route_entmax_backward");
+}
+
+int bsa_attend_entmax_backward(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                               const void* dO, const float* tau, float alpha, float sm_scale,
+                               void* dQ, void* dK, void* dV, int32_t g_dtype, void* ws,
+                               size_t ws_bytes, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if (s->mode != BSA_PREFILL)
+    return fail(BSA_ERR_INVALID, "bsa_attend_entmax_backward needs BSA_PREFILL");
+  if (s->dtype != BSA_BF16)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax_backward supports bf16 inputs only");
+  if (s->block != 64)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax_backward works on 64-token tiles (block 64)");
+  if (!(alpha > 1.f) || !std::isfinite(alpha)) return fail(BSA_ERR_INVALID, "alpha must be > 1");
+  if (alpha > 2.f) return fail(BSA_ERR_UNSUPPORTED, "alpha > 2 is not supported");
+  bsa::AttendArgs f;
+  const int32_t one = 1;
+  if ((rc = attend_common(s, Q, K, V, &one, &one, 1, sm_scale, const_cast<void*>(dO), s->dtype,
+                          f)) != BSA_OK)
+    return rc;
+  if ((rc = check_ptr("dQ", dQ)) != BSA_OK) return rc;
+  if ((rc = check_ptr("dK", dK)) != BSA_OK) return rc;
+  if ((rc = check_ptr("dV", dV)) != BSA_OK) return rc;
+  if (!tau) return fail(BSA_ERR_INVALID, "tau is NULL");
+  if ((reinterpret_cast<uintptr_t>(tau) & 3u) != 0)
+    return fail(BSA_ERR_UNSUPPORTED, "tau must be 4-byte aligned");
+  if (g_dtype != s->dtype && g_dtype != BSA_F32)
+    return fail(BSA_ERR_UNSUPPORTED, "g_dtype must be the input dtype or BSA_F32");
+  if ((rc = check_strides("dQ/dK/dV", s->q_stride, g_dtype)) != BSA_OK) return rc;
+  const size_t per = align_up(static_cast<size_t>(s->batch) * s->n_q_heads * s->q_len * 4);
+  if ((rc = check_ws(ws, ws_bytes, 2 * per)) != BSA_OK) return rc;
+  char* base = static_cast<char*>(ws);
+  bsa::BwdArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.dO = dO;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.qs = f.qs;
+  a.ks = f.ks;
+  a.vs = f.vs;
+  a.os = f.os;
+  a.delta = reinterpret_cast<float*>(base);
+  a.zbuf = reinterpret_cast<float*>(base + per);
+  a.batch = s->batch;
+  a.hq = s->n_q_heads;
+  a.hkv = s->n_kv_heads;
+  a.d = s->head_dim;
+  a.B = 64;
+  a.k_max = 1;
+  a.nrow = f.nrow;
+  a.nblk = f.nblk;
+  a.n = s->q_len;
+  a.sm_scale = f.sm_scale;
+  a.bf16 = true;
+  a.g_f32 = g_dtype == BSA_F32;
+  a.ent = true;
+  a.alpha = alpha;
+  a.tau = tau;
+  return device_status(bsa::launch_attend_backward(a, static_cast<hipStream_t>(stream)),
+                       "attend_entmax_backward");
 }
 
 int bsa_attend_entmax(const bsa_shape* s, const void* Q, const void* K, const void* V,

@@ -30,6 +30,8 @@
 //   bwd_reduce    blocks split into several chunks: the chunks' fp32 partials
 //                 summed in chunk order (deterministic), then stored.
 // Every gradient element is written exactly once; keys no query attends get 0.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "walk.hpp"
@@ -198,9 +200,31 @@ struct DqLds {
   alignas(16) uint16_t v[2][64 * Swz<D>::ST];
 };
 
+// Entmax weights of a score: t = x - tau with x = (alpha - 1) sm_scale s;
+// on the support (t > 0) the unnormalised weight t^(1/(alpha-1)) and the
+// Jacobian weight t^((2-alpha)/(alpha-1)) (p^(2-alpha) up to the
+// normaliser's power), with the closed forms of alpha = 1.5 and 2.
+__device__ __forceinline__ void ent_pow(float t, float alpha, float ib, float ig, float& pb,
+                                        float& pg) {
+  if (alpha == 1.5f) {
+    pb = t * t;
+    pg = t;
+  } else if (alpha == 2.f) {
+    pb = t;
+    pg = 1.f;
+  } else {
+    const float l2 = __log2f(t);
+    pb = __builtin_amdgcn_exp2f(ib * l2);
+    pg = __builtin_amdgcn_exp2f(ig * l2);
+  }
+}
+
 // QT query tiles of 16 per wavefront, NW wavefronts; a unit is one query head
-// x 16 QT queries of the query block, as in the forward kernel.
-template <int D, int QT, int NW>
+// x 16 QT queries of the query block, as in the forward kernel.  ENT: the
+// token-level entmax attention (dense causal, tau per query): a first walk
+// over the tiles gathers each query's normaliser and the VJP's mean
+// <g, dP> / sum g, the second forms dz and dQ.
+template <int D, int QT, int NW, bool ENT>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   constexpr int NT = NW * 64;
   constexpr int QPW = 16 * QT;
@@ -238,8 +262,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   if (qmax > a.n - 1) qmax = a.n - 1;
 
   const int64_t rowid = static_cast<int64_t>(pair) * a.nrow + i;
-  int n = a.cnt[rowid];
-  n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
+  int n = 0;
+  if constexpr (!ENT) {
+    n = a.cnt[rowid];
+    n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
+  }
   TileWalk walk{a.idx + rowid * a.k_max, n, nsub, a.B, a.nblk, a.n, qmax};
 
   const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
@@ -252,7 +279,27 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   // d = 32ks + 8(l/16) .. +7; rows past n read as zero.
   uint4 qf[QT][KS], df[QT][KS];
   float dl[QT], lse2[QT];
-  {
+  const int64_t hrow = (static_cast<int64_t>(b) * a.hq + h) * a.n;
+  if constexpr (ENT) {
+    // entmax: Q and dO fragments, and tau (x units) in place of lse
+    const auto rq = make_rsrc(static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h,
+                              active ? head_bytes(a.n, a.qs.t, D, 2) : 0u);
+    const auto rdo = make_rsrc(static_cast<const uint16_t*>(a.dO) + b * a.os.b + h * a.os.h,
+                               active ? head_bytes(a.n, a.os.t, D, 2) : 0u);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int64_t t = qpos0 + qt * 16 + (lane & 15);
+      const uint32_t tq = static_cast<uint32_t>(t);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c0 = ks * 32 + (lane >> 4) * 8;
+        qf[qt][ks] = buf_load16(rq, tq * static_cast<uint32_t>(a.qs.t * 2) + c0 * 2);
+        df[qt][ks] = buf_load16(rdo, tq * static_cast<uint32_t>(a.os.t * 2) + c0 * 2);
+      }
+      lse2[qt] = t < a.n ? a.tau[hrow + t] : INFINITY;  // past the end: no support
+      dl[qt] = 0.f;
+    }
+  } else {
     const uint32_t qbytes = active ? head_bytes(a.n, a.qs.t, D, 2) : 0u;
     const uint32_t obytes = active ? head_bytes(a.n, a.os.t, D, a.o_f32 ? 4 : 2) : 0u;
     const auto rq = make_rsrc(static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h, qbytes);
@@ -287,7 +334,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
         part = fmaf(bf16_hi(dv.w), ov[7], part);
       }
       dl[qt] = xsum16(part);
-      const int64_t hrow = (static_cast<int64_t>(b) * a.hq + h) * a.n;
       float L = t < a.n ? a.lse[hrow + t] : -INFINITY;
       // a query without weights (no key, or past the end) gets P = 0
       lse2[qt] = L > -INFINITY ? L * kLog2e : INFINITY;
@@ -328,15 +374,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
 
   if (a.dbpart)
     for (int e = lane; e < a.k_max; e += 64) lds_db[w][e] = 0.f;
-  const int nraw = n * nsub;
+  // entmax: per query column the sums over its keys of t^(1/(alpha-1)) (the
+  // normaliser Z), of g dP and of g (g = t^((2-alpha)/(alpha-1)))
+  const float a1s = (a.alpha - 1.f) * a.sm_scale;
+  const float ib = 1.f / (a.alpha - 1.f), ig = (2.f - a.alpha) / (a.alpha - 1.f);
+  float zs[QT], gds[QT], gs[QT], zf[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) zs[qt] = gds[qt] = gs[qt] = zf[qt] = 0.f;
+  // entmax: all causal tiles, walked twice
+  const int nraw = ENT ? static_cast<int>(qmax / 64) + 1 : n * nsub;
+  // one walk over the tiles; entmax runs the gathering walk (0) first
+  auto walk_pass = [&](auto pass_c) {
+  constexpr int pass = decltype(pass_c)::value;
   for (int base = 0; base < nraw; base += kMaxTilesBwd) {
     if (w == 0) {
       int c = 0;
       for (int r = 0; r < kMaxTilesBwd && base + r < nraw; r += 64) {
         const int T = base + r + lane;
-        int64_t k0 = T >= nraw ? -1 : walk.key0(T);
+        int64_t k0 = T >= nraw ? -1 : (ENT ? 64 * static_cast<int64_t>(T) : walk.key0(T));
         float tb = 0.f;
-        if (a.wsel && k0 >= 0) {
+        if (!ENT && a.wsel && k0 >= 0) {
           // the prior: sigma ln w of the tile's block, dropped when w <= 0
           const float wv = a.wsel[rowid * a.k_max + T / nsub];
           if (wv > 0.f)
@@ -407,27 +464,44 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
             f32x4 ds;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              float p = __builtin_amdgcn_exp2f(fmaf(s[qt][j], sc, eoff[qt]));
-              if (diag && rel0 + kt * 16 + j - qt * 16 > 0) p = 0.f;  // key after query
-              ds[j] = p * (dp[qt][j] - dl[qt]);
-              dbs += ds[j];
+              const bool masked = diag && rel0 + kt * 16 + j - qt * 16 > 0;  // key after query
+              if constexpr (ENT) {
+                const float tt = fmaf(s[qt][j], a1s, -lse2[qt]);
+                float pb = 0.f, pg = 0.f;
+                if (tt > 0.f && !masked) ent_pow(tt, a.alpha, ib, ig, pb, pg);
+                if constexpr (pass == 0) {
+                  zs[qt] += pb;
+                  gds[qt] = fmaf(pg, dp[qt][j], gds[qt]);
+                  gs[qt] += pg;
+                }
+                if constexpr (pass == 1) ds[j] = zf[qt] * pg * (dp[qt][j] - dl[qt]);
+              } else {
+                float p = __builtin_amdgcn_exp2f(fmaf(s[qt][j], sc, eoff[qt]));
+                if (masked) p = 0.f;
+                ds[j] = p * (dp[qt][j] - dl[qt]);
+                dbs += ds[j];
+              }
             }
-            if (kt & 1)
-              dsf[qt][kt >> 1] = pack_frag(dsp[qt], ds);
-            else
-              dsp[qt] = ds;
+            if constexpr (pass == 1) {
+              if (kt & 1)
+                dsf[qt][kt >> 1] = pack_frag(dsp[qt], ds);
+              else
+                dsp[qt] = ds;
+            }
           }
         }
         // dQ^T += K^T dS^T
+        if constexpr (pass == 1) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+          for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const uint4 kf = tr_frag<D>(kt_, kk, dt, lane);
+            for (int dt = 0; dt < DT; ++dt) {
+              const uint4 kf = tr_frag<D>(kt_, kk, dt, lane);
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) acc[dt][qt] = mfma16(kf, dsf[qt][kk], acc[dt][qt]);
-          }
-        if (a.dbpart) {
+              for (int qt = 0; qt < QT; ++qt) acc[dt][qt] = mfma16(kf, dsf[qt][kk], acc[dt][qt]);
+            }
+        }
+        if (!ENT && a.dbpart) {
           // this unit's part of dL/d(bias) of the tile's list entry (a block
           // of two tiles adds twice)
           dbs = wave_sum(dbs);
@@ -439,6 +513,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
       buf ^= 1;
     }
   }
+  if constexpr (ENT && pass == 0) {
+    // each query's normaliser and VJP mean, shared with the key side
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float z = xsum16(zs[qt]), gsum = xsum16(gs[qt]), gd = xsum16(gds[qt]);
+      dl[qt] = gsum > 0.f ? gd / gsum : 0.f;
+      // g = (t^(1/(alpha-1)) / Z)^(2-alpha) = t^((2-alpha)/(alpha-1)) Z^(alpha-2)
+      zf[qt] = z > 0.f ? __builtin_amdgcn_exp2f((a.alpha - 2.f) * __log2f(z)) : 0.f;
+      const int64_t t = qpos0 + qt * 16 + (lane & 15);
+      if (active && lane < 16 && t < a.n) {
+        a.delta[hrow + t] = dl[qt];
+        a.zbuf[hrow + t] = z;
+      }
+    }
+  }
+  };
+  if constexpr (ENT) walk_pass(std::integral_constant<int, 0>{});
+  walk_pass(std::integral_constant<int, 1>{});
 
   if (!active) return;
   if (a.dbpart)
@@ -476,7 +568,9 @@ struct DkvLds {
 constexpr int kMaxChunk = 64;
 
 // NW = B / 16 wavefronts, wave w owning keys 16w .. 16w+15 of the block.
-template <int D, int NW>
+// ENT: the token-level entmax attention; one item per (KV head, key block),
+// its rows every query block from the key block on (dense causal).
+template <int D, int NW, bool ENT>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   constexpr int NT = NW * 64;
   constexpr int KS = D / 32;
@@ -488,11 +582,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   __shared__ DkvLds<D> lds;
   __shared__ int rows[kMaxChunk];
   __shared__ float rbias[kMaxChunk];  // prior bias of block j in each row, score units
+  __shared__ float lds_iz[ENT ? 2 : 1][64];  // entmax: 1 / Z of each query
+  __shared__ float lds_zf[ENT ? 2 : 1][64];  // entmax: Z^(alpha-2)
   __shared__ int lds_nr;
 
-  if (static_cast<int>(blockIdx.x) >= a.counters[0]) return;
-  const int4 item = a.items[blockIdx.x];
-  const int pair = item.x, j = item.y, chunk = item.z, slot = item.w;
+  int pair, j, chunk = 0, slot = -1;
+  if constexpr (ENT) {
+    // key blocks near the start have the most rows: they go first
+    const int npair = a.batch * a.hkv;
+    j = static_cast<int>(blockIdx.x / npair);
+    pair = static_cast<int>(blockIdx.x % npair);
+  } else {
+    if (static_cast<int>(blockIdx.x) >= a.counters[0]) return;
+    const int4 item = a.items[blockIdx.x];
+    pair = item.x;
+    j = item.y;
+    chunk = item.z;
+    slot = item.w;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -501,7 +608,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
 
   // rows of this chunk: ranks [chunk * a.chunk, +a.chunk) among the set bits
   // of block j's column, ascending
-  if (w == 0) {
+  if (ENT) {
+    if (tid == 0) lds_nr = a.nrow - j;
+  } else if (w == 0) {
     const int lo = chunk * a.chunk, hi = lo + a.chunk;
     const uint32_t* col = a.bits + static_cast<int64_t>(pair) * a.nwords * a.nblk + j;
     int base = 0;
@@ -547,7 +656,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   }
   __syncthreads();
   const int nr = lds_nr;
-  if (a.wsel) {
+  if (!ENT && a.wsel) {
     // the routing weight of block j in each row's list: 8 threads per row
     // scan the entries (a row lists j once; rows only hold j when w > 0)
     for (int i = tid / 8; i < nr; i += NT / 8) {
@@ -564,13 +673,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   const float sc = a.sm_scale * kLog2e;
 
   uint4 qreg[QITEMS], oreg[QITEMS];
-  float lreg = 0.f, dreg = 0.f;
+  float lreg = 0.f, dreg = 0.f, zreg = 0.f;
   // unit u -> query head and first query position
   auto unit_of = [&](int uu, int& h, int64_t& t0) {
     const int qq = uu % qtiles;
     const int rest = uu / qtiles;
     h = g * G + rest % G;
-    t0 = static_cast<int64_t>(rows[rest / G]) * B + qq * 64;
+    t0 = static_cast<int64_t>(ENT ? j + rest / G : rows[rest / G]) * B + qq * 64;
   };
   auto load_unit = [&](int uu) {
     int h;
@@ -593,8 +702,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
     if (tid < 64) {
       const int64_t t = t0 + tid;
       const int64_t hrow = (static_cast<int64_t>(b) * a.hq + h) * a.n;
-      const float L = t < a.n ? a.lse[hrow + t] : -INFINITY;
-      lreg = L > -INFINITY ? L * kLog2e : INFINITY;
+      if constexpr (ENT) {
+        lreg = t < a.n ? a.tau[hrow + t] : INFINITY;  // past the end: no support
+        zreg = t < a.n ? a.zbuf[hrow + t] : 0.f;
+      } else {
+        const float L = t < a.n ? a.lse[hrow + t] : -INFINITY;
+        lreg = L > -INFINITY ? L * kLog2e : INFINITY;
+      }
       dreg = t < a.n ? a.delta[hrow + t] : 0.f;
     }
   };
@@ -611,6 +725,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
     if (tid < 64) {
       lds.lse2[buf][tid] = lreg;
       lds.dl[buf][tid] = dreg;
+      if constexpr (ENT) {
+        lds_iz[buf][tid] = zreg > 0.f ? 1.f / zreg : 0.f;
+        lds_zf[buf][tid] = zreg > 0.f ? __builtin_amdgcn_exp2f((a.alpha - 2.f) * __log2f(zreg)) : 0.f;
+      }
     }
   };
 
@@ -647,20 +765,41 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
         }
       const bool diag = key0 + 15 > t0;
       const int64_t rel0 = key0 + (lane & 15) - t0 - (lane >> 4) * 4;  // key - query at qt = e = 0
-      const float tbs = a.wsel ? rbias[uu / qtiles / G] * sc : 0.f;  // the row's prior bias
+      const float tbs = !ENT && a.wsel ? rbias[uu / qtiles / G] * sc : 0.f;  // the row's prior bias
+      const float a1s = (a.alpha - 1.f) * a.sm_scale;
+      const float ib = 1.f / (a.alpha - 1.f), ig = (2.f - a.alpha) / (a.alpha - 1.f);
       f32x4 p[4], ds[4];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
-        const float4 L = *reinterpret_cast<const float4*>(&lds.lse2[buf][qt * 16 + (lane >> 4) * 4]);
-        const float4 Dl = *reinterpret_cast<const float4*>(&lds.dl[buf][qt * 16 + (lane >> 4) * 4]);
+        const int qo = qt * 16 + (lane >> 4) * 4;
+        const float4 L = *reinterpret_cast<const float4*>(&lds.lse2[buf][qo]);
+        const float4 Dl = *reinterpret_cast<const float4*>(&lds.dl[buf][qo]);
         const float Lv[4] = {L.x, L.y, L.z, L.w};
         const float Dv[4] = {Dl.x, Dl.y, Dl.z, Dl.w};
+        float Iz[4] = {0.f, 0.f, 0.f, 0.f}, Zf[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (ENT) {
+          const float4 iz = *reinterpret_cast<const float4*>(&lds_iz[buf][qo]);
+          const float4 zf = *reinterpret_cast<const float4*>(&lds_zf[buf][qo]);
+          Iz[0] = iz.x; Iz[1] = iz.y; Iz[2] = iz.z; Iz[3] = iz.w;
+          Zf[0] = zf.x; Zf[1] = zf.y; Zf[2] = zf.z; Zf[3] = zf.w;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[qt][e], sc, tbs - Lv[e]));
-          if (diag && rel0 - qt * 16 - e > 0) pv = 0.f;  // key after query
-          p[qt][e] = pv;
-          ds[qt][e] = pv * (dp[qt][e] - Dv[e]);
+          const bool masked = diag && rel0 - qt * 16 - e > 0;  // key after query
+          if constexpr (ENT) {
+            // entmax weights from tau (x units): p = t^(1/(alpha-1)) / Z and
+            // dz = Z^(alpha-2) t^((2-alpha)/(alpha-1)) (dP - <g, dP> / sum g)
+            const float tt = fmaf(s[qt][e], a1s, -Lv[e]);
+            float pb = 0.f, pg = 0.f;
+            if (tt > 0.f && !masked) ent_pow(tt, a.alpha, ib, ig, pb, pg);
+            p[qt][e] = pb * Iz[e];
+            ds[qt][e] = Zf[e] * pg * (dp[qt][e] - Dv[e]);
+          } else {
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[qt][e], sc, tbs - Lv[e]));
+            if (masked) pv = 0.f;
+            p[qt][e] = pv;
+            ds[qt][e] = pv * (dp[qt][e] - Dv[e]);
+          }
         }
       }
 #pragma unroll
@@ -773,12 +912,19 @@ hipError_t bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   const int G = a.hq / a.hkv;
   const int units = G * (a.B / (16 * QT));
   const int wpb = (units + NW - 1) / NW;
-  hipLaunchKernelGGL((bwd_dq<D, QT, NW>), dim3(static_cast<unsigned>(npair) * a.nrow * wpb),
-                     dim3(NW * 64), 0, stream, a, wpb);
+  const dim3 gq(static_cast<unsigned>(npair) * a.nrow * wpb);
+  if (a.ent) {
+    // token-level entmax attention: B = 64 rows, dense causal
+    hipLaunchKernelGGL((bwd_dq<D, QT, NW, true>), gq, dim3(NW * 64), 0, stream, a, wpb);
+    hipLaunchKernelGGL((bwd_dkv<D, 4, true>), dim3(static_cast<unsigned>(npair) * a.nblk),
+                       dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((bwd_dq<D, QT, NW, false>), gq, dim3(NW * 64), 0, stream, a, wpb);
   if (a.B == 64)
-    hipLaunchKernelGGL((bwd_dkv<D, 4>), dim3(a.max_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkv<D, 4, false>), dim3(a.max_items), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_dkv<D, 8>), dim3(a.max_items), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkv<D, 8, false>), dim3(a.max_items), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -789,6 +935,7 @@ int attend_bwd_max_prior_width() { return kMaxPriorEntries; }
 
 hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream) {
   const unsigned npair = static_cast<unsigned>(a.batch) * a.hkv;
+  if (a.ent) return a.d == 64 ? bwd_bf16<64>(a, stream) : bwd_bf16<128>(a, stream);
   hipLaunchKernelGGL(bwd_mark, dim3(npair * a.nwords), dim3(256), a.nblk * sizeof(uint32_t), stream, a);
   hipLaunchKernelGGL(bwd_plan, dim3(1), dim3(kPlanThreads), 0, stream, a);
   hipError_t e = hipGetLastError();

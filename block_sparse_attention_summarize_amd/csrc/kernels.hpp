@@ -159,6 +159,14 @@ struct BwdArgs {
   int64_t n;
   float sm_scale;
   bool bf16, o_f32, g_f32;
+  // token-level entmax attention (dense causal, B = 64; idx, cnt, the plan
+  // and lse unused): tau per query [batch, hq, n] in units of
+  // x = (alpha - 1) sm_scale q.k; zbuf (workspace [batch, hq, n]) receives
+  // each query's normaliser, delta its <g, dP> / sum g
+  bool ent;
+  float alpha;
+  const float* tau;
+  float* zbuf;
 };
 int attend_bwd_units(int group, int B);  // units per row of the query side
 int attend_bwd_max_prior_width();        // k_max limit when dL/dw is requested

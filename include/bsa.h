@@ -30,7 +30,8 @@
  *                               masks of 64-query tiles.
  *            bsa_attend_entmax  token-level alpha-entmax attention
  *                               ("AdaSplash-2"), dense causal, zero tiles
- *                               skipped.
+ *                               skipped; bsa_attend_entmax_backward its
+ *                               gradients.
  *   Decode   bsa_decode_topk    Stage 1 (top-k) and Stage 2 for one decode
  *                               step in a single launch (bsa_decode_topk_paged,
  *                               bsa_summarize_blocks_paged: the same over a
@@ -106,7 +107,8 @@ typedef enum {
   BSA_OP_DECODE_TOPK = 5,
   BSA_OP_ATTEND_PREFILL_PRIOR = 6, /* bsa_attend_prefill with wsel != NULL */
   BSA_OP_ATTEND_BACKWARD = 7,      /* bsa_attend_backward; k_or_cap = k_max */
-  BSA_OP_ROUTE_ENTMAX_BACKWARD = 8 /* bsa_route_entmax_backward */
+  BSA_OP_ROUTE_ENTMAX_BACKWARD = 8, /* bsa_route_entmax_backward */
+  BSA_OP_ATTEND_ENTMAX_BACKWARD = 9  /* bsa_attend_entmax_backward */
 } bsa_op;
 
 /* Problem description, read only during the call. */
@@ -375,6 +377,33 @@ int bsa_route_entmax_backward(const bsa_shape *shape, const void *Q, const float
 int bsa_attend_entmax(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                       float alpha, int32_t refine, float sm_scale, void *O, int32_t o_dtype,
                       float *tau_out, void *stream);
+
+/*
+ * Backward of the token-level alpha-entmax attention ("AdaSplash-2",
+ * sections 1 and 4: entmax attention is trained, and its backward skips the
+ * zero blocks).  With the forward's threshold tau_t (tau_out, x units), the
+ * weights of query t are recomputed as p_j = [x_j - tau_t]_+^(1/(alpha-1)) / Z_t
+ * (Z_t their sum) and, with dP_j = dO_t . v_j and g = p^(2-alpha) on the
+ * support, the entmax vector-Jacobian product gives
+ *   dz_j = g_j (dP_j - <g, dP> / sum g),   z_j = sm_scale q_t . k_j,
+ *   dQ_t = sm_scale sum_j dz_j k_j,  dK_j = sm_scale sum_t dz_tj q_t,
+ *   dV_j = sum_t p_tj dO_t  (key sums over the group's query heads).
+ * A first walk over each query's causal key tiles gathers Z and <g, dP> /
+ * sum g, a second forms dQ; the key side walks the query tiles from each key
+ * tile on.  Products for keys outside every support of a tile are zero.
+ *   Q, K, V bf16 [batch, H, N, d] as given to bsa_attend_entmax (shape with
+ *         mode BSA_PREFILL, block 64); alpha in (1, 2]; sm_scale 0: 1/sqrt(d).
+ *   dO    bf16 [batch, Hq, N, d] with o_stride.
+ *   tau   fp32 [batch, Hq, N]: tau_out of bsa_attend_entmax.
+ *   dQ, dK, dV  out, g_dtype (bf16 or BSA_F32), strides of Q, K, V.
+ *   ws    bsa_workspace_size(BSA_OP_ATTEND_ENTMAX_BACKWARD, shape, 0) bytes.
+ * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED (fp32 inputs, block != 64,
+ * alpha > 2, strides), BSA_ERR_WORKSPACE.
+ */
+int bsa_attend_entmax_backward(const bsa_shape *shape, const void *Q, const void *K,
+                               const void *V, const void *dO, const float *tau, float alpha,
+                               float sm_scale, void *dQ, void *dK, void *dV, int32_t g_dtype,
+                               void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Active-block masks of per-token selections ("DashAttention", Estágio 2,

@@ -83,3 +83,62 @@ def test_entmax_attention_argument_errors():
         bsa.attend_entmax(x["Q"], x["K"], x["V"], 1.5, refine=9)
     with pytest.raises(bsa.BsaError, match="bf16"):
         bsa.attend_entmax(x["Q"].float(), x["K"].float(), x["V"].float(), 1.5)
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+BWD_TOL = 1e-2  # of each gradient tensor's largest magnitude (as the block-sparse backward)
+
+
+def _check_grad(name, g, ref, bf16_out):
+    g = _cpu(g).astype(np.float64).reshape(ref.shape)
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    err = np.abs(g - ref)
+    bound = BWD_TOL * scale + (parity.half_ulp_bf16(ref) if bf16_out else 0.0)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, (f"{name}: {len(bad)} out of bounds, first {bad[0].tolist()}: "
+                           f"{g[tuple(bad[0])]} vs {ref[tuple(bad[0])]} (scale {scale:.3g})")
+    return float((err / scale).max())
+
+
+@pytest.mark.parametrize("name", ["a15_gqa", "a2_sparsemax", "a125", "a175_newton", "a15_d64"])
+@pytest.mark.parametrize("g_f32", [True, False])
+def test_entmax_attention_backward_matches_oracle(name, g_f32):
+    """dQ, dK, dV from the forward's tau against the oracle's gradients with
+    exact thresholds."""
+    w = CASES[name]
+    print(f"[entmax attention backward] {name} g_f32={g_f32}", flush=True)
+    x = parity.make(w)
+    do_st, do = synth.gen_stored(w, "do")
+    dO = parity.to_device(do_st, w.dtype)
+    O, tau = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=2, want_tau=True)
+    grads = bsa.attend_entmax_backward(x["Q"], x["K"], x["V"], dO, tau, w.alpha,
+                                       grad_dtype=torch.float32 if g_f32 else None)
+    torch.cuda.synchronize()
+    refs = oracle.entmax_attend_backward(x["q"], x["k"], x["v"], do, w.alpha)
+    e = [_check_grad(nm, g, r, not g_f32) for nm, g, r in zip(("dQ", "dK", "dV"), grads, refs)]
+    print("max err / scale: dQ %.2e dK %.2e dV %.2e" % tuple(e))
+
+
+def test_entmax_attention_backward_sums_and_determinism():
+    """The key gradients of a KV head sum to zero and the value gradients to
+    the upstream gradients (entmax weights sum to one); two calls agree."""
+    w = CASES["a15_gqa"]
+    x = parity.make(w)
+    dO = torch.randn(x["Q"].shape, generator=torch.Generator().manual_seed(9)).to(
+        "cuda", torch.bfloat16)
+    _, tau = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, want_tau=True)
+    g1 = bsa.attend_entmax_backward(x["Q"], x["K"], x["V"], dO, tau, w.alpha,
+                                    grad_dtype=torch.float32)
+    g2 = bsa.attend_entmax_backward(x["Q"], x["K"], x["V"], dO, tau, w.alpha,
+                                    grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    dK, dV = g1[1].double(), g1[2].double()
+    assert float(dK.sum(dim=2).abs().max()) <= 1e-3 * float(dK.abs().sum(dim=2).max())
+    G = w.hq // w.hkv
+    ref = dO.double().reshape(1, w.hkv, G, w.n, w.d).sum(dim=(2, 3))
+    assert float((dV.sum(dim=2) - ref).abs().max()) <= 1e-2 * float(ref.abs().max())
