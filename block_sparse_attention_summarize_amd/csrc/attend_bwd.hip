@@ -441,6 +441,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
         const int rel0 = k0 - qpos0 + (lane >> 4) * 4 - (lane & 15);
         uint4 dsf[QT][2];
         f32x4 dsp[QT];
+        bool pair_live[2];
+        bool live_pair = false;  // entmax: some weight in the current pair of slices
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           f32x4 s[QT], dp[QT];
@@ -449,14 +451,54 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
             s[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
             dp[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
+          if constexpr (ENT && pass == 0) {
+            // S first: a 16-key slice outside every support of the wave's
+            // queries has no dP, dz or dQ work (zero blocks skipped)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const uint4 kf = row_frag<D>(kt_, kt, ks, lane);
-            const uint4 vf = row_frag<D>(vt_, kt, ks, lane);
+            for (int ks = 0; ks < KS; ++ks) {
+              const uint4 kf = row_frag<D>(kt_, kt, ks, lane);
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) {
-              s[qt] = mfma16(kf, qf[qt][ks], s[qt]);
-              dp[qt] = mfma16(vf, df[qt][ks], dp[qt]);
+              for (int qt = 0; qt < QT; ++qt) s[qt] = mfma16(kf, qf[qt][ks], s[qt]);
+            }
+            bool any = false;
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                any |= fmaf(s[qt][j], a1s, -lse2[qt]) > 0.f &&
+                       !(diag && rel0 + kt * 16 + j - qt * 16 > 0);
+            const bool live = __ballot(any) != 0;
+            live_pair = (kt & 1) ? (live_pair || live) : live;
+            if (live) {
+#pragma unroll
+              for (int ks = 0; ks < KS; ++ks) {
+                const uint4 vf = row_frag<D>(vt_, kt, ks, lane);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) dp[qt] = mfma16(vf, df[qt][ks], dp[qt]);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              const uint4 kf = row_frag<D>(kt_, kt, ks, lane);
+              const uint4 vf = row_frag<D>(vt_, kt, ks, lane);
+#pragma unroll
+              for (int qt = 0; qt < QT; ++qt) {
+                s[qt] = mfma16(kf, qf[qt][ks], s[qt]);
+                dp[qt] = mfma16(vf, df[qt][ks], dp[qt]);
+              }
+            }
+            if constexpr (ENT) {
+              // the dQ products of a pair of slices outside every support are skipped
+              bool any = false;
+#pragma unroll
+              for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                  any |= fmaf(s[qt][j], a1s, -lse2[qt]) > 0.f &&
+                         !(diag && rel0 + kt * 16 + j - qt * 16 > 0);
+              const bool live = __ballot(any) != 0;
+              live_pair = (kt & 1) ? (live_pair || live) : live;
             }
           }
 #pragma unroll
@@ -489,17 +531,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
                 dsp[qt] = ds;
             }
           }
+          if (kt & 1) pair_live[kt >> 1] = !ENT || live_pair;
         }
         // dQ^T += K^T dS^T
         if constexpr (pass == 1) {
 #pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
+          for (int kk = 0; kk < 2; ++kk) {
+            if (!pair_live[kk]) continue;  // entmax: both slices outside every support
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
               const uint4 kf = tr_frag<D>(kt_, kk, dt, lane);
 #pragma unroll
               for (int qt = 0; qt < QT; ++qt) acc[dt][qt] = mfma16(kf, dsf[qt][kk], acc[dt][qt]);
             }
+          }
         }
         if (!ENT && a.dbpart) {
           // this unit's part of dL/d(bias) of the tile's list entry (a block
@@ -756,15 +801,41 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
         s[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
         dp[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-          s[qt] = mfma16(row_frag<D>(qt_, qt, ks, lane), kf[ks], s[qt]);
-          dp[qt] = mfma16(row_frag<D>(ot_, qt, ks, lane), vf[ks], dp[qt]);
-        }
       const bool diag = key0 + 15 > t0;
       const int64_t rel0 = key0 + (lane & 15) - t0 - (lane >> 4) * 4;  // key - query at qt = e = 0
+      bool live = true;
+      if constexpr (ENT) {
+        // S first: keys outside every support of the tile's queries have no
+        // dP, dV or dK work (zero blocks skipped)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) s[qt] = mfma16(row_frag<D>(qt_, qt, ks, lane), kf[ks], s[qt]);
+        const float a1s_ = (a.alpha - 1.f) * a.sm_scale;
+        bool any = false;
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          const float4 L = *reinterpret_cast<const float4*>(&lds.lse2[buf][qt * 16 + (lane >> 4) * 4]);
+          const float Lv[4] = {L.x, L.y, L.z, L.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            any |= fmaf(s[qt][e], a1s_, -Lv[e]) > 0.f && !(diag && rel0 - qt * 16 - e > 0);
+        }
+        live = __ballot(any) != 0;
+        if (live)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) dp[qt] = mfma16(row_frag<D>(ot_, qt, ks, lane), vf[ks], dp[qt]);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) {
+            s[qt] = mfma16(row_frag<D>(qt_, qt, ks, lane), kf[ks], s[qt]);
+            dp[qt] = mfma16(row_frag<D>(ot_, qt, ks, lane), vf[ks], dp[qt]);
+          }
+      }
       const float tbs = !ENT && a.wsel ? rbias[uu / qtiles / G] * sc : 0.f;  // the row's prior bias
       const float a1s = (a.alpha - 1.f) * a.sm_scale;
       const float ib = 1.f / (a.alpha - 1.f), ig = (2.f - a.alpha) / (a.alpha - 1.f);
@@ -804,6 +875,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
+        if (!live) break;
         const uint4 pf = pack_frag(p[2 * kk], p[2 * kk + 1]);
         const uint4 sf = pack_frag(ds[2 * kk], ds[2 * kk + 1]);
 #pragma unroll
