@@ -65,12 +65,12 @@ def _load():
                                    P, I, P, P, P, D]
         lib.orc_token_union.argtypes = [P, P, I, I, I, I, I, P, P, P]
         lib.orc_entmax_attend.argtypes = [P, P, P, I, I, I, I, I, D, D, P, I, P, P, P]
-        lib.orc_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, I, P, P, I, D, P, P, D, P,
-                                            P, P, P]
+        lib.orc_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, I, ctypes.c_int, P, P, I,
+                                            D, P, P, D, P, P, P, P]
         lib.orc_entmax_vjp.argtypes = [P, P, I, D, P]
         lib.orc_entmax_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, D, D, P, P, P]
-        lib.orc_route_entmax_backward.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, D, D, D,
-                                                  ctypes.c_uint32, P, P]
+        lib.orc_route_entmax_backward.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I,
+                                                  ctypes.c_int, D, D, D, ctypes.c_uint32, P, P]
         lib.orc_version.restype = ctypes.c_char_p
         _lib = lib
     return _lib
@@ -252,10 +252,11 @@ def entmax_attend(Q, K, V, alpha, req=None, sm_scale=None):
 
 
 def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None, rowmask=None, wsel=None,
-                    sigma=0.0):
+                    sigma=0.0, mode=MODE_PREFILL):
     """Gradients (dQ, dK, dV) in fp64 of the causal block-sparse attention
-    (prefill rows, selection idx/cnt per query block) for upstream dO.
-    rowmask [nb, hkv, nrow] (bool): only those query blocks contribute.
+    (prefill rows, selection idx/cnt per query block; mode=MODE_TOKEN:
+    per query token) for upstream dO.
+    rowmask [nb, hkv, nrow] (bool): only those selection rows contribute.
     wsel, sigma: the prior-induced softmax; then (dQ, dK, dV, dwsel) with
     dwsel = dL/dw in the layout of idx."""
     Q, K, V, dO = _f32(Q), _f32(K), _f32(V), _f32(dO)
@@ -277,7 +278,7 @@ def attend_backward(Q, K, V, dO, B, idx, cnt, sm_scale=None, rowmask=None, wsel=
         assert wsel.shape == idx.shape
         dwsel = np.empty(idx.shape, np.float64)
     _load().orc_attend_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), nb, hq, hkv, n, d, B,
-                                _ptr(idx), _ptr(cnt), idx.shape[-1], float(sm_scale),
+                                int(mode), _ptr(idx), _ptr(cnt), idx.shape[-1], float(sm_scale),
                                 _ptr(rowmask), _ptr(wsel), float(sigma), _ptr(dwsel), _ptr(dQ),
                                 _ptr(dK), _ptr(dV))
     return (dQ, dK, dV) if wsel is None else (dQ, dK, dV, dwsel)
@@ -311,8 +312,9 @@ def entmax_vjp(p, dp, alpha):
 
 
 def route_entmax_backward(qhat, S, probs, idx, cnt, dwsel, n, B, alpha, gamma,
-                          score_scale=None, force=FORCE_DIAG):
-    """Routing part of the gradient (prefill block rows): dL/dQ and dL/dK in
+                          score_scale=None, force=FORCE_DIAG, mode=MODE_PREFILL):
+    """Routing part of the gradient (prefill block rows; mode=MODE_TOKEN: a
+    row per query token, qhat the queries themselves): dL/dQ and dL/dK in
     fp64 through qhat -> logits -> entmax -> group mean w, given dL/dw."""
     qhat, S, probs, dwsel = _f64(qhat), _f64(S), _f64(probs), _f64(dwsel)
     nb, hq, nrow, d = qhat.shape
@@ -325,7 +327,8 @@ def route_entmax_backward(qhat, S, probs, idx, cnt, dwsel, n, B, alpha, gamma,
     dK = np.empty((nb, hkv, n, d), np.float64)
     _load().orc_route_entmax_backward(_ptr(qhat), _ptr(S), _ptr(probs), _ptr(idx), _ptr(cnt),
                                       idx.shape[-1], _ptr(dwsel), nb, hq, hkv, n, d, B,
-                                      float(alpha), float(gamma), float(score_scale), force,
+                                      int(mode), float(alpha), float(gamma), float(score_scale),
+                                      force,
                                       _ptr(dQ), _ptr(dK))
     return dQ, dK
 

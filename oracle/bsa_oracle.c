@@ -804,7 +804,10 @@ void orc_entmax_attend(const float *Q, const float *K, const float *V, int64_t n
  *   dK_u += sm_scale ds_u q_t,  dV_u += p_u dO_t   (KV head h / G: the
  *   group's query heads add into the same dK, dV).
  *   Q, dO : [nb, hq, n, d];  K, V : [nb, hkv, n, d] (fp32); idx/cnt per query
- *   block.  dQ [nb, hq, n, d], dK, dV [nb, hkv, n, d]: fp64, overwritten.
+ *   block (mode ORC_MODE_PREFILL) or per query token (ORC_MODE_TOKEN, the
+ *   per-token selections of "DashAttention", Estágio 1: row t lists the blocks
+ *   query t attends).  dQ [nb, hq, n, d], dK, dV [nb, hkv, n, d]: fp64,
+ *   overwritten.
  *   rowmask: NULL, or [nb, hkv, nrow] bytes; then only the queries of the
  *   query blocks whose byte is nonzero contribute (a sample: dQ of those
  *   queries, and dK, dV of every key block all of whose selecting rows are
@@ -817,11 +820,12 @@ void orc_entmax_attend(const float *Q, const float *K, const float *V, int64_t n
  */
 void orc_attend_backward(const float *Q, const float *K, const float *V, const float *dO,
                          int64_t nb, int64_t hq, int64_t hkv, int64_t n, int64_t d, int64_t B,
-                         const int32_t *idx, const int32_t *cnt, int64_t kmax, double sm_scale,
-                         const uint8_t *rowmask, const double *wsel, double sigma, double *dwsel,
-                         double *dQ, double *dK, double *dV) {
+                         int mode, const int32_t *idx, const int32_t *cnt, int64_t kmax,
+                         double sm_scale, const uint8_t *rowmask, const double *wsel,
+                         double sigma, double *dwsel, double *dQ, double *dK, double *dV) {
   int64_t G = hq / hkv;
-  int64_t nrow = (n + B - 1) / B;
+  int64_t rq = mode == ORC_MODE_TOKEN ? 1 : B; /* queries per selection row */
+  int64_t nrow = (n + rq - 1) / rq;
   int64_t cap = kmax * B + 1;
   double *p = (double *)malloc(sizeof(double) * (size_t)cap);
   int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
@@ -835,7 +839,7 @@ void orc_attend_backward(const float *Q, const float *K, const float *V, const f
     for (int64_t h = 0; h < hq; ++h)
       for (int64_t t = 0; t < n; ++t) {
         int64_t g = h / G;
-        int64_t rowid = (b * hkv + g) * nrow + t / B;
+        int64_t rowid = (b * hkv + g) * nrow + t / rq;
         if (rowmask && !rowmask[rowid]) continue;
         const float *qv = Q + ((b * hq + h) * n + t) * d;
         const float *gv = dO + ((b * hq + h) * n + t) * d;
@@ -923,7 +927,9 @@ void orc_entmax_vjp(const double *p, const double *dp, int64_t n, double alpha, 
 
 /*
  * Gradient of the loss through the entmax routing of prefill block rows
- * (orc_route_entmax, mode prefill) given dL/dw for the listed blocks
+ * (orc_route_entmax, mode prefill) or of every query token (mode token: the
+ * row's routing query is the token's own query and its own block is the
+ * diagonal) given dL/dw for the listed blocks
  * (dwsel, layout of idx; from orc_attend_backward).  The listed routed
  * (not forced) block j of row r has w_j = (1/G) sum_h p_hj, so head h's
  * probabilities get dp_hj = dw_j / G (0 for blocks not listed, e.g. cut by
@@ -933,7 +939,8 @@ void orc_entmax_vjp(const double *p, const double *dp, int64_t n, double alpha, 
  *   dS_j   += gamma * score_scale * sum_{h in group, r} dz_hj qhat_h,
  * and the mean pools (qhat = mean of the row's queries, S = mean of the
  * block's keys, q-bar = 0) spread them evenly: dQ_t = dqhat_row(t) / n_row,
- * dK_u = dS_block(u) / n_block (n = the block's token count).
+ * dK_u = dS_block(u) / n_block (n = the block's token count; a token row has
+ * n_row = 1).
  *   qhat [nb, hq, nrow, d], S [nb, hkv, nblk, d], probs [nb, hq, nrow, nblk]
  *   (fp64, from orc_qpool / orc_summarize / orc_route_entmax);
  *   dQ [nb, hq, n, d], dK [nb, hkv, n, d]: fp64, overwritten with the
@@ -942,10 +949,12 @@ void orc_entmax_vjp(const double *p, const double *dp, int64_t n, double alpha, 
 void orc_route_entmax_backward(const double *qhat, const double *S, const double *probs,
                                const int32_t *idx, const int32_t *cnt, int64_t idx_width,
                                const double *dwsel, int64_t nb, int64_t hq, int64_t hkv,
-                               int64_t n, int64_t d, int64_t B, double alpha, double gamma,
-                               double score_scale, uint32_t force, double *dQ, double *dK) {
+                               int64_t n, int64_t d, int64_t B, int mode, double alpha,
+                               double gamma, double score_scale, uint32_t force, double *dQ,
+                               double *dK) {
   int64_t G = hq / hkv;
-  int64_t nrow = (n + B - 1) / B, nblk = nrow;
+  int64_t rq = mode == ORC_MODE_TOKEN ? 1 : B; /* queries pooled per row */
+  int64_t nrow = (n + rq - 1) / rq, nblk = (n + B - 1) / B;
   double *dp = (double *)malloc(sizeof(double) * (size_t)nblk);
   double *pc = (double *)malloc(sizeof(double) * (size_t)nblk);
   double *dz = (double *)malloc(sizeof(double) * (size_t)nblk);
@@ -959,7 +968,8 @@ void orc_route_entmax_backward(const double *qhat, const double *S, const double
         int64_t g = h / G;
         int64_t forced[3];
         int nforced = 0;
-        int64_t cend = row_setup(ORC_MODE_PREFILL, 1, r, 0, B, force, forced, &nforced);
+        int64_t cend = row_setup(mode == ORC_MODE_TOKEN ? ORC_MODE_TOKEN : ORC_MODE_PREFILL, 1, r,
+                                 0, B, force, forced, &nforced);
         int64_t rowid = (b * hkv + g) * nrow + r, hrow = (b * hq + h) * nrow + r;
         for (int64_t j = 0; j < nblk; ++j) dp[j] = 0.0;
         for (int64_t a = 0; a < cnt[rowid]; ++a) {
@@ -993,7 +1003,7 @@ void orc_route_entmax_backward(const double *qhat, const double *S, const double
   for (int64_t b = 0; b < nb; ++b) {
     for (int64_t h = 0; h < hq; ++h)
       for (int64_t t = 0; t < n; ++t) {
-        int64_t r = t / B, nr = (r + 1) * B < n ? B : n - r * B;
+        int64_t r = t / rq, nr = (r + 1) * rq < n ? rq : n - r * rq;
         for (int64_t c = 0; c < d; ++c)
           dQ[((b * hq + h) * n + t) * d + c] = dqh[((b * hq + h) * nrow + r) * d + c] / (double)nr;
       }
