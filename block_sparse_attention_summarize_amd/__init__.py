@@ -38,7 +38,7 @@ PREFILL, DECODE, TOKEN = 0, 1, 2
 FORCE_DIAG, FORCE_FIRST, FORCE_TAIL = 1, 2, 4
 OP_SUMMARIZE, OP_ROUTE_TOPK, OP_ROUTE_ENTMAX, OP_ATTEND_PREFILL, OP_ATTEND_DECODE, \
     OP_DECODE_TOPK, OP_ATTEND_PREFILL_PRIOR, OP_ATTEND_BACKWARD, OP_ROUTE_ENTMAX_BACKWARD, \
-    OP_ATTEND_ENTMAX_BACKWARD = range(10)
+    OP_ATTEND_ENTMAX_BACKWARD, OP_ATTEND_BACKWARD_PRIOR = range(11)
 STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BSA_ERR_DEVICE",
           -4: "BSA_ERR_WORKSPACE"}
 
@@ -294,11 +294,12 @@ def attend_prefill(Q, K, V, B, idx, cnt, sm_scale=0.0, out_dtype=None, out=None,
 
 
 def attend_backward(Q, K, V, O, dO, lse, B, idx, cnt, sm_scale=0.0, grad_dtype=None, ws=None,
-                    wsel=None, sigma=0.0, want_dwsel=False):
-    """Gradients (dQ, dK, dV) of attend_prefill's output (block rows, bf16)
-    for upstream gradient dO, given the forward's O and lse.  The gradients
-    take the strides of Q, K, V; dO is brought to O's strides and Q's dtype.
-    wsel, sigma: the forward's prior; want_dwsel: also return dL/dw."""
+                    wsel=None, sigma=0.0, want_dwsel=False, token=False):
+    """Gradients (dQ, dK, dV) of attend_prefill's output (bf16; block rows,
+    or token=True for per-token selections) for upstream gradient dO, given
+    the forward's O and lse.  The gradients take the strides of Q, K, V; dO
+    is brought to O's strides and Q's dtype.  wsel, sigma: the forward's
+    prior; want_dwsel: also return dL/dw."""
     b, hq, n, d = Q.shape
     gdt = grad_dtype or Q.dtype
     dQ = torch.empty_strided(Q.size(), Q.stride(), dtype=gdt, device=Q.device)
@@ -309,8 +310,10 @@ def attend_backward(Q, K, V, O, dO, lse, B, idx, cnt, sm_scale=0.0, grad_dtype=N
         t.copy_(dO)
         dO = t
     shape = make_shape(batch=b, hq=hq, hkv=K.shape[1], d=d, B=B, dtype=_dtype_code(Q),
-                       mode=PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=O)
-    wsb, nws = _workspace(OP_ATTEND_BACKWARD, shape, idx.shape[-1], Q.device, ws)
+                       mode=TOKEN if token else PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K,
+                       v=V, o=O)
+    op = OP_ATTEND_BACKWARD if wsel is None else OP_ATTEND_BACKWARD_PRIOR
+    wsb, nws = _workspace(op, shape, idx.shape[-1], Q.device, ws)
     dw = torch.empty(idx.shape, dtype=torch.float32, device=Q.device) if want_dwsel else None
     if wsel is not None:
         assert wsel.shape == idx.shape and wsel.dtype == torch.float32 and wsel.is_contiguous()
@@ -323,14 +326,16 @@ def attend_backward(Q, K, V, O, dO, lse, B, idx, cnt, sm_scale=0.0, grad_dtype=N
 
 
 def route_entmax_backward(Q, S, probs, idx, cnt, dwsel, B, alpha, gamma, dQ, dK,
-                          score_scale=0.0, ws=None):
+                          score_scale=0.0, ws=None, token=False):
     """Adds the gradient through the entmax routing weights (prefill block
-    rows) to dQ and dK in place: dwsel from attend_backward, probs the
-    routing's probs_out, S the summaries it scored.  Returns (dQ, dK)."""
+    rows; token=True: a row per query token) to dQ and dK in place: dwsel
+    from attend_backward, probs the routing's probs_out, S the summaries it
+    scored.  Returns (dQ, dK)."""
     b, hq, n, d = Q.shape
     assert dQ.stride() == Q.stride() and dQ.dtype == dK.dtype
     shape = make_shape(batch=b, hq=hq, hkv=S.shape[1], d=d, B=B, dtype=_dtype_code(Q),
-                       mode=PREFILL, q_len=n, kv_len=n, q=Q, k=dK, v=dK, o=Q)
+                       mode=TOKEN if token else PREFILL, q_len=n, kv_len=n, q=Q, k=dK, v=dK,
+                       o=Q)
     wsb, nws = _workspace(OP_ROUTE_ENTMAX_BACKWARD, shape, 0, Q.device, ws)
     _check(lib.bsa_route_entmax_backward(ctypes.byref(shape), _ptr(Q), _ptr(S), _ptr(probs),
                                          _ptr(idx), _ptr(cnt), idx.shape[-1], _ptr(dwsel), alpha,

@@ -214,18 +214,29 @@ MaskWs mask_ws(const bsa_shape* s, bool prior) {
 // sums of key blocks split over several work items.
 constexpr int kBwdChunk = 32;                  // query blocks per key-side work item
 constexpr int64_t kMaxBwdBlocks = 16384;       // one LDS word per key block when marking
+// Per-token selections (BSA_TOKEN) add the tile masks of bsa_token_mask (the
+// rows are 64-query tiles listing the union of their tokens' blocks), the
+// position of every block in each tile's list and, with a prior, the tiles'
+// per-query bias and the per-(entry, query) sums of dS behind dL/dw.
 struct BwdWs {
-  size_t delta, bits, items, red, counters, part, dbpart, total;
-  int64_t max_items, max_red, slots, nwords;
+  size_t delta, bits, items, red, counters, part, dbpart, tpos, uidx, ubits, ucnt, ubias, dbtok,
+      total;
+  int64_t max_items, max_red, slots, nwords, nrow;
 };
-BwdWs bwd_ws(const bsa_shape* s, int32_t k_max) {
+BwdWs bwd_ws(const bsa_shape* s, int32_t k_max, bool prior) {
   BwdWs w{};
+  const bool tok = s->mode == BSA_TOKEN;
   const int64_t npair = static_cast<int64_t>(s->batch) * s->n_kv_heads;
-  const int64_t nrow = nrow_of(s), nblk = nblk_of(s);
-  const int64_t k = std::max<int64_t>(1, std::min<int64_t>(k_max, nblk));
-  // (row, block) pairs with block <= row: sum over rows of min(k, r + 1)
-  const int64_t per = nrow <= k ? nrow * (nrow + 1) / 2 : k * (k + 1) / 2 + (nrow - k) * k;
+  const int64_t nblk = nblk_of(s);
+  const int64_t nrow = tok ? ntile_of(s) : nrow_of(s);
+  const int64_t rowq = tok ? 64 : s->block;
+  const int64_t k = tok ? nblk : std::max<int64_t>(1, std::min<int64_t>(k_max, nblk));
+  // (row, block) pairs with the block starting at or before the row's last
+  // query: sum over rows of min(k, that many blocks)
+  int64_t per = 0;
+  for (int64_t r = 0; r < nrow; ++r) per += std::min<int64_t>(k, ((r + 1) * rowq - 1) / s->block + 1);
   const int64_t E = npair * per;
+  w.nrow = nrow;
   w.nwords = (nrow + 31) / 32;
   w.max_items = npair * nblk + (E + kBwdChunk - 1) / kBwdChunk;
   w.max_red = std::min<int64_t>(npair * nblk, E / (kBwdChunk + 1) + 1);
@@ -237,10 +248,22 @@ BwdWs bwd_ws(const bsa_shape* s, int32_t k_max) {
   w.counters = align_up(8);
   w.part = align_up(static_cast<size_t>(w.slots) * 2 * s->block * s->head_dim * 4);
   // per-unit sums of dS for dL/dw (the prior's gradient)
-  w.dbpart = align_up(static_cast<size_t>(npair * nrow) *
-                      bsa::attend_bwd_units(s->n_q_heads / s->n_kv_heads, s->block) *
-                      std::max<int32_t>(k_max, 1) * 4);
-  w.total = w.delta + w.bits + w.items + w.red + w.counters + w.part + w.dbpart;
+  w.dbpart = tok ? 0
+                 : align_up(static_cast<size_t>(npair * nrow) *
+                            bsa::attend_bwd_units(s->n_q_heads / s->n_kv_heads, s->block) *
+                            std::max<int32_t>(k_max, 1) * 4);
+  if (tok) {
+    const size_t rl = static_cast<size_t>(npair * nrow * nblk);  // (row, list entry) slots
+    w.tpos = align_up(rl * 4);
+    w.uidx = align_up(rl * 4);
+    w.ubits = align_up(rl * 8);
+    w.ucnt = align_up(static_cast<size_t>(npair * nrow) * 4);
+    w.ubias = prior ? align_up(rl * 64 * 4) : 0;
+    w.dbtok = prior ? align_up(rl * bsa::attend_bwd_tok_parts(s->n_q_heads / s->n_kv_heads) * 64 * 4)
+                    : 0;
+  }
+  w.total = w.delta + w.bits + w.items + w.red + w.counters + w.part + w.dbpart + w.tpos +
+            w.uidx + w.ubits + w.ucnt + w.ubias + w.dbtok;
   return w;
 }
 // Routing backward: the routing queries and dL/d(logit) of every head-row.
@@ -253,7 +276,7 @@ RouteBwdWs route_bwd_ws(const bsa_shape* s) {
   w.qhat = align_up(rows * s->head_dim * 4);
   w.dz = align_up(rows * nblk_of(s) * 4);
   w.dqh = align_up(rows * s->head_dim * 4);
-  w.dsp = align_up(rows * s->head_dim * 4);  // n_blk == n_rows in prefill
+  w.dsp = align_up(static_cast<size_t>(s->batch) * s->n_q_heads * nblk_of(s) * s->head_dim * 4);
   w.total = w.qhat + w.dz + w.dqh + w.dsp;
   return w;
 }
@@ -389,9 +412,12 @@ size_t bsa_workspace_size(int32_t op, const bsa_shape* s, int32_t k_or_cap) {
     case BSA_OP_ATTEND_PREFILL_PRIOR:
       return s->mode == BSA_TOKEN ? mask_ws(s, true).total : 0;
     case BSA_OP_ATTEND_BACKWARD:
-      return s->mode == BSA_PREFILL && k_or_cap >= 1 ? bwd_ws(s, k_or_cap).total : 0;
+    case BSA_OP_ATTEND_BACKWARD_PRIOR:
+      return (s->mode == BSA_PREFILL || s->mode == BSA_TOKEN) && k_or_cap >= 1
+                 ? bwd_ws(s, k_or_cap, op == BSA_OP_ATTEND_BACKWARD_PRIOR).total
+                 : 0;
     case BSA_OP_ROUTE_ENTMAX_BACKWARD:
-      return s->mode == BSA_PREFILL ? route_bwd_ws(s).total : 0;
+      return s->mode == BSA_PREFILL || s->mode == BSA_TOKEN ? route_bwd_ws(s).total : 0;
     case BSA_OP_ATTEND_ENTMAX_BACKWARD:
       // each query's <g, dP> / sum g and normaliser
       return s->mode == BSA_PREFILL
@@ -822,7 +848,9 @@ int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const 
                         void* dV, int32_t g_dtype, void* ws, size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
-  if (s->mode != BSA_PREFILL) return fail(BSA_ERR_INVALID, "bsa_attend_backward needs BSA_PREFILL");
+  const bool tok = s->mode == BSA_TOKEN;
+  if (s->mode != BSA_PREFILL && !tok)
+    return fail(BSA_ERR_INVALID, "bsa_attend_backward needs BSA_PREFILL or BSA_TOKEN");
   if (s->dtype != BSA_BF16)
     return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_backward supports bf16 inputs only");
   bsa::AttendArgs f;
@@ -843,9 +871,12 @@ int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const 
   if ((wsel && (reinterpret_cast<uintptr_t>(wsel) & 3u) != 0) ||
       (dwsel && (reinterpret_cast<uintptr_t>(dwsel) & 3u) != 0))
     return fail(BSA_ERR_UNSUPPORTED, "wsel and dwsel must be 4-byte aligned");
-  if (dwsel && k_max > bsa::attend_bwd_max_prior_width())
-    return fail(BSA_ERR_UNSUPPORTED, "dwsel supports k_max <= %d",
+  if (!tok && dwsel && k_max > bsa::attend_bwd_max_prior_width())
+    return fail(BSA_ERR_UNSUPPORTED, "dwsel supports k_max <= %d with block rows",
                 bsa::attend_bwd_max_prior_width());
+  if (tok && nblk_of(s) > kMaxTokenBlocks)
+    return fail(BSA_ERR_UNSUPPORTED, "per-token selections support at most %lld blocks",
+                (long long)kMaxTokenBlocks);
   if ((rc = check_strides("dO", s->o_stride, s->dtype)) != BSA_OK) return rc;
   if ((rc = check_strides("dQ/dK/dV", s->q_stride, g_dtype)) != BSA_OK) return rc;
   const int64_t gsz = elem_bytes(g_dtype), osz = elem_bytes(o_dtype);
@@ -857,10 +888,17 @@ int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const 
   if (nblk_of(s) > kMaxBwdBlocks)
     return fail(BSA_ERR_UNSUPPORTED, "the backward supports at most %lld blocks",
                 (long long)kMaxBwdBlocks);
-  const BwdWs bw = bwd_ws(s, k_max);
+  const BwdWs bw = bwd_ws(s, k_max, wsel != nullptr);
   if (bw.max_items >= (int64_t(1) << 31)) return fail(BSA_ERR_UNSUPPORTED, "problem too large");
   if ((rc = check_ws(ws, ws_bytes, bw.total)) != BSA_OK) return rc;
   char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base + off;
+    off += bytes;
+    return p;
+  };
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   bsa::BwdArgs a{};
   a.Q = Q;
   a.K = K;
@@ -877,26 +915,57 @@ int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const 
   a.lse = lse;
   a.idx = idx;
   a.cnt = cnt;
-  a.delta = reinterpret_cast<float*>(base);
-  a.bits = reinterpret_cast<uint32_t*>(base + bw.delta);
-  a.items = reinterpret_cast<int4*>(base + bw.delta + bw.bits);
-  a.red = reinterpret_cast<int4*>(base + bw.delta + bw.bits + bw.items);
-  a.counters = reinterpret_cast<int*>(base + bw.delta + bw.bits + bw.items + bw.red);
-  a.part = reinterpret_cast<float*>(base + bw.delta + bw.bits + bw.items + bw.red + bw.counters);
-  a.wsel = wsel;
+  a.delta = reinterpret_cast<float*>(take(bw.delta));
+  a.bits = reinterpret_cast<uint32_t*>(take(bw.bits));
+  a.items = reinterpret_cast<int4*>(take(bw.items));
+  a.red = reinterpret_cast<int4*>(take(bw.red));
+  a.counters = reinterpret_cast<int*>(take(bw.counters));
+  a.part = reinterpret_cast<float*>(take(bw.part));
+  float* dbpart = reinterpret_cast<float*>(take(bw.dbpart));
   a.sigma = wsel ? sigma : 0.f;
   a.dwsel = dwsel;
-  a.dbpart = dwsel ? reinterpret_cast<float*>(base + bw.delta + bw.bits + bw.items + bw.red +
-                                              bw.counters + bw.part)
-                   : nullptr;
-  a.units = bsa::attend_bwd_units(s->n_q_heads / s->n_kv_heads, s->block);
+  a.units = bsa::attend_bwd_units(s->n_q_heads / s->n_kv_heads, tok ? 64 : s->block);
+  a.rowq = s->block;
+  if (tok) {
+    // the tiles' masks (and per-query prior bias) first, as the forward builds them
+    a.tpos = reinterpret_cast<int32_t*>(take(bw.tpos));
+    int32_t* uidx = reinterpret_cast<int32_t*>(take(bw.uidx));
+    uint64_t* ubits = reinterpret_cast<uint64_t*>(take(bw.ubits));
+    int32_t* ucnt = reinterpret_cast<int32_t*>(take(bw.ucnt));
+    float* ubias = reinterpret_cast<float*>(take(bw.ubias));
+    float* dbtok = reinterpret_cast<float*>(take(bw.dbtok));
+    bsa::TokenMaskArgs m;
+    if ((rc = token_mask_args(s, idx, cnt, k_max, uidx, ucnt, ubits, m)) != BSA_OK) return rc;
+    if (wsel) {
+      m.wsel = wsel;
+      m.sigma = sigma;
+      m.ubias = ubias;
+    }
+    const hipError_t e = bsa::launch_token_mask(m, st);
+    if (e != hipSuccess) return device_status(e, "attend_backward/token_mask");
+    a.tok = true;
+    a.rowq = 64;
+    a.idx = uidx;
+    a.cnt = ucnt;
+    a.tbits = ubits;
+    a.tbias = m.ubias;
+    a.dbtok = dwsel ? dbtok : nullptr;
+    a.nparts = bsa::attend_bwd_tok_parts(s->n_q_heads / s->n_kv_heads);
+    a.pidx = idx;
+    a.pcnt = cnt;
+    a.pw = wsel;
+    a.pwidth = k_max;
+  } else {
+    a.wsel = wsel;
+    a.dbpart = dwsel ? dbpart : nullptr;
+  }
   a.batch = s->batch;
   a.hq = s->n_q_heads;
   a.hkv = s->n_kv_heads;
   a.d = s->head_dim;
   a.B = s->block;
-  a.k_max = k_max;
-  a.nrow = f.nrow;
+  a.k_max = tok ? f.nblk : k_max;
+  a.nrow = static_cast<int>(bw.nrow);
   a.nblk = f.nblk;
   a.nwords = static_cast<int>(bw.nwords);
   a.chunk = kBwdChunk;
@@ -908,8 +977,7 @@ int bsa_attend_backward(const bsa_shape* s, const void* Q, const void* K, const 
   a.o_f32 = o_dtype == BSA_F32;
   a.g_f32 = g_dtype == BSA_F32;
   static_assert(kBwdChunk <= 64, "chunk rows are staged in a 64-entry LDS list");
-  return device_status(bsa::launch_attend_backward(a, static_cast<hipStream_t>(stream)),
-                       "attend_backward");
+  return device_status(bsa::launch_attend_backward(a, st), "attend_backward");
 }
 
 int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
@@ -919,8 +987,9 @@ int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
                               size_t ws_bytes, void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
-  if (s->mode != BSA_PREFILL)
-    return fail(BSA_ERR_INVALID, "bsa_route_entmax_backward needs BSA_PREFILL");
+  const bool tok = s->mode == BSA_TOKEN;
+  if (s->mode != BSA_PREFILL && !tok)
+    return fail(BSA_ERR_INVALID, "bsa_route_entmax_backward needs BSA_PREFILL or BSA_TOKEN");
   if ((rc = check_ptr("Q", Q)) != BSA_OK) return rc;
   if ((rc = check_ptr("S", S)) != BSA_OK) return rc;
   if ((rc = check_ptr("probs", probs)) != BSA_OK) return rc;
@@ -948,7 +1017,7 @@ int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
   qa.hq = s->n_q_heads;
   qa.hkv = s->n_kv_heads;
   qa.d = s->head_dim;
-  qa.B = s->block;
+  qa.B = tok ? 1 : s->block;  // token rows: the query itself
   qa.nrow = static_cast<int>(nrow_of(s));
   qa.q_len = s->q_len;
   qa.bf16 = s->dtype == BSA_BF16;
@@ -975,6 +1044,8 @@ int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
   a.d = s->head_dim;
   a.B = s->block;
   a.nrow = qa.nrow;
+  a.rowq = qa.B;
+  a.rowdiv = tok ? s->block : 1;
   a.nblk = static_cast<int>(nblk_of(s));
   a.width = width;
   a.n = s->q_len;
@@ -1035,6 +1106,7 @@ int bsa_attend_entmax_backward(const bsa_shape* s, const void* Q, const void* K,
   a.hkv = s->n_kv_heads;
   a.d = s->head_dim;
   a.B = 64;
+  a.rowq = 64;
   a.k_max = 1;
   a.nrow = f.nrow;
   a.nblk = f.nblk;

@@ -30,6 +30,16 @@
 //   bwd_reduce    blocks split into several chunks: the chunks' fp32 partials
 //                 summed in chunk order (deterministic), then stored.
 // Every gradient element is written exactly once; keys no query attends get 0.
+//
+// Per-token selections ("DashAttention", Estágio 1 routes every query and
+// Estágio 2 masks each token to its own blocks): the rows are 64-query tiles
+// whose lists are the unions of their tokens' blocks, each entry with the
+// word of the tokens that chose it (and, with a prior, every token's own bias);
+// both sides then zero P for the queries outside the word.  dL/dw of a token's
+// entry is sigma / w times the sum of dS over the block's keys and the group's
+// heads: the query side leaves per (entry, query) sums in order, and
+// bwd_dwsel_tok maps each token's own entries onto them.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -49,6 +59,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxTilesBwd = 256;  // tile-list chunk staged in LDS (query side)
 constexpr int kMaxPriorEntries = 80;  // list width with a prior (per-wave sums in LDS)
+constexpr int kBwdQT = 2, kBwdNW = 4;  // query side: 16-query tiles per wave, waves
 
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -146,9 +157,14 @@ __global__ __launch_bounds__(256) void bwd_mark(BwdArgs a) {
     if (s < (c > a.k_max ? a.k_max : c)) {
       const int j = a.idx[row * a.k_max + s];
       // block j is attended by row r only when it starts at or before the
-      // row's last query: j <= r (query and key blocks are both B long)
+      // row's last query (j <= r for block rows, query and key blocks both B long)
       const bool live = !a.wsel || a.wsel[row * a.k_max + s] > 0.f;  // the prior drops w <= 0
-      if (j >= 0 && j < a.nblk && j <= r0 + rr && live) atomicOr(&words[j], 1u << rr);
+      if (j >= 0 && j < a.nblk &&
+          static_cast<int64_t>(j) * a.B <= static_cast<int64_t>(r0 + rr + 1) * a.rowq - 1 && live) {
+        atomicOr(&words[j], 1u << rr);
+        // token tiles: where block j sits in the row's list (read by the key side)
+        if (a.tpos) a.tpos[(pair * a.nblk + j) * a.nrow + r0 + rr] = s;
+      }
     }
   }
   __syncthreads();
@@ -219,12 +235,21 @@ __device__ __forceinline__ void ent_pow(float t, float alpha, float ib, float ig
   }
 }
 
+// The query-side workgroups holding some head of the queries of sub-tile qs
+// (units qs*G .. qs*G+G-1, NW units a workgroup) are first_wg .. last_wg.
+__device__ __host__ inline int dq_first_wg(int qs, int G, int NW) { return qs * G / NW; }
+__device__ __host__ inline int dq_last_wg(int qs, int G, int NW) { return (qs * G + G - 1) / NW; }
+
 // QT query tiles of 16 per wavefront, NW wavefronts; a unit is one query head
-// x 16 QT queries of the query block, as in the forward kernel.  ENT: the
+// x 16 QT queries of the row, as in the forward kernel.  ENT: the
 // token-level entmax attention (dense causal, tau per query): a first walk
 // over the tiles gathers each query's normaliser and the VJP's mean
-// <g, dP> / sum g, the second forms dz and dQ.
-template <int D, int QT, int NW, bool ENT>
+// <g, dP> / sum g, the second forms dz and dQ.  TOK: per-token selections
+// (rows are 64-query tiles): a query whose token did not choose the tile's
+// block gets P = 0, and with a prior each query's bias is its own sigma ln w;
+// the sums of dS per (entry, query) over the group's heads (for dL/dw) go to
+// dbtok, one part per workgroup holding some of those heads.
+template <int D, int QT, int NW, bool ENT, bool TOK>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   constexpr int NT = NW * 64;
   constexpr int QPW = 16 * QT;
@@ -237,7 +262,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   __shared__ int lds_tiles[kMaxTilesBwd];
   __shared__ int lds_tent[kMaxTilesBwd];    // list entry of each tile
   __shared__ float lds_tbias[kMaxTilesBwd];  // prior bias of its block, score units
-  __shared__ float lds_db[NW][kMaxPriorEntries];  // per wave: dL/d(bias) per list entry
+  __shared__ float lds_db[TOK ? 1 : NW][kMaxPriorEntries];  // per wave: dL/d(bias) per list entry
+  __shared__ uint64_t lds_tbits[TOK ? kMaxTilesBwd : 1];   // TOK: the entry's token word
+  __shared__ float lds_dbq[TOK ? 2 : 1][NW][16 * QT];      // TOK: per wave, per query: sum of dS
   __shared__ int lds_ntiles;
 
   const int tid = threadIdx.x;
@@ -245,7 +272,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   const int w = tid >> 6;
   const int G = a.hq / a.hkv;
   const int nsub = a.B / 64;
-  const int qsub = a.B / QPW;
+  const int qsub = a.rowq / QPW;
   const int units = G * qsub;
   int pair, i, sub;
   map_wg(blockIdx.x, a.batch * a.hkv, a.nrow, wpb, pair, i, sub);
@@ -255,10 +282,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   const int hh = active ? u % G : 0;
   const int qs = active ? u / G : 0;
   const int h = g * G + hh;
-  const int qpos0 = i * a.B + qs * QPW;
+  const int qpos0 = i * a.rowq + qs * QPW;
   int qs_max = 0;
   for (int uu = sub * NW; uu < sub * NW + NW && uu < units; ++uu) qs_max = max(qs_max, uu / G);
-  int64_t qmax = static_cast<int64_t>(i) * a.B + qs_max * QPW + QPW - 1;
+  int64_t qmax = static_cast<int64_t>(i) * a.rowq + qs_max * QPW + QPW - 1;
   if (qmax > a.n - 1) qmax = a.n - 1;
 
   const int64_t rowid = static_cast<int64_t>(pair) * a.nrow + i;
@@ -372,7 +399,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
     }
   };
 
-  if (a.dbpart)
+  if (!TOK && a.dbpart)
     for (int e = lane; e < a.k_max; e += 64) lds_db[w][e] = 0.f;
   // entmax: per query column the sums over its keys of t^(1/(alpha-1)) (the
   // normaliser Z), of g dP and of g (g = t^((2-alpha)/(alpha-1)))
@@ -383,6 +410,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   for (int qt = 0; qt < QT; ++qt) zs[qt] = gds[qt] = gs[qt] = zf[qt] = 0.f;
   // entmax: all causal tiles, walked twice
   const int nraw = ENT ? static_cast<int>(qmax / 64) + 1 : n * nsub;
+  // TOK with a prior: this lane's query columns' bias for the current and the
+  // next tile (logit units, -inf where the token did not choose the block)
+  float bcur[QT], bnxt[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) bcur[qt] = bnxt[qt] = 0.f;
+  auto load_bias = [&](int tt, float (&dst)[QT]) {
+    const float* bp = a.tbias + (rowid * a.k_max + lds_tent[tt]) * 64 + qs * QPW + (lane & 15);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) dst[qt] = bp[qt * 16];
+  };
+  const bool tok_bias = TOK && a.tbias != nullptr && active;
+  float dbacc = 0.f;  // TOK, wave 0: this query's dS sum over the entry's tiles and heads
+
   // one walk over the tiles; entmax runs the gathering walk (0) first
   auto walk_pass = [&](auto pass_c) {
   constexpr int pass = decltype(pass_c)::value;
@@ -407,6 +447,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
           lds_tiles[pos] = static_cast<int>(k0);
           lds_tent[pos] = T / nsub;
           lds_tbias[pos] = tb;
+          if constexpr (TOK) lds_tbits[pos] = a.tbits[rowid * a.k_max + T / nsub];
         }
         c += __popcll(mk);
       }
@@ -417,22 +458,40 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
     int buf = 0;
     if (ntiles > 0) {
       load_tile(lds_tiles[0]);
+      if (tok_bias) load_bias(0, bcur);
       store_tile(0);
     }
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       const int k0 = lds_tiles[t];
       const bool more = t + 1 < ntiles;
-      if (more) load_tile(lds_tiles[t + 1]);
+      if (more) {
+        load_tile(lds_tiles[t + 1]);
+        if (tok_bias) load_bias(t + 1, bnxt);
+      }
+      // TOK: bit 16qt + c says whether query qpos0 + 16qt + c chose the
+      // tile's block; a wave none of whose queries did has nothing to add
+      const uint64_t qbits = TOK ? lds_tbits[t] >> (qs * QPW) : ~0ull;
+      const bool wave_on = !TOK || (qbits & (QPW == 64 ? ~0ull : (1ull << QPW) - 1)) != 0;
+      float dcol[QT];  // TOK: per query column, the sum of dS over the tile
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) dcol[qt] = 0.f;
       // a wave whose queries all precede the tile has nothing to add
-      if (active && k0 <= qpos0 + QPW - 1) {
+      if (active && k0 <= qpos0 + QPW - 1 && wave_on) {
         const uint16_t* kt_ = lds.k[buf];
         const uint16_t* vt_ = lds.v[buf];
-        // exponent offset per query column: the block's bias minus lse
+        // exponent offset per query column: the bias minus lse
         float eoff[QT];
         const float tbs = lds_tbias[t] * sc;
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) eoff[qt] = tbs - lse2[qt];
+        for (int qt = 0; qt < QT; ++qt) {
+          if constexpr (TOK) {
+            const bool on = (qbits >> (qt * 16 + (lane & 15))) & 1ull;
+            eoff[qt] = on ? (tok_bias ? bcur[qt] * kLog2e : 0.f) - lse2[qt] : -INFINITY;
+          } else {
+            eoff[qt] = tbs - lse2[qt];
+          }
+        }
         float dbs = 0.f;  // this wave's sum of dS over the tile (prior gradient)
         // S^T and dP^T, one 16-key slice at a time (lane l holds keys
         // 16kt + 4(l/16) + j of query column 16qt + l%16), turned into dS^T
@@ -521,7 +580,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
                 float p = __builtin_amdgcn_exp2f(fmaf(s[qt][j], sc, eoff[qt]));
                 if (masked) p = 0.f;
                 ds[j] = p * (dp[qt][j] - dl[qt]);
-                dbs += ds[j];
+                if constexpr (TOK)
+                  dcol[qt] += ds[j];
+                else
+                  dbs += ds[j];
               }
             }
             if constexpr (pass == 1) {
@@ -546,15 +608,51 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
             }
           }
         }
-        if (!ENT && a.dbpart) {
+        if (!ENT && !TOK && a.dbpart) {
           // this unit's part of dL/d(bias) of the tile's list entry (a block
           // of two tiles adds twice)
           dbs = wave_sum(dbs);
           if (lane == 0) lds_db[w][lds_tent[t]] += dbs;
         }
       }
+      if constexpr (TOK) {
+        if (a.dbtok) {
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            const float v = xsum16(dcol[qt]);
+            if (lane < 16) lds_dbq[buf][w][qt * 16 + lane] = v;
+          }
+        }
+      }
       if (more) store_tile(buf ^ 1);
+      if constexpr (TOK) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) bcur[qt] = bnxt[qt];
+      }
       __syncthreads();
+      if constexpr (TOK) {
+        if (a.dbtok && w == 0) {
+          // query `lane` of the row: add the heads this workgroup holds, and
+          // store once the entry's last tile is done
+          const int qsq = lane / QPW;
+          bool mine = false;
+#pragma unroll
+          for (int w2 = 0; w2 < NW; ++w2) {
+            const int u2 = sub * NW + w2;
+            if (u2 < units && u2 / G == qsq) {
+              dbacc += lds_dbq[buf][w2][lane % QPW];
+              mine = true;
+            }
+          }
+          const int e = lds_tent[t];
+          if (t + 1 == ntiles || lds_tent[t + 1] != e) {
+            if (mine)
+              a.dbtok[((rowid * a.k_max + e) * a.nparts + sub - dq_first_wg(qsq, G, NW)) * 64 + lane] =
+                  dbacc;
+            dbacc = 0.f;
+          }
+        }
+      }
       buf ^= 1;
     }
   }
@@ -578,7 +676,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   walk_pass(std::integral_constant<int, 1>{});
 
   if (!active) return;
-  if (a.dbpart)
+  if (!TOK && a.dbpart)
     for (int e = lane; e < a.k_max; e += 64)
       a.dbpart[(rowid * a.units + u) * a.k_max + e] = lds_db[w][e];
 #pragma unroll
@@ -615,6 +713,9 @@ constexpr int kMaxChunk = 64;
 // NW = B / 16 wavefronts, wave w owning keys 16w .. 16w+15 of the block.
 // ENT: the token-level entmax attention; one item per (KV head, key block),
 // its rows every query block from the key block on (dense causal).
+// Token tiles (a.tok): a query whose token did not choose block j, or whose
+// bias is -inf, gets P = 0, and a prior's bias enters through the query's
+// exponent offset (lse - bias).
 template <int D, int NW, bool ENT>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   constexpr int NT = NW * 64;
@@ -627,6 +728,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   __shared__ DkvLds<D> lds;
   __shared__ int rows[kMaxChunk];
   __shared__ float rbias[kMaxChunk];  // prior bias of block j in each row, score units
+  __shared__ int rent[kMaxChunk];     // token tiles: the list entry of block j in each row
   __shared__ float lds_iz[ENT ? 2 : 1][64];  // entmax: 1 / Z of each query
   __shared__ float lds_zf[ENT ? 2 : 1][64];  // entmax: Z^(alpha-2)
   __shared__ int lds_nr;
@@ -701,6 +803,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   }
   __syncthreads();
   const int nr = lds_nr;
+  if (!ENT && a.tok)
+    for (int i = tid; i < nr; i += NT) rent[i] = a.tpos[(static_cast<int64_t>(pair) * a.nblk + j) * a.nrow + rows[i]];
   if (!ENT && a.wsel) {
     // the routing weight of block j in each row's list: 8 threads per row
     // scan the entries (a row lists j once; rows only hold j when w > 0)
@@ -713,7 +817,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
     }
   }
   __syncthreads();
-  const int qtiles = B / 64;              // 64-query tiles per query block
+  const int qtiles = a.rowq / 64;         // 64-query tiles per row
   const int nunits = nr * G * qtiles;     // (row, head, query tile), row-major
   const float sc = a.sm_scale * kLog2e;
 
@@ -724,12 +828,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
     const int qq = uu % qtiles;
     const int rest = uu / qtiles;
     h = g * G + rest % G;
-    t0 = static_cast<int64_t>(ENT ? j + rest / G : rows[rest / G]) * B + qq * 64;
+    t0 = static_cast<int64_t>(ENT ? j + rest / G : rows[rest / G]) * a.rowq + qq * 64;
   };
   auto load_unit = [&](int uu) {
     int h;
     int64_t t0;
     unit_of(uu, h, t0);
+    const int ri = uu / qtiles / G;  // slot of the unit's row
+    (void)ri;
     const auto rq = make_rsrc(static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h,
                               head_bytes(a.n, a.qs.t, D, 2));
     const auto rdo = make_rsrc(static_cast<const uint16_t*>(a.dO) + b * a.os.b + h * a.os.h,
@@ -752,7 +858,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
         zreg = t < a.n ? a.zbuf[hrow + t] : 0.f;
       } else {
         const float L = t < a.n ? a.lse[hrow + t] : -INFINITY;
-        lreg = L > -INFINITY ? L * kLog2e : INFINITY;
+        float bias = 0.f;
+        bool on = L > -INFINITY;
+        if (a.tok) {
+          // the query's own choice of block j and its bias
+          const int64_t le = (static_cast<int64_t>(pair) * a.nrow + rows[ri]) * a.k_max + rent[ri];
+          on = on && ((a.tbits[le] >> tid) & 1ull);
+          if (a.tbias) {
+            bias = a.tbias[le * 64 + tid];
+            on = on && bias > -INFINITY;
+          }
+        }
+        lreg = on ? (L - bias) * kLog2e : INFINITY;
       }
       dreg = t < a.n ? a.delta[hrow + t] : 0.f;
     }
@@ -977,22 +1094,68 @@ __global__ __launch_bounds__(64) void bwd_dwsel(BwdArgs a) {
   }
 }
 
+// Token tiles: dL/dw of every token's list entry, sigma / w times the sum of
+// dS over the entry's keys and the group's heads (the parts of the query-side
+// workgroups holding those heads, in order).  One thread per token.
+__global__ __launch_bounds__(64) void bwd_dwsel_tok(BwdArgs a) {
+  const int64_t rowid = blockIdx.x;  // (pair, tile)
+  const int64_t pair = rowid / a.nrow;
+  const int q = threadIdx.x;
+  const int64_t t = (rowid % a.nrow) * 64 + q;
+  if (t >= a.n) return;
+  const int G = a.hq / a.hkv;
+  constexpr int QPW = 16 * kBwdQT;
+  const int qsq = q / QPW;
+  const int np = dq_last_wg(qsq, G, kBwdNW) - dq_first_wg(qsq, G, kBwdNW) + 1;  // parts, in order
+  int c = a.cnt[rowid];
+  c = c < 0 ? 0 : (c > a.k_max ? a.k_max : c);
+  const int32_t* list = a.idx + rowid * a.k_max;
+  const int64_t prow = (pair * a.n + t) * a.pwidth;
+  int pc = a.pcnt[pair * a.n + t];
+  pc = pc < 0 ? 0 : (pc > a.pwidth ? a.pwidth : pc);
+  for (int s = 0; s < a.pwidth; ++s) {
+    float out = 0.f;
+    const int j = s < pc ? a.pidx[prow + s] : -1;
+    const float wv = s < pc ? a.pw[prow + s] : 0.f;
+    // a block after the token attends nothing; w <= 0 drops the block
+    if (j >= 0 && j < a.nblk && wv > 0.f && static_cast<int64_t>(j) * a.B <= t) {
+      int lo = 0, hi = c;  // the tile's list is ascending
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (list[mid] < j)
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      if (lo < c && list[lo] == j) {
+        float acc = 0.f;
+        for (int p = 0; p < np; ++p) acc += a.dbtok[((rowid * a.k_max + lo) * a.nparts + p) * 64 + q];
+        out = a.sigma / wv * acc;
+      }
+    }
+    a.dwsel[prow + s] = out;
+  }
+}
+
 template <int D>
 hipError_t bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   const int npair = a.batch * a.hkv;
-  constexpr int QT = 2, NW = 4;
+  constexpr int QT = kBwdQT, NW = kBwdNW;
   const int G = a.hq / a.hkv;
-  const int units = G * (a.B / (16 * QT));
+  const int units = G * (a.rowq / (16 * QT));
   const int wpb = (units + NW - 1) / NW;
   const dim3 gq(static_cast<unsigned>(npair) * a.nrow * wpb);
   if (a.ent) {
     // token-level entmax attention: B = 64 rows, dense causal
-    hipLaunchKernelGGL((bwd_dq<D, QT, NW, true>), gq, dim3(NW * 64), 0, stream, a, wpb);
+    hipLaunchKernelGGL((bwd_dq<D, QT, NW, true, false>), gq, dim3(NW * 64), 0, stream, a, wpb);
     hipLaunchKernelGGL((bwd_dkv<D, 4, true>), dim3(static_cast<unsigned>(npair) * a.nblk),
                        dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((bwd_dq<D, QT, NW, false>), gq, dim3(NW * 64), 0, stream, a, wpb);
+  if (a.tok)
+    hipLaunchKernelGGL((bwd_dq<D, QT, NW, false, true>), gq, dim3(NW * 64), 0, stream, a, wpb);
+  else
+    hipLaunchKernelGGL((bwd_dq<D, QT, NW, false, false>), gq, dim3(NW * 64), 0, stream, a, wpb);
   if (a.B == 64)
     hipLaunchKernelGGL((bwd_dkv<D, 4, false>), dim3(a.max_items), dim3(256), 0, stream, a);
   else
@@ -1002,8 +1165,14 @@ hipError_t bwd_bf16(const BwdArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int attend_bwd_units(int group, int B) { return group * (B / 32); }
+int attend_bwd_units(int group, int B) { return group * (B / (16 * kBwdQT)); }
 int attend_bwd_max_prior_width() { return kMaxPriorEntries; }
+int attend_bwd_tok_parts(int group) {
+  int m = 1;
+  for (int qs = 0; qs < 64 / (16 * kBwdQT); ++qs)
+    m = std::max(m, dq_last_wg(qs, group, kBwdNW) - dq_first_wg(qs, group, kBwdNW) + 1);
+  return m;
+}
 
 hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream) {
   const unsigned npair = static_cast<unsigned>(a.batch) * a.hkv;
@@ -1016,7 +1185,9 @@ hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream) {
   e = a.d == 64 ? bwd_bf16<64>(a, stream) : bwd_bf16<128>(a, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce, dim3(a.max_red * kRedSlices), dim3(256), 0, stream, a);
-  if (a.dwsel)
+  if (a.dwsel && a.tok)
+    hipLaunchKernelGGL(bwd_dwsel_tok, dim3(static_cast<unsigned>(npair) * a.nrow), dim3(64), 0, stream, a);
+  else if (a.dwsel)
     hipLaunchKernelGGL(bwd_dwsel, dim3(static_cast<unsigned>(npair) * a.nrow), dim3(64), 0, stream, a);
   return hipGetLastError();
 }

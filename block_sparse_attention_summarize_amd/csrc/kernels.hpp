@@ -167,9 +167,25 @@ struct BwdArgs {
   float alpha;
   const float* tau;
   float* zbuf;
+  // per-token selections: a row is a 64-query tile (rowq = 64; block rows
+  // have rowq = B) whose list idx/cnt is the union of its tokens' blocks
+  // (bsa_token_mask), each entry with the word of the tokens that chose it
+  bool tok;
+  int rowq;
+  const uint64_t* tbits;  // [batch * hkv * nrow, k_max]
+  const float* tbias;     // nullptr, or [.., k_max, 64]: sigma ln w (or -inf) per query
+  int32_t* tpos;          // workspace [batch * hkv, nblk, nrow]: list entry of block j in row r
+  float* dbtok;           // workspace [batch * hkv * nrow, k_max, nparts, 64]: dS sums (dL/dw)
+  int nparts;             // query-side workgroups that share one query's heads, at most
+  // per-token lists and weights, for dL/dw [batch, hkv, n, width]
+  const int32_t* pidx;
+  const int32_t* pcnt;
+  const float* pw;
+  int pwidth;
 };
 int attend_bwd_units(int group, int B);  // units per row of the query side
 int attend_bwd_max_prior_width();        // k_max limit when dL/dw is requested
+int attend_bwd_tok_parts(int group);     // nparts of the token-mode dL/dw sums
 hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream);
 
 // Routing part of the gradient of entmax-routed prefill (block rows): dL/dw
@@ -188,6 +204,8 @@ struct RouteBwdArgs {
   void* dK;
   Strides3 qs, ks;     // of dQ, dK (elements of the gradient dtype)
   int batch, hq, hkv, d, B, nrow, nblk, width;
+  int rowq;    // queries pooled per row: B (block rows) or 1 (token rows)
+  int rowdiv;  // row r's own block is r / rowdiv: 1 (block rows) or B (token rows)
   int64_t n;
   float alpha, fscale;  // fscale = gamma * score_scale
   bool g_f32;

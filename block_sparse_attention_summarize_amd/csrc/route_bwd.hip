@@ -1,8 +1,9 @@
-// Backward of the entmax routing of prefill block rows: the gradient of the
-// loss with respect to the routing weights (dL/dw of the listed blocks, from
-// the prior-induced softmax's backward) carried to the queries and keys
-// ("DashAttention", Estágio 1: unlike top-k, entmax routing is
-// differentiable, so gradients reach the block summaries of Estágio 0).
+// Backward of the entmax routing of prefill block rows, or of every query
+// token (a row per token, its routing query the token's own query): the
+// gradient of the loss with respect to the routing weights (dL/dw of the
+// listed blocks, from the prior-induced softmax's backward) carried to the
+// queries and keys ("DashAttention", Estágio 1: unlike top-k, entmax routing
+// is differentiable, so gradients reach the block summaries of Estágio 0).
 //
 //   entmax_vjp_rows  one workgroup per (batch, query head, row): the listed
 //                    routed block j of the head's KV group has w_j = mean over
@@ -13,8 +14,9 @@
 //                    part of dS_j = sum over rows of dz q-hat: fp32 products
 //                    on MFMA tiles staged in LDS.
 //   route_bwd_spread the mean pools' adjoint: dQ_t += dqhat_row / (tokens in
-//                    the row), dK_u += (sum over the group's heads of the
-//                    parts) / (tokens in the block), four elements a thread.
+//                    the row; 1 for token rows), dK_u += (sum over the
+//                    group's heads of the parts) / (tokens in the block),
+//                    four elements a thread.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -85,11 +87,12 @@ __global__ __launch_bounds__(kVjpThreads) void entmax_vjp_rows(RouteBwdArgs a) {
 // Batched fp32 product on MFMA tiles, C[64 x D] = A[64 x K] B[K x D] per
 // workgroup, with A read through element strides (so it may be a transposed
 // view of dz) and both tiles staged in LDS with K contiguous.
-//   KEY = false: rows r (query blocks) of head h, K = blocks j < r:
-//                A = dz[h][r][j], B = S[g][j][c] -> dqhat[h][r][c].
-//   KEY = true:  rows j (key blocks), one head h of the group, K = rows
-//                r > j: A = dz[h][r][j], B = qhat[h][r][c] -> that head's
-//                part of dS[g][j][c] (the parts are summed when spread).
+//   KEY = false: rows r of head h, K = the blocks before r's own block
+//                r / rowdiv: A = dz[h][r][j], B = S[g][j][c] -> dqhat[h][r][c].
+//   KEY = true:  rows j (key blocks), one head h of the group, K = the rows
+//                whose own block follows j: A = dz[h][r][j],
+//                B = qhat[h][r][c] -> that head's part of dS[g][j][c] (the
+//                parts are summed when spread).
 constexpr int kGT = 64;      // output rows per workgroup, K per chunk
 constexpr int kGPad = 4;     // LDS row padding (floats)
 
@@ -100,11 +103,12 @@ __global__ __launch_bounds__(256) void route_bwd_gemm(RouteBwdArgs a) {
   __shared__ float Bs[D][KS];    // [c][k]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = a.hq / a.hkv;
-  const int nmt = (a.nrow + kGT - 1) / kGT;  // nrow == nblk (prefill)
+  const int mtot = KEY ? a.nblk : a.nrow;  // output rows
+  const int nmt = (mtot + kGT - 1) / kGT;
   const int mt = blockIdx.x % nmt;
   const int64_t bh = blockIdx.x / nmt;  // (b, h)
   const int m0 = mt * kGT;
-  const int mrows = a.nrow - m0 < kGT ? a.nrow - m0 : kGT;
+  const int mrows = mtot - m0 < kGT ? mtot - m0 : kGT;
   f32x4_t acc[D / 16];
 #pragma unroll
   for (int ct = 0; ct < D / 16; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -143,19 +147,19 @@ __global__ __launch_bounds__(256) void route_bwd_gemm(RouteBwdArgs a) {
   const int64_t hrow = bh * a.nrow;
   if constexpr (!KEY) {
     const float* S = a.S + (b * a.hkv + g) * a.nblk * D;
-    // candidates of rows m0.. are the blocks before them
-    const int kend = m0 + mrows - 1;
+    // candidates of rows m0.. are the blocks before their own blocks
+    const int kend = (m0 + mrows - 1) / a.rowdiv;
     for (int k0 = 0; k0 < kend; k0 += kGT)
       chunk(a.dz + (hrow + m0) * a.nblk + k0, a.nblk, 1, kend - k0 < kGT ? kend - k0 : kGT,
             S + static_cast<int64_t>(k0) * D);
   } else {
-    // rows after block m0 hold it among their candidates
-    for (int r0 = m0 + 1; r0 < a.nrow; r0 += kGT)
+    // rows whose own block follows block m0 hold it among their candidates
+    for (int r0 = (m0 + 1) * a.rowdiv; r0 < a.nrow; r0 += kGT)
       chunk(a.dz + (hrow + r0) * a.nblk + m0, 1, a.nblk, a.nrow - r0 < kGT ? a.nrow - r0 : kGT,
             a.qhat + (hrow + r0) * D);
   }
   // lane l holds rows 16w + 4(l/16) + i, columns 16ct + l%16
-  float* out = (KEY ? a.dsp : a.dqh) + (hrow + m0) * D;
+  float* out = (KEY ? a.dsp + bh * a.nblk * D : a.dqh + hrow * D) + static_cast<int64_t>(m0) * D;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = 16 * w + (lane >> 4) * 4 + i;
@@ -214,14 +218,15 @@ __global__ __launch_bounds__(256) void route_bwd_spread(const float* src, int pa
 hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t stream) {
   const unsigned rows = static_cast<unsigned>(a.batch) * a.hq * a.nrow;
   hipLaunchKernelGGL(entmax_vjp_rows, dim3(rows), dim3(kVjpThreads), 0, stream, a);
-  const unsigned nmt = static_cast<unsigned>((a.nrow + kGT - 1) / kGT);
-  const dim3 gg(static_cast<unsigned>(a.batch) * a.hq * nmt);
+  const unsigned bh = static_cast<unsigned>(a.batch) * a.hq;
+  const dim3 gq(bh * static_cast<unsigned>((a.nrow + kGT - 1) / kGT));
+  const dim3 gk(bh * static_cast<unsigned>((a.nblk + kGT - 1) / kGT));
   if (a.d == 64) {
-    hipLaunchKernelGGL((route_bwd_gemm<64, false>), gg, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((route_bwd_gemm<64, true>), gg, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((route_bwd_gemm<64, false>), gq, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((route_bwd_gemm<64, true>), gk, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((route_bwd_gemm<128, false>), gg, dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((route_bwd_gemm<128, true>), gg, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((route_bwd_gemm<128, false>), gq, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((route_bwd_gemm<128, true>), gk, dim3(256), 0, stream, a);
   }
   const int G = a.hq / a.hkv;
   auto grid_of = [&](int heads) {
@@ -230,14 +235,14 @@ hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t strea
   };
   if (a.g_f32) {
     hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1,
-                       a.dQ, a.qs, a.hq, a.nrow, a.B, a.n, a.d);
+                       a.dQ, a.qs, a.hq, a.nrow, a.rowq, a.n, a.d);
     hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp, G,
-                       a.dK, a.ks, a.hkv, a.nrow, a.B, a.n, a.d);
+                       a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
   } else {
     hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1,
-                       a.dQ, a.qs, a.hq, a.nrow, a.B, a.n, a.d);
+                       a.dQ, a.qs, a.hq, a.nrow, a.rowq, a.n, a.d);
     hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp, G,
-                       a.dK, a.ks, a.hkv, a.nrow, a.B, a.n, a.d);
+                       a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
   }
   return hipGetLastError();
 }

@@ -108,7 +108,8 @@ typedef enum {
   BSA_OP_ATTEND_PREFILL_PRIOR = 6, /* bsa_attend_prefill with wsel != NULL */
   BSA_OP_ATTEND_BACKWARD = 7,      /* bsa_attend_backward; k_or_cap = k_max */
   BSA_OP_ROUTE_ENTMAX_BACKWARD = 8, /* bsa_route_entmax_backward */
-  BSA_OP_ATTEND_ENTMAX_BACKWARD = 9  /* bsa_attend_entmax_backward */
+  BSA_OP_ATTEND_ENTMAX_BACKWARD = 9, /* bsa_attend_entmax_backward */
+  BSA_OP_ATTEND_BACKWARD_PRIOR = 10  /* bsa_attend_backward with wsel; k_or_cap = k_max */
 } bsa_op;
 
 /* Problem description, read only during the call. */
@@ -282,8 +283,9 @@ int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, con
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Backward of Stage 2, causal prefill with block rows: the gradients of
- * bsa_attend_prefill's output for a fixed selection (the selection itself
+ * Backward of Stage 2, causal prefill with block rows or per-token
+ * selections: the gradients of bsa_attend_prefill's output for a fixed
+ * selection (the selection itself
  * gets none; with a prior, the routing weights do).  The pages single out the backward pass as
  * where training time goes and skip its zero blocks ("AdaSplash-2", section
  * 4); training the sparse attention end to end is "DashAttention",
@@ -301,21 +303,30 @@ int bsa_attend_prefill(const bsa_shape *shape, const void *Q, const void *K, con
  *   Q, K, V, idx, cnt, k_max, sm_scale, wsel, sigma  as given to
  *         bsa_attend_prefill (bf16 only; the entries of a row must be
  *         distinct, as the routing calls produce them; wsel NULL: no prior).
- *   dwsel NULL, or out fp32 in the layout of idx (needs wsel, k_max <= 80):
- *         dL/dw_j = sigma / w_j * sum of dS_tu over the entry's (query, key)
- *         pairs of every query head of the group (the logits of block j
- *         carry sigma ln w_j); 0 for entries beyond cnt or with w_j <= 0.
+ *   Token mode (shape->mode == BSA_TOKEN; "DashAttention", Estágio 1 routes
+ *         every query token): idx/cnt (and wsel) per token as in
+ *         bsa_attend_prefill.  The call first builds the 64-query tile masks
+ *         of bsa_token_mask in ws; the rows of both walks are then those
+ *         tiles, and a query's weights on a block its token did not choose
+ *         are zero.
+ *   dwsel NULL, or out fp32 in the layout of idx (needs wsel; block rows:
+ *         k_max <= 80): dL/dw_j = sigma / w_j * sum of dS_tu over the entry's
+ *         (query, key) pairs of every query head of the group (the logits of
+ *         block j carry sigma ln w_j); 0 for entries beyond cnt, with
+ *         w_j <= 0, or (token mode) for a block after the token.
  *         bsa_route_entmax_backward carries it to Q and K.
  *   O     the forward output, o_dtype (bf16 or BSA_F32), with o_stride.
  *   dO    bf16 [batch, Hq, q_len, d] with o_stride.
  *   lse   fp32 [batch, Hq, q_len] written by bsa_attend_prefill.
  *   dQ, dK, dV  out, g_dtype (bf16 or BSA_F32), with the strides of Q, K, V;
  *         every element is written (0 for keys no query attends).
- *   ws    bsa_workspace_size(BSA_OP_ATTEND_BACKWARD, shape, k_max) bytes,
- *         256-byte aligned; scratch afterwards.
- * Errors: BSA_ERR_INVALID (mode other than BSA_PREFILL, null pointers),
- * BSA_ERR_UNSUPPORTED (fp32 inputs, more than 16384 blocks, strides,
- * alignment), BSA_ERR_WORKSPACE.
+ *   ws    bsa_workspace_size(BSA_OP_ATTEND_BACKWARD, shape, k_max) bytes
+ *         without a prior, BSA_OP_ATTEND_BACKWARD_PRIOR with wsel (the same
+ *         for block rows; token mode adds the tiles' per-query bias and the
+ *         sums behind dwsel), 256-byte aligned; scratch afterwards.
+ * Errors: BSA_ERR_INVALID (mode BSA_DECODE, null pointers),
+ * BSA_ERR_UNSUPPORTED (fp32 inputs, more than 16384 blocks (token mode:
+ * 4096), strides, alignment), BSA_ERR_WORKSPACE.
  */
 int bsa_attend_backward(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                         const void *O, int32_t o_dtype, const void *dO, const float *lse,
@@ -324,8 +335,11 @@ int bsa_attend_backward(const bsa_shape *shape, const void *Q, const void *K, co
                         void *dV, int32_t g_dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Backward of Stage 1, alpha-entmax routing of prefill block rows: the part of
- * the gradient that flows through the routing weights into the queries and
+ * Backward of Stage 1, alpha-entmax routing of prefill block rows (or, with
+ * shape->mode == BSA_TOKEN, of every query token: each token is a row whose
+ * routing query is its own query and whose candidates are the blocks before
+ * its own): the part of the gradient that flows through the routing weights
+ * into the queries and
  * the keys ("DashAttention", Estágio 1: entmax routing is differentiable, so
  * gradients pass the routing decision back to the block summaries of
  * Estágio 0).  With w_j = (1/G) sum_h p_hj the listed routed blocks' weights
@@ -334,8 +348,8 @@ int bsa_attend_backward(const bsa_shape *shape, const void *Q, const void *K, co
  * dz_j = g_j (dp_j - <g, dp> / sum g); then
  *   dqhat_h = gamma * score_scale * sum_j dz_hj S_j,
  *   dS_j = gamma * score_scale * sum over the group's heads and rows of dz q-hat,
- * and the mean pools give every query of row r dqhat / (tokens of the row)
- * and every key of block j dS_j / (tokens of the block) (summaries with a
+ * and the mean pools give every query of row r dqhat / (tokens of the row;
+ * 1 for a token row) and every key of block j dS_j / (tokens of the block) (summaries with a
  * zero learned query).  These are ADDED to dQ and dK (run after
  * bsa_attend_backward wrote the attention part).
  *   Q      the forward's queries (the routing queries are recomputed).
@@ -346,8 +360,8 @@ int bsa_attend_backward(const bsa_shape *shape, const void *Q, const void *K, co
  *   alpha, gamma, score_scale  as given to bsa_route_entmax (0: 1/sqrt(d)).
  *   dQ, dK in/out, g_dtype (input dtype or BSA_F32), strides of Q and K.
  *   ws     bsa_workspace_size(BSA_OP_ROUTE_ENTMAX_BACKWARD, shape, 0) bytes.
- * Errors: BSA_ERR_INVALID (mode other than BSA_PREFILL, alpha <= 1, null
- * pointers), BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
+ * Errors: BSA_ERR_INVALID (mode BSA_DECODE, alpha <= 1, null pointers),
+ * BSA_ERR_UNSUPPORTED, BSA_ERR_WORKSPACE.
  */
 int bsa_route_entmax_backward(const bsa_shape *shape, const void *Q, const float *S,
                               const float *probs, const int32_t *idx, const int32_t *cnt,

@@ -272,7 +272,7 @@ def test_backward_validation_and_workspace():
     assert need == (al(4 * 645 * 4) + al(2 * 1 * nblk * 4) + al(items * 16) + al(red * 16) + al(8)
                     + al(slots * 2 * 64 * 128 * 4) + al(2 * nrow * units * 4 * 4))
     assert backward(s, ws_bytes=need - 1) == -4
-    assert backward(shape(mode=bsa.TOKEN)) == -1 and "BSA_PREFILL" in err()
+    assert backward(shape(mode=bsa.DECODE, q_len=1)) == -1 and "BSA_TOKEN" in err()
     assert backward(shape(dtype=bsa.F32)) == -2 and "bf16" in err()
     assert backward(s, lse=None) == -1 and "lse" in err()
     assert backward(s, dO=None) == -1 and "dO" in err()
@@ -282,7 +282,34 @@ def test_backward_validation_and_workspace():
     # more key blocks than the marking kernel holds in LDS
     big = shape(q_len=64 * 16385, kv_len=64 * 16385, hq=2, hkv=1)
     assert backward(big, ws_bytes=0) == -2 and "16384" in err()
-    assert lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD, ctypes.byref(shape(mode=bsa.TOKEN)), 4) == 0
+    assert lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD, ctypes.byref(shape(mode=bsa.DECODE)), 4) == 0
+    # the prior's variant is the same size for block rows
+    assert lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD_PRIOR, ctypes.byref(s), 4) == need
+
+
+def test_token_backward_workspace():
+    # per-token selections: the rows are the 11 64-query tiles, each listing
+    # up to all 11 blocks; the tile masks, the list positions and (with a
+    # prior) the per-query bias and dS sums come on top
+    s = shape(q_len=64 * 10 + 5, kv_len=64 * 10 + 5, mode=bsa.TOKEN)
+    al = lambda x: (x + 255) // 256 * 256
+    nrow = nblk = 11
+    E = 2 * sum(min(nblk, r + 1) for r in range(nrow))
+    items = 2 * nblk + -(-E // 32)
+    red = min(2 * nblk, E // 33 + 1)
+    slots = E // 32 + red + 1
+    rl = 2 * nrow * nblk
+    base = (al(4 * 645 * 4) + al(2 * 1 * nblk * 4) + al(items * 16) + al(red * 16) + al(8)
+            + al(slots * 2 * 64 * 128 * 4) + al(rl * 4) + al(rl * 4) + al(rl * 8) + al(2 * nrow * 4))
+    need = lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD, ctypes.byref(s), 6)
+    assert need == base
+    prior = lib.bsa_workspace_size(bsa.OP_ATTEND_BACKWARD_PRIOR, ctypes.byref(s), 6)
+    assert prior == base + al(rl * 64 * 4) + al(rl * 1 * 64 * 4)  # G = 2: one part
+    assert backward(s, k_max=6, ws_bytes=need - 1) == -4
+    assert backward(s, k_max=6, wsel=FAKE, ws_bytes=prior - 1) == -4
+    # more blocks than the tile masks hold
+    big = shape(q_len=64 * 4097, kv_len=64 * 4097, hq=2, hkv=1, mode=bsa.TOKEN)
+    assert backward(big, ws_bytes=0) == -2 and "4096" in err()
 
 
 def test_backward_prior_and_routing_backward_validation():
@@ -296,7 +323,13 @@ def test_backward_prior_and_routing_backward_validation():
     # q-hat, dz (4 rows x 4 blocks), dL/dq-hat and the heads' parts of dL/dS
     assert need == 3 * al(1 * 4 * 4 * 128 * 4) + al(1 * 4 * 4 * 4 * 4)
     assert route_backward(s, ws_bytes=need - 1) == -4
-    assert route_backward(shape(mode=bsa.TOKEN)) == -1 and "BSA_PREFILL" in err()
+    assert route_backward(shape(mode=bsa.DECODE, q_len=1)) == -1 and "BSA_TOKEN" in err()
+    # token rows: q-hat, dL/dq-hat and dz per (head, token); the heads' dS
+    # parts per block
+    t = shape(mode=bsa.TOKEN)
+    tneed = lib.bsa_workspace_size(bsa.OP_ROUTE_ENTMAX_BACKWARD, ctypes.byref(t), 0)
+    assert tneed == 2 * al(4 * 256 * 128 * 4) + al(4 * 256 * 4 * 4) + al(4 * 4 * 128 * 4)
+    assert route_backward(t, ws_bytes=tneed - 1) == -4
     assert route_backward(s, alpha=1.0) == -1 and "alpha" in err()
     assert route_backward(s, dwsel=None) == -1 and "dwsel" in err()
     assert route_backward(s, width=0) == -1
