@@ -24,10 +24,11 @@ times and attention TFLOP/s, and `entmax_attn_prefill_n16k` (token-level
 alpha-entmax attention, dense causal with zero key tiles skipped) timed
 beside the dense causal softmax of the same inputs (every block selected),
 `backward` (the gradients dQ, dK, dV of the headline attention for its
-selection, beside the forward that feeds them) and `train_entmax_prior` (a
+selection, beside the forward that feeds them), `train_entmax_prior` (a
 training pass of entmax routing with the prior-induced softmax, sigma = 1, on
 the N = 65536 entmax inputs: forward, then the attention gradients with
-dL/dw and the routing gradient into dQ and dK).
+dL/dw and the routing gradient into dQ and dK) and `train_token_prior` (the
+same pass with every query token routed, on the per-token inputs).
 """
 from __future__ import annotations
 
@@ -474,14 +475,16 @@ def run_backward(bsa, torch, w, r, steps, warmup):
     return out
 
 
-def run_train_entmax(bsa, torch, steps, warmup, sigma=1.0):
+def run_train_entmax(bsa, torch, steps, warmup, name=ENTMAX, sigma=1.0):
     """One training pass of entmax-routed prefill with the prior (the
-    N = 65536 entmax workload with sigma = 1): forward = summaries, entmax
-    routing (probabilities and weights kept), biased attention with its
-    log-normaliser; backward = attention gradients with dL/dw, then the
-    routing gradient added to dQ and dK.  Timed as two event-bracketed
-    phases per step."""
-    w = synth.WORKLOADS[ENTMAX]
+    N = 65536 entmax workload, or the per-token one, with sigma = 1): forward
+    = summaries, entmax routing (probabilities and weights kept), biased
+    attention with its log-normaliser; backward = attention gradients with
+    dL/dw, then the routing gradient added to dQ and dK.  Timed as two
+    event-bracketed phases per step."""
+    w = synth.WORKLOADS[name]
+    token = w.mode == "token"
+    nrow = w.n if token else w.nblk
     x = device_inputs(w, torch)
     Q, K, V = x["Q"], x["K"], x["V"]
     del x
@@ -490,17 +493,20 @@ def run_train_entmax(bsa, torch, steps, warmup, sigma=1.0):
     del do_st
     width = w.idx_width
     S = torch.empty((w.batch, w.hkv, w.nblk, w.d), dtype=torch.float32, device="cuda")
-    idx = torch.empty((w.batch, w.hkv, w.nblk, width), dtype=torch.int32, device="cuda")
-    cnt = torch.empty((w.batch, w.hkv, w.nblk), dtype=torch.int32, device="cuda")
+    idx = torch.empty((w.batch, w.hkv, nrow, width), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((w.batch, w.hkv, nrow), dtype=torch.int32, device="cuda")
     wsel = torch.empty(idx.shape, dtype=torch.float32, device="cuda")
     O = torch.empty_like(Q)
-    shape_r = bsa._route_shape(Q, S, w.B, False, None, False)
+    shape_r = bsa._route_shape(Q, S, w.B, False, None, token)
     rws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_ENTMAX, shape_r, w.cap), dtype=torch.uint8,
                       device="cuda")
     shape = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B, dtype=bsa.BF16,
-                           mode=bsa.PREFILL, q_len=w.n, kv_len=w.n, q=Q, k=K, v=V, o=O)
-    bws = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_BACKWARD, shape, width), dtype=torch.uint8,
-                      device="cuda")
+                           mode=bsa.TOKEN if token else bsa.PREFILL, q_len=w.n, kv_len=w.n, q=Q,
+                           k=K, v=V, o=O)
+    aws = torch.empty(max(bsa.workspace_size(bsa.OP_ATTEND_PREFILL_PRIOR, shape, width), 1),
+                      dtype=torch.uint8, device="cuda")
+    bws = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_BACKWARD_PRIOR, shape, width),
+                      dtype=torch.uint8, device="cuda")
     gws = torch.empty(bsa.workspace_size(bsa.OP_ROUTE_ENTMAX_BACKWARD, shape, 0),
                       dtype=torch.uint8, device="cuda")
     st = {}
@@ -509,16 +515,17 @@ def run_train_entmax(bsa, torch, steps, warmup, sigma=1.0):
         bsa.summarize(K, w.B, out=S)
         _, _, st["probs"], _ = bsa.route_entmax(Q, S, w.B, w.alpha, w.gamma, w.cap, w.force,
                                                 n_bins=w.n_bins, max_iter=w.max_iter, ws=rws,
-                                                out=(idx, cnt), wsel=wsel, want_probs=True)
+                                                out=(idx, cnt), wsel=wsel, want_probs=True,
+                                                token=token)
         _, st["L"] = bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O, wsel=wsel, sigma=sigma,
-                                        want_lse=True)
+                                        want_lse=True, token=token, ws=aws)
 
     def backward():
         dQ, dK, dV, dw = bsa.attend_backward(Q, K, V, O, dO, st["L"], w.B, idx, cnt, ws=bws,
                                              wsel=wsel, sigma=sigma, want_dwsel=True,
-                                             grad_dtype=torch.float32)
+                                             grad_dtype=torch.float32, token=token)
         bsa.route_entmax_backward(Q, S, st["probs"], idx, cnt, dw, w.B, w.alpha, w.gamma, dQ, dK,
-                                  ws=gws)
+                                  ws=gws, token=token)
 
     for _ in range(warmup):
         forward()
@@ -536,8 +543,9 @@ def run_train_entmax(bsa, torch, steps, warmup, sigma=1.0):
     torch.cuda.synchronize()
     fwd = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     bwd = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    flops = 4.0 * w.d * prefill_pairs(w, idx.cpu().numpy(), cnt.cpu().numpy())
-    del Q, K, V, dO, S, idx, cnt, wsel, O, rws, bws, gws, st
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    flops = 4.0 * w.d * (token_pairs(w, idx_h, cnt_h) if token else prefill_pairs(w, idx_h, cnt_h))
+    del Q, K, V, dO, S, idx, cnt, wsel, O, rws, aws, bws, gws, st
     torch.cuda.empty_cache()
     return {"workload": w.name, "prior_sigma": sigma, "forward_ms": fwd, "backward_ms": bwd,
             "train_step_ms": fwd + bwd, "attention_flops": flops,
@@ -587,6 +595,9 @@ def main():
     if not a.no_backward:
         extra["backward"] = run_backward(bsa, torch, w, r, a.steps, a.warmup)
         extra["train_entmax_prior"] = run_train_entmax(bsa, torch, a.steps, a.warmup)
+        if not a.no_token:
+            extra["train_token_prior"] = run_train_entmax(bsa, torch, a.steps, a.warmup,
+                                                          name=TOKEN)
     if not a.no_decode:
         extra["decode"] = run_decode(bsa, torch, a.steps, a.warmup)
     for name, flag in ((ENTMAX, a.no_entmax), (LONG, a.no_long), (TOKEN, a.no_token)):

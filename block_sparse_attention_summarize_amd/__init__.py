@@ -345,26 +345,33 @@ def route_entmax_backward(Q, S, probs, idx, cnt, dwsel, B, alpha, gamma, dQ, dK,
 
 
 class _SparseAttention(torch.autograd.Function):
-    """attend_prefill (block rows) with attend_backward as its gradient; the
-    selection is an input without gradient."""
+    """attend_prefill with attend_backward as its gradient; the selection is
+    an input without gradient, the routing weights wsel (prior) get dL/dw."""
 
     @staticmethod
-    def forward(ctx, Q, K, V, B, idx, cnt, sm_scale):
-        O, L = attend_prefill(Q, K, V, B, idx, cnt, sm_scale, want_lse=True)
-        ctx.save_for_backward(Q, K, V, O, L, idx, cnt)
-        ctx.B, ctx.sm_scale = B, sm_scale
+    def forward(ctx, Q, K, V, wsel, B, idx, cnt, sm_scale, sigma, token):
+        O, L = attend_prefill(Q, K, V, B, idx, cnt, sm_scale, token=token, wsel=wsel,
+                              sigma=sigma, want_lse=True)
+        ctx.save_for_backward(Q, K, V, O, L, idx, cnt, wsel)
+        ctx.B, ctx.sm_scale, ctx.sigma, ctx.token = B, sm_scale, sigma, token
         return O
 
     @staticmethod
     def backward(ctx, dO):
-        Q, K, V, O, L, idx, cnt = ctx.saved_tensors
-        dQ, dK, dV = attend_backward(Q, K, V, O, dO, L, ctx.B, idx, cnt, ctx.sm_scale)
-        return dQ, dK, dV, None, None, None, None
+        Q, K, V, O, L, idx, cnt, wsel = ctx.saved_tensors
+        want_dw = wsel is not None and ctx.needs_input_grad[3]
+        g = attend_backward(Q, K, V, O, dO, L, ctx.B, idx, cnt, ctx.sm_scale, wsel=wsel,
+                            sigma=ctx.sigma, want_dwsel=want_dw, token=ctx.token)
+        dw = g[3] if want_dw else None
+        return g[0], g[1], g[2], dw, None, None, None, None, None, None
 
 
-def sparse_attention(Q, K, V, B, idx, cnt, sm_scale=0.0):
-    """Differentiable causal block-sparse attention over a fixed selection."""
-    return _SparseAttention.apply(Q, K, V, B, idx, cnt, sm_scale)
+def sparse_attention(Q, K, V, B, idx, cnt, sm_scale=0.0, wsel=None, sigma=0.0, token=False):
+    """Differentiable causal block-sparse attention over a fixed selection
+    (block rows, or per-token selections with token=True); with routing
+    weights wsel (shaped like idx) the prior-induced softmax, whose weights
+    receive dL/dw when they require grad."""
+    return _SparseAttention.apply(Q, K, V, wsel, B, idx, cnt, sm_scale, sigma, token)
 
 
 def attend_entmax(Q, K, V, alpha, refine=2, sm_scale=0.0, out_dtype=None, out=None,

@@ -276,7 +276,9 @@ RouteBwdWs route_bwd_ws(const bsa_shape* s) {
   w.qhat = align_up(rows * s->head_dim * 4);
   w.dz = align_up(rows * nblk_of(s) * 4);
   w.dqh = align_up(rows * s->head_dim * 4);
-  w.dsp = align_up(static_cast<size_t>(s->batch) * s->n_q_heads * nblk_of(s) * s->head_dim * 4);
+  w.dsp = align_up(static_cast<size_t>(s->batch) * s->n_q_heads *
+                   bsa::route_bwd_key_splits(static_cast<int>(nrow_of(s))) * nblk_of(s) *
+                   s->head_dim * 4);
   w.total = w.qhat + w.dz + w.dqh + w.dsp;
   return w;
 }
@@ -1046,6 +1048,7 @@ int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
   a.nrow = qa.nrow;
   a.rowq = qa.B;
   a.rowdiv = tok ? s->block : 1;
+  a.ksplit = bsa::route_bwd_key_splits(a.nrow);
   a.nblk = static_cast<int>(nblk_of(s));
   a.width = width;
   a.n = s->q_len;

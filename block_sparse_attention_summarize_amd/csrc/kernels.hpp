@@ -199,17 +199,20 @@ struct RouteBwdArgs {
   const float* dwsel;  // layout of idx
   float* dz;           // [batch, hq, nrow, nblk] workspace: dL/d(q-hat . S)
   float* dqh;          // [batch, hq, nrow, d] workspace: dL/d(q-hat)
-  float* dsp;          // [batch, hq, nblk, d] workspace: each head's part of dL/dS
+  float* dsp;          // [batch, hq, ksplit, nblk, d] workspace: each head's (and row
+                       // range's) part of dL/dS
   void* dQ;
   void* dK;
   Strides3 qs, ks;     // of dQ, dK (elements of the gradient dtype)
   int batch, hq, hkv, d, B, nrow, nblk, width;
   int rowq;    // queries pooled per row: B (block rows) or 1 (token rows)
   int rowdiv;  // row r's own block is r / rowdiv: 1 (block rows) or B (token rows)
+  int ksplit;  // row ranges the key-side product is split into
   int64_t n;
   float alpha, fscale;  // fscale = gamma * score_scale
   bool g_f32;
 };
+int route_bwd_key_splits(int nrow);  // ksplit for nrow routing rows
 hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t stream);
 
 // Active blocks of every 64-query tile from per-token selections

@@ -5,14 +5,16 @@
 // queries and keys ("DashAttention", Estágio 1: unlike top-k, entmax routing
 // is differentiable, so gradients reach the block summaries of Estágio 0).
 //
-//   entmax_vjp_rows  one workgroup per (batch, query head, row): the listed
+//   entmax_vjp_rows  one wavefront per (batch, query head, row): the listed
 //                    routed block j of the head's KV group has w_j = mean over
 //                    the group of p_j, so dp_j = dw_j / G; with g = p^(2-alpha)
 //                    on the support, dz_j = g_j (dp_j - <g, dp> / sum g),
 //                    scaled by gamma * score_scale (the logits' factor).
 //   route_bwd_gemm   dqhat = dz S (over the row's candidates) and each head's
-//                    part of dS_j = sum over rows of dz q-hat: fp32 products
-//                    on MFMA tiles staged in LDS.
+//                    part of dS_j = sum over rows of dz q-hat, the rows split
+//                    into ranges of kKeyRows (one partial each, summed in
+//                    order when spread): fp32 products on MFMA tiles staged in
+//                    LDS.
 //   route_bwd_spread the mean pools' adjoint: dQ_t += dqhat_row / (tokens in
 //                    the row; 1 for token rows), dK_u += (sum over the
 //                    group's heads of the parts) / (tokens in the block),
@@ -24,29 +26,27 @@ namespace bsa {
 
 namespace {
 
-constexpr int kVjpThreads = 256;
+constexpr int kVjpThreads = 256;  // four rows a workgroup, one wavefront each
+constexpr int kVjpRows = kVjpThreads / kWave;
+constexpr int kKeyRows = 1024;     // rows per partial of the key-side product
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int NT>
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane_id() == 0) red[w] = v;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int k = 0; k < NT / kWave; ++k) t += red[k];
-  return t;
+// g = p^(2-alpha) on the support (alpha = 1.5: sqrt p; alpha = 2: 1)
+__device__ __forceinline__ float entmax_g(float p, float alpha, float expo) {
+  if (!(p > 0.f)) return 0.f;
+  if (alpha == 1.5f) return __builtin_sqrtf(p);
+  if (alpha == 2.f) return 1.f;
+  return __builtin_amdgcn_exp2f(expo * __log2f(p));
 }
 
-__device__ __forceinline__ float entmax_g(float p, float expo) {
-  return p > 0.f ? __builtin_amdgcn_exp2f(expo * __log2f(p)) : 0.f;
-}
-
-__global__ __launch_bounds__(kVjpThreads) void entmax_vjp_rows(RouteBwdArgs a) {
-  __shared__ float red[kVjpThreads / kWave];
-  const int64_t hrow = blockIdx.x;  // (b * hq + h) * nrow + r
+__global__ __launch_bounds__(kVjpThreads) void entmax_vjp_rows(RouteBwdArgs a, int64_t nrows) {
+  extern __shared__ uint32_t listed[];  // [kVjpRows][nwords]: the row's listed blocks
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nwords = (a.nblk + 31) / 32;
+  uint32_t* mark = listed + wv * nwords;
+  for (int k = lane; k < nwords; k += kWave) mark[k] = 0u;
+  const int64_t hrow = static_cast<int64_t>(blockIdx.x) * kVjpRows + wv;  // (b * hq + h) * nrow + r
+  const bool live = hrow < nrows;
   const int r = static_cast<int>(hrow % a.nrow);
   const int64_t bh = hrow / a.nrow;
   const int h = static_cast<int>(bh % a.hq);
@@ -57,30 +57,34 @@ __global__ __launch_bounds__(kVjpThreads) void entmax_vjp_rows(RouteBwdArgs a) {
   float* dz = a.dz + hrow * a.nblk;
   const float expo = 2.f - a.alpha;
   float sg = 0.f;
-  for (int j = threadIdx.x; j < a.nblk; j += kVjpThreads) sg += entmax_g(p[j], expo);
-  sg = block_sum<kVjpThreads>(sg, red);
-  int c = a.cnt[rowid];
+  if (live)
+    for (int j = lane; j < a.nblk; j += kWave) sg += entmax_g(p[j], a.alpha, expo);
+  sg = wave_sum(sg);
+  int c = live ? a.cnt[rowid] : 0;
   c = c < 0 ? 0 : (c > a.width ? a.width : c);
   const int32_t* list = a.idx + rowid * a.width;
   const float* dw = a.dwsel + rowid * a.width;
   const float invG = 1.f / static_cast<float>(G);
+  __syncthreads();  // marks cleared
   float sgd = 0.f;
-  for (int e = threadIdx.x; e < c; e += kVjpThreads) {
+  for (int e = lane; e < c; e += kWave) {
     const int j = list[e];
     // forced blocks are no candidates (p = 0) and so carry no gradient
-    if (j >= 0 && j < a.nblk) sgd += entmax_g(p[j], expo) * dw[e] * invG;
-  }
-  sgd = block_sum<kVjpThreads>(sgd, red);
-  const float m = sg > 0.f ? sgd / sg : 0.f;
-  for (int j = threadIdx.x; j < a.nblk; j += kVjpThreads)
-    dz[j] = -a.fscale * entmax_g(p[j], expo) * m;
-  __syncthreads();  // the listed blocks' values below replace these
-  for (int e = threadIdx.x; e < c; e += kVjpThreads) {
-    const int j = list[e];
     if (j >= 0 && j < a.nblk) {
-      const float g = entmax_g(p[j], expo);
-      if (g > 0.f) dz[j] = a.fscale * g * (dw[e] * invG - m);
+      sgd += entmax_g(p[j], a.alpha, expo) * dw[e] * invG;
+      atomicOr(&mark[j >> 5], 1u << (j & 31));
     }
+  }
+  sgd = wave_sum(sgd);
+  __syncthreads();  // marks set
+  if (!live) return;
+  const float m = sg > 0.f ? sgd / sg : 0.f;
+  // unlisted blocks, then the listed ones: every dz written once
+  for (int j = lane; j < a.nblk; j += kWave)
+    if (!((mark[j >> 5] >> (j & 31)) & 1u)) dz[j] = -a.fscale * entmax_g(p[j], a.alpha, expo) * m;
+  for (int e = lane; e < c; e += kWave) {
+    const int j = list[e];
+    if (j >= 0 && j < a.nblk) dz[j] = a.fscale * entmax_g(p[j], a.alpha, expo) * (dw[e] * invG - m);
   }
 }
 
@@ -105,8 +109,10 @@ __global__ __launch_bounds__(256) void route_bwd_gemm(RouteBwdArgs a) {
   const int G = a.hq / a.hkv;
   const int mtot = KEY ? a.nblk : a.nrow;  // output rows
   const int nmt = (mtot + kGT - 1) / kGT;
-  const int mt = blockIdx.x % nmt;
-  const int64_t bh = blockIdx.x / nmt;  // (b, h)
+  const int ks = KEY ? static_cast<int>(blockIdx.x % a.ksplit) : 0;  // row range (key side)
+  const int xi = KEY ? static_cast<int>(blockIdx.x / a.ksplit) : static_cast<int>(blockIdx.x);
+  const int mt = xi % nmt;
+  const int64_t bh = xi / nmt;  // (b, h)
   const int m0 = mt * kGT;
   const int mrows = mtot - m0 < kGT ? mtot - m0 : kGT;
   f32x4_t acc[D / 16];
@@ -114,17 +120,54 @@ __global__ __launch_bounds__(256) void route_bwd_gemm(RouteBwdArgs a) {
   for (int ct = 0; ct < D / 16; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // one K chunk of 64 staged and multiplied
-  auto chunk = [&](const float* abase, int64_t am, int64_t ak, int kn, const float* bbase) {
+  // A's contiguous dimension (k when ak == 1, else m) is read four floats at a
+  // time when its stride keeps them 16-byte aligned (vec), B's rows always
+  auto chunk = [&](const float* abase, int64_t am, int64_t ak, int kn, const float* bbase,
+                   bool vec) {
     __syncthreads();
-    for (int e = tid; e < kGT * kGT; e += 256) {
-      // walk the contiguous dimension of A across neighbouring threads
-      const int m = ak == 1 ? e / kGT : e % kGT;
-      const int k = ak == 1 ? e % kGT : e / kGT;
-      As[m][k] = (m < mrows && k < kn) ? abase[m * am + k * ak] : 0.f;
+    if (vec) {
+      for (int e = tid; e < kGT * kGT / 4; e += 256) {
+        const int o = e / (kGT / 4), i4 = (e % (kGT / 4)) * 4;  // outer, inner (contiguous)
+        const int m = ak == 1 ? o : i4, k = ak == 1 ? i4 : o;
+        const bool in = ak == 1 ? (m < mrows && k < kn) : (k < kn && m < mrows);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (in) {
+          const int lim = ak == 1 ? kn - k : mrows - m;  // valid elements from here
+          const float* src = abase + m * am + k * ak;
+          if (lim >= 4) {
+            v = *reinterpret_cast<const float4*>(src);
+          } else {
+            const int64_t st = ak == 1 ? 1 : am;
+            v.x = src[0];
+            if (lim > 1) v.y = src[st];
+            if (lim > 2) v.z = src[2 * st];
+          }
+        }
+        if (ak == 1) {
+          *reinterpret_cast<float4*>(&As[m][k]) = v;
+        } else {
+          As[m][k] = v.x;
+          As[m + 1][k] = v.y;
+          As[m + 2][k] = v.z;
+          As[m + 3][k] = v.w;
+        }
+      }
+    } else {
+      for (int e = tid; e < kGT * kGT; e += 256) {
+        // walk the contiguous dimension of A across neighbouring threads
+        const int m = ak == 1 ? e / kGT : e % kGT;
+        const int k = ak == 1 ? e % kGT : e / kGT;
+        As[m][k] = (m < mrows && k < kn) ? abase[m * am + k * ak] : 0.f;
+      }
     }
-    for (int e = tid; e < kGT * D; e += 256) {
-      const int k = e / D, c = e % D;
-      Bs[c][k] = k < kn ? bbase[static_cast<int64_t>(k) * D + c] : 0.f;
+    for (int e = tid; e < kGT * D / 4; e += 256) {
+      const int k = e / (D / 4), c = (e % (D / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (k < kn) v = *reinterpret_cast<const float4*>(bbase + static_cast<int64_t>(k) * D + c);
+      Bs[c][k] = v.x;
+      Bs[c + 1][k] = v.y;
+      Bs[c + 2][k] = v.z;
+      Bs[c + 3][k] = v.w;
     }
     __syncthreads();
     const int lr = lane & 15, lk = (lane >> 4) * 4;
@@ -145,21 +188,26 @@ __global__ __launch_bounds__(256) void route_bwd_gemm(RouteBwdArgs a) {
   const int64_t b = bh / a.hq;
   const int h = static_cast<int>(bh % a.hq), g = h / G;
   const int64_t hrow = bh * a.nrow;
+  const bool vec = a.nblk % 4 == 0;  // dz rows of whole float4s
   if constexpr (!KEY) {
     const float* S = a.S + (b * a.hkv + g) * a.nblk * D;
     // candidates of rows m0.. are the blocks before their own blocks
     const int kend = (m0 + mrows - 1) / a.rowdiv;
     for (int k0 = 0; k0 < kend; k0 += kGT)
       chunk(a.dz + (hrow + m0) * a.nblk + k0, a.nblk, 1, kend - k0 < kGT ? kend - k0 : kGT,
-            S + static_cast<int64_t>(k0) * D);
+            S + static_cast<int64_t>(k0) * D, vec);
   } else {
-    // rows whose own block follows block m0 hold it among their candidates
-    for (int r0 = (m0 + 1) * a.rowdiv; r0 < a.nrow; r0 += kGT)
-      chunk(a.dz + (hrow + r0) * a.nblk + m0, 1, a.nblk, a.nrow - r0 < kGT ? a.nrow - r0 : kGT,
-            a.qhat + (hrow + r0) * D);
+    // rows whose own block follows block m0 hold it among their candidates;
+    // this workgroup takes those in its range
+    const int rend = min(a.nrow, (ks + 1) * kKeyRows);
+    for (int r0 = max((m0 + 1) * a.rowdiv, ks * kKeyRows); r0 < rend; r0 += kGT)
+      chunk(a.dz + (hrow + r0) * a.nblk + m0, 1, a.nblk, rend - r0 < kGT ? rend - r0 : kGT,
+            a.qhat + (hrow + r0) * D, vec);
   }
-  // lane l holds rows 16w + 4(l/16) + i, columns 16ct + l%16
-  float* out = (KEY ? a.dsp + bh * a.nblk * D : a.dqh + hrow * D) + static_cast<int64_t>(m0) * D;
+  // lane l holds rows 16w + 4(l/16) + i, columns 16ct + l%16 (the key side's
+  // empty ranges store zeros)
+  float* out = (KEY ? a.dsp + (bh * a.ksplit + ks) * a.nblk * D : a.dqh + hrow * D) +
+               static_cast<int64_t>(m0) * D;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = 16 * w + (lane >> 4) * 4 + i;
@@ -215,12 +263,16 @@ __global__ __launch_bounds__(256) void route_bwd_spread(const float* src, int pa
 
 }  // namespace
 
+int route_bwd_key_splits(int nrow) { return (nrow + kKeyRows - 1) / kKeyRows; }
+
 hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t stream) {
-  const unsigned rows = static_cast<unsigned>(a.batch) * a.hq * a.nrow;
-  hipLaunchKernelGGL(entmax_vjp_rows, dim3(rows), dim3(kVjpThreads), 0, stream, a);
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.hq * a.nrow;
+  const size_t mark_bytes = static_cast<size_t>(kVjpRows) * ((a.nblk + 31) / 32) * 4;
+  hipLaunchKernelGGL(entmax_vjp_rows, dim3(static_cast<unsigned>((rows + kVjpRows - 1) / kVjpRows)),
+                     dim3(kVjpThreads), mark_bytes, stream, a, rows);
   const unsigned bh = static_cast<unsigned>(a.batch) * a.hq;
   const dim3 gq(bh * static_cast<unsigned>((a.nrow + kGT - 1) / kGT));
-  const dim3 gk(bh * static_cast<unsigned>((a.nblk + kGT - 1) / kGT));
+  const dim3 gk(bh * static_cast<unsigned>((a.nblk + kGT - 1) / kGT) * a.ksplit);
   if (a.d == 64) {
     hipLaunchKernelGGL((route_bwd_gemm<64, false>), gq, dim3(256), 0, stream, a);
     hipLaunchKernelGGL((route_bwd_gemm<64, true>), gk, dim3(256), 0, stream, a);
@@ -236,13 +288,13 @@ hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t strea
   if (a.g_f32) {
     hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1,
                        a.dQ, a.qs, a.hq, a.nrow, a.rowq, a.n, a.d);
-    hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp, G,
-                       a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
+    hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp,
+                       G * a.ksplit, a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
   } else {
     hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1,
                        a.dQ, a.qs, a.hq, a.nrow, a.rowq, a.n, a.d);
-    hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp, G,
-                       a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
+    hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp,
+                       G * a.ksplit, a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
   }
   return hipGetLastError();
 }

@@ -201,3 +201,29 @@ def test_token_backward_full_size_sampled():
     sv = dV.double().sum(dim=2)
     ref_v = x["dO"].double().reshape(1, w.hkv, G, w.n, w.d).sum(dim=(2, 3))
     assert float((sv - ref_v).abs().max()) <= 1e-3 * float(ref_v.abs().max() + w.n)
+
+
+def test_token_autograd_wrapper_with_prior():
+    """sparse_attention(..., wsel, token=True).backward(dO) gives
+    attend_backward's dQ, dK, dV and dL/dw."""
+    w = PRIOR["tokent_g4"]
+    print("[token autograd wrapper]", flush=True)
+    x = _inputs(w)
+    S = bsa.summarize(x["K"], w.B)
+    wsel = torch.empty((1, w.hkv, w.n, w.idx_width), dtype=torch.float32, device="cuda")
+    idx, cnt, _, _ = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
+                                      max_iter=w.max_iter, wsel=wsel, token=True)
+    Q = x["Q"].clone().requires_grad_()
+    K = x["K"].clone().requires_grad_()
+    V = x["V"].clone().requires_grad_()
+    wp = wsel.clone().requires_grad_()
+    O = bsa.sparse_attention(Q, K, V, w.B, idx, cnt, wsel=wp, sigma=w.sigma, token=True)
+    O.backward(x["dO"])
+    O2, L = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt, token=True, wsel=wsel,
+                               sigma=w.sigma, want_lse=True)
+    ref = bsa.attend_backward(x["Q"], x["K"], x["V"], O2, x["dO"], L, w.B, idx, cnt, wsel=wsel,
+                              sigma=w.sigma, want_dwsel=True, token=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O.detach(), O2)
+    for t, r in zip((Q, K, V, wp), ref):
+        assert torch.equal(t.grad, r)
