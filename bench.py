@@ -329,25 +329,32 @@ def run_entmax_attn(bsa, torch, steps, warmup, refine=2):
     t_ent = timed(lambda: bsa.attend_entmax(Q, K, V, w.alpha, refine=refine, out=O))
     t_soft = timed(lambda: bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O))
     dense = 4.0 * w.d * w.hq * w.batch * w.n * (w.n + 1) / 2
-    _, tau = bsa.attend_entmax(Q, K, V, w.alpha, refine=refine, want_tau=True)
-    # the backward from the forward's tau, for a seeded upstream gradient
+    _, tau, live = bsa.attend_entmax(Q, K, V, w.alpha, refine=refine, want_tau=True,
+                                     want_live=True)
+    nt = (w.n + 63) // 64
+    lv = live.cpu().numpy().view(np.uint32)
+    live_frac = float(np.unpackbits(lv.view(np.uint8)).sum()) / (w.batch * w.hkv * nt * (nt + 1) / 2)
+    # the backward from the forward's tau (walking its live tiles, and every
+    # causal tile), for a seeded upstream gradient
     do_st, _ = synth.gen_stored(w, "do")
     dO = torch.from_numpy(do_st.view(np.int16)).to("cuda").view(torch.bfloat16)
     shape = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=64, dtype=bsa.BF16,
                            mode=bsa.PREFILL, q_len=w.n, kv_len=w.n, q=Q, k=K, v=V, o=dO)
     ews = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_ENTMAX_BACKWARD, shape, 0),
                       dtype=torch.uint8, device="cuda")
-    t_bwd = timed(lambda: bsa.attend_entmax_backward(Q, K, V, dO, tau, w.alpha, ws=ews))
+    t_bwd = timed(lambda: bsa.attend_entmax_backward(Q, K, V, dO, tau, w.alpha, ws=ews, live=live))
+    t_bwd_all = timed(lambda: bsa.attend_entmax_backward(Q, K, V, dO, tau, w.alpha, ws=ews))
     torch.cuda.synchronize()
-    del x, Q, K, V, O, idx, cnt, tau, dO, ews
+    del x, Q, K, V, O, idx, cnt, tau, live, dO, ews
     torch.cuda.empty_cache()
     return {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
             "seq_len": w.n, "head_dim": w.d, "alpha": w.alpha, "refine": refine,
             "query_scale": w.q_scale, "ms_per_step": t_ent,
             "dense_equiv_TFLOP_per_s": dense / t_ent / 1e9,
             "dense_softmax_ms": t_soft, "dense_softmax_TFLOP_per_s": dense / t_soft / 1e9,
-            "speedup_vs_dense_softmax": t_soft / t_ent, "backward_ms": t_bwd,
-            "backward_dense_equiv_TFLOP_per_s": 2.5 * dense / t_bwd / 1e9}
+            "speedup_vs_dense_softmax": t_soft / t_ent, "live_tile_fraction": live_frac,
+            "backward_ms": t_bwd, "backward_dense_equiv_TFLOP_per_s": 2.5 * dense / t_bwd / 1e9,
+            "backward_all_tiles_ms": t_bwd_all}
 
 
 def run_decode(bsa, torch, steps, warmup, with_paged=True):

@@ -86,12 +86,12 @@ lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32
                                    _sz, _P]
 lib.bsa_attend_backward.argtypes = [_SP, _P, _P, _P, _P, _i32, _P, _P, _P, _P, _i32, _f32, _P, _f32,
                                     _P, _P, _P, _P, _i32, _P, _sz, _P]
-lib.bsa_attend_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, _P, _i32,
+lib.bsa_attend_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, _P, _i32,
                                            _P, _sz, _P]
 lib.bsa_route_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _P, _f32, _f32, _f32, _P,
                                           _P, _i32, _P, _sz, _P]
 lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
-lib.bsa_attend_entmax.argtypes = [_SP, _P, _P, _P, _f32, _i32, _f32, _P, _i32, _P, _P]
+lib.bsa_attend_entmax.argtypes = [_SP, _P, _P, _P, _f32, _i32, _f32, _P, _i32, _P, _P, _P]
 lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
 lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
                                 _P, _sz, _P]
@@ -375,23 +375,34 @@ def sparse_attention(Q, K, V, B, idx, cnt, sm_scale=0.0, wsel=None, sigma=0.0, t
 
 
 def attend_entmax(Q, K, V, alpha, refine=2, sm_scale=0.0, out_dtype=None, out=None,
-                  want_tau=False):
+                  want_tau=False, want_live=False):
     """Causal token-level alpha-entmax attention (bf16 Q [b, Hq, N, d],
-    K/V [b, Hkv, N, d]).  Returns O, or (O, tau) with want_tau."""
+    K/V [b, Hkv, N, d]).  Returns O, (O, tau) with want_tau, and the live
+    key tiles [b, Hkv, T, ceil(T/32)] uint32 (T = ceil(N/64)) appended with
+    want_live."""
     b, hq, n, d = Q.shape
+    hkv = K.shape[1]
     odt = out_dtype or Q.dtype
     O = out if out is not None else torch.empty((b, hq, n, d), dtype=odt, device=Q.device)
     tau = torch.empty((b, hq, n), dtype=torch.float32, device=Q.device) if want_tau else None
-    shape = make_shape(batch=b, hq=hq, hkv=K.shape[1], d=d, B=64, dtype=_dtype_code(Q),
+    nt = (n + 63) // 64
+    live = (torch.empty((b, hkv, nt, (nt + 31) // 32), dtype=torch.int32, device=Q.device)
+            if want_live else None)
+    shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=64, dtype=_dtype_code(Q),
                        mode=PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=O)
     _check(lib.bsa_attend_entmax(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), alpha, refine,
-                                 sm_scale, _ptr(O), _dtype_code(O), _ptr(tau), _stream(Q)))
-    return (O, tau) if want_tau else O
+                                 sm_scale, _ptr(O), _dtype_code(O), _ptr(tau), _ptr(live),
+                                 _stream(Q)))
+    res = (O,) + ((tau,) if want_tau else ()) + ((live,) if want_live else ())
+    return res if len(res) > 1 else O
 
 
-def attend_entmax_backward(Q, K, V, dO, tau, alpha, sm_scale=0.0, grad_dtype=None, ws=None):
+def attend_entmax_backward(Q, K, V, dO, tau, alpha, sm_scale=0.0, grad_dtype=None, ws=None,
+                           live=None):
     """Gradients (dQ, dK, dV) of attend_entmax's output for upstream dO, given
-    the forward's tau (want_tau=True).  Gradients take the strides of Q, K, V."""
+    the forward's tau (want_tau=True) and, optionally, its live key tiles
+    (want_live=True), which the backward then walks alone.  Gradients take
+    the strides of Q, K, V."""
     b, hq, n, d = Q.shape
     gdt = grad_dtype or Q.dtype
     dQ = torch.empty_strided(Q.size(), Q.stride(), dtype=gdt, device=Q.device)
@@ -403,7 +414,8 @@ def attend_entmax_backward(Q, K, V, dO, tau, alpha, sm_scale=0.0, grad_dtype=Non
                        mode=PREFILL, q_len=n, kv_len=K.shape[2], q=Q, k=K, v=V, o=dO)
     wsb, nws = _workspace(OP_ATTEND_ENTMAX_BACKWARD, shape, 0, Q.device, ws)
     _check(lib.bsa_attend_entmax_backward(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V),
-                                          _ptr(dO), _ptr(tau), alpha, sm_scale, _ptr(dQ),
+                                          _ptr(dO), _ptr(tau), _ptr(live), alpha, sm_scale,
+                                          _ptr(dQ),
                                           _ptr(dK), _ptr(dV), _dtype_code(dQ), _ptr(wsb), nws,
                                           _stream(Q)))
     return dQ, dK, dV

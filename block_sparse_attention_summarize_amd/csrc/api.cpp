@@ -1060,7 +1060,8 @@ int bsa_route_entmax_backward(const bsa_shape* s, const void* Q, const float* S,
 }
 
 int bsa_attend_entmax_backward(const bsa_shape* s, const void* Q, const void* K, const void* V,
-                               const void* dO, const float* tau, float alpha, float sm_scale,
+                               const void* dO, const float* tau, const uint32_t* live,
+                               float alpha, float sm_scale,
                                void* dQ, void* dK, void* dV, int32_t g_dtype, void* ws,
                                size_t ws_bytes, void* stream) {
   int rc;
@@ -1084,6 +1085,10 @@ int bsa_attend_entmax_backward(const bsa_shape* s, const void* Q, const void* K,
   if (!tau) return fail(BSA_ERR_INVALID, "tau is NULL");
   if ((reinterpret_cast<uintptr_t>(tau) & 3u) != 0)
     return fail(BSA_ERR_UNSUPPORTED, "tau must be 4-byte aligned");
+  if (live && (reinterpret_cast<uintptr_t>(live) & 3u) != 0)
+    return fail(BSA_ERR_UNSUPPORTED, "live must be 4-byte aligned");
+  if (live && (s->q_len + 63) / 64 > 2048)
+    return fail(BSA_ERR_UNSUPPORTED, "live supports at most %d tokens", 64 * 2048);
   if (g_dtype != s->dtype && g_dtype != BSA_F32)
     return fail(BSA_ERR_UNSUPPORTED, "g_dtype must be the input dtype or BSA_F32");
   if ((rc = check_strides("dQ/dK/dV", s->q_stride, g_dtype)) != BSA_OK) return rc;
@@ -1120,13 +1125,15 @@ int bsa_attend_entmax_backward(const bsa_shape* s, const void* Q, const void* K,
   a.ent = true;
   a.alpha = alpha;
   a.tau = tau;
+  a.live = live;
+  a.nlw = static_cast<int>((f.nrow + 31) / 32);
   return device_status(bsa::launch_attend_backward(a, static_cast<hipStream_t>(stream)),
                        "attend_entmax_backward");
 }
 
 int bsa_attend_entmax(const bsa_shape* s, const void* Q, const void* K, const void* V,
                       float alpha, int32_t refine, float sm_scale, void* O, int32_t o_dtype,
-                      float* tau_out, void* stream) {
+                      float* tau_out, uint32_t* live_out, void* stream) {
   int rc;
   if ((rc = check_shape(s)) != BSA_OK) return rc;
   if (s->mode != BSA_PREFILL) return fail(BSA_ERR_INVALID, "bsa_attend_entmax needs BSA_PREFILL");
@@ -1141,6 +1148,8 @@ int bsa_attend_entmax(const bsa_shape* s, const void* Q, const void* K, const vo
     return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax supports at most %d tokens",
                 64 * bsa::entmax_attend_max_tiles());
   if (tau_out && !aligned16(tau_out)) return fail(BSA_ERR_UNSUPPORTED, "tau_out must be 16-byte aligned");
+  if (live_out && (reinterpret_cast<uintptr_t>(live_out) & 3u) != 0)
+    return fail(BSA_ERR_UNSUPPORTED, "live_out must be 4-byte aligned");
   // the shared argument checks of the attention calls (a dummy selection)
   bsa::AttendArgs t;
   static const int32_t one = 0;
@@ -1156,6 +1165,7 @@ int bsa_attend_entmax(const bsa_shape* s, const void* Q, const void* K, const vo
   a.vs = t.vs;
   a.os = t.os;
   a.tau = tau_out;
+  a.live = live_out;
   a.batch = s->batch;
   a.hq = s->n_q_heads;
   a.hkv = s->n_kv_heads;

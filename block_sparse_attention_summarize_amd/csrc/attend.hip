@@ -274,7 +274,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
       if constexpr (TOK) qbits = lds_tbits[t] >> (qs * QPW);
 
       if (active && (!TOK || (qbits & (QPW == 64 ? ~0ull : (1ull << QPW) - 1)) != 0)) {
-        // S^T tiles: lane l holds keys 16kt + 4(l/16) + j of query column 16qt + l%16
+        // S^T tiles: lane l holds keys 16kt + 4(l/16) + j of query column 16qt + l%16.
+        // The two MFMA phases run at raised wave priority, so the SIMD's other
+        // wavefront, in its softmax, yields the matrix unit to them (measured
+        // ~2 % faster at the 32k GQA workload).
+        __builtin_amdgcn_s_setprio(1);
         f32x4 s[4][QT];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -308,6 +312,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
               for (int j = 0; j < 4; ++j)
                 if (rel0 + kt * 16 + j - qt * 16 > 0) s[kt][qt][j] = -INFINITY;
         }
+        __builtin_amdgcn_s_setprio(0);
         // running max per query; the accumulators are rescaled only when it
         // grows by more than 2^kRescale (p stays <= 2^kRescale, exact after
         // normalising)
@@ -357,6 +362,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
             pf[qt][kk].w = pack_bf16x2(p[2 * kk + 1][2], p[2 * kk + 1][3]);
           }
         }
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -379,6 +385,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if (more) store_tile(buf ^ 1);
       if constexpr (BIAS && TOK) {
 #pragma unroll

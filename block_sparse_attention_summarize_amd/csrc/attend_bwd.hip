@@ -432,6 +432,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
       for (int r = 0; r < kMaxTilesBwd && base + r < nraw; r += 64) {
         const int T = base + r + lane;
         int64_t k0 = T >= nraw ? -1 : (ENT ? 64 * static_cast<int64_t>(T) : walk.key0(T));
+        // entmax with the forward's live tiles: only those have weights
+        if (ENT && a.live && k0 >= 0 && !((a.live[rowid * a.nlw + (T >> 5)] >> (T & 31)) & 1u))
+          k0 = -1;
         float tb = 0.f;
         if (!ENT && a.wsel && k0 >= 0) {
           // the prior: sigma ln w of the tile's block, dropped when w <= 0
@@ -709,6 +712,7 @@ struct DkvLds {
   alignas(16) float dl[2][64];
 };
 constexpr int kMaxChunk = 64;
+constexpr int kMaxEntRows = 2048;  // entmax key side: query tiles a key tile can have
 
 // NW = B / 16 wavefronts, wave w owning keys 16w .. 16w+15 of the block.
 // ENT: the token-level entmax attention; one item per (KV head, key block),
@@ -731,6 +735,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   __shared__ int rent[kMaxChunk];     // token tiles: the list entry of block j in each row
   __shared__ float lds_iz[ENT ? 2 : 1][64];  // entmax: 1 / Z of each query
   __shared__ float lds_zf[ENT ? 2 : 1][64];  // entmax: Z^(alpha-2)
+  __shared__ uint16_t erows[ENT ? kMaxEntRows : 1];  // entmax with live tiles: the query tiles
   __shared__ int lds_nr;
 
   int pair, j, chunk = 0, slot = -1;
@@ -756,7 +761,22 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
   // rows of this chunk: ranks [chunk * a.chunk, +a.chunk) among the set bits
   // of block j's column, ascending
   if (ENT) {
-    if (tid == 0) lds_nr = a.nrow - j;
+    if (!a.live) {
+      if (tid == 0) lds_nr = a.nrow - j;
+    } else if (w == 0) {
+      // the query tiles from j on whose live row holds key tile j
+      int c = 0;
+      for (int base = j; base < a.nrow; base += 64) {
+        const int i = base + lane;
+        const bool on = i < a.nrow &&
+                        ((a.live[(static_cast<int64_t>(pair) * a.nrow + i) * a.nlw + (j >> 5)] >>
+                          (j & 31)) & 1u);
+        const uint64_t mk = __ballot(on);
+        if (on) erows[c + lanes_below(mk)] = static_cast<uint16_t>(i);
+        c += __popcll(mk);
+      }
+      if (lane == 0) lds_nr = c;
+    }
   } else if (w == 0) {
     const int lo = chunk * a.chunk, hi = lo + a.chunk;
     const uint32_t* col = a.bits + static_cast<int64_t>(pair) * a.nwords * a.nblk + j;
@@ -817,7 +837,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
     }
   }
   __syncthreads();
-  const int qtiles = a.rowq / 64;         // 64-query tiles per row
+  // queries per row: 64 whenever the key block is (block rows of 64, token
+  // tiles, entmax), so the unit arithmetic below folds to constants there
+  const int rowq = (ENT || B == 64) ? 64 : a.rowq;
+  const int qtiles = rowq / 64;           // 64-query tiles per row
   const int nunits = nr * G * qtiles;     // (row, head, query tile), row-major
   const float sc = a.sm_scale * kLog2e;
 
@@ -828,7 +851,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv(BwdArgs a) {
     const int qq = uu % qtiles;
     const int rest = uu / qtiles;
     h = g * G + rest % G;
-    t0 = static_cast<int64_t>(ENT ? j + rest / G : rows[rest / G]) * a.rowq + qq * 64;
+    const int row = ENT ? (a.live ? static_cast<int>(erows[rest / G]) : j + rest / G) : rows[rest / G];
+    t0 = static_cast<int64_t>(row) * rowq + qq * 64;
   };
   auto load_unit = [&](int uu) {
     int h;

@@ -448,6 +448,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void entmax_attn_bf16(EntmaxAttnAr
     if (mark) {
       // the output and later refinements visit only tiles with some x > lo
       __syncthreads();
+      if (a.live) {
+        // the workgroup's marks, OR-ed into its query tile's row (the other
+        // workgroups of the tile hold other heads of the group)
+        uint32_t* row = a.live + (static_cast<int64_t>(pair) * nqt + i) * ((nqt + 31) / 32);
+        for (int t = tid; t <= (ntile - 1) >> 5; t += NT)
+          if (live[t] != 0u) atomicOr(row + t, live[t]);
+      }
       if (w == 0) {
         int c = 0;
         for (int base = 0; base < ntile; base += 64) {
@@ -463,8 +470,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void entmax_attn_bf16(EntmaxAttnAr
     }
   }
   if (a.refine == 0) {
-    // no refinement: every tile is visited
+    // no refinement: every tile is visited (and every causal tile is live)
     list_all();
+    if (a.live && sub == 0) {
+      uint32_t* row = a.live + (static_cast<int64_t>(pair) * nqt + i) * ((nqt + 31) / 32);
+      for (int t = tid; t <= (ntile - 1) >> 5; t += NT)
+        row[t] = (t < (ntile >> 5)) ? ~0u : (1u << (ntile & 31)) - 1u;
+    }
   }
 
   // ---- pass 4: output over the live tiles ----
@@ -544,6 +556,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void entmax_attn_bf16(EntmaxAttnAr
   }
 }
 
+// Clears the live-tile rows before the attention ORs its marks into them.
+__global__ __launch_bounds__(256) void clear_words(uint32_t* p, int64_t n) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e < n) p[e] = 0u;
+}
+
 template <int D>
 hipError_t entmax_launch(const EntmaxAttnArgs& a, hipStream_t stream) {
   constexpr int QT = 2, NW = 4;
@@ -551,6 +569,11 @@ hipError_t entmax_launch(const EntmaxAttnArgs& a, hipStream_t stream) {
   const int units = G * (64 / (16 * QT));
   const int wpb = (units + NW - 1) / NW;
   const int nqt = static_cast<int>((a.n + 63) / 64);
+  if (a.live) {
+    const int64_t words = static_cast<int64_t>(a.batch) * a.hkv * nqt * ((nqt + 31) / 32);
+    hipLaunchKernelGGL(clear_words, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0,
+                       stream, a.live, words);
+  }
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * nqt * wpb;
   if (a.out_f32)
     hipLaunchKernelGGL((entmax_attn_bf16<D, QT, NW, true>), dim3(grid), dim3(NW * 64), 0, stream,

@@ -167,6 +167,8 @@ struct BwdArgs {
   float alpha;
   const float* tau;
   float* zbuf;
+  const uint32_t* live;  // optional [batch * hkv, nrow, nlw]: the forward's live key tiles
+  int nlw;
   // per-token selections: a row is a 64-query tile (rowq = 64; block rows
   // have rowq = B) whose list idx/cnt is the union of its tokens' blocks
   // (bsa_token_mask), each entry with the word of the tokens that chose it
@@ -245,6 +247,8 @@ struct EntmaxAttnArgs {
   void* O;
   Strides3 qs, ks, vs, os;
   float* tau;  // optional [batch, hq, n]: the threshold used, in units of x
+  uint32_t* live;  // optional [batch, hkv, ntile, nlw]: key tiles with some x above the
+                   // bracket's lower end, per query tile (union over the group's heads)
   int batch, hq, hkv, d, refine;
   int64_t n;
   float sm_scale, alpha;

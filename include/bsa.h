@@ -385,12 +385,18 @@ int bsa_route_entmax_backward(const bsa_shape *shape, const void *Q, const float
  *   O [batch, Hq, N, d] bf16 or fp32 (o_dtype); sm_scale 0 means 1/sqrt(d).
  *   refine in [0, 8] (0: tau = the histogram lower bound).
  *   tau_out NULL or fp32 [batch, Hq, N]: the threshold used, in units of x.
+ *   live_out NULL or uint32 [batch, Hkv, T, ceil(T / 32)], T = ceil(N / 64):
+ *         bit j % 32 of word j / 32 of row (b, g, i) is set when key tile j
+ *         holds an x above the bracket's lower end for some query of query
+ *         tile i and some query head of KV head g -- a superset of the tiles
+ *         with nonzero weights, which bsa_attend_entmax_backward then walks
+ *         alone.  With refine = 0 every causal tile is set.  Written whole.
  * Errors: BSA_ERR_INVALID (alpha <= 1, refine outside [0, 8], bad shape),
  * BSA_ERR_UNSUPPORTED (alpha > 2, fp32 inputs, N > 131072, strides).
  */
 int bsa_attend_entmax(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                       float alpha, int32_t refine, float sm_scale, void *O, int32_t o_dtype,
-                      float *tau_out, void *stream);
+                      float *tau_out, uint32_t *live_out, void *stream);
 
 /*
  * Backward of the token-level alpha-entmax attention ("AdaSplash-2",
@@ -409,13 +415,16 @@ int bsa_attend_entmax(const bsa_shape *shape, const void *Q, const void *K, cons
  *         mode BSA_PREFILL, block 64); alpha in (1, 2]; sm_scale 0: 1/sqrt(d).
  *   dO    bf16 [batch, Hq, N, d] with o_stride.
  *   tau   fp32 [batch, Hq, N]: tau_out of bsa_attend_entmax.
+ *   live  NULL (walk every causal tile) or live_out of the same
+ *         bsa_attend_entmax call: both sides then visit only its tiles.
  *   dQ, dK, dV  out, g_dtype (bf16 or BSA_F32), strides of Q, K, V.
  *   ws    bsa_workspace_size(BSA_OP_ATTEND_ENTMAX_BACKWARD, shape, 0) bytes.
  * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED (fp32 inputs, block != 64,
  * alpha > 2, strides), BSA_ERR_WORKSPACE.
  */
 int bsa_attend_entmax_backward(const bsa_shape *shape, const void *Q, const void *K,
-                               const void *V, const void *dO, const float *tau, float alpha,
+                               const void *V, const void *dO, const float *tau,
+                               const uint32_t *live, float alpha,
                                float sm_scale, void *dQ, void *dK, void *dV, int32_t g_dtype,
                                void *ws, size_t ws_bytes, void *stream);
 

@@ -105,17 +105,21 @@ def _check_grad(name, g, ref, bf16_out):
 
 @pytest.mark.parametrize("name", ["a15_gqa", "a2_sparsemax", "a125", "a175_newton", "a15_d64"])
 @pytest.mark.parametrize("g_f32", [True, False])
-def test_entmax_attention_backward_matches_oracle(name, g_f32):
-    """dQ, dK, dV from the forward's tau against the oracle's gradients with
-    exact thresholds."""
+@pytest.mark.parametrize("use_live", [False, True])
+def test_entmax_attention_backward_matches_oracle(name, g_f32, use_live):
+    """dQ, dK, dV from the forward's tau (and, with use_live, walking only
+    the forward's live key tiles) against the oracle's gradients with exact
+    thresholds."""
     w = CASES[name]
-    print(f"[entmax attention backward] {name} g_f32={g_f32}", flush=True)
+    print(f"[entmax attention backward] {name} g_f32={g_f32} live={use_live}", flush=True)
     x = parity.make(w)
     do_st, do = synth.gen_stored(w, "do")
     dO = parity.to_device(do_st, w.dtype)
-    O, tau = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=2, want_tau=True)
+    O, tau, live = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=2, want_tau=True,
+                                     want_live=True)
     grads = bsa.attend_entmax_backward(x["Q"], x["K"], x["V"], dO, tau, w.alpha,
-                                       grad_dtype=torch.float32 if g_f32 else None)
+                                       grad_dtype=torch.float32 if g_f32 else None,
+                                       live=live if use_live else None)
     torch.cuda.synchronize()
     refs = oracle.entmax_attend_backward(x["q"], x["k"], x["v"], do, w.alpha)
     e = [_check_grad(nm, g, r, not g_f32) for nm, g, r in zip(("dQ", "dK", "dV"), grads, refs)]
@@ -142,3 +146,42 @@ def test_entmax_attention_backward_sums_and_determinism():
     G = w.hq // w.hkv
     ref = dO.double().reshape(1, w.hkv, G, w.n, w.d).sum(dim=(2, 3))
     assert float((dV.sum(dim=2) - ref).abs().max()) <= 1e-2 * float(ref.abs().max())
+
+
+@pytest.mark.parametrize("name", ["a15_gqa", "a2_sparsemax", "a175_newton"])
+@pytest.mark.parametrize("refine", [2, 0])
+def test_entmax_live_tiles_cover_every_support(name, refine):
+    """The forward's live key tiles hold every key with a nonzero oracle
+    weight for every query of the tile and every head of the group (and,
+    with refine = 0, are every causal tile); the same output either way."""
+    w = CASES[name]
+    print(f"[entmax live tiles] {name} refine={refine}", flush=True)
+    x = parity.make(w)
+    O1 = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=refine)
+    O2, live = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=refine, want_live=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+    nt = (w.n + 63) // 64
+    lv = _cpu(live).astype(np.int64) & 0xFFFFFFFF
+    bits = np.zeros((w.hkv, nt, nt), bool)
+    for j in range(nt):
+        bits[:, :, j] = (lv[0, :, :, j >> 5] >> (j & 31)) & 1
+    causal = np.tril(np.ones((nt, nt), bool))
+    assert not (bits & ~causal).any()
+    if refine == 0:
+        assert (bits == causal).all()
+        return
+    G = w.hq // w.hkv
+    rng = np.random.default_rng(31)
+    req = np.array([[0, h, t] for h in range(w.hq) for t in rng.choice(w.n, 24, replace=False)])
+    _, tau, _ = oracle.entmax_attend(x["q"], x["k"], x["v"], w.alpha, req=req)
+    q = x["q"].astype(np.float64)
+    k = x["k"].astype(np.float64)
+    sc = (w.alpha - 1) / np.sqrt(w.d)
+    for (b, h, t), tt in zip(req, tau):
+        xs = sc * (k[0, h // G, :t + 1] @ q[0, h, t])
+        # (a margin far below the bracket's width keeps fp32 scores' rounding out)
+        for j in np.unique(np.nonzero(xs > tt + 1e-4)[0] // 64):
+            assert bits[h // G, t // 64, j], (h, t, j)
+    frac = bits.sum() / (causal.sum() * w.hkv)
+    print(f"live fraction {frac:.3f}")
