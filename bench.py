@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-decode", action="store_true", help="skip the decode extra")
     p.add_argument("--no-backward", action="store_true", help="skip the backward extra")
+    p.add_argument("--no-train", action="store_true",
+                   help="skip the training-pass extras (entmax routing with the prior)")
     p.add_argument("--no-entmax", action="store_true", help="skip the entmax prefill extra")
     p.add_argument("--no-long", action="store_true", help="skip the N=262144 prefill extra")
     p.add_argument("--no-token", action="store_true", help="skip the per-token routing extra")
@@ -599,20 +601,31 @@ def main():
                      "traffic": read_traffic(kernel_src), "avg_launch_ms": att_s * 1e3},
     }
     extra = {}
+
+    def done(name):  # progress on stderr; the result line stays alone on stdout
+        print(f"[bench] {name} done", file=sys.stderr, flush=True)
+
     if not a.no_backward:
         extra["backward"] = run_backward(bsa, torch, w, r, a.steps, a.warmup)
+        done("backward")
+    if not a.no_backward and not a.no_train:
         extra["train_entmax_prior"] = run_train_entmax(bsa, torch, a.steps, a.warmup)
+        done("train_entmax_prior")
         if not a.no_token:
             extra["train_token_prior"] = run_train_entmax(bsa, torch, a.steps, a.warmup,
                                                           name=TOKEN)
+            done("train_token_prior")
     if not a.no_decode:
         extra["decode"] = run_decode(bsa, torch, a.steps, a.warmup)
+        done("decode")
     for name, flag in ((ENTMAX, a.no_entmax), (LONG, a.no_long), (TOKEN, a.no_token)):
         if not flag:
             extra[name] = prefill_extra(run_prefill(bsa, torch, synth.WORKLOADS[name], a.steps,
                                                     a.warmup, keep_inputs=False))
+            done(name)
     if not a.no_entmax_attn:
         extra[ENTMAX_ATTN] = run_entmax_attn(bsa, torch, a.steps, a.warmup)
+        done(ENTMAX_ATTN)
     if extra:
         out["extra"] = extra
     if not a.no_cpu:
