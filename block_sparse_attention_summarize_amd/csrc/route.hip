@@ -85,79 +85,101 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
 // of a 16-wide d chunk: the dot products run over every d exactly once, in
 // fp32 products and fp32 accumulation as on the VALU.  Unless `fill`, tiles
 // right of every row's candidates (the candidate end grows with the row) are
-// not written at all (their readers only look at the candidates).
+// not written at all (their readers only look at the candidates).  A
+// workgroup takes `jgroup` consecutive block tiles of its row tile: the rows'
+// fragments are read from LDS into registers once and only the summaries are
+// staged per block tile (many rows, as with per-token routing, re-read them
+// far less often).
 // ---------------------------------------------------------------------------
 constexpr int kTile = 64;
 constexpr int kPad = 4;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void scores_mfma(ScoreArgs a, int fill) {
+__global__ __launch_bounds__(kThreads) void scores_mfma(ScoreArgs a, int fill, int jgroup) {
   __shared__ float qs[kTile][D + kPad];
   __shared__ float ss[kTile][D + kPad];
   const int nrt = (a.nrow + kTile - 1) / kTile;
   const int njt = (a.nblk + kTile - 1) / kTile;
+  const int ngt = (njt + jgroup - 1) / jgroup;
   int id = blockIdx.x;
-  const int jt = id % njt;
-  id /= njt;
+  const int gt = id % ngt;
+  id /= ngt;
   const int rt = id % nrt;
   const int bh = id / nrt;  // (b, q-hat head)
   const int b = bh / a.qheads;
   const int sg_row = b * a.hkv + (bh % a.qheads) / a.group;
-  const int r0 = rt * kTile, j0 = jt * kTile;
+  const int r0 = rt * kTile;
   const int rn = a.nrow - r0 < kTile ? a.nrow - r0 : kTile;
-  const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  float* out = a.scores + (static_cast<int64_t>(bh) * a.nrow + r0) * a.nblk + j0;
   const int ce = a.rule.entmax ? 0 : 1;
   const int tok_b = a.rule.mode == 2 ? a.rule.B : 1;
-  if (j0 >= (r0 + rn - 1) / tok_b + ce) {  // right of the last row's candidates
-    if (!fill) return;
-    for (int e = tid; e < kTile * kTile; e += kThreads) {
-      const int r = e / kTile, j = e % kTile;
-      if (r < rn && j < jn) out[static_cast<int64_t>(r) * a.nblk + j] = -INFINITY;
-    }
-    return;
-  }
+  const int jend = (r0 + rn - 1) / tok_b + ce;  // blocks past every row's candidates
   constexpr int V4 = D / 4;
-  const float* qg = a.qhat + (static_cast<int64_t>(bh) * a.nrow + r0) * D;
-  const float* sg = a.S + (static_cast<int64_t>(sg_row) * a.nblk + j0) * D;
-  const auto rq = make_rsrc(qg, static_cast<uint32_t>(rn) * D * 4);
-  const auto rs = make_rsrc(sg, static_cast<uint32_t>(jn) * D * 4);
-  for (int e = tid; e < kTile * V4; e += kThreads) {
-    const int r = e / V4, c = e % V4;
-    *reinterpret_cast<uint4*>(&qs[r][c * 4]) = buf_load16(rq, static_cast<uint32_t>(e) * 16);
-    *reinterpret_cast<uint4*>(&ss[r][c * 4]) = buf_load16(rs, static_cast<uint32_t>(e) * 16);
-  }
-  __syncthreads();
-  f32x4_t acc[4];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int KC = D / 16;
   const int lr = lane & 15, lk = (lane >> 4) * 4;
-#pragma unroll 2
-  for (int kc = 0; kc < D; kc += 16) {
-    const float4 av = *reinterpret_cast<const float4*>(&qs[16 * w + lr][kc + lk]);
-    float4 bv[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) bv[ct] = *reinterpret_cast<const float4*>(&ss[16 * ct + lr][kc + lk]);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv[ct].x, acc[ct], 0, 0, 0);
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv[ct].y, acc[ct], 0, 0, 0);
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv[ct].z, acc[ct], 0, 0, 0);
-      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv[ct].w, acc[ct], 0, 0, 0);
+  float4 av[KC];  // this lane's row fragments, read once
+  bool staged = false;
+  for (int jt = gt * jgroup; jt < njt && jt < (gt + 1) * jgroup; ++jt) {
+    const int j0 = jt * kTile;
+    const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
+    float* out = a.scores + (static_cast<int64_t>(bh) * a.nrow + r0) * a.nblk + j0;
+    if (j0 >= jend) {  // right of the last row's candidates
+      if (!fill) break;
+      for (int e = tid; e < kTile * kTile; e += kThreads) {
+        const int r = e / kTile, j = e % kTile;
+        if (r < rn && j < jn) out[static_cast<int64_t>(r) * a.nblk + j] = -INFINITY;
+      }
+      continue;
     }
-  }
-  // lane l holds rows 16w + 4(l/16) + i, block 16ct + l%16
+    const float* sg = a.S + (static_cast<int64_t>(sg_row) * a.nblk + j0) * D;
+    const auto rs = make_rsrc(sg, static_cast<uint32_t>(jn) * D * 4);
+    __syncthreads();  // the previous tile's summaries are read
+    if (!staged) {
+      const float* qg = a.qhat + (static_cast<int64_t>(bh) * a.nrow + r0) * D;
+      const auto rq = make_rsrc(qg, static_cast<uint32_t>(rn) * D * 4);
+      for (int e = tid; e < kTile * V4; e += kThreads) {
+        const int r = e / V4, c = e % V4;
+        *reinterpret_cast<uint4*>(&qs[r][c * 4]) = buf_load16(rq, static_cast<uint32_t>(e) * 16);
+      }
+    }
+    for (int e = tid; e < kTile * V4; e += kThreads) {
+      const int r = e / V4, c = e % V4;
+      *reinterpret_cast<uint4*>(&ss[r][c * 4]) = buf_load16(rs, static_cast<uint32_t>(e) * 16);
+    }
+    __syncthreads();
+    if (!staged) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * w + (lane >> 4) * 4 + i;
-    const int cend = (r0 + r) / tok_b + ce - j0;
+      for (int k = 0; k < KC; ++k) av[k] = *reinterpret_cast<const float4*>(&qs[16 * w + lr][16 * k + lk]);
+      staged = true;
+    }
+    f32x4_t acc[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int j = 16 * ct + lr;
-      if (r < rn && j < jn)
-        out[static_cast<int64_t>(r) * a.nblk + j] = j < cend ? acc[ct][i] * a.scale : -INFINITY;
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      float4 bv[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) bv[ct] = *reinterpret_cast<const float4*>(&ss[16 * ct + lr][16 * k + lk]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].x, bv[ct].x, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].y, bv[ct].y, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].z, bv[ct].z, acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].w, bv[ct].w, acc[ct], 0, 0, 0);
+      }
+    }
+    // lane l holds rows 16w + 4(l/16) + i, block 16ct + l%16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + (lane >> 4) * 4 + i;
+      const int cend = (r0 + r) / tok_b + ce - j0;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int j = 16 * ct + lr;
+        if (r < rn && j < jn)
+          out[static_cast<int64_t>(r) * a.nblk + j] = j < cend ? acc[ct][i] * a.scale : -INFINITY;
+      }
     }
   }
 }
@@ -841,14 +863,19 @@ __global__ __launch_bounds__(kThreads, MINW) void entmax_rows_kernel(EntmaxArgs 
 
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t stream, bool fill) {
   if (a.rule.mode != 1) {
-    const unsigned tiles = static_cast<unsigned>((a.nrow + kTile - 1) / kTile) *
-                           static_cast<unsigned>((a.nblk + kTile - 1) / kTile);
+    // block tiles per workgroup: enough row tiles to fill the chip with one
+    // workgroup each when rows are many (per-token routing), else one
+    const int nrt = (a.nrow + kTile - 1) / kTile, njt = (a.nblk + kTile - 1) / kTile;
+    const int64_t rowtiles = static_cast<int64_t>(a.batch) * a.qheads * nrt;
+    const int jgroup = rowtiles >= 4096 ? njt : 1;
+    const unsigned tiles = static_cast<unsigned>(nrt) *
+                           static_cast<unsigned>((njt + jgroup - 1) / jgroup);
     const unsigned grid = static_cast<unsigned>(a.batch) * a.qheads * tiles;
     const int f = fill ? 1 : 0;
     if (a.d == 64)
-      hipLaunchKernelGGL(scores_mfma<64>, dim3(grid), dim3(kThreads), 0, stream, a, f);
+      hipLaunchKernelGGL(scores_mfma<64>, dim3(grid), dim3(kThreads), 0, stream, a, f, jgroup);
     else
-      hipLaunchKernelGGL(scores_mfma<128>, dim3(grid), dim3(kThreads), 0, stream, a, f);
+      hipLaunchKernelGGL(scores_mfma<128>, dim3(grid), dim3(kThreads), 0, stream, a, f, jgroup);
     return hipGetLastError();
   }
   const int nchunk = (a.nblk + kChunk - 1) / kChunk;
