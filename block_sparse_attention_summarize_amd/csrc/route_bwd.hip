@@ -217,14 +217,34 @@ __global__ __launch_bounds__(256) void route_bwd_gemm(RouteBwdArgs a) {
   }
 }
 
+// The key side's partials of one KV head (its heads' and row ranges' parts)
+// summed in order into the first part, so that the tokens of a block read
+// one value instead of every part.  Four elements per thread.
+__global__ __launch_bounds__(256) void route_bwd_sum_parts(float* dsp, int parts, int64_t slab,
+                                                           int64_t total) {
+  const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;  // in [groups, slab]
+  if (e >= total) return;
+  const int64_t grp = e / slab, off = e % slab;
+  float* base = dsp + grp * parts * slab + off;
+  float4 v = *reinterpret_cast<const float4*>(base);
+  for (int p = 1; p < parts; ++p) {
+    const float4 x = *reinterpret_cast<const float4*>(base + p * slab);
+    v.x += x.x;
+    v.y += x.y;
+    v.z += x.z;
+    v.w += x.w;
+  }
+  *reinterpret_cast<float4*>(base) = v;
+}
+
 // The mean pools' adjoint, added to the gradient: every token of block r
-// gets src[r] / (tokens of the block), summed over `parts` consecutive heads
-// of src (the group's heads for dK, one head for dQ).  Four elements per
-// thread; blockIdx.y is the batch.
+// gets src[r] / (tokens of the block), summed over the first `parts` of the
+// `pstride` consecutive parts of each head of src (the group's heads for dK,
+// one head for dQ).  Four elements per thread; blockIdx.y is the batch.
 template <typename GT>
-__global__ __launch_bounds__(256) void route_bwd_spread(const float* src, int parts, void* dst,
-                                                        Strides3 st, int heads, int nrow, int B,
-                                                        int64_t n, int d) {
+__global__ __launch_bounds__(256) void route_bwd_spread(const float* src, int parts, int pstride,
+                                                        void* dst, Strides3 st, int heads,
+                                                        int nrow, int B, int64_t n, int d) {
   const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
   const int64_t per_head = n * d;
   if (e >= heads * per_head) return;
@@ -237,7 +257,7 @@ __global__ __launch_bounds__(256) void route_bwd_spread(const float* src, int pa
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int p = 0; p < parts; ++p) {
     const float4 x = *reinterpret_cast<const float4*>(
-        src + (((b * heads + hd) * parts + p) * nrow + r) * d + c);
+        src + (((b * heads + hd) * pstride + p) * nrow + r) * d + c);
     v.x += x.x;
     v.y += x.y;
     v.z += x.z;
@@ -281,20 +301,29 @@ hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t strea
     hipLaunchKernelGGL((route_bwd_gemm<128, true>), gk, dim3(256), 0, stream, a);
   }
   const int G = a.hq / a.hkv;
+  // many key-side parts (row ranges): summed once per KV head first
+  const int kparts = G * a.ksplit;
+  const int ksum = a.ksplit > 1 ? 1 : kparts;
+  if (a.ksplit > 1) {
+    const int64_t slab = static_cast<int64_t>(a.nblk) * a.d;
+    const int64_t total = static_cast<int64_t>(a.batch) * a.hkv * slab;
+    hipLaunchKernelGGL(route_bwd_sum_parts, dim3(static_cast<unsigned>((total / 4 + 255) / 256)),
+                       dim3(256), 0, stream, a.dsp, kparts, slab, total);
+  }
   auto grid_of = [&](int heads) {
     const int64_t elems = static_cast<int64_t>(heads) * a.n * a.d / 4;
     return dim3(static_cast<unsigned>((elems + 255) / 256), static_cast<unsigned>(a.batch));
   };
   if (a.g_f32) {
-    hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1,
+    hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1, 1,
                        a.dQ, a.qs, a.hq, a.nrow, a.rowq, a.n, a.d);
     hipLaunchKernelGGL(route_bwd_spread<float>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp,
-                       G * a.ksplit, a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
+                       ksum, kparts, a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
   } else {
     hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hq), dim3(256), 0, stream, a.dqh, 1,
-                       a.dQ, a.qs, a.hq, a.nrow, a.rowq, a.n, a.d);
+                       1, a.dQ, a.qs, a.hq, a.nrow, a.rowq, a.n, a.d);
     hipLaunchKernelGGL(route_bwd_spread<uint16_t>, grid_of(a.hkv), dim3(256), 0, stream, a.dsp,
-                       G * a.ksplit, a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
+                       ksum, kparts, a.dK, a.ks, a.hkv, a.nblk, a.B, a.n, a.d);
   }
   return hipGetLastError();
 }
