@@ -39,6 +39,8 @@ CASES = {
                                force=synth.FORCE_DIAG | synth.FORCE_FIRST, planted_blocks=2),
     # 8 query heads per KV head, B = 128
     "g8_b128": BASE.scaled(hq=8, hkv=1, n=128 * 5, B=128, k_total=2, planted_blocks=1),
+    # two sequences
+    "batch2": BASE.scaled(batch=2, hq=4, hkv=2, n=64 * 6 + 9, k_total=3, planted_blocks=1),
 }
 
 
@@ -243,7 +245,7 @@ def test_backward_through_prior_and_entmax_routing(name, g_f32):
     x = _inputs(w)
     S = bsa.summarize(x["K"], w.B)
     width = w.idx_width
-    wsel = torch.empty((1, w.hkv, w.nblk, width), dtype=torch.float32, device="cuda")
+    wsel = torch.empty((w.batch, w.hkv, w.nblk, width), dtype=torch.float32, device="cuda")
     idx, cnt, probs, _ = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
                                           max_iter=w.max_iter, want_probs=True, wsel=wsel)
     O, L = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt, wsel=wsel, sigma=w.sigma,

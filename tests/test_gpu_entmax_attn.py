@@ -24,6 +24,7 @@ CASES = {
     "a125": BASE.scaled(hq=4, hkv=4, n=64 * 3 + 1, alpha=1.25, q_scale=2.0, planted_blocks=1),
     "a175_newton": BASE.scaled(hq=4, hkv=2, n=64 * 3 + 9, alpha=1.75, q_scale=3.0, planted_blocks=1),
     "a15_d64": BASE.scaled(hq=6, hkv=3, d=64, n=64 * 6, planted_blocks=2),
+    "a15_batch2": BASE.scaled(batch=2, hq=4, hkv=2, n=64 * 3 + 21, planted_blocks=1),
 }
 
 
@@ -103,7 +104,8 @@ def _check_grad(name, g, ref, bf16_out):
     return float((err / scale).max())
 
 
-@pytest.mark.parametrize("name", ["a15_gqa", "a2_sparsemax", "a125", "a175_newton", "a15_d64"])
+@pytest.mark.parametrize("name", ["a15_gqa", "a2_sparsemax", "a125", "a175_newton", "a15_d64",
+                                  "a15_batch2"])
 @pytest.mark.parametrize("g_f32", [True, False])
 @pytest.mark.parametrize("use_live", [False, True])
 def test_entmax_attention_backward_matches_oracle(name, g_f32, use_live):

@@ -33,6 +33,10 @@ SMALL = {
                                                      planted_blocks=4),
     "long_b128_g2": W["bf16_long_prefill_n256k"].scaled(hq=4, hkv=2, n=128 * 9 + 127, k_total=4,
                                                         planted_blocks=3),
+    # two sequences (bf16 and fp32)
+    "bf16_batch2": W["bf16_gqa_prefill_n32k"].scaled(batch=2, hq=4, hkv=2, n=64 * 8 + 21,
+                                                     k_total=3, planted_blocks=2),
+    "fp32_batch2": W["fp32_prefill_n1k"].scaled(batch=2, n=64 * 5 + 7, hq=2, hkv=1, k_total=3),
 }
 DECODE = {
     "decode": W["bf16_decode_l128k"].scaled(batch=4, hq=8, hkv=2, n=64 * 40, k_total=9,

@@ -48,6 +48,9 @@ PRIOR = {
     # G = 3: a workgroup holds heads of two query sub-tiles
     "tokent_g3": ENT.scaled(hq=6, hkv=2, n=64 * 10 + 17, cap=5, gamma=6.0, sigma=1.2,
                             planted_blocks=3, loc_amp=2.0),
+    # two sequences
+    "tokent_batch2": ENT.scaled(batch=2, hq=4, hkv=1, n=64 * 5 + 3, cap=4, gamma=4.0, sigma=0.8,
+                                planted_blocks=2, loc_amp=2.0),
 }
 
 
@@ -106,7 +109,7 @@ def test_token_backward_through_prior_and_entmax_routing(name, g_f32):
     x = _inputs(w)
     S = bsa.summarize(x["K"], w.B)
     width = w.idx_width
-    wsel = torch.empty((1, w.hkv, w.n, width), dtype=torch.float32, device="cuda")
+    wsel = torch.empty((w.batch, w.hkv, w.n, width), dtype=torch.float32, device="cuda")
     idx, cnt, probs, _ = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
                                           max_iter=w.max_iter, want_probs=True, wsel=wsel,
                                           token=True)
@@ -162,7 +165,7 @@ def test_token_backward_full_size_sampled():
     x = _inputs(w)
     S = bsa.summarize(x["K"], w.B)
     width = w.idx_width
-    wsel = torch.empty((1, w.hkv, w.n, width), dtype=torch.float32, device="cuda")
+    wsel = torch.empty((w.batch, w.hkv, w.n, width), dtype=torch.float32, device="cuda")
     idx, cnt, _, _ = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
                                       max_iter=w.max_iter, wsel=wsel, token=True)
     O, L = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt, token=True, wsel=wsel,
@@ -210,7 +213,7 @@ def test_token_autograd_wrapper_with_prior():
     print("[token autograd wrapper]", flush=True)
     x = _inputs(w)
     S = bsa.summarize(x["K"], w.B)
-    wsel = torch.empty((1, w.hkv, w.n, w.idx_width), dtype=torch.float32, device="cuda")
+    wsel = torch.empty((w.batch, w.hkv, w.n, w.idx_width), dtype=torch.float32, device="cuda")
     idx, cnt, _, _ = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
                                       max_iter=w.max_iter, wsel=wsel, token=True)
     Q = x["Q"].clone().requires_grad_()
