@@ -1120,11 +1120,13 @@ __global__ __launch_bounds__(64) void bwd_dwsel(BwdArgs a) {
 
 // Token tiles: dL/dw of every token's list entry, sigma / w times the sum of
 // dS over the entry's keys and the group's heads (the parts of the query-side
-// workgroups holding those heads, in order).  One thread per token.
-__global__ __launch_bounds__(64) void bwd_dwsel_tok(BwdArgs a) {
+// workgroups holding those heads, in order).  Four threads per token, each
+// taking every fourth entry.
+constexpr int kDwTok = 4;
+__global__ __launch_bounds__(64 * kDwTok) void bwd_dwsel_tok(BwdArgs a) {
   const int64_t rowid = blockIdx.x;  // (pair, tile)
   const int64_t pair = rowid / a.nrow;
-  const int q = threadIdx.x;
+  const int q = threadIdx.x & 63, s0 = threadIdx.x >> 6;
   const int64_t t = (rowid % a.nrow) * 64 + q;
   if (t >= a.n) return;
   const int G = a.hq / a.hkv;
@@ -1137,7 +1139,7 @@ __global__ __launch_bounds__(64) void bwd_dwsel_tok(BwdArgs a) {
   const int64_t prow = (pair * a.n + t) * a.pwidth;
   int pc = a.pcnt[pair * a.n + t];
   pc = pc < 0 ? 0 : (pc > a.pwidth ? a.pwidth : pc);
-  for (int s = 0; s < a.pwidth; ++s) {
+  for (int s = s0; s < a.pwidth; s += kDwTok) {
     float out = 0.f;
     const int j = s < pc ? a.pidx[prow + s] : -1;
     const float wv = s < pc ? a.pw[prow + s] : 0.f;
@@ -1210,7 +1212,8 @@ hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_reduce, dim3(a.max_red * kRedSlices), dim3(256), 0, stream, a);
   if (a.dwsel && a.tok)
-    hipLaunchKernelGGL(bwd_dwsel_tok, dim3(static_cast<unsigned>(npair) * a.nrow), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dwsel_tok, dim3(static_cast<unsigned>(npair) * a.nrow), dim3(64 * kDwTok), 0,
+                       stream, a);
   else if (a.dwsel)
     hipLaunchKernelGGL(bwd_dwsel, dim3(static_cast<unsigned>(npair) * a.nrow), dim3(64), 0, stream, a);
   return hipGetLastError();
