@@ -187,3 +187,30 @@ def test_entmax_live_tiles_cover_every_support(name, refine):
             assert bits[h // G, t // 64, j], (h, t, j)
     frac = bits.sum() / (causal.sum() * w.hkv)
     print(f"live fraction {frac:.3f}")
+
+
+def test_entmax_attention_backward_full_size_live_tiles_change_nothing():
+    """The token-level entmax attention workload at its full size (N = 16384,
+    32/8 heads): walking only the forward's live key tiles gives the same
+    gradient bits as walking every causal tile (the skipped tiles hold no
+    weight, and the kept ones are summed in the same order), and the
+    gradients obey the identities of normalised weights."""
+    w = synth.WORKLOADS["entmax_attn_prefill_n16k"]
+    print("[entmax attention backward] full size", flush=True)
+    x = parity.make(w)
+    dO = torch.randn(x["Q"].shape, generator=torch.Generator().manual_seed(11)).to(
+        "cuda", torch.bfloat16)
+    _, tau, live = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, want_tau=True,
+                                     want_live=True)
+    g_live = bsa.attend_entmax_backward(x["Q"], x["K"], x["V"], dO, tau, w.alpha,
+                                        grad_dtype=torch.float32, live=live)
+    g_all = bsa.attend_entmax_backward(x["Q"], x["K"], x["V"], dO, tau, w.alpha,
+                                       grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for nm, a_, b_ in zip(("dQ", "dK", "dV"), g_live, g_all):
+        assert torch.equal(a_, b_), nm
+    dK, dV = g_live[1].double(), g_live[2].double()
+    assert float(dK.sum(dim=2).abs().max()) <= 1e-3 * float(dK.abs().sum(dim=2).max())
+    G = w.hq // w.hkv
+    ref = dO.double().reshape(w.batch, w.hkv, G, w.n, w.d).sum(dim=(2, 3))
+    assert float((dV.sum(dim=2) - ref).abs().max()) <= 1e-2 * float(ref.abs().max())
