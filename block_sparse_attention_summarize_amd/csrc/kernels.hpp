@@ -124,8 +124,9 @@ struct AttendArgs {
 };
 hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream);
 
-// Gradients of the causal block-sparse prefill attention (block rows, bf16,
-// q_len == kv_len == n) for a fixed selection idx/cnt [batch, hkv, nrow, k_max].
+// Gradients of the causal block-sparse prefill attention (bf16, q_len ==
+// kv_len == n) for a fixed selection idx/cnt [batch, hkv, nrow, k_max]: block
+// rows, or (tok) 64-query tiles listing the union of their tokens' blocks.
 // dQ, dK, dV are written with the strides of Q, K, V (elements of the
 // gradient dtype); dO has the strides of O.
 struct BwdArgs {
@@ -190,8 +191,9 @@ int attend_bwd_max_prior_width();        // k_max limit when dL/dw is requested
 int attend_bwd_tok_parts(int group);     // nparts of the token-mode dL/dw sums
 hipError_t launch_attend_backward(const BwdArgs& a, hipStream_t stream);
 
-// Routing part of the gradient of entmax-routed prefill (block rows): dL/dw
-// of the listed blocks -> dQ, dK (added to the caller's gradients).
+// Routing part of the gradient of entmax-routed prefill (block rows, or a
+// row per query token): dL/dw of the listed blocks -> dQ, dK (added to the
+// caller's gradients).
 struct RouteBwdArgs {
   const float* qhat;   // [batch, hq, nrow, d] routing queries (workspace)
   const float* S;      // [batch, hkv, nblk, d] summaries
