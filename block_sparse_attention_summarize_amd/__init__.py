@@ -2,8 +2,9 @@
 
 Thin ctypes binding of ``libbsa.so`` (C ABI in ``include/bsa.h``).  PyTorch is
 used only for device memory and streams: every step runs in the library's HIP
-kernels.  Importing this package fails loudly if the library has not been
-built (``python -m block_sparse_attention_summarize_amd.build``).
+kernels.  The library is loaded at the first call into it, which raises
+ImportError if it has not been built
+(``python -m block_sparse_attention_summarize_amd.build``).
 
 Stages (names as in the C ABI):
   summarize        keys -> per-block summaries (mean pool, or learned query)
@@ -25,13 +26,6 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsa.so")
-
-if not os.path.exists(LIB_PATH):
-    raise ImportError(
-        f"libbsa.so not found at {LIB_PATH}; build it with "
-        "`python -m block_sparse_attention_summarize_amd.build`")
-
-lib = ctypes.CDLL(LIB_PATH)
 
 F32, BF16 = 0, 1
 PREFILL, DECODE, TOKEN = 0, 1, 2
@@ -73,38 +67,66 @@ _u32 = ctypes.c_uint32
 _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 _SP = ctypes.POINTER(Shape)
-lib.bsa_summarize.argtypes = [_SP, _P, _P, _P, _P]
-lib.bsa_summarize_blocks.argtypes = [_SP, _P, _P, _P, _P, _P]
 _PP = ctypes.POINTER(Pages)
-lib.bsa_summarize_blocks_paged.argtypes = [_SP, _PP, _P, _P, _P, _P, _P]
-lib.bsa_decode_topk_paged.argtypes = [_SP, _PP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P,
-                                      _P, _i32, _P, _sz, _P]
-lib.bsa_route_topk.argtypes = [_SP, _P, _P, _P, _i32, _u32, _f32, _P, _P, _P, _P, _sz, _P]
-lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, _u32, _f32, _P,
-                                 _P, _P, _P, _P, _P, _sz, _P]
-lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32, _P, _i32, _P, _P,
-                                   _sz, _P]
-lib.bsa_attend_backward.argtypes = [_SP, _P, _P, _P, _P, _i32, _P, _P, _P, _P, _i32, _f32, _P, _f32,
-                                    _P, _P, _P, _P, _i32, _P, _sz, _P]
-lib.bsa_attend_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, _P, _i32,
-                                           _P, _sz, _P]
-lib.bsa_route_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _P, _f32, _f32, _f32, _P,
+
+
+def _declare(lib):
+    """Sets the argument and result types of every exported entry point."""
+    lib.bsa_summarize.argtypes = [_SP, _P, _P, _P, _P]
+    lib.bsa_summarize_blocks.argtypes = [_SP, _P, _P, _P, _P, _P]
+    lib.bsa_summarize_blocks_paged.argtypes = [_SP, _PP, _P, _P, _P, _P, _P]
+    lib.bsa_decode_topk_paged.argtypes = [_SP, _PP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P,
                                           _P, _i32, _P, _sz, _P]
-lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
-lib.bsa_attend_entmax.argtypes = [_SP, _P, _P, _P, _f32, _i32, _f32, _P, _i32, _P, _P, _P]
-lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
-lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
-                                _P, _sz, _P]
-for _f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_summarize_blocks_paged,
-           lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill, lib.bsa_token_mask,
-           lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged,
-           lib.bsa_attend_entmax, lib.bsa_attend_backward, lib.bsa_route_entmax_backward,
-           lib.bsa_attend_entmax_backward):
-    _f.restype = ctypes.c_int
-lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
-lib.bsa_workspace_size.restype = _sz
-lib.bsa_last_error.restype = ctypes.c_char_p
-lib.bsa_version.restype = ctypes.c_char_p
+    lib.bsa_route_topk.argtypes = [_SP, _P, _P, _P, _i32, _u32, _f32, _P, _P, _P, _P, _sz, _P]
+    lib.bsa_route_entmax.argtypes = [_SP, _P, _P, _P, _f32, _f32, _i32, _i32, _i32, _u32, _f32, _P,
+                                     _P, _P, _P, _P, _P, _sz, _P]
+    lib.bsa_attend_prefill.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _f32, _P, _f32, _P, _i32, _P, _P,
+                                       _sz, _P]
+    lib.bsa_attend_backward.argtypes = [_SP, _P, _P, _P, _P, _i32, _P, _P, _P, _P, _i32, _f32, _P, _f32,
+                                        _P, _P, _P, _P, _i32, _P, _sz, _P]
+    lib.bsa_attend_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, _P, _i32,
+                                               _P, _sz, _P]
+    lib.bsa_route_entmax_backward.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _P, _f32, _f32, _f32, _P,
+                                              _P, _i32, _P, _sz, _P]
+    lib.bsa_token_mask.argtypes = [_SP, _P, _P, _i32, _P, _P, _P, _P]
+    lib.bsa_attend_entmax.argtypes = [_SP, _P, _P, _P, _f32, _i32, _f32, _P, _i32, _P, _P, _P]
+    lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
+    lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
+                                    _P, _sz, _P]
+    for f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_summarize_blocks_paged,
+               lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill, lib.bsa_token_mask,
+               lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged,
+               lib.bsa_attend_entmax, lib.bsa_attend_backward, lib.bsa_route_entmax_backward,
+               lib.bsa_attend_entmax_backward):
+        f.restype = ctypes.c_int
+    lib.bsa_workspace_size.argtypes = [_i32, _SP, _i32]
+    lib.bsa_workspace_size.restype = _sz
+    lib.bsa_last_error.restype = ctypes.c_char_p
+    lib.bsa_version.restype = ctypes.c_char_p
+
+
+class _Library:
+    """libbsa.so, loaded at the first call into it.
+
+    Loading on first use lets the package be imported to build the library
+    from a clean checkout; any call made before the library exists raises
+    ImportError (there is no fallback path)."""
+
+    _cdll = None
+
+    def __getattr__(self, name):
+        if _Library._cdll is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"libbsa.so not found at {LIB_PATH}; build it with "
+                    "`python -m block_sparse_attention_summarize_amd.build`")
+            cdll = ctypes.CDLL(LIB_PATH)
+            _declare(cdll)
+            _Library._cdll = cdll
+        return getattr(_Library._cdll, name)
+
+
+lib = _Library()
 
 
 class BsaError(RuntimeError):
