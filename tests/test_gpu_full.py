@@ -1,11 +1,14 @@
 """Parity at the full sizes of the benchmark's workloads, in the launch
 configuration the benchmark times.
 
-Routing is checked on every row (bit-exact where the gap rule applies, valid
-elsewhere; per-token routing on sampled tokens).  Attention is checked in full where the oracle finishes in
-seconds (fp32 prefill N=1024, decode) and otherwise on every query token of a
-few seeded query blocks for every head (the first, the last, and seeded
-picks), against the fp64 oracle attending over the GPU's own selection.
+Routing is checked on every row (bit-exact where the gap or margin rule
+applies, valid elsewhere; per-token routing on sampled tokens).  Attention is
+checked in full where the oracle finishes in seconds (fp32 prefill N=1024,
+decode) and otherwise on every query token of sampled query blocks, for every
+head of each KV head's group: per KV head 64 seeded blocks, the first and the
+last, and the blocks holding planted queries (at most 64 of them), against the
+fp64 oracle attending over the GPU's own selection (split over host threads,
+each oracle call single-threaded).
 Each test generates its inputs (up to ~26 GB of host memory for the decode
 cache) and frees them before the next."""
 import gc
@@ -25,32 +28,29 @@ if not torch.cuda.is_available():  # pragma: no cover
 import block_sparse_attention_summarize_amd as bsa  # noqa: E402
 
 W = synth.WORKLOADS
+# share of entmax rows whose selection equals the oracle's exactly (rows
+# without a margin may differ near a threshold or at the cap and are then
+# checked for validity)
+ENTMAX_MATCH_FLOOR = 0.99
 
 
 def _cpu(t):
     return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-def _sample_blocks(w, extra, seed):
-    rng = np.random.default_rng(seed)
-    picks = {0, w.nblk - 1} | set(rng.choice(w.nblk, size=extra, replace=False).tolist())
-    return sorted(picks)
-
-
-def _requests(w, blocks):
-    Bq = w.B
-    return np.array([[0, h, t] for i in blocks for h in range(w.hq)
-                     for t in range(i * Bq, min((i + 1) * Bq, w.n))], np.int64)
-
-
-def _check_sampled(w, x, O, idx, cnt, blocks):
-    req = _requests(w, blocks)
-    ref, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, idx, cnt, req=req)
+def _check_sampled(w, x, O, idx, cnt):
+    """Attention on every token of the sampled query blocks (per KV head: 64
+    seeded blocks, the first and last, and the planted-query blocks), every
+    head of the group, against the oracle over the GPU's selection."""
+    blocks = parity.sample_query_blocks(w)
+    req = parity.block_requests(w, blocks)
+    ref, pairs = parity.attend_threads(x["q"], x["k"], x["v"], w.B, idx, cnt, req)
     Oh = _cpu(O)
     got = Oh[req[:, 0], req[:, 1], req[:, 2]]
     worst = parity.check_attention(w, got, ref, w.dtype == "f32")
-    print(f"sampled query blocks {blocks}: {len(req)} rows, {int(pairs.sum())} pairs, "
-          f"max abs err {worst:.3e}", flush=True)
+    nblk = sum(len(v) for v in blocks.values())
+    print(f"sampled {nblk} query blocks over {len(blocks)} KV heads: {len(req)} rows, "
+          f"{int(pairs.sum())} pairs, max abs err {worst:.3e}", flush=True)
 
 
 def _free():
@@ -83,7 +83,7 @@ def test_full_topk_prefill(name):
         worst = parity.check_attention(w, _cpu(O).reshape(out.shape), out, w.dtype == "f32")
         print(f"attention: all rows, max abs err {worst:.3e}", flush=True)
     else:
-        _check_sampled(w, x, O, gi, gc_, _sample_blocks(w, 3, w.seed + 100))
+        _check_sampled(w, x, O, gi, gc_)
     del x, S, O, idx, cnt, ws
     _free()
 
@@ -97,31 +97,27 @@ def test_full_entmax_prefill():
                                             max_iter=w.max_iter, want_probs=True, want_tau=True)
     O = bsa.attend_prefill(x["Q"], x["K"], x["V"], w.B, idx, cnt)
     torch.cuda.synchronize()
-    ref = oracle.route_entmax(oracle.qpool(x["q"], w.B), oracle.summarize(x["k"], w.B), w.B,
-                              w.alpha, w.gamma, w.cap, w.force, max_iter=w.max_iter)
+    qh, Sref = oracle.qpool(x["q"], w.B), oracle.summarize(x["k"], w.B)
+    ref = oracle.route_entmax(qh, Sref, w.B, w.alpha, w.gamma, w.cap, w.force,
+                              max_iter=w.max_iter)
+    ref_x = oracle.route_entmax(qh, Sref, w.B, w.alpha, w.gamma, w.cap, w.force,
+                                max_iter=parity.EXACT_ITERS)
+    own = np.arange(w.nblk)
+    lg = parity.entmax_logits(w, qh, Sref, own)
     gp, gt = _cpu(probs), _cpu(tau)
-    rt = ref["tau"]
-    fin = np.isfinite(rt)
-    assert np.array_equal(fin, np.isfinite(gt))
-    clear = parity.entmax_clear(w, ref)
-    assert np.abs(gt[fin & clear] - rt[fin & clear]).max(initial=0) < 2e-5
-    assert np.abs(gp - ref["probs"])[clear].max(initial=0) < 2e-5
-    # the probabilities of every resolved head-row sum to one
-    sums = gp.sum(-1)[fin]
-    assert np.abs(sums - 1).max() < 1e-4
+    # the probabilities of every head-row with candidates sum to one
+    fin = np.isfinite(ref["tau"])
+    assert np.abs(gp.sum(-1)[fin] - 1).max() < 1e-4
     gi, gc_ = _cpu(idx), _cpu(cnt)
-    G = w.hq // w.hkv
-    row_clear = clear.reshape(w.batch, w.hkv, G, -1).all(axis=2) & (ref["capgap"] > parity.GAP)
-    same = (gi == ref["idx"]).all(-1) & (gc_ == ref["cnt"])
-    assert same[row_clear].all(), f"{int((~same & row_clear).sum())} clear rows differ"
-    for r in zip(*np.nonzero(~same)):
-        sel = gi[r][:gc_[r]]
-        assert r[2] in sel and np.all(np.diff(sel) > 0) and sel.max() <= r[2]
-    print(f"routing: rows {same.size}, clear {int(row_clear.sum())}, match {same.mean():.4f}, "
-          f"mean support {float((ref['probs'] > 0).sum(-1).mean()):.1f}, "
-          f"mean count {float(gc_.mean()):.1f}", flush=True)
-    del probs, tau, gp, ref
-    _check_sampled(w, x, O, gi, gc_, _sample_blocks(w, 1, w.seed + 100))
+    rep = {}
+    parity.check_entmax_rows(w, gi, gc_, gp, gt, ref, ref_x, lg, own, rep)
+    rep["mean_support"] = float((ref["probs"] > 0).sum(-1).mean())
+    print(f"routing: {rep}", flush=True)
+    # rows without a margin may still differ near a threshold or at the cap;
+    # on this workload they almost never do
+    assert rep["match_rate"] >= ENTMAX_MATCH_FLOOR, rep
+    del probs, tau, gp, gt, ref, ref_x, lg
+    _check_sampled(w, x, O, gi, gc_)
     del x, S, O, idx, cnt
     _free()
 
@@ -155,7 +151,7 @@ def test_full_decode_step():
 def test_full_token_entmax_prefill():
     """Per-token entmax routing at full size: sampled tokens' rows are checked
     one by one (a token's row is the decode row of a cache of length t + 1),
-    the tile masks of every tile, and attention on every query of a few
+    the tile masks of every tile, and attention on every query of 18
     sampled tiles for every head."""
     w = W["token_entmax_prefill_n32k"]
     print(f"[full token entmax prefill] {w}", flush=True)
@@ -173,33 +169,24 @@ def test_full_token_entmax_prefill():
     Sref = oracle.summarize(x["k"], w.B)
     assert np.abs(_cpu(S) - Sref).max() < 2e-6
     rng = np.random.default_rng(w.seed + 200)
-    tiles = sorted({0, (w.n - 1) // 64} | set(rng.choice(w.n // 64, size=2, replace=False).tolist()))
-    toks = sorted(set(rng.choice(w.n, size=96, replace=False).tolist())
+    tiles = sorted({0, (w.n - 1) // 64} | set(rng.choice(w.n // 64, size=16, replace=False).tolist()))
+    toks = sorted(set(rng.choice(w.n, size=256, replace=False).tolist())
                   | {t for tl in tiles for t in (tl * 64, tl * 64 + 63)} | {w.n - 1})
     gp, gt = _cpu(probs), _cpu(tau)
-    checked = same_n = clear_n = 0
-    for t in toks:
-        one = oracle.route_entmax(x["q"][:, :, t:t + 1].astype(np.float64), Sref, w.B, w.alpha,
-                                  w.gamma, w.cap, w.force, max_iter=w.max_iter,
-                                  mode=oracle.MODE_DECODE, kv_lens=[t + 1])
-        clear = parity.entmax_clear(w, one)[:, :, 0]
-        fin = np.isfinite(one["tau"][:, :, 0])
-        assert np.array_equal(fin, np.isfinite(gt[:, :, t]))
-        m = fin & clear
-        assert np.abs(gt[:, :, t][m] - one["tau"][:, :, 0][m]).max(initial=0) < 2e-5
-        assert np.abs(gp[:, :, t] - one["probs"][:, :, 0])[clear].max(initial=0) < 2e-5
-        row_clear = clear.reshape(w.batch, w.hkv, -1).all(-1) & (one["capgap"][:, :, 0] > parity.GAP)
-        same = (gi[:, :, t] == one["idx"][:, :, 0]).all(-1) & (gc[:, :, t] == one["cnt"][:, :, 0])
-        assert same[row_clear].all(), f"token {t}: clear rows differ"
-        assert np.abs(gw[:, :, t] - one["wsel"][:, :, 0])[row_clear].max(initial=0) < 2e-5
-        for g in np.nonzero(~same[0])[0]:
-            sel = gi[0, g, t, :gc[0, g, t]]
-            assert t // w.B in sel and np.all(np.diff(sel) > 0) and sel.max() <= t // w.B
-        checked += same.size
-        same_n += int(same.sum())
-        clear_n += int(row_clear.sum())
-    print(f"routing: {checked} sampled rows, clear {clear_n}, match {same_n / checked:.4f}, "
-          f"mean count {gc.mean():.1f}", flush=True)
+    toks = np.array(toks)
+    ones = [oracle.route_entmax(x["q"][:, :, t:t + 1].astype(np.float64), Sref, w.B, w.alpha,
+                                w.gamma, w.cap, w.force, max_iter=it, mode=oracle.MODE_DECODE,
+                                kv_lens=[t + 1])
+            for it in (w.max_iter, parity.EXACT_ITERS) for t in toks]
+    ref, ref_x = ({k: np.concatenate([o[k] for o in part], axis=2) for k in part[0]}
+                  for part in (ones[:len(toks)], ones[len(toks):]))
+    own = toks // w.B
+    lg = parity.entmax_logits(w, x["q"][:, :, toks].astype(np.float64), Sref, own)
+    rep = {}
+    parity.check_entmax_rows(w, gi[:, :, toks], gc[:, :, toks], gp[:, :, toks], gt[:, :, toks],
+                             ref, ref_x, lg, own, rep, gw=gw[:, :, toks])
+    print(f"routing: {len(toks)} sampled tokens, {rep}", flush=True)
+    assert rep["match_rate"] >= ENTMAX_MATCH_FLOOR, rep
     # the tile masks of every tile, bit-exact against the oracle's union of
     # the GPU's per-token selections
     ru, rn, rb = oracle.token_union(gi, gc, w.nblk)
@@ -209,8 +196,8 @@ def test_full_token_entmax_prefill():
     del probs, tau, gp, gu, gb, ru, rb, uidx, ubits
     req = np.array([[0, h, t] for tl in tiles for h in range(w.hq)
                     for t in range(tl * 64, min(tl * 64 + 64, w.n))], np.int64)
-    ref, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, gi, gc, req=req,
-                               mode=oracle.MODE_TOKEN, wsel=gw, sigma=w.sigma)
+    ref, pairs = parity.attend_threads(x["q"], x["k"], x["v"], w.B, gi, gc, req,
+                                       mode=oracle.MODE_TOKEN, wsel=gw, sigma=w.sigma)
     got = _cpu(O)[req[:, 0], req[:, 1], req[:, 2]]
     worst = parity.check_attention(w, got, ref, False)
     print(f"attention: tiles {tiles}, {len(req)} rows, {int(pairs.sum())} pairs, "

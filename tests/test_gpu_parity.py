@@ -185,29 +185,19 @@ def test_route_entmax(name):
     idx, cnt, probs, tau = bsa.route_entmax(x["Q"], S, w.B, w.alpha, w.gamma, w.cap, w.force,
                                             max_iter=w.max_iter, want_probs=True, want_tau=True,
                                             wsel=wsel)
-    ref = oracle.route_entmax(oracle.qpool(x["q"], w.B), oracle.summarize(x["k"], w.B), w.B,
-                              w.alpha, w.gamma, w.cap, w.force, max_iter=w.max_iter)
-    gp, gt = _cpu(probs), _cpu(tau)
-    rt = ref["tau"]
-    fin = np.isfinite(rt)
-    assert np.array_equal(fin, np.isfinite(gt))
-    # rows whose support is decided with margin: tau and p agree to fp32 rounding
-    clear = parity.entmax_clear(w, ref)
-    assert np.abs(gt[fin & clear] - rt[fin & clear]).max(initial=0) < 2e-5
-    assert np.abs(gp - ref["probs"])[clear].max(initial=0) < 2e-5
-    gi, gc = _cpu(idx), _cpu(cnt)
-    row_clear = clear.reshape(w.batch, w.hkv, w.hq // w.hkv, -1).all(axis=2) & (ref["capgap"] > parity.GAP)
-    same = (gi == ref["idx"]).all(-1) & (gc == ref["cnt"])
-    assert same[row_clear].all(), f"{int((~same & row_clear).sum())} clear rows differ"
-    # routing weights of the listed blocks (group-mean p, 1 when forced)
-    gw = _cpu(wsel)
-    assert np.abs(gw - ref["wsel"])[row_clear].max(initial=0) < 2e-5
-    # every row: the diagonal is present, ids ascending and within the causal range
-    for r in zip(*np.nonzero(~same)):
-        sel = gi[r][:gc[r]]
-        assert r[2] in sel and np.all(np.diff(sel) > 0) and sel.max() <= r[2]
-    print(f"rows {same.size}, clear {int(row_clear.sum())}, match {same.mean():.4f}, "
-          f"mean support {float((ref['probs'] > 0).sum(-1).mean()):.1f}")
+    qh, Sref = oracle.qpool(x["q"], w.B), oracle.summarize(x["k"], w.B)
+    ref = oracle.route_entmax(qh, Sref, w.B, w.alpha, w.gamma, w.cap, w.force,
+                              max_iter=w.max_iter)
+    ref_x = oracle.route_entmax(qh, Sref, w.B, w.alpha, w.gamma, w.cap, w.force,
+                                max_iter=parity.EXACT_ITERS)
+    own = np.arange(w.nblk)
+    lg = parity.entmax_logits(w, qh, Sref, own)
+    # exact on rows decided with margin; threshold, weights, support, count
+    # and cap order valid on every row
+    rep = {}
+    parity.check_entmax_rows(w, _cpu(idx), _cpu(cnt), _cpu(probs), _cpu(tau), ref, ref_x, lg,
+                             own, rep, gw=_cpu(wsel))
+    print(rep)
 
 
 @pytest.mark.parametrize("sigma", [0.5, 1.0])
