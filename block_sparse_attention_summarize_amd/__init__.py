@@ -38,7 +38,8 @@ STATUS = {0: "BSA_OK", -1: "BSA_ERR_INVALID", -2: "BSA_ERR_UNSUPPORTED", -3: "BS
 
 EXPORTS = ("bsa_summarize", "bsa_summarize_blocks", "bsa_summarize_blocks_paged",
            "bsa_route_topk", "bsa_route_entmax", "bsa_attend_prefill", "bsa_token_mask",
-           "bsa_attend_decode", "bsa_decode_topk", "bsa_decode_topk_paged", "bsa_attend_entmax",
+           "bsa_attend_decode", "bsa_decode_topk", "bsa_decode_topk_noalloc",
+           "bsa_decode_topk_paged", "bsa_attend_entmax",
            "bsa_attend_backward", "bsa_route_entmax_backward", "bsa_attend_entmax_backward",
            "bsa_workspace_size",
            "bsa_last_error", "bsa_version")
@@ -93,9 +94,12 @@ def _declare(lib):
     lib.bsa_attend_decode.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _i32, _f32, _P, _i32, _P, _sz, _P]
     lib.bsa_decode_topk.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P, _P, _i32,
                                     _P, _sz, _P]
+    lib.bsa_decode_topk_noalloc.argtypes = [_SP, _P, _P, _P, _P, _P, _i32, _u32, _f32, _f32, _P, _P,
+                                            _P, _i32, _P]
     for f in (lib.bsa_summarize, lib.bsa_summarize_blocks, lib.bsa_summarize_blocks_paged,
                lib.bsa_route_topk, lib.bsa_route_entmax, lib.bsa_attend_prefill, lib.bsa_token_mask,
-               lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_paged,
+               lib.bsa_attend_decode, lib.bsa_decode_topk, lib.bsa_decode_topk_noalloc,
+               lib.bsa_decode_topk_paged,
                lib.bsa_attend_entmax, lib.bsa_attend_backward, lib.bsa_route_entmax_backward,
                lib.bsa_attend_entmax_backward):
         f.restype = ctypes.c_int
@@ -500,6 +504,29 @@ def decode_step(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None, score_sc
     _check(lib.bsa_decode_topk(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(S),
                                _ptr(kv_lens), k_total, force, score_scale, sm_scale, _ptr(idx),
                                _ptr(cnt), _ptr(O), _dtype_code(O), _ptr(wsb), n, _stream(q)))
+    return O, idx, cnt
+
+
+def decode_step_noalloc(q, K, V, S, B, k_total, force=FORCE_TAIL, kv_lens=None,
+                        score_scale=0.0, sm_scale=0.0, out_dtype=None, out=None, sel=None):
+    """decode_step through bsa_decode_topk_noalloc: no workspace; the
+    library's static per-GPU scratch is used instead (calls overlapping on
+    one GPU race).  Returns (O, idx, cnt)."""
+    b, hq, _, d = q.shape
+    hkv, L = K.shape[1], K.shape[2]
+    odt = out_dtype or q.dtype
+    O = out if out is not None else torch.empty((b, hq, 1, d), dtype=odt, device=q.device)
+    if sel is not None:
+        idx, cnt = sel
+    else:
+        idx = torch.empty((b, hkv, 1, k_total), dtype=torch.int32, device=q.device)
+        cnt = torch.empty((b, hkv, 1), dtype=torch.int32, device=q.device)
+    shape = make_shape(batch=b, hq=hq, hkv=hkv, d=d, B=B, dtype=_dtype_code(q), mode=DECODE,
+                       q_len=1, kv_len=L, q=q, k=K, v=V, o=O)
+    _check(lib.bsa_decode_topk_noalloc(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(S),
+                                       _ptr(kv_lens), k_total, force, score_scale, sm_scale,
+                                       _ptr(idx), _ptr(cnt), _ptr(O), _dtype_code(O),
+                                       _stream(q)))
     return O, idx, cnt
 
 

@@ -3,9 +3,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "bsa.h"
@@ -1185,6 +1187,77 @@ int bsa_decode_topk(const bsa_shape* s, const void* Q, const void* K, const void
                     int32_t o_dtype, void* ws, size_t ws_bytes, void* stream) {
   return decode_topk_impl(s, nullptr, Q, K, V, S, kv_lens, k_total, force, score_scale, sm_scale,
                           idx, cnt, O, o_dtype, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of bsa_decode_topk_noalloc: one copy per GPU, created with the
+// code object.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is ever
+// handed to kernels.
+__device__ __align__(256) unsigned char scratch[BSA_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int static_scratch(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BSA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      const hipError_t ge = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (ge != hipSuccess || !p)
+        return fail(BSA_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(ge));
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bsa_decode_topk_noalloc(const bsa_shape* s, const void* Q, const void* K, const void* V,
+                            const float* S, const int32_t* kv_lens, int32_t k_total,
+                            uint32_t force, float score_scale, float sm_scale, int32_t* idx,
+                            int32_t* cnt, void* O, int32_t o_dtype, void* stream) {
+  int rc;
+  if ((rc = check_shape(s)) != BSA_OK) return rc;
+  if (s->mode != BSA_DECODE) return fail(BSA_ERR_INVALID, "bsa_decode_topk_noalloc needs BSA_DECODE");
+  if ((rc = check_force(s, force)) != BSA_OK) return rc;
+  if (k_total < 1 || k_total < popcount3(force))
+    return fail(BSA_ERR_INVALID, "k_total (%d) must be >= 1 and >= the number of forced blocks",
+                k_total);
+  if ((idx == nullptr) != (cnt == nullptr))
+    return fail(BSA_ERR_INVALID, "idx and cnt must both be given or both be NULL");
+  {
+    // every argument is checked before the device is touched
+    bsa::DecodeArgs probe;
+    if ((rc = decode_args(s, Q, K, V, S, kv_lens, idx, cnt, k_total, force, score_scale, sm_scale,
+                          O, o_dtype, 1, 1, probe, nullptr)) != BSA_OK)
+      return rc;
+  }
+  const int parts = decode_parts(s, k_total, force);
+  const size_t need = decode_ws(s, parts, k_total, true).total;
+  if (need > BSA_STATIC_SCRATCH_BYTES)
+    return fail(BSA_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of scratch; the static array holds %zu",
+                need, static_cast<size_t>(BSA_STATIC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (need > 0 && (rc = static_scratch(&ws)) != BSA_OK) return rc;
+  return decode_topk_impl(s, nullptr, Q, K, V, S, kv_lens, k_total, force, score_scale, sm_scale,
+                          idx, cnt, O, o_dtype, ws, need, stream);
 }
 
 int bsa_decode_topk_paged(const bsa_shape* s, const bsa_pages* pages, const void* Q,

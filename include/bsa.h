@@ -40,7 +40,9 @@
  * Conventions shared by every call
  *   - Tensors are device pointers owned by the caller.  The library never
  *     allocates device memory; scratch space is the caller's `ws` buffer of at
- *     least bsa_workspace_size(...) bytes (NULL allowed when that size is 0).
+ *     least bsa_workspace_size(...) bytes (NULL allowed when that size is 0),
+ *     except in bsa_decode_topk_noalloc, which uses a static device array of
+ *     the library instead.
  *   - Q, K, V, O are [batch, heads, tokens, head_dim] with head_dim contiguous
  *     and explicit element strides for (batch, head, token).  Base pointers
  *     must be 16-byte aligned and strides multiples of 8 elements (bf16) or 4
@@ -60,8 +62,9 @@
  *     but never dereferenced out of bounds: lengths are clamped to
  *     [1, kv_len], counts to [0, width], and block ids outside the valid range
  *     are skipped.
- *   - The library holds no state; calls on different streams may overlap as
- *     long as their output buffers and workspaces do not.
+ *   - The library holds no state besides that static array; calls on
+ *     different streams may overlap as long as their output buffers and
+ *     workspaces do not (bsa_decode_topk_noalloc calls on one GPU never may).
  */
 #ifndef BSA_H
 #define BSA_H
@@ -499,6 +502,27 @@ int bsa_decode_topk_paged(const bsa_shape *shape, const bsa_pages *pages, const 
                           int32_t k_total, uint32_t force_flags, float score_scale,
                           float sm_scale, int32_t *idx, int32_t *cnt, void *O, int32_t o_dtype,
                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * bsa_decode_topk with no workspace argument, for callers that cannot
+ * allocate device memory: code recorded into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc.  It calls no allocator.  The
+ * scratch that the partitioned decode path needs (routing candidates and
+ * partial softmax states, used when batch x n_kv_heads is small) lives in a
+ * static device array of the library, BSA_STATIC_SCRATCH_BYTES on each GPU
+ * the library runs on, held until the process ends; every slot a call reads
+ * is written earlier in the same call, so no clearing is needed.  All calls
+ * on one GPU share that array: calls that overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  A shape whose
+ * scratch would exceed the array returns BSA_ERR_UNSUPPORTED before anything
+ * is enqueued.  Arguments, outputs and other errors as bsa_decode_topk.
+ */
+#define BSA_STATIC_SCRATCH_BYTES (4u << 20)
+int bsa_decode_topk_noalloc(const bsa_shape *shape, const void *Q, const void *K,
+                            const void *V, const float *S, const int32_t *kv_lens,
+                            int32_t k_total, uint32_t force_flags, float score_scale,
+                            float sm_scale, int32_t *idx, int32_t *cnt, void *O,
+                            int32_t o_dtype, void *stream);
 
 /* Scratch bytes needed by `op` for this shape; k_or_cap is k_total (top-k),
  * cap (entmax) or k_max (attend).  Returns 0 when none is needed or the

@@ -334,3 +334,18 @@ def test_backward_prior_and_routing_backward_validation():
     assert route_backward(s, dwsel=None) == -1 and "dwsel" in err()
     assert route_backward(s, width=0) == -1
     assert route_backward(s, g_dtype=5) == -2
+
+
+def test_decode_noalloc_validation():
+    """The allocation-free decode entry point validates on the host before it
+    looks up its static scratch (no HIP call on these paths)."""
+    def call(s, k=5, force=bsa.FORCE_TAIL, O=FAKE):
+        return lib.bsa_decode_topk_noalloc(None if s is None else ctypes.byref(s), FAKE, FAKE,
+                                           FAKE, FAKE, None, k, force, 0.0, 0.0, FAKE, FAKE, O,
+                                           bsa.BF16, None)
+    dec = dict(mode=bsa.DECODE, q_len=1, kv_len=4096)
+    assert call(None) == -1 and "NULL" in err()
+    assert call(shape()) == -1 and "BSA_DECODE" in err()
+    assert call(shape(**dec), k=0) == -1 and "k_total" in err()
+    assert call(shape(**dec), force=8) == -1
+    assert call(shape(**dec), O=None) == -1
