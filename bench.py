@@ -5,30 +5,35 @@ MI355X.
 A step is one pass of the whole hot path over one batch of seeded synthetic
 input already resident in HBM: key summaries (Stage 0), top-k routing
 (Stage 1) and fine attention over the selected blocks (Stage 2).  The headline
-workload is causal bf16 GQA prefill, batch 1, 32 query / 8 KV heads,
-N = 32768, d = 128, B = 64, top-16 blocks per 64-query block.
+workload is the largest single-GPU prefill: causal bf16 GQA prefill, batch 1,
+16 query / 2 KV heads, N = 262144, d = 128, B = 128, top-32 blocks per
+128-query block (diagonal and block 0 always kept).
 
 Printed: one JSON line.  `value` is prefill TFLOP/s counted on the selected
 blocks only (4 d flops per causal query-key pair actually attended) over the
 whole step.  `roofline` covers the dominant kernel (the MFMA attention) timed
-with HIP events on its stream inside the timed region; `cpu_baseline` is the
-fp64 oracle timed on this host on a bounded sample.  `extra` holds the other
-workloads of the method: `decode` (batch 16, 32/8 heads, L = 131072, top-32 +
-tail; GB/s with the 256 MB last-level cache flushed between steps; `paged`:
-the same step over the cache stored as a shuffled pool of 64-token pages),
-`entmax_prefill_n64k` (alpha = 1.5 entmax routing, N = 65536, cap 64),
-`bf16_long_prefill_n256k` (16/2 heads, N = 262144, B = 128, top-32) and
+with HIP events on its stream inside the timed region (mean, median and min
+launch time); `cpu_baseline` is the fp64 oracle timed on one pinned host core
+on a bounded sample of the same workload, with the host described.  `extra`
+holds the other workloads: `bf16_gqa_prefill_n32k` (32/8 heads, N = 32768,
+B = 64, top-16), `fp32_prefill_n1k` (fp32, 2 heads, N = 1024, d = 64, top-4),
+`decode` (batch 16, 32/8 heads, L = 131072, top-32 + tail; GB/s with the
+last-level cache flushed between steps; `paged`: the same step over the
+cache stored as a shuffled pool of 64-token pages), `entmax_prefill_n64k`
+(alpha = 1.5 entmax routing, N = 65536, cap 64) and
 `token_entmax_prefill_n32k` (every query token routed by alpha-entmax, cap
 32, attention over 64-query tile masks), each with its step time, per-stage
 times and attention TFLOP/s, and `entmax_attn_prefill_n16k` (token-level
 alpha-entmax attention, dense causal with zero key tiles skipped) timed
 beside the dense causal softmax of the same inputs (every block selected),
-`backward` (the gradients dQ, dK, dV of the headline attention for its
+`backward` (the gradients dQ, dK, dV of the N = 32768 attention for its
 selection, beside the forward that feeds them), `train_entmax_prior` (a
 training pass of entmax routing with the prior-induced softmax, sigma = 1, on
 the N = 65536 entmax inputs: forward, then the attention gradients with
 dL/dw and the routing gradient into dQ and dK) and `train_token_prior` (the
-same pass with every query token routed, on the per-token inputs).
+same pass with every query token routed, on the per-token inputs);
+`cpu_baselines` times the oracle on the other workloads (in full where it
+finishes in seconds, else on a sample).
 """
 from __future__ import annotations
 
@@ -46,13 +51,20 @@ import synth
 HERE = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-HEADLINE = "bf16_gqa_prefill_n32k"
+# fp32 VALU without packed fp32 (disabled in every kernel here): 256 CUs x 4
+# SIMDs x 16 lanes x 2 flops (fma) x 2.4 GHz
+PEAK_F32_VALU_TFLOPS = 78.6
+HEADLINE = "bf16_long_prefill_n256k"
+GQA32K = "bf16_gqa_prefill_n32k"
+FP32 = "fp32_prefill_n1k"
 DECODE = "bf16_decode_l128k"
 ENTMAX = "entmax_prefill_n64k"
 LONG = "bf16_long_prefill_n256k"
 TOKEN = "token_entmax_prefill_n32k"
 ENTMAX_ATTN = "entmax_attn_prefill_n16k"
-COUNTERS = os.path.join(HERE, "profiles", "attend_prefill_bf16_gqa_n32k_counters.txt")
+PROFILES = os.path.join(HERE, "profiles")
+COUNTERS = {HEADLINE: "attend_prefill_bf16_long_n256k_counters.txt",
+            GQA32K: "attend_prefill_bf16_gqa_n32k_counters.txt"}
 
 
 def parse():
@@ -60,18 +72,24 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--workload", default=HEADLINE,
+                   help="prefill workload of the headline line (a profiling aid)")
+    p.add_argument("--only", action="store_true",
+                   help="the headline workload alone: no extras, no CPU baseline")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--no-decode", action="store_true", help="skip the decode extra")
     p.add_argument("--no-backward", action="store_true", help="skip the backward extra")
     p.add_argument("--no-train", action="store_true",
                    help="skip the training-pass extras (entmax routing with the prior)")
     p.add_argument("--no-entmax", action="store_true", help="skip the entmax prefill extra")
-    p.add_argument("--no-long", action="store_true", help="skip the N=262144 prefill extra")
+    p.add_argument("--no-gqa", action="store_true",
+                   help="skip the N=32768 prefill extra (and the backward that uses it)")
+    p.add_argument("--no-fp32", action="store_true", help="skip the fp32 N=1024 prefill extra")
     p.add_argument("--no-token", action="store_true", help="skip the per-token routing extra")
     p.add_argument("--no-entmax-attn", action="store_true",
                    help="skip the token-level entmax attention extra")
-    p.add_argument("--cpu-sample-blocks", type=int, default=12)
+    p.add_argument("--cpu-sample-blocks", type=int, default=6,
+                   help="query blocks (all heads) of the headline's CPU-baseline sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
     return p.parse_args()
@@ -90,10 +108,12 @@ def copy_calibration(mib, reps=3):
 
 
 def device_inputs(w, torch):
-    """Seeded q, k, v of workload w: exact fp32 host copies and device tensors."""
-    out = {}
+    """Seeded q, k, v of workload w: exact fp32 host copies, device tensors and
+    the SHA-256 (first 16 hex digits) of each stored tensor."""
+    out = {"sha256": {}}
     for name in ("q", "k", "v"):
         stored, exact = synth.gen_stored(w, name)
+        out["sha256"][name] = hashlib.sha256(np.ascontiguousarray(stored).data).hexdigest()[:16]
         if w.dtype == "bf16":
             dev = torch.from_numpy(stored.view(np.int16)).to("cuda").view(torch.bfloat16)
         else:
@@ -138,13 +158,15 @@ def source_digest(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(kernel_src):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source."""
-    if not os.path.exists(COUNTERS):
+def read_traffic(workload, kernel_src):
+    """HBM bytes per launch from the committed counter summary of the
+    workload's attention, if it was taken on the current kernel source."""
+    name = COUNTERS.get(workload)
+    path = os.path.join(PROFILES, name) if name else None
+    if not path or not os.path.exists(path):
         return None
     fields = {}
-    for line in open(COUNTERS):
+    for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
@@ -156,29 +178,94 @@ def read_traffic(kernel_src):
         return None
 
 
-def cpu_baseline(w, x, idx_h, cnt_h, total_flops, nsample):
-    """The fp64 oracle on this host: routing of every row, attention on a
-    seeded sample of query blocks, extrapolated by attended pairs."""
-    import oracle
-    t0 = time.perf_counter()
-    S = oracle.summarize(x["k"], w.B)
-    qh = oracle.qpool(x["q"], w.B)
-    oracle.route_topk(qh, S, w.B, w.k_total, w.force)
-    t_route = time.perf_counter() - t0
-    rng = np.random.default_rng(12345)
+def host_info():
+    """The host the CPU baseline runs on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": model}
+
+
+class pinned_core:
+    """Pins this process to one core of its affinity set for the duration
+    (the oracle is single-threaded), then restores the set."""
+
+    def __enter__(self):
+        self.saved = os.sched_getaffinity(0)
+        self.core = min(self.saved)
+        os.sched_setaffinity(0, {self.core})
+        return self
+
+    def __exit__(self, *exc):
+        os.sched_setaffinity(0, self.saved)
+
+
+def _sample_req(w, nsample, seed=12345):
+    rng = np.random.default_rng(seed)
     blocks = np.sort(rng.choice(w.nblk, size=min(nsample, w.nblk), replace=False))
-    req = np.array([[0, h, t] for i in blocks for h in range(w.hq)
+    req = np.array([[b, h, t] for b in range(w.batch) for i in blocks for h in range(w.hq)
                     for t in range(i * w.B, min((i + 1) * w.B, w.n))], np.int64)
-    t0 = time.perf_counter()
-    _, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, idx_h, cnt_h, req=req)
-    t_att = time.perf_counter() - t0
+    return blocks, req
+
+
+def cpu_baseline(w, x, idx_h, cnt_h, total_flops, nsample):
+    """The fp64 oracle on one pinned host core: summaries and routing of every
+    row, attention on a seeded sample of query blocks (every head),
+    extrapolated by attended pairs to the full step (top-k or entmax
+    routing; a sample of every block is the full step)."""
+    import oracle
+    with pinned_core() as pin:
+        t0 = time.perf_counter()
+        S = oracle.summarize(x["k"], w.B)
+        qh = oracle.qpool(x["q"], w.B)
+        if w.router == "topk":
+            oracle.route_topk(qh, S, w.B, w.k_total, w.force)
+        else:
+            oracle.route_entmax(qh, S, w.B, w.alpha, w.gamma, w.cap, w.force,
+                                max_iter=w.max_iter)
+        t_route = time.perf_counter() - t0
+        blocks, req = _sample_req(w, nsample)
+        t0 = time.perf_counter()
+        _, pairs = oracle.attend(x["q"], x["k"], x["v"], w.B, idx_h, cnt_h, req=req)
+        t_att = time.perf_counter() - t0
     total_pairs = total_flops / (4 * w.d)
-    t_total = t_route + t_att * total_pairs / max(int(pairs.sum()), 1)
-    return {"value": total_flops / t_total / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"routing of all {w.batch * w.hkv * w.nblk} rows ({t_route:.1f} s) + attention "
-                      f"of {len(blocks)} seeded query blocks x {w.hq} heads ({t_att:.1f} s, "
-                      f"{int(pairs.sum())} pairs), extrapolated by pair count to the full step",
-            "seconds_per_step_extrapolated": t_total}
+    full = len(blocks) == w.nblk
+    t_total = t_route + (t_att if full else t_att * total_pairs / max(int(pairs.sum()), 1))
+    value = total_flops / t_total / 1e12
+    host = host_info()
+    return {"value": value, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": (f"routing of all {w.batch * w.hkv * w.nblk} rows ({t_route:.1f} s) + "
+                       f"attention of {len(blocks)} seeded query blocks x {w.hq} heads "
+                       f"({t_att:.1f} s, {int(pairs.sum())} pairs)"
+                       + ("" if full else ", extrapolated by pair count to the full step")),
+            "seconds_per_step": t_total, "measured": "full step" if full else "extrapolated",
+            "pinned_core": pin.core, "host": host,
+            "ideal_all_cores_not_measured": {"value": value * host["affinity_cpus"],
+                                             "seconds_per_step": t_total / host["affinity_cpus"]}}
+
+
+def cpu_baseline_decode(w, x, idx_h, cnt_h, total_bytes):
+    """The oracle's decode step on one pinned core: routing of every (batch,
+    KV head) row over the cached summaries and attention of every query head
+    (the full step; the summaries are the cache, computed once and untimed)."""
+    import oracle
+    S = oracle.summarize(x["k"], w.B)
+    with pinned_core() as pin:
+        t0 = time.perf_counter()
+        oracle.route_topk(x["q"].astype(np.float64), S, w.B, w.k_total, w.force,
+                          mode=oracle.MODE_DECODE, kv_lens=w.lens())
+        oracle.attend(x["q"], x["k"], x["v"], w.B, idx_h, cnt_h, mode=oracle.MODE_DECODE,
+                      kv_lens=w.lens())
+        t = time.perf_counter() - t0
+    return {"value": total_bytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "the full step: routing of all rows and attention of every query head",
+            "seconds_per_step": t, "pinned_core": pin.core}
 
 
 def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
@@ -246,8 +333,11 @@ def run_prefill(bsa, torch, w, steps, warmup, keep_inputs=True):
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
     flops = 4.0 * w.d * (token_pairs(w, idx_h, cnt_h) if token else prefill_pairs(w, idx_h, cnt_h))
     stage = lambda a_, b_: float(np.mean([e[a_].elapsed_time(e[b_]) for e in ev]))
+    att_ms = [e[2].elapsed_time(e[3]) for e in ev]
     res = {"workload": w.name, "flops": flops, "elapsed_s": elapsed,
            "attend_s": stage(2, 3) * 1e-3,
+           "attend_ms": {"mean": float(np.mean(att_ms)), "median": float(np.median(att_ms)),
+                         "min": float(np.min(att_ms)), "max": float(np.max(att_ms))},
            "stages_ms": {"summarize": stage(0, 1), "route": stage(1, 2), "attend": stage(2, 3)},
            "sparsity_vs_causal": 1.0 - flops / (4.0 * w.d * w.hq * w.n * (w.n + 1) / 2),
            "idx_h": idx_h, "cnt_h": cnt_h, "steps": steps}
@@ -281,11 +371,15 @@ def prefill_extra(r):
     w = synth.WORKLOADS[r["workload"]]
     ms = r["elapsed_s"] / r["steps"] * 1e3
     att = r["flops"] / r["attend_s"] / 1e12
-    out = {"workload": w.name, "router": w.router, "batch": w.batch, "q_heads": w.hq,
-           "kv_heads": w.hkv, "seq_len": w.n, "head_dim": w.d, "block": w.B,
+    f32 = w.dtype == "f32"
+    peak = PEAK_F32_VALU_TFLOPS if f32 else PEAK_BF16_TFLOPS
+    out = {"workload": w.name, "router": w.router, "dtype": w.dtype, "batch": w.batch,
+           "q_heads": w.hq, "kv_heads": w.hkv, "seq_len": w.n, "head_dim": w.d, "block": w.B,
            "ms_per_step": ms, "flops_per_step": r["flops"],
            "TFLOP_per_s_step": r["flops"] / ms / 1e9,
-           "attend_TFLOP_per_s": att, "attend_frac_mfma_peak": att / PEAK_BF16_TFLOPS,
+           "attend_TFLOP_per_s": att, "attend_ms": r["attend_ms"],
+           "attend_TFLOP_per_s_median": r["flops"] / r["attend_ms"]["median"] / 1e9,
+           ("attend_frac_fp32_valu_peak" if f32 else "attend_frac_mfma_peak"): att / peak,
            "stages_ms": r["stages_ms"], "sparsity_vs_causal": r["sparsity_vs_causal"],
            "mean_selected_blocks": float(r["cnt_h"].mean())}
     if w.router == "topk":
@@ -298,6 +392,8 @@ def prefill_extra(r):
         out.update(r["token"])
     if w.router == "entmax":
         out["prior_sigma"] = w.sigma
+    if r.get("traffic") is not None:
+        out["attend_hbm_bytes_per_launch"] = r["traffic"]
     return out
 
 
@@ -359,7 +455,7 @@ def run_entmax_attn(bsa, torch, steps, warmup, refine=2):
             "backward_all_tiles_ms": t_bwd_all}
 
 
-def run_decode(bsa, torch, steps, warmup, with_paged=True):
+def run_decode(bsa, torch, steps, warmup, with_paged=True, with_cpu=False):
     w = synth.WORKLOADS[DECODE]
     x = device_inputs(w, torch)
     S = bsa.summarize(x["K"], w.B)  # cached summaries, computed once
@@ -392,6 +488,12 @@ def run_decode(bsa, torch, steps, warmup, with_paged=True):
 
     times = timed(step)
     O_ref = O.clone()
+    c = cnt.cpu().numpy()
+    kv_bytes = int(c.sum()) * w.B * w.d * 2 * 2  # selected K and V blocks (all full here)
+    sum_bytes = w.batch * w.hkv * (w.nblk - 1) * w.d * 4  # fp32 summaries of the candidates
+    qo_bytes = 2 * w.batch * w.hq * w.d * 2
+    total = kv_bytes + sum_bytes + qo_bytes
+    cpu = cpu_baseline_decode(w, x, idx.cpu().numpy(), c, total) if with_cpu else None
     paged = None
     if with_paged:
         # the same cache as a shuffled pool of pages of B tokens behind page tables
@@ -413,11 +515,6 @@ def run_decode(bsa, torch, steps, warmup, with_paged=True):
         paged = {"us_per_step_median": float(np.median(ptimes)) * 1e6,
                  "same_output_as_contiguous": bool(torch.equal(O, O_ref)),
                  "pages": int(w.batch * nb), "page_tokens": w.B}
-    c = cnt.cpu().numpy()
-    kv_bytes = int(c.sum()) * w.B * w.d * 2 * 2  # selected K and V blocks (all full here)
-    sum_bytes = w.batch * w.hkv * (w.nblk - 1) * w.d * 4  # fp32 summaries of the candidates
-    qo_bytes = 2 * w.batch * w.hq * w.d * 2
-    total = kv_bytes + sum_bytes + qo_bytes
     t = float(np.median(times))
     return {"workload": w.name, "batch": w.batch, "hq": w.hq, "hkv": w.hkv, "kv_len": w.n,
             "head_dim": w.d, "block": w.B, "top_k": w.k_total - 1, "forced": "tail",
@@ -427,7 +524,8 @@ def run_decode(bsa, torch, steps, warmup, with_paged=True):
             "frac_hbm_peak": total / t / 1e9 / PEAK_HBM_GBS,
             "cache_flush": "512 MiB read before every timed step"} | (
         {} if paged is None else {"paged": paged | {
-            "GB_per_s": total / (paged["us_per_step_median"] * 1e-6) / 1e9}})
+            "GB_per_s": total / (paged["us_per_step_median"] * 1e-6) / 1e9}}) | (
+        {} if cpu is None else {"cpu_baseline": cpu})
 
 
 def run_backward(bsa, torch, w, r, steps, warmup):
@@ -579,13 +677,21 @@ def main():
         sys.exit(2)
     w = synth.WORKLOADS[a.workload]
     assert w.mode == "prefill" and w.dtype == "bf16"
+    if a.only:
+        a.no_cpu = a.no_decode = a.no_backward = a.no_train = a.no_entmax = True
+        a.no_gqa = a.no_fp32 = a.no_token = a.no_entmax_attn = True
+    kernel_src = os.path.join(HERE, "block_sparse_attention_summarize_amd", "csrc", "attend.hip")
+
+    def done(name):  # progress on stderr; the result line stays alone on stdout
+        print(f"[bench] {name} done", file=sys.stderr, flush=True)
+
     r = run_prefill(bsa, torch, w, a.steps, a.warmup)
+    done(w.name)
     flops, elapsed = r["flops"], r["elapsed_s"]
     ms = elapsed / a.steps * 1e3
     value = flops * a.steps / elapsed / 1e12
     att_s = r["attend_s"]
     achieved = flops / att_s / 1e12
-    kernel_src = os.path.join(HERE, "block_sparse_attention_summarize_amd", "csrc", "attend.hip")
     out = {
         "metric": "block-sparse attn prefill TFLOP/s (% MFMA peak); decode KV GB/s (% HBM)",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -593,21 +699,50 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) with planted blocks)",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
                    "seq_len": w.n, "head_dim": w.d, "block": w.B, "top_k": w.k_total,
-                   "flops_per_step": flops, "sparsity_vs_causal": r["sparsity_vs_causal"]},
+                   "forced": {0: "none", 1: "diagonal", 3: "diagonal + block 0"}.get(w.force),
+                   "flops_per_step": flops, "sparsity_vs_causal": r["sparsity_vs_causal"],
+                   "inputs_sha256": r["x"]["sha256"]},
         "frac_mfma_peak_step": value / PEAK_BF16_TFLOPS,
         "stages_ms": r["stages_ms"],
         "roofline": {"kernel": "attend_prefill_bf16", "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": read_traffic(kernel_src), "avg_launch_ms": att_s * 1e3},
+                     "traffic": read_traffic(w.name, kernel_src), "avg_launch_ms": att_s * 1e3,
+                     "launch_ms": r["attend_ms"],
+                     "frac_at_median_launch": flops / r["attend_ms"]["median"] / 1e9
+                     / PEAK_BF16_TFLOPS,
+                     "algorithmic_flops_per_launch": flops},
     }
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, r["x"], r["idx_h"], r["cnt_h"], flops,
+                                           a.cpu_sample_blocks)
+        done("cpu_baseline")
+    del r
+    torch.cuda.empty_cache()
     extra = {}
-
-    def done(name):  # progress on stderr; the result line stays alone on stdout
-        print(f"[bench] {name} done", file=sys.stderr, flush=True)
-
-    if not a.no_backward:
-        extra["backward"] = run_backward(bsa, torch, w, r, a.steps, a.warmup)
-        done("backward")
+    cpu_extra = {}
+    if not a.no_gqa:
+        w2 = synth.WORKLOADS[GQA32K]
+        r2 = run_prefill(bsa, torch, w2, a.steps, a.warmup)
+        r2["traffic"] = read_traffic(GQA32K, kernel_src)
+        extra[GQA32K] = prefill_extra(r2)
+        done(GQA32K)
+        if not a.no_cpu:
+            cpu_extra[GQA32K] = cpu_baseline(w2, r2["x"], r2["idx_h"], r2["cnt_h"], r2["flops"], 8)
+            done(f"{GQA32K} cpu")
+        if not a.no_backward:
+            extra["backward"] = run_backward(bsa, torch, w2, r2, a.steps, a.warmup)
+            done("backward")
+        del r2
+        torch.cuda.empty_cache()
+    if not a.no_fp32:
+        w1 = synth.WORKLOADS[FP32]
+        r1 = run_prefill(bsa, torch, w1, a.steps, a.warmup)
+        extra[FP32] = prefill_extra(r1)
+        done(FP32)
+        if not a.no_cpu:
+            cpu_extra[FP32] = cpu_baseline(w1, r1["x"], r1["idx_h"], r1["cnt_h"], r1["flops"],
+                                           w1.nblk)
+        del r1
     if not a.no_backward and not a.no_train:
         extra["train_entmax_prior"] = run_train_entmax(bsa, torch, a.steps, a.warmup)
         done("train_entmax_prior")
@@ -616,21 +751,29 @@ def main():
                                                           name=TOKEN)
             done("train_token_prior")
     if not a.no_decode:
-        extra["decode"] = run_decode(bsa, torch, a.steps, a.warmup)
+        extra["decode"] = run_decode(bsa, torch, a.steps, a.warmup, with_cpu=not a.no_cpu)
         done("decode")
-    for name, flag in ((ENTMAX, a.no_entmax), (LONG, a.no_long), (TOKEN, a.no_token)):
-        if not flag:
-            extra[name] = prefill_extra(run_prefill(bsa, torch, synth.WORKLOADS[name], a.steps,
-                                                    a.warmup, keep_inputs=False))
-            done(name)
+    if not a.no_entmax:
+        w4 = synth.WORKLOADS[ENTMAX]
+        r4 = run_prefill(bsa, torch, w4, a.steps, a.warmup, keep_inputs=not a.no_cpu)
+        extra[ENTMAX] = prefill_extra(r4)
+        done(ENTMAX)
+        if not a.no_cpu:
+            cpu_extra[ENTMAX] = cpu_baseline(w4, r4["x"], r4["idx_h"], r4["cnt_h"], r4["flops"], 4)
+            done(f"{ENTMAX} cpu")
+        del r4
+        torch.cuda.empty_cache()
+    if not a.no_token:
+        extra[TOKEN] = prefill_extra(run_prefill(bsa, torch, synth.WORKLOADS[TOKEN], a.steps,
+                                                 a.warmup, keep_inputs=False))
+        done(TOKEN)
     if not a.no_entmax_attn:
         extra[ENTMAX_ATTN] = run_entmax_attn(bsa, torch, a.steps, a.warmup)
         done(ENTMAX_ATTN)
+    if cpu_extra:
+        extra["cpu_baselines"] = cpu_extra
     if extra:
         out["extra"] = extra
-    if not a.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, r["x"], r["idx_h"], r["cnt_h"], flops,
-                                           a.cpu_sample_blocks)
     print(json.dumps(out), flush=True)
 
 
