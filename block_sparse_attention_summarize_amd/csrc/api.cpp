@@ -1141,11 +1141,11 @@ int bsa_attend_entmax(const bsa_shape* s, const void* Q, const void* K, const vo
   if (s->mode != BSA_PREFILL) return fail(BSA_ERR_INVALID, "bsa_attend_entmax needs BSA_PREFILL");
   if (s->dtype != BSA_BF16) return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax takes bf16 inputs");
   if (!(alpha > 1.f) || !std::isfinite(alpha)) return fail(BSA_ERR_INVALID, "alpha must be > 1");
-  if (alpha > 2.f)
-    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax supports 1 < alpha <= 2 (got %g)",
+  if (alpha > 16.f)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax supports 1 < alpha <= 16 (got %g)",
                 static_cast<double>(alpha));
-  if (refine < 0 || refine > 8)
-    return fail(BSA_ERR_INVALID, "refine must be in [0, 8] (got %d)", refine);
+  if (refine < 0 || refine > 24)
+    return fail(BSA_ERR_INVALID, "refine must be in [0, 24] (got %d)", refine);
   if ((s->q_len + 63) / 64 > bsa::entmax_attend_max_tiles())
     return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax supports at most %d tokens",
                 64 * bsa::entmax_attend_max_tiles());

@@ -12,9 +12,10 @@
 //      [x_max - 1, x_max]); its closed-form roots with every count at its bin's
 //      lower and upper edge bracket tau;
 //   3. `refine` passes of the hybrid step of 2.B from the bracket's lower end
-//      (Halley for alpha <= 1.5, Newton for 1.5 < alpha <= 2, each kept
-//      inside the bracket, else bisection), the first of which also marks the
-//      key tiles holding any x above that lower end;
+//      (Halley for alpha <= 1.5, Newton for 1.5 < alpha <= 2, and for
+//      alpha > 2 a secant through the bracket ends with the Illinois halving;
+//      each kept inside the bracket, else bisection), the first of which also
+//      marks the key tiles holding any x above that lower end;
 //   4. the output: only the marked tiles (a tile with every x <= tau has zero
 //      weight), p on the matrix cores against V, normalised by its sum.
 // S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16 as in the
@@ -379,6 +380,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void entmax_attn_bf16(EntmaxAttnAr
   // bracket per query column (fp64)
   // bracket [lo, hi]: h = mass - 1 >= 0 at lo, < 0 at hi
   double lo[QT], hi[QT], tau[QT];
+  // alpha > 2: the mass values at the bracket ends (valid once the end has
+  // been evaluated: side bit 1 lo, bit 2 hi) and which end the last iterate
+  // replaced, for the bracketed secant.  No NaN sentinels: this file is built
+  // without NaN semantics.
+  double hlo[QT], hhi[QT];
+  int side[QT], have[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    hlo[qt] = hhi[qt] = 0.0;
+    side[qt] = have[qt] = 0;
+  }
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     int cnt[16];
@@ -433,15 +445,35 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void entmax_attn_bf16(EntmaxAttnAr
       const double h0 = static_cast<double>(col_sum(f0[qt])) - 1.0;
       const double d1 = col_sum(f1[qt]);  // -dh/dtau
       const double d2 = col_sum(f2[qt]);  // d2h/dtau2
-      if (h0 >= 0.0)
+      // the iterate replaces the bracket end on its side; for alpha > 2 the
+      // other end's mass value is halved when it is kept twice in a row
+      // (Illinois), so the secant cannot stall on one side
+      if (h0 >= 0.0) {
+        if (side[qt] > 0) hhi[qt] *= 0.5;
         lo[qt] = tau[qt];
-      else
+        hlo[qt] = h0;
+        side[qt] = 1;
+        have[qt] |= 1;
+      } else {
+        if (side[qt] < 0) hlo[qt] *= 0.5;
         hi[qt] = tau[qt];
+        hhi[qt] = h0;
+        side[qt] = -1;
+        have[qt] |= 2;
+      }
       double nt;
-      if (alpha <= 1.5f)
+      if (alpha <= 1.5f) {
         nt = tau[qt] + 2.0 * h0 * d1 / (2.0 * d1 * d1 - h0 * d2);  // Halley
-      else
+      } else if (alpha <= 2.f) {
         nt = tau[qt] + h0 / d1;  // Newton
+      } else {
+        // secant through the bracket ends (bisection until both are known):
+        // the mass has a kink of unbounded slope at every key, which defeats
+        // the derivative steps
+        nt = (have[qt] == 3 && hlo[qt] > hhi[qt])
+                 ? lo[qt] + hlo[qt] * (hi[qt] - lo[qt]) / (hlo[qt] - hhi[qt])
+                 : 0.5 * (lo[qt] + hi[qt]);
+      }
       if (!(nt >= lo[qt] && nt <= hi[qt])) nt = (h0 == 0.0) ? tau[qt] : 0.5 * (lo[qt] + hi[qt]);
       tau[qt] = nt;
     }

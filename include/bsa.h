@@ -379,14 +379,18 @@ int bsa_route_entmax_backward(const bsa_shape *shape, const void *Q, const float
  * p_j = [x_j - tau_t]_+^(1/(alpha-1)) with sum_j p_j = 1 (exact zeros outside
  * the support); o_t = sum_j p_j v_j, with the weights renormalised by their
  * sum.  tau_t is bracketed by a 16-bin histogram of x_max - x on [0, 1)
- * ("AdaSplash-2", 2.A), then refined by `refine` hybrid steps (Halley for
- * alpha <= 1.5, Newton for 1.5 < alpha <= 2; bisection when a step leaves the
- * bracket); key tiles of 64 with no x above the bracket's lower end are
- * skipped in the later passes.  alpha > 2 (the pages' secant branch) is not
- * supported.
+ * ("AdaSplash-2", 2.A), then refined by `refine` steps of the hybrid solver
+ * of 2.B: Halley for alpha <= 1.5, Newton for 1.5 < alpha <= 2, and for
+ * alpha > 2 a secant through the bracket ends (Illinois halving of a kept
+ * end), with bisection whenever a step would leave the bracket; key tiles of
+ * 64 with no x above the bracket's lower end are skipped in the later
+ * passes.  The mass has a kink of unbounded slope at every key when
+ * alpha > 2, so the secant needs more steps there than the 1-2 that suffice
+ * up to alpha = 2 (about 8 at alpha = 2.5 and 12 at alpha = 3 for the
+ * output to settle within 1e-2).
  *   Q, K, V bf16 [batch, H, N, d] (q_len == kv_len == N <= 131072);
  *   O [batch, Hq, N, d] bf16 or fp32 (o_dtype); sm_scale 0 means 1/sqrt(d).
- *   refine in [0, 8] (0: tau = the histogram lower bound).
+ *   alpha in (1, 16]; refine in [0, 24] (0: tau = the histogram lower bound).
  *   tau_out NULL or fp32 [batch, Hq, N]: the threshold used, in units of x.
  *   live_out NULL or uint32 [batch, Hkv, T, ceil(T / 32)], T = ceil(N / 64):
  *         bit j % 32 of word j / 32 of row (b, g, i) is set when key tile j
@@ -394,8 +398,8 @@ int bsa_route_entmax_backward(const bsa_shape *shape, const void *Q, const float
  *         tile i and some query head of KV head g -- a superset of the tiles
  *         with nonzero weights, which bsa_attend_entmax_backward then walks
  *         alone.  With refine = 0 every causal tile is set.  Written whole.
- * Errors: BSA_ERR_INVALID (alpha <= 1, refine outside [0, 8], bad shape),
- * BSA_ERR_UNSUPPORTED (alpha > 2, fp32 inputs, N > 131072, strides).
+ * Errors: BSA_ERR_INVALID (alpha <= 1, refine outside [0, 24], bad shape),
+ * BSA_ERR_UNSUPPORTED (alpha > 16, fp32 inputs, N > 131072, strides).
  */
 int bsa_attend_entmax(const bsa_shape *shape, const void *Q, const void *K, const void *V,
                       float alpha, int32_t refine, float sm_scale, void *O, int32_t o_dtype,

@@ -49,6 +49,37 @@ def test_entmax_attention_matches_oracle(name, out_f32):
           f"mean support {sup.mean():.1f} of {(w.n + 1) / 2:.0f} keys")
 
 
+SECANT = {
+    "a25_secant": (BASE.scaled(hq=4, hkv=2, n=64 * 4 + 9, alpha=2.5, q_scale=2.0,
+                               planted_blocks=2), 10),
+    "a3_secant": (BASE.scaled(hq=4, hkv=2, n=64 * 4 + 33, alpha=3.0, q_scale=2.0,
+                              planted_blocks=2), 14),
+    "a3_sharp": (BASE.scaled(hq=4, hkv=1, n=64 * 3 + 5, alpha=3.0, q_scale=6.0,
+                             planted_blocks=1), 14),
+    "a25_d64_batch2": (BASE.scaled(batch=2, hq=4, hkv=2, d=64, n=64 * 3 + 1, alpha=2.5,
+                                   planted_blocks=1), 10),
+}
+
+
+@pytest.mark.parametrize("name", list(SECANT))
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_entmax_attention_secant_above_alpha_2(name, out_f32):
+    """alpha > 2 ("AdaSplash-2", 2.B: secant with a bisection safeguard) against
+    the oracle's exact threshold, with the refinement budget the header
+    states for these alphas."""
+    w, refine = SECANT[name]
+    print(f"[entmax attention, secant] {name} refine={refine} out_f32={out_f32}", flush=True)
+    x = parity.make(w)
+    O, tau = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=refine,
+                               out_dtype=torch.float32 if out_f32 else None, want_tau=True)
+    ref, rtau, sup = oracle.entmax_attend(x["q"], x["k"], x["v"], w.alpha)
+    worst = parity.check_attention(w, _cpu(O).reshape(ref.shape), ref, out_f32)
+    terr = np.abs(_cpu(tau).ravel() - rtau)
+    assert terr.max() < 1e-3, terr.max()
+    print(f"max abs err {worst:.3e}, tau err max {terr.max():.2e} median {np.median(terr):.2e}, "
+          f"mean support {sup.mean():.1f}")
+
+
 def test_entmax_attention_zero_query_is_the_causal_mean():
     w = CASES["a15_gqa"]
     x = parity.make(w)
@@ -78,10 +109,10 @@ def test_entmax_attention_argument_errors():
     x = parity.make(w)
     with pytest.raises(bsa.BsaError, match="alpha"):
         bsa.attend_entmax(x["Q"], x["K"], x["V"], 1.0)
-    with pytest.raises(bsa.BsaError, match="alpha <= 2"):
-        bsa.attend_entmax(x["Q"], x["K"], x["V"], 3.0)
+    with pytest.raises(bsa.BsaError, match="alpha <= 16"):
+        bsa.attend_entmax(x["Q"], x["K"], x["V"], 17.0)
     with pytest.raises(bsa.BsaError, match="refine"):
-        bsa.attend_entmax(x["Q"], x["K"], x["V"], 1.5, refine=9)
+        bsa.attend_entmax(x["Q"], x["K"], x["V"], 1.5, refine=25)
     with pytest.raises(bsa.BsaError, match="bf16"):
         bsa.attend_entmax(x["Q"].float(), x["K"].float(), x["V"].float(), 1.5)
 

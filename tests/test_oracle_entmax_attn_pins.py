@@ -49,7 +49,7 @@ def test_entmax_attention_matches_sort_based_closed_forms(alpha):
     assert sup.min() >= 1 and sup.max() < n  # sparse somewhere
 
 
-@pytest.mark.parametrize("alpha", [1.25, 1.75, 3.0])
+@pytest.mark.parametrize("alpha", [1.25, 1.75, 2.5, 3.0])
 def test_entmax_attention_threshold_vs_library_root_finder(alpha):
     Q, K, V = _case(4100, n=29)
     req = np.array([[0, h, t] for h in range(4) for t in (0, 5, 17, 28)], np.int64)
