@@ -11,6 +11,9 @@
 //                         with fp32 accumulation; the online softmax is fp32.
 //                         V stays row-major in LDS and its transposed MFMA
 //                         operand comes from ds_read_b64_tr_b16.
+//   attend_prefill_pp     the same computation for plain block rows with many
+//                         key tiles: eight wavefronts in two groups half a
+//                         tile apart, alternating MFMA and softmax phases.
 //   attend_prefill_f32    fp32 inputs: one query per lane, VALU dot products
 //                         (fp32 matrix rate is not the bound at these sizes).
 // With per-token selections (TOK) a row is a tile of 64 queries whose list
@@ -68,6 +71,8 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
 }
 constexpr int kMaxTiles = 1024;  // tile-list chunk staged in LDS
 constexpr int kMaxTilesTok = 512;  // the same with a 64-bit token word per tile
+constexpr int kPingPongMinTiles = 32;  // list width (in 64-key tiles) from which the
+                                       // ping-pong kernel serves plain block rows
 
 // QT query tiles of 16 per wavefront, NW wavefronts per workgroup.  A "unit"
 // is one query head x 16*QT queries of the query block; the workgroup's
@@ -531,6 +536,344 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
   for (int c = 0; c < D; ++c) Og[c] = o[c] * inv;
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant for plain block rows (no token masks, no prior).  Eight
+// wavefronts per workgroup, one workgroup per CU: waves 0-3 and 4-7 share the
+// four SIMDs pairwise and run the same tile sequence half a tile apart.  Each
+// wavefront alternates a matrix phase (P V of the previous tile, then S^T of
+// the current one) and a vector phase (the current tile's online softmax), and
+// every phase ends at a workgroup barrier, so on each SIMD one wavefront's
+// MFMAs run while the other's softmax occupies the VALU.  K/V tiles arrive
+// through direct-to-LDS buffer loads into three rotating buffers (unpadded,
+// 16-byte chunks XOR-swizzled per row for conflict-free fragment reads).
+// ---------------------------------------------------------------------------
+template <int D>
+struct PpLds {
+  static constexpr int NC = D / 8;     // 16-byte chunks per row
+  static constexpr int RPL = 16 / NC;  // rows per 256-byte bank line
+  __host__ __device__ static constexpr int kswz(int r) { return (r / RPL) & (NC - 1); }
+  __host__ __device__ static constexpr int vswz(int r) { return ((r / RPL) & (NC / 2 - 1)) << 1; }
+  alignas(16) uint16_t k[3][64 * D];
+  alignas(16) uint16_t v[3][64 * D];
+};
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane (the
+// wave's 1 KB block starts at lds, which must be wave-uniform)
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, 0, 0, 0);
+}
+
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(512, 1) void attend_prefill_pp(AttendArgs a, int wpb) {
+  constexpr int NW = 8, QT = 2, QPW = 32;
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int NC = D / 8;
+  constexpr int NI = 64 * NC / 64 / NW;  // 1 KB DMA instructions per wave per tensor
+  __shared__ PpLds<D> lds;
+  __shared__ int lds_tiles[kMaxTiles];
+  __shared__ int lds_ntiles;
+  using L = PpLds<D>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int grp = w >> 2;  // 0: leads, 1: half a tile behind
+  const int G = a.hq / a.hkv;
+  const int nsub = a.B / 64;
+  const int qsub = a.B / QPW;
+  const int units = G * qsub;
+  int pair, i, sub;
+  map_wg(blockIdx.x, a.batch * a.hkv, a.nrow, wpb, pair, i, sub);
+  const int b = pair / a.hkv, g = pair % a.hkv;
+  const int u = sub * NW + w;
+  const bool active = u < units;
+  const int hh = active ? u % G : 0;
+  const int qs = active ? u / G : 0;
+  const int h = g * G + hh;
+  const int qpos0 = i * a.B + qs * QPW;
+  int qs_max = 0;
+  for (int uu = sub * NW; uu < sub * NW + NW && uu < units; ++uu) qs_max = max(qs_max, uu / G);
+  int64_t qmax = static_cast<int64_t>(i) * a.B + qs_max * QPW + QPW - 1;
+  if (qmax > a.q_len - 1) qmax = a.q_len - 1;
+
+  const int64_t rowid = static_cast<int64_t>(pair) * a.nrow + i;
+  int n = a.cnt[rowid];
+  n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
+  TileWalk walk{a.idx + rowid * a.k_max, n, nsub, a.B, a.nblk, a.kv_len, qmax};
+  int jpre = -1;
+  if (w == 0 && lane < a.k_max * nsub) jpre = walk.list[lane / nsub];
+
+  const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
+                            head_bytes(a.kv_len, a.ks.t, D, 2));
+  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
+                            head_bytes(a.kv_len, a.vs.t, D, 2));
+  const uint32_t kst = static_cast<uint32_t>(a.ks.t * 2), vst = static_cast<uint32_t>(a.vs.t * 2);
+
+  uint4 qf[QT][KS];
+  {
+    const auto rq = make_rsrc(static_cast<const uint16_t*>(a.Q) + b * a.qs.b + h * a.qs.h,
+                              active ? head_bytes(a.q_len, a.qs.t, D, 2) : 0u);
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const uint32_t t = static_cast<uint32_t>(qpos0 + qt * 16 + (lane & 15));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[qt][ks] = buf_load16(rq, t * static_cast<uint32_t>(a.qs.t * 2) + (ks * 32 + (lane >> 4) * 8) * 2);
+    }
+  }
+
+  f32x4 o[DT][QT];
+  f32x4 lsum[QT];
+  float m[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    lsum[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[qt] = -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sc = a.sm_scale * kLog2e;
+  const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+
+  // DMA: wave instruction it fills bytes [1 KB (w NI + it), +1 KB) of a
+  // tile; lane l's 16 bytes land at LDS chunk q = 64 (w NI + it) + l, i.e.
+  // row q / NC, physical chunk q % NC, which holds logical chunk p ^ swz(row)
+  uint32_t koff[NI], voff[NI];
+#pragma unroll
+  for (int it = 0; it < NI; ++it) {
+    const int q = (w * NI + it) * 64 + lane;
+    const int r = q / NC, p = q % NC;
+    koff[it] = static_cast<uint32_t>(r) * kst + ((p ^ L::kswz(r)) * 16);
+    voff[it] = static_cast<uint32_t>(r) * vst + ((p ^ L::vswz(r)) * 16);
+  }
+  auto load_tile = [&](int k0, int buf) {
+    const uint32_t kb = static_cast<uint32_t>(k0) * kst, vb = static_cast<uint32_t>(k0) * vst;
+#pragma unroll
+    for (int it = 0; it < NI; ++it) {
+      lds_dma16(rk, &lds.k[buf][(w * NI + it) * 512], koff[it] + kb);
+      lds_dma16(rv, &lds.v[buf][(w * NI + it) * 512], voff[it] + vb);
+    }
+  };
+  // this lane's K fragment offset (elements) per k-step and V transposing-read
+  // offset per d tile, at key tile 0 / the first 16 rows: the swizzles depend
+  // only on the row within its 16-row (K) or 8-row (V) group, so the other key
+  // tiles and halves are the same offsets plus a constant
+  int kfo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int r = lane & 15;
+    kfo[ks] = r * D + ((ks * 4 + (lane >> 4)) ^ L::kswz(r)) * 8;
+  }
+  int vfo[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int s16 = lane & 15;
+    const int r = (lane >> 4) * 4 + (s16 >> 2);
+    const int c = dt * 2 + ((s16 & 3) >> 1);
+    vfo[dt] = r * D + (c ^ L::vswz(r)) * 8 + (s16 & 1) * 4;
+  }
+  static_assert(L::kswz(16) == L::kswz(0) && L::vswz(16) == L::vswz(0) &&
+                L::vswz(32) == L::vswz(0), "swizzles repeat every 16 rows");
+
+  f32x4 s[4][QT];
+  uint4 pf[QT][2];
+  // matrix phase: P V of tile tp (weights pf) and S^T = K Q^T of tile ts
+  auto mphase = [&](int tp, int ts) {
+    __builtin_amdgcn_s_setprio(1);
+    if (tp >= 0) {
+      const uint16_t* vb = lds.v[tp % 3];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) lsum[qt] = mfma16(ones, pf[qt][kk], lsum[qt]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          typedef __attribute__((address_space(3))) v4i16 lds_v4;
+          const uint16_t* vp = vb + vfo[dt] + kk * 32 * D;
+          const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp));
+          const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 16 * D));
+          const uint2 u0 = __builtin_bit_cast(uint2, r0), u1 = __builtin_bit_cast(uint2, r1);
+          const uint4 vf = make_uint4(u0.x, u0.y, u1.x, u1.y);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma16(vf, pf[qt][kk], o[dt][qt]);
+        }
+      }
+      // issue order: eight fragment reads ahead, then two MFMAs per two reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int r = 0; r < 12; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+    }
+    if (ts >= 0) {
+      const uint16_t* kb = lds.k[ts % 3];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const uint4 kf = *reinterpret_cast<const uint4*>(kb + kfo[ks] + kt * 16 * D);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+#pragma unroll
+      for (int r = 0; r < 10; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 1);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // vector phase: online softmax of s (tile at key k0) into pf
+  auto vphase = [&](int k0) {
+    if (k0 + 63 > qpos0) {
+      const int rel0 = k0 - qpos0 + (lane >> 4) * 4 - (lane & 15);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (rel0 + kt * 16 + j - qt * 16 > 0) s[kt][qt][j] = -INFINITY;
+    }
+    float mx[QT];
+    bool grow = false;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float t0 = max3f(s[0][qt][0], s[0][qt][1], s[0][qt][2]);
+      const float t1 = max3f(s[0][qt][3], s[1][qt][0], s[1][qt][1]);
+      const float t2 = max3f(s[1][qt][2], s[1][qt][3], s[2][qt][0]);
+      const float t3 = max3f(s[2][qt][1], s[2][qt][2], s[2][qt][3]);
+      const float t4 = max3f(s[3][qt][0], s[3][qt][1], s[3][qt][2]);
+      const float t5 = max3f(t0, t1, t2);
+      const float t6 = max3f(t3, t4, s[3][qt][3]);
+      float v = fmaxf(t5, t6);
+      v = xmax16(v);
+      mx[qt] = v * sc;
+      grow |= mx[qt] > m[qt] + kRescale;
+    }
+    if (__ballot(grow) != 0) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const float mn = fmaxf(m[qt], mx[qt]);
+        const float f = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[qt] - mn);
+        m[qt] = mn;
+        lsum[qt] *= f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][qt] *= f;
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float nb = m[qt] == -INFINITY ? 0.f : -m[qt];
+      float p[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[kt][j] = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][j], sc, nb));
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        pf[qt][kk].x = pack_bf16x2(p[2 * kk][0], p[2 * kk][1]);
+        pf[qt][kk].y = pack_bf16x2(p[2 * kk][2], p[2 * kk][3]);
+        pf[qt][kk].z = pack_bf16x2(p[2 * kk + 1][0], p[2 * kk + 1][1]);
+        pf[qt][kk].w = pack_bf16x2(p[2 * kk + 1][2], p[2 * kk + 1][3]);
+      }
+    }
+  };
+
+  const int nraw = n * nsub;
+  for (int base = 0; base < nraw; base += kMaxTiles) {
+    if (w == 0) {
+      int c = 0;
+#pragma clang loop unroll(disable)
+      for (int r = 0; r < kMaxTiles && base + r < nraw; r += 64) {
+        const int T = base + r + lane;
+        const int64_t k0 = T >= nraw ? -1 : (T < 64 ? walk.key0_of(jpre, T) : walk.key0(T));
+        const uint64_t mk = __ballot(k0 >= 0);
+        if (k0 >= 0) lds_tiles[c + lanes_below(mk)] = static_cast<int>(k0);
+        c += __popcll(mk);
+      }
+      if (lane == 0) lds_ntiles = c;
+    }
+    __syncthreads();
+    const int ntiles = lds_ntiles;
+    if (ntiles > 0) load_tile(lds_tiles[0], 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q fragments and tile 0
+    __syncthreads();
+    // Slot sl: group 0 runs its phase sl, group 1 its phase sl - 1; phase 2t
+    // is the matrix phase (P V of tile t-1, S^T of tile t), phase 2t+1 the
+    // softmax of tile t.  Tile t is read in slots 2t .. 2t+3; its loads go
+    // out at slot 2t-2 (into the buffer tile t-3 left at slot 2t-3) and are
+    // complete before the barrier that ends slot 2t-1.
+    const int nslots = 2 * ntiles + 2;
+#pragma clang loop unroll(disable)
+    for (int sl = 0; sl < nslots; ++sl) {
+      if (!(sl & 1) && (sl >> 1) + 1 < ntiles) load_tile(lds_tiles[(sl >> 1) + 1], ((sl >> 1) + 1) % 3);
+      const int ph = sl - grp;
+      if (active && ph >= 0) {
+        const int t = ph >> 1;
+        if (!(ph & 1))
+          mphase(t >= 1 ? t - 1 : -1, t < ntiles ? t : -1);
+        else if (t < ntiles)
+          vphase(lds_tiles[t]);
+      }
+      if (sl & 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this slot pair's loads
+      __syncthreads();
+    }
+  }
+
+  if (!active) return;
+  uint8_t* Ob = static_cast<uint8_t*>(a.O);
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const float lt = lsum[qt][0];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int64_t t = qpos0 + qt * 16 + (lane & 15);
+    if (t >= a.q_len) continue;
+    if (a.lse && lane < 16)
+      a.lse[(static_cast<int64_t>(b) * a.hq + h) * a.q_len + t] =
+          lt > 0.f ? (m[qt] + __log2f(lt)) * kLn2 : -INFINITY;
+    const int64_t off = b * a.os.b + h * a.os.h + t * a.os.t;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d0 = dt * 16 + (lane >> 4) * 4;
+      const f32x4 v = o[dt][qt] * inv;
+      if constexpr (OUT_F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(Ob) + off + d0) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        uint2 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Ob) + off + d0) = pk;
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t prefill_pp_launch(const AttendArgs& a, hipStream_t stream) {
+  const int G = a.hq / a.hkv;
+  const int units = G * (a.B / 32);
+  const int wpb = (units + 7) / 8;
+  const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow * wpb;
+  if (a.out_f32)
+    hipLaunchKernelGGL((attend_prefill_pp<D, true>), dim3(grid), dim3(512), 0, stream, a, wpb);
+  else
+    hipLaunchKernelGGL((attend_prefill_pp<D, false>), dim3(grid), dim3(512), 0, stream, a, wpb);
+  return hipGetLastError();
+}
+
 template <int D, int QT, int NW, bool TOK, bool BIAS>
 hipError_t prefill_bf16_launch(const AttendArgs& a, hipStream_t stream) {
   const int G = a.hq / a.hkv;
@@ -551,8 +894,12 @@ hipError_t prefill_bf16_dispatch(const AttendArgs& a, hipStream_t stream) {
   if (a.bits)
     return a.tbias ? prefill_bf16_launch<D, 2, 4, true, true>(a, stream)
                    : prefill_bf16_launch<D, 2, 4, true, false>(a, stream);
-  return a.wsel ? prefill_bf16_launch<D, 2, 4, false, true>(a, stream)
-                : prefill_bf16_launch<D, 2, 4, false, false>(a, stream);
+  if (a.wsel) return prefill_bf16_launch<D, 2, 4, false, true>(a, stream);
+  // rows of many key tiles: the ping-pong kernel (measured 3-5 % faster at 64
+  // tiles a row); short rows keep two independent 4-wave workgroups per CU,
+  // which hide each other's tails better (16 tiles a row: ~6 % faster)
+  return a.k_max * (a.B / 64) >= kPingPongMinTiles ? prefill_pp_launch<D>(a, stream)
+                                                   : prefill_bf16_launch<D, 2, 4, false, false>(a, stream);
 }
 
 }  // namespace

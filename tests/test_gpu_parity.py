@@ -37,6 +37,17 @@ SMALL = {
     "bf16_batch2": W["bf16_gqa_prefill_n32k"].scaled(batch=2, hq=4, hkv=2, n=64 * 8 + 21,
                                                      k_total=3, planted_blocks=2),
     "fp32_batch2": W["fp32_prefill_n1k"].scaled(batch=2, n=64 * 5 + 7, hq=2, hkv=1, k_total=3),
+    # lists of 32 or more key tiles: the ping-pong prefill kernel
+    "wide_gqa": W["bf16_gqa_prefill_n32k"].scaled(hq=8, hkv=2, n=64 * 45 + 13, k_total=34,
+                                                  planted_blocks=5),
+    "wide_b128_g8": W["bf16_long_prefill_n256k"].scaled(hq=8, hkv=1, n=128 * 24 + 77, k_total=16,
+                                                        planted_blocks=4),
+    "wide_d64_batch2": W["bf16_gqa_prefill_n32k"].scaled(batch=2, d=64, hq=4, hkv=2,
+                                                         n=64 * 40 + 5, k_total=33,
+                                                         force=synth.FORCE_DIAG,
+                                                         planted_blocks=3),
+    "wide_g3_dense": W["bf16_gqa_prefill_n32k"].scaled(hq=3, hkv=1, n=64 * 36, k_total=36,
+                                                       planted_blocks=2),
 }
 DECODE = {
     "decode": W["bf16_decode_l128k"].scaled(batch=4, hq=8, hkv=2, n=64 * 40, k_total=9,
