@@ -82,20 +82,15 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
     else
       return static_cast<float>(qp[c]);
   };
-  // the attention's query heads (scaled for exp2) and the routing query (the
-  // group's sum) are read together, before the summaries stream
-  for (int e = tid; e < gs * D; e += kNT) {
-    const int hh = e / D, c = e % D;
-    qa[hh][c] = qval(h0 + hh, c) * scl;
-  }
+  // the attention's query heads, scaled for exp2
+  auto load_qa = [&]() {
+    for (int e = tid; e < gs * D; e += kNT) {
+      const int hh = e / D, c = e % D;
+      qa[hh][c] = qval(h0 + hh, c) * scl;
+    }
+  };
 
   if (a.route) {
-    for (int c = tid; c < D; c += kNT) {
-      float s = 0.f;
-      for (int hh = 0; hh < G; ++hh) s += qval(g * G + hh, c);
-      qh[c] = s;
-    }
-    __syncthreads();
     RowRule rule;
     rule.mode = 1;
     rule.entmax = 0;
@@ -107,7 +102,6 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
     const int n = ri.cand_end;
     // stream the summaries of the candidates, kUnroll loads in flight per lane
     const int c4 = lane % LPR;
-    const float4 q4 = reinterpret_cast<const float4*>(qh)[c4];
     const auto rs = make_rsrc(a.S + static_cast<int64_t>(row) * a.nblk * D,
                               static_cast<uint32_t>(n) * D * 4);  // candidates only
     constexpr int STEP = kNW * RPW;        // rows per workgroup load instruction
@@ -122,6 +116,18 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
         v[u] = buf_load16(rs, j * (D * 4) + c4 * 16);
       }
     };
+    // the first round of summaries is requested before the query heads, so
+    // the two reads' latencies overlap; then the attention heads and the
+    // routing query (the group's sum)
+    if (n > 0) issue(0, va);
+    load_qa();
+    for (int c = tid; c < D; c += kNT) {
+      float s = 0.f;
+      for (int hh = 0; hh < G; ++hh) s += qval(g * G + hh, c);
+      qh[c] = s;
+    }
+    __syncthreads();
+    const float4 q4 = reinterpret_cast<const float4*>(qh)[c4];
     auto reduce = [&](int base, const uint4 (&v)[kUnroll]) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -134,7 +140,6 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
         if (c4 == 0 && j < n) dyn[j] = p * a.score_scale;
       }
     };
-    if (n > 0) issue(0, va);
     for (int base = 0; base < n; base += 2 * ROUND) {
       issue(base + ROUND, vb);
       reduce(base, va);
@@ -203,6 +208,7 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
       __syncthreads();
     }
   } else {
+    load_qa();
     int c = a.cnt[row];
     c = c < 0 ? 0 : (c > a.k_total ? a.k_total : c);
     for (int p = tid; p < c; p += kNT) sel[p] = a.idx[static_cast<int64_t>(row) * a.k_total + p];

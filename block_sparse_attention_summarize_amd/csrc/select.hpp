@@ -190,15 +190,22 @@ __device__ inline int wave_topm(const uint32_t (&key)[E], const bool (&valid)[E]
     for (int e = 0; e < E; ++e) sel[e] = false;
     return 0;
   }
-  // T ends as the m-th largest key: the largest value with >= m keys >= T
+  // T ends as the m-th largest key: the largest value with >= m keys >= T.
+  // Two bits per step: the counts at T|11, T|10 and T|01 (in that order they
+  // can only grow) decide both bits at once, as two one-bit steps would, with
+  // three independent ballot chains instead of two dependent ones.
   uint32_t T = 0;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    int c = 0;
+  for (int bit = 30; bit >= 0; bit -= 2) {
+    const uint32_t c3 = T | (3u << bit), c2 = T | (2u << bit), c1 = T | (1u << bit);
+    int n3 = 0, n2 = 0, n1 = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) c += __popcll(__ballot(k[e] >= cand));
-    T = c >= m ? cand : T;
+    for (int e = 0; e < E; ++e) {
+      n3 += __popcll(__ballot(k[e] >= c3));
+      n2 += __popcll(__ballot(k[e] >= c2));
+      n1 += __popcll(__ballot(k[e] >= c1));
+    }
+    T = n3 >= m ? c3 : (n2 >= m ? c2 : (n1 >= m ? c1 : T));
   }
   int greater = 0;
 #pragma unroll
