@@ -442,8 +442,17 @@ def run_entmax_attn(bsa, torch, steps, warmup, refine=2):
                       dtype=torch.uint8, device="cuda")
     t_bwd = timed(lambda: bsa.attend_entmax_backward(Q, K, V, dO, tau, w.alpha, ws=ews, live=live))
     t_bwd_all = timed(lambda: bsa.attend_entmax_backward(Q, K, V, dO, tau, w.alpha, ws=ews))
+    del ews
+    # the dense softmax's own backward on the same inputs (every block
+    # selected), for the training-step comparison ("AdaSplash-2", 4)
+    Os, Ls = bsa.attend_prefill(Q, K, V, w.B, idx, cnt, want_lse=True)
+    dshape = bsa.make_shape(batch=w.batch, hq=w.hq, hkv=w.hkv, d=w.d, B=w.B, dtype=bsa.BF16,
+                            mode=bsa.PREFILL, q_len=w.n, kv_len=w.n, q=Q, k=K, v=V, o=Os)
+    dws = torch.empty(bsa.workspace_size(bsa.OP_ATTEND_BACKWARD, dshape, nb), dtype=torch.uint8,
+                      device="cuda")
+    t_soft_bwd = timed(lambda: bsa.attend_backward(Q, K, V, Os, dO, Ls, w.B, idx, cnt, ws=dws))
     torch.cuda.synchronize()
-    del x, Q, K, V, O, idx, cnt, tau, live, dO, ews
+    del x, Q, K, V, O, idx, cnt, tau, live, dO, Os, Ls, dws
     torch.cuda.empty_cache()
     return {"workload": w.name, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
             "seq_len": w.n, "head_dim": w.d, "alpha": w.alpha, "refine": refine,
@@ -452,7 +461,9 @@ def run_entmax_attn(bsa, torch, steps, warmup, refine=2):
             "dense_softmax_ms": t_soft, "dense_softmax_TFLOP_per_s": dense / t_soft / 1e9,
             "speedup_vs_dense_softmax": t_soft / t_ent, "live_tile_fraction": live_frac,
             "backward_ms": t_bwd, "backward_dense_equiv_TFLOP_per_s": 2.5 * dense / t_bwd / 1e9,
-            "backward_all_tiles_ms": t_bwd_all}
+            "backward_all_tiles_ms": t_bwd_all, "dense_softmax_backward_ms": t_soft_bwd,
+            "training_pass_ms": t_ent + t_bwd, "dense_softmax_training_pass_ms": t_soft + t_soft_bwd,
+            "training_pass_speedup_vs_dense_softmax": (t_soft + t_soft_bwd) / (t_ent + t_bwd)}
 
 
 def run_decode(bsa, torch, steps, warmup, with_paged=True, with_cpu=False):
