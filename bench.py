@@ -715,7 +715,10 @@ def main():
                    "inputs_sha256": r["x"]["sha256"]},
         "frac_mfma_peak_step": value / PEAK_BF16_TFLOPS,
         "stages_ms": r["stages_ms"],
-        "roofline": {"kernel": "attend_prefill_bf16", "bound": "mfma", "achieved": achieved,
+        # the library serves plain block rows of 32 or more 64-key tiles with its
+        # ping-pong kernel, shorter rows with the 4-wavefront one
+        "roofline": {"kernel": "attend_prefill_pp" if w.idx_width * (w.B // 64) >= 32
+                     else "attend_prefill_bf16", "bound": "mfma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": read_traffic(w.name, kernel_src), "avg_launch_ms": att_s * 1e3,
                      "launch_ms": r["attend_ms"],
