@@ -425,6 +425,21 @@ def run_entmax_attn(bsa, torch, steps, warmup, refine=2):
         return e0.elapsed_time(e1) / steps
 
     t_ent = timed(lambda: bsa.attend_entmax(Q, K, V, w.alpha, refine=refine, out=O))
+    # one refinement step ("AdaSplash-2", 2.A: 1-2 iterations from the
+    # histogram start): its time, and its distance from a converged run
+    # (refine 8) of the same kernel
+    t_ent1 = timed(lambda: bsa.attend_entmax(Q, K, V, w.alpha, refine=1, out=O))
+    O8, tau8 = bsa.attend_entmax(Q, K, V, w.alpha, refine=8, want_tau=True)
+
+    def distance(r):
+        Or, taur = bsa.attend_entmax(Q, K, V, w.alpha, refine=r, want_tau=True)
+        dt, do_ = (taur - tau8).abs(), (Or.float() - O8.float()).abs()
+        return {"tau_max_abs_diff_vs_refine8": float(dt.max()),
+                "tau_p99_abs_diff_vs_refine8": float(torch.quantile(dt.flatten()[::64], 0.99)),
+                "out_max_abs_diff_vs_refine8": float(do_.max())}
+    one_step = {"ms_per_step": t_ent1, **distance(1)}
+    default_steps = distance(refine)
+    del O8, tau8
     t_soft = timed(lambda: bsa.attend_prefill(Q, K, V, w.B, idx, cnt, out=O))
     dense = 4.0 * w.d * w.hq * w.batch * w.n * (w.n + 1) / 2
     _, tau, live = bsa.attend_entmax(Q, K, V, w.alpha, refine=refine, want_tau=True,
@@ -463,7 +478,8 @@ def run_entmax_attn(bsa, torch, steps, warmup, refine=2):
             "backward_ms": t_bwd, "backward_dense_equiv_TFLOP_per_s": 2.5 * dense / t_bwd / 1e9,
             "backward_all_tiles_ms": t_bwd_all, "dense_softmax_backward_ms": t_soft_bwd,
             "training_pass_ms": t_ent + t_bwd, "dense_softmax_training_pass_ms": t_soft + t_soft_bwd,
-            "training_pass_speedup_vs_dense_softmax": (t_soft + t_soft_bwd) / (t_ent + t_bwd)}
+            "training_pass_speedup_vs_dense_softmax": (t_soft + t_soft_bwd) / (t_ent + t_bwd),
+            "refine_1": one_step, "refine_default_vs_refine8": default_steps}
 
 
 def run_decode(bsa, torch, steps, warmup, with_paged=True, with_cpu=False):

@@ -14,7 +14,8 @@
 //   3. `refine` passes of the hybrid step of 2.B from the bracket's lower end
 //      (Halley for alpha <= 1.5, Newton for 1.5 < alpha <= 2, and for
 //      alpha > 2 a secant through the bracket ends with the Illinois halving;
-//      each kept inside the bracket, else bisection), the first of which also
+//      each kept inside the bracket: a Halley step outside it falls back to
+//      the Newton step, then bisection), the first of which also
 //      marks, per wavefront, the key tiles holding any x above that lower end;
 //   4. the output: only the marked tiles (a tile with every x <= tau has zero
 //      weight), p on the matrix cores against V, normalised by its sum.
@@ -587,6 +588,12 @@ __global__ __launch_bounds__(512, 1) void entmax_attn_bf16(EntmaxAttnArgs a, int
                  ? lo[qt] + hlo[qt] * (hi[qt] - lo[qt]) / (hlo[qt] - hhi[qt])
                  : 0.5 * (lo[qt] + hi[qt]);
       }
+      // for alpha <= 2 the mass is convex and decreasing in tau, so a Newton
+      // step from the root's left stays between the iterate and the root: it
+      // replaces a Halley step that leaves the bracket (Halley overshoots
+      // where keys leave the support between the iterate and the root), and
+      // bisection is the last resort
+      if (alpha <= 1.5f && !(nt >= lo[qt] && nt <= hi[qt])) nt = tau[qt] + h0 / d1;
       if (!(nt >= lo[qt] && nt <= hi[qt])) nt = (h0 == 0.0) ? tau[qt] : 0.5 * (lo[qt] + hi[qt]);
       tau[qt] = nt;
     }

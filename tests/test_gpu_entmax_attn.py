@@ -104,6 +104,32 @@ def test_entmax_attention_long_sampled():
     print(f"{len(req)} sampled rows, max abs err {worst:.3e}, mean support {sup.mean():.1f}")
 
 
+def test_entmax_attention_full_size_two_passes_converge():
+    """Every row of the token-level entmax workload at full size (N = 16384,
+    32/8 heads) reaches its threshold in the two refinement passes: against
+    sixteen passes on all 524 288 rows, and against the oracle's exact root on
+    rows whose root lies within 2e-4 of the bracket's upper end with a key
+    leaving the support in between (where an unguarded Halley step
+    overshoots) plus seeded ones."""
+    w = synth.WORKLOADS["entmax_attn_prefill_n16k"]
+    print("[entmax attention] full size, two passes", flush=True)
+    x = parity.make(w)
+    _, tau2 = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=2, want_tau=True)
+    _, tau16 = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=16, want_tau=True)
+    t2, t16 = _cpu(tau2)[0], _cpu(tau16)[0]
+    gap = np.abs(t2 - t16)
+    assert gap.max() < 1e-4, (gap.max(), np.unravel_index(gap.argmax(), gap.shape))
+    rng = np.random.default_rng(13)
+    rows = [(10, 200), (17, 11158), (18, 4808), (26, 11205)]
+    rows += [(int(h), int(t)) for h, t in zip(rng.integers(0, w.hq, 12), rng.integers(0, w.n, 12))]
+    req = np.array([[0, h, t] for h, t in rows], np.int64)
+    _, rtau, _ = oracle.entmax_attend(x["q"], x["k"], x["v"], w.alpha, req=req)
+    got = np.array([t2[h, t] for h, t in rows])
+    assert np.abs(got - rtau).max() < 1e-4, np.abs(got - rtau).max()
+    print(f"max |tau(2) - tau(16)| {gap.max():.2e}, vs exact on {len(rows)} rows "
+          f"{np.abs(got - rtau).max():.2e}")
+
+
 def test_entmax_attention_argument_errors():
     w = CASES["a15_gqa"]
     x = parity.make(w)
