@@ -25,6 +25,8 @@ CASES = {
     "a175_newton": BASE.scaled(hq=4, hkv=2, n=64 * 3 + 9, alpha=1.75, q_scale=3.0, planted_blocks=1),
     "a15_d64": BASE.scaled(hq=6, hkv=3, d=64, n=64 * 6, planted_blocks=2),
     "a15_batch2": BASE.scaled(batch=2, hq=4, hkv=2, n=64 * 3 + 21, planted_blocks=1),
+    # a group of 8 heads: two workgroups per query tile share the live rows
+    "a15_g8": BASE.scaled(hq=16, hkv=2, n=64 * 4 + 50, planted_blocks=2),
 }
 
 
@@ -130,6 +132,28 @@ def test_entmax_attention_full_size_two_passes_converge():
           f"{np.abs(got - rtau).max():.2e}")
 
 
+def test_entmax_attention_longest_sequence_sampled():
+    """The longest sequence the kernel takes (2048 key tiles, ragged: N =
+    131072 - 5), one head: sampled rows, the last ones included, against the
+    oracle."""
+    w = BASE.scaled(hq=1, hkv=1, n=131072 - 5, planted_blocks=8)
+    print("[entmax attention] N = 131067", flush=True)
+    x = parity.make(w)
+    O, tau = bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, out_dtype=torch.float32,
+                               want_tau=True)
+    rng = np.random.default_rng(21)
+    rows = sorted({0, 64, 65535, w.n - 64, w.n - 2, w.n - 1}
+                  | set(rng.choice(w.n, 18, replace=False).tolist()))
+    req = np.array([[0, 0, t] for t in rows], np.int64)
+    ref, rtau, sup = oracle.entmax_attend(x["q"], x["k"], x["v"], w.alpha, req=req)
+    got = _cpu(O)[0, 0, rows]
+    worst = parity.check_attention(w, got, ref, True)
+    terr = np.abs(_cpu(tau)[0, 0, rows] - rtau)
+    assert terr.max() < 1e-3, terr.max()
+    print(f"{len(rows)} rows, max abs err {worst:.3e}, tau err max {terr.max():.2e}, "
+          f"mean support {sup.mean():.1f}")
+
+
 def test_entmax_attention_argument_errors():
     w = CASES["a15_gqa"]
     x = parity.make(w)
@@ -207,7 +231,7 @@ def test_entmax_attention_backward_sums_and_determinism():
     assert float((dV.sum(dim=2) - ref).abs().max()) <= 1e-2 * float(ref.abs().max())
 
 
-@pytest.mark.parametrize("name", ["a15_gqa", "a2_sparsemax", "a175_newton"])
+@pytest.mark.parametrize("name", ["a15_gqa", "a2_sparsemax", "a175_newton", "a15_g8"])
 @pytest.mark.parametrize("refine", [2, 0])
 def test_entmax_live_tiles_cover_every_support(name, refine):
     """The forward's live key tiles hold every key with a nonzero oracle
