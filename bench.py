@@ -63,7 +63,8 @@ LONG = "bf16_long_prefill_n256k"
 TOKEN = "token_entmax_prefill_n32k"
 ENTMAX_ATTN = "entmax_attn_prefill_n16k"
 PROFILES = os.path.join(HERE, "profiles")
-COUNTERS = {HEADLINE: "attend_prefill_bf16_long_n256k_counters.txt",
+COUNTERS = {ENTMAX_ATTN: "entmax_attn_bf16_n16k_counters.txt",
+            HEADLINE: "attend_prefill_bf16_long_n256k_counters.txt",
             GQA32K: "attend_prefill_bf16_gqa_n32k_counters.txt"}
 
 
@@ -92,7 +93,22 @@ def parse():
                    help="query blocks (all heads) of the headline's CPU-baseline sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    p.add_argument("--entmax-attn-only", action="store_true",
+                   help="only run the token-level entmax attention forward (counter runs)")
     return p.parse_args()
+
+
+def entmax_attn_only(steps, warmup, refine=2):
+    """The token-level entmax attention forward alone, for counter runs."""
+    import torch
+    import block_sparse_attention_summarize_amd as bsa
+    w = synth.WORKLOADS[ENTMAX_ATTN]
+    x = device_inputs(w, torch)
+    O = torch.empty_like(x["Q"])
+    for _ in range(warmup + steps):
+        bsa.attend_entmax(x["Q"], x["K"], x["V"], w.alpha, refine=refine, out=O)
+    torch.cuda.synchronize()
+    print(json.dumps({"entmax_attn_launches": warmup + steps, "refine": refine}))
 
 
 def copy_calibration(mib, reps=3):
@@ -479,7 +495,11 @@ def run_entmax_attn(bsa, torch, steps, warmup, refine=2):
             "backward_all_tiles_ms": t_bwd_all, "dense_softmax_backward_ms": t_soft_bwd,
             "training_pass_ms": t_ent + t_bwd, "dense_softmax_training_pass_ms": t_soft + t_soft_bwd,
             "training_pass_speedup_vs_dense_softmax": (t_soft + t_soft_bwd) / (t_ent + t_bwd),
-            "refine_1": one_step, "refine_default_vs_refine8": default_steps}
+            "refine_1": one_step, "refine_default_vs_refine8": default_steps,
+            "hbm_bytes_per_launch": read_traffic(
+                ENTMAX_ATTN, os.path.join(HERE, "block_sparse_attention_summarize_amd", "csrc",
+                                          "entmax_attn.hip")),
+            "algorithmic_bytes_per_launch": (2 * w.hq + 2 * w.hkv) * w.batch * w.n * w.d * 2}
 
 
 def run_decode(bsa, torch, steps, warmup, with_paged=True, with_cpu=False):
@@ -692,6 +712,9 @@ def main():
     a = parse()
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)
+        return
+    if a.entmax_attn_only:
+        entmax_attn_only(a.steps, a.warmup)
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
