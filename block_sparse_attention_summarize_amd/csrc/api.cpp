@@ -1089,8 +1089,9 @@ int bsa_attend_entmax_backward(const bsa_shape* s, const void* Q, const void* K,
     return fail(BSA_ERR_UNSUPPORTED, "tau must be 4-byte aligned");
   if (live && (reinterpret_cast<uintptr_t>(live) & 3u) != 0)
     return fail(BSA_ERR_UNSUPPORTED, "live must be 4-byte aligned");
-  if (live && (s->q_len + 63) / 64 > 2048)
-    return fail(BSA_ERR_UNSUPPORTED, "live supports at most %d tokens", 64 * 2048);
+  if ((s->q_len + 63) / 64 > 2048)
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_attend_entmax_backward supports at most %d tokens",
+                64 * 2048);
   if (g_dtype != s->dtype && g_dtype != BSA_F32)
     return fail(BSA_ERR_UNSUPPORTED, "g_dtype must be the input dtype or BSA_F32");
   if ((rc = check_strides("dQ/dK/dV", s->q_stride, g_dtype)) != BSA_OK) return rc;

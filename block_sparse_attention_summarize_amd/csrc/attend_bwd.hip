@@ -58,6 +58,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxTilesBwd = 256;  // tile-list chunk staged in LDS (query side)
+constexpr int kMaxEntTilesDq = 2048;  // entmax query side: key tiles of one sequence
 constexpr int kMaxPriorEntries = 80;  // list width with a prior (per-wave sums in LDS)
 constexpr int kBwdQT = 2, kBwdNW = 4;  // query side: 16-query tiles per wave, waves
 
@@ -265,6 +266,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
   __shared__ float lds_db[TOK ? 1 : NW][kMaxPriorEntries];  // per wave: dL/d(bias) per list entry
   __shared__ uint64_t lds_tbits[TOK ? kMaxTilesBwd : 1];   // TOK: the entry's token word
   __shared__ float lds_dbq[TOK ? 2 : 1][NW][16 * QT];      // TOK: per wave, per query: sum of dS
+  // ENT: per wave, the key tiles where some of its queries has weight (found
+  // by the gathering walk; the second walk skips the others)
+  __shared__ uint32_t lds_wlive[ENT ? NW : 1][ENT ? kMaxEntTilesDq / 32 : 1];
   __shared__ int lds_ntiles;
 
   const int tid = threadIdx.x;
@@ -401,6 +405,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
 
   if (!TOK && a.dbpart)
     for (int e = lane; e < a.k_max; e += 64) lds_db[w][e] = 0.f;
+  if constexpr (ENT)
+    for (int e = lane; e < kMaxEntTilesDq / 32; e += 64) lds_wlive[w][e] = 0u;
   // entmax: per query column the sums over its keys of t^(1/(alpha-1)) (the
   // normaliser Z), of g dP and of g (g = t^((2-alpha)/(alpha-1)))
   const float a1s = (a.alpha - 1.f) * a.sm_scale;
@@ -479,8 +485,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
       float dcol[QT];  // TOK: per query column, the sum of dS over the tile
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) dcol[qt] = 0.f;
-      // a wave whose queries all precede the tile has nothing to add
-      if (active && k0 <= qpos0 + QPW - 1 && wave_on) {
+      // a wave whose queries all precede the tile has nothing to add, and
+      // (entmax, second walk) nor has one none of whose queries weights it
+      const bool wave_live =
+          !ENT || pass == 0 ||
+          ((__builtin_amdgcn_readfirstlane(lds_wlive[w][(k0 >> 6) >> 5]) >> ((k0 >> 6) & 31)) & 1u);
+      if (active && k0 <= qpos0 + QPW - 1 && wave_on && wave_live) {
         const uint16_t* kt_ = lds.k[buf];
         const uint16_t* vt_ = lds.v[buf];
         // exponent offset per query column: the bias minus lse
@@ -505,6 +515,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
         f32x4 dsp[QT];
         bool pair_live[2];
         bool live_pair = false;  // entmax: some weight in the current pair of slices
+        bool tile_live = false;  // entmax: some weight in the tile
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           f32x4 s[QT], dp[QT];
@@ -531,6 +542,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
                        !(diag && rel0 + kt * 16 + j - qt * 16 > 0);
             const bool live = __ballot(any) != 0;
             live_pair = (kt & 1) ? (live_pair || live) : live;
+            tile_live |= live;
             if (live) {
 #pragma unroll
               for (int ks = 0; ks < KS; ++ks) {
@@ -610,6 +622,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq(BwdArgs a, int wpb) {
               for (int qt = 0; qt < QT; ++qt) acc[dt][qt] = mfma16(kf, dsf[qt][kk], acc[dt][qt]);
             }
           }
+        }
+        if constexpr (ENT && pass == 0) {
+          // (only this wave writes its words; the walks see the same tiles)
+          if (lane == 0 && tile_live) lds_wlive[w][(k0 >> 6) >> 5] |= 1u << ((k0 >> 6) & 31);
         }
         if (!ENT && !TOK && a.dbpart) {
           // this unit's part of dL/d(bias) of the tile's list entry (a block

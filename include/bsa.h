@@ -416,10 +416,12 @@ int bsa_attend_entmax(const bsa_shape *shape, const void *Q, const void *K, cons
  *   dQ_t = sm_scale sum_j dz_j k_j,  dK_j = sm_scale sum_t dz_tj q_t,
  *   dV_j = sum_t p_tj dO_t  (key sums over the group's query heads).
  * A first walk over each query's causal key tiles gathers Z and <g, dP> /
- * sum g, a second forms dQ; the key side walks the query tiles from each key
- * tile on.  Products for keys outside every support of a tile are zero.
+ * sum g, a second forms dQ over the tiles where the walk found weight; the
+ * key side walks the query tiles from each key tile on.  Products for keys
+ * outside every support of a tile are zero.
  *   Q, K, V bf16 [batch, H, N, d] as given to bsa_attend_entmax (shape with
- *         mode BSA_PREFILL, block 64); alpha in (1, 2]; sm_scale 0: 1/sqrt(d).
+ *         mode BSA_PREFILL, block 64, N <= 131072); alpha in (1, 2];
+ *         sm_scale 0: 1/sqrt(d).
  *   dO    bf16 [batch, Hq, N, d] with o_stride.
  *   tau   fp32 [batch, Hq, N]: tau_out of bsa_attend_entmax.
  *   live  NULL (walk every causal tile) or live_out of the same
@@ -427,7 +429,7 @@ int bsa_attend_entmax(const bsa_shape *shape, const void *Q, const void *K, cons
  *   dQ, dK, dV  out, g_dtype (bf16 or BSA_F32), strides of Q, K, V.
  *   ws    bsa_workspace_size(BSA_OP_ATTEND_ENTMAX_BACKWARD, shape, 0) bytes.
  * Errors: BSA_ERR_INVALID, BSA_ERR_UNSUPPORTED (fp32 inputs, block != 64,
- * alpha > 2, strides), BSA_ERR_WORKSPACE.
+ * alpha > 2, N > 131072, strides), BSA_ERR_WORKSPACE.
  */
 int bsa_attend_entmax_backward(const bsa_shape *shape, const void *Q, const void *K,
                                const void *V, const void *dO, const float *tau,
