@@ -349,3 +349,34 @@ def test_decode_noalloc_validation():
     assert call(shape(**dec), k=0) == -1 and "k_total" in err()
     assert call(shape(**dec), force=8) == -1
     assert call(shape(**dec), O=None) == -1
+
+
+def test_entmax_attention_validation():
+    """Token-level entmax attention and its backward: every argument is
+    checked on the host before anything is enqueued."""
+    s = shape(q_len=64 * 5 + 3, kv_len=64 * 5 + 3)
+
+    def fwd(sh, alpha=1.5, refine=2, O=FAKE, tau=None, live=None):
+        return lib.bsa_attend_entmax(ctypes.byref(sh), FAKE, FAKE, FAKE, alpha, refine, 0.0, O,
+                                     sh.dtype, tau, live, None)
+
+    def bwd(sh, alpha=1.5, tau=FAKE, live=None, ws_bytes=None):
+        n = lib.bsa_workspace_size(bsa.OP_ATTEND_ENTMAX_BACKWARD, ctypes.byref(sh), 0)
+        return lib.bsa_attend_entmax_backward(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, tau, live,
+                                              alpha, 0.0, FAKE, FAKE, FAKE, sh.dtype,
+                                              ctypes.c_void_p(0x200000),
+                                              n if ws_bytes is None else ws_bytes, None)
+
+    assert fwd(s, alpha=1.0) == -1 and "alpha" in err()
+    assert fwd(s, alpha=17.0) == -2 and "alpha <= 16" in err()
+    assert fwd(s, refine=25) == -1 and "refine" in err()
+    assert fwd(s, O=None) == -1
+    assert fwd(shape(dtype=bsa.F32)) == -2 and "bf16" in err()
+    assert fwd(s, tau=ctypes.c_void_p(0x100004)) == -2 and "aligned" in err()
+    big = shape(q_len=131072 + 64, kv_len=131072 + 64, hq=1, hkv=1)
+    assert fwd(big) == -2 and "131072" in err()
+    assert bwd(s, alpha=2.5) == -2
+    assert bwd(s, tau=None) == -1 and "tau" in err()
+    assert bwd(shape(q_len=320, kv_len=320, B=128)) == -2 and "block 64" in err()
+    assert bwd(big) == -2 and "131072" in err()
+    assert bwd(s, ws_bytes=0) == -4
