@@ -27,6 +27,7 @@
 // Single-token decode lives in decode.hip.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lds_tiles.hpp"
 #include "walk.hpp"
 
 namespace bsa {
@@ -557,13 +558,6 @@ struct PpLds {
   alignas(16) uint16_t v[3][64 * D];
 };
 
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane (the
-// wave's 1 KB block starts at lds, which must be wave-uniform)
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, 0, 0, 0);
-}
-
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(512, 1) void attend_prefill_pp(AttendArgs a, int wpb) {
   constexpr int NW = 8, QT = 2, QPW = 32;
@@ -605,9 +599,9 @@ __global__ __launch_bounds__(512, 1) void attend_prefill_pp(AttendArgs a, int wp
   int jpre = -1;
   if (w == 0 && lane < a.k_max * nsub) jpre = walk.list[lane / nsub];
 
-  const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
+  const auto rk = make_desc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
                             head_bytes(a.kv_len, a.ks.t, D, 2));
-  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
+  const auto rv = make_desc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
                             head_bytes(a.kv_len, a.vs.t, D, 2));
   const uint32_t kst = static_cast<uint32_t>(a.ks.t * 2), vst = static_cast<uint32_t>(a.vs.t * 2);
 

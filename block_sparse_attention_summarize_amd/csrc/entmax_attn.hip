@@ -217,9 +217,9 @@ __global__ __launch_bounds__(512, 1) void entmax_attn_bf16(EntmaxAttnArgs a, int
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) valid[qt] = active && qpos0 + qt * 16 + (lane & 15) < a.n;
 
-  const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
+  const auto rk = make_desc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
                             head_bytes(a.n, a.ks.t, D, 2));
-  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
+  const auto rv = make_desc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
                             head_bytes(a.n, a.vs.t, D, 2));
   const uint32_t kst = static_cast<uint32_t>(a.ks.t * 2), vst = static_cast<uint32_t>(a.vs.t * 2);
 

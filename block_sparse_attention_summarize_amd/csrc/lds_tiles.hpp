@@ -27,12 +27,34 @@ static_assert(SwzTile<128>::kswz(16) == SwzTile<128>::kswz(0) &&
               "swizzles repeat every 16 rows");
 
 // 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane (the
-// wave's 1 KB block starts at lds, which must be wave-uniform).  A plain
-// function, not a lambda or template, so that the host pass of every kernel
-// that calls it sees one definition.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, 0, 0, 0);
+// wave's 1 KB block starts at lds, which must be wave-uniform).  The load is
+// issued from assembly, so the compiler does not know that it writes LDS and
+// inserts no wait for it before later LDS reads: it cannot tell the rotating
+// tile buffers apart and would otherwise wait for every load in flight,
+// including those just issued for a later tile (measured 3.5 % of the long
+// prefill).  Callers order the loads with their own vmcnt waits and barriers.
+// The descriptor is the one make_rsrc builds (base, stride 0, extent,
+// raw-buffer flags), held in SGPRs.  Plain functions, not lambdas or
+// templates, so that the host pass of every kernel that calls them sees one
+// definition.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  d.y = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xFFFFu);
+  d.z = __builtin_amdgcn_readfirstlane(bytes);
+  d.w = 0x00020000u;
+  return d;
+}
+__device__ __forceinline__ void lds_dma16(const u32x4& d, const void* lds, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (const __attribute__((address_space(3))) void*)lds)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(d)
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N): all but the N youngest vector memory operations of this
