@@ -55,6 +55,10 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   extern __shared__ float dyn[];    // [nblk] scores, then the merge buffer
   __shared__ float qh[D];
   __shared__ float qa[GS][D];
+  // bf16 with up to 4 heads: q.k by packed bf16 dot products from the
+  // queries as stored (more heads keep the fp32 form: registers)
+  constexpr bool kDot = sizeof(T) == 2 && GS <= 4;
+  __shared__ uint16_t qr[kDot ? GS : 1][D];
   __shared__ int hist[256];
   __shared__ int bcast[2];
   __shared__ int wave_tot[kNW];
@@ -86,7 +90,10 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
   auto load_qa = [&]() {
     for (int e = tid; e < gs * D; e += kNT) {
       const int hh = e / D, c = e % D;
-      qa[hh][c] = qval(h0 + hh, c) * scl;
+      if constexpr (kDot)
+        qr[hh][c] = (Qb + (h0 + hh) * a.qs.h)[c];
+      else
+        qa[hh][c] = qval(h0 + hh, c) * scl;
     }
   };
 
@@ -299,47 +306,116 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
       x[6] = __uint_as_float(u[RPL - 1].z); x[7] = __uint_as_float(u[RPL - 1].w);
     }
   };
+  // kDot: the lane's 8 query elements of each head as bf16 pairs; q.k by
+  // packed bf16 dot products (exact products, fp32 sums), scaled after the
+  // reduction over the key's lanes; each V slice is unpacked once for all
+  // heads
+  uint4 qp[kDot ? GS : 1];
+  if constexpr (kDot) {
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+      qp[hh] = hh < gs ? *reinterpret_cast<const uint4*>(&qr[hh][c8 * 8]) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  auto dot8 = [&](const uint4& k, const uint4& q) {
+    float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.x),
+                                                __builtin_bit_cast(bf16x2_t, q.x), 0.f, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.y),
+                                          __builtin_bit_cast(bf16x2_t, q.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.z),
+                                          __builtin_bit_cast(bf16x2_t, q.z), acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.w),
+                                           __builtin_bit_cast(bf16x2_t, q.w), acc, false);
+  };
   auto compute = [&](int ch, const uint4 (&kb)[KPC][RPL], const uint4 (&vb)[KPC][RPL]) {
     const int t0 = chunk_t0(ch);
     if (t0 < 0) return;
     bool ok[KPC];
 #pragma unroll
     for (int it = 0; it < KPC; ++it) ok[it] = t0 + it * KPI + kg < L;
+    if constexpr (kDot) {
+      float sv[GS][KPC];
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-      if (hh >= gs) break;
-      float s[KPC];
-      float mx = -INFINITY;
+      for (int hh = 0; hh < GS; ++hh) {
+        if (hh >= gs) break;
 #pragma unroll
-      for (int it = 0; it < KPC; ++it) {
-        float kv[8];
-        unpack(kb[it], kv);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(kv[e], qa[hh][c8 * 8 + e], acc);
-        acc = lane_sum<LPK>(acc);
-        s[it] = ok[it] ? acc : -INFINITY;
-        mx = fmaxf(mx, s[it]);
+        for (int it = 0; it < KPC; ++it) {
+          const float acc = lane_sum<LPK>(dot8(kb[it][0], qp[hh]));
+          sv[hh][it] = ok[it] ? acc * scl : -INFINITY;
+        }
       }
-      if constexpr (LPK == 8) mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
-      mx = swap32_max(swap16_max(mx));
-      const float mn = fmaxf(m[hh], mx);
-      const float base = mn == -INFINITY ? 0.f : mn;
-      const float f = __builtin_amdgcn_exp2f(m[hh] - base);
-      m[hh] = mn;
-      float ls = 0.f;
+      float base[GS], ls[GS];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] *= f;
+      for (int hh = 0; hh < GS; ++hh) {
+        if (hh >= gs) break;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int it = 0; it < KPC; ++it) mx = fmaxf(mx, sv[hh][it]);
+        if constexpr (LPK == 8) mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
+        mx = swap32_max(swap16_max(mx));
+        const float mn = fmaxf(m[hh], mx);
+        base[hh] = mn == -INFINITY ? 0.f : mn;
+        const float f = __builtin_amdgcn_exp2f(m[hh] - base[hh]);
+        m[hh] = mn;
+        ls[hh] = 0.f;
+        l[hh] *= f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] *= f;
+      }
 #pragma unroll
       for (int it = 0; it < KPC; ++it) {
-        const float p = __builtin_amdgcn_exp2f(s[it] - base);
         float vv[8];
         unpack(vb[it], vv);
-        ls += p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(p, vv[e], o[hh][e]);
+        for (int hh = 0; hh < GS; ++hh) {
+          if (hh >= gs) break;
+          const float p = __builtin_amdgcn_exp2f(sv[hh][it] - base[hh]);
+          ls[hh] += p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(p, vv[e], o[hh][e]);
+        }
       }
-      l[hh] = l[hh] * f + ls;
+#pragma unroll
+      for (int hh = 0; hh < GS; ++hh) {
+        if (hh >= gs) break;
+        l[hh] += ls[hh];
+      }
+    } else {
+  #pragma unroll
+      for (int hh = 0; hh < GS; ++hh) {
+        if (hh >= gs) break;
+        float s[KPC];
+        float mx = -INFINITY;
+  #pragma unroll
+        for (int it = 0; it < KPC; ++it) {
+          float kv[8];
+          unpack(kb[it], kv);
+          float acc = 0.f;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fmaf(kv[e], qa[hh][c8 * 8 + e], acc);
+          acc = lane_sum<LPK>(acc);
+          s[it] = ok[it] ? acc : -INFINITY;
+          mx = fmaxf(mx, s[it]);
+        }
+        if constexpr (LPK == 8) mx = fmaxf(mx, __shfl_xor(mx, 8, kWave));
+        mx = swap32_max(swap16_max(mx));
+        const float mn = fmaxf(m[hh], mx);
+        const float base = mn == -INFINITY ? 0.f : mn;
+        const float f = __builtin_amdgcn_exp2f(m[hh] - base);
+        m[hh] = mn;
+        float ls = 0.f;
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] *= f;
+  #pragma unroll
+        for (int it = 0; it < KPC; ++it) {
+          const float p = __builtin_amdgcn_exp2f(s[it] - base);
+          float vv[8];
+          unpack(vb[it], vv);
+          ls += p;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(p, vv[e], o[hh][e]);
+        }
+        l[hh] = l[hh] * f + ls;
+      }
     }
   };
   {
