@@ -107,26 +107,48 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
     rule.kv_lens = a.kv_lens;
     const RowInfo ri = row_info(rule, b, 0);
     const int n = ri.cand_end;
-    // stream the summaries of the candidates, kUnroll loads in flight per lane
+    // Stream the summaries of the candidates.  Wavefront w takes the slices
+    // of kSel candidates w, w + kNW, ... (its own contiguous rows), in rounds
+    // of kUnroll loads per lane with the next round in flight, and the scores
+    // go to LDS.  With a top-m below kSel a wavefront selects the exact top-m
+    // of each slice it finished at once (wave_topm, no barrier: the slices end
+    // at different times, so this first round of the tournament overlaps the
+    // other wavefronts' streaming); its survivors, in id order and padded
+    // with -1, wait in bk0/bi0 for the remaining rounds.
     const int c4 = lane % LPR;
     const auto rs = make_rsrc(a.S + static_cast<int64_t>(row) * a.nblk * D,
                               static_cast<uint32_t>(n) * D * 4);  // candidates only
-    constexpr int STEP = kNW * RPW;        // rows per workgroup load instruction
-    constexpr int ROUND = STEP * kUnroll;  // rows per load round
+    constexpr int RROWS = RPW * kUnroll;  // rows per wavefront round
+    constexpr int RPS = kSel / RROWS;     // rounds per slice
+    static_assert(kSel % RROWS == 0, "slice of whole rounds");
+    const int nslice = (n + kSel - 1) / kSel;
+    const int nq = nslice > w ? ((nslice - 1 - w) / kNW + 1) * RPS : 0;  // this wavefront's rounds
+    auto round_row0 = [&](int q) { return (w + (q / RPS) * kNW) * kSel + (q % RPS) * RROWS; };
     // two register buffers: the next round's loads are in flight while the
     // current one is reduced (rows past n read as zero, nothing is written)
     uint4 va[kUnroll], vb[kUnroll];
-    auto issue = [&](int base, uint4 (&v)[kUnroll]) {
+    auto issue = [&](int q, uint4 (&v)[kUnroll]) {
+      const int r0 = q < nq ? round_row0(q) : n;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t j = static_cast<uint32_t>(base + u * STEP + w * RPW + lane / LPR);
+        const uint32_t j = static_cast<uint32_t>(r0 + u * RPW + lane / LPR);
         v[u] = buf_load16(rs, j * (D * 4) + c4 * 16);
       }
     };
+    int m = a.k_total - ri.nforced;
+    m = m < 0 ? 0 : m;
+    const bool waves_first = m > 0 && m < kSel;
+    const int cap = nslice * (m > 0 ? m : 1);
+    uint32_t* bk0 = reinterpret_cast<uint32_t*>(sel + a.k_total);
+    int32_t* bi0 = reinterpret_cast<int32_t*>(bk0 + cap);
+    uint32_t* bk1 = reinterpret_cast<uint32_t*>(bi0 + cap);
+    int32_t* bi1 = reinterpret_cast<int32_t*>(bk1 + cap);
+    uint32_t* fk = reinterpret_cast<uint32_t*>(bi1 + cap);
+    int32_t* fi = reinterpret_cast<int32_t*>(fk + a.k_total);
     // the first round of summaries is requested before the query heads, so
     // the two reads' latencies overlap; then the attention heads and the
     // routing query (the group's sum)
-    if (n > 0) issue(0, va);
+    if (nq > 0) issue(0, va);
     load_qa();
     for (int c = tid; c < D; c += kNT) {
       float s = 0.f;
@@ -135,10 +157,11 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
     }
     __syncthreads();
     const float4 q4 = reinterpret_cast<const float4*>(qh)[c4];
-    auto reduce = [&](int base, const uint4 (&v)[kUnroll]) {
+    auto reduce = [&](int q, const uint4 (&v)[kUnroll]) {
+      const int r0 = round_row0(q);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int j = base + u * STEP + w * RPW + lane / LPR;
+        const int j = r0 + u * RPW + lane / LPR;
         float p = q4.x * __uint_as_float(v[u].x);
         p = fmaf(q4.y, __uint_as_float(v[u].y), p);
         p = fmaf(q4.z, __uint_as_float(v[u].z), p);
@@ -146,18 +169,42 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
         p = lane_sum<LPR>(p);
         if (c4 == 0 && j < n) dyn[j] = p * a.score_scale;
       }
+      if (!waves_first || q % RPS != RPS - 1) return;
+      // the slice is complete: its exact top-m (element e of lane l is
+      // candidate r0 + 64 e + l, so ties go to the lower id)
+      __builtin_amdgcn_wave_barrier();
+      const int sl = w + (q / RPS) * kNW;
+      uint32_t key[4];
+      bool valid[4], pick[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = sl * kSel + e * kWave + lane;
+        valid[e] = i < n && !is_forced(ri, i);
+        key[e] = valid[e] ? float_key(dyn[i]) : 0u;
+      }
+      wave_topm<4>(key, valid, m, pick);
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t mk = __ballot(pick[e]);
+        if (pick[e]) {
+          const int pos = sl * m + cnt + lanes_below(mk);
+          bk0[pos] = key[e];
+          bi0[pos] = sl * kSel + e * kWave + lane;
+        }
+        cnt += __popcll(mk);
+      }
+      for (int t = cnt + lane; t < m; t += kWave) bi0[sl * m + t] = -1;
     };
-    for (int base = 0; base < n; base += 2 * ROUND) {
-      issue(base + ROUND, vb);
-      reduce(base, va);
-      if (base + ROUND >= n) break;
-      issue(base + 2 * ROUND, va);
-      reduce(base + ROUND, vb);
+    for (int q = 0; q < nq; q += 2) {
+      issue(q + 1, vb);
+      reduce(q, va);
+      if (q + 1 >= nq) break;
+      issue(q + 2, va);
+      reduce(q + 1, vb);
     }
     __syncthreads();
     const int n_elig = n - ri.nforced_below(n);
-    int m = a.k_total - ri.nforced;
-    m = m < 0 ? 0 : m;
     auto get = [&](int e, uint32_t& key) -> bool {
       if (e >= n || is_forced(ri, e)) return false;
       key = float_key(dyn[e]);
@@ -166,25 +213,20 @@ __global__ __launch_bounds__(kNT) void decode_fused(DecodeArgs a) {
     int32_t* gidx = a.idx ? a.idx + static_cast<int64_t>(row) * a.k_total : nullptr;
     const bool write = gidx != nullptr && hs == 0;
     if (m < kSel) {
-      // per-wave exact top-m of 256-candidate slices, then of the survivors
-      // (ballot bit-splitting, two barriers per round); forced blocks added
-      // around the routed ids, which lie strictly between them
-      const int cap = ((n + kSel - 1) / kSel) * (m > 0 ? m : 1);
-      uint32_t* bk0 = reinterpret_cast<uint32_t*>(sel + a.k_total);
-      int32_t* bi0 = reinterpret_cast<int32_t*>(bk0 + cap);
-      uint32_t* bk1 = reinterpret_cast<uint32_t*>(bi0 + cap);
-      int32_t* bi1 = reinterpret_cast<int32_t*>(bk1 + cap);
-      uint32_t* fk = reinterpret_cast<uint32_t*>(bi1 + cap);
-      int32_t* fi = reinterpret_cast<int32_t*>(fk + a.k_total);
+      // the remaining rounds over the slices' survivors (per-wave exact top-m
+      // of 256-entry slices, ballot bit-splitting, until one slice is left);
+      // forced blocks added around the routed ids, which lie strictly between
+      // them
+      const int len = nslice * m;
       const int nr = m == 0 ? 0
                             : tournament<kNT>(
-                                  n, m,
+                                  len, m,
                                   [&](int i, uint32_t& key, int32_t& id, bool& valid) {
-                                    valid = i < n && !is_forced(ri, i);
-                                    key = valid ? float_key(dyn[i]) : 0u;
-                                    id = i;
+                                    valid = i < len && bi0[i] >= 0;
+                                    key = valid ? bk0[i] : 0u;
+                                    id = valid ? bi0[i] : -1;
                                   },
-                                  bk0, bi0, bk1, bi1, fk, fi, a.k_total);
+                                  bk1, bi1, bk0, bi0, fk, fi, a.k_total);
       const int lead = (ri.f0 == 0 && (a.force & 2u)) ? 1 : 0;
       for (int q = tid; q < nr; q += kNT) sel[lead + q] = fi[q];
       if (tid == 0) {
