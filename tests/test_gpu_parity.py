@@ -354,6 +354,13 @@ DECODE_WIDE = {
     # more routed blocks than the partitioned path keeps
     "decode_k300": W["bf16_decode_l128k"].scaled(batch=1, hq=4, hkv=1, n=64 * 400, k_total=301,
                                                  kv_lens=(64 * 400,)),
+    # more 256-candidate slices than wavefronts (12: four wavefronts take two
+    # each, the ragged row 6), and a top-100 whose slice survivors need two
+    # more tournament rounds (11 x 100 -> 5 x 100 -> 2 x 100 -> 100)
+    "decode_slices": W["bf16_decode_l128k"].scaled(batch=2, hq=4, hkv=1, n=64 * 3000 + 17,
+                                                   k_total=33, kv_lens=(64 * 3000 + 17, 64 * 1300 + 5)),
+    "decode_slices_k101": W["bf16_decode_l128k"].scaled(batch=1, hq=8, hkv=2, n=64 * 2600,
+                                                        k_total=101, kv_lens=(64 * 2600,)),
 }
 
 
