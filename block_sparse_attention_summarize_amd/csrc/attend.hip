@@ -46,16 +46,18 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c)
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Double-buffered K and V tiles, both row-major (64 keys x D).  Row padding
-// spreads each read instruction over all 64 banks: K fragments read 16 B from
-// 16 rows (a 16-B pad staggers rows by 4 banks); the transposing V reads take
-// 32 B from each of 8 rows per half-wave (a 32-B pad staggers rows by 8).
-template <int D>
-struct PrefillLds {
-  static constexpr int KST = D + 8;   // K row stride (bf16 elements)
-  static constexpr int VST = D + 16;  // V row stride
-  alignas(16) uint16_t k[2][64 * KST];
-  alignas(16) uint16_t v[2][64 * VST];
+// K and V tiles (64 keys x D, bf16) in NBUF rotating buffers, filled by
+// direct-to-LDS loads.  Rows are unpadded; the 16-byte chunks of a row are
+// XOR-swizzled so that the K fragment reads (16 rows x 16 bytes per half-wave)
+// and the transposing V reads (8 rows x 32 bytes) hit every bank once.
+template <int D, int NBUF = 3>
+struct PpLds {
+  static constexpr int NC = D / 8;     // 16-byte chunks per row
+  static constexpr int RPL = 16 / NC;  // rows per 256-byte bank line
+  __host__ __device__ static constexpr int kswz(int r) { return (r / RPL) & (NC - 1); }
+  __host__ __device__ static constexpr int vswz(int r) { return ((r / RPL) & (NC / 2 - 1)) << 1; }
+  alignas(16) uint16_t k[NBUF][64 * D];
+  alignas(16) uint16_t v[NBUF][64 * D];
 };
 
 constexpr float kRescale = 8.f;  // lazy rescale threshold, log2 units
@@ -81,22 +83,21 @@ constexpr int kPingPongMinTiles = 32;  // list width (in 64-key tiles) from whic
 // so they share every K/V tile staged in LDS.
 template <int D, int QT, int NW, bool OUT_F32, bool TOK, bool BIAS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArgs a, int wpb) {
-  constexpr int NT = NW * 64;
   constexpr int QPW = 16 * QT;  // queries per wave
   constexpr int KS = D / 32;    // k-steps of S^T = K Q^T
   constexpr int DT = D / 16;    // 16-row d tiles of O^T
-  constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int KTOT = 64 * CPR;                // 16-byte chunks per K (or V) tile
-  constexpr int KITEMS = (KTOT + NT - 1) / NT;  // per thread
+  constexpr int NC = D / 8;     // 16-byte chunks per row
+  constexpr int NI = 64 * NC / 64 / NW;  // 1 KB direct-to-LDS loads per wave per tensor
+  static_assert(NI >= 1 && NI * NW * 64 == 64 * NC, "tile split over the wavefronts");
   constexpr int MAXT = TOK ? kMaxTilesTok : kMaxTiles;
-  __shared__ PrefillLds<D> lds;
+  __shared__ PpLds<D, 2> lds;
   __shared__ int lds_tiles[MAXT];
   __shared__ uint64_t lds_tbits[TOK ? MAXT : 1];
   // BIAS: the tile's bias in score units (block rows) or its list entry (token tiles)
   __shared__ float lds_tbias[BIAS && !TOK ? MAXT : 1];
   __shared__ int lds_tent[BIAS && TOK ? MAXT : 1];
   __shared__ int lds_ntiles;
-  using L = PrefillLds<D>;
+  using L = PpLds<D, 2>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -130,9 +131,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
   int jpre = -1;
   if (w == 0 && lane < a.k_max * nsub) jpre = walk.list[lane / nsub];
 
-  const auto rk = make_rsrc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
+  const auto rk = make_desc(static_cast<const uint16_t*>(a.K) + b * a.ks.b + g * a.ks.h,
                             head_bytes(a.kv_len, a.ks.t, D, 2));
-  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
+  const auto rv = make_desc(static_cast<const uint16_t*>(a.V) + b * a.vs.b + g * a.vs.h,
                             head_bytes(a.kv_len, a.vs.t, D, 2));
   const uint32_t kst = static_cast<uint32_t>(a.ks.t * 2), vst = static_cast<uint32_t>(a.vs.t * 2);
 
@@ -175,40 +176,41 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
     for (int qt = 0; qt < QT; ++qt) dst[qt] = bp[qt * 16] * inv_sm;
   };
 
-  uint4 kreg[KITEMS];
-  uint4 vreg[KITEMS];
-  auto load_tile = [&](int k0) {
+  // direct-to-LDS loads: wave instruction it fills bytes [1 KB (w NI + it),
+  // +1 KB) of a tile; lane l's 16 bytes land at chunk q = 64 (w NI + it) + l,
+  // i.e. row q / NC, physical chunk q % NC, which holds logical chunk p ^ swz(row)
+  uint32_t koff[NI], voff[NI];
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int flat = tid + NT * it;
-      const int r = flat / CPR, c = flat % CPR;
-      if (KTOT % NT == 0 || flat < KTOT)
-        kreg[it] = buf_load16(rk, static_cast<uint32_t>(k0 + r) * kst + c * 16);
-    }
+  for (int it = 0; it < NI; ++it) {
+    const int q = (w * NI + it) * 64 + lane;
+    const int r = q / NC, p = q % NC;
+    koff[it] = static_cast<uint32_t>(r) * kst + ((p ^ L::kswz(r)) * 16);
+    voff[it] = static_cast<uint32_t>(r) * vst + ((p ^ L::vswz(r)) * 16);
+  }
+  auto load_tile = [&](int k0, int buf) {
+    const uint32_t kb = static_cast<uint32_t>(k0) * kst, vb = static_cast<uint32_t>(k0) * vst;
 #pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int flat = tid + NT * it;
-      const int r = flat / CPR, c = flat % CPR;
-      if (KTOT % NT == 0 || flat < KTOT)
-        vreg[it] = buf_load16(rv, static_cast<uint32_t>(k0 + r) * vst + c * 16);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int flat = tid + NT * it;
-      const int r = flat / CPR, c = flat % CPR;
-      if (KTOT % NT == 0 || flat < KTOT)
-        *reinterpret_cast<uint4*>(&lds.k[buf][r * L::KST + c * 8]) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < KITEMS; ++it) {
-      const int flat = tid + NT * it;
-      const int r = flat / CPR, c = flat % CPR;
-      if (KTOT % NT == 0 || flat < KTOT)
-        *reinterpret_cast<uint4*>(&lds.v[buf][r * L::VST + c * 8]) = vreg[it];
+    for (int it = 0; it < NI; ++it) {
+      lds_dma16(rk, &lds.k[buf][(w * NI + it) * 512], koff[it] + kb);
+      lds_dma16(rv, &lds.v[buf][(w * NI + it) * 512], voff[it] + vb);
     }
   };
+  // this lane's K fragment offset (elements) per k-step and V transposing-read
+  // offset per d tile at rows 0-15 (the swizzles repeat every 16 rows)
+  int kfo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int r = lane & 15;
+    kfo[ks] = r * D + ((ks * 4 + (lane >> 4)) ^ L::kswz(r)) * 8;
+  }
+  int vfo[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int s16 = lane & 15;
+    const int r = (lane >> 4) * 4 + (s16 >> 2);
+    const int c = dt * 2 + ((s16 & 3) >> 1);
+    vfo[dt] = r * D + (c ^ L::vswz(r)) * 8 + (s16 & 1) * 4;
+  }
 
   // The workgroup's tiles (valid, not entirely in its future) are compacted
   // into LDS by wave 0, kMaxTiles raw entries at a time, so the main loop
@@ -247,20 +249,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
     const int ntiles = lds_ntiles;
     int buf = 0;
     if (ntiles > 0) {
-      load_tile(lds_tiles[0]);
+      load_tile(lds_tiles[0], 0);
       if constexpr (BIAS && TOK) load_bias(0, bcur);
-      store_tile(0);
     }
-    // Drain every outstanding vector load (the Q fragments) here, so that the
-    // loop's only pending loads are the next tile's prefetch and the MFMAs on
-    // the current tile never wait for it.
+    // Drain every outstanding vector load (the Q fragments, tile 0) here, so
+    // that the loop's only pending loads are the next tile's and the MFMAs on
+    // the current tile never wait for them.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       const int k0 = lds_tiles[t];
       const bool more = t + 1 < ntiles;
+      // the other buffer's last reads (tile t - 1) ended at the barrier
       if (more) {
-        load_tile(lds_tiles[t + 1]);
+        load_tile(lds_tiles[t + 1], buf ^ 1);
         if constexpr (BIAS && TOK) load_bias(t + 1, bnxt);
       }
       // bias of the tile for each query column (score units)
@@ -294,8 +296,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt) {
-            const uint4 kf = *reinterpret_cast<const uint4*>(
-                &lds.k[buf][(kt * 16 + (lane & 15)) * L::KST + ks * 32 + (lane >> 4) * 8]);
+            const uint4 kf = *reinterpret_cast<const uint4*>(&lds.k[buf][kfo[ks] + kt * 16 * D]);
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) s[kt][qt] = mfma16(kf, qf[qt][ks], s[kt][qt]);
           }
@@ -378,12 +379,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
             // V^T fragment by two transposing reads of the row-major V tile:
             // keys 32kk + 4G + e and 32kk + 16 + 4G + e (G = lane/16) for
             // column 16dt + lane%16, the key order of the P fragment
-            const int s16 = lane & 15;
-            const uint16_t* vp = &lds.v[buf][(kk * 32 + (lane >> 4) * 4 + (s16 >> 2)) * L::VST +
-                                             dt * 16 + 4 * (s16 & 3)];
+            const uint16_t* vp = &lds.v[buf][vfo[dt] + kk * 32 * D];
             typedef __attribute__((address_space(3))) v4i16 lds_v4;
             const v4i16 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp));
-            const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 16 * L::VST));
+            const v4i16 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(vp + 16 * D));
             const uint2 u0 = __builtin_bit_cast(uint2, r0), u1 = __builtin_bit_cast(uint2, r1);
             const uint4 vf = make_uint4(u0.x, u0.y, u1.x, u1.y);
 #pragma unroll
@@ -392,11 +391,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
         }
       }
       __builtin_amdgcn_s_setprio(0);
-      if (more) store_tile(buf ^ 1);
       if constexpr (BIAS && TOK) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) bcur[qt] = bnxt[qt];
       }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile t + 1 is in LDS
       __syncthreads();
       buf ^= 1;
     }
@@ -548,15 +547,6 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
 // through direct-to-LDS buffer loads into three rotating buffers (unpadded,
 // 16-byte chunks XOR-swizzled per row for conflict-free fragment reads).
 // ---------------------------------------------------------------------------
-template <int D>
-struct PpLds {
-  static constexpr int NC = D / 8;     // 16-byte chunks per row
-  static constexpr int RPL = 16 / NC;  // rows per 256-byte bank line
-  __host__ __device__ static constexpr int kswz(int r) { return (r / RPL) & (NC - 1); }
-  __host__ __device__ static constexpr int vswz(int r) { return ((r / RPL) & (NC / 2 - 1)) << 1; }
-  alignas(16) uint16_t k[3][64 * D];
-  alignas(16) uint16_t v[3][64 * D];
-};
 
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(512, 1) void attend_prefill_pp(AttendArgs a, int wpb) {

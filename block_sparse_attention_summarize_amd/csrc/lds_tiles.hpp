@@ -51,10 +51,15 @@ __device__ __forceinline__ void lds_dma16(const u32x4& d, const void* lds, uint3
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (const __attribute__((address_space(3))) void*)lds)));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m0), "v"(voff), "s"(d)
-               : "memory", "m0");
+  // M0 (the load's LDS base, read when the instruction issues) is saved and
+  // restored around it, so the compiler's view of M0 is unchanged
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(m0), "v"(voff), "s"(d)
+      : "memory");
 }
 
 // s_waitcnt vmcnt(N): all but the N youngest vector memory operations of this
