@@ -14,7 +14,7 @@
 //   attend_prefill_pp     the same computation for plain block rows with many
 //                         key tiles: eight wavefronts in two groups half a
 //                         tile apart, alternating MFMA and softmax phases.
-//   attend_prefill_f32    fp32 inputs: one query per lane, VALU dot products
+//   attend_prefill_f32    fp32 inputs: each query over D/16 lanes, VALU dot products
 //                         (fp32 matrix rate is not the bound at these sizes).
 // With per-token selections (TOK) a row is a tile of 64 queries whose list
 // holds the blocks any of its tokens selected, each with a 64-bit word of the
@@ -433,14 +433,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
 }
 
 // ---------------------------------------------------------------------------
-// fp32 prefill: one query per lane, 32-key tiles in LDS read by broadcast.
+// fp32 prefill: each query is spread over LPQ = D/16 lanes (16 dimensions
+// each), 64 queries per workgroup, so a query block keeps LPQ times more
+// wavefronts busy than one query per lane would.  The workgroup's tiles of 32
+// keys are listed in LDS, then staged (K and V, 16-byte loads by every
+// thread, rows past the sequence read as zero) into two LDS buffers, the next
+// tile's loads in flight while the current one is used.  q.k is summed over
+// the query's lanes; each of them runs the same online softmax for its
+// dimensions of o.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
-  constexpr int KT = 32;
-  __shared__ float ks[KT][D];
-  __shared__ float vs[KT][D];
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(4 * D) void attend_prefill_f32(AttendArgs a) {
+  constexpr int LPQ = D / 16;     // lanes per query
+  constexpr int NT = 64 * LPQ;    // threads: 64 queries
+  constexpr int KT = 32;          // keys per tile
+  constexpr int F4 = KT * D / 4;  // 16-byte chunks per tile and tensor
+  constexpr int PT = F4 / NT;     // per thread
+  static_assert(PT * NT == F4 && (LPQ == 4 || LPQ == 8), "tile split over the workgroup");
+  constexpr int MAXT = 256;       // tile-list chunk staged in LDS
+  __shared__ float4 ks[2][F4];
+  __shared__ float4 vs[2][F4];
+  __shared__ int tk0[MAXT];  // first key of the tile
+  __shared__ int tent[MAXT];  // its list entry
+  __shared__ int ntl;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int qi = tid / LPQ;  // query of the block
+  const int ds = tid % LPQ;  // dimensions [16 ds, 16 ds + 16)
   const bool tok = a.bits != nullptr;  // rows are 64-query tiles
   const int nsub = tok ? 1 : a.B / 64;
   const int qb = tok ? 64 : a.B;
@@ -455,85 +474,167 @@ __global__ __launch_bounds__(64) void attend_prefill_f32(AttendArgs a) {
   const int G = a.hq / a.hkv;
   const int g = h / G;
   const int64_t qpos0 = static_cast<int64_t>(i) * qb + qs * 64;
-  const int64_t t = qpos0 + lane;
+  const int64_t t = qpos0 + qi;
   int64_t qmax = qpos0 + 63;
   if (qmax > a.q_len - 1) qmax = a.q_len - 1;
   const float* Qg = static_cast<const float*>(a.Q) + b * a.qs.b + h * a.qs.h;
-  const float* Kg = static_cast<const float*>(a.K) + b * a.ks.b + g * a.ks.h;
-  const float* Vg = static_cast<const float*>(a.V) + b * a.vs.b + g * a.vs.h;
+  const auto rk = make_rsrc(static_cast<const float*>(a.K) + b * a.ks.b + g * a.ks.h,
+                            head_bytes(a.kv_len, a.ks.t, D, 4));
+  const auto rv = make_rsrc(static_cast<const float*>(a.V) + b * a.vs.b + g * a.vs.h,
+                            head_bytes(a.kv_len, a.vs.t, D, 4));
+  const uint32_t kst = static_cast<uint32_t>(a.ks.t * 4), vst = static_cast<uint32_t>(a.vs.t * 4);
   const float sc = a.sm_scale * kLog2e;
-  float q[D], o[D];
+  float q[16], o[16];
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    q[c] = t < a.q_len ? Qg[t * a.qs.t + c] * sc : 0.f;
-    o[c] = 0.f;
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const float4 v = t < a.q_len ? *reinterpret_cast<const float4*>(Qg + t * a.qs.t + ds * 16 + c4 * 4)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    q[c4 * 4 + 0] = v.x * sc;
+    q[c4 * 4 + 1] = v.y * sc;
+    q[c4 * 4 + 2] = v.z * sc;
+    q[c4 * 4 + 3] = v.w * sc;
   }
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = 0.f;
   float m = -INFINITY, l = 0.f;
   const int64_t rowid = (static_cast<int64_t>(b) * a.hkv + g) * a.nrow + i;
   int n = a.cnt[rowid];
   n = n < 0 ? 0 : (n > a.k_max ? a.k_max : n);
   const int32_t* list = a.idx + rowid * a.k_max;
-  for (int s = 0; s < n; ++s) {
-    const int j = list[s];
-    if (j < 0 || j >= a.nblk) continue;
-    // this lane's token selected block j (always, for block rows)
-    bool on = !tok || ((a.bits[rowid * a.k_max + s] >> lane) & 1ull);
-    // prior: bias of the block for this query, log2 units (scores are too)
-    float bias2 = 0.f;
-    if (a.tbias) {
-      bias2 = a.tbias[(rowid * a.k_max + s) * 64 + lane] * kLog2e;
-    } else if (a.wsel) {
-      const float wv = a.wsel[rowid * a.k_max + s];
-      if (!(wv > 0.f)) continue;
-      bias2 = a.sigma * __log2f(wv);
+  const int tpb = a.B / KT;  // tiles per block
+
+  float4 kr[PT], vr[PT];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < PT; ++it) {
+      const int f = tid + NT * it;
+      const uint32_t r = static_cast<uint32_t>(k0 + f / (D / 4)), c = f % (D / 4);
+      kr[it] = __builtin_bit_cast(float4, buf_load16(rk, r * kst + c * 16));
+      vr[it] = __builtin_bit_cast(float4, buf_load16(rv, r * vst + c * 16));
     }
-    on = on && bias2 != -INFINITY;
-    for (int64_t k0 = static_cast<int64_t>(j) * a.B; k0 < static_cast<int64_t>(j + 1) * a.B;
-         k0 += KT) {
-      if (k0 > qmax || k0 >= a.kv_len) break;
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < PT; ++it) {
+      ks[buf][tid + NT * it] = kr[it];
+      vs[buf][tid + NT * it] = vr[it];
+    }
+  };
+  // sum over the query's LPQ consecutive lanes (every one of them gets it)
+  auto qsum = [&](float v) {
+    v += dppf<0xB1>(v);  // lane ^ 1
+    v += dppf<0x4E>(v);  // lane ^ 2
+    if constexpr (LPQ == 8) v += dppf<0x141>(v);  // the other quad of the 8-lane half
+    return v;
+  };
+
+  const int nraw = n * tpb;
+  for (int base = 0; base < nraw; base += MAXT) {
+    if (tid < 64) {
+      int c = 0;
+      for (int r = 0; r < MAXT && base + r < nraw; r += 64) {
+        const int T = base + r + lane;
+        bool ok = T < nraw;
+        int k0 = 0;
+        if (ok) {
+          const int j = list[T / tpb];
+          ok = j >= 0 && j < a.nblk;
+          if (ok) {
+            const int64_t kk = static_cast<int64_t>(j) * a.B + (T % tpb) * KT;
+            ok = kk <= qmax && kk < a.kv_len;
+            if (ok && a.wsel && !a.tbias) ok = a.wsel[rowid * a.k_max + T / tpb] > 0.f;
+            k0 = static_cast<int>(kk);
+          }
+        }
+        const uint64_t mk = __ballot(ok);
+        if (ok) {
+          tk0[c + lanes_below(mk)] = k0;
+          tent[c + lanes_below(mk)] = T / tpb;
+        }
+        c += __popcll(mk);
+      }
+      if (lane == 0) ntl = c;
+    }
+    __syncthreads();
+    const int nt = ntl;
+    if (nt > 0) {
+      load_tile(tk0[0]);
+      store_tile(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < nt; ++it) {
+      const int buf = it & 1;
+      if (it + 1 < nt) load_tile(tk0[it + 1]);
+      const int k0 = tk0[it], s = tent[it];
+      // this query's token selected the block (always, for block rows), and
+      // the prior's bias of the block for it, log2 units (scores are too)
+      bool on = !tok || ((a.bits[rowid * a.k_max + s] >> qi) & 1ull);
+      float bias2 = 0.f;
+      if (a.tbias)
+        bias2 = a.tbias[(rowid * a.k_max + s) * 64 + qi] * kLog2e;
+      else if (a.wsel)
+        bias2 = a.sigma * __log2f(a.wsel[rowid * a.k_max + s]);
+      on = on && bias2 != -INFINITY;
+      // 8 keys at a time, each group its own online-softmax step; the loop
+      // is kept rolled so that a group's LDS reads are not all hoisted
+#pragma unroll 1
+      for (int r0 = 0; r0 < KT; r0 += 8) {
+        const float4* kb = &ks[buf][r0 * (D / 4) + ds * 4];
+        const float4* vb = &vs[buf][r0 * (D / 4) + ds * 4];
+        float sv[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          float acc = 0.f;
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const float4 kv = kb[r * (D / 4) + c4];
+            acc = fmaf(q[c4 * 4 + 0], kv.x, acc);
+            acc = fmaf(q[c4 * 4 + 1], kv.y, acc);
+            acc = fmaf(q[c4 * 4 + 2], kv.z, acc);
+            acc = fmaf(q[c4 * 4 + 3], kv.w, acc);
+          }
+          acc = qsum(acc);
+          const int64_t key = k0 + r0 + r;
+          sv[r] = (key > t || key >= a.kv_len || !on) ? -INFINITY : acc + bias2;
+          mx = fmaxf(mx, sv[r]);
+        }
+        const float mnew = fmaxf(m, mx);
+        const float bse = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = exp2f(m - bse);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) o[c] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float p = exp2f(sv[r] - bse);
+          l += p;
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const float4 vv = vb[r * (D / 4) + c4];
+            o[c4 * 4 + 0] = fmaf(p, vv.x, o[c4 * 4 + 0]);
+            o[c4 * 4 + 1] = fmaf(p, vv.y, o[c4 * 4 + 1]);
+            o[c4 * 4 + 2] = fmaf(p, vv.z, o[c4 * 4 + 2]);
+            o[c4 * 4 + 3] = fmaf(p, vv.w, o[c4 * 4 + 3]);
+          }
+        }
+      }
+      // the other buffer's last reads (tile it - 1) ended at the last barrier
+      if (it + 1 < nt) store_tile(buf ^ 1);
       __syncthreads();
-      for (int e = lane; e < KT * D; e += 64) {
-        const int r = e / D, c = e % D;
-        const int64_t tt = k0 + r;
-        ks[r][c] = tt < a.kv_len ? Kg[tt * a.ks.t + c] : 0.f;
-        vs[r][c] = tt < a.kv_len ? Vg[tt * a.vs.t + c] : 0.f;
-      }
-      __syncthreads();
-      float sv[KT];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < KT; ++r) {
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < D; ++c) acc = fmaf(q[c], ks[r][c], acc);
-        const int64_t key = k0 + r;
-        sv[r] = (key > t || key >= a.kv_len || !on) ? -INFINITY : acc + bias2;
-        mx = fmaxf(mx, sv[r]);
-      }
-      const float mnew = fmaxf(m, mx);
-      const float base = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(m - base);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int c = 0; c < D; ++c) o[c] *= alpha;
-#pragma unroll
-      for (int r = 0; r < KT; ++r) {
-        const float p = exp2f(sv[r] - base);
-        l += p;
-#pragma unroll
-        for (int c = 0; c < D; ++c) o[c] = fmaf(p, vs[r][c], o[c]);
-      }
     }
   }
   if (t >= a.q_len) return;
-  if (a.lse)
+  if (a.lse && ds == 0)
     a.lse[(static_cast<int64_t>(b) * a.hq + h) * a.q_len + t] =
         l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* Og = static_cast<float*>(a.O) + b * a.os.b + h * a.os.h + t * a.os.t;
+  float* Og = static_cast<float*>(a.O) + b * a.os.b + h * a.os.h + t * a.os.t + ds * 16;
 #pragma unroll
-  for (int c = 0; c < D; ++c) Og[c] = o[c] * inv;
+  for (int c4 = 0; c4 < 4; ++c4)
+    *reinterpret_cast<float4*>(Og + c4 * 4) =
+        make_float4(o[c4 * 4] * inv, o[c4 * 4 + 1] * inv, o[c4 * 4 + 2] * inv, o[c4 * 4 + 3] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -914,9 +1015,9 @@ hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream) {
   if (a.bf16) return a.d == 64 ? prefill_bf16_dispatch<64>(a, stream) : prefill_bf16_dispatch<128>(a, stream);
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hq * a.nrow * (a.bits ? 1 : a.B / 64);
   if (a.d == 64)
-    hipLaunchKernelGGL(attend_prefill_f32<64>, dim3(grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(attend_prefill_f32<64>, dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(attend_prefill_f32<128>, dim3(grid), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(attend_prefill_f32<128>, dim3(grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
