@@ -434,32 +434,37 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attend_prefill_bf16(AttendArg
 
 // ---------------------------------------------------------------------------
 // fp32 prefill: each query is spread over LPQ = D/16 lanes (16 dimensions
-// each), 64 queries per workgroup, so a query block keeps LPQ times more
-// wavefronts busy than one query per lane would.  The workgroup's tiles of 32
-// keys are listed in LDS, then staged (K and V, 16-byte loads by every
-// thread, rows past the sequence read as zero) into two LDS buffers, the next
-// tile's loads in flight while the current one is used.  q.k is summed over
-// the query's lanes; each of them runs the same online softmax for its
-// dimensions of o.
+// each), 64 queries per group of LPQ wavefronts, and a workgroup holds
+// NS = 16/LPQ such groups for the same 64 queries: the workgroup's tiles of 32
+// keys are listed in LDS, group g takes tiles g, g + NS, ..., staging each (K
+// and V, 16-byte loads by every thread of the group, rows past the sequence
+// read as zero) into its two LDS buffers, the next tile's loads in flight
+// while the current one is used.  q.k is summed over the query's lanes; each
+// of them runs the same online softmax for its dimensions of o.  At the end
+// the groups' (m, l, o) are merged through LDS.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(4 * D) void attend_prefill_f32(AttendArgs a) {
+__global__ __launch_bounds__(1024) void attend_prefill_f32(AttendArgs a) {
   constexpr int LPQ = D / 16;     // lanes per query
-  constexpr int NT = 64 * LPQ;    // threads: 64 queries
+  constexpr int NTG = 64 * LPQ;   // threads of a group: 64 queries
+  constexpr int NS = 16 / LPQ;    // groups (key splits)
   constexpr int KT = 32;          // keys per tile
   constexpr int F4 = KT * D / 4;  // 16-byte chunks per tile and tensor
-  constexpr int PT = F4 / NT;     // per thread
-  static_assert(PT * NT == F4 && (LPQ == 4 || LPQ == 8), "tile split over the workgroup");
+  constexpr int PT = F4 / NTG;    // per thread
+  static_assert(PT * NTG == F4 && (LPQ == 4 || LPQ == 8), "tile split over a group");
   constexpr int MAXT = 256;       // tile-list chunk staged in LDS
-  __shared__ float4 ks[2][F4];
-  __shared__ float4 vs[2][F4];
+  // [group][buffer][K, V]; reused for the merge once every tile is done
+  __shared__ float4 kv[NS][2][2][F4];
+  static_assert(sizeof(kv) >= (NS * NTG * 16 + NS * 64 * 2) * sizeof(float), "merge area");
   __shared__ int tk0[MAXT];  // first key of the tile
   __shared__ int tent[MAXT];  // its list entry
   __shared__ int ntl;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int qi = tid / LPQ;  // query of the block
-  const int ds = tid % LPQ;  // dimensions [16 ds, 16 ds + 16)
+  const int grp = tid / NTG;
+  const int gt = tid % NTG;
+  const int qi = gt / LPQ;  // query of the block
+  const int ds = gt % LPQ;  // dimensions [16 ds, 16 ds + 16)
   const bool tok = a.bits != nullptr;  // rows are 64-query tiles
   const int nsub = tok ? 1 : a.B / 64;
   const int qb = tok ? 64 : a.B;
@@ -507,7 +512,7 @@ __global__ __launch_bounds__(4 * D) void attend_prefill_f32(AttendArgs a) {
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < PT; ++it) {
-      const int f = tid + NT * it;
+      const int f = gt + NTG * it;
       const uint32_t r = static_cast<uint32_t>(k0 + f / (D / 4)), c = f % (D / 4);
       kr[it] = __builtin_bit_cast(float4, buf_load16(rk, r * kst + c * 16));
       vr[it] = __builtin_bit_cast(float4, buf_load16(rv, r * vst + c * 16));
@@ -516,8 +521,8 @@ __global__ __launch_bounds__(4 * D) void attend_prefill_f32(AttendArgs a) {
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < PT; ++it) {
-      ks[buf][tid + NT * it] = kr[it];
-      vs[buf][tid + NT * it] = vr[it];
+      kv[grp][buf][0][gt + NTG * it] = kr[it];
+      kv[grp][buf][1][gt + NTG * it] = vr[it];
     }
   };
   // sum over the query's LPQ consecutive lanes (every one of them gets it)
@@ -557,79 +562,117 @@ __global__ __launch_bounds__(4 * D) void attend_prefill_f32(AttendArgs a) {
     }
     __syncthreads();
     const int nt = ntl;
-    if (nt > 0) {
-      load_tile(tk0[0]);
+    if (grp < nt) {
+      load_tile(tk0[grp]);
       store_tile(0);
     }
     __syncthreads();
-    for (int it = 0; it < nt; ++it) {
+    const int nit = (nt + NS - 1) / NS;
+    for (int it = 0; it < nit; ++it) {
       const int buf = it & 1;
-      if (it + 1 < nt) load_tile(tk0[it + 1]);
-      const int k0 = tk0[it], s = tent[it];
-      // this query's token selected the block (always, for block rows), and
-      // the prior's bias of the block for it, log2 units (scores are too)
-      bool on = !tok || ((a.bits[rowid * a.k_max + s] >> qi) & 1ull);
-      float bias2 = 0.f;
-      if (a.tbias)
-        bias2 = a.tbias[(rowid * a.k_max + s) * 64 + qi] * kLog2e;
-      else if (a.wsel)
-        bias2 = a.sigma * __log2f(a.wsel[rowid * a.k_max + s]);
-      on = on && bias2 != -INFINITY;
-      // 8 keys at a time, each group its own online-softmax step; the loop
-      // is kept rolled so that a group's LDS reads are not all hoisted
+      const int cur = it * NS + grp, nxt = cur + NS;
+      if (nxt < nt) load_tile(tk0[nxt]);
+      if (cur < nt) {
+        const int k0 = tk0[cur], s = tent[cur];
+        // this query's token selected the block (always, for block rows), and
+        // the prior's bias of the block for it, log2 units (scores are too)
+        bool on = !tok || ((a.bits[rowid * a.k_max + s] >> qi) & 1ull);
+        float bias2 = 0.f;
+        if (a.tbias)
+          bias2 = a.tbias[(rowid * a.k_max + s) * 64 + qi] * kLog2e;
+        else if (a.wsel)
+          bias2 = a.sigma * __log2f(a.wsel[rowid * a.k_max + s]);
+        on = on && bias2 != -INFINITY;
+        // 8 keys at a time, each group its own online-softmax step; the loop
+        // is kept rolled so that a group's LDS reads are not all hoisted
 #pragma unroll 1
-      for (int r0 = 0; r0 < KT; r0 += 8) {
-        const float4* kb = &ks[buf][r0 * (D / 4) + ds * 4];
-        const float4* vb = &vs[buf][r0 * (D / 4) + ds * 4];
-        float sv[8];
-        float mx = -INFINITY;
+        for (int r0 = 0; r0 < KT; r0 += 8) {
+          const float4* kb = &kv[grp][buf][0][r0 * (D / 4) + ds * 4];
+          const float4* vb = &kv[grp][buf][1][r0 * (D / 4) + ds * 4];
+          float sv[8];
+          float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          float acc = 0.f;
+          for (int r = 0; r < 8; ++r) {
+            float acc = 0.f;
 #pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const float4 kv = kb[r * (D / 4) + c4];
-            acc = fmaf(q[c4 * 4 + 0], kv.x, acc);
-            acc = fmaf(q[c4 * 4 + 1], kv.y, acc);
-            acc = fmaf(q[c4 * 4 + 2], kv.z, acc);
-            acc = fmaf(q[c4 * 4 + 3], kv.w, acc);
+            for (int c4 = 0; c4 < 4; ++c4) {
+              const float4 kq = kb[r * (D / 4) + c4];
+              acc = fmaf(q[c4 * 4 + 0], kq.x, acc);
+              acc = fmaf(q[c4 * 4 + 1], kq.y, acc);
+              acc = fmaf(q[c4 * 4 + 2], kq.z, acc);
+              acc = fmaf(q[c4 * 4 + 3], kq.w, acc);
+            }
+            acc = qsum(acc);
+            const int64_t key = k0 + r0 + r;
+            sv[r] = (key > t || key >= a.kv_len || !on) ? -INFINITY : acc + bias2;
+            mx = fmaxf(mx, sv[r]);
           }
-          acc = qsum(acc);
-          const int64_t key = k0 + r0 + r;
-          sv[r] = (key > t || key >= a.kv_len || !on) ? -INFINITY : acc + bias2;
-          mx = fmaxf(mx, sv[r]);
-        }
-        const float mnew = fmaxf(m, mx);
-        const float bse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = exp2f(m - bse);
-        m = mnew;
-        l *= alpha;
+          const float mnew = fmaxf(m, mx);
+          const float bse = mnew == -INFINITY ? 0.f : mnew;
+          const float alpha = exp2f(m - bse);
+          m = mnew;
+          l *= alpha;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) o[c] *= alpha;
+          for (int c = 0; c < 16; ++c) o[c] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float p = exp2f(sv[r] - bse);
-          l += p;
+          for (int r = 0; r < 8; ++r) {
+            const float p = exp2f(sv[r] - bse);
+            l += p;
 #pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const float4 vv = vb[r * (D / 4) + c4];
-            o[c4 * 4 + 0] = fmaf(p, vv.x, o[c4 * 4 + 0]);
-            o[c4 * 4 + 1] = fmaf(p, vv.y, o[c4 * 4 + 1]);
-            o[c4 * 4 + 2] = fmaf(p, vv.z, o[c4 * 4 + 2]);
-            o[c4 * 4 + 3] = fmaf(p, vv.w, o[c4 * 4 + 3]);
+            for (int c4 = 0; c4 < 4; ++c4) {
+              const float4 vv = vb[r * (D / 4) + c4];
+              o[c4 * 4 + 0] = fmaf(p, vv.x, o[c4 * 4 + 0]);
+              o[c4 * 4 + 1] = fmaf(p, vv.y, o[c4 * 4 + 1]);
+              o[c4 * 4 + 2] = fmaf(p, vv.z, o[c4 * 4 + 2]);
+              o[c4 * 4 + 3] = fmaf(p, vv.w, o[c4 * 4 + 3]);
+            }
           }
         }
       }
-      // the other buffer's last reads (tile it - 1) ended at the last barrier
-      if (it + 1 < nt) store_tile(buf ^ 1);
+      // the other buffer's last reads (this group's previous tile) ended at
+      // the last barrier
+      if (nxt < nt) store_tile(buf ^ 1);
       __syncthreads();
     }
   }
-  if (t >= a.q_len) return;
+  // merge the groups: every group's state to LDS (the tile buffers are free:
+  // the last barrier ended their reads), then group 0 combines
+  float* mo = reinterpret_cast<float*>(&kv[0][0][0][0]);  // [NS][NTG][16]
+  float* ml = mo + NS * NTG * 16;                            // [NS][64][2]
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4)
+    *reinterpret_cast<float4*>(mo + (grp * NTG + gt) * 16 + c4 * 4) =
+        make_float4(o[c4 * 4], o[c4 * 4 + 1], o[c4 * 4 + 2], o[c4 * 4 + 3]);
+  if (ds == 0) {
+    ml[(grp * 64 + qi) * 2] = m;
+    ml[(grp * 64 + qi) * 2 + 1] = l;
+  }
+  __syncthreads();
+  if (grp != 0 || t >= a.q_len) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int gg = 0; gg < NS; ++gg) M = fmaxf(M, ml[(gg * 64 + qi) * 2]);
+  const float bse = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = 0.f;
+#pragma unroll
+  for (int gg = 0; gg < NS; ++gg) {
+    const float f = exp2f(ml[(gg * 64 + qi) * 2] - bse);
+    L = fmaf(ml[(gg * 64 + qi) * 2 + 1], f, L);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const float4 v = *reinterpret_cast<const float4*>(mo + (gg * NTG + gt) * 16 + c4 * 4);
+      o[c4 * 4 + 0] = fmaf(v.x, f, o[c4 * 4 + 0]);
+      o[c4 * 4 + 1] = fmaf(v.y, f, o[c4 * 4 + 1]);
+      o[c4 * 4 + 2] = fmaf(v.z, f, o[c4 * 4 + 2]);
+      o[c4 * 4 + 3] = fmaf(v.w, f, o[c4 * 4 + 3]);
+    }
+  }
   if (a.lse && ds == 0)
     a.lse[(static_cast<int64_t>(b) * a.hq + h) * a.q_len + t] =
-        l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+        L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   float* Og = static_cast<float*>(a.O) + b * a.os.b + h * a.os.h + t * a.os.t + ds * 16;
 #pragma unroll
   for (int c4 = 0; c4 < 4; ++c4)
@@ -1015,9 +1058,9 @@ hipError_t launch_attend_prefill(const AttendArgs& a, hipStream_t stream) {
   if (a.bf16) return a.d == 64 ? prefill_bf16_dispatch<64>(a, stream) : prefill_bf16_dispatch<128>(a, stream);
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hq * a.nrow * (a.bits ? 1 : a.B / 64);
   if (a.d == 64)
-    hipLaunchKernelGGL(attend_prefill_f32<64>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attend_prefill_f32<64>, dim3(grid), dim3(1024), 0, stream, a);
   else
-    hipLaunchKernelGGL(attend_prefill_f32<128>, dim3(grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(attend_prefill_f32<128>, dim3(grid), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
