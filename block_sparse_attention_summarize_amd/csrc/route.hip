@@ -709,7 +709,9 @@ __device__ inline float entmax_tau(const float (&x)[K], double lo, double hi, fl
   return static_cast<float>(0.5 * (l2 + h2));
 }
 
-template <int E, int MINW>
+// AK: alpha known at compile time (1: 1.5, 2: 2; 0: the run-time a.alpha), so
+// that the closed-form cases carry no pow() code and its registers.
+template <int E, int MINW, int AK>
 __global__ __launch_bounds__(kThreads, MINW) void entmax_rows_kernel(EntmaxArgs a) {
   __shared__ int bins[kWaves][16];
   __shared__ float live_x[kWaves][kWave];
@@ -724,7 +726,7 @@ __global__ __launch_bounds__(kThreads, MINW) void entmax_rows_kernel(EntmaxArgs 
   const int b = static_cast<int>(bg / a.hkv);
   const RowInfo ri = row_info(a.rule, b, row);
   const int n = ri.cand_end;  // <= 64 E
-  const float alpha = a.alpha;
+  const float alpha = AK == 1 ? 1.5f : AK == 2 ? 2.f : a.alpha;
   const double ad = alpha;
   float wsum[E];
 #pragma unroll
@@ -898,11 +900,23 @@ hipError_t launch_route_entmax(const EntmaxArgs& a, hipStream_t stream) {
     // per-token rows: many short rows, one wavefront each
     const int64_t rows = static_cast<int64_t>(a.batch) * a.hkv * a.nrow;
     const unsigned grid = static_cast<unsigned>((rows + kWaves - 1) / kWaves);
-    // latency-bound: 8 logits per lane fit three wavefronts per SIMD
-    if (a.nblk <= 8 * kWave)
-      hipLaunchKernelGGL((entmax_rows_kernel<8, 3>), dim3(grid), dim3(kThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((entmax_rows_kernel<16, 1>), dim3(grid), dim3(kThreads), 0, stream, a);
+    const bool small = a.nblk <= 8 * kWave;
+    if (a.alpha == 1.5f) {
+      if (small)
+        hipLaunchKernelGGL((entmax_rows_kernel<8, 3, 1>), dim3(grid), dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((entmax_rows_kernel<16, 1, 1>), dim3(grid), dim3(kThreads), 0, stream, a);
+    } else if (a.alpha == 2.f) {
+      if (small)
+        hipLaunchKernelGGL((entmax_rows_kernel<8, 3, 2>), dim3(grid), dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((entmax_rows_kernel<16, 1, 2>), dim3(grid), dim3(kThreads), 0, stream, a);
+    } else {
+      if (small)
+        hipLaunchKernelGGL((entmax_rows_kernel<8, 3, 0>), dim3(grid), dim3(kThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((entmax_rows_kernel<16, 1, 0>), dim3(grid), dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
   }
   const unsigned grid = static_cast<unsigned>(a.batch) * a.hkv * a.nrow;
