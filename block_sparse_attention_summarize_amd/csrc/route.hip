@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
 // workgroup takes `jgroup` consecutive block tiles of its row tile: the rows'
 // fragments are read from LDS into registers once and only the summaries are
 // staged per block tile (many rows, as with per-token routing, re-read them
-// far less often).
+// far less often), the next tile's loads in flight in registers while the
+// current tile's products run, then stored to the other of two LDS buffers.
 // ---------------------------------------------------------------------------
 constexpr int kTile = 64;
 constexpr int kPad = 4;
@@ -97,8 +98,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void scores_mfma(ScoreArgs a, int fill, int jgroup) {
-  __shared__ float qs[kTile][D + kPad];
-  __shared__ float ss[kTile][D + kPad];
+  // two staging buffers: the row tile is staged in buf[1] once and read into
+  // registers, after which buf[1] takes every other block tile
+  __shared__ float buf[2][kTile][D + kPad];
   const int nrt = (a.nrow + kTile - 1) / kTile;
   const int njt = (a.nblk + kTile - 1) / kTile;
   const int ngt = (njt + jgroup - 1) / jgroup;
@@ -117,69 +119,102 @@ __global__ __launch_bounds__(kThreads) void scores_mfma(ScoreArgs a, int fill, i
   const int jend = (r0 + rn - 1) / tok_b + ce;  // blocks past every row's candidates
   constexpr int V4 = D / 4;
   constexpr int KC = D / 16;
+  constexpr int PF = kTile * V4 / kThreads;  // 16-byte loads per thread and tile
+  static_assert(PF * kThreads == kTile * V4, "tile split over the threads");
   const int lr = lane & 15, lk = (lane >> 4) * 4;
-  float4 av[KC];  // this lane's row fragments, read once
-  bool staged = false;
-  for (int jt = gt * jgroup; jt < njt && jt < (gt + 1) * jgroup; ++jt) {
+  // the workgroup's block tiles: [jt0, jtc) hold candidates, [jtc, jt1) do not
+  const int jt0 = gt * jgroup;
+  const int jt1 = njt < (gt + 1) * jgroup ? njt : (gt + 1) * jgroup;
+  const int jtlast = (jend + kTile - 1) / kTile;  // first tile with no candidate
+  const int jtc = jt1 < jtlast ? jt1 : jtlast;
+  uint4 pre[PF];
+  // summaries of block tile jt into registers (rows past n_blk read as zero)
+  auto fetch = [&](int jt) {
+    const int j0 = jt * kTile;
+    const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
+    const auto rs = make_rsrc(a.S + (static_cast<int64_t>(sg_row) * a.nblk + j0) * D,
+                              static_cast<uint32_t>(jn) * D * 4);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) pre[i] = buf_load16(rs, static_cast<uint32_t>(tid + i * kThreads) * 16);
+  };
+  auto put = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int e = tid + i * kThreads, r = e / V4, c = e % V4;
+      *reinterpret_cast<uint4*>(&buf[k][r][c * 4]) = pre[i];
+    }
+  };
+  if (jt0 < jtc) {
+    {
+      const float* qg = a.qhat + (static_cast<int64_t>(bh) * a.nrow + r0) * D;
+      const auto rq = make_rsrc(qg, static_cast<uint32_t>(rn) * D * 4);
+      uint4 qv[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) qv[i] = buf_load16(rq, static_cast<uint32_t>(tid + i * kThreads) * 16);
+      fetch(jt0);
+#pragma unroll
+      for (int i = 0; i < PF; ++i) {
+        const int e = tid + i * kThreads, r = e / V4, c = e % V4;
+        *reinterpret_cast<uint4*>(&buf[1][r][c * 4]) = qv[i];
+      }
+      put(0);
+    }
+    __syncthreads();
+    float4 av[KC];  // this lane's row fragments, read once
+#pragma unroll
+    for (int k = 0; k < KC; ++k) av[k] = *reinterpret_cast<const float4*>(&buf[1][16 * w + lr][16 * k + lk]);
+    __syncthreads();  // buf[1] is free for the second block tile
+    for (int jt = jt0; jt < jtc; ++jt) {
+      const int cur = (jt - jt0) & 1;
+      const bool more = jt + 1 < jtc;
+      if (more) fetch(jt + 1);  // in flight during this tile's products
+      const int j0 = jt * kTile;
+      const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
+      float* out = a.scores + (static_cast<int64_t>(bh) * a.nrow + r0) * a.nblk + j0;
+      f32x4_t acc[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        float4 bv[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) bv[ct] = *reinterpret_cast<const float4*>(&buf[cur][16 * ct + lr][16 * k + lk]);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].x, bv[ct].x, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].y, bv[ct].y, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].z, bv[ct].z, acc[ct], 0, 0, 0);
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].w, bv[ct].w, acc[ct], 0, 0, 0);
+        }
+      }
+      // the next tile into the other buffer (last read before the previous
+      // barrier), ahead of this tile's stores so that the wait for its loads
+      // does not also wait for them
+      if (more) put(cur ^ 1);
+      // lane l holds rows 16w + 4(l/16) + i, block 16ct + l%16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + (lane >> 4) * 4 + i;
+        const int cend = (r0 + r) / tok_b + ce - j0;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int j = 16 * ct + lr;
+          if (r < rn && j < jn)
+            out[static_cast<int64_t>(r) * a.nblk + j] = j < cend ? acc[ct][i] * a.scale : -INFINITY;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (!fill) return;
+  // right of the last row's candidates
+  for (int jt = jtc > jt0 ? jtc : jt0; jt < jt1; ++jt) {
     const int j0 = jt * kTile;
     const int jn = a.nblk - j0 < kTile ? a.nblk - j0 : kTile;
     float* out = a.scores + (static_cast<int64_t>(bh) * a.nrow + r0) * a.nblk + j0;
-    if (j0 >= jend) {  // right of the last row's candidates
-      if (!fill) break;
-      for (int e = tid; e < kTile * kTile; e += kThreads) {
-        const int r = e / kTile, j = e % kTile;
-        if (r < rn && j < jn) out[static_cast<int64_t>(r) * a.nblk + j] = -INFINITY;
-      }
-      continue;
-    }
-    const float* sg = a.S + (static_cast<int64_t>(sg_row) * a.nblk + j0) * D;
-    const auto rs = make_rsrc(sg, static_cast<uint32_t>(jn) * D * 4);
-    __syncthreads();  // the previous tile's summaries are read
-    if (!staged) {
-      const float* qg = a.qhat + (static_cast<int64_t>(bh) * a.nrow + r0) * D;
-      const auto rq = make_rsrc(qg, static_cast<uint32_t>(rn) * D * 4);
-      for (int e = tid; e < kTile * V4; e += kThreads) {
-        const int r = e / V4, c = e % V4;
-        *reinterpret_cast<uint4*>(&qs[r][c * 4]) = buf_load16(rq, static_cast<uint32_t>(e) * 16);
-      }
-    }
-    for (int e = tid; e < kTile * V4; e += kThreads) {
-      const int r = e / V4, c = e % V4;
-      *reinterpret_cast<uint4*>(&ss[r][c * 4]) = buf_load16(rs, static_cast<uint32_t>(e) * 16);
-    }
-    __syncthreads();
-    if (!staged) {
-#pragma unroll
-      for (int k = 0; k < KC; ++k) av[k] = *reinterpret_cast<const float4*>(&qs[16 * w + lr][16 * k + lk]);
-      staged = true;
-    }
-    f32x4_t acc[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      float4 bv[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) bv[ct] = *reinterpret_cast<const float4*>(&ss[16 * ct + lr][16 * k + lk]);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].x, bv[ct].x, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].y, bv[ct].y, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].z, bv[ct].z, acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[k].w, bv[ct].w, acc[ct], 0, 0, 0);
-      }
-    }
-    // lane l holds rows 16w + 4(l/16) + i, block 16ct + l%16
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + (lane >> 4) * 4 + i;
-      const int cend = (r0 + r) / tok_b + ce - j0;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int j = 16 * ct + lr;
-        if (r < rn && j < jn)
-          out[static_cast<int64_t>(r) * a.nblk + j] = j < cend ? acc[ct][i] * a.scale : -INFINITY;
-      }
+    for (int e = tid; e < kTile * kTile; e += kThreads) {
+      const int r = e / kTile, j = e % kTile;
+      if (r < rn && j < jn) out[static_cast<int64_t>(r) * a.nblk + j] = -INFINITY;
     }
   }
 }
