@@ -88,6 +88,93 @@ __global__ __launch_bounds__(kVjpThreads) void entmax_vjp_rows(RouteBwdArgs a, i
   }
 }
 
+// The same for rows of whole float4s (n_blk % 4 == 0, n_blk <= kVjpVecMax):
+// each lane reads four probabilities at a time and keeps their g in
+// registers (up to kVjpCache * 256 blocks; the rest is read again), the
+// listed blocks' dw / G sit in LDS beside their marks, and dz is written in
+// one pass of 16-byte stores.
+constexpr int kVjpCache = 8;     // 256-block chunks whose g stay in registers
+constexpr int kVjpVecMax = 3840;  // keeps the dynamic LDS within 64 KB
+
+__global__ __launch_bounds__(kVjpThreads) void entmax_vjp_rows_vec(RouteBwdArgs a, int64_t nrows) {
+  extern __shared__ uint32_t vlds[];  // [kVjpRows][nwords marks, n_blk dw / G]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nblk = a.nblk;
+  const int nwords = (nblk + 31) / 32;
+  uint32_t* mark = vlds + wv * (nwords + nblk);
+  float* dwl = reinterpret_cast<float*>(mark + nwords);
+  for (int k = lane; k < nwords; k += kWave) mark[k] = 0u;
+  const int64_t hrow = static_cast<int64_t>(blockIdx.x) * kVjpRows + wv;  // (b * hq + h) * nrow + r
+  const bool live = hrow < nrows;
+  const int r = static_cast<int>(hrow % a.nrow);
+  const int64_t bh = hrow / a.nrow;
+  const int h = static_cast<int>(bh % a.hq);
+  const int64_t b = bh / a.hq;
+  const int G = a.hq / a.hkv;
+  const int64_t rowid = (b * a.hkv + h / G) * a.nrow + r;
+  const float* p = a.probs + hrow * nblk;
+  float* dz = a.dz + hrow * nblk;
+  const float expo = 2.f - a.alpha;
+  auto g4 = [&](int j) {
+    const float4 v = *reinterpret_cast<const float4*>(p + j);
+    return make_float4(entmax_g(v.x, a.alpha, expo), entmax_g(v.y, a.alpha, expo),
+                       entmax_g(v.z, a.alpha, expo), entmax_g(v.w, a.alpha, expo));
+  };
+  float4 gc[kVjpCache];
+  float sg = 0.f;
+  if (live) {
+#pragma unroll
+    for (int ch = 0; ch < kVjpCache; ++ch) {
+      const int j = ch * 256 + lane * 4;
+      gc[ch] = j < nblk ? g4(j) : make_float4(0.f, 0.f, 0.f, 0.f);
+      sg += (gc[ch].x + gc[ch].y) + (gc[ch].z + gc[ch].w);
+    }
+    for (int j = kVjpCache * 256 + lane * 4; j < nblk; j += 256) {
+      const float4 gv = g4(j);
+      sg += (gv.x + gv.y) + (gv.z + gv.w);
+    }
+  }
+  sg = wave_sum(sg);
+  int c = live ? a.cnt[rowid] : 0;
+  c = c < 0 ? 0 : (c > a.width ? a.width : c);
+  const int32_t* list = a.idx + rowid * a.width;
+  const float* dw = a.dwsel + rowid * a.width;
+  const float invG = 1.f / static_cast<float>(G);
+  __syncthreads();  // marks cleared
+  float sgd = 0.f;
+  for (int e = lane; e < c; e += kWave) {
+    const int j = list[e];
+    // forced blocks are no candidates (p = 0) and so carry no gradient
+    if (j >= 0 && j < nblk) {
+      const float dv = dw[e] * invG;
+      sgd += entmax_g(p[j], a.alpha, expo) * dv;
+      dwl[j] = dv;
+      atomicOr(&mark[j >> 5], 1u << (j & 31));
+    }
+  }
+  sgd = wave_sum(sgd);
+  __syncthreads();  // marks and dw set
+  if (!live) return;
+  const float m = sg > 0.f ? sgd / sg : 0.f;
+  auto put = [&](int j, const float4& gv) {
+    float gg[4] = {gv.x, gv.y, gv.z, gv.w};
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int jj = j + q;
+      const bool listed = (mark[jj >> 5] >> (jj & 31)) & 1u;
+      o[q] = a.fscale * gg[q] * ((listed ? dwl[jj] : 0.f) - m);
+    }
+    *reinterpret_cast<float4*>(dz + j) = make_float4(o[0], o[1], o[2], o[3]);
+  };
+#pragma unroll
+  for (int ch = 0; ch < kVjpCache; ++ch) {
+    const int j = ch * 256 + lane * 4;
+    if (j < nblk) put(j, gc[ch]);
+  }
+  for (int j = kVjpCache * 256 + lane * 4; j < nblk; j += 256) put(j, g4(j));
+}
+
 // Batched fp32 product on MFMA tiles, C[64 x D] = A[64 x K] B[K x D] per
 // workgroup, with A read through element strides (so it may be a transposed
 // view of dz) and both tiles staged in LDS with K contiguous.
@@ -287,9 +374,14 @@ int route_bwd_key_splits(int nrow) { return (nrow + kKeyRows - 1) / kKeyRows; }
 
 hipError_t launch_route_entmax_backward(const RouteBwdArgs& a, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.batch) * a.hq * a.nrow;
-  const size_t mark_bytes = static_cast<size_t>(kVjpRows) * ((a.nblk + 31) / 32) * 4;
-  hipLaunchKernelGGL(entmax_vjp_rows, dim3(static_cast<unsigned>((rows + kVjpRows - 1) / kVjpRows)),
-                     dim3(kVjpThreads), mark_bytes, stream, a, rows);
+  const unsigned vgrid = static_cast<unsigned>((rows + kVjpRows - 1) / kVjpRows);
+  if (a.nblk % 4 == 0 && a.nblk <= kVjpVecMax) {
+    const size_t lds_bytes = static_cast<size_t>(kVjpRows) * ((a.nblk + 31) / 32 + a.nblk) * 4;
+    hipLaunchKernelGGL(entmax_vjp_rows_vec, dim3(vgrid), dim3(kVjpThreads), lds_bytes, stream, a, rows);
+  } else {
+    const size_t mark_bytes = static_cast<size_t>(kVjpRows) * ((a.nblk + 31) / 32) * 4;
+    hipLaunchKernelGGL(entmax_vjp_rows, dim3(vgrid), dim3(kVjpThreads), mark_bytes, stream, a, rows);
+  }
   const unsigned bh = static_cast<unsigned>(a.batch) * a.hq;
   const dim3 gq(bh * static_cast<unsigned>((a.nrow + kGT - 1) / kGT));
   const dim3 gk(bh * static_cast<unsigned>((a.nblk + kGT - 1) / kGT) * a.ksplit);
