@@ -34,6 +34,12 @@ TOPK = {
     "tok_d64_mha": W["bf16_gqa_prefill_n32k"].scaled(mode="token", d=64, hq=3, hkv=3,
                                                      n=64 * 7 + 1, k_total=3,
                                                      force=synth.FORCE_DIAG, planted_blocks=2),
+    # 4096 tiles of 64 token rows: the score tiles of a row tile are walked by
+    # one workgroup, the next block tile's summaries loading during the
+    # current tile's products (and the score matrix written in full)
+    "tok_many_rows": W["bf16_gqa_prefill_n32k"].scaled(mode="token", batch=4, d=64, hq=8, hkv=8,
+                                                       n=64 * 128, k_total=6,
+                                                       force=synth.FORCE_DIAG, planted_blocks=4),
 }
 ENTMAX = {
     "tok_entmax_g4": W["entmax_prefill_n64k"].scaled(mode="token", hq=8, hkv=2, n=64 * 30 + 5,
